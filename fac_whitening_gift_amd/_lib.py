@@ -1,0 +1,301 @@
+"""ctypes binding of libgift.so (include/gift.h): argument marshalling only.
+
+Every computation happens in the HIP kernels behind the C ABI.  This module
+turns torch device tensors into the ABI's descriptors and pointers, passes
+torch's current HIP stream, and raises on a non-OK status.  If the library
+is not built it raises instead of falling back to anything else.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgift.so")
+
+RANK = 32
+MAX_SKETCH = 64
+BLOCK = 128
+
+GIFT_OK = 0
+DTYPE_F32, DTYPE_BF16 = 0, 1
+DAMP_FLOOR, DAMP_FLOOR_PLUS_TAIL = 0, 1
+SCALE_TENSOR, SCALE_BLOCK128 = 0, 1
+FLAG_NONFINITE, FLAG_ZERO_AMAX = 1, 2
+OP_WHITEN_QUANTIZE, OP_DEQUANT_UNWHITEN, OP_EUCLID_ROUNDTRIP, OP_ROUNDTRIP_ERROR = 0, 1, 2, 3
+
+COEF_ALPHA, COEF_BETA, COEF_LAMBDA_ISO, COEF_LAMBDA_FLOOR, COEF_TRACE, COEF_SIGMA2_TAIL = range(6)
+COEF_DW = 8
+COEF_DU = 8 + RANK
+COEF_COUNT = 8 + 2 * RANK
+
+EXPORTS = (
+    "gift_refresh_factor", "gift_refresh_workspace_bytes", "gift_whiten_quantize",
+    "gift_dequant_unwhiten", "gift_euclid_fp8_roundtrip", "gift_roundtrip_error",
+    "gift_group_workspace_bytes", "gift_status_string", "gift_last_error",
+    "gift_abi_version",
+)
+
+
+class GiftError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("%s: %s" % (status_name(status), detail))
+        self.status = status
+
+
+class _Factor(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("U", ctypes.c_void_p), ("theta", ctypes.c_void_p), ("coef", ctypes.c_void_p)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
+                ("G", ctypes.c_void_p), ("q", ctypes.c_void_p), ("inv_scale", ctypes.c_void_p),
+                ("G_hat", ctypes.c_void_p), ("factor", ctypes.POINTER(_Factor)),
+                ("W_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load libgift.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgift.so is not built: run python -m fac_whitening_gift_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ, U64, F = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                             ctypes.c_uint64, ctypes.c_float)
+    LP = ctypes.POINTER(_Layer)
+    sig = {
+        "gift_refresh_factor": (I, [P, I, I64, ctypes.POINTER(_Factor), F, I, I, I, U64, P, P, P,
+                                    SZ, P]),
+        "gift_refresh_workspace_bytes": (SZ, [I64, I64, I, I]),
+        "gift_whiten_quantize": (I, [LP, I, I, P, P, SZ, P]),
+        "gift_dequant_unwhiten": (I, [LP, I, I, P, SZ, P]),
+        "gift_euclid_fp8_roundtrip": (I, [LP, I, I, P, P, SZ, P]),
+        "gift_roundtrip_error": (I, [LP, I, P, P, SZ, P]),
+        "gift_group_workspace_bytes": (SZ, [I, LP, I, I]),
+        "gift_status_string": (ctypes.c_char_p, [I]),
+        "gift_last_error": (ctypes.c_char_p, []),
+        "gift_abi_version": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_name(s):
+    return load().gift_status_string(int(s)).decode()
+
+
+def _check(status):
+    if status != GIFT_OK:
+        raise GiftError(status, load().gift_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, shape, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+# --------------------------------------------------------------------------
+# Python-side holders of device tensors (the ABI structs point into them)
+# --------------------------------------------------------------------------
+
+class Factor:
+    """Device buffers of one rank-32 factor: U (d_in x 32), theta (32), coef."""
+
+    def __init__(self, d_in, device="cuda", U=None, theta=None, coef=None):
+        self.d_in = int(d_in)
+        self.U = U if U is not None else torch.zeros(d_in, RANK, device=device)
+        self.theta = theta if theta is not None else torch.zeros(RANK, device=device)
+        self.coef = coef if coef is not None else torch.zeros(COEF_COUNT, device=device)
+        _dev(self.U, torch.float32, (d_in, RANK), "U")
+        _dev(self.theta, torch.float32, (RANK,), "theta")
+        _dev(self.coef, torch.float32, (COEF_COUNT,), "coef")
+        self._struct = _Factor(self.d_in, RANK, self.U.data_ptr(), self.theta.data_ptr(),
+                               self.coef.data_ptr())
+
+    @property
+    def alpha(self):
+        return self.coef[COEF_ALPHA]
+
+    @property
+    def d_w(self):
+        return self.coef[COEF_DW:COEF_DW + RANK]
+
+    @property
+    def d_u(self):
+        return self.coef[COEF_DU:COEF_DU + RANK]
+
+
+class Layer:
+    """One layer of a grouped call: G (d_out x d_in fp32) and its outputs.
+
+    q, inv_scale and G_hat are allocated on G's device when not given;
+    inv_scale has 1 element, or d_out x d_in/128 for block scaling.
+    """
+
+    def __init__(self, G, factor=None, q=None, inv_scale=None, G_hat=None, W_out=None,
+                 block128=False, d_out=None, d_in=None, allocate=True):
+        if G is not None:
+            d_out, d_in = G.shape
+            dev = G.device
+        else:
+            dev = (q if q is not None else G_hat).device
+        self.d_out, self.d_in = int(d_out), int(d_in)
+        self.G = G
+        self.factor = factor
+        if allocate:
+            if q is None:
+                q = torch.empty(self.d_out, self.d_in, dtype=torch.uint8, device=dev)
+            if inv_scale is None:
+                shape = (self.d_out, self.d_in // BLOCK) if block128 else (1,)
+                inv_scale = torch.empty(shape, dtype=torch.float32, device=dev)
+            if G_hat is None:
+                G_hat = torch.empty(self.d_out, self.d_in, dtype=torch.float32, device=dev)
+        self.q, self.inv_scale, self.G_hat, self.W_out = q, inv_scale, G_hat, W_out
+        shape = (self.d_out, self.d_in)
+        _dev(G, torch.float32, shape, "G")
+        _dev(q, torch.uint8, shape, "q")
+        _dev(G_hat, torch.float32, shape, "G_hat")
+        _dev(W_out, torch.float32, shape, "W_out")
+        _dev(inv_scale, torch.float32, None, "inv_scale")
+        if factor is not None and factor.d_in != self.d_in:
+            raise ValueError("factor d_in %d != layer d_in %d" % (factor.d_in, self.d_in))
+
+
+def _layers_array(layers):
+    arr = (_Layer * max(1, len(layers)))()
+    for i, L in enumerate(layers):
+        arr[i].d_out = L.d_out
+        arr[i].d_in = L.d_in
+        arr[i].G = _ptr(L.G)
+        arr[i].q = _ptr(L.q)
+        arr[i].inv_scale = _ptr(L.inv_scale)
+        arr[i].G_hat = _ptr(L.G_hat)
+        arr[i].factor = (ctypes.pointer(L.factor._struct) if L.factor is not None
+                         else ctypes.POINTER(_Factor)())
+        arr[i].W_out = _ptr(L.W_out)
+    return arr
+
+
+def _workspace(nbytes, device, ws):
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small: %d < %d bytes" %
+                             (ws.numel() * ws.element_size(), nbytes))
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _device_of(layers):
+    for L in layers:
+        for t in (L.G, L.q, L.G_hat):
+            if t is not None:
+                return t.device
+    return torch.device("cuda")
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+
+def gift_group_workspace_bytes(op, layers, scaling=SCALE_TENSOR):
+    arr = _layers_array(layers)
+    return int(load().gift_group_workspace_bytes(op, arr, len(layers), scaling))
+
+
+def gift_refresh_workspace_bytes(d_in, n_tokens, x_dtype=DTYPE_BF16, sketch_width=MAX_SKETCH):
+    return int(load().gift_refresh_workspace_bytes(d_in, n_tokens, x_dtype, sketch_width))
+
+
+def gift_whiten_quantize(layers, scaling=SCALE_TENSOR, flags=None, ws=None, stream=None):
+    lib = load()
+    arr = _layers_array(layers)
+    need = lib.gift_group_workspace_bytes(OP_WHITEN_QUANTIZE, arr, len(layers), scaling)
+    ws = _workspace(need, _device_of(layers), ws)
+    _check(lib.gift_whiten_quantize(arr, len(layers), scaling, _ptr(flags), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gift_dequant_unwhiten(layers, scaling=SCALE_TENSOR, ws=None, stream=None):
+    lib = load()
+    arr = _layers_array(layers)
+    need = lib.gift_group_workspace_bytes(OP_DEQUANT_UNWHITEN, arr, len(layers), scaling)
+    ws = _workspace(need, _device_of(layers), ws)
+    _check(lib.gift_dequant_unwhiten(arr, len(layers), scaling, _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+
+
+def gift_euclid_fp8_roundtrip(layers, scaling=SCALE_TENSOR, flags=None, ws=None, stream=None):
+    lib = load()
+    arr = _layers_array(layers)
+    need = lib.gift_group_workspace_bytes(OP_EUCLID_ROUNDTRIP, arr, len(layers), scaling)
+    ws = _workspace(need, _device_of(layers), ws)
+    _check(lib.gift_euclid_fp8_roundtrip(arr, len(layers), scaling, _ptr(flags), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gift_roundtrip_error(layers, out=None, ws=None, stream=None):
+    """-> device fp64 tensor (n_layers, 2): sum (G^-G)^2, sum G^2."""
+    lib = load()
+    arr = _layers_array(layers)
+    dev = _device_of(layers)
+    if out is None:
+        out = torch.empty(len(layers), 2, dtype=torch.float64, device=dev)
+    _dev(out, torch.float64, (len(layers), 2), "out")
+    need = lib.gift_group_workspace_bytes(OP_ROUNDTRIP_ERROR, arr, len(layers), SCALE_TENSOR)
+    ws = _workspace(need, dev, ws)
+    _check(lib.gift_roundtrip_error(arr, len(layers), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+    return out
+
+
+def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,
+                        sketch_width=MAX_SKETCH, power_steps=4, seed=0, sketch=None,
+                        A_out=None, ws=None, stream=None):
+    lib = load()
+    if X.dtype == torch.bfloat16:
+        xdt = DTYPE_BF16
+    elif X.dtype == torch.float32:
+        xdt = DTYPE_F32
+    else:
+        raise ValueError("X must be bf16 or fp32")
+    n_tokens, d_in = X.shape
+    if d_in != factor.d_in:
+        raise ValueError("X width %d != factor d_in %d" % (d_in, factor.d_in))
+    _dev(X, X.dtype, None, "X")
+    _dev(sketch, torch.float32, (d_in, sketch_width), "sketch")
+    _dev(A_out, torch.float32, (d_in, d_in), "A_out")
+    need = lib.gift_refresh_workspace_bytes(d_in, n_tokens, xdt, sketch_width)
+    ws = _workspace(need, X.device, ws)
+    _check(lib.gift_refresh_factor(_ptr(X), xdt, n_tokens, ctypes.byref(factor._struct),
+                                   float(damp_eps), damping_mode, sketch_width, power_steps,
+                                   ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(sketch),
+                                   _ptr(A_out), _ptr(ws), ws.numel() * ws.element_size() * ws.element_size(), _stream(stream)))

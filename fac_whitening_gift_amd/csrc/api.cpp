@@ -1,0 +1,336 @@
+// Host side of the C ABI declared in include/gift.h: argument validation,
+// workspace carving and grouping of layers into launches.  Every call only
+// enqueues kernels on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "device.hpp"
+
+namespace gift {
+hipError_t launch_whiten_quantize(const GroupDev& g, bool block, bool write_w, hipStream_t s);
+hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool write_w,
+                                hipStream_t s);
+hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s);
+hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
+int row_tiles(int64_t d_out);
+int flat_tiles(int64_t n);
+
+// refresh.hip
+size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype, int width);
+gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const gift_factor* f,
+                           float damp_eps, int damping_mode, int width, int power_steps,
+                           uint64_t seed, const float* sketch, float* A_out, void* ws,
+                           size_t ws_bytes, hipStream_t s, std::string* err);
+}  // namespace gift
+
+using namespace gift;
+
+namespace {
+
+thread_local std::string t_err;
+
+gift_status fail(gift_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_err = buf;
+  return s;
+}
+
+gift_status hip_fail(hipError_t e, const char* where) {
+  return fail(GIFT_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 36;
+
+enum class Op { Whiten, Dequant, Euclid, Error };
+
+bool whitened(const gift_layer& L, Op op) {
+  return L.factor != nullptr && (op == Op::Whiten || op == Op::Dequant);
+}
+
+// Per-layer workspace needs of one grouped op.
+struct LayerWs {
+  size_t cbuf = 0, part = 0, part2 = 0;
+  size_t total() const { return align_up(cbuf) + align_up(part) + align_up(part2); }
+};
+
+LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
+  LayerWs w;
+  const int64_t n = L.d_out * L.d_in;
+  switch (op) {
+    case Op::Whiten:
+      if (!block) {
+        if (L.factor) {
+          w.cbuf = (size_t)L.d_out * kRank * sizeof(float);
+          w.part = (size_t)row_tiles(L.d_out) * sizeof(uint32_t);
+        } else {
+          w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
+        }
+      }
+      break;
+    case Op::Euclid:
+      if (!block) w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
+      break;
+    case Op::Dequant:
+      break;
+    case Op::Error:
+      w.part2 = (size_t)flat_tiles(n) * 2 * sizeof(double);
+      break;
+  }
+  return w;
+}
+
+size_t group_ws(const gift_layer* layers, int n, Op op, bool block) {
+  size_t t = 0;
+  for (int i = 0; i < n; ++i) t += layer_ws(layers[i], op, block).total();
+  return t;
+}
+
+gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
+  if (n < 0) return fail(GIFT_ERR_INVALID_ARG, "n_layers < 0");
+  if (n > 0 && !layers) return fail(GIFT_ERR_INVALID_ARG, "layers is NULL");
+  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128)
+    return fail(GIFT_ERR_INVALID_ARG, "unknown scaling %d", scaling);
+  for (int i = 0; i < n; ++i) {
+    const gift_layer& L = layers[i];
+    if (L.d_out < 1 || L.d_in < 1 || L.d_out > kMaxDim || L.d_in > kMaxDim ||
+        L.d_out * L.d_in > kMaxElems)
+      return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: d_out=%lld d_in=%lld out of range", i,
+                  (long long)L.d_out, (long long)L.d_in);
+    if (L.d_in % 4)
+      return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: d_in %% 4 != 0", i);
+    if (scaling == GIFT_SCALE_BLOCK128 && L.d_in % kBlock)
+      return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: block scaling needs d_in %% 128 == 0", i);
+    const bool need_g = op != Op::Dequant;
+    const bool need_q = op != Op::Error;
+    const bool need_ghat = op != Op::Whiten;
+    if ((need_g && !L.G) || (need_q && (!L.q || !L.inv_scale)) || (need_ghat && !L.G_hat))
+      return fail(GIFT_ERR_INVALID_ARG, "layer %d: a required tensor pointer is NULL", i);
+    if (!aligned16(L.G) || !aligned16(L.q) || !aligned16(L.inv_scale) || !aligned16(L.G_hat) ||
+        !aligned16(L.W_out))
+      return fail(GIFT_ERR_INVALID_ARG, "layer %d: device pointers must be 16-byte aligned", i);
+    if (whitened(L, op)) {
+      const gift_factor& f = *L.factor;
+      if (f.rank != kRank)
+        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor rank %d != %d", i, f.rank, kRank);
+      if (f.d_in != L.d_in)
+        return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor d_in %d != layer d_in %lld", i,
+                    f.d_in, (long long)L.d_in);
+      if (L.d_in < 64 || L.d_in % 16)
+        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: whitening needs d_in >= 64, %% 16 == 0",
+                    i);
+      if (!f.U || !f.coef || !aligned16(f.U) || !aligned16(f.coef))
+        return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor U/coef NULL or misaligned", i);
+    }
+  }
+  return GIFT_OK;
+}
+
+// Walk the layers selected by `pick` in chunks of kMaxGroup, filling the
+// descriptors (workspace slices in layer order) and calling `launch`.
+template <class Pick, class Launch>
+gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void* ws,
+                        uint32_t* flags, double* out, Pick pick, int (*tiles)(const gift_layer&),
+                        Launch launch) {
+  // workspace offsets in layer order (independent of the chunking)
+  std::vector<size_t> off(n + 1, 0);
+  for (int i = 0; i < n; ++i) off[i + 1] = off[i] + layer_ws(layers[i], op, block).total();
+  GroupDev g{};
+  g.flags = flags;
+  g.out = out;
+  int first = -1;
+  auto flush = [&]() -> gift_status {
+    if (g.n == 0) return GIFT_OK;
+    hipError_t e = launch(g, first);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    g.n = 0;
+    g.total_tiles = 0;
+    first = -1;
+    return GIFT_OK;
+  };
+  for (int i = 0; i < n; ++i) {
+    const gift_layer& L = layers[i];
+    if (!pick(L)) continue;
+    if (first < 0) first = i;
+    LayerWs lw = layer_ws(L, op, block);
+    char* base = (char*)ws + off[i];
+    LayerDev& d = g.L[g.n];
+    d = LayerDev{};
+    d.G = L.G;
+    d.q = L.q;
+    d.inv = L.inv_scale;
+    d.Ghat = L.G_hat;
+    d.Wout = L.W_out;
+    if (whitened(L, op)) {
+      d.U = L.factor->U;
+      d.coef = L.factor->coef;
+    }
+    d.cbuf = lw.cbuf ? (float*)base : nullptr;
+    base += align_up(lw.cbuf);
+    d.part = lw.part ? (uint32_t*)base : nullptr;
+    base += align_up(lw.part);
+    d.part2 = lw.part2 ? (double*)base : nullptr;
+    d.d_out = L.d_out;
+    d.d_in = L.d_in;
+    d.n_tiles = tiles(L);
+    d.tile_begin = g.total_tiles;
+    g.total_tiles += d.n_tiles;
+    ++g.n;
+    if (g.n == kMaxGroup) {
+      gift_status s = flush();
+      if (s != GIFT_OK) return s;
+    }
+  }
+  return flush();
+}
+
+int tiles_rows(const gift_layer& L) { return row_tiles(L.d_out); }
+int tiles_flat(const gift_layer& L) { return flat_tiles(L.d_out * L.d_in); }
+
+gift_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(GIFT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (need && !ws) return fail(GIFT_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws && ((uintptr_t)ws % kAlign))
+    return fail(GIFT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return GIFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gift_abi_version(void) { return GIFT_ABI_VERSION; }
+
+const char* gift_last_error(void) { return t_err.c_str(); }
+
+const char* gift_status_string(int s) {
+  switch (s) {
+    case GIFT_OK: return "GIFT_OK";
+    case GIFT_ERR_INVALID_ARG: return "GIFT_ERR_INVALID_ARG";
+    case GIFT_ERR_UNSUPPORTED_SHAPE: return "GIFT_ERR_UNSUPPORTED_SHAPE";
+    case GIFT_ERR_WORKSPACE_TOO_SMALL: return "GIFT_ERR_WORKSPACE_TOO_SMALL";
+    case GIFT_ERR_HIP: return "GIFT_ERR_HIP";
+    default: return "GIFT_ERR_UNKNOWN";
+  }
+}
+
+size_t gift_group_workspace_bytes(int op, const gift_layer* layers, int n_layers, int scaling) {
+  if (n_layers <= 0 || !layers) return 0;
+  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  switch (op) {
+    case GIFT_OP_WHITEN_QUANTIZE: return group_ws(layers, n_layers, Op::Whiten, block);
+    case GIFT_OP_DEQUANT_UNWHITEN: return group_ws(layers, n_layers, Op::Dequant, block);
+    case GIFT_OP_EUCLID_ROUNDTRIP: return group_ws(layers, n_layers, Op::Euclid, block);
+    case GIFT_OP_ROUNDTRIP_ERROR: return group_ws(layers, n_layers, Op::Error, false);
+    default: return 0;
+  }
+}
+
+gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int scaling,
+                                 uint32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::Whiten, scaling);
+  if (s != GIFT_OK) return s;
+  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Whiten, block));
+  if (s != GIFT_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  for (int wgrp = 0; wgrp < 2; ++wgrp) {
+    const bool white = wgrp == 0;
+    bool any_w = false;
+    for (int i = 0; i < n_layers; ++i)
+      if ((layers[i].factor != nullptr) == white && layers[i].W_out) any_w = true;
+    auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
+    if (white)
+      s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
+                      tiles_rows, [&](const GroupDev& g, int) {
+                        return launch_whiten_quantize(g, block, any_w, st);
+                      });
+    else
+      s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
+                      tiles_flat, [&](const GroupDev& g, int) {
+                        return launch_flat_quantize(g, block, false, any_w, st);
+                      });
+    if (s != GIFT_OK) return s;
+  }
+  return GIFT_OK;
+}
+
+gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int scaling, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::Dequant, scaling);
+  if (s != GIFT_OK) return s;
+  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Dequant, block));
+  if (s != GIFT_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  for (int wgrp = 0; wgrp < 2; ++wgrp) {
+    const bool white = wgrp == 0;
+    auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
+    s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles_rows,
+                    [&](const GroupDev& g, int) { return launch_dequant(g, block, white, st); });
+    if (s != GIFT_OK) return s;
+  }
+  return GIFT_OK;
+}
+
+gift_status gift_euclid_fp8_roundtrip(const gift_layer* layers, int n_layers, int scaling,
+                                      uint32_t* dev_flags, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::Euclid, scaling);
+  if (s != GIFT_OK) return s;
+  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Euclid, block));
+  if (s != GIFT_OK) return s;
+  bool any_w = false;
+  for (int i = 0; i < n_layers; ++i) any_w |= layers[i].W_out != nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  return run_grouped(layers, n_layers, Op::Euclid, block, ws, dev_flags, nullptr,
+                     [](const gift_layer&) { return true; }, tiles_flat,
+                     [&](const GroupDev& g, int) {
+                       return launch_flat_quantize(g, block, true, any_w, st);
+                     });
+}
+
+gift_status gift_roundtrip_error(const gift_layer* layers, int n_layers, double* dev_out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::Error, GIFT_SCALE_TENSOR);
+  if (s != GIFT_OK) return s;
+  if (n_layers > 0 && (!dev_out || ((uintptr_t)dev_out & 7u)))
+    return fail(GIFT_ERR_INVALID_ARG, "dev_out NULL or not 8-byte aligned");
+  s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Error, false));
+  if (s != GIFT_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  return run_grouped(layers, n_layers, Op::Error, false, ws, nullptr, dev_out,
+                     [](const gift_layer&) { return true; }, tiles_flat,
+                     [&](const GroupDev& g, int first) { return launch_error(g, first, st); });
+}
+
+size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype,
+                                    int sketch_width) {
+  return refresh_workspace_bytes(d_in, n_tokens, x_dtype, sketch_width);
+}
+
+gift_status gift_refresh_factor(const void* X, int x_dtype, int64_t n_tokens,
+                                const gift_factor* f, float damp_eps, int damping_mode,
+                                int sketch_width, int power_steps, uint64_t seed,
+                                const float* sketch, float* A_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return refresh_factor(X, x_dtype, n_tokens, f, damp_eps, damping_mode, sketch_width,
+                        power_steps, seed, sketch, A_out, ws, ws_bytes, (hipStream_t)stream,
+                        &t_err);
+}
+
+}  // extern "C"

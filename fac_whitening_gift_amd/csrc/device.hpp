@@ -1,0 +1,158 @@
+// Device-side helpers shared by the gfx950 kernels: the OCP E4M3 codec,
+// wave/workgroup reductions and the grouped-launch descriptors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gift.h"
+
+namespace gift {
+
+constexpr int kRank = GIFT_RANK;
+constexpr int kBlock = GIFT_BLOCK;
+constexpr int kMaxGroup = 16;          // layers per grouped launch
+constexpr float kE4M3Max = 448.0f;     // largest finite OCP E4M3 magnitude
+
+// ---------------------------------------------------------------------------
+// E4M3 codec.  The hardware conversion rounds to nearest even on the OCP E4M3
+// grid; the explicit median-of-three clamp makes every finite input (and
+// +-inf) saturate to +-448 instead of overflowing, and NaN inputs are mapped
+// to 0x7F explicitly so the code does not depend on the NaN the converter
+// emits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_nan_fix(uint32_t packed, float a, float b,
+                                                 float c, float d) {
+  uint32_t m = (a != a ? 0x000000ffu : 0u) | (b != b ? 0x0000ff00u : 0u) |
+               (c != c ? 0x00ff0000u : 0u) | (d != d ? 0xff000000u : 0u);
+  return (packed & ~m) | (0x7f7f7f7fu & m);
+}
+
+// Encode four already-scaled fp32 values; byte i of the result = element i.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+  float ca = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  float cb = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  float cc = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+  float cd = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, w, true);
+  return e4m3_nan_fix((uint32_t)w, a, b, c, d);
+}
+
+__device__ __forceinline__ uint8_t e4m3_encode1(float a) {
+  return (uint8_t)(e4m3_encode4(a, 0.f, 0.f, 0.f) & 0xffu);
+}
+
+// Decode byte `sel` (0..3) of a packed word.
+__device__ __forceinline__ float e4m3_decode(uint32_t packed, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 3);
+  }
+}
+
+// |x| as an unsigned bit pattern: ordering these is ordering |x|, with NaN
+// above +inf above every finite value.
+__device__ __forceinline__ uint32_t abs_bits(float x) {
+  return __float_as_uint(x) & 0x7fffffffu;
+}
+
+// scale / inv / flags from an amax given as |x| bits (IEEE division).
+struct Scale {
+  float scale, inv;
+  uint32_t flags;
+};
+__device__ __forceinline__ Scale scale_from_amax_bits(uint32_t bits) {
+  Scale s;
+  float a = __uint_as_float(bits);
+  s.flags = bits >= 0x7f800000u ? GIFT_FLAG_NONFINITE : 0u;
+  if (bits == 0u) {
+    s.scale = 1.0f;
+    s.inv = 1.0f;
+    s.flags |= GIFT_FLAG_ZERO_AMAX;
+  } else {
+    s.scale = kE4M3Max / a;
+    s.inv = a / kE4M3Max;
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// reductions (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, 64);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {  // within 32 lanes
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, 64);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Workgroup max of one value per thread; every thread gets the result.
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds /*kThreads/64*/) {
+  constexpr int kWaves = kThreads / 64;
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = v;
+  __syncthreads();
+  uint32_t r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = r > lds[i] ? r : lds[i];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// grouped-launch descriptors (passed by value as kernel arguments)
+// ---------------------------------------------------------------------------
+struct LayerDev {
+  const float* G;
+  uint8_t* q;
+  float* inv;
+  float* Ghat;
+  float* Wout;
+  const float* U;       // d_in x 32 (NULL: Euclidean layer)
+  const float* coef;    // GIFT_COEF_COUNT
+  float* cbuf;          // workspace: d_out x 32 row coefficients
+  uint32_t* part;       // workspace: one partial amax per tile
+  double* part2;        // workspace: two fp64 partial sums per tile
+  int64_t d_out, d_in;
+  int tile_begin, n_tiles;
+};
+
+struct GroupDev {
+  int n;
+  int total_tiles;
+  uint32_t* flags;      // may be NULL
+  double* out;          // roundtrip_error output, may be NULL
+  LayerDev L[kMaxGroup];
+};
+
+__device__ __forceinline__ int find_layer(const GroupDev& g, int tile) {
+  int l = 0;
+#pragma unroll 1
+  for (int i = 1; i < g.n; ++i)
+    if (tile >= g.L[i].tile_begin) l = i;
+  return l;
+}
+
+}  // namespace gift

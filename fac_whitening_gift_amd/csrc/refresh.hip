@@ -1,0 +1,744 @@
+// Factor refresh on gfx950: A = X^T X / N, a top-32 eigensolve by randomized
+// subspace iteration, and the whitening coefficients.
+//
+// The pages only name the refresh (GIFT review: the input-side factor
+// A = E[a a^T] is refreshed every 50 steps, "Load-bearing premise"; referee
+// report major comment 2 on Algorithm 1) and the rank (32, free-parameter
+// ledger).  Steps, in launch order:
+//   1. k_syrk: upper-triangle 128x128 tiles of X^T X on MFMA (bf16 inputs on
+//      v_mfma_f32_16x16x32_bf16, fp32 inputs on v_mfma_f32_16x16x4_f32),
+//      split over token ranges; fp32 partial tiles in the workspace.
+//   2. k_syrk_reduce: fixed-order sum of the partials, / N, mirrored -> A.
+//   3. k_trace: tr(A) in fp64, fixed order.
+//   4. k_sketch: Omega from Philox4x32-10 + Box-Muller (unless given).
+//   5. subspace iteration: Y = A Q on fp32 MFMA (k_gemm_aq), Q = orth(Y) by
+//      CholeskyQR2 (Fukaya et al.) with an fp64 Gram matrix (k_gram,
+//      k_chol, k_apply); power_steps repetitions.
+//   6. Rayleigh-Ritz: B = Q^T A Q (k_gemm_aq + k_gram), cyclic Jacobi on B in
+//      one workgroup (Golub & Van Loan, sym.schur2 rotations, round-robin
+//      ordering so 32 disjoint rotations run at once), sort, coefficients;
+//      U = Q V[:, :32] (k_apply).
+#include <math.h>
+
+#include <string>
+
+#include "device.hpp"
+
+namespace gift {
+
+namespace {
+
+constexpr int kT = 256;            // threads per workgroup
+constexpr int kSyrkTile = 128;
+constexpr int kKStep = 32;         // tokens per SYRK step
+constexpr int kW = GIFT_MAX_SKETCH;  // largest subspace width
+constexpr int kGramRows = 64;      // rows of Q per Gram workgroup
+constexpr double kDropTol = 1e-12;  // CholeskyQR pivot drop threshold (relative)
+constexpr int kMaxSweeps = 30;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+size_t al(size_t x) { return (x + 255) / 256 * 256; }
+
+struct SyrkPlan {
+  int nb, npairs, nsplit;
+  int64_t chunk;
+};
+
+SyrkPlan syrk_plan(int64_t d, int64_t n) {
+  SyrkPlan p;
+  p.nb = (int)((d + kSyrkTile - 1) / kSyrkTile);
+  p.npairs = p.nb * (p.nb + 1) / 2;
+  int64_t steps = (n + kKStep - 1) / kKStep;
+  int64_t want = (512 + p.npairs - 1) / p.npairs;           // about 2 workgroups per CU
+  int64_t maxs = steps / 8 > 0 ? steps / 8 : 1;            // at least 8 K-steps each
+  int64_t s = want < maxs ? want : maxs;
+  if (s < 1) s = 1;
+  p.chunk = ((steps + s - 1) / s) * kKStep;
+  p.nsplit = (int)((n + p.chunk - 1) / p.chunk);
+  return p;
+}
+
+struct WsLayout {
+  size_t A, part, om, y, q, q1, gram, T, tr, total;
+};
+
+WsLayout ws_layout(int64_t d, int64_t n, int w) {
+  SyrkPlan p = syrk_plan(d, n);
+  WsLayout L;
+  size_t o = 0;
+  L.A = o; o += al((size_t)d * d * 4);
+  L.part = o; o += al((size_t)p.nsplit * p.npairs * kSyrkTile * kSyrkTile * 4);
+  L.om = o; o += al((size_t)d * w * 4);
+  L.y = o; o += al((size_t)d * w * 4);
+  L.q = o; o += al((size_t)d * w * 4);
+  L.q1 = o; o += al((size_t)d * w * 4);
+  L.gram = o; o += al((size_t)((d + kGramRows - 1) / kGramRows) * kW * kW * 8);
+  L.T = o; o += al((size_t)kW * kW * 8);
+  L.tr = o; o += al(64);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// 1. SYRK partial tiles
+// ---------------------------------------------------------------------------
+template <bool kBf16>
+struct SyrkLds;
+template <>
+struct SyrkLds<true> {
+  static constexpr int kPad = 8;  // elements; row = 40 bf16 = 80 B
+  uint16_t a[kSyrkTile][kKStep + kPad];
+  uint16_t b[kSyrkTile][kKStep + kPad];
+};
+template <>
+struct SyrkLds<false> {
+  static constexpr int kPad = 4;  // row = 36 floats = 144 B
+  float a[kSyrkTile][kKStep + kPad];
+  float b[kSyrkTile][kKStep + kPad];
+};
+
+__device__ __forceinline__ void decode_pair(int pair, int nb, int& bi, int& bj) {
+  int i = 0, rem = pair;
+  while (rem >= nb - i) {
+    rem -= nb - i;
+    ++i;
+  }
+  bi = i;
+  bj = i + rem;
+}
+
+// bf16: thread t loads columns c0+2(t%64), +1 for tokens n0+8(t/64)..+7 and
+// stores each column's 8 tokens as one 16-byte LDS row segment.
+__device__ __forceinline__ void syrk_load_tile(uint16_t (*lds)[kKStep + 8], const uint16_t* X,
+                                               int64_t n0, int64_t n_end, int c0, int d) {
+  const int cp = threadIdx.x & 63, tg = threadIdx.x >> 6;
+  const int col = c0 + 2 * cp;
+  uint32_t v[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int64_t n = n0 + 8 * tg + s;
+    v[s] = (n < n_end && col < d) ? *reinterpret_cast<const uint32_t*>(X + n * d + col) : 0u;
+  }
+  uint4 lo, hi;
+  lo.x = (v[0] & 0xffffu) | (v[1] << 16);
+  lo.y = (v[2] & 0xffffu) | (v[3] << 16);
+  lo.z = (v[4] & 0xffffu) | (v[5] << 16);
+  lo.w = (v[6] & 0xffffu) | (v[7] << 16);
+  hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
+  hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
+  hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
+  hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
+  *reinterpret_cast<uint4*>(&lds[2 * cp][8 * tg]) = lo;
+  *reinterpret_cast<uint4*>(&lds[2 * cp + 1][8 * tg]) = hi;
+}
+
+// fp32: thread t loads column c0+(t%128) for tokens n0+16(t/128)..+15.
+__device__ __forceinline__ void syrk_load_tile(float (*lds)[kKStep + 4], const float* X,
+                                               int64_t n0, int64_t n_end, int c0, int d) {
+  const int c = threadIdx.x & 127, tg = threadIdx.x >> 7;
+  const int col = c0 + c;
+  float v[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int64_t n = n0 + 16 * tg + s;
+    v[s] = (n < n_end && col < d) ? X[n * d + col] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<float4*>(&lds[c][16 * tg + 4 * q]) =
+        make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kT) void k_syrk(const void* Xv, int64_t N, int d, int nb,
+                                             int64_t chunk, float* part, int npairs) {
+  __shared__ SyrkLds<kBf16> sm;
+  int bi, bj;
+  decode_pair(blockIdx.x, nb, bi, bj);
+  const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
+  const bool diag = bi == bj;
+  const int64_t n_begin = (int64_t)blockIdx.y * chunk;
+  const int64_t n_end = min(N, n_begin + chunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int r16 = lane & 15, g = lane >> 4;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t n0 = n_begin; n0 < n_end; n0 += kKStep) {
+    __syncthreads();
+    if constexpr (kBf16) {
+      const uint16_t* X = static_cast<const uint16_t*>(Xv);
+      syrk_load_tile(sm.a, X, n0, n_end, ci0, d);
+      if (!diag) syrk_load_tile(sm.b, X, n0, n_end, cj0, d);
+    } else {
+      const float* X = static_cast<const float*>(Xv);
+      syrk_load_tile(sm.a, X, n0, n_end, ci0, d);
+      if (!diag) syrk_load_tile(sm.b, X, n0, n_end, cj0, d);
+    }
+    __syncthreads();
+    auto& tb = diag ? sm.a : sm.b;
+    if constexpr (kBf16) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fa[t] = *reinterpret_cast<const bf16x8*>(&sm.a[64 * wi + 16 * t + r16][8 * g]);
+        fb[t] = *reinterpret_cast<const bf16x8*>(&tb[64 * wj + 16 * t + r16][8 * g]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    } else {
+      // 8 MFMAs of K=4; lane group g's k-slot in MFMA s is token 8g+s
+      float fa[4][8], fb[4][8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&sm.a[64 * wi + 16 * t + r16][8 * g]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&sm.a[64 * wi + 16 * t + r16][8 * g + 4]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&tb[64 * wj + 16 * t + r16][8 * g]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&tb[64 * wj + 16 * t + r16][8 * g + 4]);
+        fa[t][0] = a0.x; fa[t][1] = a0.y; fa[t][2] = a0.z; fa[t][3] = a0.w;
+        fa[t][4] = a1.x; fa[t][5] = a1.y; fa[t][6] = a1.z; fa[t][7] = a1.w;
+        fb[t][0] = b0.x; fb[t][1] = b0.y; fb[t][2] = b0.z; fb[t][3] = b0.w;
+        fb[t][4] = b1.x; fb[t][5] = b1.y; fb[t][6] = b1.z; fb[t][7] = b1.w;
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
+    }
+  }
+  // D layout: lane holds rows 4g..4g+3 of column r16 of each 16x16 tile
+  float* out = part + ((size_t)blockIdx.y * npairs + blockIdx.x) * kSyrkTile * kSyrkTile;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wi + 16 * a + 4 * g + i, c = 64 * wj + 16 * b + r16;
+        out[r * kSyrkTile + c] = acc[a][b][i];
+      }
+}
+
+// 2. A[i][j] = A[j][i] = (sum_s part[s]) / N  over the upper triangle
+__global__ __launch_bounds__(kT) void k_syrk_reduce(const float* part, int nsplit, int npairs,
+                                                    int nb, int d, float inv_n_unused,
+                                                    int64_t N, float* A) {
+  int bi, bj;
+  decode_pair(blockIdx.x, nb, bi, bj);
+  const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
+  const float fn = (float)N;
+  for (int e = threadIdx.x; e < kSyrkTile * kSyrkTile; e += kT) {
+    const int r = e / kSyrkTile, c = e % kSyrkTile;
+    const int i = ci0 + r, j = cj0 + c;
+    if (i >= d || j >= d || (bi == bj && r > c)) continue;
+    float s = 0.f;
+    for (int k = 0; k < nsplit; ++k)
+      s += part[((size_t)k * npairs + blockIdx.x) * kSyrkTile * kSyrkTile + e];
+    const float a = s / fn;
+    A[(int64_t)i * d + j] = a;
+    A[(int64_t)j * d + i] = a;
+  }
+}
+
+// 3. trace
+__global__ __launch_bounds__(kT) void k_trace(const float* A, int d, double* tr) {
+  __shared__ double sh[kT / 64];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < d; i += kT) s += (double)A[(int64_t)i * d + i];
+  s = wave_sum_f64(s);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kT / 64; ++w) t += sh[w];
+    *tr = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Philox4x32-10 + Box-Muller sketch (Salmon et al., SC'11)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint32_t hi0 = __umulhi(M0, c[0]), lo0 = M0 * c[0];
+    const uint32_t hi1 = __umulhi(M1, c[2]), lo1 = M1 * c[2];
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+  }
+}
+
+__global__ __launch_bounds__(kT) void k_sketch(float* om, int64_t total, uint64_t seed) {
+  const int64_t c = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (4 * c >= total) return;
+  uint32_t w[4] = {(uint32_t)c, (uint32_t)(c >> 32), 0u, 0u};
+  philox10(w, (uint32_t)seed, (uint32_t)(seed >> 32));
+  double z[4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const double u1 = ((double)w[2 * p] + 1.0) * 0x1p-32;
+    const double u2 = (double)w[2 * p + 1] * 0x1p-32;
+    const double r = sqrt(-2.0 * log(u1));
+    double sn, cs;
+    sincos(2.0 * M_PI * u2, &sn, &cs);
+    z[2 * p] = r * cs;
+    z[2 * p + 1] = r * sn;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (4 * c + e < total) om[4 * c + e] = (float)z[e];
+}
+
+// ---------------------------------------------------------------------------
+// 5a. Y = A Q  (A d x d fp32 symmetric, Q d x w) on v_mfma_f32_16x16x4_f32.
+// Workgroup: 16 rows of Y; each wave a quarter of K; fixed-order wave sum.
+// Lane group g's k-slot in MFMA s of a 16-wide K chunk is k0 + 4g + s.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_gemm_aq(const float* __restrict__ A,
+                                                const float* __restrict__ Q, int d, int w,
+                                                float* __restrict__ Y) {
+  __shared__ float red[kT / 64][16][kW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int ntile = w / 16;
+  const int kq = d / 4;  // d % 64 == 0 is not required: d % 16 == 0 and kq % 16 handled below
+  f32x4 acc[kW / 16];
+#pragma unroll
+  for (int t = 0; t < kW / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // wave's K range: 16-aligned quarters
+  const int kchunks = d / 16;
+  const int kc_begin = wave * kchunks / 4, kc_end = (wave + 1) * kchunks / 4;
+  (void)kq;
+  const float* arow = A + (int64_t)(row0 + r16) * d;
+  for (int kc = kc_begin; kc < kc_end; ++kc) {
+    const int k0 = 16 * kc + 4 * g;
+    const float4 a = *reinterpret_cast<const float4*>(arow + k0);
+    const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float* qrow = Q + (int64_t)(k0 + s) * w;
+#pragma unroll
+      for (int t = 0; t < kW / 16; ++t)
+        if (t < ntile)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], qrow[16 * t + r16], acc[t], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kW / 16; ++t)
+    if (t < ntile)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][4 * g + i][16 * t + r16] = acc[t][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * w; e += kT) {
+    const int r = e / w, c = e % w;
+    float s = red[0][r][c];
+#pragma unroll
+    for (int v = 1; v < kT / 64; ++v) s += red[v][r][c];
+    Y[(int64_t)(row0 + r) * w + c] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5b. Gram partials: part[chunk][a][b] = sum_{i in chunk} P[i][a] R[i][b] (fp64)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_gram(const float* __restrict__ P,
+                                             const float* __restrict__ R, int d, int w,
+                                             double* __restrict__ part) {
+  __shared__ float sp[kGramRows][kW + 1];
+  __shared__ float sr[kGramRows][kW + 1];
+  const int i0 = blockIdx.x * kGramRows;
+  const int rows = min(kGramRows, d - i0);
+  for (int e = threadIdx.x; e < kGramRows * w; e += kT) {
+    const int r = e / w, c = e % w;
+    sp[r][c] = r < rows ? P[(int64_t)(i0 + r) * w + c] : 0.f;
+    sr[r][c] = r < rows ? R[(int64_t)(i0 + r) * w + c] : 0.f;
+  }
+  __syncthreads();
+  // thread -> output (a, b0..b0+15)
+  const int a = threadIdx.x >> 2, b0 = (threadIdx.x & 3) * 16;
+  if (a >= w) return;
+  double s[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s[k] = 0.0;
+  for (int r = 0; r < rows; ++r) {
+    const double pa = sp[r][a];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s[k] += pa * (double)sr[r][b0 + k];
+  }
+  double* out = part + (size_t)blockIdx.x * kW * kW;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (b0 + k < w) out[a * kW + b0 + k] = s[k];
+}
+
+// fixed-order reduction of the Gram partials into LDS (w x w, fp64)
+__device__ void gram_reduce(const double* part, int nchunks, int w, double (*G)[kW + 1]) {
+  for (int e = threadIdx.x; e < w * w; e += kT) {
+    const int a = e / w, b = e % w;
+    double s = 0.0;
+    for (int c = 0; c < nchunks; ++c) s += part[(size_t)c * kW * kW + a * kW + b];
+    G[a][b] = s;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// 5c. Cholesky of the Gram matrix (one workgroup, fp64) and T = R^-1.
+// Pivots below kDropTol * max diagonal mark a column as dependent: its row of
+// R and column of T are zero, so that column of the orthonormalised Q is 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_chol(const double* part, int nchunks, int w,
+                                             double* Tout) {
+  __shared__ double G[kW][kW + 1];
+  __shared__ double R[kW][kW + 1];
+  __shared__ int keep[kW];
+  __shared__ double maxdiag;
+  gram_reduce(part, nchunks, w, G);
+  if (threadIdx.x == 0) {
+    double m = 0.0;
+    for (int i = 0; i < w; ++i) m = fmax(m, G[i][i]);
+    maxdiag = m;
+  }
+  for (int e = threadIdx.x; e < kW * (kW + 1); e += kT) R[e / (kW + 1)][e % (kW + 1)] = 0.0;
+  __syncthreads();
+  // right-looking Cholesky, G = R^T R (R upper triangular)
+  for (int k = 0; k < w; ++k) {
+    const double piv = G[k][k];
+    const bool ok = maxdiag > 0.0 && piv > kDropTol * maxdiag;
+    const double rkk = ok ? sqrt(piv) : 0.0;
+    if (threadIdx.x == 0) keep[k] = ok;
+    for (int j = k + threadIdx.x; j < w; j += kT) R[k][j] = ok ? (j == k ? rkk : G[k][j] / rkk) : 0.0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < (w - k - 1) * (w - k - 1); e += kT) {
+      const int i = k + 1 + e / (w - k - 1), j = k + 1 + e % (w - k - 1);
+      G[i][j] -= R[k][i] * R[k][j];
+    }
+    __syncthreads();
+  }
+  // T = R^-1 column by column (upper triangular back substitution); dropped
+  // columns of R (zero diagonal) give zero columns and rows of T.
+  for (int c = threadIdx.x; c < w; c += kT) {
+    double* col = Tout + c;  // column c, stride kW
+    for (int i = w - 1; i >= 0; --i) {
+      double v;
+      if (!keep[i] || !keep[c] || i > c) {
+        v = 0.0;
+      } else {
+        double s = (i == c) ? 1.0 : 0.0;
+        for (int j = i + 1; j <= c; ++j) s -= R[i][j] * col[j * kW];
+        v = s / R[i][i];
+      }
+      col[i * kW] = v;
+    }
+  }
+}
+
+// 5d. Out[i][c] = sum_k In[i][k] T[k][c]  (fp64 accumulate), c < ncols
+__global__ __launch_bounds__(kT) void k_apply(const float* __restrict__ In, int d, int w,
+                                              const double* __restrict__ T, int ncols,
+                                              float* __restrict__ Out) {
+  __shared__ double sT[kW][kW];
+  __shared__ float sIn[16][kW];
+  for (int e = threadIdx.x; e < w * ncols; e += kT) sT[e / ncols][e % ncols] = T[(e / ncols) * kW + e % ncols];
+  const int i0 = blockIdx.x * 16;
+  for (int e = threadIdx.x; e < 16 * w; e += kT) sIn[e / w][e % w] = In[(int64_t)(i0 + e / w) * w + e % w];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * ncols; e += kT) {
+    const int r = e / ncols, c = e % ncols;
+    double s = 0.0;
+    for (int k = 0; k < w; ++k) s += (double)sIn[r][k] * sT[k][c];
+    Out[(int64_t)(i0 + r) * ncols + c] = (float)s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 6. Rayleigh-Ritz: Jacobi eigensolver of B = Q^T A Q, sort, coefficients.
+// ---------------------------------------------------------------------------
+struct CoefArgs {
+  float eps;
+  int mode;
+  int d;
+  int w;
+};
+
+__global__ __launch_bounds__(kT) void k_ritz(const double* part, int nchunks, CoefArgs ca,
+                                             const double* trace, double* Tout, float* theta,
+                                             float* coef) {
+  __shared__ double B[kW][kW + 1];
+  __shared__ double V[kW][kW + 1];
+  __shared__ double rc[kW / 2], rs[kW / 2];
+  __shared__ int rp[kW / 2], rq[kW / 2];
+  __shared__ double ev[kW];
+  __shared__ int order[kW];
+  __shared__ double red[kT / 64];
+  __shared__ int done;
+  const int w = ca.w;
+  gram_reduce(part, nchunks, w, B);
+  // symmetrise, V = I
+  for (int e = threadIdx.x; e < w * w; e += kT) {
+    const int a = e / w, b = e % w;
+    V[a][b] = a == b ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < w * w; e += kT) {
+    const int a = e / w, b = e % w;
+    if (a < b) {
+      const double m = 0.5 * (B[a][b] + B[b][a]);
+      B[a][b] = m;
+      B[b][a] = m;
+    }
+  }
+  __syncthreads();
+  const int m = w - 1;  // round-robin over w players (w even)
+  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+    // convergence test: off-diagonal mass vs total
+    double off = 0.0, tot = 0.0;
+    for (int e = threadIdx.x; e < w * w; e += kT) {
+      const int a = e / w, b = e % w;
+      const double v = B[a][b] * B[a][b];
+      tot += v;
+      if (a != b) off += v;
+    }
+    off = wave_sum_f64(off);
+    tot = wave_sum_f64(tot);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = off;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double o = 0.0;
+      for (int i = 0; i < kT / 64; ++i) o += red[i];
+      red[0] = o;
+    }
+    __syncthreads();
+    const double off_all = red[0];
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int i = 0; i < kT / 64; ++i) t += red[i];
+      done = !(off_all > 1e-30 * t);
+    }
+    __syncthreads();
+    if (done) break;
+    for (int round = 0; round < m; ++round) {
+      if (threadIdx.x < w / 2) {
+        const int i = threadIdx.x;
+        int p, q;
+        if (i == 0) {
+          p = m;
+          q = round;
+        } else {
+          p = (round + i) % m;
+          q = (round - i + m) % m;
+        }
+        if (p > q) { const int t = p; p = q; q = t; }
+        const double apq = B[p][q], app = B[p][p], aqq = B[q][q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0) {
+          const double tau = (aqq - app) / (2.0 * apq);
+          const double t = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau))
+                                      : -1.0 / (-tau + sqrt(1.0 + tau * tau));
+          c = 1.0 / sqrt(1.0 + t * t);
+          s = t * c;
+        }
+        rp[i] = p; rq[i] = q; rc[i] = c; rs[i] = s;
+      }
+      __syncthreads();
+      // rows: B <- J^T B
+      for (int e = threadIdx.x; e < (w / 2) * w; e += kT) {
+        const int i = e / w, col = e % w;
+        const int p = rp[i], q = rq[i];
+        const double c = rc[i], s = rs[i];
+        const double bp = B[p][col], bq = B[q][col];
+        B[p][col] = c * bp - s * bq;
+        B[q][col] = s * bp + c * bq;
+      }
+      __syncthreads();
+      // columns: B <- B J, V <- V J
+      for (int e = threadIdx.x; e < (w / 2) * w; e += kT) {
+        const int i = e / w, row = e % w;
+        const int p = rp[i], q = rq[i];
+        const double c = rc[i], s = rs[i];
+        const double bp = B[row][p], bq = B[row][q];
+        B[row][p] = c * bp - s * bq;
+        B[row][q] = s * bp + c * bq;
+        const double vp = V[row][p], vq = V[row][q];
+        V[row][p] = c * vp - s * vq;
+        V[row][q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+  // sort eigenvalues descending (rank by count; ties by index)
+  if (threadIdx.x < w) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x < w) {
+    const int i = threadIdx.x;
+    const double x = ev[i];
+    int rank = 0;
+    for (int j = 0; j < w; ++j) rank += (ev[j] > x) || (ev[j] == x && j < i);
+    order[rank] = i;
+  }
+  __syncthreads();
+  // T[:, k] = V[:, order[k]] for the top rank
+  for (int e = threadIdx.x; e < w * kRank; e += kT) {
+    const int r = e / kRank, k = e % kRank;
+    Tout[r * kW + k] = V[r][order[k]];
+  }
+  if (threadIdx.x == 0) {
+    const double t = *trace;
+    double sum = 0.0, th[kRank];
+    for (int k = 0; k < kRank; ++k) {
+      th[k] = fmax(ev[order[k]], 0.0);
+      sum += th[k];
+    }
+    const double lam_floor = (double)ca.eps * t / ca.d;
+    const double tail = ca.d > kRank ? fmax(0.0, (t - sum) / (ca.d - kRank)) : 0.0;
+    double lam = ca.mode == GIFT_DAMP_FLOOR_PLUS_TAIL ? lam_floor + tail : lam_floor;
+    lam = fmax(lam, 1e-30);
+    const double s0 = sqrt(lam);
+    coef[GIFT_COEF_ALPHA] = (float)(1.0 / s0);
+    coef[GIFT_COEF_BETA] = (float)s0;
+    coef[GIFT_COEF_LAMBDA_ISO] = (float)lam;
+    coef[GIFT_COEF_LAMBDA_FLOOR] = (float)lam_floor;
+    coef[GIFT_COEF_TRACE] = (float)t;
+    coef[GIFT_COEF_SIGMA2_TAIL] = (float)tail;
+    coef[6] = 0.f;
+    coef[7] = 0.f;
+    for (int k = 0; k < kRank; ++k) {
+      const double s = sqrt(th[k] + lam);
+      // (th+lam)^-1/2 - lam^-1/2 and (th+lam)^1/2 - lam^1/2 without cancellation
+      coef[GIFT_COEF_DW + k] = (float)(-th[k] / (s * s0 * (s + s0)));
+      coef[GIFT_COEF_DU + k] = (float)(th[k] / (s + s0));
+      theta[k] = (float)th[k];
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host orchestration
+// ---------------------------------------------------------------------------
+size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int, int width) {
+  if (d_in < 1 || n_tokens < 1 || width < 1) return 0;
+  return ws_layout(d_in, n_tokens, width).total;
+}
+
+#define GIFT_HIP(call)                                                          \
+  do {                                                                          \
+    hipError_t e_ = (call);                                                     \
+    if (e_ != hipSuccess) {                                                     \
+      *err = std::string("refresh: ") + hipGetErrorString(e_);                  \
+      return GIFT_ERR_HIP;                                                      \
+    }                                                                           \
+  } while (0)
+
+gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const gift_factor* f,
+                           float damp_eps, int damping_mode, int width, int power_steps,
+                           uint64_t seed, const float* sketch, float* A_out, void* ws,
+                           size_t ws_bytes, hipStream_t st, std::string* err) {
+  auto bad = [&](gift_status s, const char* msg) {
+    *err = std::string("gift_refresh_factor: ") + msg;
+    return s;
+  };
+  if (!f) return bad(GIFT_ERR_INVALID_ARG, "factor is NULL");
+  if (!X || !f->U || !f->theta || !f->coef) return bad(GIFT_ERR_INVALID_ARG, "NULL pointer");
+  auto mis = [](const void* p) { return ((uintptr_t)p & 15u) != 0; };
+  if (mis(X) || mis(f->U) || mis(f->theta) || mis(f->coef) || mis(sketch) || mis(A_out))
+    return bad(GIFT_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (x_dtype != GIFT_DTYPE_F32 && x_dtype != GIFT_DTYPE_BF16)
+    return bad(GIFT_ERR_INVALID_ARG, "unknown x_dtype");
+  if (damping_mode != GIFT_DAMP_FLOOR && damping_mode != GIFT_DAMP_FLOOR_PLUS_TAIL)
+    return bad(GIFT_ERR_INVALID_ARG, "unknown damping_mode");
+  if (!(damp_eps >= 0.f) || !isfinite(damp_eps)) return bad(GIFT_ERR_INVALID_ARG, "bad damp_eps");
+  if (f->rank != kRank) return bad(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be 32");
+  const int d = f->d_in;
+  if (d < 64 || d % 16 || d > 16384)
+    return bad(GIFT_ERR_UNSUPPORTED_SHAPE, "d_in must be in [64, 16384] and a multiple of 16");
+  if (n_tokens < 1 || n_tokens > (int64_t(1) << 31))
+    return bad(GIFT_ERR_UNSUPPORTED_SHAPE, "n_tokens out of range");
+  if (width < kRank || width > kW || width % 16)
+    return bad(GIFT_ERR_UNSUPPORTED_SHAPE, "sketch_width must be 32, 48 or 64");
+  if (power_steps < 0 || power_steps > 64) return bad(GIFT_ERR_INVALID_ARG, "power_steps out of range");
+  const WsLayout L = ws_layout(d, n_tokens, width);
+  if (ws_bytes < L.total) {
+    *err = "gift_refresh_factor: workspace too small (" + std::to_string(ws_bytes) + " < " +
+           std::to_string(L.total) + ")";
+    return GIFT_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (!ws || ((uintptr_t)ws & 255u)) return bad(GIFT_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+
+  char* base = static_cast<char*>(ws);
+  float* A = A_out ? A_out : reinterpret_cast<float*>(base + L.A);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  float* om = reinterpret_cast<float*>(base + L.om);
+  float* Y = reinterpret_cast<float*>(base + L.y);
+  float* Q = reinterpret_cast<float*>(base + L.q);
+  float* Q1 = reinterpret_cast<float*>(base + L.q1);
+  double* gram = reinterpret_cast<double*>(base + L.gram);
+  double* T = reinterpret_cast<double*>(base + L.T);
+  double* tr = reinterpret_cast<double*>(base + L.tr);
+  const SyrkPlan p = syrk_plan(d, n_tokens);
+  const int w = width;
+  const int gchunks = (d + kGramRows - 1) / kGramRows;
+
+  // 1-3: covariance and trace
+  if (x_dtype == GIFT_DTYPE_BF16)
+    k_syrk<true><<<dim3(p.npairs, p.nsplit), kT, 0, st>>>(X, n_tokens, d, p.nb, p.chunk, part, p.npairs);
+  else
+    k_syrk<false><<<dim3(p.npairs, p.nsplit), kT, 0, st>>>(X, n_tokens, d, p.nb, p.chunk, part, p.npairs);
+  GIFT_HIP(hipGetLastError());
+  k_syrk_reduce<<<p.npairs, kT, 0, st>>>(part, p.nsplit, p.npairs, p.nb, d, 0.f, n_tokens, A);
+  k_trace<<<1, kT, 0, st>>>(A, d, tr);
+  GIFT_HIP(hipGetLastError());
+  // 4: sketch
+  const float* omega = sketch;
+  if (!omega) {
+    const int64_t total = (int64_t)d * w;
+    const int64_t ctr = (total + 3) / 4;
+    k_sketch<<<(unsigned)((ctr + kT - 1) / kT), kT, 0, st>>>(om, total, seed);
+    omega = om;
+  }
+  // 5: subspace iteration; orth = CholeskyQR2 (Y -> Q1 -> Q)
+  auto orth = [&](const float* Yin) -> hipError_t {
+    k_gram<<<gchunks, kT, 0, st>>>(Yin, Yin, d, w, gram);
+    k_chol<<<1, kT, 0, st>>>(gram, gchunks, w, T);
+    k_apply<<<d / 16, kT, 0, st>>>(Yin, d, w, T, w, Q1);
+    k_gram<<<gchunks, kT, 0, st>>>(Q1, Q1, d, w, gram);
+    k_chol<<<1, kT, 0, st>>>(gram, gchunks, w, T);
+    k_apply<<<d / 16, kT, 0, st>>>(Q1, d, w, T, w, Q);
+    return hipGetLastError();
+  };
+  k_gemm_aq<<<d / 16, kT, 0, st>>>(A, omega, d, w, Y);
+  GIFT_HIP(orth(Y));
+  for (int s = 0; s < power_steps; ++s) {
+    k_gemm_aq<<<d / 16, kT, 0, st>>>(A, Q, d, w, Y);
+    GIFT_HIP(orth(Y));
+  }
+  // 6: Rayleigh-Ritz
+  k_gemm_aq<<<d / 16, kT, 0, st>>>(A, Q, d, w, Y);
+  k_gram<<<gchunks, kT, 0, st>>>(Q, Y, d, w, gram);
+  CoefArgs ca{damp_eps, damping_mode, d, w};
+  k_ritz<<<1, kT, 0, st>>>(gram, gchunks, ca, tr, T, f->theta, f->coef);
+  k_apply<<<d / 16, kT, 0, st>>>(Q, d, w, T, kRank, f->U);
+  GIFT_HIP(hipGetLastError());
+  return GIFT_OK;
+}
+
+}  // namespace gift

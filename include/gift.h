@@ -1,0 +1,221 @@
+/*
+ * gift.h -- C ABI of the GIFT FP8 gradient round trip on MI355X (gfx950).
+ *
+ * GIFT (GIFT review: pith.science review of arXiv 2607.07494, "GIFT:
+ * Geometry-Informed Low-precision Gradient Communication for LLM
+ * Pretraining") sends each selected layer's weight gradient G through FP8 in
+ * whitened coordinates: G is right-multiplied by the inverse square root of a
+ * rank-32 approximation of the input-side K-FAC factor A = X^T X / N before
+ * quantization, and by its square root after dequantization ("What carries
+ * the argument", "Core claim"; rank 32 and the 50-step refresh in the
+ * free-parameter ledger).  Layers not selected use plain ("Euclidean") FP8
+ * with one scale per tensor ("The pith").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensor pointers inside gift_factor / gift_layer, and X, sketch, A_out,
+ *   dev_flags, dev_out and ws, are DEVICE pointers on the current HIP device,
+ *   allocated and owned by the caller.  The library allocates and frees
+ *   nothing and keeps no state between calls.
+ * - The gift_layer / gift_factor arrays themselves are HOST memory, read
+ *   during the call only.
+ * - All matrices are dense, row-major, with leading dimension = row length.
+ *   Every device pointer must be 16-byte aligned.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Calls only enqueue work on it and return; results are visible to later
+ *   work on that stream.  No host synchronisation happens inside a call.
+ * - `ws` is a device workspace of at least the size the matching
+ *   gift_*_workspace_bytes() query returns.  Its contents on entry are
+ *   ignored; on return they are scratch.  Two calls in flight at the same
+ *   time (different streams) need different workspaces.
+ * - Argument errors are reported synchronously, before anything is
+ *   enqueued: the call returns a gift_status other than GIFT_OK and
+ *   gift_last_error() holds a one-line explanation.  Errors raised by the
+ *   HIP runtime while enqueueing return GIFT_ERR_HIP.
+ * - Data-dependent conditions (a non-finite value met while computing an
+ *   amax, an all-zero tensor) are not errors: the call OR-s the GIFT_FLAG_*
+ *   bits into *dev_flags (when dev_flags is not NULL); the caller zeroes it.
+ */
+#ifndef GIFT_H
+#define GIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GIFT_ABI_VERSION 1
+
+/* Rank of the factor (GIFT review, free-parameter ledger: rank 32). */
+#define GIFT_RANK 32
+/* Largest subspace width of the refresh eigensolve (rank + oversampling). */
+#define GIFT_MAX_SKETCH 64
+/* Row-segment length of 1x128 block scaling. */
+#define GIFT_BLOCK 128
+
+typedef enum gift_status {
+    GIFT_OK = 0,
+    GIFT_ERR_INVALID_ARG = 1,        /* NULL pointer, bad enum, misalignment */
+    GIFT_ERR_UNSUPPORTED_SHAPE = 2,  /* a size outside what the kernels take */
+    GIFT_ERR_WORKSPACE_TOO_SMALL = 3,
+    GIFT_ERR_HIP = 4                 /* HIP runtime error while enqueueing */
+} gift_status;
+
+/* Activation dtype for the factor refresh. */
+enum { GIFT_DTYPE_F32 = 0, GIFT_DTYPE_BF16 = 1 };
+
+/* Damping reading of the factor (the pages fix neither damping nor scaling):
+ *  FLOOR:           lambda_iso = eps * tr(A) / d_in
+ *  FLOOR_PLUS_TAIL: lambda_iso = eps * tr(A) / d_in + mean discarded eigenvalue
+ *                   (t - sum theta) / (d_in - rank), clamped at 0. */
+enum { GIFT_DAMP_FLOOR = 0, GIFT_DAMP_FLOOR_PLUS_TAIL = 1 };
+
+/* FP8 scaling granularity: one scale per tensor, or one per 128 consecutive
+ * elements of a row (requires d_in % 128 == 0). */
+enum { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1 };
+
+/* Bits OR-ed into *dev_flags. */
+#define GIFT_FLAG_NONFINITE 1u  /* an amax was NaN or +inf                   */
+#define GIFT_FLAG_ZERO_AMAX 2u  /* a tensor / block was all zero: scale = 1 */
+
+/* Layout of gift_factor.coef (fp32, GIFT_COEF_COUNT entries). */
+enum {
+    GIFT_COEF_ALPHA = 0,        /* lambda_iso^-1/2                            */
+    GIFT_COEF_BETA = 1,         /* lambda_iso^+1/2                            */
+    GIFT_COEF_LAMBDA_ISO = 2,
+    GIFT_COEF_LAMBDA_FLOOR = 3,
+    GIFT_COEF_TRACE = 4,        /* tr(A)                                      */
+    GIFT_COEF_SIGMA2_TAIL = 5,  /* mean discarded eigenvalue                  */
+    GIFT_COEF_DW = 8,           /* D_w[32] = (theta+lambda)^-1/2 - lambda^-1/2 */
+    GIFT_COEF_DU = 8 + GIFT_RANK, /* D_u[32] = (theta+lambda)^1/2 - lambda^1/2 */
+    GIFT_COEF_COUNT = 8 + 2 * GIFT_RANK
+};
+
+/*
+ * Rank-32 input-side factor A_r = U diag(theta) U^T + lambda_iso I of one
+ * distinct layer input.  Its inverse square root is
+ *     A_r^-1/2 = alpha I + U diag(D_w) U^T
+ * and its square root A_r^1/2 = beta I + U diag(D_u) U^T (U orthonormal).
+ * Written by gift_refresh_factor; a caller may also fill it itself.
+ */
+typedef struct gift_factor {
+    int32_t d_in;     /* rows of U; 64 <= d_in, d_in % 16 == 0                 */
+    int32_t rank;     /* must be GIFT_RANK                                    */
+    float *U;         /* device, d_in x rank, row-major                       */
+    float *theta;     /* device, rank: Ritz values, descending, >= 0          */
+    float *coef;      /* device, GIFT_COEF_COUNT floats (layout above)        */
+} gift_factor;
+
+/*
+ * One layer of a grouped call.  factor == NULL marks a Euclidean layer (plain
+ * FP8 of G), otherwise the layer is whitened with *factor (factor->d_in must
+ * equal d_in).  Which pointers an entry point reads or writes is listed at
+ * the entry point; the others may be NULL.
+ */
+typedef struct gift_layer {
+    int64_t d_out;               /* rows of G, >= 1                            */
+    int64_t d_in;                /* columns of G, >= 1; % 4 == 0; % 16 == 0 and
+                                    >= 64 when factor != NULL; % 128 == 0 for
+                                    block scaling                              */
+    const float *G;              /* device, d_out x d_in fp32 gradient         */
+    uint8_t *q;                  /* device, d_out x d_in OCP E4M3 codes        */
+    float *inv_scale;            /* device: 1 float (tensor scaling) or
+                                    d_out x (d_in/128) (block scaling)         */
+    float *G_hat;                /* device, d_out x d_in fp32 reconstruction   */
+    const gift_factor *factor;   /* HOST pointer or NULL                       */
+    float *W_out;                /* optional device d_out x d_in: the whitened
+                                    fp32 tensor before scaling (or G itself for
+                                    a Euclidean layer); NULL = not written     */
+} gift_layer;
+
+/*
+ * gift_refresh_factor -- rebuild one factor from a batch of layer inputs
+ * (GIFT review, "Load-bearing premise": the factor is refreshed every 50
+ * steps; referee report major comment 2: the input-side factor A = E[a a^T]).
+ *
+ *   A       = X^T X / N                  (bf16 or fp32 X, fp32 accumulation)
+ *   t       = tr(A), lambda_floor = damp_eps * t / d_in
+ *   Omega   = sketch (device, d_in x sketch_width fp32) or, when sketch is
+ *             NULL, a standard Gaussian drawn from Philox4x32-10 with key
+ *             `seed` and Box-Muller (element n = i*width + j uses counter
+ *             n/4, lanes (0,1) -> pair 1, (2,3) -> pair 2)
+ *   Q       = orth(A Omega); power_steps times Q = orth(A Q)
+ *   B       = Q^T A Q; theta, V = top-rank eigenpairs of B; U = Q V
+ *   lambda_iso, alpha, beta, D_w, D_u per damping_mode (see above).
+ *
+ * X: device, n_tokens x f->d_in, x_dtype.  f: host struct with device
+ * buffers, written.  A_out: optional device d_in x d_in fp32, receives A.
+ * sketch_width: rank <= width <= 64, multiple of 16.  power_steps >= 0.
+ */
+gift_status gift_refresh_factor(const void *X, int x_dtype, int64_t n_tokens,
+                                const gift_factor *f, float damp_eps,
+                                int damping_mode, int sketch_width,
+                                int power_steps, uint64_t seed,
+                                const float *sketch, float *A_out,
+                                void *ws, size_t ws_bytes, void *stream);
+
+size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens,
+                                    int x_dtype, int sketch_width);
+
+/*
+ * gift_whiten_quantize -- the send side, grouped over n_layers layers.
+ * For each layer: W = G A_r^-1/2 (factor != NULL) or W = G (factor == NULL);
+ * amax = max |W| per tensor (or per 128-element row segment); scale =
+ * 448 / amax, inv = amax / 448 (scale = inv = 1 when amax == 0); q =
+ * E4M3(W * scale) rounded to nearest even, saturated to +-448, NaN -> 0x7F.
+ * Reads G (and the factor); writes q, inv_scale, and W_out when given.
+ * The FP8 format and the scaling rule are this library's reading of
+ * "a single FP8 scale factor" ("The pith") and of reference [28].
+ */
+gift_status gift_whiten_quantize(const gift_layer *layers, int n_layers,
+                                 int scaling, uint32_t *dev_flags,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gift_dequant_unwhiten -- the receive side ("maps the result back", "The
+ * pith"): W^ = decode(q) * inv; G_hat = W^ A_r^1/2 (factor != NULL) or
+ * G_hat = W^ (factor == NULL).  Reads q, inv_scale (and the factor); writes
+ * G_hat.
+ */
+gift_status gift_dequant_unwhiten(const gift_layer *layers, int n_layers,
+                                  int scaling, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/*
+ * gift_euclid_fp8_roundtrip -- the Euclidean baseline ("Core claim": the
+ * comparison GIFT is measured against): q = E4M3(G * scale), G_hat =
+ * decode(q) * inv, ignoring layer.factor.  Reads G; writes q, inv_scale,
+ * G_hat.
+ */
+gift_status gift_euclid_fp8_roundtrip(const gift_layer *layers, int n_layers,
+                                      int scaling, uint32_t *dev_flags,
+                                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gift_roundtrip_error -- per layer l: dev_out[2l] = sum (G_hat - G)^2 and
+ * dev_out[2l+1] = sum G^2, accumulated in fp64 in a fixed order (relative
+ * reconstruction error, "Core claim").  Reads G and G_hat.
+ */
+gift_status gift_roundtrip_error(const gift_layer *layers, int n_layers,
+                                 double *dev_out, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+/* Workspace query for the four grouped calls.  op: 0 whiten_quantize,
+ * 1 dequant_unwhiten, 2 euclid_fp8_roundtrip, 3 roundtrip_error. */
+enum { GIFT_OP_WHITEN_QUANTIZE = 0, GIFT_OP_DEQUANT_UNWHITEN = 1,
+       GIFT_OP_EUCLID_ROUNDTRIP = 2, GIFT_OP_ROUNDTRIP_ERROR = 3 };
+size_t gift_group_workspace_bytes(int op, const gift_layer *layers,
+                                  int n_layers, int scaling);
+
+const char *gift_status_string(int status);
+/* Thread-local detail of the last failing call on this thread. */
+const char *gift_last_error(void);
+int gift_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GIFT_H */

@@ -1,0 +1,97 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/gift.h declares, and rejects bad arguments synchronously (these
+calls return before any HIP call, so they need no GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import fac_whitening_gift_amd as fg
+from fac_whitening_gift_amd import _lib
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gift.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gift_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fg.load()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fg.EXPORTS)
+    assert lib.gift_abi_version() == 1
+
+
+def test_status_strings():
+    for s, name in enumerate(["GIFT_OK", "GIFT_ERR_INVALID_ARG", "GIFT_ERR_UNSUPPORTED_SHAPE",
+                              "GIFT_ERR_WORKSPACE_TOO_SMALL", "GIFT_ERR_HIP"]):
+        assert fg.status_name(s) == name
+
+
+def _layer(d_out=64, d_in=128, factor=None, ptr=0x10000):
+    L = _lib._Layer()
+    L.d_out, L.d_in = d_out, d_in
+    L.G = L.q = L.inv_scale = L.G_hat = ptr
+    L.W_out = None
+    L.factor = factor if factor is not None else ctypes.POINTER(_lib._Factor)()
+    return L
+
+
+def _call_whiten(layers, scaling=fg.SCALE_TENSOR, ws=0x100000, ws_bytes=1 << 30):
+    lib = fg.load()
+    arr = (_lib._Layer * len(layers))(*layers)
+    return lib.gift_whiten_quantize(arr, len(layers), scaling, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(d_in=130), 2),
+    (dict(d_out=0), 2),
+    (dict(d_in=1 << 25), 2),
+    (dict(ptr=0x10004), 1),
+    (dict(ptr=None), 1),
+])
+def test_layer_validation(case, status):
+    assert _call_whiten([_layer(**case)]) == status
+    assert fg.load().gift_last_error()
+
+
+def test_block_scaling_needs_multiple_of_128():
+    assert _call_whiten([_layer(d_in=192)], scaling=fg.SCALE_BLOCK128) == 2
+    assert _call_whiten([_layer(d_in=192)], scaling=7) == 1
+
+
+def test_factor_validation():
+    f = _lib._Factor(128, 32, 0x20000, 0x30000, 0x40000)
+    assert _call_whiten([_layer(d_in=256, factor=ctypes.pointer(f))]) == 1   # d_in mismatch
+    f_bad_rank = _lib._Factor(128, 16, 0x20000, 0x30000, 0x40000)
+    assert _call_whiten([_layer(d_in=128, factor=ctypes.pointer(f_bad_rank))]) == 2
+    f_small = _lib._Factor(32, 32, 0x20000, 0x30000, 0x40000)
+    assert _call_whiten([_layer(d_in=32, factor=ctypes.pointer(f_small))]) == 2
+
+
+def test_workspace_validation():
+    f = _lib._Factor(128, 32, 0x20000, 0x30000, 0x40000)
+    layers = [_layer(d_in=128, factor=ctypes.pointer(f))]
+    need = fg.load().gift_group_workspace_bytes(
+        _lib.OP_WHITEN_QUANTIZE, (_lib._Layer * 1)(*layers), 1, fg.SCALE_TENSOR)
+    assert need > 0
+    assert _call_whiten(layers, ws_bytes=need - 1) == 3
+    assert _call_whiten(layers, ws=0x100010) == 1     # not 256-byte aligned
+    assert _call_whiten(layers, ws=None) == 1
+
+
+def test_error_and_dequant_validation():
+    lib = fg.load()
+    arr = (_lib._Layer * 1)(_layer())
+    assert lib.gift_roundtrip_error(arr, 1, None, 0x100000, 1 << 30, None) == 1
+    arr[0].G_hat = None
+    assert lib.gift_dequant_unwhiten(arr, 1, 0, 0x100000, 1 << 30, None) == 1
+    assert lib.gift_euclid_fp8_roundtrip(arr, -1, 0, None, 0x100000, 1 << 30, None) == 1
