@@ -34,7 +34,7 @@ EXPORTS = (
     "gift_refresh_factor", "gift_refresh_workspace_bytes", "gift_whiten_quantize",
     "gift_dequant_unwhiten", "gift_euclid_fp8_roundtrip", "gift_roundtrip_error",
     "gift_group_workspace_bytes", "gift_status_string", "gift_last_error",
-    "gift_abi_version",
+    "gift_abi_version", "gift_draw_sketch",
 )
 
 
@@ -82,6 +82,7 @@ def load():
         "gift_status_string": (ctypes.c_char_p, [I]),
         "gift_last_error": (ctypes.c_char_p, []),
         "gift_abi_version": (I, []),
+        "gift_draw_sketch": (I, [P, I64, I, U64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -299,3 +300,13 @@ def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_T
                                    float(damp_eps), damping_mode, sketch_width, power_steps,
                                    ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(sketch),
                                    _ptr(A_out), _ptr(ws), ws.numel() * ws.element_size() * ws.element_size(), _stream(stream)))
+
+
+def gift_draw_sketch(d_in, width=MAX_SKETCH, seed=0, out=None, device="cuda", stream=None):
+    """-> device fp32 (d_in, width) Gaussian sketch (Philox4x32-10 + Box-Muller)."""
+    if out is None:
+        out = torch.empty(d_in, width, dtype=torch.float32, device=device)
+    _dev(out, torch.float32, (d_in, width), "out")
+    _check(load().gift_draw_sketch(_ptr(out), d_in, width,
+                                   ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _stream(stream)))
+    return out

@@ -24,6 +24,8 @@ gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const g
                            float damp_eps, int damping_mode, int width, int power_steps,
                            uint64_t seed, const float* sketch, float* A_out, void* ws,
                            size_t ws_bytes, hipStream_t s, std::string* err);
+gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t s,
+                        std::string* err);
 }  // namespace gift
 
 using namespace gift;
@@ -331,6 +333,10 @@ gift_status gift_refresh_factor(const void* X, int x_dtype, int64_t n_tokens,
   return refresh_factor(X, x_dtype, n_tokens, f, damp_eps, damping_mode, sketch_width,
                         power_steps, seed, sketch, A_out, ws, ws_bytes, (hipStream_t)stream,
                         &t_err);
+}
+
+gift_status gift_draw_sketch(float* out, int64_t d_in, int width, uint64_t seed, void* stream) {
+  return draw_sketch(out, d_in, width, seed, (hipStream_t)stream, &t_err);
 }
 
 }  // extern "C"

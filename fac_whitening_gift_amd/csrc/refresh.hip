@@ -233,8 +233,7 @@ __global__ __launch_bounds__(kT) void k_syrk(const void* Xv, int64_t N, int d, i
 
 // 2. A[i][j] = A[j][i] = (sum_s part[s]) / N  over the upper triangle
 __global__ __launch_bounds__(kT) void k_syrk_reduce(const float* part, int nsplit, int npairs,
-                                                    int nb, int d, float inv_n_unused,
-                                                    int64_t N, float* A) {
+                                                    int nb, int d, int64_t N, float* A) {
   int bi, bj;
   decode_pair(blockIdx.x, nb, bi, bj);
   const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
@@ -640,6 +639,27 @@ size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int, int width) {
   return ws_layout(d_in, n_tokens, width).total;
 }
 
+gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t st,
+                        std::string* err) {
+  if (!out || ((uintptr_t)out & 15u)) {
+    *err = "gift_draw_sketch: out NULL or not 16-byte aligned";
+    return GIFT_ERR_INVALID_ARG;
+  }
+  if (d < 1 || width < 1 || d * (int64_t)width > (int64_t(1) << 34)) {
+    *err = "gift_draw_sketch: size out of range";
+    return GIFT_ERR_UNSUPPORTED_SHAPE;
+  }
+  const int64_t total = d * width;
+  const int64_t ctr = (total + 3) / 4;
+  k_sketch<<<(unsigned)((ctr + kT - 1) / kT), kT, 0, st>>>(out, total, seed);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("gift_draw_sketch: ") + hipGetErrorString(e);
+    return GIFT_ERR_HIP;
+  }
+  return GIFT_OK;
+}
+
 #define GIFT_HIP(call)                                                          \
   do {                                                                          \
     hipError_t e_ = (call);                                                     \
@@ -704,7 +724,7 @@ gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const g
   else
     k_syrk<false><<<dim3(p.npairs, p.nsplit), kT, 0, st>>>(X, n_tokens, d, p.nb, p.chunk, part, p.npairs);
   GIFT_HIP(hipGetLastError());
-  k_syrk_reduce<<<p.npairs, kT, 0, st>>>(part, p.nsplit, p.npairs, p.nb, d, 0.f, n_tokens, A);
+  k_syrk_reduce<<<p.npairs, kT, 0, st>>>(part, p.nsplit, p.npairs, p.nb, d, n_tokens, A);
   k_trace<<<1, kT, 0, st>>>(A, d, tr);
   GIFT_HIP(hipGetLastError());
   // 4: sketch

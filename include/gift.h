@@ -160,6 +160,18 @@ size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens,
                                     int x_dtype, int sketch_width);
 
 /*
+ * gift_draw_sketch -- the Gaussian sketch gift_refresh_factor draws when it
+ * is given none: out (device, d_in x width fp32, row-major) element
+ * n = i*width + j is normal number n of the Philox4x32-10 stream with key
+ * (seed low word, seed high word) (Salmon et al., SC'11): counter
+ * (n/4, 0, 0, 0) gives words w0..w3; (w0, w1) and (w2, w3) each make one
+ * Box-Muller pair r cos(2 pi u2), r sin(2 pi u2) with r = sqrt(-2 ln u1),
+ * u1 = (w + 1) 2^-32, u2 = w 2^-32, evaluated in fp64 and rounded to fp32.
+ */
+gift_status gift_draw_sketch(float *out, int64_t d_in, int width, uint64_t seed,
+                             void *stream);
+
+/*
  * gift_whiten_quantize -- the send side, grouped over n_layers layers.
  * For each layer: W = G A_r^-1/2 (factor != NULL) or W = G (factor == NULL);
  * amax = max |W| per tensor (or per 128-element row segment); scale =

@@ -21,7 +21,9 @@ implementation's reading, each marked where it is taken:
 4. Damping: A_r = U diag(Theta) U^T + lambda_iso I.  Reading "floor+tail"
    (default): lambda_iso = lambda_floor + mean of the discarded spectrum,
    (t - sum Theta) / (d_in - r), the isotropic residual of probabilistic
-   PCA; reading "floor": lambda_iso = lambda_floor.
+   PCA; reading "floor": lambda_iso = lambda_floor.  lambda_iso is kept at
+   or above 1e-30 so an all-zero input (t = 0) still gives finite
+   coefficients (whitening then reduces to a scalar multiple).
 5. Whitening is input-side, G -> G A_r^{-1/2}; un-whitening is
    W -> W A_r^{1/2}.  With U orthonormal,
    A_r^{-1/2} = alpha I + U diag(D_w) U^T, alpha = lambda_iso^{-1/2},
@@ -50,6 +52,7 @@ SKETCH_WIDTH = 64
 POWER_STEPS = 4
 DAMP_EPS = 1e-3
 BLOCK = 128
+LAMBDA_MIN = 1e-30
 
 DAMPING_FLOOR = "floor"
 DAMPING_FLOOR_PLUS_TAIL = "floor+tail"
@@ -115,7 +118,7 @@ def damping(t, theta, d, eps=DAMP_EPS, mode=DAMPING_FLOOR_PLUS_TAIL):
         lam = lam_floor
     else:
         raise ValueError(mode)
-    return lam, lam_floor, tail
+    return max(lam, LAMBDA_MIN), lam_floor, tail
 
 
 def coefficients(theta, lam):

@@ -1,0 +1,180 @@
+"""Device parity of the factor refresh against the oracle.
+
+* sketch: the device's Philox4x32-10 + Box-Muller draw against the oracle's
+  own implementation of the same published definition;
+* covariance A = X^T X / N within 1e-5 relative Frobenius, exactly symmetric;
+* factor, with the same sketch passed to both sides: Ritz values within 1e-4
+  relative, the whitening and un-whitening operators A_r^{-1/2} P and
+  A_r^{1/2} P within 1e-4 on a probe P, coefficients within 1e-5;
+* exact low rank (rank 20 < 32): the dependent sketch directions are dropped
+  and the 20 eigenpairs still come out exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import fac_whitening_gift_amd as fg
+from oracle import gift as og
+from oracle import philox
+from gpu_util import DEV, host, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_refresh(X_dev, d, sketch=None, mode=fg.DAMP_FLOOR_PLUS_TAIL, width=64, steps=4,
+                 seed=0, eps=1e-3):
+    f = fg.Factor(d)
+    A = torch.empty(d, d, dtype=torch.float32, device=DEV)
+    fg.gift_refresh_factor(X_dev, f, damp_eps=eps, damping_mode=mode, sketch_width=width,
+                           power_steps=steps, seed=seed, sketch=sketch, A_out=A)
+    torch.cuda.synchronize()
+    return f, A
+
+
+def _check_factor(f_dev, f_orc, P, tol_op=1e-4, tol_theta=1e-4, n_theta=32):
+    U = host(f_dev.U).astype(np.float64)
+    th = host(f_dev.theta).astype(np.float64)
+    c = host(f_dev.coef).astype(np.float64)
+    assert np.allclose(th[:n_theta], f_orc.theta[:n_theta], rtol=tol_theta,
+                       atol=1e-7 * f_orc.theta[0])
+    for k, ref in ((fg.COEF_LAMBDA_ISO, f_orc.lambda_iso), (fg.COEF_ALPHA, f_orc.alpha),
+                   (fg.COEF_BETA, f_orc.beta), (fg.COEF_TRACE, f_orc.trace),
+                   (fg.COEF_LAMBDA_FLOOR, f_orc.lambda_floor)):
+        assert abs(c[k] - ref) <= 1e-5 * abs(ref), k
+    dw = c[fg.COEF_DW:fg.COEF_DW + 32]
+    du = c[fg.COEF_DU:fg.COEF_DU + 32]
+    W_dev = og.whiten_with(P, U, c[fg.COEF_ALPHA], dw)
+    W_orc = og.whiten(P, f_orc)
+    assert rel_fro(W_dev, W_orc) <= tol_op
+    assert rel_fro(og.unwhiten_with(P, U, c[fg.COEF_BETA], du), og.unwhiten(P, f_orc)) <= tol_op
+    # U has orthonormal columns (to fp32 rounding)
+    assert np.linalg.norm(U.T @ U - np.eye(32)) < 1e-5
+
+
+def test_sketch_matches_oracle_philox():
+    say("sketch d=1000 w=64 seed=0x123456789")
+    seed = 0x1_2345_6789
+    out = host(fg.gift_draw_sketch(1000, 64, seed))
+    ref = philox.gaussian_sketch(1000, 64, seed).astype(np.float32)
+    diff_ulp = np.abs(out.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert diff_ulp.max() <= 1
+    assert np.count_nonzero(diff_ulp) <= 4
+    # ragged total (not a multiple of 4) and another seed
+    out2 = host(fg.gift_draw_sketch(33, 3, 7))
+    ref2 = philox.gaussian_sketch(33, 3, 7).astype(np.float32)
+    assert np.max(np.abs(out2 - ref2) / np.maximum(np.abs(ref2), 1e-30)) <= 2 ** -23
+
+
+@pytest.mark.parametrize("n,d,bf16", [(4096, 512, False), (8192, 1024, True), (1000, 192, True),
+                                      (17, 64, False), (3000, 1040, True)])
+def test_covariance(n, d, bf16):
+    say("covariance n=%d d=%d bf16=%s" % (n, d, bf16))
+    spec = synth.InputSpec("x", d, n, 1.5, bf16=bf16)
+    inp = synth.draw_input(spec, seed=n + d, as_bf16=bf16)
+    X = inp["X"]
+    Xh = X.float().numpy()
+    f, A = _run_refresh(X.to(DEV), d, steps=1)
+    Ad = host(A)
+    assert np.array_equal(Ad, Ad.T)
+    assert rel_fro(Ad, og.covariance(Xh)) <= 1e-5
+    tr = float(host(f.coef)[fg.COEF_TRACE])
+    assert abs(tr - np.trace(og.covariance(Xh))) <= 1e-5 * abs(tr)
+
+
+@pytest.mark.parametrize("mode", [fg.DAMP_FLOOR_PLUS_TAIL, fg.DAMP_FLOOR])
+def test_factor_single_layer(mode):
+    """d_in 512, 4096 fp32 tokens, the same sketch on both sides."""
+    say("factor single layer mode=%d" % mode)
+    spec = synth.InputSpec("x", 512, 4096, 1.5, bf16=False)
+    inp = synth.draw_input(spec, seed=41)
+    omega = synth.gaussian_sketch(512, 64, seed=42)
+    f_dev, _ = _run_refresh(inp["X"].to(DEV), 512, sketch=omega.to(DEV), mode=mode)
+    omode = og.DAMPING_FLOOR_PLUS_TAIL if mode == fg.DAMP_FLOOR_PLUS_TAIL else og.DAMPING_FLOOR
+    f_orc = og.refresh_factor(inp["X"].numpy(), omega.numpy().astype(np.float64), mode=omode)
+    P = np.random.default_rng(3).standard_normal((64, 512))
+    _check_factor(f_dev, f_orc, P)
+
+
+def test_factor_with_device_sketch_is_close():
+    """Without a sketch the device draws its own (Philox); the oracle draws
+    the same definition in fp64: the operators agree."""
+    say("factor device sketch")
+    spec = synth.InputSpec("x", 512, 4096, 1.5, bf16=False)
+    inp = synth.draw_input(spec, seed=43)
+    f_dev, _ = _run_refresh(inp["X"].to(DEV), 512, seed=99)
+    f_orc = og.refresh_factor(inp["X"].numpy(), philox.gaussian_sketch(512, 64, 99))
+    P = np.random.default_rng(4).standard_normal((64, 512))
+    _check_factor(f_dev, f_orc, P)
+
+
+def test_exact_low_rank_drops_dependent_directions():
+    say("factor exact rank 20")
+    rng = np.random.default_rng(8)
+    d, k, n = 256, 20, 2048
+    B = np.linalg.qr(rng.standard_normal((d, k)))[0] * np.linspace(3, 0.5, k)
+    X = (rng.standard_normal((n, k)) @ B.T).astype(np.float32)
+    omega = synth.gaussian_sketch(d, 64, seed=5)
+    f_dev, _ = _run_refresh(torch.from_numpy(X).to(DEV), d, sketch=omega.to(DEV))
+    A = og.covariance(X)
+    w, V = np.linalg.eigh(A)
+    w, V = w[::-1], V[:, ::-1]
+    th = host(f_dev.theta).astype(np.float64)
+    U = host(f_dev.U).astype(np.float64)
+    assert np.allclose(th[:k], w[:k], rtol=1e-4)
+    assert np.all(th[k:] <= 1e-5 * w[0])
+    Pk = U[:, :k] @ U[:, :k].T
+    assert np.linalg.norm(Pk - V[:, :k] @ V[:, :k].T) < 1e-4
+    assert np.all(np.isfinite(host(f_dev.coef)))
+
+
+@pytest.mark.parametrize("width,steps", [(32, 4), (48, 2), (64, 0)])
+def test_width_and_power_steps(width, steps):
+    say("factor width=%d steps=%d" % (width, steps))
+    spec = synth.InputSpec("x", 256, 2048, 2.0, bf16=True)
+    inp = synth.draw_input(spec, seed=44, as_bf16=True)
+    omega = synth.gaussian_sketch(256, width, seed=45)
+    f_dev, _ = _run_refresh(inp["X"].to(DEV), 256, sketch=omega.to(DEV), width=width, steps=steps)
+    f_orc = og.refresh_factor(inp["X"].float().numpy(), omega.numpy().astype(np.float64),
+                              power_steps=steps)
+    P = np.random.default_rng(5).standard_normal((32, 256))
+    # same subspace iteration on both sides: only the well-separated head of
+    # the spectrum is compared when the iteration is short or narrow
+    _check_factor(f_dev, f_orc, P, tol_op=1e-3 if steps < 4 or width < 64 else 1e-4,
+                  tol_theta=1e-3, n_theta=16)
+
+
+def test_refresh_is_deterministic():
+    say("refresh determinism")
+    spec = synth.InputSpec("x", 1024, 8192, 1.5, bf16=True)
+    inp = synth.draw_input(spec, seed=46, as_bf16=True)
+    X = inp["X"].to(DEV)
+    f1, A1 = _run_refresh(X, 1024, seed=3)
+    f2, A2 = _run_refresh(X, 1024, seed=3)
+    assert torch.equal(A1, A2) and torch.equal(f1.U, f2.U) and torch.equal(f1.coef, f2.coef)
+
+
+@pytest.fixture(scope="module")
+def block_inputs():
+    w = synth.llama_block()
+    out = []
+    for k, spec in enumerate(w.inputs):
+        inp = synth.draw_input(spec, seed=800 + k, as_bf16=True)
+        out.append((spec, inp))
+    return out
+
+
+def test_full_block_factors(block_inputs):
+    """The four inputs of a hidden-1024 block (8192 bf16 tokens, d_in 1024 and
+    2816), refreshed as the benchmark does, against the oracle."""
+    for k, (spec, inp) in enumerate(block_inputs):
+        say("factor %s d=%d" % (spec.name, spec.d_in))
+        omega = synth.gaussian_sketch(spec.d_in, 64, seed=900 + k)
+        f_dev, A = _run_refresh(inp["X"].to(DEV), spec.d_in, sketch=omega.to(DEV))
+        Xh = inp["X"].float().numpy()
+        A_orc = og.covariance(Xh)
+        assert rel_fro(host(A), A_orc) <= 1e-5
+        f_orc = og.refresh_factor(Xh, omega.numpy().astype(np.float64), A=A_orc)
+        P = np.random.default_rng(k).standard_normal((32, spec.d_in))
+        _check_factor(f_dev, f_orc, P)

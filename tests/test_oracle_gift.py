@@ -87,6 +87,10 @@ def test_damping_readings():
     assert lf == 1e-3 * 10 / 6 and tail == (10 - 6) / 4 and lam == lf + tail
     lam1, lf1, _ = og.damping(10.0, theta, 6, 1e-3, og.DAMPING_FLOOR)
     assert lam1 == lf1
+    # all-zero input: damping is held at its floor, coefficients stay finite
+    lam0, _, _ = og.damping(0.0, np.zeros(2), 6, 1e-3, og.DAMPING_FLOOR_PLUS_TAIL)
+    assert lam0 == og.LAMBDA_MIN
+    assert all(np.all(np.isfinite(c)) for c in og.coefficients(np.zeros(2), lam0))
 
 
 # ---------------------------------------------------------------- whitening
