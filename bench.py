@@ -108,21 +108,22 @@ def main():
                                     device=dev)
             layers.append(fg.Layer(G, factor=factors[l.input]))
         ring.append(layers)
-    ws_ref = {}
-    for spec in w.inputs:
-        nb = fg.gift_refresh_workspace_bytes(spec.d_in, spec.tokens, fg.DTYPE_BF16, 64)
-        ws_ref[spec.name] = torch.empty(nb, dtype=torch.uint8, device=dev)
+    items = [dict(X=inputs[spec.name]["X"], factor=factors[spec.name], seed=0)
+             for spec in w.inputs]
+    ws_ref = torch.empty(fg.gift_refresh_group_workspace_bytes(items), dtype=torch.uint8,
+                         device=dev)
     nb_w = max(fg.gift_group_workspace_bytes(0, ring[0], fg.SCALE_TENSOR), 256)
     ws_w = torch.empty(nb_w, dtype=torch.uint8, device=dev)
     nb_e = max(fg.gift_group_workspace_bytes(2, ring[0], fg.SCALE_TENSOR), 256)
     ws_e = torch.empty(nb_e, dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(256, dtype=torch.uint8, device=dev)
+    nb_d = max(fg.gift_group_workspace_bytes(1, ring[0], fg.SCALE_TENSOR), 256)
+    ws_d = torch.empty(nb_d, dtype=torch.uint8, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def refresh_all(seed):
-        for k, spec in enumerate(w.inputs):
-            fg.gift_refresh_factor(inputs[spec.name]["X"], factors[spec.name], seed=seed + k,
-                                   ws=ws_ref[spec.name])
+        for k, it in enumerate(items):
+            it["seed"] = seed + k
+        fg.gift_refresh_factors(items, ws=ws_ref)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     refresh_all(1)
@@ -184,12 +185,15 @@ def main():
 
     t_eu = timed_loop(lambda L: fg.gift_euclid_fp8_roundtrip(L, ws=ws_e), 20)
     ring_b = [[fg.Layer(L.G, factor=L.factor, block128=True) for L in layers] for layers in ring]
+    nb_b = max(fg.gift_group_workspace_bytes(0, ring_b[0], fg.SCALE_BLOCK128),
+               fg.gift_group_workspace_bytes(1, ring_b[0], fg.SCALE_BLOCK128), 256)
+    ws_b = torch.empty(nb_b, dtype=torch.uint8, device=dev)
     t_b = []
     for s in range(20):
         a, b = ev(), ev()
         a.record()
-        fg.gift_whiten_quantize(ring_b[s % len(ring_b)], scaling=fg.SCALE_BLOCK128, ws=ws_d)
-        fg.gift_dequant_unwhiten(ring_b[s % len(ring_b)], scaling=fg.SCALE_BLOCK128, ws=ws_d)
+        fg.gift_whiten_quantize(ring_b[s % len(ring_b)], scaling=fg.SCALE_BLOCK128, ws=ws_b)
+        fg.gift_dequant_unwhiten(ring_b[s % len(ring_b)], scaling=fg.SCALE_BLOCK128, ws=ws_b)
         b.record()
         t_b.append((a, b))
     torch.cuda.synchronize()

@@ -9,7 +9,8 @@ from ._lib import (  # noqa: F401
     Factor, Layer, GiftError, load, status_name,
     gift_refresh_factor, gift_refresh_workspace_bytes, gift_whiten_quantize,
     gift_dequant_unwhiten, gift_euclid_fp8_roundtrip, gift_roundtrip_error,
-    gift_group_workspace_bytes, gift_draw_sketch,
+    gift_group_workspace_bytes, gift_draw_sketch, gift_factor_pack_bytes,
+    gift_prepare_factor, gift_refresh_factors, gift_refresh_group_workspace_bytes,
     RANK, MAX_SKETCH, BLOCK, DTYPE_F32, DTYPE_BF16, DAMP_FLOOR, DAMP_FLOOR_PLUS_TAIL,
     SCALE_TENSOR, SCALE_BLOCK128, FLAG_NONFINITE, FLAG_ZERO_AMAX, EXPORTS,
     COEF_ALPHA, COEF_BETA, COEF_LAMBDA_ISO, COEF_LAMBDA_FLOOR, COEF_TRACE, COEF_SIGMA2_TAIL,

@@ -34,7 +34,8 @@ EXPORTS = (
     "gift_refresh_factor", "gift_refresh_workspace_bytes", "gift_whiten_quantize",
     "gift_dequant_unwhiten", "gift_euclid_fp8_roundtrip", "gift_roundtrip_error",
     "gift_group_workspace_bytes", "gift_status_string", "gift_last_error",
-    "gift_abi_version", "gift_draw_sketch",
+    "gift_abi_version", "gift_draw_sketch", "gift_factor_pack_bytes", "gift_prepare_factor",
+    "gift_refresh_factors", "gift_refresh_group_workspace_bytes",
 )
 
 
@@ -46,7 +47,14 @@ class GiftError(RuntimeError):
 
 class _Factor(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("U", ctypes.c_void_p), ("theta", ctypes.c_void_p), ("coef", ctypes.c_void_p)]
+                ("U", ctypes.c_void_p), ("theta", ctypes.c_void_p), ("coef", ctypes.c_void_p),
+                ("packs", ctypes.c_void_p)]
+
+
+class _RefreshInput(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("n_tokens", ctypes.c_int64),
+                ("factor", ctypes.POINTER(_Factor)), ("sketch", ctypes.c_void_p),
+                ("A_out", ctypes.c_void_p), ("seed", ctypes.c_uint64)]
 
 
 class _Layer(ctypes.Structure):
@@ -83,6 +91,10 @@ def load():
         "gift_last_error": (ctypes.c_char_p, []),
         "gift_abi_version": (I, []),
         "gift_draw_sketch": (I, [P, I64, I, U64, P]),
+        "gift_factor_pack_bytes": (SZ, [I64]),
+        "gift_prepare_factor": (I, [ctypes.POINTER(_Factor), P]),
+        "gift_refresh_factors": (I, [ctypes.POINTER(_RefreshInput), I, F, I, I, I, P, SZ, P]),
+        "gift_refresh_group_workspace_bytes": (SZ, [ctypes.POINTER(_RefreshInput), I, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -129,18 +141,30 @@ def _dev(t, dtype, shape, name):
 # --------------------------------------------------------------------------
 
 class Factor:
-    """Device buffers of one rank-32 factor: U (d_in x 32), theta (32), coef."""
+    """Device buffers of one rank-32 factor: U (d_in x 32), theta (32), coef,
+    and (by default, when d_in % 32 == 0) the operand packs of U.
 
-    def __init__(self, d_in, device="cuda", U=None, theta=None, coef=None):
+    A factor built from given U / coef values has stale packs until
+    gift_prepare_factor(factor) runs; gift_refresh_factor(s) rewrite them.
+    packs=False leaves the pointer NULL (every grouped call re-packs U).
+    """
+
+    def __init__(self, d_in, device="cuda", U=None, theta=None, coef=None, packs=True):
         self.d_in = int(d_in)
+        device = U.device if U is not None else device
         self.U = U if U is not None else torch.zeros(d_in, RANK, device=device)
         self.theta = theta if theta is not None else torch.zeros(RANK, device=device)
         self.coef = coef if coef is not None else torch.zeros(COEF_COUNT, device=device)
         _dev(self.U, torch.float32, (d_in, RANK), "U")
         _dev(self.theta, torch.float32, (RANK,), "theta")
         _dev(self.coef, torch.float32, (COEF_COUNT,), "coef")
+        self.packs = None
+        if packs and self.d_in % 32 == 0:
+            nb = int(load().gift_factor_pack_bytes(self.d_in))
+            self.packs = torch.empty(nb, dtype=torch.uint8, device=self.U.device)
         self._struct = _Factor(self.d_in, RANK, self.U.data_ptr(), self.theta.data_ptr(),
-                               self.coef.data_ptr())
+                               self.coef.data_ptr(),
+                               self.packs.data_ptr() if self.packs is not None else None)
 
     @property
     def alpha(self):
@@ -276,6 +300,59 @@ def gift_roundtrip_error(layers, out=None, ws=None, stream=None):
     _check(lib.gift_roundtrip_error(arr, len(layers), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
     return out
+
+
+def gift_factor_pack_bytes(d_in):
+    return int(load().gift_factor_pack_bytes(d_in))
+
+
+def gift_prepare_factor(factor, stream=None):
+    """Rewrite factor.packs from factor.U."""
+    _check(load().gift_prepare_factor(ctypes.byref(factor._struct), _stream(stream)))
+
+
+def _refresh_array(items):
+    arr = (_RefreshInput * max(1, len(items)))()
+    for i, it in enumerate(items):
+        X, factor = it["X"], it["factor"]
+        if X.dtype == torch.bfloat16:
+            xdt = DTYPE_BF16
+        elif X.dtype == torch.float32:
+            xdt = DTYPE_F32
+        else:
+            raise ValueError("X must be bf16 or fp32")
+        if X.dim() != 2 or X.shape[1] != factor.d_in:
+            raise ValueError("X must be n_tokens x %d" % factor.d_in)
+        _dev(X, X.dtype, None, "X")
+        sk, A = it.get("sketch"), it.get("A_out")
+        arr[i].X = X.data_ptr()
+        arr[i].x_dtype = xdt
+        arr[i].n_tokens = X.shape[0]
+        arr[i].factor = ctypes.pointer(factor._struct)
+        arr[i].sketch = sk.data_ptr() if sk is not None else None
+        arr[i].A_out = A.data_ptr() if A is not None else None
+        arr[i].seed = int(it.get("seed", 0)) & 0xFFFFFFFFFFFFFFFF
+    return arr
+
+
+def gift_refresh_group_workspace_bytes(items, sketch_width=MAX_SKETCH):
+    arr = _refresh_array(items)
+    return int(load().gift_refresh_group_workspace_bytes(arr, len(items), sketch_width))
+
+
+def gift_refresh_factors(items, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,
+                         sketch_width=MAX_SKETCH, power_steps=4, ws=None, stream=None):
+    """items: list of dicts {X, factor, [sketch], [A_out], [seed]}."""
+    lib = load()
+    for it in items:
+        _dev(it.get("sketch"), torch.float32, (it["factor"].d_in, sketch_width), "sketch")
+        _dev(it.get("A_out"), torch.float32, (it["factor"].d_in, it["factor"].d_in), "A_out")
+    arr = _refresh_array(items)
+    need = lib.gift_refresh_group_workspace_bytes(arr, len(items), sketch_width)
+    ws = _workspace(need, items[0]["X"].device, ws)
+    _check(lib.gift_refresh_factors(arr, len(items), float(damp_eps), damping_mode, sketch_width,
+                                    power_steps, _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
 
 
 def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,

@@ -15,8 +15,10 @@ hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool wr
                                 hipStream_t s);
 hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s);
 hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
+hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
 int row_tiles(int64_t d_out);
 int flat_tiles(int64_t n);
+size_t pack_bytes(int64_t d_in);
 
 // refresh.hip
 size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype, int width);
@@ -26,6 +28,10 @@ gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const g
                            size_t ws_bytes, hipStream_t s, std::string* err);
 gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t s,
                         std::string* err);
+size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int width);
+gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps, int damping_mode,
+                            int width, int power_steps, void* ws, size_t ws_bytes, hipStream_t st,
+                            std::string* err);
 }  // namespace gift
 
 using namespace gift;
@@ -94,10 +100,56 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
   return w;
 }
 
+// Operand packs: one region per distinct factor (identified by its U
+// pointer) among the whitened layers of the call, at the start of ws.
+struct Packs {
+  std::vector<const float*> U;
+  std::vector<int> d_in;
+  std::vector<size_t> off;
+  size_t bytes = 0;
+  size_t find(const float* u) const {
+    for (size_t i = 0; i < U.size(); ++i)
+      if (U[i] == u) return off[i];
+    return 0;
+  }
+};
+
+Packs plan_packs(const gift_layer* layers, int n, Op op) {
+  Packs p;
+  for (int i = 0; i < n; ++i) {
+    if (!whitened(layers[i], op) || layers[i].factor->packs) continue;
+    const float* u = layers[i].factor->U;
+    bool seen = false;
+    for (const float* v : p.U) seen |= v == u;
+    if (seen) continue;
+    p.U.push_back(u);
+    p.d_in.push_back((int)layers[i].d_in);
+    p.off.push_back(p.bytes);
+    p.bytes += align_up(pack_bytes(layers[i].d_in));
+  }
+  return p;
+}
+
 size_t group_ws(const gift_layer* layers, int n, Op op, bool block) {
-  size_t t = 0;
+  size_t t = plan_packs(layers, n, op).bytes;
   for (int i = 0; i < n; ++i) t += layer_ws(layers[i], op, block).total();
   return t;
+}
+
+gift_status run_packs(const Packs& p, void* ws, hipStream_t st) {
+  PackGroup pg{};
+  for (size_t i = 0; i < p.U.size(); ++i) {
+    PackDev& d = pg.f[pg.n++];
+    d.U = p.U[i];
+    d.P = reinterpret_cast<uint4*>((char*)ws + p.off[i]);
+    d.d_in = p.d_in[i];
+    if (pg.n == kMaxGroup || i + 1 == p.U.size()) {
+      hipError_t e = launch_pack(pg, st);
+      if (e != hipSuccess) return hip_fail(e, "pack launch");
+      pg.n = 0;
+    }
+  }
+  return GIFT_OK;
 }
 
 gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
@@ -130,10 +182,10 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
       if (f.d_in != L.d_in)
         return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor d_in %d != layer d_in %lld", i,
                     f.d_in, (long long)L.d_in);
-      if (L.d_in < 64 || L.d_in % 16)
-        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: whitening needs d_in >= 64, %% 16 == 0",
+      if (L.d_in < 64 || L.d_in % 32)
+        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: whitening needs d_in >= 64, %% 32 == 0",
                     i);
-      if (!f.U || !f.coef || !aligned16(f.U) || !aligned16(f.coef))
+      if (!f.U || !f.coef || !aligned16(f.U) || !aligned16(f.coef) || !aligned16(f.packs))
         return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor U/coef NULL or misaligned", i);
     }
   }
@@ -146,8 +198,10 @@ template <class Pick, class Launch>
 gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void* ws,
                         uint32_t* flags, double* out, Pick pick, int (*tiles)(const gift_layer&),
                         Launch launch) {
-  // workspace offsets in layer order (independent of the chunking)
-  std::vector<size_t> off(n + 1, 0);
+  // workspace: operand packs first, then per-layer slices in layer order
+  // (independent of the chunking)
+  const Packs packs = plan_packs(layers, n, op);
+  std::vector<size_t> off(n + 1, packs.bytes);
   for (int i = 0; i < n; ++i) off[i + 1] = off[i] + layer_ws(layers[i], op, block).total();
   GroupDev g{};
   g.flags = flags;
@@ -178,6 +232,8 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     if (whitened(L, op)) {
       d.U = L.factor->U;
       d.coef = L.factor->coef;
+      d.P = L.factor->packs ? static_cast<const uint4*>(L.factor->packs)
+                            : reinterpret_cast<const uint4*>((char*)ws + packs.find(L.factor->U));
     }
     d.cbuf = lw.cbuf ? (float*)base : nullptr;
     base += align_up(lw.cbuf);
@@ -249,6 +305,8 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
   s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Whiten, block));
   if (s != GIFT_OK) return s;
   hipStream_t st = (hipStream_t)stream;
+  s = run_packs(plan_packs(layers, n_layers, Op::Whiten), ws, st);
+  if (s != GIFT_OK) return s;
   for (int wgrp = 0; wgrp < 2; ++wgrp) {
     const bool white = wgrp == 0;
     bool any_w = false;
@@ -278,10 +336,13 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
   s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Dequant, block));
   if (s != GIFT_OK) return s;
   hipStream_t st = (hipStream_t)stream;
+  s = run_packs(plan_packs(layers, n_layers, Op::Dequant), ws, st);
+  if (s != GIFT_OK) return s;
   for (int wgrp = 0; wgrp < 2; ++wgrp) {
     const bool white = wgrp == 0;
     auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
-    s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles_rows,
+    s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick,
+                    white ? tiles_rows : tiles_flat,
                     [&](const GroupDev& g, int) { return launch_dequant(g, block, white, st); });
     if (s != GIFT_OK) return s;
   }
@@ -333,6 +394,38 @@ gift_status gift_refresh_factor(const void* X, int x_dtype, int64_t n_tokens,
   return refresh_factor(X, x_dtype, n_tokens, f, damp_eps, damping_mode, sketch_width,
                         power_steps, seed, sketch, A_out, ws, ws_bytes, (hipStream_t)stream,
                         &t_err);
+}
+
+size_t gift_factor_pack_bytes(int64_t d_in) { return d_in > 0 ? pack_bytes(d_in) : 0; }
+
+gift_status gift_prepare_factor(const gift_factor* f, void* stream) {
+  if (!f || !f->U || !f->packs) return fail(GIFT_ERR_INVALID_ARG, "factor, U or packs is NULL");
+  if (!aligned16(f->U) || !aligned16(f->packs))
+    return fail(GIFT_ERR_INVALID_ARG, "U / packs must be 16-byte aligned");
+  if (f->rank != kRank) return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be 32");
+  if (f->d_in < 64 || f->d_in % 32 || f->d_in > kMaxDim)
+    return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "d_in must be >= 64 and a multiple of 32");
+  PackGroup pg{};
+  pg.n = 1;
+  pg.f[0].U = f->U;
+  pg.f[0].P = static_cast<uint4*>(f->packs);
+  pg.f[0].d_in = f->d_in;
+  hipError_t e = launch_pack(pg, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return GIFT_OK;
+}
+
+gift_status gift_refresh_factors(const gift_refresh_input* inputs, int n, float damp_eps,
+                                 int damping_mode, int sketch_width, int power_steps, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return refresh_factors(inputs, n, damp_eps, damping_mode, sketch_width, power_steps, ws,
+                         ws_bytes, (hipStream_t)stream, &t_err);
+}
+
+size_t gift_refresh_group_workspace_bytes(const gift_refresh_input* inputs, int n,
+                                          int sketch_width) {
+  if (!inputs || n <= 0) return 0;
+  return refresh_group_workspace_bytes(inputs, n, sketch_width);
 }
 
 gift_status gift_draw_sketch(float* out, int64_t d_in, int width, uint64_t seed, void* stream) {

@@ -132,6 +132,7 @@ struct LayerDev {
   float* Wout;
   const float* U;       // d_in x 32 (NULL: Euclidean layer)
   const float* coef;    // GIFT_COEF_COUNT
+  const uint4* P;       // workspace: the factor's split MFMA operand packs
   float* cbuf;          // workspace: d_out x 32 row coefficients
   uint32_t* part;       // workspace: one partial amax per tile
   double* part2;        // workspace: two fp64 partial sums per tile
@@ -145,6 +146,17 @@ struct GroupDev {
   uint32_t* flags;      // may be NULL
   double* out;          // roundtrip_error output, may be NULL
   LayerDev L[kMaxGroup];
+};
+
+// One factor to pack: U (d_in x 32 fp32) -> P (bf16x3 operand packs).
+struct PackDev {
+  const float* U;
+  uint4* P;
+  int d_in;
+};
+struct PackGroup {
+  int n;
+  PackDev f[kMaxGroup];
 };
 
 __device__ __forceinline__ int find_layer(const GroupDev& g, int tile) {

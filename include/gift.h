@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GIFT_ABI_VERSION 1
+#define GIFT_ABI_VERSION 2
 
 /* Rank of the factor (GIFT review, free-parameter ledger: rank 32). */
 #define GIFT_RANK 32
@@ -101,12 +101,24 @@ enum {
  * Written by gift_refresh_factor; a caller may also fill it itself.
  */
 typedef struct gift_factor {
-    int32_t d_in;     /* rows of U; 64 <= d_in, d_in % 16 == 0                 */
+    int32_t d_in;     /* rows of U; 64 <= d_in, % 16 == 0 (% 32 to whiten)    */
     int32_t rank;     /* must be GIFT_RANK                                    */
     float *U;         /* device, d_in x rank, row-major                       */
     float *theta;     /* device, rank: Ritz values, descending, >= 0          */
     float *coef;      /* device, GIFT_COEF_COUNT floats (layout above)        */
+    void *packs;      /* optional device buffer of gift_factor_pack_bytes(d_in)
+                         bytes: U split into the bf16 operand layouts of the
+                         whitening kernels.  Written by gift_refresh_factor(s)
+                         and gift_prepare_factor; it must be rewritten after
+                         U changes.  NULL: every grouped call re-packs U into
+                         its workspace.                                     */
 } gift_factor;
+
+/* Size of gift_factor.packs for a factor with d_in rows (d_in % 32 == 0). */
+size_t gift_factor_pack_bytes(int64_t d_in);
+
+/* Rewrite f->packs from f->U (for callers that fill U themselves). */
+gift_status gift_prepare_factor(const gift_factor *f, void *stream);
 
 /*
  * One layer of a grouped call.  factor == NULL marks a Euclidean layer (plain
@@ -116,7 +128,7 @@ typedef struct gift_factor {
  */
 typedef struct gift_layer {
     int64_t d_out;               /* rows of G, >= 1                            */
-    int64_t d_in;                /* columns of G, >= 1; % 4 == 0; % 16 == 0 and
+    int64_t d_in;                /* columns of G, >= 1; % 4 == 0; % 32 == 0 and
                                     >= 64 when factor != NULL; % 128 == 0 for
                                     block scaling                              */
     const float *G;              /* device, d_out x d_in fp32 gradient         */
@@ -158,6 +170,33 @@ gift_status gift_refresh_factor(const void *X, int x_dtype, int64_t n_tokens,
 
 size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens,
                                     int x_dtype, int sketch_width);
+
+/*
+ * gift_refresh_factors -- gift_refresh_factor for n inputs in one grouped
+ * pass: every launch covers all inputs, so the small serial steps of the
+ * eigensolve of different inputs run concurrently.  Per input: X (device,
+ * n_tokens x factor->d_in, x_dtype), factor (host struct, device buffers
+ * written), sketch / A_out optional as above, seed of its Philox sketch.
+ * The scalar arguments apply to every input.  The workspace is laid out per
+ * input in order; query it with gift_refresh_group_workspace_bytes.
+ */
+typedef struct gift_refresh_input {
+    const void *X;
+    int32_t x_dtype;
+    int64_t n_tokens;
+    const gift_factor *factor;   /* HOST pointer                              */
+    const float *sketch;         /* device d_in x sketch_width, or NULL       */
+    float *A_out;                /* device d_in x d_in, or NULL               */
+    uint64_t seed;
+} gift_refresh_input;
+
+gift_status gift_refresh_factors(const gift_refresh_input *inputs, int n,
+                                 float damp_eps, int damping_mode,
+                                 int sketch_width, int power_steps,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+size_t gift_refresh_group_workspace_bytes(const gift_refresh_input *inputs,
+                                          int n, int sketch_width);
 
 /*
  * gift_draw_sketch -- the Gaussian sketch gift_refresh_factor draws when it

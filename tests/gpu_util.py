@@ -26,9 +26,12 @@ def upload_factor(f):
     coef[fg.COEF_SIGMA2_TAIL] = f.sigma2_tail
     coef[fg.COEF_DW:fg.COEF_DW + fg.RANK] = f.d_w
     coef[fg.COEF_DU:fg.COEF_DU + fg.RANK] = f.d_u
-    return fg.Factor(f.d_in, U=torch.from_numpy(np.ascontiguousarray(f.U, dtype=np.float32)).to(DEV),
-                     theta=torch.from_numpy(np.asarray(f.theta, dtype=np.float32)).to(DEV),
-                     coef=torch.from_numpy(coef).to(DEV))
+    df = fg.Factor(f.d_in, U=torch.from_numpy(np.ascontiguousarray(f.U, dtype=np.float32)).to(DEV),
+                   theta=torch.from_numpy(np.asarray(f.theta, dtype=np.float32)).to(DEV),
+                   coef=torch.from_numpy(coef).to(DEV))
+    if df.packs is not None:
+        fg.gift_prepare_factor(df)
+    return df
 
 
 def factor_host(df):

@@ -178,3 +178,30 @@ def test_full_block_factors(block_inputs):
         f_orc = og.refresh_factor(Xh, omega.numpy().astype(np.float64), A=A_orc)
         P = np.random.default_rng(k).standard_normal((32, spec.d_in))
         _check_factor(f_dev, f_orc, P)
+
+
+def test_grouped_refresh_matches_oracle_and_writes_packs(block_inputs):
+    """All four block inputs plus one fp32 input in one grouped call; each
+    factor against the oracle, and the operand packs the refresh writes equal
+    gift_prepare_factor's."""
+    say("grouped refresh 5 inputs")
+    items, ref = [], []
+    for k, (spec, inp) in enumerate(block_inputs):
+        omega = synth.gaussian_sketch(spec.d_in, 64, seed=950 + k)
+        f = fg.Factor(spec.d_in)
+        items.append(dict(X=inp["X"].to(DEV), factor=f, sketch=omega.to(DEV)))
+        ref.append((inp["X"].float().numpy(), omega.numpy().astype(np.float64)))
+    spec32 = synth.InputSpec("x32", 512, 4096, 1.5, bf16=False)
+    inp32 = synth.draw_input(spec32, seed=961)
+    om32 = synth.gaussian_sketch(512, 64, seed=962)
+    items.append(dict(X=inp32["X"].to(DEV), factor=fg.Factor(512), sketch=om32.to(DEV)))
+    ref.append((inp32["X"].numpy(), om32.numpy().astype(np.float64)))
+    fg.gift_refresh_factors(items)
+    torch.cuda.synchronize()
+    for k, (it, (Xh, om)) in enumerate(zip(items, ref)):
+        f_orc = og.refresh_factor(Xh, om)
+        P = np.random.default_rng(20 + k).standard_normal((16, Xh.shape[1]))
+        _check_factor(it["factor"], f_orc, P)
+        packs = it["factor"].packs.clone()
+        fg.gift_prepare_factor(it["factor"])
+        assert torch.equal(packs, it["factor"].packs)

@@ -288,3 +288,23 @@ def test_full_block_grouped_parity(block_1024, block):
         assert rel_fro(gh, ref) <= TOL, l.name
         e, gs = og.error_sums(G, gh)
         assert abs(err[i, 0] - e) <= 1e-12 * e
+
+
+def test_factor_packs_and_workspace_packing_agree():
+    """A factor carrying its operand packs and one without (packed into the
+    workspace on every call) give identical codes and reconstructions."""
+    say("packs vs workspace packing")
+    inp, f = _factor_for(512, seed=71)
+    G = _gradient(100, inp, seed=72)
+    with_p = upload_factor(f)
+    without = fg.Factor(512, U=with_p.U, theta=with_p.theta, coef=with_p.coef, packs=False)
+    assert without.packs is None
+    for block in (False, True):
+        sc = fg.SCALE_BLOCK128 if block else fg.SCALE_TENSOR
+        La = fg.Layer(to_dev(G), factor=with_p, block128=block)
+        Lb = fg.Layer(to_dev(G), factor=without, block128=block)
+        for L in (La, Lb):
+            fg.gift_whiten_quantize([L], scaling=sc)
+            fg.gift_dequant_unwhiten([L], scaling=sc)
+        assert np.array_equal(host(La.q), host(Lb.q))
+        assert np.array_equal(host(La.G_hat), host(Lb.G_hat))
