@@ -16,7 +16,8 @@ hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool wr
 hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s);
 hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
-int row_tiles(int64_t d_out);
+int row_blocks(int64_t d_out);
+int col_groups(int64_t d_in, bool block);
 int flat_tiles(int64_t n);
 size_t pack_bytes(int64_t d_in);
 
@@ -70,28 +71,40 @@ bool whitened(const gift_layer& L, Op op) {
 
 // Per-layer workspace needs of one grouped op.
 struct LayerWs {
-  size_t cbuf = 0, part = 0, part2 = 0;
-  size_t total() const { return align_up(cbuf) + align_up(part) + align_up(part2); }
+  size_t cbuf = 0, part = 0, part2 = 0, amax = 0;
+  size_t total() const {
+    return align_up(cbuf) + align_up(part) + align_up(part2) + align_up(amax);
+  }
 };
+
+// tiles of a whitened layer's row kernels: row blocks x column groups
+int row_tiles(const gift_layer& L, bool block) {
+  return row_blocks(L.d_out) * col_groups(L.d_in, block);
+}
 
 LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
   LayerWs w;
   const int64_t n = L.d_out * L.d_in;
+  const size_t cpart = L.factor ? (size_t)col_groups(L.d_in, block) * L.d_out * kRank * sizeof(float)
+                                : 0;
   switch (op) {
     case Op::Whiten:
-      if (!block) {
-        if (L.factor) {
-          w.cbuf = (size_t)L.d_out * kRank * sizeof(float);
-          w.part = (size_t)row_tiles(L.d_out) * sizeof(uint32_t);
-        } else {
-          w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
-        }
+      if (L.factor) {
+        w.cbuf = cpart;
+        if (!block) w.amax = sizeof(uint32_t);
+      } else if (!block) {
+        w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
+        w.amax = sizeof(uint32_t);
       }
       break;
     case Op::Euclid:
-      if (!block) w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
+      if (!block) {
+        w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
+        w.amax = sizeof(uint32_t);
+      }
       break;
     case Op::Dequant:
+      if (L.factor) w.cbuf = cpart;
       break;
     case Op::Error:
       w.part2 = (size_t)flat_tiles(n) * 2 * sizeof(double);
@@ -194,10 +207,9 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
 
 // Walk the layers selected by `pick` in chunks of kMaxGroup, filling the
 // descriptors (workspace slices in layer order) and calling `launch`.
-template <class Pick, class Launch>
+template <class Pick, class Tiles, class Launch>
 gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void* ws,
-                        uint32_t* flags, double* out, Pick pick, int (*tiles)(const gift_layer&),
-                        Launch launch) {
+                        uint32_t* flags, double* out, Pick pick, Tiles tiles, Launch launch) {
   // workspace: operand packs first, then per-layer slices in layer order
   // (independent of the chunking)
   const Packs packs = plan_packs(layers, n, op);
@@ -240,8 +252,11 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     d.part = lw.part ? (uint32_t*)base : nullptr;
     base += align_up(lw.part);
     d.part2 = lw.part2 ? (double*)base : nullptr;
+    base += align_up(lw.part2);
+    d.amax = lw.amax ? (uint32_t*)base : nullptr;
     d.d_out = L.d_out;
     d.d_in = L.d_in;
+    d.ngrp = whitened(L, op) ? col_groups(L.d_in, block) : 1;
     d.n_tiles = tiles(L);
     d.tile_begin = g.total_tiles;
     g.total_tiles += d.n_tiles;
@@ -254,7 +269,6 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
   return flush();
 }
 
-int tiles_rows(const gift_layer& L) { return row_tiles(L.d_out); }
 int tiles_flat(const gift_layer& L) { return flat_tiles(L.d_out * L.d_in); }
 
 gift_status check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -313,6 +327,7 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
     for (int i = 0; i < n_layers; ++i)
       if ((layers[i].factor != nullptr) == white && layers[i].W_out) any_w = true;
     auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
+    auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L, block); };
     if (white)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
@@ -341,8 +356,10 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
   for (int wgrp = 0; wgrp < 2; ++wgrp) {
     const bool white = wgrp == 0;
     auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
-    s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick,
-                    white ? tiles_rows : tiles_flat,
+    auto tiles = [&](const gift_layer& L) {
+      return white ? row_tiles(L, block) : tiles_flat(L);
+    };
+    s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles,
                     [&](const GroupDev& g, int) { return launch_dequant(g, block, white, st); });
     if (s != GIFT_OK) return s;
   }

@@ -133,11 +133,13 @@ struct LayerDev {
   const float* U;       // d_in x 32 (NULL: Euclidean layer)
   const float* coef;    // GIFT_COEF_COUNT
   const uint4* P;       // workspace: the factor's split MFMA operand packs
-  float* cbuf;          // workspace: d_out x 32 row coefficients
-  uint32_t* part;       // workspace: one partial amax per tile
+  float* cbuf;          // workspace: ngrp x d_out x 32 partial row coefficients
+  uint32_t* part;       // workspace: one partial amax per tile (Euclidean)
+  uint32_t* amax;       // workspace: the layer's amax as |x| bits
   double* part2;        // workspace: two fp64 partial sums per tile
   int64_t d_out, d_in;
   int tile_begin, n_tiles;
+  int ngrp;             // column groups (row kernels)
 };
 
 struct GroupDev {
