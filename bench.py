@@ -1,26 +1,32 @@
 """Benchmark of the GIFT FP8 gradient round trip on one MI355X.
 
-Workload: one Llama-style block at hidden 1024 -- q, k, v, o (1024 x 1024),
-gate and up (2816 x 1024), down (1024 x 2816) fp32 weight gradients, 8192
-bf16 activation tokens per distinct input (attention in, o in, MLP in,
-down in) with a power-law spectrum of exponent 1.5; rank-32 factors; all 7
-matrices whitened; per-tensor E4M3.
+Default workload (the metric's configuration): one Llama-style block at
+hidden 1024 -- q, k, v, o (1024 x 1024), gate and up (2816 x 1024), down
+(1024 x 2816) fp32 weight gradients, 8192 bf16 activation tokens per
+distinct input (attention in, o in, MLP in, down in) with a power-law
+spectrum of exponent 1.5; rank-32 factors; all 7 matrices whitened;
+per-tensor E4M3.
 
-One step = the per-step path of GIFT over the block: the grouped
-whiten + quantize of the 7 gradients and the grouped dequantize + un-whiten,
-with the factor refresh of the 4 inputs run inside the timed loop every 50
-steps (the paper's refresh interval), so it is amortized exactly as in
-training.  Each step takes the next gradient set from a ring of resident
-sets whose footprint is several times the 256 MB Infinity Cache, so every
-step reads its gradients from HBM.  Inputs are resident in HBM before the
-timed region.  One JSON line on stdout.
+One step = the per-step path of GIFT over the workload: the grouped
+whiten + quantize of the whitened gradients, the grouped dequantize +
+un-whiten, the Euclidean round trip of the layers not selected (none in the
+default workload), and the grouped factor refresh of every input run inside
+the timed loop every 50 steps (the paper's refresh interval), so it is
+amortized exactly as in training.  Each step takes the next gradient set
+from a ring of resident sets whose footprint is several times the 256 MB
+Infinity Cache, so the gradients come from HBM.  Inputs are resident before
+the timed region.  One JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+    python bench.py --workload stack300m     # 24 blocks + embed/head, top-8 by rho
+    python bench.py --workload stack600m     # 24 blocks at 1536/4096, 16384 tokens
+    python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
 """
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -28,7 +34,6 @@ import time
 METRIC = ("GB/s of fp32 gradient through whiten→FP8→unwhiten (% HBM peak); "
           "rel. error vs Euclid")
 HBM_PEAK_GBS = 8000.0
-VALU_F32_PEAK_TFLOPS = 78.6     # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 REFRESH_EVERY = 50
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,10 +44,19 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="block1024",
+                   choices=["block1024", "stack300m", "stack600m"])
     p.add_argument("--ring", type=int, default=4, help="resident gradient sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--study", default=None, choices=["staleness"])
+    p.add_argument("--blocks", type=int, default=1)
+    p.add_argument("--hidden", type=int, default=4096)
+    p.add_argument("--mlp", type=int, default=11008)
+    p.add_argument("--tokens", type=int, default=16384)
+    p.add_argument("--angle", type=float, default=0.02)
+    p.add_argument("--study-steps", type=int, default=50)
     return p.parse_args()
 
 
@@ -72,23 +86,58 @@ def load_traffic(kernel, src_hash, elems):
     return t.get("hbm_bytes_per_launch")
 
 
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def build_workload(args):
+    import synth
+    if args.workload == "block1024":
+        w = synth.llama_block(hidden=1024, mlp=2816, tokens=8192, exponent=1.5)
+        return w, None, args.ring
+    if args.workload == "stack300m":
+        w = synth.llama_stack(24, 1024, 2816, 8192, exponent_range=(1.0, 2.0), vocab=32000)
+        return w, 8, 1
+    w = synth.llama_stack(24, 1536, 4096, 16384, exponent=1.5)
+    return w, None, 1
+
+
+def describe(args, w, select_k, ring):
+    if args.workload == "block1024":
+        return ("%s: q,k,v,o 1024x1024, gate/up 2816x1024, down 1024x2816 fp32 gradients; 8192 "
+                "bf16 tokens per input, spectrum i^-1.5; rank 32; per-tensor E4M3; refresh every "
+                "%d steps; ring of %d gradient sets" % (w.name, REFRESH_EVERY, ring))
+    if args.workload == "stack300m":
+        return ("%s: 24 Llama blocks (hidden 1024, MLP 2816) + 32000x1024 embedding and head "
+                "(Euclidean); 8192 bf16 tokens per input, per-input spectrum exponent ~U[1,2]; "
+                "GIFT on the top-%d layers by theta_1/tr(A), the rest Euclidean; per-tensor E4M3; "
+                "refresh of all 96 inputs every %d steps" % (w.name, select_k, REFRESH_EVERY))
+    return ("%s: 24 Llama blocks (hidden 1536, MLP 4096); 16384 bf16 tokens per input, spectrum "
+            "i^-1.5; all 168 layers whitened; per-tensor E4M3; refresh of all 96 inputs every "
+            "%d steps" % (w.name, REFRESH_EVERY))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: the GIFT path here has no inter-GPU part "
               "(the collective is out of scope); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.study == "staleness":
+        print(json.dumps(staleness_study(args)), flush=True)
+        return
 
     import numpy as np
     import torch
 
     import synth
     import fac_whitening_gift_amd as fg
+    from fac_whitening_gift_amd.select import select_layers
 
     fg.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.llama_block(hidden=1024, mlp=2816, tokens=8192, exponent=1.5)
+    w, select_k, ring_n = build_workload(args)
     elems = w.gradient_elements
     grad_bytes = 4 * elems
     log(args, "workload %s: %d layers, %.1f M gradient elements" %
@@ -99,197 +148,201 @@ def main():
     for k, spec in enumerate(w.inputs):
         inputs[spec.name] = synth.draw_input(spec, seed=1000 + k, device=dev, as_bf16=True)
         factors[spec.name] = fg.Factor(spec.d_in, device=dev)
-    ring = []
-    for r in range(args.ring):
-        layers = []
-        for i, l in enumerate(w.layers):
-            inp = inputs[l.input]
-            G = synth.draw_gradient(l.d_out, inp["Q"], inp["ev"], seed=5000 + 100 * r + i,
-                                    device=dev)
-            layers.append(fg.Layer(G, factor=factors[l.input]))
-        ring.append(layers)
-    items = [dict(X=inputs[spec.name]["X"], factor=factors[spec.name], seed=0)
-             for spec in w.inputs]
-    ws_ref = torch.empty(fg.gift_refresh_group_workspace_bytes(items), dtype=torch.uint8,
-                         device=dev)
-    nb_w = max(fg.gift_group_workspace_bytes(0, ring[0], fg.SCALE_TENSOR), 256)
-    ws_w = torch.empty(nb_w, dtype=torch.uint8, device=dev)
-    nb_e = max(fg.gift_group_workspace_bytes(2, ring[0], fg.SCALE_TENSOR), 256)
-    ws_e = torch.empty(nb_e, dtype=torch.uint8, device=dev)
-    nb_d = max(fg.gift_group_workspace_bytes(1, ring[0], fg.SCALE_TENSOR), 256)
-    ws_d = torch.empty(nb_d, dtype=torch.uint8, device=dev)
-    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    items = [dict(X=inputs[s.name]["X"], factor=factors[s.name], seed=0) for s in w.inputs]
+    ws_ref = torch.empty(max(fg.gift_refresh_group_workspace_bytes(items), 256),
+                         dtype=torch.uint8, device=dev)
 
     def refresh_all(seed):
         for k, it in enumerate(items):
             it["seed"] = seed + k
         fg.gift_refresh_factors(items, ws=ws_ref)
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     refresh_all(1)
     torch.cuda.synchronize()
+    layer_factor = [factors[l.input] if l.input is not None else None for l in w.layers]
+    if select_k is None:
+        selected = [i for i, f in enumerate(layer_factor) if f is not None]
+    else:
+        selected = select_layers(layer_factor, select_k)
+    sel = set(selected)
+    log(args, "whitened layers: %s" % [w.layers[i].name for i in selected])
+
+    ring = []
+    for r in range(ring_n):
+        gl, el = [], []
+        for i, l in enumerate(w.layers):
+            if l.input is not None:
+                inp = inputs[l.input]
+                G = synth.draw_gradient(l.d_out, inp["Q"], inp["ev"], seed=5000 + 1000 * r + i,
+                                        device=dev)
+            else:
+                G = synth.draw_isotropic_gradient(l.d_out, l.d_in, seed=5000 + 1000 * r + i,
+                                                  device=dev)
+            if i in sel:
+                gl.append(fg.Layer(G, factor=layer_factor[i]))
+            else:
+                el.append(fg.Layer(G))
+        ring.append((gl, el))
+    gl0, el0 = ring[0]
+
+    def ws_for(op, layers, scaling=fg.SCALE_TENSOR):
+        nb = fg.gift_group_workspace_bytes(op, layers, scaling) if layers else 0
+        return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+    ws_w, ws_d, ws_e = ws_for(0, gl0), ws_for(1, gl0), ws_for(2, el0)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(s, timed):
-        layers = ring[s % len(ring)]
+        gl, el = ring[s % len(ring)]
         if s % REFRESH_EVERY == 0:
             refresh_all(7 * s + 1)
+        marks = [ev(), ev(), ev()] if timed else None
         if timed:
-            e0, e1, e2 = ev(), ev(), ev()
-            e0.record()
-            fg.gift_whiten_quantize(layers, flags=flags, ws=ws_w)
-            e1.record()
-            fg.gift_dequant_unwhiten(layers, ws=ws_d)
-            e2.record()
-            return e0, e1, e2
-        fg.gift_whiten_quantize(layers, flags=flags, ws=ws_w)
-        fg.gift_dequant_unwhiten(layers, ws=ws_d)
-        return None
+            marks[0].record()
+        if gl:
+            fg.gift_whiten_quantize(gl, flags=flags, ws=ws_w)
+        if timed:
+            marks[1].record()
+        if gl:
+            fg.gift_dequant_unwhiten(gl, ws=ws_d)
+        if el:
+            fg.gift_euclid_fp8_roundtrip(el, flags=flags, ws=ws_e)
+        if timed:
+            marks[2].record()
+        return marks
 
     for s in range(args.warmup):
         step(s + 1, False)          # warm-up steps never hit the refresh slot
     torch.cuda.synchronize()
     log(args, "timing %d steps" % args.steps)
     marks = []
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         marks.append(step(s, True))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     t_wq = np.array([a.elapsed_time(b) for a, b, c in marks]) * 1e-3
-    t_du = np.array([b.elapsed_time(c) for a, b, c in marks]) * 1e-3
     value = grad_bytes * args.steps / elapsed / 1e9
     ms_per_step = elapsed / args.steps * 1e3
 
-    # ---- refresh on its own ------------------------------------------------
-    r0, r1 = ev(), ev()
-    r0.record()
-    for _ in range(3):
-        refresh_all(11)
-    r1.record()
-    torch.cuda.synchronize()
-    refresh_ms = r0.elapsed_time(r1) / 3
-    syrk_flops = sum(2.0 * s.tokens * s.d_in * s.d_in for s in w.inputs)
-
-    # ---- Euclidean baseline and 1x128 variant (same ring) -------------------
-    def timed_loop(fn, n):
-        es = []
-        for s in range(n):
-            a, b = ev(), ev()
-            a.record()
-            fn(ring[s % len(ring)])
-            b.record()
-            es.append((a, b))
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) for a, b in es]) * 1e-3
-
-    t_eu = timed_loop(lambda L: fg.gift_euclid_fp8_roundtrip(L, ws=ws_e), 20)
-    ring_b = [[fg.Layer(L.G, factor=L.factor, block128=True) for L in layers] for layers in ring]
-    nb_b = max(fg.gift_group_workspace_bytes(0, ring_b[0], fg.SCALE_BLOCK128),
-               fg.gift_group_workspace_bytes(1, ring_b[0], fg.SCALE_BLOCK128), 256)
-    ws_b = torch.empty(nb_b, dtype=torch.uint8, device=dev)
-    t_b = []
-    for s in range(20):
+    # ---- the pieces on their own -------------------------------------------
+    def timed(fn, n=10):
         a, b = ev(), ev()
+        fn()
+        torch.cuda.synchronize()
         a.record()
-        fg.gift_whiten_quantize(ring_b[s % len(ring_b)], scaling=fg.SCALE_BLOCK128, ws=ws_b)
-        fg.gift_dequant_unwhiten(ring_b[s % len(ring_b)], scaling=fg.SCALE_BLOCK128, ws=ws_b)
+        for i in range(n):
+            fn()
         b.record()
-        t_b.append((a, b))
-    torch.cuda.synchronize()
-    t_b = np.array([a.elapsed_time(b) for a, b in t_b]) * 1e-3
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3
 
-    # ---- quality: relative error vs Euclidean FP8 ---------------------------
-    layers = ring[0]
-    fg.gift_whiten_quantize(layers, ws=ws_w)
-    fg.gift_dequant_unwhiten(layers, ws=ws_d)
-    err_g = fg.gift_roundtrip_error(layers).cpu().numpy()
-    eu_layers = [fg.Layer(L.G) for L in layers]
-    fg.gift_euclid_fp8_roundtrip(eu_layers, ws=ws_e)
-    err_e = fg.gift_roundtrip_error(eu_layers).cpu().numpy()
-    m1_g = float(np.sqrt(err_g[:, 0].sum() / err_g[:, 1].sum()))
-    m1_e = float(np.sqrt(err_e[:, 0].sum() / err_e[:, 1].sum()))
-    # K-FAC-metric error: ||(G^-G) S|| / ||G S||, S = (A + lambda_floor I)^-1/2 from
-    # the exact covariance (measurement only; fp64 torch on the device)
-    num_g = num_e = den = 0.0
-    S_cache = {}
-    for L, E, l in zip(layers, eu_layers, w.layers):
-        if l.input not in S_cache:
-            X = inputs[l.input]["X"].double()
-            A = X.T @ X / X.shape[0]
-            lam = 1e-3 * torch.trace(A) / A.shape[0]
-            ev_, V = torch.linalg.eigh(A)
-            S_cache[l.input] = (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
-        S = S_cache[l.input]
-        G = L.G.double()
-        num_g += float(torch.linalg.norm((L.G_hat.double() - G) @ S) ** 2)
-        num_e += float(torch.linalg.norm((E.G_hat.double() - G) @ S) ** 2)
-        den += float(torch.linalg.norm(G @ S) ** 2)
-    m2_g, m2_e = float(np.sqrt(num_g / den)), float(np.sqrt(num_e / den))
+    refresh_s = timed(lambda: refresh_all(11), 3)
+    syrk_flops = sum(2.0 * s.tokens * s.d_in * s.d_in for s in w.inputs)
+    t_whiten = float(np.median(t_wq))
+    t_dq = timed(lambda: fg.gift_dequant_unwhiten(gl0, ws=ws_d)) if gl0 else 0.0
+    t_eu = timed(lambda: fg.gift_euclid_fp8_roundtrip(el0, ws=ws_e)) if el0 else 0.0
+    gift_elems = sum(L.d_out * L.d_in for L in gl0)
+    all_eu = [fg.Layer(L.G) for L in gl0 + el0]
+    ws_all = ws_for(2, all_eu)
+    t_eu_all = timed(lambda: fg.gift_euclid_fp8_roundtrip(all_eu, ws=ws_all))
+    blk = [fg.Layer(L.G, factor=L.factor, block128=True) for L in gl0]
+    ws_b = ws_for(0, blk, fg.SCALE_BLOCK128)
+    ws_b2 = ws_for(1, blk, fg.SCALE_BLOCK128)
+    t_b = timed(lambda: (fg.gift_whiten_quantize(blk, scaling=fg.SCALE_BLOCK128, ws=ws_b),
+                         fg.gift_dequant_unwhiten(blk, scaling=fg.SCALE_BLOCK128, ws=ws_b2))) \
+        if blk else 0.0
+    del all_eu, blk
+
+    # ---- quality: relative error vs Euclidean FP8 on the whitened layers -----
+    quality = quality_report(gl0, w, selected, inputs, ws_w, ws_d) if gl0 else None
 
     # ---- roofline of the dominant launch -------------------------------------
     src = kernel_source_hash()
-    wq, du = float(np.mean(t_wq)), float(np.mean(t_du))
-    if du >= wq:
-        kname, t_k, alg_bytes, alg_flops = "dequant_unwhiten", du, 5.0 * elems, 128.0 * elems
+    if t_dq >= t_whiten:
+        kname, t_k = "dequant_unwhiten", t_dq
     else:
-        kname, t_k, alg_bytes, alg_flops = "whiten_quantize", wq, 5.0 * elems, 192.0 * elems
-    gbs = alg_bytes / t_k / 1e9
-    tfl = alg_flops / t_k / 1e12
-    traffic = load_traffic(kname, src, elems)
-    if tfl / VALU_F32_PEAK_TFLOPS > gbs / HBM_PEAK_GBS:
-        roof = {"bound": "alu", "achieved": round(tfl, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tfl / VALU_F32_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = traffic
-    roof["kernel"] = kname
-    roof["hbm_achieved_gbs"] = round(gbs, 1)
-    roof["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
-    roof["launch_ms"] = round(t_k * 1e3, 4)
-    roof["source_hash"] = src
+        kname, t_k = "whiten_quantize", t_whiten
+    alg_bytes = 5.0 * gift_elems                 # 4 B of fp32 + 1 B of code per element
+    gbs = alg_bytes / t_k / 1e9 if t_k > 0 else 0.0
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(kname, src, gift_elems), "kernel": kname,
+            "launch_ms": round(t_k * 1e3, 4), "source_hash": src}
 
-    # ---- CPU baseline: the oracle on the host ------------------------------
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layers, w, args)
+    if not args.no_cpu_baseline and args.workload == "block1024":
+        cpu = cpu_baseline(gl0, args)
 
-    rt = wq + du
+    rt = t_whiten + t_dq
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: q,k,v,o 1024x1024, gate/up 2816x1024, down 1024x2816 fp32 "
-                               "gradients; 8192 bf16 tokens per input, spectrum i^-1.5; rank 32; "
-                               "per-tensor E4M3; refresh every %d steps; ring of %d gradient "
-                               "sets" % (w.name, REFRESH_EVERY, args.ring),
-                   "layers": len(w.layers), "gradient_elements": elems},
+        "config": {"workload": describe(args, w, select_k, ring_n), "layers": len(w.layers),
+                   "whitened_layers": len(gl0), "gradient_elements": elems},
         "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
-        "roundtrip_only_gbps": round(grad_bytes / rt / 1e9, 2),
-        "whiten_quantize_ms": round(wq * 1e3, 4), "dequant_unwhiten_ms": round(du * 1e3, 4),
-        "layers_per_s": round(len(w.layers) / rt, 1),
-        "refresh_ms_4_inputs": round(refresh_ms, 3),
-        "refresh_syrk_mfma_frac_lower_bound": round(syrk_flops / (refresh_ms * 1e-3) / 1e12 /
+        "roundtrip_only_gbps": round(4 * gift_elems / rt / 1e9, 2) if rt > 0 else None,
+        "whiten_quantize_ms": round(t_whiten * 1e3, 4), "dequant_unwhiten_ms": round(t_dq * 1e3, 4),
+        "euclid_rest_ms": round(t_eu * 1e3, 4),
+        "layers_per_s": round(len(w.layers) * args.steps / elapsed, 1),
+        "refresh_ms": round(refresh_s * 1e3, 3), "refresh_inputs": len(w.inputs),
+        "refresh_syrk_mfma_frac_lower_bound": round(syrk_flops / refresh_s / 1e12 /
                                                      MFMA_BF16_PEAK_TFLOPS, 4),
-        "euclid_roundtrip_gbps": round(grad_bytes / float(np.mean(t_eu)) / 1e9, 2),
-        "block128_roundtrip_gbps": round(grad_bytes / float(np.mean(t_b)) / 1e9, 2),
-        "quality": {"m1_gift": round(m1_g, 5), "m1_euclid": round(m1_e, 5),
-                    "m1_ratio": round(m1_g / m1_e, 4), "m2_gift": round(m2_g, 5),
-                    "m2_euclid": round(m2_e, 5), "m2_ratio": round(m2_g / m2_e, 4),
-                    "damping": "floor+tail"},
+        "euclid_all_layers_gbps": round(grad_bytes / t_eu_all / 1e9, 2),
+        "block128_roundtrip_gbps": round(4 * gift_elems / t_b / 1e9, 2) if t_b > 0 else None,
+        "quality": quality,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(layers, w, args):
+def quality_report(gl, w, selected, inputs, ws_w, ws_d):
+    """M1 (plain relative Frobenius) from the device error sums and M2 (error
+    in the K-FAC metric of the exact sample covariance, fp64 torch on the
+    device as measurement harness) for GIFT and for Euclidean FP8 of the same
+    gradients."""
+    import numpy as np
+    import torch
+
+    import fac_whitening_gift_amd as fg
+    fg.gift_whiten_quantize(gl, ws=ws_w)
+    fg.gift_dequant_unwhiten(gl, ws=ws_d)
+    err_g = fg.gift_roundtrip_error(gl).cpu().numpy()
+    eu = [fg.Layer(L.G) for L in gl]
+    fg.gift_euclid_fp8_roundtrip(eu)
+    err_e = fg.gift_roundtrip_error(eu).cpu().numpy()
+    m1_g = float(np.sqrt(err_g[:, 0].sum() / err_g[:, 1].sum()))
+    m1_e = float(np.sqrt(err_e[:, 0].sum() / err_e[:, 1].sum()))
+    num_g = num_e = den = 0.0
+    S_cache = {}
+    for L, E, i in zip(gl, eu, selected):
+        name = w.layers[i].input
+        if name not in S_cache:
+            X = inputs[name]["X"].double()
+            A = X.T @ X / X.shape[0]
+            lam = 1e-3 * torch.trace(A) / A.shape[0]
+            ev_, V = torch.linalg.eigh(A)
+            S_cache[name] = (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
+        S = S_cache[name]
+        G = L.G.double()
+        num_g += float(torch.linalg.norm((L.G_hat.double() - G) @ S) ** 2)
+        num_e += float(torch.linalg.norm((E.G_hat.double() - G) @ S) ** 2)
+        den += float(torch.linalg.norm(G @ S) ** 2)
+    m2_g, m2_e = float(np.sqrt(num_g / den)), float(np.sqrt(num_e / den))
+    return {"m1_gift": round(m1_g, 5), "m1_euclid": round(m1_e, 5),
+            "m1_ratio": round(m1_g / m1_e, 4), "m2_gift": round(m2_g, 5),
+            "m2_euclid": round(m2_e, 5), "m2_ratio": round(m2_g / m2_e, 4),
+            "m2_reduction": round(1 - m2_g / m2_e, 4), "damping": "floor+tail"}
+
+
+def cpu_baseline(layers, args):
     """The oracle (fp64 numpy, as it stands) on the host: the same round trip
     (whiten, E4M3, dequantize, un-whiten) on the block's gradients, repeated
     until about cpu_seconds of work; GB/s of fp32 gradient."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import gift as og
@@ -297,7 +350,7 @@ def cpu_baseline(layers, w, args):
     log(args, "cpu baseline (oracle)")
     host = []
     for L in layers:
-        c = L.factor.coef.cpu().numpy().astype(np.float64)
+        c = L.factor.coef.cpu().numpy().astype("float64")
         f = og.factor_from_parts(L.factor.U.cpu().numpy(), L.factor.theta.cpu().numpy(),
                                  c[2], c[3], c[4], c[5])
         host.append((L.G.cpu().numpy(), f))
@@ -318,6 +371,94 @@ def cpu_baseline(layers, w, args):
                       "BLAS threads %d, host CPUs %d" % (passes, sum(G.nbytes for G, _ in host)
                                                          / 1e6, el, threads,
                                                          len(os.sched_getaffinity(0)))}
+
+
+# ---------------------------------------------------------------------------
+# staleness study
+# ---------------------------------------------------------------------------
+
+def staleness_study(args, device="cuda:0"):
+    """Error of the round trip as a function of steps since the last factor
+    refresh (the falsifier the GIFT review proposes: if at step 49 the stale
+    factor's error reaches Euclidean FP8's, the refresh interval is too long).
+
+    Every input's eigenbasis rotates by R(t) = V B(t*angle) V^T (all principal
+    angles exactly t*angle); at step t fresh activations X_t and gradients G_t
+    are drawn from the rotated covariance.  Methods per step: Euclidean, GIFT
+    with the factor refreshed at t = 0 (stale), GIFT refreshed at t (fresh),
+    each with per-tensor and 1x128 scaling.  M1 from the device error sums; M2
+    in the metric of the population covariance C_t (C_t^-1/2 is known in
+    closed form for the generator, so no eigensolve is needed)."""
+    import torch
+
+    import synth
+    import fac_whitening_gift_amd as fg
+
+    dev = torch.device(device)
+    w = synth.llama_stack(args.blocks, args.hidden, args.mlp, args.tokens, exponent=1.5)
+    base, rots = {}, {}
+    for k, spec in enumerate(w.inputs):
+        g = torch.Generator(device=dev).manual_seed(3000 + k)
+        base[spec.name] = synth.haar(spec.d_in, g, dev)
+        rots[spec.name] = synth.rotation_pair(spec.d_in, 4000 + k, dev)
+    stale = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
+    fresh = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
+    rows = []
+    for t in range(args.study_steps):
+        Qt, X = {}, {}
+        for k, spec in enumerate(w.inputs):
+            Qt[spec.name] = synth.rotate_input(base[spec.name], rots[spec.name], t * args.angle) \
+                if t else base[spec.name]
+            X[spec.name] = synth.draw_input(spec, seed=7000 + 100 * t + k, device=dev,
+                                            Q=Qt[spec.name], as_bf16=True)
+        if t == 0:
+            fg.gift_refresh_factors([dict(X=X[s.name]["X"], factor=stale[s.name], seed=s_i)
+                                     for s_i, s in enumerate(w.inputs)])
+        fg.gift_refresh_factors([dict(X=X[s.name]["X"], factor=fresh[s.name], seed=s_i)
+                                 for s_i, s in enumerate(w.inputs)])
+        res = {"step": t}
+        for block in (False, True):
+            sc = fg.SCALE_BLOCK128 if block else fg.SCALE_TENSOR
+            acc = {m: [0.0, 0.0, 0.0] for m in ("euclid", "stale", "fresh")}
+            den1 = 0.0
+            for i, l in enumerate(w.layers):
+                inp = X[l.input]
+                G = synth.draw_gradient(l.d_out, Qt[l.input], inp["ev"], seed=9000 + 100 * t + i,
+                                        device=dev)
+                lam = 1e-3 * float(inp["ev"].double().sum()) / l.d_in
+                Sdiag = (inp["ev"].double() + lam).rsqrt().float()
+                GS = (G @ Qt[l.input]) * Sdiag
+                den2 = float(GS.double().pow(2).sum())
+                for m, fac in (("euclid", None), ("stale", stale[l.input]),
+                               ("fresh", fresh[l.input])):
+                    L = fg.Layer(G, factor=fac, block128=block)
+                    if fac is None:
+                        fg.gift_euclid_fp8_roundtrip([L], scaling=sc)
+                    else:
+                        fg.gift_whiten_quantize([L], scaling=sc)
+                        fg.gift_dequant_unwhiten([L], scaling=sc)
+                    e = fg.gift_roundtrip_error([L]).cpu().numpy()[0]
+                    ES = ((L.G_hat - G) @ Qt[l.input]) * Sdiag
+                    acc[m][0] += float(e[0])
+                    acc[m][1] += float(ES.double().pow(2).sum())
+                    acc[m][2] += den2
+                den1 += float(e[1])
+            tag = "b128" if block else "tensor"
+            for m, (e1, e2, d2) in acc.items():
+                res["m1_%s_%s" % (m, tag)] = math.sqrt(e1 / den1)
+                res["m2_%s_%s" % (m, tag)] = math.sqrt(e2 / d2)
+        rows.append(res)
+        if not args.quiet:
+            print("[staleness] %s" % json.dumps({k: (round(v, 5) if isinstance(v, float) else v)
+                                                for k, v in res.items()}),
+                  file=sys.stderr, flush=True)
+    last = rows[-1]
+    return {"study": "staleness", "workload": w.name, "angle_rad_per_step": args.angle,
+            "steps": len(rows), "refresh_at": 0,
+            "falsified_at_last_step_m2": bool(last["m2_stale_tensor"] >= last["m2_euclid_tensor"]),
+            "falsified_at_last_step_m1": bool(last["m1_stale_tensor"] >= last["m1_euclid_tensor"]),
+            "rows": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                     for r in rows]}
 
 
 if __name__ == "__main__":

@@ -346,3 +346,30 @@ def rel_error_kfac(G, G_hat, S):
     G = np.asarray(G, dtype=np.float64)
     E = np.asarray(G_hat, dtype=np.float64) - G
     return float(np.linalg.norm(E @ S) / np.linalg.norm(G @ S))
+
+
+# --------------------------------------------------------------------------
+# selective deployment
+# --------------------------------------------------------------------------
+
+def anisotropy(f):
+    """rho = theta_1 / tr(A) of a factor: the share of the input's second
+    moment in its leading direction (reading of the pages' "numerically
+    vulnerable" layers, GIFT review referee report major comment 3)."""
+    return float(f.theta[0]) / f.trace if f.trace > 0 else 0.0
+
+
+def select_top_k(rhos, k):
+    """Indices (ascending) of the k layers with the largest rho; None marks a
+    layer that is never whitened; equal rho goes to the lower index."""
+    eligible = [i for i, r in enumerate(rhos) if r is not None]
+    chosen = []
+    for _ in range(min(max(k, 0), len(eligible))):
+        best = None
+        for i in eligible:
+            if i in chosen:
+                continue
+            if best is None or rhos[i] > rhos[best]:
+                best = i
+        chosen.append(best)
+    return sorted(chosen)

@@ -205,3 +205,27 @@ def test_grouped_refresh_matches_oracle_and_writes_packs(block_inputs):
         packs = it["factor"].packs.clone()
         fg.gift_prepare_factor(it["factor"])
         assert torch.equal(packs, it["factor"].packs)
+
+
+def test_selection_from_device_factors():
+    """rho from the device factors matches the oracle's (relative 1e-4), and so
+    does the top-k choice, on inputs with clearly different spectra."""
+    from fac_whitening_gift_amd.select import anisotropy, select_layers
+    say("selection by theta_1 / tr(A)")
+    exps = [1.0, 2.0, 1.4, 1.8, 1.2]
+    facs, rho_o = [], []
+    for k, e in enumerate(exps):
+        spec = synth.InputSpec("x%d" % k, 256, 2048, e, bf16=True)
+        inp = synth.draw_input(spec, seed=60 + k, as_bf16=True)
+        om = synth.gaussian_sketch(256, 64, seed=70 + k)
+        f = fg.Factor(256)
+        fg.gift_refresh_factor(inp["X"].to(DEV), f, sketch=om.to(DEV))
+        facs.append(f)
+        rho_o.append(og.anisotropy(og.refresh_factor(inp["X"].float().numpy(),
+                                                     om.numpy().astype(np.float64))))
+    rho_d = [anisotropy(f) for f in facs]
+    assert np.allclose(rho_d, rho_o, rtol=1e-4)
+    layer_factors = [facs[0], None, facs[1], facs[1], facs[2], facs[3], facs[4], None]
+    rhos_o = [None if f is None else rho_o[facs.index(f)] for f in layer_factors]
+    for k in (1, 2, 4, 10):
+        assert select_layers(layer_factors, k) == og.select_top_k(rhos_o, k)

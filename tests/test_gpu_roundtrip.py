@@ -160,7 +160,8 @@ def _gift_parity(G, df, block):
 @pytest.mark.parametrize("d_out,d_in,block", [(256, 512, False), (256, 512, True),
                                               (37, 512, False), (37, 512, True),
                                               (1, 64, False), (129, 128, True),
-                                              (200, 1024, False)])
+                                              (200, 1024, False), (300, 96, False),
+                                              (513, 160, False), (700, 384, True)])
 def test_gift_parity(d_out, d_in, block):
     say("gift parity %dx%d block=%s" % (d_out, d_in, block))
     inp, f = _factor_for(d_in, seed=d_in + 3)

@@ -1,0 +1,32 @@
+"""The staleness study at a small scale: the factor from step 0 loses its
+advantage as the eigenbasis rotates; a fresh factor keeps it; Euclidean FP8
+is unaffected."""
+
+import argparse
+
+import numpy as np
+import pytest
+
+import bench
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_staleness_small():
+    say("staleness study hidden 256 mlp 512, 6 steps of 0.15 rad")
+    args = argparse.Namespace(blocks=1, hidden=256, mlp=512, tokens=4096, angle=0.15,
+                              study_steps=6, quiet=True)
+    out = bench.staleness_study(args)
+    rows = out["rows"]
+    assert len(rows) == 6
+    r0, r5 = rows[0], rows[-1]
+    # at t = 0 the stale factor is the fresh one
+    assert abs(r0["m2_stale_tensor"] - r0["m2_fresh_tensor"]) <= 1e-6
+    # GIFT beats Euclid in the K-FAC metric while fresh
+    for r in rows:
+        assert r["m2_fresh_tensor"] < 0.7 * r["m2_euclid_tensor"]
+        assert r["m2_fresh_b128"] < 0.8 * r["m2_euclid_b128"]
+    # the stale factor degrades with the rotation
+    assert r5["m2_stale_tensor"] > 1.5 * r0["m2_stale_tensor"]
+    assert np.all(np.diff([r["m2_stale_tensor"] for r in rows]) > -1e-3)
