@@ -50,7 +50,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--quiet", action="store_true")
-    p.add_argument("--study", default=None, choices=["staleness"])
+    p.add_argument("--counters", action="store_true",
+                   help="for runs under hardware-counter collection: no device QR or "
+                        "eigendecomposition (host QR for the input bases, no M2 report)")
+    p.add_argument("--study", default=None, choices=["staleness", "copy"])
     p.add_argument("--blocks", type=int, default=1)
     p.add_argument("--hidden", type=int, default=4096)
     p.add_argument("--mlp", type=int, default=11008)
@@ -126,6 +129,9 @@ def main():
     if args.study == "staleness":
         print(json.dumps(staleness_study(args)), flush=True)
         return
+    if args.study == "copy":
+        print(json.dumps(copy_calibration()), flush=True)
+        return
 
     import numpy as np
     import torch
@@ -146,7 +152,8 @@ def main():
     # ---- resident inputs ---------------------------------------------------
     inputs, factors = {}, {}
     for k, spec in enumerate(w.inputs):
-        inputs[spec.name] = synth.draw_input(spec, seed=1000 + k, device=dev, as_bf16=True)
+        inputs[spec.name] = synth.draw_input(spec, seed=1000 + k, device=dev, as_bf16=True,
+                                             host_qr=args.counters)
         factors[spec.name] = fg.Factor(spec.d_in, device=dev)
     items = [dict(X=inputs[s.name]["X"], factor=factors[s.name], seed=0) for s in w.inputs]
     ws_ref = torch.empty(max(fg.gift_refresh_group_workspace_bytes(items), 256),
@@ -256,7 +263,8 @@ def main():
     del all_eu, blk
 
     # ---- quality: relative error vs Euclidean FP8 on the whitened layers -----
-    quality = quality_report(gl0, w, selected, inputs, ws_w, ws_d) if gl0 else None
+    quality = quality_report(gl0, w, selected, inputs, ws_w, ws_d) \
+        if gl0 and not args.counters else None
 
     # ---- roofline of the dominant launch -------------------------------------
     src = kernel_source_hash()
@@ -371,6 +379,32 @@ def cpu_baseline(layers, args):
                       "BLAS threads %d, host CPUs %d" % (passes, sum(G.nbytes for G, _ in host)
                                                          / 1e6, el, threads,
                                                          len(os.sched_getaffinity(0)))}
+
+
+# ---------------------------------------------------------------------------
+# copy calibration
+# ---------------------------------------------------------------------------
+
+def copy_calibration(mib=1024, reps=5, device="cuda:0"):
+    """A plain device-to-device copy of a known size (torch's copy kernel),
+    for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run: the
+    counters' reading for this kernel divided by the bytes it must move."""
+    import torch
+
+    n = mib * 2 ** 20 // 4
+    a = torch.randn(n, device=device)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    return {"study": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": reps + 1,
+            "us_per_copy": round(t * 1e6, 2), "GBps": round(8 * n / t / 1e9, 1)}
 
 
 # ---------------------------------------------------------------------------

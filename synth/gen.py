@@ -130,10 +130,18 @@ def _gen(seed, device):
     return g
 
 
-def haar(d, gen, device="cpu", dtype=torch.float32):
-    """Haar-random orthogonal d x d matrix (QR of a Gaussian, sign-fixed)."""
+def haar(d, gen, device="cpu", dtype=torch.float32, host_qr=False):
+    """Haar-random orthogonal d x d matrix (QR of a Gaussian, sign-fixed).
+
+    host_qr: draw the Gaussian on `device` but factor it on the host (for
+    runs under hardware-counter collection, which the device QR does not
+    survive)."""
     z = torch.randn(d, d, generator=gen, device=device, dtype=torch.float64
                     if torch.device(device).type == "cpu" else torch.float32)
+    if host_qr and torch.device(device).type != "cpu":
+        q, r = torch.linalg.qr(z.cpu().double())
+        q = q * torch.sign(torch.diagonal(r)).unsqueeze(0)
+        return q.to(device=device, dtype=dtype)
     q, r = torch.linalg.qr(z)
     q = q * torch.sign(torch.diagonal(r)).unsqueeze(0)
     return q.to(dtype)
@@ -149,7 +157,7 @@ def to_bf16_values(x):
     return x.to(torch.bfloat16).to(torch.float32)
 
 
-def draw_input(spec, seed, device="cpu", tokens=None, Q=None, as_bf16=False):
+def draw_input(spec, seed, device="cpu", tokens=None, Q=None, as_bf16=False, host_qr=False):
     """-> dict(Q, ev, X): eigenbasis, spectrum and N x d activations.
 
     X is fp32 (holding bf16 values when spec.bf16) unless as_bf16, which
@@ -158,7 +166,7 @@ def draw_input(spec, seed, device="cpu", tokens=None, Q=None, as_bf16=False):
     n = spec.tokens if tokens is None else tokens
     g = _gen(seed, device)
     if Q is None:
-        Q = haar(spec.d_in, g, device)
+        Q = haar(spec.d_in, g, device, host_qr=host_qr)
     ev = power_law(spec.d_in, spec.exponent, device)
     z = torch.randn(n, spec.d_in, generator=g, device=device, dtype=torch.float32)
     X = (z * ev.sqrt()) @ Q.T
