@@ -16,8 +16,10 @@ hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool wr
 hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s);
 hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
-int row_blocks(int64_t d_out);
-int col_groups(int64_t d_in, bool block);
+int64_t row_blocks(int64_t d_out);
+int col_groups(int64_t d_in);
+int frag_floats();
+int cop_bytes();
 int flat_tiles(int64_t n);
 size_t pack_bytes(int64_t d_in);
 
@@ -71,27 +73,29 @@ bool whitened(const gift_layer& L, Op op) {
 
 // Per-layer workspace needs of one grouped op.
 struct LayerWs {
-  size_t cbuf = 0, part = 0, part2 = 0, amax = 0;
+  size_t cbuf = 0, cfin = 0, part = 0, part2 = 0, amax = 0;
   size_t total() const {
-    return align_up(cbuf) + align_up(part) + align_up(part2) + align_up(amax);
+    return align_up(cbuf) + align_up(cfin) + align_up(part) + align_up(part2) + align_up(amax);
   }
 };
 
-// tiles of a whitened layer's row kernels: row blocks x column groups
-int row_tiles(const gift_layer& L, bool block) {
-  return row_blocks(L.d_out) * col_groups(L.d_in, block);
-}
+// workgroups of a whitened layer's tile kernels: row blocks x column groups
+int row_tiles(const gift_layer& L) { return (int)(row_blocks(L.d_out) * col_groups(L.d_in)); }
 
 LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
   LayerWs w;
   const int64_t n = L.d_out * L.d_in;
-  const size_t cpart = L.factor ? (size_t)col_groups(L.d_in, block) * L.d_out * kRank * sizeof(float)
-                                : 0;
+  const size_t frag = (size_t)row_blocks(L.d_out) * frag_floats() * sizeof(float);
+  const size_t cop = (size_t)row_blocks(L.d_out) * cop_bytes();
   switch (op) {
     case Op::Whiten:
       if (L.factor) {
-        w.cbuf = cpart;
-        if (!block) w.amax = sizeof(uint32_t);
+        w.cbuf = (size_t)col_groups(L.d_in) * frag;  // partial c per column group
+        w.cfin = cop;                                  // c' of every row (operand form)
+        if (!block) {  // one amax per tile, the layer amax
+          w.part = (size_t)row_tiles(L) * sizeof(uint32_t);
+          w.amax = sizeof(uint32_t);
+        }
       } else if (!block) {
         w.part = (size_t)flat_tiles(n) * sizeof(uint32_t);
         w.amax = sizeof(uint32_t);
@@ -104,7 +108,10 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
       }
       break;
     case Op::Dequant:
-      if (L.factor) w.cbuf = cpart;
+      if (L.factor) {
+        w.cbuf = (size_t)col_groups(L.d_in) * frag;
+        w.cfin = cop;
+      }
       break;
     case Op::Error:
       w.part2 = (size_t)flat_tiles(n) * 2 * sizeof(double);
@@ -225,6 +232,7 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     g.n = 0;
     g.total_tiles = 0;
+    g.total_rb = 0;
     first = -1;
     return GIFT_OK;
   };
@@ -249,6 +257,8 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     }
     d.cbuf = lw.cbuf ? (float*)base : nullptr;
     base += align_up(lw.cbuf);
+    d.cfin = lw.cfin ? (float*)base : nullptr;
+    base += align_up(lw.cfin);
     d.part = lw.part ? (uint32_t*)base : nullptr;
     base += align_up(lw.part);
     d.part2 = lw.part2 ? (double*)base : nullptr;
@@ -256,10 +266,13 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     d.amax = lw.amax ? (uint32_t*)base : nullptr;
     d.d_out = L.d_out;
     d.d_in = L.d_in;
-    d.ngrp = whitened(L, op) ? col_groups(L.d_in, block) : 1;
+    d.n_rb = row_blocks(L.d_out);
+    d.ngrp = whitened(L, op) ? col_groups(L.d_in) : 1;
     d.n_tiles = tiles(L);
     d.tile_begin = g.total_tiles;
     g.total_tiles += d.n_tiles;
+    d.rb_begin = g.total_rb;
+    if (whitened(L, op)) g.total_rb += (int)d.n_rb;
     ++g.n;
     if (g.n == kMaxGroup) {
       gift_status s = flush();
@@ -327,7 +340,7 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
     for (int i = 0; i < n_layers; ++i)
       if ((layers[i].factor != nullptr) == white && layers[i].W_out) any_w = true;
     auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
-    auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L, block); };
+    auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L); };
     if (white)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
@@ -357,7 +370,7 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
     const bool white = wgrp == 0;
     auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
     auto tiles = [&](const gift_layer& L) {
-      return white ? row_tiles(L, block) : tiles_flat(L);
+      return white ? row_tiles(L) : tiles_flat(L);
     };
     s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles,
                     [&](const GroupDev& g, int) { return launch_dequant(g, block, white, st); });

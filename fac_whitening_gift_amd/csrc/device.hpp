@@ -28,15 +28,29 @@ __device__ __forceinline__ uint32_t e4m3_nan_fix(uint32_t packed, float a, float
   return (packed & ~m) | (0x7f7f7f7fu & m);
 }
 
-// Encode four already-scaled fp32 values; byte i of the result = element i.
-__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+// Encode four already-scaled values that are not NaN (true whenever the
+// amax they were scaled by is finite); byte i of the result = element i.
+__device__ __forceinline__ uint32_t e4m3_encode4_num(float a, float b, float c, float d) {
   float ca = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
   float cb = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
   float cc = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
   float cd = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, w, true);
-  return e4m3_nan_fix((uint32_t)w, a, b, c, d);
+  return (uint32_t)w;
+}
+
+// Encode four already-scaled fp32 values, any of them possibly NaN.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+  return e4m3_nan_fix(e4m3_encode4_num(a, b, c, d), a, b, c, d);
+}
+
+// Encode with the scale of an amax: values scaled by the scale of a finite
+// amax are never NaN, so the NaN mapping is only needed for a non-finite one.
+__device__ __forceinline__ uint32_t e4m3_encode4_scaled(const float4& v, float scale,
+                                                        bool nonfinite) {
+  const float a = v.x * scale, b = v.y * scale, c = v.z * scale, d = v.w * scale;
+  return nonfinite ? e4m3_encode4(a, b, c, d) : e4m3_encode4_num(a, b, c, d);
 }
 
 __device__ __forceinline__ uint8_t e4m3_encode1(float a) {
@@ -132,19 +146,23 @@ struct LayerDev {
   float* Wout;
   const float* U;       // d_in x 32 (NULL: Euclidean layer)
   const float* coef;    // GIFT_COEF_COUNT
-  const uint4* P;       // workspace: the factor's split MFMA operand packs
-  float* cbuf;          // workspace: ngrp x d_out x 32 partial row coefficients
-  uint32_t* part;       // workspace: one partial amax per tile (Euclidean)
+  const uint4* P;       // the factor's split MFMA operand packs
+  float* cbuf;          // workspace: column-group partials of the row coefficients
+  float* cfin;          // workspace: c' of every row, split into the bf16 operand form
+  uint32_t* part;       // workspace: one partial amax per tile
   uint32_t* amax;       // workspace: the layer's amax as |x| bits
   double* part2;        // workspace: two fp64 partial sums per tile
   int64_t d_out, d_in;
+  int64_t n_rb;         // row blocks of the tile kernels
+  int ngrp;             // column groups of the tile kernels
   int tile_begin, n_tiles;
-  int ngrp;             // column groups (row kernels)
+  int rb_begin;         // first row block of the layer in the group
 };
 
 struct GroupDev {
   int n;
   int total_tiles;
+  int total_rb;         // row blocks over the group (tile kernels)
   uint32_t* flags;      // may be NULL
   double* out;          // roundtrip_error output, may be NULL
   LayerDev L[kMaxGroup];
@@ -161,11 +179,21 @@ struct PackGroup {
   PackDev f[kMaxGroup];
 };
 
+// Layer of a workgroup: all tile_begin values are read at once (one round
+// trip to the kernel arguments, not one per layer).
 __device__ __forceinline__ int find_layer(const GroupDev& g, int tile) {
   int l = 0;
-#pragma unroll 1
-  for (int i = 1; i < g.n; ++i)
-    if (tile >= g.L[i].tile_begin) l = i;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < g.n && tile >= g.L[i].tile_begin) l = i;
+  return l;
+}
+
+__device__ __forceinline__ int find_layer_rb(const GroupDev& g, int rb) {
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < g.n && rb >= g.L[i].rb_begin) l = i;
   return l;
 }
 

@@ -20,25 +20,28 @@
 // in the two 16-column result tiles of that chunk, and its result (lane l:
 // ranks 4g..4g+3 and 16+4g..+3 of row l%16) is used unchanged as the K=32
 // operand of the second product W^T = U C'^T with the rank order permuted the
-// same way.  U's two operand forms are split and packed once per call
-// (k_pack_u).
+// same way.  U's two operand forms are split and packed when the factor is
+// refreshed (or once per call, k_pack_u).
 //
-// A workgroup takes kRT*16 rows over the full row length; its 8 waves split
-// the 32-column chunks, reduce c across waves through LDS, and then apply the
-// correction to their own chunks (re-reading G, most recent chunk first).
-// Per-tensor scaling takes two launches (pass 1: c' and a partial amax per
-// workgroup; pass 2: the amax of the layer from the partials, W again and the
-// codes); 1x128 block scaling needs only the row and is one launch.
+// Work is split into strips of 16 rows over the full row length (one
+// workgroup each), so a row's c never leaves its workgroup.  Per-tensor
+// scaling takes two launches (pass 1: c' and the strip's amax; pass 2: the
+// layer amax, W again and the codes); 1x128 block scaling and the
+// dequantize side are one launch each.
+#include <type_traits>
+
 #include "device.hpp"
+
+// No implicit contraction of a*b + c into fma: the two whitening passes of
+// per-tensor scaling must compute bit-identical W (pass 1 takes its amax,
+// pass 2 encodes it), and pass 1 multiplies c by D_w in registers where pass
+// 2 reads the rounded product back.  Every fma below is written out.
+#pragma clang fp contract(off)
 
 namespace gift {
 
 constexpr int kThreads = 256;       // flat kernels
 constexpr int kFlatTile = 4096;     // elements per workgroup (flat kernels)
-constexpr int kWaves = 8;           // waves per workgroup (row kernels)
-constexpr int kRowThreads = 64 * kWaves;
-constexpr int kRT = 2;              // 16-row tiles per row workgroup
-constexpr int kRows = 16 * kRT;
 constexpr int kChunk = 32;          // columns per MFMA K chunk
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -133,67 +136,82 @@ __global__ __launch_bounds__(kThreads) void k_pack_u(PackGroup pg) {
 }
 
 // ---------------------------------------------------------------------------
-// row-workgroup geometry.  A layer's row kernels use tiles of kRows rows x
-// one column group; a column group is kWaves units of `unit` chunks, one unit
-// per wave (unit = 2 chunks for per-tensor scaling, 4 = one 128-column
-// segment for block scaling).  tile = row_block * ngrp + group.
+// tile geometry.  A workgroup owns a tile of kTR x 16 = 64 gradient rows by
+// one column group of kTW * kCPW 32-column chunks; each wave takes kCPW
+// chunks of the group for all 64 rows, so every operand-pack load feeds four
+// 16-row MFMA tiles.  A row's c = g U is split over the column groups: each
+// tile stores its partial (summed over its waves through LDS), and the next
+// pass sums the partials of a row block in column-group order.
+//
+// Memory-wait discipline: a wave issues all loads of its chunks together
+// (unconditionally inside a wave-uniform branch), and stores come last, so
+// the compiler waits for exactly the operands in use; with a store in flight
+// every wait for a load would become a wait for all memory operations.
+//
+// Partial and final row coefficients are kept in "fragment" order:
+// [row block][rt * 8 + k][lane] holds, for the lane's row 16 rt + lane % 16,
+// rank rank_of(k, lane / 16) -- exactly the eight values a lane feeds to the
+// second product, so they are read and written coalesced.
 // ---------------------------------------------------------------------------
-struct RowCtx {
-  int64_t row[kRT];   // clamped row of each 16-row tile for this lane
-  bool ok[kRT];       // row < d_out
-  int grp;            // column group of the workgroup
-  int c0, c1;         // this wave's chunk range (may be empty)
+constexpr int kTW = 8;                    // waves per tile workgroup
+constexpr int kTileThreads = 64 * kTW;
+constexpr int kTR = 4;                    // 16-row MFMA tiles per workgroup
+constexpr int kTileRows = 16 * kTR;
+constexpr int kFrag = kTR * 8 * 64;       // floats of one row block's coefficients
+constexpr int kReduceThreads = kTR * 64;  // one thread per lane of each 16-row tile
+// Above this many tiles in a layer the per-tile amax partials are first
+// reduced by one workgroup (k_amax_final) instead of by every quantize
+// workgroup.
+constexpr int kPartialLimit = 2048;
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+// f(integral_constant<int, n>) for the wave-uniform n, 1 <= n <= kMax;
+// nothing for n < 1
+template <int kMax, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (kMax > 0) {
+    if (n >= kMax) f(std::integral_constant<int, kMax>{});
+    else with_count<kMax - 1>(n, f);
+  }
+}
+
+struct Tile {
+  int64_t row[kTR];  // this lane's gradient row in each 16-row tile (clamped)
+  bool ok[kTR];      // row < d_out
+  int64_t rb;        // row block
+  int cg;            // column group
+  int c0;            // first chunk of this wave
+  int nmine;         // chunks of this wave (0..kCPW, wave-uniform)
   int lane, wave, r16, g;
 };
 
-__device__ __forceinline__ RowCtx row_ctx(const LayerDev& L, int tile, int unit) {
-  RowCtx x;
+template <int kCPW>
+__device__ __forceinline__ Tile tile_ctx(const LayerDev& L, int tile) {
+  Tile x;
   x.lane = threadIdx.x & 63;
-  x.wave = threadIdx.x >> 6;
+  x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   x.r16 = x.lane & 15;
   x.g = x.lane >> 4;
-  x.grp = tile % L.ngrp;
-  const int64_t row0 = (int64_t)(tile / L.ngrp) * kRows;
+  x.rb = tile / L.ngrp;
+  x.cg = tile % L.ngrp;
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    const int64_t r = row0 + 16 * rt + x.r16;
+  for (int rt = 0; rt < kTR; ++rt) {
+    const int64_t r = x.rb * kTileRows + 16 * rt + x.r16;
     x.ok[rt] = r < L.d_out;
     x.row[rt] = x.ok[rt] ? r : L.d_out - 1;
   }
   const int nch = (int)(L.d_in / kChunk);
-  const int u = x.grp * kWaves + x.wave;
-  x.c0 = min(nch, u * unit);
-  x.c1 = min(nch, x.c0 + unit);
+  x.c0 = (x.cg * kTW + x.wave) * kCPW;
+  const int left = nch - x.c0;
+  x.nmine = left <= 0 ? 0 : (left < kCPW ? left : kCPW);
   return x;
-}
-
-// Two-stage software pipeline over n iterations: the loads of iteration i+1
-// are issued before the compute of iteration i.
-// pipeline2 with the first iteration's buffer already loaded (its loads were
-// issued before other independent loads of the caller)
-template <class Buf, class Map, class Load, class Comp>
-__device__ __forceinline__ void pipeline2_from(int n, Buf& a, Map map, Load load, Comp comp) {
-  Buf b;
-  for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load(map(i + 1), b);
-    comp(map(i), a);
-    if (i + 1 >= n) break;
-    if (i + 2 < n) load(map(i + 2), a);
-    comp(map(i + 1), b);
-  }
-}
-
-template <class Buf, class Map, class Load, class Comp>
-__device__ __forceinline__ void pipeline2(int n, Map map, Load load, Comp comp) {
-  Buf a, b;
-  if (n > 0) load(map(0), a);
-  for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load(map(i + 1), b);
-    comp(map(i), a);
-    if (i + 1 >= n) break;
-    if (i + 2 < n) load(map(i + 2), a);
-    comp(map(i + 1), b);
-  }
 }
 
 __device__ __forceinline__ void load_a(const uint4* P, int c, int lane, uint4 (&a)[2][3]) {
@@ -214,146 +232,23 @@ __device__ __forceinline__ const uint4* p2_of(const LayerDev& L) {
   return L.P + (size_t)(L.d_in / kChunk) * 2 * 3 * 64;
 }
 
-// rank index of element j (0..7) of a lane's c vector
-__device__ __forceinline__ int rank_of(int j, int g) { return 16 * (j >> 2) + 4 * g + (j & 3); }
+// rank index of element k (0..7) of a lane's c vector
+__device__ __forceinline__ int rank_of(int k, int g) { return 16 * (k >> 2) + 4 * g + (k & 3); }
 
-// Sum the 8 waves' partial c (16 values per lane) in a fixed order and store
-// the workgroup's partial for its column group: cpart[grp][row][rank].
-__device__ __forceinline__ void store_cpart(const LayerDev& L, const RowCtx& x, int tile,
-                                            f32x4 (&acc)[2][kRT], float (*red)[kRT * 8][64]) {
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[x.wave][rt * 8 + h * 4 + i][x.lane] = acc[h][rt][i];
-  __syncthreads();
-  const int64_t row0 = (int64_t)(tile / L.ngrp) * kRows;
-  for (int p = threadIdx.x; p < kRT * 8 * 64; p += kRowThreads) {
-    const int q = p >> 6, ln = p & 63;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[w][q][ln];
-    const int rt = q >> 3, j = q & 7;
-    const int64_t row = row0 + 16 * rt + (ln & 15);
-    if (row < L.d_out) L.cbuf[((int64_t)x.grp * L.d_out + row) * kRank + rank_of(j, ln >> 4)] = s;
-  }
+// gradient values of one chunk for this lane and 16-row tile: columns
+// 32c + 4g .. +3 (t = 0) and 32c + 16 + 4g .. +3 (t = 1) of its row
+__device__ __forceinline__ void load_gc(const LayerDev& L, int64_t row, int g, int c,
+                                        float4 (&v)[2]) {
+  const float* p = L.G + row * L.d_in + kChunk * c + 4 * g;
+  v[0] = *reinterpret_cast<const float4*>(p);
+  v[1] = *reinterpret_cast<const float4*>(p + 16);
 }
 
-// c of the workgroup's rows = fixed-order sum of the column-group partials.
-// The 32 rows x 8 rank quads are spread over the workgroup (one float4 per
-// group per thread, all loads in flight together) and summed into LDS; then
-// each lane takes its 8 ranks of each row tile, times dk[rank] * extra, split
-// into the second product's bf16 operands.  Contains a workgroup barrier.
-struct CSum {
-  float v[kRows][kRank + 4];
-};
-
-__device__ __forceinline__ void load_c_operands(const LayerDev& L, const RowCtx& x, int tile,
-                                                const float* dk, float extra, CSum& cs,
-                                                bf16x8 (&b)[kRT][3]) {
-  constexpr int kItems = kRows * kRank / 4;  // float4 items per workgroup
-  constexpr int kBatch = 8;
-  const int64_t row0 = (int64_t)(tile / L.ngrp) * kRows;
-  for (int e = threadIdx.x; e < kItems; e += kRowThreads) {
-    const int r = e >> 3, q4 = e & 7;
-    const int64_t row = min(row0 + r, L.d_out - 1);
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g0 = 0; g0 < L.ngrp; g0 += kBatch) {
-      float4 u[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int gi = g0 + k < L.ngrp ? g0 + k : L.ngrp - 1;
-        u[k] = *reinterpret_cast<const float4*>(L.cbuf + ((int64_t)gi * L.d_out + row) * kRank +
-                                                4 * q4);
-      }
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        if (g0 + k < L.ngrp) {
-          sum.x += u[k].x; sum.y += u[k].y; sum.z += u[k].z; sum.w += u[k].w;
-        }
-      }
-    }
-    *reinterpret_cast<float4*>(&cs.v[r][4 * q4]) = sum;
-  }
-  __syncthreads();
-  float d8[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) d8[j] = dk[rank_of(j, x.g)] * extra;
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    float cp[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cp[j] = cs.v[16 * rt + x.r16][rank_of(j, x.g)] * d8[j];
-    split3(cp, b[rt]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// first product, partial over a column group: c^T = U^T G^T (G fp32 split
-// three ways), or U^T decode(q)^T on the exact codes (dequantize; with block
-// scaling each 128-column segment's product is scaled by its inv).
-// ---------------------------------------------------------------------------
-struct G1Buf {
-  uint4 a[2][3];
-  float4 g[kRT][2];
-};
-
-template <int kUnit>
-__global__ __launch_bounds__(kRowThreads) void k_cpart_g(GroupDev gd) {
-  const int l = find_layer(gd, blockIdx.x);
-  const LayerDev& L = gd.L[l];
-  const int tile = blockIdx.x - L.tile_begin;
-  const RowCtx x = row_ctx(L, tile, kUnit);
-  // the per-tensor amax slot starts at 0; the next launch max-combines into it
-  if (L.amax && tile == 0 && threadIdx.x == 0) *L.amax = 0u;
-  __shared__ float red[kWaves][kRT * 8][64];
-  const uint4* P1 = L.P;
-  const int64_t d_in = L.d_in;
-  f32x4 acc[2][kRT];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[h][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pipeline2<G1Buf>(
-      x.c1 - x.c0, [&](int i) { return x.c0 + i; },
-      [&](int c, G1Buf& b) {
-        load_a(P1, c, x.lane, b.a);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const float* gp = L.G + x.row[rt] * d_in + kChunk * c + 4 * x.g;
-          b.g[rt][0] = *reinterpret_cast<const float4*>(gp);
-          b.g[rt][1] = *reinterpret_cast<const float4*>(gp + 16);
-        }
-      },
-      [&](int, const G1Buf& b) {
-        bf16x8 a[2][3];
-        as_ops(b.a, a);
-        bf16x8 sp[kRT][3];
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const float4 u = b.g[rt][0], v = b.g[rt][1];
-          const float gv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-          split3(gv, sp[rt]);
-        }
-        f32x4 t4[2 * kRT];
-        const bf16x8(*pa[2 * kRT])[3];
-        const bf16x8(*pb[2 * kRT])[3];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            t4[h * kRT + rt] = acc[h][rt];
-            pa[h * kRT + rt] = &a[h];
-            pb[h * kRT + rt] = &sp[rt];
-          }
-        mfma3x3_n<2 * kRT>(pa, pb, t4);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) acc[h][rt] = t4[h * kRT + rt];
-      });
-  store_cpart(L, x, tile, acc, red);
+__device__ __forceinline__ void load_qc(const LayerDev& L, int64_t row, int g, int c,
+                                        uint32_t (&v)[2]) {
+  const uint8_t* p = L.q + row * L.d_in + kChunk * c + 4 * g;
+  v[0] = *reinterpret_cast<const uint32_t*>(p);
+  v[1] = *reinterpret_cast<const uint32_t*>(p + 16);
 }
 
 __device__ __forceinline__ void decode8(uint32_t lo, uint32_t hi, float (&v)[8]) {
@@ -364,111 +259,6 @@ __device__ __forceinline__ void decode8(uint32_t lo, uint32_t hi, float (&v)[8])
   }
 }
 
-struct Q1Buf {
-  uint4 a[2][3];
-  uint32_t q[kRT][2];
-};
-
-template <bool kBlockScale>
-__global__ __launch_bounds__(kRowThreads) void k_cpart_q(GroupDev gd) {
-  constexpr int kUnit = kBlockScale ? kBlock / kChunk : 2;
-  const int l = find_layer(gd, blockIdx.x);
-  const LayerDev& L = gd.L[l];
-  const int tile = blockIdx.x - L.tile_begin;
-  const RowCtx x = row_ctx(L, tile, kUnit);
-  __shared__ float red[kWaves][kRT * 8][64];
-  const uint4* P1 = L.P;
-  const int64_t d_in = L.d_in;
-  f32x4 acc[2][kRT];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[h][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pipeline2<Q1Buf>(
-      x.c1 - x.c0, [&](int i) { return x.c0 + i; },
-      [&](int c, Q1Buf& b) {
-        load_a(P1, c, x.lane, b.a);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const uint8_t* qp = L.q + x.row[rt] * d_in + kChunk * c + 4 * x.g;
-          b.q[rt][0] = *reinterpret_cast<const uint32_t*>(qp);
-          b.q[rt][1] = *reinterpret_cast<const uint32_t*>(qp + 16);
-        }
-      },
-      [&](int, const Q1Buf& b) {
-        bf16x8 a[2][3];
-        as_ops(b.a, a);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          float v[8];
-          decode8(b.q[rt][0], b.q[rt][1], v);
-          bf16x8 bq;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bq[i] = (__bf16)v[i];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) acc[h][rt] = mfma3x1(a[h], bq, acc[h][rt]);
-        }
-      });
-  if (kBlockScale && x.c0 < x.c1) {
-    // the wave's unit is exactly one 128-column segment
-    const int64_t nseg = d_in / kBlock;
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-      const float s = L.inv[x.row[rt] * nseg + (x.c0 >> 2)];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[h][rt][i] *= s;
-    }
-  }
-  store_cpart(L, x, tile, acc, red);
-}
-
-// ---------------------------------------------------------------------------
-// whitened tensor for one chunk: w = alpha g + correction
-// ---------------------------------------------------------------------------
-struct G3Buf {
-  uint4 a[2][3];
-  float4 g[2][kRT];
-};
-
-__device__ __forceinline__ void load_g3(const LayerDev& L, const RowCtx& x, int c, G3Buf& b) {
-  load_a(p2_of(L), c, x.lane, b.a);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt)
-      b.g[t][rt] = *reinterpret_cast<const float4*>(L.G + x.row[rt] * L.d_in + kChunk * c +
-                                                    16 * t + 4 * x.g);
-}
-
-__device__ __forceinline__ void whiten_chunk(const G3Buf& b, const bf16x8 (&cb)[kRT][3],
-                                             float alpha, float4 (&w)[2][kRT]) {
-  bf16x8 a[2][3];
-  as_ops(b.a, a);
-  f32x4 corr[2 * kRT];
-  const bf16x8(*pa[2 * kRT])[3];
-  const bf16x8(*pb[2 * kRT])[3];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-      corr[t * kRT + rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pa[t * kRT + rt] = &a[t];
-      pb[t * kRT + rt] = &cb[rt];
-    }
-  mfma3x3_n<2 * kRT>(pa, pb, corr);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-      const f32x4 c = corr[t * kRT + rt];
-      const float4 gv = b.g[t][rt];
-      w[t][rt] = make_float4(fmaf(alpha, gv.x, c[0]), fmaf(alpha, gv.y, c[1]),
-                             fmaf(alpha, gv.z, c[2]), fmaf(alpha, gv.w, c[3]));
-    }
-}
-
 __device__ __forceinline__ uint32_t amax4(uint32_t m, const float4& v) {
   m = max(m, abs_bits(v.x));
   m = max(m, abs_bits(v.y));
@@ -476,205 +266,439 @@ __device__ __forceinline__ uint32_t amax4(uint32_t m, const float4& v) {
   return max(m, abs_bits(v.w));
 }
 
-// ---------------------------------------------------------------------------
-// per-tensor scaling, pass 1: partial amax of W per workgroup
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRowThreads) void k_whiten_amax(GroupDev gd) {
-  const int l = find_layer(gd, blockIdx.x);
-  const LayerDev& L = gd.L[l];
-  const int tile = blockIdx.x - L.tile_begin;
-  const RowCtx x = row_ctx(L, tile, 2);
-  __shared__ uint32_t mx[kWaves];
-  __shared__ CSum cs;
-  G3Buf first;
-  if (x.c0 < x.c1) load_g3(L, x, x.c0, first);
-  bf16x8 b[kRT][3];
-  load_c_operands(L, x, tile, L.coef + GIFT_COEF_DW, 1.f, cs, b);
-  const float alpha = L.coef[GIFT_COEF_ALPHA];
-  uint32_t m = 0u;
-  pipeline2_from<G3Buf>(
-      x.c1 - x.c0, first, [&](int i) { return x.c0 + i; },
-      [&](int c, G3Buf& buf) { load_g3(L, x, c, buf); },
-      [&](int, const G3Buf& buf) {
-        float4 w[2][kRT];
-        whiten_chunk(buf, b, alpha, w);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            if (x.ok[rt]) m = amax4(m, w[t][rt]);
-      });
-  m = block_max_u32<kRowThreads>(m, mx);
-  // unsigned max is order-independent: the result does not depend on timing
-  if (threadIdx.x == 0) atomicMax(L.amax, m);
+// first product, one chunk and 16-row tile: acc[h] += (U^T)_h (g split three ways)
+__device__ __forceinline__ void cpart_g(const bf16x8 (&a)[2][3], const float4 (&gv)[2],
+                                        f32x4 (&acc)[2]) {
+  const float v[8] = {gv[0].x, gv[0].y, gv[0].z, gv[0].w, gv[1].x, gv[1].y, gv[1].z, gv[1].w};
+  bf16x8 sp[3];
+  split3(v, sp);
+  const bf16x8(*pa2[2])[3] = {&a[0], &a[1]};
+  const bf16x8(*pb2[2])[3] = {&sp, &sp};
+  mfma3x3_n<2>(pa2, pb2, acc);
 }
 
-// per-tensor scaling, pass 2: layer amax from the partials, W again, codes
-template <bool kWriteW>
-__global__ __launch_bounds__(kRowThreads) void k_whiten_quant(GroupDev gd) {
-  const int l = find_layer(gd, blockIdx.x);
-  const LayerDev& L = gd.L[l];
+// first product on codes (exact in bf16): acc[h] += (U^T)_h decode(q)
+__device__ __forceinline__ void cpart_q(const bf16x8 (&a)[2][3], const uint32_t (&qv)[2],
+                                        f32x4 (&acc)[2]) {
+  float v[8];
+  decode8(qv[0], qv[1], v);
+  bf16x8 bq;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bq[i] = (__bf16)v[i];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) acc[h] = mfma3x1(a[h], bq, acc[h]);
+}
+
+// second product, one chunk and 16-row tile: corr[t] = (c' U^T) for the
+// lane's 2 x 4 columns
+__device__ __forceinline__ void correction(const bf16x8 (&a)[2][3], const bf16x8 (&cb)[3],
+                                           f32x4 (&corr)[2]) {
+  corr[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  corr[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8(*pa2[2])[3] = {&a[0], &a[1]};
+  const bf16x8(*pb2[2])[3] = {&cb, &cb};
+  mfma3x3_n<2>(pa2, pb2, corr);
+}
+
+// Sum the waves' partial c (acc of every wave) in wave order through LDS and
+// store the tile's partial for its column group in fragment order, in two
+// halves of kTR / 2 row tiles (32 KB of LDS).  Contains workgroup barriers.
+__device__ __forceinline__ void store_partial(const LayerDev& L, const Tile& x,
+                                              const f32x4 (&acc)[kTR][2],
+                                              float (*red)[kTR * 4][64]) {
+  float* out = L.cbuf + ((int64_t)x.cg * L.n_rb + x.rb) * kFrag;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half) __syncthreads();  // the first half has been read
+#pragma unroll
+    for (int r = 0; r < kTR / 2; ++r)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[x.wave][r * 8 + 4 * h + i][x.lane] = acc[half * (kTR / 2) + r][h][i];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kFrag / 2 / kTileThreads; ++e) {
+      const int p = e * kTileThreads + threadIdx.x;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kTW; ++w) s += red[w][p >> 6][p & 63];
+      out[half * (kFrag / 2) + p] = s;
+    }
+  }
+}
+
+// The row block's c' operand of the second product, already split three
+// ways: [rt][split][lane] 16-byte groups of 8 bf16 (kCOp uint4 per row
+// block), into LDS.  Contains a workgroup barrier.
+constexpr int kCOp = kTR * 3 * 64;
+__device__ __forceinline__ void stage_c(const LayerDev& L, const Tile& x, uint4* lds) {
+  const uint4* src = reinterpret_cast<const uint4*>(L.cfin) + x.rb * kCOp;
+  for (int e = threadIdx.x; e < kCOp; e += kTileThreads) lds[e] = src[e];
+  __syncthreads();
+}
+
+// the lane's operand of the second product for 16-row tile rt
+__device__ __forceinline__ void c_operand(const uint4* lds, int rt, int lane, bf16x8 (&cb)[3]) {
+#pragma unroll
+  for (int s = 0; s < 3; ++s) cb[s] = as_bf16x8(lds[(rt * 3 + s) * 64 + lane]);
+}
+
+// ---------------------------------------------------------------------------
+// first product of a tile: partial c over the column group (whiten: of G;
+// dequantize: of the codes, each chunk scaled by its inverse scale).
+// ---------------------------------------------------------------------------
+template <int kCPW, bool kCodes, bool kBlockScale>
+__global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
+  // a local copy: the descriptor's fields stay in scalar registers
+  const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
-  const RowCtx x = row_ctx(L, tile, 2);
-  G3Buf first;
-  if (x.c0 < x.c1) load_g3(L, x, x.c0, first);
-  const Scale sc = scale_from_amax_bits(*L.amax);
+  const Tile x = tile_ctx<kCPW>(L, tile);
+  __shared__ float red[kTW][kTR * 4][64];
+  f32x4 acc[kTR][2];
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nseg = L.d_in / kBlock;
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    uint4 pa[n][2][3];
+    float4 gv[kCodes ? 1 : n][kTR][2];
+    uint32_t qv[kCodes ? n : 1][kTR][2];
+    float sc[kBlockScale ? n : 1][kTR];
+    static_for<n>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      load_a(L.P, x.c0 + j, x.lane, pa[j]);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        if constexpr (kCodes) load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
+        else load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+        if constexpr (kBlockScale) sc[j][rt] = L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)];
+      }
+    });
+    static_for<n>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      bf16x8 a[2][3];
+      as_ops(pa[j], a);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        if constexpr (kCodes) {
+          if constexpr (kBlockScale) {
+            f32x4 t[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            cpart_q(a, qv[j][rt], t);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc[rt][h] += t[h] * sc[j][rt];
+          } else {
+            cpart_q(a, qv[j][rt], acc[rt]);
+          }
+        } else {
+          cpart_g(a, gv[j][rt], acc[rt]);
+        }
+      }
+    });
+  });
+  store_partial(L, x, acc, red);
+}
+
+// ---------------------------------------------------------------------------
+// c' of every row block: the column-group partials summed in group order,
+// times the lane's rank coefficient (whiten: D_w; dequantize: D_u, and the
+// tensor's inverse scale for per-tensor scaling).  One workgroup per row block.
+// ---------------------------------------------------------------------------
+template <bool kDequant, bool kBlockScale>
+__global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
+  const LayerDev L = gd.L[find_layer_rb(gd, blockIdx.x)];
+  const int64_t rb = blockIdx.x - L.rb_begin;
+  const int rt = threadIdx.x >> 6, lane = threadIdx.x & 63;  // one lane of one 16-row tile
+  const float* dk = L.coef + (kDequant ? GIFT_COEF_DU : GIFT_COEF_DW);
+  const float extra = (kDequant && !kBlockScale) ? L.inv[0] : 1.f;
+  float d8[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d8[k] = dk[rank_of(k, lane >> 4)] * extra;
+  // partials in group order; eight groups' loads in flight at a time
+  constexpr int kB = 8;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* base = L.cbuf + rb * kFrag + rt * 8 * 64 + lane;
+  const int64_t stride = L.n_rb * kFrag;
+  for (int c0 = 0; c0 < L.ngrp; c0 += kB) {
+    float v[kB][8];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int cg = c0 + b < L.ngrp ? c0 + b : L.ngrp - 1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[b][k] = base[cg * stride + k * 64];
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (c0 + b < L.ngrp)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[k] += v[b][k];
+  }
+  float cp[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cp[k] = s[k] * d8[k];
+  bf16x8 cb[3];
+  split3(cp, cb);
+  uint4* out = reinterpret_cast<uint4*>(L.cfin) + rb * kCOp;
+#pragma unroll
+  for (int sp = 0; sp < 3; ++sp) out[(rt * 3 + sp) * 64 + lane] = __builtin_bit_cast(uint4, cb[sp]);
+}
+
+// ---------------------------------------------------------------------------
+// whiten pass 2.
+//   kBlock128 = false (per-tensor scaling): W of the tile, its amax to the
+//     layer's partials.
+//   kBlock128 = true (1x128 block scaling, the last pass): W, the segment
+//     amax (the 4 chunks of a segment are held by 4 / kCPW waves), codes and
+//     inverse scales, optionally W.
+// ---------------------------------------------------------------------------
+template <int kCPW, bool kBlock128, bool kWriteW>
+__global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
+  constexpr int kWPS = 4 / kCPW;  // waves per segment (block scaling)
+  static_assert(!kBlock128 || kCPW <= 4, "a segment spans whole waves");
+  const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
+  const int tile = blockIdx.x - L.tile_begin;
+  const Tile x = tile_ctx<kCPW>(L, tile);
+  __shared__ uint4 cs[kCOp];
+  __shared__ uint32_t mx[kBlock128 ? kTW * kTR * 64 : kTW];
+  const uint4* P2 = p2_of(L);
+  const float alpha = L.coef[GIFT_COEF_ALPHA];
+  // this wave's operands and gradient in flight while c' is staged
+  uint4 pa[kCPW][2][3];
+  float4 gv[kCPW][kTR][2];
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    static_for<decltype(N)::value>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      load_a(P2, x.c0 + j, x.lane, pa[j]);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+    });
+  });
+  stage_c(L, x, cs);
+  float4 w[kCPW][kTR][2];
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    static_for<decltype(N)::value>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      bf16x8 a[2][3];
+      as_ops(pa[j], a);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        bf16x8 cb[3];
+        c_operand(cs, rt, x.lane, cb);
+        f32x4 corr[2];
+        correction(a, cb, corr);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float4 gg = gv[j][rt][t];
+          w[j][rt][t] = make_float4(fmaf(alpha, gg.x, corr[t][0]), fmaf(alpha, gg.y, corr[t][1]),
+                                    fmaf(alpha, gg.z, corr[t][2]), fmaf(alpha, gg.w, corr[t][3]));
+        }
+      }
+    });
+  });
+  if constexpr (!kBlock128) {
+    uint32_t m = 0u;
+    with_count<kCPW>(x.nmine, [&](auto N) {
+      static_for<decltype(N)::value>([&](auto J) {
+#pragma unroll
+        for (int rt = 0; rt < kTR; ++rt)
+          if (x.ok[rt]) m = amax4(amax4(m, w[J.value][rt][0]), w[J.value][rt][1]);
+      });
+    });
+    m = block_max_u32<kTileThreads>(m, mx);
+    if (threadIdx.x == 0) L.part[tile] = m;
+  } else {
+    // per-segment amax: lane max over its chunks of the segment, then over
+    // the lanes of the same row (xor 16, 32), then over the segment's waves
+    uint32_t (*sm)[kTR][64] = reinterpret_cast<uint32_t (*)[kTR][64]>(mx);
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) {
+      uint32_t m = 0u;
+      with_count<kCPW>(x.nmine, [&](auto N) {
+        static_for<decltype(N)::value>([&](auto J) {
+          m = amax4(amax4(m, w[J.value][rt][0]), w[J.value][rt][1]);
+        });
+      });
+      m = max(m, (uint32_t)__shfl_xor(m, 16, 64));
+      m = max(m, (uint32_t)__shfl_xor(m, 32, 64));
+      sm[x.wave][rt][x.lane] = m;
+    }
+    __syncthreads();
+    if (x.nmine == 0) return;  // wave-uniform; no barrier below
+    const int w0 = x.wave - x.wave % kWPS;
+    const int seg = x.c0 / 4;
+    const int64_t nseg = L.d_in / kBlock;
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int v = 0; v < kWPS; ++v) m = max(m, sm[w0 + v][rt][x.lane]);
+      const Scale sc = scale_from_amax_bits(m);
+      if (!x.ok[rt]) continue;
+      if (x.g == 0 && x.wave == w0) {
+        L.inv[x.row[rt] * nseg + seg] = sc.inv;
+        if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
+      }
+      with_count<kCPW>(x.nmine, [&](auto N) {
+        static_for<decltype(N)::value>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int64_t o = x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g;
+            const float4 v = w[j][rt][t];
+            *reinterpret_cast<uint32_t*>(L.q + o) = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
+            if constexpr (kWriteW) *reinterpret_cast<float4*>(L.Wout + o) = v;
+          }
+        });
+      });
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-tensor whiten pass 3: layer amax from the tile partials (or from
+// k_amax_final for very tall layers), W again from the row block's c', codes.
+// ---------------------------------------------------------------------------
+template <int kCPW, bool kWriteW>
+__global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
+  const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
+  const int tile = blockIdx.x - L.tile_begin;
+  const Tile x = tile_ctx<kCPW>(L, tile);
+  __shared__ uint4 cs[kCOp];
+  __shared__ uint32_t mx[kTW];
+  const uint4* P2 = p2_of(L);
+  const float alpha = L.coef[GIFT_COEF_ALPHA];
+  uint4 pa[kCPW][2][3];
+  float4 gv[kCPW][kTR][2];
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    static_for<decltype(N)::value>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      load_a(P2, x.c0 + j, x.lane, pa[j]);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+    });
+  });
+  uint32_t m = 0u;
+  if (L.n_tiles > kPartialLimit) {
+    m = *L.amax;
+  } else {
+    for (int i = threadIdx.x; i < L.n_tiles; i += kTileThreads) m = max(m, L.part[i]);
+    m = block_max_u32<kTileThreads>(m, mx);
+  }
+  const Scale sc = scale_from_amax_bits(m);
   if (tile == 0 && threadIdx.x == 0) {
     L.inv[0] = sc.inv;
     if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
   }
-  __shared__ CSum cs;
-  bf16x8 b[kRT][3];
-  load_c_operands(L, x, tile, L.coef + GIFT_COEF_DW, 1.f, cs, b);
-  const float alpha = L.coef[GIFT_COEF_ALPHA];
-  pipeline2_from<G3Buf>(
-      x.c1 - x.c0, first, [&](int i) { return x.c0 + i; },
-      [&](int c, G3Buf& buf) { load_g3(L, x, c, buf); },
-      [&](int c, const G3Buf& buf) {
-        float4 w[2][kRT];
-        whiten_chunk(buf, b, alpha, w);
+  stage_c(L, x, cs);
+  if (x.nmine == 0) return;  // wave-uniform; no barrier below
+  const bool nonfinite = (sc.flags & GIFT_FLAG_NONFINITE) != 0;
+  uint32_t codes[kCPW][kTR][2];
+  float4 wv[kWriteW ? kCPW : 1][kTR][2];
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    static_for<n>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      bf16x8 a[2][3];
+      as_ops(pa[j], a);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int rt = 0; rt < kTR; ++rt) {
+        bf16x8 cb[3];
+        c_operand(cs, rt, x.lane, cb);
+        f32x4 corr[2];
+        correction(a, cb, corr);
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            if (!x.ok[rt]) continue;
-            const int64_t o = x.row[rt] * L.d_in + kChunk * c + 16 * t + 4 * x.g;
-            const float4 v = w[t][rt];
-            *reinterpret_cast<uint32_t*>(L.q + o) =
-                e4m3_encode4(v.x * sc.scale, v.y * sc.scale, v.z * sc.scale, v.w * sc.scale);
-            if (kWriteW) *reinterpret_cast<float4*>(L.Wout + o) = v;
-          }
-      });
-}
-
-// ---------------------------------------------------------------------------
-// 1x128 block scaling: each wave owns one 128-column segment of 32 rows; a
-// segment's amax is the max over the lane's 32 values and the four lanes that
-// hold the same row.
-// ---------------------------------------------------------------------------
-template <bool kWriteW>
-__global__ __launch_bounds__(kRowThreads) void k_whiten_b128(GroupDev gd) {
-  constexpr int kPer = kBlock / kChunk;
-  const int l = find_layer(gd, blockIdx.x);
-  const LayerDev& L = gd.L[l];
-  const int tile = blockIdx.x - L.tile_begin;
-  const RowCtx x = row_ctx(L, tile, kPer);
-  __shared__ CSum cs;
-  const bool busy = x.c0 < x.c1;
-  G3Buf buf[2];
-  if (busy) load_g3(L, x, x.c0, buf[0]);
-  bf16x8 b[kRT][3];
-  load_c_operands(L, x, tile, L.coef + GIFT_COEF_DW, 1.f, cs, b);
-  if (!busy) return;  // no barrier below
-  const float alpha = L.coef[GIFT_COEF_ALPHA];
-  const int64_t nseg = L.d_in / kBlock;
-  float4 w[kPer][2][kRT];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (k + 1 < kPer) load_g3(L, x, x.c0 + k + 1, buf[(k + 1) & 1]);
-    whiten_chunk(buf[k & 1], b, alpha, w[k]);
-  }
-  const int seg = x.c0 / kPer;
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    uint32_t m = 0u;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) m = amax4(m, w[k][t][rt]);
-    m = max(m, (uint32_t)__shfl_xor(m, 16, 64));
-    m = max(m, (uint32_t)__shfl_xor(m, 32, 64));
-    const Scale sc = scale_from_amax_bits(m);
-    if (!x.ok[rt]) continue;
-    if (x.g == 0) {
-      L.inv[x.row[rt] * nseg + seg] = sc.inv;
-      if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int64_t o2 = x.row[rt] * L.d_in + kChunk * (x.c0 + k) + 16 * t + 4 * x.g;
-        const float4 v = w[k][t][rt];
-        *reinterpret_cast<uint32_t*>(L.q + o2) =
-            e4m3_encode4(v.x * sc.scale, v.y * sc.scale, v.z * sc.scale, v.w * sc.scale);
-        if (kWriteW) *reinterpret_cast<float4*>(L.Wout + o2) = v;
+        for (int t = 0; t < 2; ++t) {
+          const float4 gg = gv[j][rt][t];
+          const float4 v = make_float4(fmaf(alpha, gg.x, corr[t][0]), fmaf(alpha, gg.y, corr[t][1]),
+                                       fmaf(alpha, gg.z, corr[t][2]), fmaf(alpha, gg.w, corr[t][3]));
+          codes[j][rt][t] = e4m3_encode4_scaled(v, sc.scale, nonfinite);
+          if constexpr (kWriteW) wv[j][rt][t] = v;
+        }
       }
-  }
+    });
+    static_for<n>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        if (!x.ok[rt]) continue;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int64_t o = x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g;
+          *reinterpret_cast<uint32_t*>(L.q + o) = codes[j][rt][t];
+          if constexpr (kWriteW) *reinterpret_cast<float4*>(L.Wout + o) = wv[j][rt][t];
+        }
+      }
+    });
+  });
 }
 
 // ---------------------------------------------------------------------------
-// dequantize + un-whiten: G^ = beta W^ + (W^ U * D_u) U^T, W^ = decode(q) * inv
+// dequantize + un-whiten, pass 2: G^ = beta W^ + c'^ U^T with
+// W^ = decode(q) * inv and c'^ the row block's (W^ U) * D_u.
 // ---------------------------------------------------------------------------
-struct Q3Buf {
-  uint4 a[2][3];
-  uint32_t q[2][kRT];
-  float s[kRT];
-};
-
-template <bool kBlockScale>
-__global__ __launch_bounds__(kRowThreads) void k_unwhiten(GroupDev gd) {
-  constexpr int kUnit = kBlockScale ? kBlock / kChunk : 2;
-  const int l = find_layer(gd, blockIdx.x);
-  const LayerDev& L = gd.L[l];
+template <int kCPW, bool kBlockScale>
+__global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
+  const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
-  const RowCtx x = row_ctx(L, tile, kUnit);
-  __shared__ CSum cs;
-  const bool busy = x.c0 < x.c1;
-  const int64_t d_in = L.d_in, nseg = d_in / kBlock;
-  const float inv0 = kBlockScale ? 1.f : L.inv[0];
+  const Tile x = tile_ctx<kCPW>(L, tile);
+  __shared__ uint4 cs[kCOp];
   const uint4* P2 = p2_of(L);
-  auto load = [&](int c, Q3Buf& bf) {
-    load_a(P2, c, x.lane, bf.a);
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        bf.q[t][rt] = *reinterpret_cast<const uint32_t*>(L.q + x.row[rt] * d_in + kChunk * c +
-                                                         16 * t + 4 * x.g);
-      bf.s[rt] = kBlockScale ? L.inv[x.row[rt] * nseg + (c >> 2)] : inv0;
-    }
-  };
-  Q3Buf first;
-  if (busy) load(x.c0, first);
-  bf16x8 b[kRT][3];
-  load_c_operands(L, x, tile, L.coef + GIFT_COEF_DU, inv0, cs, b);
-  if (!busy) return;  // no barrier below
+  const int64_t nseg = L.d_in / kBlock;
+  const float inv0 = kBlockScale ? 1.f : L.inv[0];
   const float beta = L.coef[GIFT_COEF_BETA];
-  pipeline2_from<Q3Buf>(
-      x.c1 - x.c0, first, [&](int i) { return x.c0 + i; }, load,
-      [&](int c, const Q3Buf& bf) {
-        bf16x8 a[2][3];
-        as_ops(bf.a, a);
-        f32x4 cr[2 * kRT];
-        const bf16x8(*pa[2 * kRT])[3];
-        const bf16x8(*pb[2 * kRT])[3];
+  uint4 pa[kCPW][2][3];
+  uint32_t qv[kCPW][kTR][2];
+  float sc[kCPW][kTR];
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    static_for<decltype(N)::value>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      load_a(P2, x.c0 + j, x.lane, pa[j]);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
+        sc[j][rt] = kBlockScale ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
+      }
+    });
+  });
+  stage_c(L, x, cs);
+  if (x.nmine == 0) return;  // wave-uniform; no barrier below
+  float4 out[kCPW][kTR][2];
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    static_for<n>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      bf16x8 a[2][3];
+      as_ops(pa[j], a);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        bf16x8 cb[3];
+        c_operand(cs, rt, x.lane, cb);
+        f32x4 corr[2];
+        correction(a, cb, corr);
+        const float s = sc[j][rt];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t qq = qv[j][rt][t];
+          out[j][rt][t] = make_float4(fmaf(beta, e4m3_decode(qq, 0) * s, corr[t][0]),
+                                      fmaf(beta, e4m3_decode(qq, 1) * s, corr[t][1]),
+                                      fmaf(beta, e4m3_decode(qq, 2) * s, corr[t][2]),
+                                      fmaf(beta, e4m3_decode(qq, 3) * s, corr[t][3]));
+        }
+      }
+    });
+    static_for<n>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        if (!x.ok[rt]) continue;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            cr[t * kRT + rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            pa[t * kRT + rt] = &a[t];
-            pb[t * kRT + rt] = &b[rt];
-          }
-        mfma3x3_n<2 * kRT>(pa, pb, cr);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            const f32x4 corr = cr[t * kRT + rt];
-            if (!x.ok[rt]) continue;
-            const int64_t o = x.row[rt] * d_in + kChunk * c + 16 * t + 4 * x.g;
-            const float s = bf.s[rt];
-            const uint32_t qv = bf.q[t][rt];
-            float4 out;
-            out.x = fmaf(beta, e4m3_decode(qv, 0) * s, corr[0]);
-            out.y = fmaf(beta, e4m3_decode(qv, 1) * s, corr[1]);
-            out.z = fmaf(beta, e4m3_decode(qv, 2) * s, corr[2]);
-            out.w = fmaf(beta, e4m3_decode(qv, 3) * s, corr[3]);
-            *reinterpret_cast<float4*>(L.Ghat + o) = out;
-          }
-      });
+          *reinterpret_cast<float4*>(L.Ghat + x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t +
+                                     4 * x.g) = out[j][rt][t];
+      }
+    });
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -742,7 +766,7 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
       }
     }
     if (!act) continue;
-    const uint32_t c = e4m3_encode4(v.x * sc.scale, v.y * sc.scale, v.z * sc.scale, v.w * sc.scale);
+    const uint32_t c = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
     *reinterpret_cast<uint32_t*>(L.q + e) = c;
     if (kWriteW) *reinterpret_cast<float4*>(L.Wout + e) = v;
     if (kDeq) {
@@ -836,14 +860,15 @@ __global__ __launch_bounds__(kThreads) void k_err_final(GroupDev g, int out_base
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int row_blocks(int64_t d_out) { return (int)((d_out + kRows - 1) / kRows); }
-// column groups of a whitened layer: kWaves units of 2 chunks (per-tensor
-// scaling) or of one 128-column segment (block scaling)
-int col_groups(int64_t d_in, bool block) {
-  const int64_t unit = block ? kBlock / kChunk : 2;
-  const int64_t units = (d_in / kChunk + unit - 1) / unit;
-  return (int)((units + kWaves - 1) / kWaves);
+constexpr int kCPW = 1;  // chunks per wave of the tile kernels
+
+int64_t row_blocks(int64_t d_out) { return (d_out + kTileRows - 1) / kTileRows; }
+int col_groups(int64_t d_in) {
+  const int64_t nch = d_in / kChunk, per = (int64_t)kTW * kCPW;
+  return (int)((nch + per - 1) / per);
 }
+int frag_floats() { return kFrag; }
+int cop_bytes() { return kCOp * 16; }
 int flat_tiles(int64_t n) { return (int)((n + kFlatTile - 1) / kFlatTile); }
 size_t pack_bytes(int64_t d_in) { return (size_t)(d_in / kChunk) * 2 * 2 * 3 * 64 * 16; }
 
@@ -856,17 +881,20 @@ hipError_t launch_pack(const PackGroup& pg, hipStream_t s) {
 }
 
 hipError_t launch_whiten_quantize(const GroupDev& g, bool block, bool write_w, hipStream_t s) {
-  const dim3 grid(g.total_tiles), blk(kRowThreads);
+  const dim3 grid(g.total_tiles), blk(kTileThreads);
+  k_tile_cpart<kCPW, false, false><<<grid, blk, 0, s>>>(g);
+  k_tile_reduce<false, false><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
   if (block) {
-    k_cpart_g<kBlock / kChunk><<<grid, blk, 0, s>>>(g);
-    if (write_w) k_whiten_b128<true><<<grid, blk, 0, s>>>(g);
-    else k_whiten_b128<false><<<grid, blk, 0, s>>>(g);
-  } else {
-    k_cpart_g<2><<<grid, blk, 0, s>>>(g);
-    k_whiten_amax<<<grid, blk, 0, s>>>(g);
-    if (write_w) k_whiten_quant<true><<<grid, blk, 0, s>>>(g);
-    else k_whiten_quant<false><<<grid, blk, 0, s>>>(g);
+    if (write_w) k_tile_whiten<kCPW, true, true><<<grid, blk, 0, s>>>(g);
+    else k_tile_whiten<kCPW, true, false><<<grid, blk, 0, s>>>(g);
+    return hipGetLastError();
   }
+  k_tile_whiten<kCPW, false, false><<<grid, blk, 0, s>>>(g);
+  bool tall = false;
+  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_tiles > kPartialLimit;
+  if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
+  if (write_w) k_tile_quant<kCPW, true><<<grid, blk, 0, s>>>(g);
+  else k_tile_quant<kCPW, false><<<grid, blk, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -891,13 +919,15 @@ hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool wr
 
 hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s) {
   if (white) {
-    const dim3 grid(g.total_tiles), blk(kRowThreads);
+    const dim3 grid(g.total_tiles), blk(kTileThreads);
     if (block) {
-      k_cpart_q<true><<<grid, blk, 0, s>>>(g);
-      k_unwhiten<true><<<grid, blk, 0, s>>>(g);
+      k_tile_cpart<kCPW, true, true><<<grid, blk, 0, s>>>(g);
+      k_tile_reduce<true, true><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
+      k_tile_unwhiten<kCPW, true><<<grid, blk, 0, s>>>(g);
     } else {
-      k_cpart_q<false><<<grid, blk, 0, s>>>(g);
-      k_unwhiten<false><<<grid, blk, 0, s>>>(g);
+      k_tile_cpart<kCPW, true, false><<<grid, blk, 0, s>>>(g);
+      k_tile_reduce<true, false><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
+      k_tile_unwhiten<kCPW, false><<<grid, blk, 0, s>>>(g);
     }
   } else {
     const dim3 grid(g.total_tiles), blk(kThreads);

@@ -169,6 +169,31 @@ def test_gift_parity(d_out, d_in, block):
     _gift_parity(G, upload_factor(f), block)
 
 
+def _cheap_factor(d_in, seed):
+    """A factor with a random orthonormal U and a power-law theta, for row
+    lengths where the oracle's full refresh would take minutes."""
+    rng = np.random.default_rng(seed)
+    U = np.linalg.qr(rng.standard_normal((d_in, 32)))[0]
+    theta = 50.0 * np.arange(1, 33, dtype=np.float64) ** -1.5
+    return og.factor_from_parts(U, theta, 1e-2), U
+
+
+@pytest.mark.parametrize("d_out,d_in,block", [(48, 4096, False), (40, 4096, True),
+                                              (24, 8448, False), (20, 8448, True),
+                                              (32784, 64, False)])
+def test_gift_parity_long_and_tall(d_out, d_in, block):
+    """Rows longer than the chunks a wave keeps in registers (part of the row
+    is read twice), and a layer with more strips than the quantize pass
+    reduces itself (its amax goes through one reduction workgroup)."""
+    say("gift parity long/tall %dx%d block=%s" % (d_out, d_in, block))
+    f, U = _cheap_factor(d_in, seed=d_in + d_out)
+    rng = np.random.default_rng(d_out)
+    Z = rng.standard_normal((d_out, d_in))
+    G = (np.exp(rng.standard_normal((d_out, 1))) *
+         (Z + 10.0 * rng.standard_normal((d_out, 32)) @ U.T)).astype(np.float32)
+    _gift_parity(G, upload_factor(f), block)
+
+
 def test_gift_end_to_end_close_to_independent_oracle():
     """The oracle's own pipeline from G (fp64 whitening, its own rounding)
     agrees with the device to a few code flips."""
