@@ -36,7 +36,8 @@ namespace {
 
 constexpr int kT = 256;              // threads per workgroup
 constexpr int kSyrkTile = 128;
-constexpr int kKStep = 32;           // tokens per SYRK step
+constexpr int kKStep = 32;           // tokens per SYRK step (fp32 activations)
+constexpr int kKStepB = 64;          // tokens per SYRK step (bf16 activations)
 constexpr int kW = GIFT_MAX_SKETCH;  // largest subspace width
 constexpr int kGramParts = 16;       // Gram partial sums per input
 constexpr double kDropTol = 1e-12;   // CholeskyQR pivot drop threshold (relative)
@@ -57,13 +58,13 @@ SyrkPlan syrk_plan(int64_t d, int64_t n, int n_inputs) {
   SyrkPlan p;
   p.nb = (int)((d + kSyrkTile - 1) / kSyrkTile);
   p.npairs = p.nb * (p.nb + 1) / 2;
-  const int64_t steps = (n + kKStep - 1) / kKStep;
+  const int64_t steps = (n + kKStepB - 1) / kKStepB;
   const int64_t tiles = (int64_t)p.npairs * (n_inputs > 0 ? n_inputs : 1);
   const int64_t want = (512 + tiles - 1) / tiles;          // about 2 workgroups per CU
   const int64_t maxs = steps / 8 > 0 ? steps / 8 : 1;      // at least 8 K-steps each
   int64_t s = want < maxs ? want : maxs;
   if (s < 1) s = 1;
-  p.chunk = ((steps + s - 1) / s) * kKStep;
+  p.chunk = ((steps + s - 1) / s) * kKStepB;
   p.nsplit = (int)((n + p.chunk - 1) / p.chunk);
   return p;
 }
@@ -187,6 +188,118 @@ __device__ __forceinline__ void syrk_load_tile(float (*lds)[kKStep + 4], const f
         make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
+// bf16 SYRK with a double-buffered LDS tile: the next 64-token step is
+// loaded into registers while the MFMAs of the current one run, then stored
+// to the other buffer; one barrier per step.
+struct SyrkBuf {
+  uint16_t a[kSyrkTile][kKStepB + 8];  // row = 72 bf16 = 144 B (one column of X)
+  uint16_t b[kSyrkTile][kKStepB + 8];
+};
+
+// thread t: columns c0 + 2(t % 64), +1 for tokens n0 + 16(t / 64) .. +15
+struct SyrkRegs {
+  uint32_t v[16];
+};
+
+__device__ __forceinline__ void syrk_fetch(SyrkRegs& r, const uint16_t* X, int64_t n0,
+                                           int64_t n_end, int c0, int d) {
+  const int cp = threadIdx.x & 63, tg = threadIdx.x >> 6;
+  const int col = c0 + 2 * cp;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int64_t n = n0 + 16 * tg + s;
+    r.v[s] = (n < n_end && col < d) ? *reinterpret_cast<const uint32_t*>(X + n * d + col) : 0u;
+  }
+}
+
+__device__ __forceinline__ void syrk_stash(const SyrkRegs& r, uint16_t (*lds)[kKStepB + 8]) {
+  const int cp = threadIdx.x & 63, tg = threadIdx.x >> 6;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t* v = r.v + 8 * h;
+    uint4 lo, hi;
+    lo.x = (v[0] & 0xffffu) | (v[1] << 16);
+    lo.y = (v[2] & 0xffffu) | (v[3] << 16);
+    lo.z = (v[4] & 0xffffu) | (v[5] << 16);
+    lo.w = (v[6] & 0xffffu) | (v[7] << 16);
+    hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
+    hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
+    hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
+    hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
+    *reinterpret_cast<uint4*>(&lds[2 * cp][16 * tg + 8 * h]) = lo;
+    *reinterpret_cast<uint4*>(&lds[2 * cp + 1][16 * tg + 8 * h]) = hi;
+  }
+}
+
+// grid: (max npairs, max nsplit, inputs of this dtype); idx maps z -> input
+__global__ __launch_bounds__(kT) void k_syrk_bf16(RGroup g, int4 idx) {
+  const int zi = blockIdx.z == 0 ? idx.x : blockIdx.z == 1 ? idx.y : blockIdx.z == 2 ? idx.z : idx.w;
+  const RIn& R = g.r[zi];
+  if ((int)blockIdx.x >= R.npairs || (int)blockIdx.y >= R.nsplit) return;
+  __shared__ SyrkBuf sb[2];
+  int bi, bj;
+  decode_pair(blockIdx.x, R.nb, bi, bj);
+  const int d = R.d;
+  const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
+  const bool diag = bi == bj;
+  const int64_t n_begin = (int64_t)blockIdx.y * R.chunk;
+  const int64_t n_end = min(R.N, n_begin + R.chunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int r16 = lane & 15, gq = lane >> 4;
+  const uint16_t* X = static_cast<const uint16_t*>(R.X);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int steps = (int)((n_end - n_begin + kKStepB - 1) / kKStepB);
+  SyrkRegs ra, rb;
+  if (steps > 0) {
+    syrk_fetch(ra, X, n_begin, n_end, ci0, d);
+    if (!diag) syrk_fetch(rb, X, n_begin, n_end, cj0, d);
+    syrk_stash(ra, sb[0].a);
+    if (!diag) syrk_stash(rb, sb[0].b);
+  }
+  __syncthreads();
+  for (int st = 0; st < steps; ++st) {
+    const int64_t nn = n_begin + (int64_t)(st + 1) * kKStepB;  // beyond n_end: zeros
+    syrk_fetch(ra, X, nn, n_end, ci0, d);
+    if (!diag) syrk_fetch(rb, X, nn, n_end, cj0, d);
+    const SyrkBuf& cur = sb[st & 1];
+    const uint16_t (*tb)[kKStepB + 8] = diag ? cur.a : cur.b;
+#pragma unroll
+    for (int ks = 0; ks < kKStepB / 32; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fa[t] = *reinterpret_cast<const bf16x8*>(&cur.a[64 * wi + 16 * t + r16][32 * ks + 8 * gq]);
+        fb[t] = *reinterpret_cast<const bf16x8*>(&tb[64 * wj + 16 * t + r16][32 * ks + 8 * gq]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
+    SyrkBuf& nxt = sb[(st + 1) & 1];
+    syrk_stash(ra, nxt.a);
+    if (!diag) syrk_stash(rb, nxt.b);
+    __syncthreads();
+  }
+  // D layout: lane holds rows 4gq..4gq+3 of column r16 of each 16x16 tile
+  float* out = R.part + ((size_t)blockIdx.y * R.npairs + blockIdx.x) * kSyrkTile * kSyrkTile;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wi + 16 * a + 4 * gq + i, c = 64 * wj + 16 * b + r16;
+        out[r * kSyrkTile + c] = acc[a][b][i];
+      }
+}
+
 // grid: (max npairs, max nsplit, inputs of this dtype); idx maps z -> input
 template <bool kBf16>
 __global__ __launch_bounds__(kT) void k_syrk(RGroup g, int4 idx) {
@@ -287,12 +400,22 @@ __global__ __launch_bounds__(kT) void k_syrk_reduce(RGroup g) {
   const size_t tstride = (size_t)R.npairs * kSyrkTile * kSyrkTile;
   const float* base = R.part + (size_t)blockIdx.x * kSyrkTile * kSyrkTile;
   for (int slab = 0; slab < kSyrkTile / 32; ++slab) {
-    for (int e = threadIdx.x; e < 32 * kSyrkTile; e += kT) {
-      const int r = e / kSyrkTile, c = e % kSyrkTile;
-      const size_t o = (size_t)(32 * slab + r) * kSyrkTile + c;
-      float s = 0.f;
-      for (int k = 0; k < R.nsplit; ++k) s += base[k * tstride + o];
-      sl[r][c] = s / fn;
+    constexpr int kPer = 32 * kSyrkTile / kT;
+    float s[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) s[q] = 0.f;
+    for (int k = 0; k < R.nsplit; ++k) {
+      float v[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        v[q] = base[k * tstride + (size_t)(32 * slab) * kSyrkTile + q * kT + threadIdx.x];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) s[q] += v[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = q * kT + threadIdx.x;
+      sl[e / kSyrkTile][e % kSyrkTile] = s[q] / fn;
     }
     __syncthreads();
     for (int e = threadIdx.x; e < 32 * kSyrkTile; e += kT) {
@@ -396,21 +519,42 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which
   const int kchunks = d / 16;
   const int kc_begin = wave * kchunks / kGemmWaves, kc_end = (wave + 1) * kchunks / kGemmWaves;
   const float* arow = A + (int64_t)(row0 + r16) * d;
-  for (int kc = kc_begin; kc < kc_end; ++kc) {
+  // one K chunk of 16: this lane's 4 values of A's row and its 4 x 4 of Q
+  struct Chunk {
+    float4 a;
+    float q[4][kW / 16];
+  };
+  auto load = [&](int kc, Chunk& c) {
     const int k0 = 16 * kc + 4 * gq;
-    const float4 a = *reinterpret_cast<const float4*>(arow + k0);
-    const float av[4] = {a.x, a.y, a.z, a.w};
-    float qv[4][kW / 16];
+    c.a = *reinterpret_cast<const float4*>(arow + k0);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < kW / 16; ++t)
-        qv[s][t] = t < ntile ? Q[(int64_t)(k0 + s) * w + 16 * t + r16] : 0.f;
+        c.q[s][t] = t < ntile ? Q[(int64_t)(k0 + s) * w + 16 * t + r16] : 0.f;
+  };
+  auto comp = [&](const Chunk& c) {
+    const float av[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < kW / 16; ++t)
-        if (t < ntile) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], qv[s][t], acc[t], 0, 0, 0);
+        if (t < ntile) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], c.q[s][t], acc[t], 0, 0, 0);
+  };
+  // two-stage pipeline; the prefetch is unconditional (the last chunk is
+  // loaded twice) so the compiler waits for exactly the chunk in use
+  if (kc_begin < kc_end) {
+    Chunk c0, c1;
+    load(kc_begin, c0);
+    int kc = kc_begin;
+    for (;;) {
+      load(kc + 1 < kc_end ? kc + 1 : kc, c1);
+      comp(c0);
+      if (++kc == kc_end) break;
+      load(kc + 1 < kc_end ? kc + 1 : kc, c0);
+      comp(c1);
+      if (++kc == kc_end) break;
+    }
   }
 #pragma unroll
   for (int t = 0; t < kW / 16; ++t)
@@ -468,10 +612,16 @@ __global__ __launch_bounds__(kT) void k_gram(RGroup g, int which) {
     if (b0 + k < w) out[a * kW + b0 + k] = s[k];
 }
 
-// fixed-order reduction of the Gram partials into LDS (w x w, fp64)
-__device__ void gram_reduce(const double* part, int w, double (*G)[kW + 1]) {
-  for (int e = threadIdx.x; e < w * w; e += kT) {
-    const int a = e / w, b = e % w;
+// The small dense kernels below run one 1024-thread workgroup per input on a
+// W x W fp64 matrix in LDS (W = sketch width 32, 48 or 64, a compile-time
+// constant so no index needs a runtime division).
+constexpr int kST = 1024;
+
+// fixed-order reduction of the Gram partials into LDS (W x W, fp64)
+template <int W>
+__device__ void gram_reduce(const double* part, double (*G)[W + 1]) {
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
     double s = 0.0;
 #pragma unroll
     for (int c = 0; c < kGramParts; ++c) s += part[(size_t)c * kW * kW + a * kW + b];
@@ -480,59 +630,80 @@ __device__ void gram_reduce(const double* part, int w, double (*G)[kW + 1]) {
   __syncthreads();
 }
 
+// sum over the workgroup of one value per thread (all threads get it)
+template <int kThreads>
+__device__ double block_sum(double v, double* red) {
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
 // ---------------------------------------------------------------------------
-// 4c. Cholesky of the Gram matrix (one workgroup per input, fp64) and
+// 4c. Cholesky of the Gram matrix, G = R^T R (R upper triangular, fp64), and
 // T = R^-1.  Pivots below kDropTol * max diagonal mark a column as
 // dependent: its row of R and column of T are zero, so that column of the
 // orthonormalised Q is 0.  grid: (inputs)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_chol(RGroup g) {
+template <int W>
+__global__ __launch_bounds__(kST) void k_chol(RGroup g) {
   const RIn& Rin = g.r[blockIdx.x];
-  const int w = g.w;
-  __shared__ double G[kW][kW + 1];
-  __shared__ double R[kW][kW + 1];
-  __shared__ double T[kW][kW + 1];
-  __shared__ int keep[kW];
-  __shared__ double maxdiag;
-  gram_reduce(Rin.gram, w, G);
-  if (threadIdx.x == 0) {
-    double m = 0.0;
-    for (int i = 0; i < w; ++i) m = fmax(m, G[i][i]);
-    maxdiag = m;
+  __shared__ double G[W][W + 1];
+  __shared__ double R[W][W + 1];
+  __shared__ double T[W][W + 1];
+  __shared__ int keep[W];
+  __shared__ double red[kST / 64];
+  gram_reduce<W>(Rin.gram, G);
+  for (int e = threadIdx.x; e < W * (W + 1); e += kST) {
+    R[e / (W + 1)][e % (W + 1)] = 0.0;
+    T[e / (W + 1)][e % (W + 1)] = 0.0;
   }
-  for (int e = threadIdx.x; e < kW * (kW + 1); e += kT) R[e / (kW + 1)][e % (kW + 1)] = 0.0;
+  double dmax = threadIdx.x < W ? G[threadIdx.x][threadIdx.x] : 0.0;
+  dmax = threadIdx.x < 64 ? dmax : 0.0;
+  // max of the diagonal through the first wave
+  for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
+  if (threadIdx.x == 0) red[0] = dmax;
   __syncthreads();
-  // right-looking Cholesky, G = R^T R (R upper triangular)
-  for (int k = 0; k < w; ++k) {
-    const double piv = G[k][k];
-    const bool ok = maxdiag > 0.0 && piv > kDropTol * maxdiag;
-    const double rkk = ok ? sqrt(piv) : 0.0;
-    if (threadIdx.x == 0) keep[k] = ok;
-    for (int j = k + threadIdx.x; j < w; j += kT) R[k][j] = ok ? (j == k ? rkk : G[k][j] / rkk) : 0.0;
+  const double maxdiag = red[0];
+  // right-looking: row k of R, then the update of the trailing upper triangle
+  for (int k = 0; k < W; ++k) {
+    if (threadIdx.x >= k && threadIdx.x < W) {  // row k of R: part of the first wave
+      const double piv = G[k][k];
+      const bool ok = maxdiag > 0.0 && piv > kDropTol * maxdiag;
+      const double rkk = ok ? sqrt(piv) : 0.0;
+      const int j = threadIdx.x;
+      if (j == k) keep[k] = ok;
+      R[k][j] = ok ? (j == k ? rkk : G[k][j] / rkk) : 0.0;
+    }
     __syncthreads();
-    const int m = w - k - 1;
-    for (int e = threadIdx.x; e < m * m; e += kT) {
-      const int i = k + 1 + e / m, j = k + 1 + e % m;
-      G[i][j] -= R[k][i] * R[k][j];
+    for (int e = threadIdx.x; e < W * W; e += kST) {
+      const int i = e / W, j = e % W;
+      if (i > k && i <= j) G[i][j] -= R[k][i] * R[k][j];
     }
     __syncthreads();
   }
-  // T = R^-1, column c by thread c (back substitution in LDS, no barrier
-  // needed: a thread reads only its own column of T)
-  if (threadIdx.x < w) {
-    const int c = threadIdx.x;
-    for (int i = w - 1; i >= 0; --i) {
+  // T = R^-1 row by row from the last: T[i][c] = (delta_ic - sum_{i<j<=c}
+  // R[i][j] T[j][c]) / R[i][i]; 16 lanes per column split the sum.
+  constexpr int kLanes = 16;
+  const int c = threadIdx.x / kLanes, part = threadIdx.x % kLanes;
+  for (int i = W - 1; i >= 0; --i) {
+    double s = 0.0;
+    if (c < W && c > i)
+      for (int j = i + 1 + part; j <= c; j += kLanes) s += R[i][j] * T[j][c];
+#pragma unroll
+    for (int o = kLanes / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (c < W && part == 0 && c >= i) {
       double v = 0.0;
-      if (keep[i] && keep[c] && i <= c) {
-        double s = (i == c) ? 1.0 : 0.0;
-        for (int j = i + 1; j <= c; ++j) s -= R[i][j] * T[j][c];
-        v = s / R[i][i];
-      }
+      if (keep[i] && keep[c]) v = ((i == c ? 1.0 : 0.0) - s) / R[i][i];
       T[i][c] = v;
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < w * w; e += kT) Rin.T[(e / w) * kW + e % w] = T[e / w][e % w];
+  for (int e = threadIdx.x; e < W * W; e += kST) Rin.T[(e / W) * kW + e % W] = T[e / W][e % W];
 }
 
 // 4d. Out = In T (fp64 accumulate), Out[i][c] for c < ncols.
@@ -560,38 +731,33 @@ __global__ __launch_bounds__(kT) void k_apply(RGroup g, int which) {
 }
 
 // ---------------------------------------------------------------------------
-// 5. Rayleigh-Ritz: Jacobi eigensolver of B = Q^T A Q, sort, coefficients.
-// grid: (inputs)
+// 5. Rayleigh-Ritz: cyclic Jacobi eigensolver of B = Q^T A Q (Golub & Van
+// Loan, sym.schur2 rotations, round-robin ordering: W/2 disjoint rotations
+// per round), sort, coefficients.  In a round every 2 x 2 block of B is
+// rotated on both sides by one thread, and the pair of columns of V by
+// others, so a round takes two barriers.  grid: (inputs)
 // ---------------------------------------------------------------------------
-__device__ double block_sum(double v, double* red) {
-  v = wave_sum_f64(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double t = 0.0;
-#pragma unroll
-  for (int i = 0; i < kT / 64; ++i) t += red[i];
-  __syncthreads();
-  return t;
-}
-
-__global__ __launch_bounds__(kT) void k_ritz(RGroup g) {
+template <int W>
+__global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
+  constexpr int kP = W / 2;   // rotations per round
+  constexpr int kM = W - 1;   // rounds per sweep
   const RIn& Rin = g.r[blockIdx.x];
-  const int w = g.w, d = Rin.d;
-  __shared__ double B[kW][kW + 1];
-  __shared__ double V[kW][kW + 1];
-  __shared__ double rc[kW / 2], rs[kW / 2];
-  __shared__ int rp[kW / 2], rq[kW / 2];
-  __shared__ double ev[kW];
-  __shared__ int order[kW];
-  __shared__ double red[kT / 64];
-  gram_reduce(Rin.gram, w, B);
-  for (int e = threadIdx.x; e < w * w; e += kT) {
-    const int a = e / w, b = e % w;
+  const int d = Rin.d;
+  __shared__ double B[W][W + 1];
+  __shared__ double V[W][W + 1];
+  __shared__ double rc[kP], rs[kP];
+  __shared__ int rp[kP], rq[kP];
+  __shared__ double ev[W];
+  __shared__ int order[W];
+  __shared__ double red[kST / 64];
+  gram_reduce<W>(Rin.gram, B);
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
     V[a][b] = a == b ? 1.0 : 0.0;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < w * w; e += kT) {
-    const int a = e / w, b = e % w;
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
     if (a < b) {
       const double m = 0.5 * (B[a][b] + B[b][a]);
       B[a][b] = m;
@@ -599,23 +765,22 @@ __global__ __launch_bounds__(kT) void k_ritz(RGroup g) {
     }
   }
   __syncthreads();
-  const int m = w - 1;  // round-robin over w players (w even)
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
     double off = 0.0, tot = 0.0;
-    for (int e = threadIdx.x; e < w * w; e += kT) {
-      const int a = e / w, b = e % w;
+    for (int e = threadIdx.x; e < W * W; e += kST) {
+      const int a = e / W, b = e % W;
       const double v = B[a][b] * B[a][b];
       tot += v;
       if (a != b) off += v;
     }
-    off = block_sum(off, red);
-    tot = block_sum(tot, red);
+    off = block_sum<kST>(off, red);
+    tot = block_sum<kST>(tot, red);
     if (!(off > kJacobiTol * tot)) break;
-    for (int round = 0; round < m; ++round) {
-      if (threadIdx.x < w / 2) {
+    for (int round = 0; round < kM; ++round) {
+      if (threadIdx.x < kP) {
         const int i = threadIdx.x;
-        int p = i == 0 ? m : (round + i) % m;
-        int q = i == 0 ? round : (round - i + m) % m;
+        int p = i == 0 ? kM : (round + i) % kM;
+        int q = i == 0 ? round : (round - i + kM) % kM;
         if (p > q) { const int t = p; p = q; q = t; }
         const double apq = B[p][q], app = B[p][p], aqq = B[q][q];
         double c = 1.0, s = 0.0;
@@ -629,44 +794,44 @@ __global__ __launch_bounds__(kT) void k_ritz(RGroup g) {
         rp[i] = p; rq[i] = q; rc[i] = c; rs[i] = s;
       }
       __syncthreads();
-      // rows: B <- J^T B
-      for (int e = threadIdx.x; e < (w / 2) * w; e += kT) {
-        const int i = e / w, col = e % w;
-        const int p = rp[i], q = rq[i];
-        const double c = rc[i], s = rs[i];
-        const double bp = B[p][col], bq = B[q][col];
-        B[p][col] = c * bp - s * bq;
-        B[q][col] = s * bp + c * bq;
+      // B <- J^T B J, one 2 x 2 block (rows of pair i, columns of pair j)
+      for (int e = threadIdx.x; e < kP * kP; e += kST) {
+        const int i = e / kP, j = e % kP;
+        const int pi = rp[i], qi = rq[i], pj = rp[j], qj = rq[j];
+        const double ci = rc[i], si = rs[i], cj = rc[j], sj = rs[j];
+        const double m00 = B[pi][pj], m01 = B[pi][qj], m10 = B[qi][pj], m11 = B[qi][qj];
+        const double r00 = ci * m00 - si * m10, r01 = ci * m01 - si * m11;
+        const double r10 = si * m00 + ci * m10, r11 = si * m01 + ci * m11;
+        B[pi][pj] = cj * r00 - sj * r01;
+        B[pi][qj] = sj * r00 + cj * r01;
+        B[qi][pj] = cj * r10 - sj * r11;
+        B[qi][qj] = sj * r10 + cj * r11;
       }
-      __syncthreads();
-      // columns: B <- B J, V <- V J
-      for (int e = threadIdx.x; e < (w / 2) * w; e += kT) {
-        const int i = e / w, row = e % w;
-        const int p = rp[i], q = rq[i];
-        const double c = rc[i], s = rs[i];
-        const double bp = B[row][p], bq = B[row][q];
-        B[row][p] = c * bp - s * bq;
-        B[row][q] = s * bp + c * bq;
-        const double vp = V[row][p], vq = V[row][q];
-        V[row][p] = c * vp - s * vq;
-        V[row][q] = s * vp + c * vq;
+      // V <- V J
+      for (int e = threadIdx.x; e < W * kP; e += kST) {
+        const int row = e / kP, j = e % kP;
+        const int pj = rp[j], qj = rq[j];
+        const double cj = rc[j], sj = rs[j];
+        const double vp = V[row][pj], vq = V[row][qj];
+        V[row][pj] = cj * vp - sj * vq;
+        V[row][qj] = sj * vp + cj * vq;
       }
       __syncthreads();
     }
   }
   // sort eigenvalues descending (rank by count; ties by index)
-  if (threadIdx.x < w) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
+  if (threadIdx.x < W) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
   __syncthreads();
-  if (threadIdx.x < w) {
+  if (threadIdx.x < W) {
     const int i = threadIdx.x;
     const double x = ev[i];
     int rank = 0;
-    for (int j = 0; j < w; ++j) rank += (ev[j] > x) || (ev[j] == x && j < i);
+    for (int j = 0; j < W; ++j) rank += (ev[j] > x) || (ev[j] == x && j < i);
     order[rank] = i;
   }
   __syncthreads();
   // T[:, k] = V[:, order[k]] for the top rank
-  for (int e = threadIdx.x; e < w * kRank; e += kT) {
+  for (int e = threadIdx.x; e < W * kRank; e += kST) {
     const int r = e / kRank, k = e % kRank;
     Rin.T[r * kW + k] = V[r][order[k]];
   }
@@ -703,6 +868,18 @@ __global__ __launch_bounds__(kT) void k_ritz(RGroup g) {
     Rin.coef[GIFT_COEF_DU + k] = (float)(th / (s + s0));
     Rin.theta[k] = (float)th;
   }
+}
+
+void chol(const RGroup& g, int nb, hipStream_t st) {
+  if (g.w == 32) k_chol<32><<<nb, kST, 0, st>>>(g);
+  else if (g.w == 48) k_chol<48><<<nb, kST, 0, st>>>(g);
+  else k_chol<64><<<nb, kST, 0, st>>>(g);
+}
+
+void ritz(const RGroup& g, int nb, hipStream_t st) {
+  if (g.w == 32) k_ritz<32><<<nb, kST, 0, st>>>(g);
+  else if (g.w == 48) k_ritz<48><<<nb, kST, 0, st>>>(g);
+  else k_ritz<64><<<nb, kST, 0, st>>>(g);
 }
 
 }  // namespace
@@ -838,7 +1015,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
         const int m = ns - k < 4 ? ns - k : 4;
         int4 idx = make_int4(sel[k], m > 1 ? sel[k + 1] : 0, m > 2 ? sel[k + 2] : 0, m > 3 ? sel[k + 3] : 0);
         const dim3 grid(maxpairs, maxsplit, m);
-        if (dt) k_syrk<true><<<grid, kT, 0, st>>>(g, idx);
+        if (dt) k_syrk_bf16<<<grid, kT, 0, st>>>(g, idx);
         else k_syrk<false><<<grid, kT, 0, st>>>(g, idx);
       }
     }
@@ -852,21 +1029,21 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     k_gemm_aq<<<rows, 64 * kGemmWaves, 0, st>>>(g, 0);
     for (int s = 0; s < power_steps; ++s) {
       k_gram<<<grams, kT, 0, st>>>(g, 0);
-      k_chol<<<nb, kT, 0, st>>>(g);
+      chol(g, nb, st);
       k_apply<<<rows, kT, 0, st>>>(g, 2);  // Q = Y T
       k_gemm_aq<<<rows, 64 * kGemmWaves, 0, st>>>(g, 1);
     }
     // final basis: CholeskyQR2 of Y
     k_gram<<<grams, kT, 0, st>>>(g, 0);
-    k_chol<<<nb, kT, 0, st>>>(g);
+    chol(g, nb, st);
     k_apply<<<rows, kT, 0, st>>>(g, 0);  // Q1 = Y T
     k_gram<<<grams, kT, 0, st>>>(g, 1);
-    k_chol<<<nb, kT, 0, st>>>(g);
+    chol(g, nb, st);
     k_apply<<<rows, kT, 0, st>>>(g, 1);  // Q = Q1 T
     // 3. Rayleigh-Ritz on B = Q^T A Q
     k_gemm_aq<<<rows, 64 * kGemmWaves, 0, st>>>(g, 1);  // Y = A Q
     k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
-    k_ritz<<<nb, kT, 0, st>>>(g);
+    ritz(g, nb, st);
     k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V
     e = hipGetLastError();
     if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
