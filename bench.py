@@ -10,9 +10,10 @@ per-tensor E4M3.
 One step = the per-step path of GIFT over the workload: the grouped
 whiten + quantize of the whitened gradients, the grouped dequantize +
 un-whiten, the Euclidean round trip of the layers not selected (none in the
-default workload), and the grouped factor refresh of every input run inside
-the timed loop every 50 steps (the paper's refresh interval), so it is
-amortized exactly as in training.  Each step takes the next gradient set
+default workload) -- prepared once and captured in a HIP graph, one replay
+per step -- and the grouped factor refresh of every input, run eagerly
+inside the timed loop every 50 steps (the paper's refresh interval), so it
+is amortized exactly as in training.  Each step takes the next gradient set
 from a ring of resident sets whose footprint is several times the 256 MB
 Infinity Cache, so the gradients come from HBM.  Inputs are resident before
 the timed region.  One JSON line on stdout.
@@ -200,40 +201,52 @@ def main():
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(s, timed):
-        gl, el = ring[s % len(ring)]
+    # Per ring slot the per-step path -- grouped whiten + quantize, grouped
+    # dequantize + un-whiten, Euclidean round trip of the other layers -- as
+    # prepared calls captured in one HIP graph (one launch per step).
+    def slot_calls(gl, el):
+        calls = []
+        if gl:
+            calls.append(fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, flags=flags, ws=ws_w))
+            calls.append(fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d))
+        if el:
+            calls.append(fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, flags=flags, ws=ws_e))
+        return calls
+
+    def capture(calls):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in calls:
+                c()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                c()
+        return graph, calls         # the calls own the workspaces the graph writes
+
+    slot_graphs = [capture(slot_calls(gl, el)) for gl, el in ring]
+    torch.cuda.synchronize()
+
+    def step(s):
         if s % REFRESH_EVERY == 0:
             refresh_all(7 * s + 1)
-        marks = [ev(), ev(), ev()] if timed else None
-        if timed:
-            marks[0].record()
-        if gl:
-            fg.gift_whiten_quantize(gl, flags=flags, ws=ws_w)
-        if timed:
-            marks[1].record()
-        if gl:
-            fg.gift_dequant_unwhiten(gl, ws=ws_d)
-        if el:
-            fg.gift_euclid_fp8_roundtrip(el, flags=flags, ws=ws_e)
-        if timed:
-            marks[2].record()
-        return marks
+        slot_graphs[s % len(ring)][0].replay()
 
     for s in range(args.warmup):
-        step(s + 1, False)          # warm-up steps never hit the refresh slot
+        step(s + 1)
     torch.cuda.synchronize()
     log(args, "timing %d steps" % args.steps)
-    marks = []
     t0 = time.perf_counter()
     for s in range(args.steps):
-        marks.append(step(s, True))
+        step(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    t_wq = np.array([a.elapsed_time(b) for a, b, c in marks]) * 1e-3
     value = grad_bytes * args.steps / elapsed / 1e9
     ms_per_step = elapsed / args.steps * 1e3
 
-    # ---- the pieces on their own -------------------------------------------
+    # ---- the pieces on their own (graph replays between events) --------------
     def timed(fn, n=10):
         a, b = ev(), ev()
         fn()
@@ -245,20 +258,26 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e-3
 
+    def timed_graph(calls, n=20):
+        if not calls:
+            return 0.0
+        held = [capture(c) for c in calls]
+        torch.cuda.synchronize()
+        return timed(lambda: [g.replay() for g, _ in held], n) / len(held)
+
     refresh_s = timed(lambda: refresh_all(11), 3)
     syrk_flops = sum(2.0 * s.tokens * s.d_in * s.d_in for s in w.inputs)
-    t_whiten = float(np.median(t_wq))
-    t_dq = timed(lambda: fg.gift_dequant_unwhiten(gl0, ws=ws_d)) if gl0 else 0.0
-    t_eu = timed(lambda: fg.gift_euclid_fp8_roundtrip(el0, ws=ws_e)) if el0 else 0.0
+    # one launch of each entry point per ring slot, replayed in turn
+    t_whiten = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, ws=ws_w)]
+                            for gl, _ in ring if gl])
+    t_dq = timed_graph([[fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d)] for gl, _ in ring if gl])
+    t_eu = timed_graph([[fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, ws=ws_e)] for _, el in ring if el])
     gift_elems = sum(L.d_out * L.d_in for L in gl0)
     all_eu = [fg.Layer(L.G) for L in gl0 + el0]
-    ws_all = ws_for(2, all_eu)
-    t_eu_all = timed(lambda: fg.gift_euclid_fp8_roundtrip(all_eu, ws=ws_all))
+    t_eu_all = timed_graph([[fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, all_eu)]])
     blk = [fg.Layer(L.G, factor=L.factor, block128=True) for L in gl0]
-    ws_b = ws_for(0, blk, fg.SCALE_BLOCK128)
-    ws_b2 = ws_for(1, blk, fg.SCALE_BLOCK128)
-    t_b = timed(lambda: (fg.gift_whiten_quantize(blk, scaling=fg.SCALE_BLOCK128, ws=ws_b),
-                         fg.gift_dequant_unwhiten(blk, scaling=fg.SCALE_BLOCK128, ws=ws_b2))) \
+    t_b = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, blk, fg.SCALE_BLOCK128),
+                        fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, blk, fg.SCALE_BLOCK128)]]) * 2 \
         if blk else 0.0
     del all_eu, blk
 

@@ -302,6 +302,52 @@ def gift_roundtrip_error(layers, out=None, ws=None, stream=None):
     return out
 
 
+class GroupCall:
+    """One grouped round-trip call prepared once: the layer descriptor array,
+    the workspace and the argument list are built here, so calling it only
+    enqueues the kernels on the current (or given) stream.  Meant for loops
+    and for HIP-graph capture; the layers' tensors must stay where they are.
+
+    op: OP_WHITEN_QUANTIZE, OP_DEQUANT_UNWHITEN, OP_EUCLID_ROUNDTRIP or
+    OP_ROUNDTRIP_ERROR (then out is the (n, 2) fp64 result, allocated when
+    not given).
+    """
+
+    def __init__(self, op, layers, scaling=SCALE_TENSOR, flags=None, ws=None, out=None):
+        lib = load()
+        self.layers = list(layers)
+        self.op = op
+        self._arr = _layers_array(self.layers)
+        n = len(self.layers)
+        dev = _device_of(self.layers)
+        sc = SCALE_TENSOR if op == OP_ROUNDTRIP_ERROR else scaling
+        need = lib.gift_group_workspace_bytes(op, self._arr, n, sc)
+        self.ws = _workspace(need, dev, ws)
+        self.flags = flags
+        wsp, wsb = _ptr(self.ws), self.ws.numel() * self.ws.element_size()
+        if op == OP_WHITEN_QUANTIZE:
+            self._fn = lib.gift_whiten_quantize
+            self._args = (self._arr, n, scaling, _ptr(flags), wsp, wsb)
+        elif op == OP_DEQUANT_UNWHITEN:
+            self._fn = lib.gift_dequant_unwhiten
+            self._args = (self._arr, n, scaling, wsp, wsb)
+        elif op == OP_EUCLID_ROUNDTRIP:
+            self._fn = lib.gift_euclid_fp8_roundtrip
+            self._args = (self._arr, n, scaling, _ptr(flags), wsp, wsb)
+        elif op == OP_ROUNDTRIP_ERROR:
+            if out is None:
+                out = torch.empty(n, 2, dtype=torch.float64, device=dev)
+            _dev(out, torch.float64, (n, 2), "out")
+            self.out = out
+            self._fn = lib.gift_roundtrip_error
+            self._args = (self._arr, n, _ptr(out), wsp, wsb)
+        else:
+            raise ValueError("unknown op %r" % (op,))
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)))
+
+
 def gift_factor_pack_bytes(d_in):
     return int(load().gift_factor_pack_bytes(d_in))
 

@@ -406,10 +406,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
 // tensor's inverse scale for per-tensor scaling).  One workgroup per row block.
 // ---------------------------------------------------------------------------
 template <bool kDequant, bool kBlockScale>
-__global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
-  const LayerDev L = gd.L[find_layer_rb(gd, blockIdx.x)];
-  const int64_t rb = blockIdx.x - L.rb_begin;
-  const int rt = threadIdx.x >> 6, lane = threadIdx.x & 63;  // one lane of one 16-row tile
+__device__ __forceinline__ void reduce_row_block(const LayerDev& L, int64_t rb, int tid) {
+  const int rt = tid >> 6, lane = tid & 63;  // one lane of one 16-row tile
   const float* dk = L.coef + (kDequant ? GIFT_COEF_DU : GIFT_COEF_DW);
   const float extra = (kDequant && !kBlockScale) ? L.inv[0] : 1.f;
   float d8[8];
@@ -442,6 +440,12 @@ __global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
   uint4* out = reinterpret_cast<uint4*>(L.cfin) + rb * kCOp;
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp) out[(rt * 3 + sp) * 64 + lane] = __builtin_bit_cast(uint4, cb[sp]);
+}
+
+template <bool kDequant, bool kBlockScale>
+__global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
+  const LayerDev L = gd.L[find_layer_rb(gd, blockIdx.x)];
+  reduce_row_block<kDequant, kBlockScale>(L, blockIdx.x - L.rb_begin, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
