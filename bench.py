@@ -78,16 +78,21 @@ def kernel_source_hash():
 
 
 def load_traffic(kernel, src_hash, elems):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
-    path = os.path.join(HERE, "profiles", "traffic_%s.json" % kernel)
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (its "traffic:" lines), if it was taken on the current kernel sources and
+    the same number of elements; else None."""
+    path = os.path.join(HERE, "profiles", "hbm_traffic_roundtrip_llama_block_h1024.md")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
-        t = json.load(fh)
-    if t.get("source_hash") != src_hash or t.get("elements") != elems:
-        return None
-    return t.get("hbm_bytes_per_launch")
+        for line in fh:
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(f.split("=", 1) for f in line.split()[1:])
+            if (kv.get("kernel") == kernel and kv.get("source_hash") == src_hash
+                    and int(kv.get("elements", -1)) == elems):
+                return int(kv["hbm_bytes_per_launch"])
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -201,18 +206,6 @@ def main():
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    # Per ring slot the per-step path -- grouped whiten + quantize, grouped
-    # dequantize + un-whiten, Euclidean round trip of the other layers -- as
-    # prepared calls captured in one HIP graph (one launch per step).
-    def slot_calls(gl, el):
-        calls = []
-        if gl:
-            calls.append(fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, flags=flags, ws=ws_w))
-            calls.append(fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d))
-        if el:
-            calls.append(fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, flags=flags, ws=ws_e))
-        return calls
-
     def capture(calls):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -226,25 +219,57 @@ def main():
                 c()
         return graph, calls         # the calls own the workspaces the graph writes
 
-    slot_graphs = [capture(slot_calls(gl, el)) for gl, el in ring]
+    # Per ring slot the per-step path -- grouped whiten + quantize, grouped
+    # dequantize + un-whiten, Euclidean round trip of the other layers -- as
+    # prepared calls, each entry point captured in a HIP graph of its own so
+    # that events between the replays time every entry point inside the timed
+    # steps.
+    slots = []
+    for gl, el in ring:
+        parts = []
+        if gl:
+            parts.append(("whiten_quantize", capture(
+                [fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, flags=flags, ws=ws_w)])))
+            parts.append(("dequant_unwhiten", capture(
+                [fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d)])))
+        if el:
+            parts.append(("euclid_rest", capture(
+                [fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, flags=flags, ws=ws_e)])))
+        slots.append(parts)
     torch.cuda.synchronize()
 
-    def step(s):
+    def step(s, marks=None):
         if s % REFRESH_EVERY == 0:
             refresh_all(7 * s + 1)
-        slot_graphs[s % len(ring)][0].replay()
+        for name, (graph, _) in slots[s % len(ring)]:
+            if marks is None:
+                graph.replay()
+                continue
+            e0, e1 = ev(), ev()
+            e0.record()
+            graph.replay()
+            e1.record()
+            marks.append((name, e0, e1))
 
     for s in range(args.warmup):
         step(s + 1)
     torch.cuda.synchronize()
     log(args, "timing %d steps" % args.steps)
+    marks = []
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(s)
+        step(s, marks)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     value = grad_bytes * args.steps / elapsed / 1e9
     ms_per_step = elapsed / args.steps * 1e3
+    per_entry = {}
+    for name, e0, e1 in marks:
+        per_entry.setdefault(name, []).append(e0.elapsed_time(e1) * 1e-3)
+    live = {k: sum(v) / len(v) for k, v in per_entry.items()}
+    t_whiten = live.get("whiten_quantize", 0.0)
+    t_dq = live.get("dequant_unwhiten", 0.0)
+    t_eu = live.get("euclid_rest", 0.0)
 
     # ---- the pieces on their own (graph replays between events) --------------
     def timed(fn, n=10):
@@ -267,17 +292,12 @@ def main():
 
     refresh_s = timed(lambda: refresh_all(11), 3)
     syrk_flops = sum(2.0 * s.tokens * s.d_in * s.d_in for s in w.inputs)
-    # one launch of each entry point per ring slot, replayed in turn
-    t_whiten = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, ws=ws_w)]
-                            for gl, _ in ring if gl])
-    t_dq = timed_graph([[fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d)] for gl, _ in ring if gl])
-    t_eu = timed_graph([[fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, ws=ws_e)] for _, el in ring if el])
     gift_elems = sum(L.d_out * L.d_in for L in gl0)
     all_eu = [fg.Layer(L.G) for L in gl0 + el0]
     t_eu_all = timed_graph([[fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, all_eu)]])
     blk = [fg.Layer(L.G, factor=L.factor, block128=True) for L in gl0]
     t_b = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, blk, fg.SCALE_BLOCK128),
-                        fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, blk, fg.SCALE_BLOCK128)]]) * 2 \
+                        fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, blk, fg.SCALE_BLOCK128)]]) \
         if blk else 0.0
     del all_eu, blk
 
