@@ -183,7 +183,7 @@ __device__ __forceinline__ void with_count(int n, F&& f) {
 }
 
 struct Tile {
-  int64_t row[kTR];  // this lane's gradient row in each 16-row tile (clamped)
+  int row[kTR];      // this lane's gradient row in each 16-row tile (clamped)
   bool ok[kTR];      // row < d_out
   int64_t rb;        // row block
   int cg;            // column group
@@ -205,7 +205,7 @@ __device__ __forceinline__ Tile tile_ctx(const LayerDev& L, int tile) {
   for (int rt = 0; rt < kTR; ++rt) {
     const int64_t r = x.rb * kTileRows + 16 * rt + x.r16;
     x.ok[rt] = r < L.d_out;
-    x.row[rt] = x.ok[rt] ? r : L.d_out - 1;
+    x.row[rt] = (int)(x.ok[rt] ? r : L.d_out - 1);
   }
   const int nch = (int)(L.d_in / kChunk);
   x.c0 = (x.cg * kTW + x.wave) * kCPW;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
             const int64_t o = x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g;
             const float4 v = w[j][rt][t];
             *reinterpret_cast<uint32_t*>(L.q + o) = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
-            if constexpr (kWriteW) *reinterpret_cast<float4*>(L.Wout + o) = v;
+            if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = v;
           }
         });
       });
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
         for (int t = 0; t < 2; ++t) {
           const int64_t o = x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g;
           *reinterpret_cast<uint32_t*>(L.q + o) = codes[j][rt][t];
-          if constexpr (kWriteW) *reinterpret_cast<float4*>(L.Wout + o) = wv[j][rt][t];
+          if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = wv[j][rt][t];
         }
       }
     });
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
     if (!act) continue;
     const uint32_t c = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
     *reinterpret_cast<uint32_t*>(L.q + e) = c;
-    if (kWriteW) *reinterpret_cast<float4*>(L.Wout + e) = v;
+    if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + e) = v;
     if (kDeq) {
       float4 o;
       o.x = e4m3_decode(c, 0) * sc.inv;

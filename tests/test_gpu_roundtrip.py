@@ -251,7 +251,12 @@ def test_grouped_launch_over_many_mixed_layers():
             specs.append((rng.standard_normal((d_out, 128)).astype(np.float32), None))
     for block in (False, True):
         sc = fg.SCALE_BLOCK128 if block else fg.SCALE_TENSOR
-        group = [fg.Layer(to_dev(G), factor=f, block128=block) for G, f in specs]
+        # W_out on every other layer only: a launch writes W for exactly those
+        group = []
+        for i, (G, f) in enumerate(specs):
+            Gd = to_dev(G)
+            group.append(fg.Layer(Gd, factor=f, block128=block,
+                                  W_out=torch.full_like(Gd, 7.0) if i % 2 else None))
         fg.gift_whiten_quantize(group, scaling=sc)
         fg.gift_dequant_unwhiten(group, scaling=sc)
         err = host(fg.gift_roundtrip_error(group))
@@ -261,6 +266,13 @@ def test_grouped_launch_over_many_mixed_layers():
             fg.gift_dequant_unwhiten([one], scaling=sc)
             assert np.array_equal(host(group[i].q), host(one.q)), i
             assert np.array_equal(host(group[i].G_hat), host(one.G_hat)), i
+            if i % 2:
+                Wg = host(group[i].W_out)
+                if f is None:
+                    assert np.array_equal(Wg, G), i
+                else:
+                    U, alpha, _, dw, _ = factor_host(f)
+                    assert rel_fro(Wg, og.whiten_with(G, U, alpha, dw)) <= TOL, i
             e, gs = og.error_sums(G, host(one.G_hat))
             assert abs(err[i, 0] - e) <= 1e-12 * max(e, 1e-300) and abs(err[i, 1] - gs) <= 1e-12 * gs
         # Euclidean layers of the group also match the oracle exactly
