@@ -25,7 +25,6 @@ the timed region.  One JSON line on stdout.
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -70,11 +69,15 @@ def log(args, msg):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for name in ("roundtrip.hip", "device.hpp", "refresh.hip"):
-        with open(os.path.join(HERE, "fac_whitening_gift_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel sources of the loaded library; warns when the
+    sources on disk differ from what the library was built from."""
+    import fac_whitening_gift_amd as fg
+    from fac_whitening_gift_amd.build import source_hash
+    built, disk = fg.build_hash(), source_hash()
+    if built != disk:
+        print("[bench] warning: libgift.so was built from other sources (%s) than the ones on "
+              "disk (%s); rebuild it" % (built, disk), file=sys.stderr, flush=True)
+    return built
 
 
 def load_traffic(kernel, src_hash, elems):
@@ -221,55 +224,43 @@ def main():
 
     # Per ring slot the per-step path -- grouped whiten + quantize, grouped
     # dequantize + un-whiten, Euclidean round trip of the other layers -- as
-    # prepared calls, each entry point captured in a HIP graph of its own so
-    # that events between the replays time every entry point inside the timed
-    # steps.
-    slots = []
-    for gl, el in ring:
-        parts = []
+    # prepared calls captured in one HIP graph (one launch per step), and each
+    # entry point also in a graph of its own for the per-call timings below.
+    def entry_calls(gl, el):
+        calls = []
         if gl:
-            parts.append(("whiten_quantize", capture(
-                [fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, flags=flags, ws=ws_w)])))
-            parts.append(("dequant_unwhiten", capture(
-                [fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d)])))
+            calls.append(("whiten_quantize",
+                          fg.GroupCall(fg.OP_WHITEN_QUANTIZE, gl, flags=flags, ws=ws_w)))
+            calls.append(("dequant_unwhiten", fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, gl, ws=ws_d)))
         if el:
-            parts.append(("euclid_rest", capture(
-                [fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, flags=flags, ws=ws_e)])))
-        slots.append(parts)
+            calls.append(("euclid_rest",
+                          fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, el, flags=flags, ws=ws_e)))
+        return calls
+
+    slot_graphs, entry_graphs = [], {}
+    for gl, el in ring:
+        calls = entry_calls(gl, el)
+        slot_graphs.append(capture([c for _, c in calls]))
+        for name, c in calls:
+            entry_graphs.setdefault(name, []).append(capture([c]))
     torch.cuda.synchronize()
 
-    def step(s, marks=None):
+    def step(s):
         if s % REFRESH_EVERY == 0:
             refresh_all(7 * s + 1)
-        for name, (graph, _) in slots[s % len(ring)]:
-            if marks is None:
-                graph.replay()
-                continue
-            e0, e1 = ev(), ev()
-            e0.record()
-            graph.replay()
-            e1.record()
-            marks.append((name, e0, e1))
+        slot_graphs[s % len(ring)][0].replay()
 
     for s in range(args.warmup):
         step(s + 1)
     torch.cuda.synchronize()
     log(args, "timing %d steps" % args.steps)
-    marks = []
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(s, marks)
+        step(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     value = grad_bytes * args.steps / elapsed / 1e9
     ms_per_step = elapsed / args.steps * 1e3
-    per_entry = {}
-    for name, e0, e1 in marks:
-        per_entry.setdefault(name, []).append(e0.elapsed_time(e1) * 1e-3)
-    live = {k: sum(v) / len(v) for k, v in per_entry.items()}
-    t_whiten = live.get("whiten_quantize", 0.0)
-    t_dq = live.get("dequant_unwhiten", 0.0)
-    t_eu = live.get("euclid_rest", 0.0)
 
     # ---- the pieces on their own (graph replays between events) --------------
     def timed(fn, n=10):
@@ -292,6 +283,18 @@ def main():
 
     refresh_s = timed(lambda: refresh_all(11), 3)
     syrk_flops = sum(2.0 * s.tokens * s.d_in * s.d_in for s in w.inputs)
+    # Each entry point on its own: its graph for every ring slot replayed in
+    # turn, back to back between two events on the launch stream (torch's
+    # current stream, where the graphs replay), right after the timed steps.
+    def entry_time(name, n=20):
+        held = entry_graphs.get(name)
+        if not held:
+            return 0.0
+        return timed(lambda: [g.replay() for g, _ in held], n) / len(held)
+
+    t_whiten = entry_time("whiten_quantize")
+    t_dq = entry_time("dequant_unwhiten")
+    t_eu = entry_time("euclid_rest")
     gift_elems = sum(L.d_out * L.d_in for L in gl0)
     all_eu = [fg.Layer(L.G) for L in gl0 + el0]
     t_eu_all = timed_graph([[fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, all_eu)]])

@@ -35,7 +35,7 @@ EXPORTS = (
     "gift_dequant_unwhiten", "gift_euclid_fp8_roundtrip", "gift_roundtrip_error",
     "gift_group_workspace_bytes", "gift_status_string", "gift_last_error",
     "gift_abi_version", "gift_draw_sketch", "gift_factor_pack_bytes", "gift_prepare_factor",
-    "gift_refresh_factors", "gift_refresh_group_workspace_bytes",
+    "gift_refresh_factors", "gift_refresh_group_workspace_bytes", "gift_build_hash",
 )
 
 
@@ -90,6 +90,7 @@ def load():
         "gift_status_string": (ctypes.c_char_p, [I]),
         "gift_last_error": (ctypes.c_char_p, []),
         "gift_abi_version": (I, []),
+        "gift_build_hash": (ctypes.c_char_p, []),
         "gift_draw_sketch": (I, [P, I64, I, U64, P]),
         "gift_factor_pack_bytes": (SZ, [I64]),
         "gift_prepare_factor": (I, [ctypes.POINTER(_Factor), P]),
@@ -102,6 +103,11 @@ def load():
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def build_hash():
+    """Hash of the sources the loaded libgift.so was built from."""
+    return load().gift_build_hash().decode()
 
 
 def status_name(s):

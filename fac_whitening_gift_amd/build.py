@@ -5,6 +5,7 @@ Every source is compiled on every call; objects go to _build/ next to this
 file and the library to fac_whitening_gift_amd/libgift.so.
 """
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -30,6 +31,21 @@ HIPFLAGS = [
 ]
 
 
+def source_hash():
+    """First 16 hex digits of the SHA-256 of every source the library is
+    built from (csrc/ and include/, in name order); compiled into the
+    library and returned by gift_build_hash()."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))]
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    for path in files:
+        if os.path.isfile(path):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -37,10 +53,10 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src):
+def _compile(src, defines=()):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + HIPFLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + HIPFLAGS + list(defines) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -51,8 +67,9 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
+    defines = ['-DGIFT_BUILD_HASH="%s"' % source_hash()]
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, defines), SOURCES))
     for _, msgs in results:
         if msgs.strip() and verbose:
             print(msgs, file=sys.stderr)

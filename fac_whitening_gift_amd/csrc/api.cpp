@@ -299,6 +299,11 @@ extern "C" {
 
 int gift_abi_version(void) { return GIFT_ABI_VERSION; }
 
+#ifndef GIFT_BUILD_HASH
+#define GIFT_BUILD_HASH "unknown"
+#endif
+const char* gift_build_hash(void) { return GIFT_BUILD_HASH; }
+
 const char* gift_last_error(void) { return t_err.c_str(); }
 
 const char* gift_status_string(int s) {

@@ -264,6 +264,9 @@ const char *gift_status_string(int status);
 /* Thread-local detail of the last failing call on this thread. */
 const char *gift_last_error(void);
 int gift_abi_version(void);
+/* Hash of the sources the library was built from (16 hex digits), so that a
+ * measurement can name the kernels it ran; "unknown" if not set by the build. */
+const char *gift_build_hash(void);
 
 #ifdef __cplusplus
 }
