@@ -21,7 +21,8 @@ BLOCK = 128
 GIFT_OK = 0
 DTYPE_F32, DTYPE_BF16 = 0, 1
 DAMP_FLOOR, DAMP_FLOOR_PLUS_TAIL = 0, 1
-SCALE_TENSOR, SCALE_BLOCK128 = 0, 1
+SCALE_TENSOR, SCALE_BLOCK128, SCALE_MXFP4 = 0, 1, 2
+MX_BLOCK = 32
 FLAG_NONFINITE, FLAG_ZERO_AMAX = 1, 2
 OP_WHITEN_QUANTIZE, OP_DEQUANT_UNWHITEN, OP_EUCLID_ROUNDTRIP, OP_ROUNDTRIP_ERROR = 0, 1, 2, 3
 
@@ -188,12 +189,14 @@ class Factor:
 class Layer:
     """One layer of a grouped call: G (d_out x d_in fp32) and its outputs.
 
-    q, inv_scale and G_hat are allocated on G's device when not given;
-    inv_scale has 1 element, or d_out x d_in/128 for block scaling.
+    q, inv_scale and G_hat are allocated on G's device when not given:
+    E4M3 codes d_out x d_in with inv_scale of 1 float (per tensor) or
+    d_out x d_in/128 floats (block128=True); with mxfp4=True, MXFP4 codes
+    d_out x d_in/2 bytes and d_out x d_in/32 E8M0 scale bytes.
     """
 
     def __init__(self, G, factor=None, q=None, inv_scale=None, G_hat=None, W_out=None,
-                 block128=False, d_out=None, d_in=None, allocate=True):
+                 block128=False, d_out=None, d_in=None, allocate=True, mxfp4=False):
         if G is not None:
             d_out, d_in = G.shape
             dev = G.device
@@ -202,21 +205,27 @@ class Layer:
         self.d_out, self.d_in = int(d_out), int(d_in)
         self.G = G
         self.factor = factor
+        self.mxfp4 = bool(mxfp4)
+        qshape = (self.d_out, self.d_in // 2) if mxfp4 else (self.d_out, self.d_in)
         if allocate:
             if q is None:
-                q = torch.empty(self.d_out, self.d_in, dtype=torch.uint8, device=dev)
+                q = torch.empty(qshape, dtype=torch.uint8, device=dev)
             if inv_scale is None:
-                shape = (self.d_out, self.d_in // BLOCK) if block128 else (1,)
-                inv_scale = torch.empty(shape, dtype=torch.float32, device=dev)
+                if mxfp4:
+                    inv_scale = torch.empty(self.d_out, self.d_in // MX_BLOCK, dtype=torch.uint8,
+                                            device=dev)
+                else:
+                    shape = (self.d_out, self.d_in // BLOCK) if block128 else (1,)
+                    inv_scale = torch.empty(shape, dtype=torch.float32, device=dev)
             if G_hat is None:
                 G_hat = torch.empty(self.d_out, self.d_in, dtype=torch.float32, device=dev)
         self.q, self.inv_scale, self.G_hat, self.W_out = q, inv_scale, G_hat, W_out
         shape = (self.d_out, self.d_in)
         _dev(G, torch.float32, shape, "G")
-        _dev(q, torch.uint8, shape, "q")
+        _dev(q, torch.uint8, qshape, "q")
         _dev(G_hat, torch.float32, shape, "G_hat")
         _dev(W_out, torch.float32, shape, "W_out")
-        _dev(inv_scale, torch.float32, None, "inv_scale")
+        _dev(inv_scale, torch.uint8 if mxfp4 else torch.float32, None, "inv_scale")
         if factor is not None and factor.d_in != self.d_in:
             raise ValueError("factor d_in %d != layer d_in %d" % (factor.d_in, self.d_in))
 

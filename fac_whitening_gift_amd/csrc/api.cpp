@@ -10,10 +10,10 @@
 #include "device.hpp"
 
 namespace gift {
-hipError_t launch_whiten_quantize(const GroupDev& g, bool block, bool write_w, hipStream_t s);
-hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool write_w,
+hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s);
+hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool write_w,
                                 hipStream_t s);
-hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s);
+hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s);
 hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
 int64_t row_blocks(int64_t d_out);
@@ -175,7 +175,8 @@ gift_status run_packs(const Packs& p, void* ws, hipStream_t st) {
 gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
   if (n < 0) return fail(GIFT_ERR_INVALID_ARG, "n_layers < 0");
   if (n > 0 && !layers) return fail(GIFT_ERR_INVALID_ARG, "layers is NULL");
-  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128)
+  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128 &&
+      scaling != GIFT_SCALE_MXFP4)
     return fail(GIFT_ERR_INVALID_ARG, "unknown scaling %d", scaling);
   for (int i = 0; i < n; ++i) {
     const gift_layer& L = layers[i];
@@ -187,6 +188,8 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
       return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: d_in %% 4 != 0", i);
     if (scaling == GIFT_SCALE_BLOCK128 && L.d_in % kBlock)
       return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: block scaling needs d_in %% 128 == 0", i);
+    if (scaling == GIFT_SCALE_MXFP4 && L.d_in % kMxBlock)
+      return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: MXFP4 needs d_in %% 32 == 0", i);
     const bool need_g = op != Op::Dequant;
     const bool need_q = op != Op::Error;
     const bool need_ghat = op != Op::Whiten;
@@ -319,7 +322,7 @@ const char* gift_status_string(int s) {
 
 size_t gift_group_workspace_bytes(int op, const gift_layer* layers, int n_layers, int scaling) {
   if (n_layers <= 0 || !layers) return 0;
-  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  const bool block = scaling != GIFT_SCALE_TENSOR;  // no per-tensor amax
   switch (op) {
     case GIFT_OP_WHITEN_QUANTIZE: return group_ws(layers, n_layers, Op::Whiten, block);
     case GIFT_OP_DEQUANT_UNWHITEN: return group_ws(layers, n_layers, Op::Dequant, block);
@@ -333,7 +336,7 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
                                  uint32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
   gift_status s = check_layers(layers, n_layers, Op::Whiten, scaling);
   if (s != GIFT_OK) return s;
-  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  const bool block = scaling != GIFT_SCALE_TENSOR;  // no per-tensor amax
   s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Whiten, block));
   if (s != GIFT_OK) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -349,12 +352,12 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
     if (white)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
-                        return launch_whiten_quantize(g, block, any_w, st);
+                        return launch_whiten_quantize(g, scaling, any_w, st);
                       });
     else
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_flat, [&](const GroupDev& g, int) {
-                        return launch_flat_quantize(g, block, false, any_w, st);
+                        return launch_flat_quantize(g, scaling, false, any_w, st);
                       });
     if (s != GIFT_OK) return s;
   }
@@ -365,7 +368,7 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
                                   size_t ws_bytes, void* stream) {
   gift_status s = check_layers(layers, n_layers, Op::Dequant, scaling);
   if (s != GIFT_OK) return s;
-  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  const bool block = scaling != GIFT_SCALE_TENSOR;
   s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Dequant, block));
   if (s != GIFT_OK) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -378,7 +381,7 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
       return white ? row_tiles(L) : tiles_flat(L);
     };
     s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles,
-                    [&](const GroupDev& g, int) { return launch_dequant(g, block, white, st); });
+                    [&](const GroupDev& g, int) { return launch_dequant(g, scaling, white, st); });
     if (s != GIFT_OK) return s;
   }
   return GIFT_OK;
@@ -389,7 +392,7 @@ gift_status gift_euclid_fp8_roundtrip(const gift_layer* layers, int n_layers, in
                                       void* stream) {
   gift_status s = check_layers(layers, n_layers, Op::Euclid, scaling);
   if (s != GIFT_OK) return s;
-  const bool block = scaling == GIFT_SCALE_BLOCK128;
+  const bool block = scaling != GIFT_SCALE_TENSOR;
   s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::Euclid, block));
   if (s != GIFT_OK) return s;
   bool any_w = false;
@@ -398,7 +401,7 @@ gift_status gift_euclid_fp8_roundtrip(const gift_layer* layers, int n_layers, in
   return run_grouped(layers, n_layers, Op::Euclid, block, ws, dev_flags, nullptr,
                      [](const gift_layer&) { return true; }, tiles_flat,
                      [&](const GroupDev& g, int) {
-                       return launch_flat_quantize(g, block, true, any_w, st);
+                       return launch_flat_quantize(g, scaling, true, any_w, st);
                      });
 }
 

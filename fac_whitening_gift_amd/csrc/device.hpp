@@ -94,6 +94,65 @@ __device__ __forceinline__ Scale scale_from_amax_bits(uint32_t bits) {
 }
 
 // ---------------------------------------------------------------------------
+// OCP MX FP4 (MXFP4): E2M1 elements, one E8M0 scale 2^(code - 127) per 32
+// consecutive elements of a row, code = floor(log2 amax) - 2 + 127 clamped
+// to [0, 254]; 0xFF is the NaN scale.  The gfx950 FP4 conversions take the
+// scale as an fp32 operand of which they use only the exponent field, round
+// to nearest even, saturate to +-6 (+-inf included), keep the sign of zero,
+// and put the first value of a pair in the low nibble.  NaN inputs are
+// mapped to +0 here; they occur only in blocks whose amax is NaN, which
+// decode to NaN through their scale.
+// ---------------------------------------------------------------------------
+constexpr int kMxBlock = 32;
+constexpr uint32_t kMxScaleNaN = 0xFFu;
+
+// E8M0 code of a block whose amax is given as |x| bits; flags as for E4M3
+__device__ __forceinline__ uint32_t mx_scale_code(uint32_t bits, uint32_t& flags) {
+  if (bits >= 0x7f800000u) {
+    flags |= GIFT_FLAG_NONFINITE;
+    return kMxScaleNaN;
+  }
+  if (bits == 0u) {
+    flags |= GIFT_FLAG_ZERO_AMAX;
+    return 127u;
+  }
+  const int field = (int)(bits >> 23);
+  const int floor_log2 = field ? field - 127 : (31 - __clz((int)bits)) - 149;
+  int e = floor_log2 - 2;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return (uint32_t)(e + 127);
+}
+
+// scale operand of the conversions (the NaN scale encodes with 2^0)
+__device__ __forceinline__ float mx_scale_operand(uint32_t code) {
+  return __uint_as_float((code == kMxScaleNaN ? 127u : code) << 23);
+}
+
+// four values -> four E2M1 codes in 16 bits, value 0 in the low nibble
+__device__ __forceinline__ uint32_t mx_encode4(float4 v, float s, bool nonfinite) {
+  if (nonfinite) {
+    v.x = v.x != v.x ? 0.f : v.x;
+    v.y = v.y != v.y ? 0.f : v.y;
+    v.z = v.z != v.z ? 0.f : v.z;
+    v.w = v.w != v.w ? 0.f : v.w;
+  }
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v.x, v.y, s, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v.z, v.w, s, 1);
+  return r & 0xffffu;
+}
+
+// four E2M1 codes (16 bits) -> code value * 2^(scale code - 127), exact
+__device__ __forceinline__ float4 mx_decode4(uint32_t c16, uint32_t code) {
+  const float s = mx_scale_operand(code);
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c16, s, 0);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c16, s, 1);
+  float4 v = make_float4(lo[0], lo[1], hi[0], hi[1]);
+  if (code == kMxScaleNaN) v = make_float4(__builtin_nanf(""), __builtin_nanf(""),
+                                           __builtin_nanf(""), __builtin_nanf(""));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
 // reductions (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

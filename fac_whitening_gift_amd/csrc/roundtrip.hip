@@ -251,6 +251,28 @@ __device__ __forceinline__ void load_qc(const LayerDev& L, int64_t row, int g, i
   v[1] = *reinterpret_cast<const uint32_t*>(p + 16);
 }
 
+// MXFP4 codes of one chunk for this lane and 16-row tile: the same 2 x 4
+// columns as load_gc, 16 bits each, and the chunk's (= the block's) scale
+__device__ __forceinline__ void load_mx(const LayerDev& L, int64_t row, int g, int c,
+                                        uint32_t (&v)[2], uint32_t& code) {
+  const uint8_t* p = L.q + row * (L.d_in / 2) + 16 * c + 2 * g;
+  v[0] = *reinterpret_cast<const uint16_t*>(p);
+  v[1] = *reinterpret_cast<const uint16_t*>(p + 8);
+  code = reinterpret_cast<const uint8_t*>(L.inv)[row * (L.d_in / kMxBlock) + c];
+}
+
+// first product on MXFP4 values (code value * 2^e is exact in bf16)
+__device__ __forceinline__ void cpart_mx(const bf16x8 (&a)[2][3], const uint32_t (&qv)[2],
+                                         uint32_t code, f32x4 (&acc)[2]) {
+  const float4 lo = mx_decode4(qv[0], code), hi = mx_decode4(qv[1], code);
+  const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  bf16x8 bq;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bq[i] = (__bf16)v[i];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) acc[h] = mfma3x1(a[h], bq, acc[h]);
+}
+
 __device__ __forceinline__ void decode8(uint32_t lo, uint32_t hi, float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -349,8 +371,9 @@ __device__ __forceinline__ void c_operand(const uint4* lds, int rt, int lane, bf
 // first product of a tile: partial c over the column group (whiten: of G;
 // dequantize: of the codes, each chunk scaled by its inverse scale).
 // ---------------------------------------------------------------------------
-template <int kCPW, bool kCodes, bool kBlockScale>
+template <int kCPW, bool kCodes, int kFmt>
 __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
+  constexpr bool kB128 = kFmt == GIFT_SCALE_BLOCK128, kMX = kFmt == GIFT_SCALE_MXFP4;
   // a local copy: the descriptor's fields stay in scalar registers
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
@@ -365,15 +388,17 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
     uint4 pa[n][2][3];
     float4 gv[kCodes ? 1 : n][kTR][2];
     uint32_t qv[kCodes ? n : 1][kTR][2];
-    float sc[kBlockScale ? n : 1][kTR];
+    float sc[kB128 ? n : 1][kTR];
+    uint32_t mc[kMX ? n : 1][kTR];
     static_for<n>([&](auto J) {
       constexpr int j = decltype(J)::value;
       load_a(L.P, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        if constexpr (kCodes) load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
+        if constexpr (kMX) load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
+        else if constexpr (kCodes) load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
         else load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
-        if constexpr (kBlockScale) sc[j][rt] = L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)];
+        if constexpr (kB128) sc[j][rt] = L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)];
       }
     });
     static_for<n>([&](auto J) {
@@ -382,8 +407,10 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
       as_ops(pa[j], a);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        if constexpr (kCodes) {
-          if constexpr (kBlockScale) {
+        if constexpr (kMX) {
+          cpart_mx(a, qv[j][rt], mc[j][rt], acc[rt]);
+        } else if constexpr (kCodes) {
+          if constexpr (kB128) {
             f32x4 t[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
             cpart_q(a, qv[j][rt], t);
 #pragma unroll
@@ -449,15 +476,17 @@ __global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
 }
 
 // ---------------------------------------------------------------------------
-// whiten pass 2.
-//   kBlock128 = false (per-tensor scaling): W of the tile, its amax to the
-//     layer's partials.
-//   kBlock128 = true (1x128 block scaling, the last pass): W, the segment
-//     amax (the 4 chunks of a segment are held by 4 / kCPW waves), codes and
-//     inverse scales, optionally W.
+// whiten pass 2, by scaling mode kFmt:
+//   GIFT_SCALE_TENSOR: W of the tile, its amax to the layer's partials.
+//   GIFT_SCALE_BLOCK128 (the last pass): W, the segment amax (the 4 chunks
+//     of a segment are held by 4 / kCPW waves), codes and inverse scales.
+//   GIFT_SCALE_MXFP4 (the last pass): W, the 32-element block amax (one
+//     chunk of one row: four lanes of one wave), E8M0 scales, E2M1 codes.
+//   The last two optionally write W.
 // ---------------------------------------------------------------------------
-template <int kCPW, bool kBlock128, bool kWriteW>
+template <int kCPW, int kFmt, bool kWriteW>
 __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
+  constexpr bool kBlock128 = kFmt == GIFT_SCALE_BLOCK128;
   constexpr int kWPS = 4 / kCPW;  // waves per segment (block scaling)
   static_assert(!kBlock128 || kCPW <= 4, "a segment spans whole waves");
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
@@ -500,7 +529,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
       }
     });
   });
-  if constexpr (!kBlock128) {
+  if constexpr (kFmt == GIFT_SCALE_TENSOR) {
     uint32_t m = 0u;
     with_count<kCPW>(x.nmine, [&](auto N) {
       static_for<decltype(N)::value>([&](auto J) {
@@ -511,6 +540,40 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
     });
     m = block_max_u32<kTileThreads>(m, mx);
     if (threadIdx.x == 0) L.part[tile] = m;
+  } else if constexpr (kFmt == GIFT_SCALE_MXFP4) {
+    if (x.nmine == 0) return;  // wave-uniform; no barrier below
+    const int64_t nblk = L.d_in / kMxBlock;
+    with_count<kCPW>(x.nmine, [&](auto N) {
+      static_for<decltype(N)::value>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+#pragma unroll
+        for (int rt = 0; rt < kTR; ++rt) {
+          uint32_t m = amax4(amax4(0u, w[j][rt][0]), w[j][rt][1]);
+          m = max(m, (uint32_t)__shfl_xor(m, 16, 64));
+          m = max(m, (uint32_t)__shfl_xor(m, 32, 64));
+          uint32_t fl = 0u;
+          const uint32_t code = mx_scale_code(m, fl);
+          const float s = mx_scale_operand(code);
+          const bool nonfinite = code == kMxScaleNaN;
+          const uint32_t q0 = mx_encode4(w[j][rt][0], s, nonfinite);
+          const uint32_t q1 = mx_encode4(w[j][rt][1], s, nonfinite);
+          if (!x.ok[rt]) continue;
+          uint8_t* p = L.q + (int64_t)x.row[rt] * (L.d_in / 2) + 16 * (x.c0 + j) + 2 * x.g;
+          *reinterpret_cast<uint16_t*>(p) = (uint16_t)q0;
+          *reinterpret_cast<uint16_t*>(p + 8) = (uint16_t)q1;
+          if (x.g == 0) {
+            reinterpret_cast<uint8_t*>(L.inv)[x.row[rt] * nblk + x.c0 + j] = (uint8_t)code;
+            if (gd.flags && fl) atomicOr(gd.flags, fl);
+          }
+          if (kWriteW && L.Wout) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              *reinterpret_cast<float4*>(L.Wout + x.row[rt] * L.d_in + kChunk * (x.c0 + j) +
+                                         16 * t + 4 * x.g) = w[j][rt][t];
+          }
+        }
+      });
+    });
   } else {
     // per-segment amax: lane max over its chunks of the segment, then over
     // the lanes of the same row (xor 16, 32), then over the segment's waves
@@ -641,27 +704,33 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
 // dequantize + un-whiten, pass 2: G^ = beta W^ + c'^ U^T with
 // W^ = decode(q) * inv and c'^ the row block's (W^ U) * D_u.
 // ---------------------------------------------------------------------------
-template <int kCPW, bool kBlockScale>
+template <int kCPW, int kFmt>
 __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
+  constexpr bool kB128 = kFmt == GIFT_SCALE_BLOCK128, kMX = kFmt == GIFT_SCALE_MXFP4;
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kCPW>(L, tile);
   __shared__ uint4 cs[kCOp];
   const uint4* P2 = p2_of(L);
   const int64_t nseg = L.d_in / kBlock;
-  const float inv0 = kBlockScale ? 1.f : L.inv[0];
+  const float inv0 = kFmt == GIFT_SCALE_TENSOR ? L.inv[0] : 1.f;
   const float beta = L.coef[GIFT_COEF_BETA];
   uint4 pa[kCPW][2][3];
   uint32_t qv[kCPW][kTR][2];
   float sc[kCPW][kTR];
+  uint32_t mc[kMX ? kCPW : 1][kTR];
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
       load_a(P2, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
-        sc[j][rt] = kBlockScale ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
+        if constexpr (kMX) {
+          load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
+        } else {
+          load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
+          sc[j][rt] = kB128 ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
+        }
       }
     });
   });
@@ -680,14 +749,19 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
         c_operand(cs, rt, x.lane, cb);
         f32x4 corr[2];
         correction(a, cb, corr);
-        const float s = sc[j][rt];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const uint32_t qq = qv[j][rt][t];
-          out[j][rt][t] = make_float4(fmaf(beta, e4m3_decode(qq, 0) * s, corr[t][0]),
-                                      fmaf(beta, e4m3_decode(qq, 1) * s, corr[t][1]),
-                                      fmaf(beta, e4m3_decode(qq, 2) * s, corr[t][2]),
-                                      fmaf(beta, e4m3_decode(qq, 3) * s, corr[t][3]));
+          float4 wv;
+          if constexpr (kMX) {
+            wv = mx_decode4(qq, mc[j][rt]);
+          } else {
+            const float s = sc[j][rt];
+            wv = make_float4(e4m3_decode(qq, 0) * s, e4m3_decode(qq, 1) * s,
+                             e4m3_decode(qq, 2) * s, e4m3_decode(qq, 3) * s);
+          }
+          out[j][rt][t] = make_float4(fmaf(beta, wv.x, corr[t][0]), fmaf(beta, wv.y, corr[t][1]),
+                                      fmaf(beta, wv.z, corr[t][2]), fmaf(beta, wv.w, corr[t][3]));
         }
       }
     });
@@ -737,16 +811,17 @@ __global__ __launch_bounds__(kThreads) void k_amax_final(GroupDev g) {
   if (threadIdx.x == 0) *L.amax = m;
 }
 
-// Euclidean quantize (pass 2 of per-tensor, or the single pass of 1x128),
-// optionally dequantizing in the same pass (the round trip).
-template <bool kBlockScale, bool kDeq, bool kWriteW>
+// Euclidean quantize (pass 2 of per-tensor, or the single pass of 1x128 and
+// MXFP4), optionally dequantizing in the same pass (the round trip).
+template <int kFmt, bool kDeq, bool kWriteW>
 __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
+  constexpr bool kB128 = kFmt == GIFT_SCALE_BLOCK128, kMX = kFmt == GIFT_SCALE_MXFP4;
   const int l = find_layer(g, blockIdx.x);
   const LayerDev& L = g.L[l];
   const int tile = blockIdx.x - L.tile_begin;
   const int64_t n = L.d_out * L.d_in, base = (int64_t)tile * kFlatTile;
   Scale sc{1.f, 1.f, 0u};
-  if (!kBlockScale) {
+  if (kFmt == GIFT_SCALE_TENSOR) {
     sc = scale_from_amax_bits(*L.amax);
     if (tile == 0 && threadIdx.x == 0) {
       L.inv[0] = sc.inv;
@@ -759,15 +834,32 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
     const bool act = e < n;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (act) v = *reinterpret_cast<const float4*>(L.G + e);
-    if (kBlockScale) {
+    uint32_t m = max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w)));
+    if constexpr (kB128) {
       // 32 consecutive lanes hold one 128-element segment (d_in % 128 == 0)
-      uint32_t m = max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w)));
       m = half_wave_max_u32(m);
       sc = scale_from_amax_bits(m);
       if (act && (threadIdx.x & 31) == 0) {
         L.inv[e / kBlock] = sc.inv;
         if (g.flags && sc.flags) atomicOr(g.flags, sc.flags);
       }
+    }
+    if constexpr (kMX) {
+      // 8 consecutive lanes hold one 32-element block (d_in % 32 == 0)
+#pragma unroll
+      for (int o = 4; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor(m, o, 64));
+      uint32_t fl = 0u;
+      const uint32_t code = mx_scale_code(m, fl);
+      const uint32_t q = mx_encode4(v, mx_scale_operand(code), code == kMxScaleNaN);
+      if (!act) continue;
+      *reinterpret_cast<uint16_t*>(L.q + e / 2) = (uint16_t)q;
+      if ((threadIdx.x & 7) == 0) {
+        reinterpret_cast<uint8_t*>(L.inv)[e / kMxBlock] = (uint8_t)code;
+        if (g.flags && fl) atomicOr(g.flags, fl);
+      }
+      if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + e) = v;
+      if (kDeq) *reinterpret_cast<float4*>(L.Ghat + e) = mx_decode4(q, code);
+      continue;
     }
     if (!act) continue;
     const uint32_t c = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
@@ -785,18 +877,24 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
 }
 
 // plain dequantize of Euclidean layers: G^ = decode(q) * inv
-template <bool kBlockScale>
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void k_flat_dequant(GroupDev g) {
   const int l = find_layer(g, blockIdx.x);
   const LayerDev& L = g.L[l];
   const int tile = blockIdx.x - L.tile_begin;
   const int64_t n = L.d_out * L.d_in, base = (int64_t)tile * kFlatTile;
-  const float inv0 = kBlockScale ? 1.f : L.inv[0];
+  const float inv0 = kFmt == GIFT_SCALE_TENSOR ? L.inv[0] : 1.f;
 #pragma unroll
   for (int i = 0; i < kFlatTile / (4 * kThreads); ++i) {
     const int64_t e = base + 4 * ((int64_t)i * kThreads + threadIdx.x);
     if (e >= n) continue;
-    const float s = kBlockScale ? L.inv[e / kBlock] : inv0;
+    if constexpr (kFmt == GIFT_SCALE_MXFP4) {
+      const uint32_t q = *reinterpret_cast<const uint16_t*>(L.q + e / 2);
+      const uint32_t code = reinterpret_cast<const uint8_t*>(L.inv)[e / kMxBlock];
+      *reinterpret_cast<float4*>(L.Ghat + e) = mx_decode4(q, code);
+      continue;
+    }
+    const float s = kFmt == GIFT_SCALE_BLOCK128 ? L.inv[e / kBlock] : inv0;
     const uint32_t c = *reinterpret_cast<const uint32_t*>(L.q + e);
     float4 o;
     o.x = e4m3_decode(c, 0) * s;
@@ -884,16 +982,22 @@ hipError_t launch_pack(const PackGroup& pg, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_whiten_quantize(const GroupDev& g, bool block, bool write_w, hipStream_t s) {
+// scaling: GIFT_SCALE_TENSOR, GIFT_SCALE_BLOCK128 or GIFT_SCALE_MXFP4
+hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s) {
   const dim3 grid(g.total_tiles), blk(kTileThreads);
-  k_tile_cpart<kCPW, false, false><<<grid, blk, 0, s>>>(g);
+  k_tile_cpart<kCPW, false, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
   k_tile_reduce<false, false><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
-  if (block) {
-    if (write_w) k_tile_whiten<kCPW, true, true><<<grid, blk, 0, s>>>(g);
-    else k_tile_whiten<kCPW, true, false><<<grid, blk, 0, s>>>(g);
+#define GIFT_TW(F, W) k_tile_whiten<kCPW, F, W><<<grid, blk, 0, s>>>(g)
+  if (scaling == GIFT_SCALE_BLOCK128) {
+    if (write_w) GIFT_TW(GIFT_SCALE_BLOCK128, true); else GIFT_TW(GIFT_SCALE_BLOCK128, false);
     return hipGetLastError();
   }
-  k_tile_whiten<kCPW, false, false><<<grid, blk, 0, s>>>(g);
+  if (scaling == GIFT_SCALE_MXFP4) {
+    if (write_w) GIFT_TW(GIFT_SCALE_MXFP4, true); else GIFT_TW(GIFT_SCALE_MXFP4, false);
+    return hipGetLastError();
+  }
+  GIFT_TW(GIFT_SCALE_TENSOR, false);
+#undef GIFT_TW
   bool tall = false;
   for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_tiles > kPartialLimit;
   if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
@@ -902,41 +1006,51 @@ hipError_t launch_whiten_quantize(const GroupDev& g, bool block, bool write_w, h
   return hipGetLastError();
 }
 
-hipError_t launch_flat_quantize(const GroupDev& g, bool block, bool deq, bool write_w,
+hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool write_w,
                                 hipStream_t s) {
   const dim3 grid(g.total_tiles), blk(kThreads);
-  if (!block) {
+  if (scaling == GIFT_SCALE_TENSOR) {
     k_flat_amax<<<grid, blk, 0, s>>>(g);
     k_amax_final<<<dim3(g.n), blk, 0, s>>>(g);
   }
-#define GIFT_FQ(B, D, W) k_flat_quant<B, D, W><<<grid, blk, 0, s>>>(g)
-  if (block) {
-    if (deq) { if (write_w) GIFT_FQ(true, true, true); else GIFT_FQ(true, true, false); }
-    else     { if (write_w) GIFT_FQ(true, false, true); else GIFT_FQ(true, false, false); }
+#define GIFT_FQ(F, D, W) k_flat_quant<F, D, W><<<grid, blk, 0, s>>>(g)
+#define GIFT_FQ_ALL(F)                                                        \
+  if (deq) { if (write_w) GIFT_FQ(F, true, true); else GIFT_FQ(F, true, false); } \
+  else     { if (write_w) GIFT_FQ(F, false, true); else GIFT_FQ(F, false, false); }
+  if (scaling == GIFT_SCALE_BLOCK128) {
+    GIFT_FQ_ALL(GIFT_SCALE_BLOCK128)
+  } else if (scaling == GIFT_SCALE_MXFP4) {
+    GIFT_FQ_ALL(GIFT_SCALE_MXFP4)
   } else {
-    if (deq) { if (write_w) GIFT_FQ(false, true, true); else GIFT_FQ(false, true, false); }
-    else     { if (write_w) GIFT_FQ(false, false, true); else GIFT_FQ(false, false, false); }
+    GIFT_FQ_ALL(GIFT_SCALE_TENSOR)
   }
+#undef GIFT_FQ_ALL
 #undef GIFT_FQ
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const GroupDev& g, bool block, bool white, hipStream_t s) {
+hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s) {
   if (white) {
     const dim3 grid(g.total_tiles), blk(kTileThreads);
-    if (block) {
-      k_tile_cpart<kCPW, true, true><<<grid, blk, 0, s>>>(g);
-      k_tile_reduce<true, true><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
-      k_tile_unwhiten<kCPW, true><<<grid, blk, 0, s>>>(g);
+    const dim3 rgrid(g.total_rb), rblk(kReduceThreads);
+    if (scaling == GIFT_SCALE_BLOCK128) {
+      k_tile_cpart<kCPW, true, GIFT_SCALE_BLOCK128><<<grid, blk, 0, s>>>(g);
+      k_tile_reduce<true, true><<<rgrid, rblk, 0, s>>>(g);
+      k_tile_unwhiten<kCPW, GIFT_SCALE_BLOCK128><<<grid, blk, 0, s>>>(g);
+    } else if (scaling == GIFT_SCALE_MXFP4) {
+      k_tile_cpart<kCPW, true, GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
+      k_tile_reduce<true, true><<<rgrid, rblk, 0, s>>>(g);
+      k_tile_unwhiten<kCPW, GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
     } else {
-      k_tile_cpart<kCPW, true, false><<<grid, blk, 0, s>>>(g);
-      k_tile_reduce<true, false><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
-      k_tile_unwhiten<kCPW, false><<<grid, blk, 0, s>>>(g);
+      k_tile_cpart<kCPW, true, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
+      k_tile_reduce<true, false><<<rgrid, rblk, 0, s>>>(g);
+      k_tile_unwhiten<kCPW, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
     }
   } else {
     const dim3 grid(g.total_tiles), blk(kThreads);
-    if (block) k_flat_dequant<true><<<grid, blk, 0, s>>>(g);
-    else k_flat_dequant<false><<<grid, blk, 0, s>>>(g);
+    if (scaling == GIFT_SCALE_BLOCK128) k_flat_dequant<GIFT_SCALE_BLOCK128><<<grid, blk, 0, s>>>(g);
+    else if (scaling == GIFT_SCALE_MXFP4) k_flat_dequant<GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
+    else k_flat_dequant<GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
   }
   return hipGetLastError();
 }

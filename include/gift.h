@@ -72,9 +72,26 @@ enum { GIFT_DTYPE_F32 = 0, GIFT_DTYPE_BF16 = 1 };
  *                   (t - sum theta) / (d_in - rank), clamped at 0. */
 enum { GIFT_DAMP_FLOOR = 0, GIFT_DAMP_FLOOR_PLUS_TAIL = 1 };
 
-/* FP8 scaling granularity: one scale per tensor, or one per 128 consecutive
- * elements of a row (requires d_in % 128 == 0). */
-enum { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1 };
+/* Payload format and scaling granularity.
+ *  GIFT_SCALE_TENSOR:   E4M3 codes (d_out x d_in bytes), one fp32 inverse
+ *                       scale per tensor.
+ *  GIFT_SCALE_BLOCK128: E4M3 codes, one fp32 inverse scale per 128
+ *                       consecutive elements of a row (d_in % 128 == 0):
+ *                       inv_scale is d_out x d_in/128 floats.
+ *  GIFT_SCALE_MXFP4:    OCP MXFP4 (OCP Microscaling Formats v1.0): E2M1
+ *                       codes, two per byte with the lower-indexed element in
+ *                       the low nibble (q is d_out x d_in/2 bytes), and one
+ *                       E8M0 scale byte per 32 consecutive elements of a row
+ *                       (d_in % 32 == 0): inv_scale points to d_out x d_in/32
+ *                       bytes, code c standing for 2^(c - 127), 0xFF for NaN.
+ *                       Scale: floor(log2 amax) - 2, clamped to [-127, 127];
+ *                       elements round to nearest even and saturate at +-6;
+ *                       an all-zero block gets 2^0, a block whose amax is NaN
+ *                       or inf the NaN scale (and its NaN elements code 0).
+ *                       The FP4 payload is this library's extension of the
+ *                       pages' FP8 round trip (GIFT review, "Core claim":
+ *                       larger gains expected at lower bit-widths). */
+enum { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1, GIFT_SCALE_MXFP4 = 2 };
 
 /* Bits OR-ed into *dev_flags. */
 #define GIFT_FLAG_NONFINITE 1u  /* an amax was NaN or +inf                   */

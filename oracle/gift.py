@@ -34,6 +34,10 @@ implementation's reading, each marked where it is taken:
    amax = max |W|; scale = fl32(448 / amax); inv = fl32(amax / 448);
    code = E4M3(fl32(W * scale)); amax == 0 gives scale = inv = 1.
 7. Dequantize W^ = fl32(decode(code) * inv); un-whiten G^ = W^ A_r^{1/2}.
+8. The FP4 payload (the direction the review expects larger gains in) is
+   the same round trip with the whitened tensor stored as OCP MXFP4
+   (oracle/mxfp4.py: E2M1 elements, one power-of-two scale per 32
+   elements of a row).
 
 Precision: inputs are fp32 (activations bf16 values held in fp32); every
 linear-algebra step runs in fp64.  The steps that decide an integer (the
@@ -46,6 +50,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import e4m3
+from . import mxfp4
 
 RANK = 32
 SKETCH_WIDTH = 64
@@ -314,6 +319,21 @@ def gift_roundtrip(G, f, block128=False):
     codes, inv, flags = quantize(W32, block128)
     What = dequantize(codes, inv, block128)
     return codes, inv, W32, unwhiten(What, f), flags
+
+
+def euclid_roundtrip_mx(G):
+    """Euclidean MXFP4: (codes, scales, G^ fp32, flags)."""
+    G32 = np.asarray(G, dtype=np.float32)
+    codes, scales, flags = mxfp4.quantize(G32)
+    return codes, scales, mxfp4.dequantize(codes, scales), flags
+
+
+def gift_roundtrip_mx(G, f):
+    """GIFT with an MXFP4 payload: whiten -> fl32 -> MXFP4 -> dequantize ->
+    un-whiten.  Returns (codes, scales, W32, G^ fp64, flags)."""
+    W32 = whiten(G, f).astype(np.float32)
+    codes, scales, flags = mxfp4.quantize(W32)
+    return codes, scales, W32, unwhiten(mxfp4.dequantize(codes, scales), f), flags
 
 
 # --------------------------------------------------------------------------

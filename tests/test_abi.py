@@ -65,6 +65,7 @@ def test_layer_validation(case, status):
 
 def test_block_scaling_needs_multiple_of_128():
     assert _call_whiten([_layer(d_in=192)], scaling=fg.SCALE_BLOCK128) == 2
+    assert _call_whiten([_layer(d_in=48)], scaling=fg.SCALE_MXFP4) == 2
     assert _call_whiten([_layer(d_in=192)], scaling=7) == 1
 
 
