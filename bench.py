@@ -302,7 +302,11 @@ def main():
     t_b = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, blk, fg.SCALE_BLOCK128),
                         fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, blk, fg.SCALE_BLOCK128)]]) \
         if blk else 0.0
-    del all_eu, blk
+    mxl = [fg.Layer(L.G, factor=L.factor, mxfp4=True) for L in gl0]
+    t_mx = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, mxl, fg.SCALE_MXFP4),
+                         fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, mxl, fg.SCALE_MXFP4)]]) \
+        if mxl else 0.0
+    del all_eu, blk, mxl
 
     # ---- quality: relative error vs Euclidean FP8 on the whitened layers -----
     quality = quality_report(gl0, w, selected, inputs, ws_w, ws_d) \
@@ -343,6 +347,7 @@ def main():
                                                      MFMA_BF16_PEAK_TFLOPS, 4),
         "euclid_all_layers_gbps": round(grad_bytes / t_eu_all / 1e9, 2),
         "block128_roundtrip_gbps": round(4 * gift_elems / t_b / 1e9, 2) if t_b > 0 else None,
+        "mxfp4_roundtrip_gbps": round(4 * gift_elems / t_mx / 1e9, 2) if t_mx > 0 else None,
         "quality": quality,
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -353,23 +358,30 @@ def main():
 def quality_report(gl, w, selected, inputs, ws_w, ws_d):
     """M1 (plain relative Frobenius) from the device error sums and M2 (error
     in the K-FAC metric of the exact sample covariance, fp64 torch on the
-    device as measurement harness) for GIFT and for Euclidean FP8 of the same
-    gradients."""
+    device as measurement harness) for GIFT and for Euclidean quantization of
+    the same gradients: per-tensor E4M3 and MXFP4."""
     import numpy as np
     import torch
 
     import fac_whitening_gift_amd as fg
     fg.gift_whiten_quantize(gl, ws=ws_w)
     fg.gift_dequant_unwhiten(gl, ws=ws_d)
-    err_g = fg.gift_roundtrip_error(gl).cpu().numpy()
     eu = [fg.Layer(L.G) for L in gl]
     fg.gift_euclid_fp8_roundtrip(eu)
-    err_e = fg.gift_roundtrip_error(eu).cpu().numpy()
-    m1_g = float(np.sqrt(err_g[:, 0].sum() / err_g[:, 1].sum()))
-    m1_e = float(np.sqrt(err_e[:, 0].sum() / err_e[:, 1].sum()))
-    num_g = num_e = den = 0.0
+    gm = [fg.Layer(L.G, factor=L.factor, mxfp4=True) for L in gl]
+    fg.gift_whiten_quantize(gm, scaling=fg.SCALE_MXFP4)
+    fg.gift_dequant_unwhiten(gm, scaling=fg.SCALE_MXFP4)
+    em = [fg.Layer(L.G, mxfp4=True) for L in gl]
+    fg.gift_euclid_fp8_roundtrip(em, scaling=fg.SCALE_MXFP4)
+    sets = {"gift": gl, "euclid": eu, "gift_mxfp4": gm, "euclid_mxfp4": em}
+    m1 = {}
+    for k, layers in sets.items():
+        err = fg.gift_roundtrip_error(layers).cpu().numpy()
+        m1[k] = float(np.sqrt(err[:, 0].sum() / err[:, 1].sum()))
+    num = {k: 0.0 for k in sets}
+    den = 0.0
     S_cache = {}
-    for L, E, i in zip(gl, eu, selected):
+    for j, i in enumerate(selected):
         name = w.layers[i].input
         if name not in S_cache:
             X = inputs[name]["X"].double()
@@ -378,15 +390,21 @@ def quality_report(gl, w, selected, inputs, ws_w, ws_d):
             ev_, V = torch.linalg.eigh(A)
             S_cache[name] = (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
         S = S_cache[name]
-        G = L.G.double()
-        num_g += float(torch.linalg.norm((L.G_hat.double() - G) @ S) ** 2)
-        num_e += float(torch.linalg.norm((E.G_hat.double() - G) @ S) ** 2)
+        G = gl[j].G.double()
+        for k, layers in sets.items():
+            num[k] += float(torch.linalg.norm((layers[j].G_hat.double() - G) @ S) ** 2)
         den += float(torch.linalg.norm(G @ S) ** 2)
-    m2_g, m2_e = float(np.sqrt(num_g / den)), float(np.sqrt(num_e / den))
-    return {"m1_gift": round(m1_g, 5), "m1_euclid": round(m1_e, 5),
-            "m1_ratio": round(m1_g / m1_e, 4), "m2_gift": round(m2_g, 5),
-            "m2_euclid": round(m2_e, 5), "m2_ratio": round(m2_g / m2_e, 4),
-            "m2_reduction": round(1 - m2_g / m2_e, 4), "damping": "floor+tail"}
+    m2 = {k: float(np.sqrt(v / den)) for k, v in num.items()}
+    return {"m1_gift": round(m1["gift"], 5), "m1_euclid": round(m1["euclid"], 5),
+            "m1_ratio": round(m1["gift"] / m1["euclid"], 4), "m2_gift": round(m2["gift"], 5),
+            "m2_euclid": round(m2["euclid"], 5), "m2_ratio": round(m2["gift"] / m2["euclid"], 4),
+            "m2_reduction": round(1 - m2["gift"] / m2["euclid"], 4),
+            "mxfp4": {"m1_gift": round(m1["gift_mxfp4"], 5),
+                      "m1_euclid": round(m1["euclid_mxfp4"], 5),
+                      "m2_gift": round(m2["gift_mxfp4"], 5),
+                      "m2_euclid": round(m2["euclid_mxfp4"], 5),
+                      "m2_reduction": round(1 - m2["gift_mxfp4"] / m2["euclid_mxfp4"], 4)},
+            "damping": "floor+tail"}
 
 
 def cpu_baseline(layers, args):
