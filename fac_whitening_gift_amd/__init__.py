@@ -8,6 +8,7 @@ include/gift.h); this package is its Python binding.  Build the library with
 from ._lib import (  # noqa: F401
     Factor, Layer, GroupCall, GiftError, load, status_name, build_hash,
     OP_WHITEN_QUANTIZE, OP_DEQUANT_UNWHITEN, OP_EUCLID_ROUNDTRIP, OP_ROUNDTRIP_ERROR,
+    OP_UNWHITEN_F32, gift_dequant_accumulate, gift_unwhiten_f32,
     gift_refresh_factor, gift_refresh_workspace_bytes, gift_whiten_quantize,
     gift_dequant_unwhiten, gift_euclid_fp8_roundtrip, gift_roundtrip_error,
     gift_group_workspace_bytes, gift_draw_sketch, gift_factor_pack_bytes,

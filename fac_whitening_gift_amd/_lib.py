@@ -25,6 +25,7 @@ SCALE_TENSOR, SCALE_BLOCK128, SCALE_MXFP4 = 0, 1, 2
 MX_BLOCK = 32
 FLAG_NONFINITE, FLAG_ZERO_AMAX = 1, 2
 OP_WHITEN_QUANTIZE, OP_DEQUANT_UNWHITEN, OP_EUCLID_ROUNDTRIP, OP_ROUNDTRIP_ERROR = 0, 1, 2, 3
+OP_UNWHITEN_F32 = 4
 
 COEF_ALPHA, COEF_BETA, COEF_LAMBDA_ISO, COEF_LAMBDA_FLOOR, COEF_TRACE, COEF_SIGMA2_TAIL = range(6)
 COEF_DW = 8
@@ -37,6 +38,7 @@ EXPORTS = (
     "gift_group_workspace_bytes", "gift_status_string", "gift_last_error",
     "gift_abi_version", "gift_draw_sketch", "gift_factor_pack_bytes", "gift_prepare_factor",
     "gift_refresh_factors", "gift_refresh_group_workspace_bytes", "gift_build_hash",
+    "gift_dequant_accumulate", "gift_unwhiten_f32",
 )
 
 
@@ -92,6 +94,8 @@ def load():
         "gift_last_error": (ctypes.c_char_p, []),
         "gift_abi_version": (I, []),
         "gift_build_hash": (ctypes.c_char_p, []),
+        "gift_dequant_accumulate": (I, [LP, I, I, I, P]),
+        "gift_unwhiten_f32": (I, [LP, I, P, SZ, P]),
         "gift_draw_sketch": (I, [P, I64, I, U64, P]),
         "gift_factor_pack_bytes": (SZ, [I64]),
         "gift_prepare_factor": (I, [ctypes.POINTER(_Factor), P]),
@@ -361,6 +365,23 @@ class GroupCall:
 
     def __call__(self, stream=None):
         _check(self._fn(*self._args, _stream(stream)))
+
+
+def gift_dequant_accumulate(layers, scaling=SCALE_TENSOR, first=False, stream=None):
+    """G_hat = decode(q) * inv (first) or G_hat + decode(q) * inv, per layer."""
+    arr = _layers_array(layers)
+    _check(load().gift_dequant_accumulate(arr, len(layers), scaling, 1 if first else 0,
+                                          _stream(stream)))
+
+
+def gift_unwhiten_f32(layers, ws=None, stream=None):
+    """G_hat = G_hat A_r^1/2 in place for the whitened layers."""
+    lib = load()
+    arr = _layers_array(layers)
+    need = lib.gift_group_workspace_bytes(OP_UNWHITEN_F32, arr, len(layers), SCALE_TENSOR)
+    ws = _workspace(need, _device_of(layers), ws)
+    _check(lib.gift_unwhiten_f32(arr, len(layers), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)))
 
 
 def gift_factor_pack_bytes(d_in):

@@ -15,6 +15,8 @@ hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool w
                                 hipStream_t s);
 hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s);
 hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
+hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStream_t s);
+hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s);
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
 int64_t row_blocks(int64_t d_out);
 int col_groups(int64_t d_in);
@@ -65,10 +67,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxElems = int64_t(1) << 36;
 
-enum class Op { Whiten, Dequant, Euclid, Error };
+enum class Op { Whiten, Dequant, Euclid, Error, Accumulate, UnwhitenF32 };
 
 bool whitened(const gift_layer& L, Op op) {
-  return L.factor != nullptr && (op == Op::Whiten || op == Op::Dequant);
+  return L.factor != nullptr && (op == Op::Whiten || op == Op::Dequant || op == Op::UnwhitenF32);
 }
 
 // Per-layer workspace needs of one grouped op.
@@ -108,6 +110,7 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
       }
       break;
     case Op::Dequant:
+    case Op::UnwhitenF32:
       if (L.factor) {
         w.cbuf = (size_t)col_groups(L.d_in) * frag;
         w.cfin = cop;
@@ -115,6 +118,8 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
       break;
     case Op::Error:
       w.part2 = (size_t)flat_tiles(n) * 2 * sizeof(double);
+      break;
+    case Op::Accumulate:
       break;
   }
   return w;
@@ -190,8 +195,8 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
       return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: block scaling needs d_in %% 128 == 0", i);
     if (scaling == GIFT_SCALE_MXFP4 && L.d_in % kMxBlock)
       return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: MXFP4 needs d_in %% 32 == 0", i);
-    const bool need_g = op != Op::Dequant;
-    const bool need_q = op != Op::Error;
+    const bool need_g = op == Op::Whiten || op == Op::Euclid || op == Op::Error;
+    const bool need_q = op != Op::Error && op != Op::UnwhitenF32;
     const bool need_ghat = op != Op::Whiten;
     if ((need_g && !L.G) || (need_q && (!L.q || !L.inv_scale)) || (need_ghat && !L.G_hat))
       return fail(GIFT_ERR_INVALID_ARG, "layer %d: a required tensor pointer is NULL", i);
@@ -247,7 +252,7 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     char* base = (char*)ws + off[i];
     LayerDev& d = g.L[g.n];
     d = LayerDev{};
-    d.G = L.G;
+    d.G = op == Op::UnwhitenF32 ? L.G_hat : L.G;
     d.q = L.q;
     d.inv = L.inv_scale;
     d.Ghat = L.G_hat;
@@ -328,6 +333,7 @@ size_t gift_group_workspace_bytes(int op, const gift_layer* layers, int n_layers
     case GIFT_OP_DEQUANT_UNWHITEN: return group_ws(layers, n_layers, Op::Dequant, block);
     case GIFT_OP_EUCLID_ROUNDTRIP: return group_ws(layers, n_layers, Op::Euclid, block);
     case GIFT_OP_ROUNDTRIP_ERROR: return group_ws(layers, n_layers, Op::Error, false);
+    case GIFT_OP_UNWHITEN_F32: return group_ws(layers, n_layers, Op::UnwhitenF32, true);
     default: return 0;
   }
 }
@@ -417,6 +423,33 @@ gift_status gift_roundtrip_error(const gift_layer* layers, int n_layers, double*
   return run_grouped(layers, n_layers, Op::Error, false, ws, nullptr, dev_out,
                      [](const gift_layer&) { return true; }, tiles_flat,
                      [&](const GroupDev& g, int first) { return launch_error(g, first, st); });
+}
+
+gift_status gift_dequant_accumulate(const gift_layer* layers, int n_layers, int scaling,
+                                    int first, void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::Accumulate, scaling);
+  if (s != GIFT_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  return run_grouped(layers, n_layers, Op::Accumulate, true, nullptr, nullptr, nullptr,
+                     [](const gift_layer&) { return true; }, tiles_flat,
+                     [&](const GroupDev& g, int) {
+                       return launch_accumulate(g, scaling, first != 0, st);
+                     });
+}
+
+gift_status gift_unwhiten_f32(const gift_layer* layers, int n_layers, void* ws, size_t ws_bytes,
+                              void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::UnwhitenF32, GIFT_SCALE_TENSOR);
+  if (s != GIFT_OK) return s;
+  s = check_ws(ws, ws_bytes, group_ws(layers, n_layers, Op::UnwhitenF32, true));
+  if (s != GIFT_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  s = run_packs(plan_packs(layers, n_layers, Op::UnwhitenF32), ws, st);
+  if (s != GIFT_OK) return s;
+  auto pick = [](const gift_layer& L) { return L.factor != nullptr; };
+  auto tiles = [](const gift_layer& L) { return row_tiles(L); };
+  return run_grouped(layers, n_layers, Op::UnwhitenF32, true, ws, nullptr, nullptr, pick, tiles,
+                     [&](const GroupDev& g, int) { return launch_unwhiten_f32(g, st); });
 }
 
 size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype,

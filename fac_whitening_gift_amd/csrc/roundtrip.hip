@@ -484,6 +484,10 @@ __global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
 //     chunk of one row: four lanes of one wave), E8M0 scales, E2M1 codes.
 //   The last two optionally write W.
 // ---------------------------------------------------------------------------
+// scaling-mode value of k_tile_whiten for un-whitening an fp32 tensor:
+// G^ = beta S + c'(D_u) U^T, written to G_hat
+constexpr int kFmtUnwhiten = 3;
+
 template <int kCPW, int kFmt, bool kWriteW>
 __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
   constexpr bool kBlock128 = kFmt == GIFT_SCALE_BLOCK128;
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
   __shared__ uint4 cs[kCOp];
   __shared__ uint32_t mx[kBlock128 ? kTW * kTR * 64 : kTW];
   const uint4* P2 = p2_of(L);
-  const float alpha = L.coef[GIFT_COEF_ALPHA];
+  const float alpha = L.coef[kFmt == kFmtUnwhiten ? GIFT_COEF_BETA : GIFT_COEF_ALPHA];
   // this wave's operands and gradient in flight while c' is staged
   uint4 pa[kCPW][2][3];
   float4 gv[kCPW][kTR][2];
@@ -540,6 +544,21 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
     });
     m = block_max_u32<kTileThreads>(m, mx);
     if (threadIdx.x == 0) L.part[tile] = m;
+  } else if constexpr (kFmt == kFmtUnwhiten) {
+    if (x.nmine == 0) return;
+    with_count<kCPW>(x.nmine, [&](auto N) {
+      static_for<decltype(N)::value>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+#pragma unroll
+        for (int rt = 0; rt < kTR; ++rt) {
+          if (!x.ok[rt]) continue;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            *reinterpret_cast<float4*>(L.Ghat + x.row[rt] * L.d_in + kChunk * (x.c0 + j) +
+                                       16 * t + 4 * x.g) = w[j][rt][t];
+        }
+      });
+    });
   } else if constexpr (kFmt == GIFT_SCALE_MXFP4) {
     if (x.nmine == 0) return;  // wave-uniform; no barrier below
     const int64_t nblk = L.d_in / kMxBlock;
@@ -905,6 +924,38 @@ __global__ __launch_bounds__(kThreads) void k_flat_dequant(GroupDev g) {
   }
 }
 
+// dequantize and accumulate: G_hat = decode(q) * inv (kFirst) or
+// fl32(G_hat + decode(q) * inv), element by element
+template <int kFmt, bool kFirst>
+__global__ __launch_bounds__(kThreads) void k_flat_accumulate(GroupDev g) {
+  const int l = find_layer(g, blockIdx.x);
+  const LayerDev& L = g.L[l];
+  const int tile = blockIdx.x - L.tile_begin;
+  const int64_t n = L.d_out * L.d_in, base = (int64_t)tile * kFlatTile;
+  const float inv0 = kFmt == GIFT_SCALE_TENSOR ? L.inv[0] : 1.f;
+#pragma unroll
+  for (int i = 0; i < kFlatTile / (4 * kThreads); ++i) {
+    const int64_t e = base + 4 * ((int64_t)i * kThreads + threadIdx.x);
+    if (e >= n) continue;
+    float4 o;
+    if constexpr (kFmt == GIFT_SCALE_MXFP4) {
+      const uint32_t q = *reinterpret_cast<const uint16_t*>(L.q + e / 2);
+      o = mx_decode4(q, reinterpret_cast<const uint8_t*>(L.inv)[e / kMxBlock]);
+    } else {
+      const float s = kFmt == GIFT_SCALE_BLOCK128 ? L.inv[e / kBlock] : inv0;
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(L.q + e);
+      o = make_float4(e4m3_decode(c, 0) * s, e4m3_decode(c, 1) * s, e4m3_decode(c, 2) * s,
+                      e4m3_decode(c, 3) * s);
+    }
+    float4* dst = reinterpret_cast<float4*>(L.Ghat + e);
+    if constexpr (!kFirst) {
+      const float4 a = *dst;
+      o = make_float4(a.x + o.x, a.y + o.y, a.z + o.z, a.w + o.w);
+    }
+    *dst = o;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_err_partial(GroupDev g) {
   const int l = find_layer(g, blockIdx.x);
   const LayerDev& L = g.L[l];
@@ -1052,6 +1103,31 @@ hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_
     else if (scaling == GIFT_SCALE_MXFP4) k_flat_dequant<GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
     else k_flat_dequant<GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStream_t s) {
+  const dim3 grid(g.total_tiles), blk(kThreads);
+#define GIFT_ACC(F)                                                     \
+  if (first) k_flat_accumulate<F, true><<<grid, blk, 0, s>>>(g);         \
+  else k_flat_accumulate<F, false><<<grid, blk, 0, s>>>(g);
+  if (scaling == GIFT_SCALE_BLOCK128) {
+    GIFT_ACC(GIFT_SCALE_BLOCK128)
+  } else if (scaling == GIFT_SCALE_MXFP4) {
+    GIFT_ACC(GIFT_SCALE_MXFP4)
+  } else {
+    GIFT_ACC(GIFT_SCALE_TENSOR)
+  }
+#undef GIFT_ACC
+  return hipGetLastError();
+}
+
+// G_hat = G_hat A_r^1/2 in place (the descriptors' G points at G_hat)
+hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s) {
+  const dim3 grid(g.total_tiles), blk(kTileThreads);
+  k_tile_cpart<kCPW, false, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
+  k_tile_reduce<true, true><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
+  k_tile_whiten<kCPW, kFmtUnwhiten, false><<<grid, blk, 0, s>>>(g);
   return hipGetLastError();
 }
 

@@ -270,10 +270,36 @@ gift_status gift_roundtrip_error(const gift_layer *layers, int n_layers,
                                  double *dev_out, void *ws, size_t ws_bytes,
                                  void *stream);
 
-/* Workspace query for the four grouped calls.  op: 0 whiten_quantize,
- * 1 dequant_unwhiten, 2 euclid_fp8_roundtrip, 3 roundtrip_error. */
+/*
+ * The receive side of a data-parallel reduction of FP8 (or MXFP4) payloads,
+ * simulated on one GPU.  In the review's data-parallel setting every rank
+ * holds its own gradient and the ranks' quantized whitened gradients are
+ * summed in the collective ("Core claim": FP8 communication of the whitened
+ * gradients); whitening is linear and the factor is shared, so the sum of
+ * the ranks' whitened gradients un-whitens to the sum of their gradients.
+ * This library's reading of the sum: fp32 additions of the dequantized
+ * payloads, rank by rank in call order, each rank with its own scales.
+ *
+ * gift_dequant_accumulate -- per layer: G_hat = decode(q) * inv (first != 0)
+ * or G_hat = fl32(G_hat + decode(q) * inv), element by element, with the
+ * dequantized value formed exactly as gift_dequant_unwhiten forms it.
+ * Reads q, inv_scale, G_hat (unless first); writes G_hat.  Ignores factor.
+ * Needs no workspace.
+ *
+ * gift_unwhiten_f32 -- per whitened layer (factor != NULL): G_hat = G_hat
+ * A_r^{1/2} in place; other layers are left alone.  Reads and writes G_hat.
+ */
+gift_status gift_dequant_accumulate(const gift_layer *layers, int n_layers,
+                                    int scaling, int first, void *stream);
+gift_status gift_unwhiten_f32(const gift_layer *layers, int n_layers,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace query for the grouped calls.  op: 0 whiten_quantize,
+ * 1 dequant_unwhiten, 2 euclid_fp8_roundtrip, 3 roundtrip_error,
+ * 4 unwhiten_f32. */
 enum { GIFT_OP_WHITEN_QUANTIZE = 0, GIFT_OP_DEQUANT_UNWHITEN = 1,
-       GIFT_OP_EUCLID_ROUNDTRIP = 2, GIFT_OP_ROUNDTRIP_ERROR = 3 };
+       GIFT_OP_EUCLID_ROUNDTRIP = 2, GIFT_OP_ROUNDTRIP_ERROR = 3,
+       GIFT_OP_UNWHITEN_F32 = 4 };
 size_t gift_group_workspace_bytes(int op, const gift_layer *layers,
                                   int n_layers, int scaling);
 

@@ -34,7 +34,10 @@ implementation's reading, each marked where it is taken:
    amax = max |W|; scale = fl32(448 / amax); inv = fl32(amax / 448);
    code = E4M3(fl32(W * scale)); amax == 0 gives scale = inv = 1.
 7. Dequantize W^ = fl32(decode(code) * inv); un-whiten G^ = W^ A_r^{1/2}.
-8. The FP4 payload (the direction the review expects larger gains in) is
+8. A data-parallel reduction of R payloads (the ranks' quantized whitened
+   gradients summed in the collective) is read as fp32 additions of the
+   dequantized payloads in rank order, then one un-whitening of the sum.
+9. The FP4 payload (the direction the review expects larger gains in) is
    the same round trip with the whitened tensor stored as OCP MXFP4
    (oracle/mxfp4.py: E2M1 elements, one power-of-two scale per 32
    elements of a row).
@@ -334,6 +337,21 @@ def gift_roundtrip_mx(G, f):
     W32 = whiten(G, f).astype(np.float32)
     codes, scales, flags = mxfp4.quantize(W32)
     return codes, scales, W32, unwhiten(mxfp4.dequantize(codes, scales), f), flags
+
+
+def reduce_payloads(payloads):
+    """fp32 sum of dequantized payloads in the given order (step 8):
+    S = D_0, then S = fl32(S + D_r).  payloads: list of (fmt, codes, scales)
+    with fmt "tensor", "block128" or "mxfp4"."""
+    S = None
+    for fmt, codes, scales in payloads:
+        if fmt == "mxfp4":
+            D = mxfp4.dequantize(codes, scales)
+        else:
+            D = dequantize(codes, scales, fmt == "block128")
+        D = np.asarray(D, dtype=np.float32)
+        S = D.copy() if S is None else (S + D).astype(np.float32)
+    return S
 
 
 # --------------------------------------------------------------------------

@@ -265,3 +265,33 @@ def test_torch_cast_agrees_with_oracle_on_whitened_tensor(layer):
     ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(codes, ref)
     assert np.array_equal(e4m3.encode(y), ref)
+
+
+# --------------------------------------------------------------------------- reduction
+
+def test_reduce_payloads_adds_in_fp32_in_order():
+    """Decoded values 2^24, 1, -2^24 (E4M3 code 0x38 = 1.0 with inverse
+    scales 2^24, 1, and code 0xB8 = -1.0 with 2^24): fp32 additions in rank
+    order give fl32(fl32(2^24 + 1) - 2^24) = 0, not the exact sum 1."""
+    one, mone = np.full((1, 4), 0x38, np.uint8), np.full((1, 4), 0xB8, np.uint8)
+    p = [("tensor", one, np.float32(2.0 ** 24)), ("tensor", one, np.float32(1.0)),
+         ("tensor", mone, np.float32(2.0 ** 24))]
+    assert np.all(og.reduce_payloads(p) == 0.0)
+    # another order keeps the 1
+    assert np.all(og.reduce_payloads([p[0], p[2], p[1]]) == 1.0)
+    # one payload is its dequantization
+    codes, inv, _ = og.quantize_tensor(np.linspace(-3, 3, 64, dtype=np.float32).reshape(2, 32))
+    assert np.array_equal(og.reduce_payloads([("tensor", codes, inv)]),
+                          og.dequantize_tensor(codes, inv))
+
+
+def test_unwhitened_sum_of_whitened_gradients_is_the_sum_of_gradients():
+    """Linearity that the reduction relies on: sum_r W_r A^{1/2} = sum_r G_r
+    when W_r = G_r A^{-1/2} with one shared factor (fp64, no quantization)."""
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((512, 96))
+    omega = rng.standard_normal((96, og.SKETCH_WIDTH))
+    f = og.refresh_factor(X, omega)
+    Gs = [rng.standard_normal((7, 96)) for _ in range(4)]
+    S = sum(og.whiten(G, f) for G in Gs)
+    assert np.allclose(og.unwhiten(S, f), sum(Gs), rtol=1e-10, atol=1e-10)
