@@ -22,6 +22,7 @@ the timed region.  One JSON line on stdout.
     python bench.py --workload stack300m     # 24 blocks + embed/head, top-8 by rho
     python bench.py --workload stack600m     # 24 blocks at 1536/4096, 16384 tokens
     python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
+    python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
 """
 
 import argparse
@@ -53,7 +54,8 @@ def parse():
     p.add_argument("--counters", action="store_true",
                    help="for runs under hardware-counter collection: no device QR or "
                         "eigendecomposition (host QR for the input bases, no M2 report)")
-    p.add_argument("--study", default=None, choices=["staleness", "copy"])
+    p.add_argument("--study", default=None, choices=["staleness", "copy", "reduce"])
+    p.add_argument("--ranks", type=int, default=8, help="ranks of the reduce study")
     p.add_argument("--blocks", type=int, default=1)
     p.add_argument("--hidden", type=int, default=4096)
     p.add_argument("--mlp", type=int, default=11008)
@@ -140,6 +142,9 @@ def main():
         return
     if args.study == "copy":
         print(json.dumps(copy_calibration()), flush=True)
+        return
+    if args.study == "reduce":
+        print(json.dumps(reduce_study(args)), flush=True)
         return
 
     import numpy as np
@@ -553,6 +558,91 @@ def staleness_study(args, device="cuda:0"):
             "falsified_at_last_step_m1": bool(last["m1_stale_tensor"] >= last["m1_euclid_tensor"]),
             "rows": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                      for r in rows]}
+
+
+# ---------------------------------------------------------------------------
+# reduce study
+# ---------------------------------------------------------------------------
+
+def reduce_study(args, device="cuda:0"):
+    """A data-parallel step on one GPU: `ranks` ranks hold independent
+    gradients of the hidden-1024 block (drawn from the same input
+    covariances), each quantizes its own (GIFT: whitened with the shared
+    factors; Euclidean: as is), and the receive side sums the dequantized
+    payloads in fp32 rank by rank and un-whitens the sum once.  Error of the
+    reduced gradient against the exact sum of the ranks' gradients: M1 and M2
+    (the K-FAC metric of the exact sample covariance), per-tensor E4M3 and
+    MXFP4; and the rates of the accumulate and un-whiten calls."""
+    import numpy as np
+    import torch
+
+    import synth
+    import fac_whitening_gift_amd as fg
+
+    dev = torch.device(device)
+    R = args.ranks
+    w = synth.llama_block(hidden=1024, mlp=2816, tokens=8192, exponent=1.5)
+    inputs, factors = {}, {}
+    for k, spec in enumerate(w.inputs):
+        inputs[spec.name] = synth.draw_input(spec, seed=1000 + k, device=dev, as_bf16=True)
+        factors[spec.name] = fg.Factor(spec.d_in, device=dev)
+    fg.gift_refresh_factors([dict(X=inputs[s.name]["X"], factor=factors[s.name], seed=k)
+                             for k, s in enumerate(w.inputs)])
+    grads = [[synth.draw_gradient(l.d_out, inputs[l.input]["Q"], inputs[l.input]["ev"],
+                                  seed=20000 + 1000 * r + i, device=dev)
+              for i, l in enumerate(w.layers)] for r in range(R)]
+    exact = [sum(grads[r][i].double() for r in range(R)) for i in range(len(w.layers))]
+    S_metric = {}
+    for spec in w.inputs:
+        X = inputs[spec.name]["X"].double()
+        A = X.T @ X / X.shape[0]
+        lam = 1e-3 * torch.trace(A) / A.shape[0]
+        ev_, V = torch.linalg.eigh(A)
+        S_metric[spec.name] = (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {"study": "reduce", "workload": w.name, "ranks": R,
+           "gradient_elements": w.gradient_elements}
+    for fmt, sc in (("e4m3_tensor", fg.SCALE_TENSOR), ("mxfp4", fg.SCALE_MXFP4)):
+        mx_ = sc == fg.SCALE_MXFP4
+        res = {}
+        for method in ("gift", "euclid"):
+            ranks = []
+            for r in range(R):
+                layers = [fg.Layer(grads[r][i], mxfp4=mx_,
+                                   factor=factors[l.input] if method == "gift" else None)
+                          for i, l in enumerate(w.layers)]
+                fg.gift_whiten_quantize(layers, scaling=sc)
+                ranks.append(layers)
+            acc = [torch.empty_like(grads[0][i]) for i in range(len(w.layers))]
+            views = [[fg.Layer(None, factor=L.factor, q=L.q, inv_scale=L.inv_scale, G_hat=a,
+                               d_out=L.d_out, d_in=L.d_in, allocate=False, mxfp4=mx_)
+                      for L, a in zip(ranks[r], acc)] for r in range(R)]
+            torch.cuda.synchronize()
+            t0, t1, t2 = ev(), ev(), ev()
+            t0.record()
+            for r in range(R):
+                fg.gift_dequant_accumulate(views[r], scaling=sc, first=r == 0)
+            t1.record()
+            if method == "gift":
+                fg.gift_unwhiten_f32(views[0])
+            t2.record()
+            torch.cuda.synchronize()
+            num1 = den1 = num2 = den2 = 0.0
+            for i, l in enumerate(w.layers):
+                E = acc[i].double() - exact[i]
+                S = S_metric[l.input]
+                num1 += float(E.pow(2).sum())
+                den1 += float(exact[i].pow(2).sum())
+                num2 += float((E @ S).pow(2).sum())
+                den2 += float((exact[i] @ S).pow(2).sum())
+            res[method] = {"m1": round(math.sqrt(num1 / den1), 5),
+                           "m2": round(math.sqrt(num2 / den2), 5),
+                           "accumulate_ms_per_rank": round(t0.elapsed_time(t1) / R, 4)}
+            if method == "gift":
+                res[method]["unwhiten_ms"] = round(t1.elapsed_time(t2), 4)
+        res["m2_reduction"] = round(1 - res["gift"]["m2"] / res["euclid"]["m2"], 4)
+        out[fmt] = res
+    return out
 
 
 if __name__ == "__main__":
