@@ -42,7 +42,9 @@ constexpr int kW = GIFT_MAX_SKETCH;  // largest subspace width
 constexpr int kGramParts = 16;       // Gram partial sums per input
 constexpr double kDropTol = 1e-12;   // CholeskyQR pivot drop threshold (relative)
 constexpr int kMaxSweeps = 20;
-constexpr double kJacobiTol = 1e-22;  // off-diagonal / total squared mass
+// off-diagonal / total squared mass at which the sweeps stop: an off-diagonal
+// norm ~3e-8 of the total, below the fp32 rounding of U and theta
+constexpr double kJacobiTol = 1e-15;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
