@@ -649,63 +649,143 @@ __device__ double block_sum(double v, double* red) {
 // 4c. Cholesky of the Gram matrix, G = R^T R (R upper triangular, fp64), and
 // T = R^-1.  Pivots below kDropTol * max diagonal mark a column as
 // dependent: its row of R and column of T are zero, so that column of the
-// orthonormalised Q is 0.  grid: (inputs)
+// orthonormalised Q is 0.  grid: (inputs), kCT threads.
+//
+// Every thread owns a fixed set of entries (i, j), i <= j, of the upper
+// triangle (at most 3) and keeps them in registers; a step needs one
+// workgroup barrier.
+//   * Factorization, step k: with p = G[k][k] (row k is final and in LDS),
+//     row k of R is G[k][.] / sqrt(p) and every entry below it takes the
+//     rank-1 update G[i][j] -= G[k][i] G[k][j] / p (right-looking Cholesky
+//     in its unnormalised form); an entry of row k+1 is stored to LDS once
+//     updated, ready for the next step.
+//   * Inverse, step k from the last row up: every entry (i, c), i <= k < c,
+//     adds R[i][k+1] T[k+1][c] to its sum, and row k of T becomes
+//     T[k][c] = (delta_kc - sum) / R[k][k] (column-oriented back
+//     substitution for all columns at once).
+// The thread owning a diagonal entry computes the pivot's reciprocal square
+// root y (the hardware estimate refined by two Newton steps) and 1/p = y^2
+// once the entry is final, and leaves them in LDS for the next step.
 // ---------------------------------------------------------------------------
+constexpr int kCT = 1024;
+
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  const double h = 0.5 * p;
+  double y = __builtin_amdgcn_rsq(p);
+  y = y * (1.5 - h * y * y);
+  y = y * (1.5 - h * y * y);
+  return y;
+}
+
 template <int W>
-__global__ __launch_bounds__(kST) void k_chol(RGroup g) {
+__global__ __launch_bounds__(kCT) void k_chol(RGroup g) {
+  constexpr int kN = W * (W + 1) / 2;          // upper-triangle entries
+  constexpr int kE = (kN + kCT - 1) / kCT;     // entries per thread
   const RIn& Rin = g.r[blockIdx.x];
-  __shared__ double G[W][W + 1];
+  __shared__ double Gs[W][W + 1];  // row k of the partly reduced G, when final
   __shared__ double R[W][W + 1];
-  __shared__ double T[W][W + 1];
-  __shared__ int keep[W];
-  __shared__ double red[kST / 64];
-  gram_reduce<W>(Rin.gram, G);
-  for (int e = threadIdx.x; e < W * (W + 1); e += kST) {
-    R[e / (W + 1)][e % (W + 1)] = 0.0;
-    T[e / (W + 1)][e % (W + 1)] = 0.0;
-  }
-  double dmax = threadIdx.x < W ? G[threadIdx.x][threadIdx.x] : 0.0;
-  dmax = threadIdx.x < 64 ? dmax : 0.0;
-  // max of the diagonal through the first wave
-  for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
-  if (threadIdx.x == 0) red[0] = dmax;
-  __syncthreads();
-  const double maxdiag = red[0];
-  // right-looking: row k of R, then the update of the trailing upper triangle
-  for (int k = 0; k < W; ++k) {
-    if (threadIdx.x >= k && threadIdx.x < W) {  // row k of R: part of the first wave
-      const double piv = G[k][k];
-      const bool ok = maxdiag > 0.0 && piv > kDropTol * maxdiag;
-      const double rkk = ok ? sqrt(piv) : 0.0;
-      const int j = threadIdx.x;
-      if (j == k) keep[k] = ok;
-      R[k][j] = ok ? (j == k ? rkk : G[k][j] / rkk) : 0.0;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < W * W; e += kST) {
-      const int i = e / W, j = e % W;
-      if (i > k && i <= j) G[i][j] -= R[k][i] * R[k][j];
-    }
-    __syncthreads();
-  }
-  // T = R^-1 row by row from the last: T[i][c] = (delta_ic - sum_{i<j<=c}
-  // R[i][j] T[j][c]) / R[i][i]; 16 lanes per column split the sum.
-  constexpr int kLanes = 16;
-  const int c = threadIdx.x / kLanes, part = threadIdx.x % kLanes;
-  for (int i = W - 1; i >= 0; --i) {
-    double s = 0.0;
-    if (c < W && c > i)
-      for (int j = i + 1 + part; j <= c; j += kLanes) s += R[i][j] * T[j][c];
+  __shared__ double Ts[W][W + 1];
+  __shared__ double pinv[W], rinv[W];  // 1/p and 1/sqrt(p) of each pivot (0: dropped)
+  __shared__ double red[kCT / 64];
+  // this thread's entries, row-major over the packed upper triangle: row i
+  // starts at i (2W + 1 - i) / 2
+  int ei[kE], ej[kE];
+  double v[kE];
 #pragma unroll
-    for (int o = kLanes / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (c < W && part == 0 && c >= i) {
-      double v = 0.0;
-      if (keep[i] && keep[c]) v = ((i == c ? 1.0 : 0.0) - s) / R[i][i];
-      T[i][c] = v;
+  for (int r = 0; r < kE; ++r) {
+    int e = threadIdx.x + r * kCT;
+    const bool none = e >= kN;
+    if (none) e = kN - 1;
+    const float b = 2.f * W + 1.f;
+    int row = (int)((b - sqrtf(b * b - 8.f * (float)e)) * 0.5f);
+    row = row < 0 ? 0 : (row > W - 1 ? W - 1 : row);
+    if (row * (2 * W + 1 - row) / 2 > e) --row;
+    if ((row + 1) * (2 * W - row) / 2 <= e) ++row;
+    ei[r] = none ? W : row;  // row W: never active
+    ej[r] = row + e - row * (2 * W + 1 - row) / 2;
+  }
+  // Gram entries: fixed-order sum of the partials, all loads in flight
+  {
+    double part[kE][kGramParts];
+#pragma unroll
+    for (int r = 0; r < kE; ++r) {
+      const int a = ei[r] < W ? ei[r] : W - 1, b = ej[r];
+#pragma unroll
+      for (int c = 0; c < kGramParts; ++c) part[r][c] = Rin.gram[(size_t)c * kW * kW + a * kW + b];
+    }
+#pragma unroll
+    for (int r = 0; r < kE; ++r) {
+      double s = 0.0;
+#pragma unroll
+      for (int c = 0; c < kGramParts; ++c) s += part[r][c];
+      v[r] = s;
+    }
+  }
+  // largest diagonal entry; row 0 to LDS
+  double dm = 0.0;
+#pragma unroll
+  for (int r = 0; r < kE; ++r) {
+    if (ei[r] < W && ei[r] == ej[r]) dm = fmax(dm, v[r]);
+    if (ei[r] == 0) Gs[0][ej[r]] = v[r];
+  }
+  for (int o = 32; o > 0; o >>= 1) dm = fmax(dm, __shfl_xor(dm, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dm;
+  // lower triangle of the output T is zero
+  for (int e = threadIdx.x; e < W * W; e += kCT)
+    if (e / W > e % W) Rin.T[(e / W) * kW + e % W] = 0.0;
+  __syncthreads();
+  double dmax = 0.0;
+#pragma unroll
+  for (int w = 0; w < kCT / 64; ++w) dmax = fmax(dmax, red[w]);
+  // the owner of a diagonal entry sets up its pivot once the entry is final
+  auto pivot = [&](int k, double p) {
+    const bool ok = dmax > 0.0 && p > kDropTol * dmax;
+    const double y = ok ? rsqrt_f64(p) : 0.0;
+    pinv[k] = y * y;
+    rinv[k] = y;
+  };
+  if (ei[0] == 0 && ej[0] == 0) pivot(0, v[0]);
+  __syncthreads();
+  // Loads are unconditional (indices clamped into the arrays) so that one
+  // wait covers them all; values read for inactive entries are discarded by
+  // the selects.
+  for (int k = 0; k < W; ++k) {
+    const double inv = pinv[k], y = rinv[k];
+    double a[kE], b[kE];
+#pragma unroll
+    for (int r = 0; r < kE; ++r) {
+      a[r] = Gs[k][ei[r] < W ? ei[r] : W - 1];
+      b[r] = Gs[k][ej[r]];
+    }
+#pragma unroll
+    for (int r = 0; r < kE; ++r) {
+      const int i = ei[r], jj = ej[r];
+      if (i == k) R[k][jj] = y != 0.0 ? v[r] * y : 0.0;
+      const double nv = v[r] - (a[r] * inv) * b[r];
+      v[r] = i > k && i < W ? nv : v[r];
+      if (i == k + 1) {
+        Gs[k + 1][jj] = v[r];
+        if (jj == k + 1) pivot(k + 1, v[r]);
+      }
     }
     __syncthreads();
   }
-  for (int e = threadIdx.x; e < W * W; e += kST) Rin.T[(e / W) * kW + e % W] = T[e / W][e % W];
+  // T = R^-1
+#pragma unroll
+  for (int r = 0; r < kE; ++r) v[r] = 0.0;
+  for (int k = W - 1; k >= 0; --k) {
+    const double y = rinv[k];
+#pragma unroll
+    for (int r = 0; r < kE; ++r) {
+      const int i = ei[r], c = ej[r];
+      if (k + 1 < W && i <= k && c > k) v[r] += R[i][k + 1] * Ts[k + 1][c];
+      if (i == k) Ts[k][c] = ((k == c ? 1.0 : 0.0) - v[r]) * y;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < kE; ++r)
+    if (ei[r] < W) Rin.T[ei[r] * kW + ej[r]] = Ts[ei[r]][ej[r]];
 }
 
 // 4d. Out = In T (fp64 accumulate), Out[i][c] for c < ncols.
@@ -873,9 +953,9 @@ __global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
 }
 
 void chol(const RGroup& g, int nb, hipStream_t st) {
-  if (g.w == 32) k_chol<32><<<nb, kST, 0, st>>>(g);
-  else if (g.w == 48) k_chol<48><<<nb, kST, 0, st>>>(g);
-  else k_chol<64><<<nb, kST, 0, st>>>(g);
+  if (g.w == 32) k_chol<32><<<nb, kCT, 0, st>>>(g);
+  else if (g.w == 48) k_chol<48><<<nb, kCT, 0, st>>>(g);
+  else k_chol<64><<<nb, kCT, 0, st>>>(g);
 }
 
 void ritz(const RGroup& g, int nb, hipStream_t st) {
