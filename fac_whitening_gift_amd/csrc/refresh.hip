@@ -14,9 +14,10 @@
 //   2. k_syrk_reduce: fixed-order sum of the partials, / N; the tile and its
 //      mirror image are written row-contiguous through LDS.  k_trace: tr(A).
 //   3. k_sketch: Omega from Philox4x32-10 + Box-Muller (unless given).
-//   4. subspace iteration: Y = A Q on fp32 MFMA (k_gemm_aq), Q = orth(Y) by
-//      CholeskyQR (Fukaya et al.) with an fp64 Gram matrix (k_gram, k_chol,
-//      k_apply); the final basis gets a second CholeskyQR pass.
+//   4. subspace iteration: Y = A Q on fp32 MFMA as partial products over
+//      disjoint K ranges (k_gemm_aq), Q = orth(Y) by CholeskyQR (Fukaya et
+//      al.) with an fp64 Gram matrix (k_gram, which also sums the partials,
+//      k_chol, k_apply); the final basis gets a second CholeskyQR pass.
 //   5. Rayleigh-Ritz: B = Q^T A Q (k_gemm_aq + k_gram), cyclic Jacobi on B in
 //      one workgroup per input (Golub & Van Loan, sym.schur2 rotations,
 //      round-robin ordering: 32 disjoint rotations at once), sort,
@@ -40,6 +41,7 @@ constexpr int kKStep = 32;           // tokens per SYRK step (fp32 activations)
 constexpr int kKStepB = 64;          // tokens per SYRK step (bf16 activations)
 constexpr int kW = GIFT_MAX_SKETCH;  // largest subspace width
 constexpr int kGramParts = 16;       // Gram partial sums per input
+constexpr int kYSplit = 4;           // K ranges of Y = A Q, summed by k_gram
 constexpr double kDropTol = 1e-12;   // CholeskyQR pivot drop threshold (relative)
 constexpr int kMaxSweeps = 20;
 // off-diagonal / total squared mass at which the sweeps stop: an off-diagonal
@@ -72,7 +74,7 @@ SyrkPlan syrk_plan(int64_t d, int64_t n, int n_inputs) {
 }
 
 struct WsLayout {
-  size_t A, part, om, y, q, q1, gram, T, tr, total;
+  size_t A, part, om, y, yp, q, q1, gram, T, tr, total;
 };
 
 WsLayout ws_layout(int64_t d, int64_t n, int w, int n_inputs) {
@@ -83,6 +85,7 @@ WsLayout ws_layout(int64_t d, int64_t n, int w, int n_inputs) {
   L.part = o; o += al((size_t)p.nsplit * p.npairs * kSyrkTile * kSyrkTile * 4);
   L.om = o; o += al((size_t)d * w * 4);
   L.y = o; o += al((size_t)d * w * 4);
+  L.yp = o; o += al((size_t)kYSplit * d * w * 4);
   L.q = o; o += al((size_t)d * w * 4);
   L.q1 = o; o += al((size_t)d * w * 4);
   L.gram = o; o += al((size_t)kGramParts * kW * kW * 8);
@@ -100,6 +103,7 @@ struct RIn {
   const float* om;
   float* om_ws;
   float* Y;
+  float* Yp;     // kYSplit partial products A Q, each d x w
   float* Q;
   float* Q1;
   double* gram;
@@ -497,15 +501,17 @@ __global__ __launch_bounds__(kT) void k_sketch(RGroup g) {
 }
 
 // ---------------------------------------------------------------------------
-// 4a. Y = A Q  (A d x d fp32 symmetric, Q d x w) on v_mfma_f32_16x16x4_f32.
-// Workgroup: 16 rows of Y; its 8 waves split K; fixed-order wave sum.
-// Lane group g's k-slot in MFMA s of a 16-wide K chunk is k0 + 4g + s.
-// grid: (max d / 16, inputs).  which: 0 = Y = A Om, 1 = Y = A Q
+// 4a. Y = A Q  (A d x d fp32 symmetric, Q d x w) on v_mfma_f32_16x16x4_f32,
+// as kYSplit partial products over disjoint K ranges (k_gram sums them in
+// split order).  Workgroup: 16 rows of one partial; its 4 waves split the
+// K range further and are summed in wave order through LDS.  Lane group g's
+// k-slot in MFMA s of a 16-wide K chunk is k0 + 4g + s.
+// grid: (max d / 16, kYSplit, inputs).  which: 0 = Y = A Om, 1 = Y = A Q
 // ---------------------------------------------------------------------------
-constexpr int kGemmWaves = 8;
+constexpr int kGemmWaves = 4;
 
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which) {
-  const RIn& R = g.r[blockIdx.y];
+  const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
   if ((int)blockIdx.x * 16 >= d) return;
   const float* __restrict__ A = R.A;
@@ -518,8 +524,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which
   f32x4 acc[kW / 16];
 #pragma unroll
   for (int t = 0; t < kW / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int kchunks = d / 16;
-  const int kc_begin = wave * kchunks / kGemmWaves, kc_end = (wave + 1) * kchunks / kGemmWaves;
+  const int kchunks = d / 16, slice = blockIdx.y * kGemmWaves + wave;
+  constexpr int kSlices = kYSplit * kGemmWaves;
+  const int kc_begin = slice * kchunks / kSlices, kc_end = (slice + 1) * kchunks / kSlices;
   const float* arow = A + (int64_t)(row0 + r16) * d;
   // one K chunk of 16: this lane's 4 values of A's row and its 4 x 4 of Q
   struct Chunk {
@@ -564,54 +571,99 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][4 * gq + i][16 * t + r16] = acc[t][i];
   __syncthreads();
+  float* __restrict__ Yp = R.Yp + (size_t)blockIdx.y * d * w;
   for (int e = threadIdx.x; e < 16 * w; e += 64 * kGemmWaves) {
     const int r = e / w, c = e % w;
     float s = red[0][r][c];
 #pragma unroll
     for (int v = 1; v < kGemmWaves; ++v) s += red[v][r][c];
-    R.Y[(int64_t)(row0 + r) * w + c] = s;
+    Yp[(int64_t)(row0 + r) * w + c] = s;
   }
 }
 
 // ---------------------------------------------------------------------------
 // 4b. Gram partials: gram[p][a][b] = sum_{i in part p} P[i][a] S[i][b] (fp64).
-// grid: (kGramParts, inputs).  which: 0 = Y^T Y, 1 = Q1^T Q1, 2 = Q^T Y
+// A workgroup takes one row range (part) and one 32 x 32 block of the
+// output; a thread accumulates one a and four consecutive b.  Rows come in
+// chunks of 64, converted to fp64 once as they are staged in LDS; the next
+// chunk's loads are issued before the current chunk is used.
+// Y comes as the kYSplit partial products of k_gemm_aq, summed here in split
+// order as rows are staged; the two diagonal blocks (Y's two column halves)
+// write the sum to Y for k_apply.
+// grid: (kGramParts * 4, inputs).  which: 0 = Y^T Y, 1 = Q1^T Q1, 2 = Q^T Y
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void k_gram(RGroup g, int which) {
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d, w = g.w;
-  const float* __restrict__ P = which == 0 ? R.Y : which == 1 ? R.Q1 : R.Q;
-  const float* __restrict__ S = which == 2 ? R.Y : P;
-  __shared__ float sp[64][kW + 1];
-  __shared__ float ss[64][kW + 1];
+  const int part = blockIdx.x >> 2, blk = blockIdx.x & 3;
+  const int a0 = (blk >> 1) * 32, b0 = (blk & 1) * 32;
+  if (a0 >= w || b0 >= w) return;
+  const bool py = which == 0, sy = which != 1;  // operand from the Y partials
+  const float* __restrict__ P = py ? R.Yp : which == 1 ? R.Q1 : R.Q;
+  const float* __restrict__ S = sy ? R.Yp : P;
+  const bool wy = sy && a0 == b0;                // writes its column half of Y
+  const size_t split = (size_t)d * w;
+  __shared__ __align__(16) double sp[64][34];
+  __shared__ __align__(16) double ss[64][34];
   const int per = ((d + kGramParts - 1) / kGramParts + 63) / 64 * 64;
-  const int i_begin = blockIdx.x * per, i_end = min(d, i_begin + per);
-  const int a = threadIdx.x >> 2, b0 = (threadIdx.x & 3) * 16;
-  double s[16];
+  const int i_begin = part * per, i_end = min(d, i_begin + per);
+  const int a = threadIdx.x >> 3, bq = (threadIdx.x & 7) * 4;
+  // staging: thread t moves float4 number t and t + 256 of each 64 x 32 block
+  float4 rp[2], rs[2];
+  auto fetch = [&](int i0) {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) s[k] = 0.0;
+    for (int h = 0; h < 2; ++h) {
+      const int f = threadIdx.x + h * kT, r = f >> 3, c = (f & 7) * 4;
+      const bool in = i0 + r < i_end;
+      const int64_t row = (int64_t)(in ? i0 + r : i_begin) * w;
+      // w is a multiple of 16, so a quad of columns is all in or all out
+      const bool pin = in && a0 + c < w, sin = in && b0 + c < w;
+      auto ld = [&](const float* X, bool ok, bool parts, int col) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!ok) return v;
+        v = *reinterpret_cast<const float4*>(X + row + col);
+        if (parts)
+#pragma unroll
+          for (int q = 1; q < kYSplit; ++q) {
+            const float4 u = *reinterpret_cast<const float4*>(X + q * split + row + col);
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+          }
+        return v;
+      };
+      rp[h] = ld(P, pin, py, a0 + c);
+      rs[h] = ld(S, sin, sy, b0 + c);
+      if (wy && sin) *reinterpret_cast<float4*>(R.Y + row + b0 + c) = rs[h];
+    }
+  };
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  if (i_begin < i_end) fetch(i_begin);
   for (int i0 = i_begin; i0 < i_end; i0 += 64) {
-    const int rows = min(64, i_end - i0);
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * w; e += kT) {
-      const int r = e / w, c = e % w;
-      sp[r][c] = r < rows ? P[(int64_t)(i0 + r) * w + c] : 0.f;
-      ss[r][c] = r < rows ? S[(int64_t)(i0 + r) * w + c] : 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int f = threadIdx.x + h * kT, r = f >> 3, c = (f & 7) * 4;
+      sp[r][c] = rp[h].x; sp[r][c + 1] = rp[h].y; sp[r][c + 2] = rp[h].z; sp[r][c + 3] = rp[h].w;
+      ss[r][c] = rs[h].x; ss[r][c + 1] = rs[h].y; ss[r][c + 2] = rs[h].z; ss[r][c + 3] = rs[h].w;
     }
     __syncthreads();
-    if (a < w) {
-      for (int r = 0; r < rows; ++r) {
-        const double pa = sp[r][a];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) s[k] += pa * (double)ss[r][b0 + k];
-      }
+    if (i0 + 64 < i_end) fetch(i0 + 64);
+    const int rows = min(64, i_end - i0);
+    for (int r = 0; r < rows; ++r) {
+      const double pa = sp[r][a];
+      const double2 q01 = *reinterpret_cast<const double2*>(&ss[r][bq]);
+      const double2 q23 = *reinterpret_cast<const double2*>(&ss[r][bq + 2]);
+      s0 += pa * q01.x;
+      s1 += pa * q01.y;
+      s2 += pa * q23.x;
+      s3 += pa * q23.y;
     }
   }
-  if (a >= w) return;
-  double* out = R.gram + (size_t)blockIdx.x * kW * kW;
-#pragma unroll
-  for (int k = 0; k < 16; ++k)
-    if (b0 + k < w) out[a * kW + b0 + k] = s[k];
+  if (a0 + a >= w) return;
+  double* out = R.gram + (size_t)part * kW * kW + (size_t)(a0 + a) * kW + b0 + bq;
+  if (b0 + bq + 0 < w) out[0] = s0;
+  if (b0 + bq + 1 < w) out[1] = s1;
+  if (b0 + bq + 2 < w) out[2] = s2;
+  if (b0 + bq + 3 < w) out[3] = s3;
 }
 
 // The small dense kernels below run one 1024-thread workgroup per input on a
@@ -1068,6 +1120,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       x.om_ws = reinterpret_cast<float*>(base + L.om);
       x.om = r.sketch ? r.sketch : x.om_ws;
       x.Y = reinterpret_cast<float*>(base + L.y);
+      x.Yp = reinterpret_cast<float*>(base + L.yp);
       x.Q = reinterpret_cast<float*>(base + L.q);
       x.Q1 = reinterpret_cast<float*>(base + L.q1);
       x.gram = reinterpret_cast<double*>(base + L.gram);
@@ -1107,13 +1160,13 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
     // 2. subspace iteration: Y = A Omega, then power_steps x (Q = orth(Y); Y = A Q)
-    const dim3 rows(maxd / 16, nb), grams(kGramParts, nb);
-    k_gemm_aq<<<rows, 64 * kGemmWaves, 0, st>>>(g, 0);
+    const dim3 rows(maxd / 16, nb), grams(kGramParts * 4, nb), gemm(maxd / 16, kYSplit, nb);
+    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 0);
     for (int s = 0; s < power_steps; ++s) {
       k_gram<<<grams, kT, 0, st>>>(g, 0);
       chol(g, nb, st);
       k_apply<<<rows, kT, 0, st>>>(g, 2);  // Q = Y T
-      k_gemm_aq<<<rows, 64 * kGemmWaves, 0, st>>>(g, 1);
+      k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 1);
     }
     // final basis: CholeskyQR2 of Y
     k_gram<<<grams, kT, 0, st>>>(g, 0);
@@ -1123,7 +1176,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     chol(g, nb, st);
     k_apply<<<rows, kT, 0, st>>>(g, 1);  // Q = Q1 T
     // 3. Rayleigh-Ritz on B = Q^T A Q
-    k_gemm_aq<<<rows, 64 * kGemmWaves, 0, st>>>(g, 1);  // Y = A Q
+    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 1);  // Y = A Q
     k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
     ritz(g, nb, st);
     k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V
