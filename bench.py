@@ -22,6 +22,8 @@ the timed region.  One JSON line on stdout.
     python bench.py --workload stack300m     # 24 blocks + embed/head, top-8 by rho
     python bench.py --workload stack600m     # 24 blocks at 1536/4096, 16384 tokens
     python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
+    python bench.py --study interval [--intervals 10,25,50,100]   # refresh-interval ablation
+    python bench.py --study rank [--rank-list 8,16,32]             # factor-rank sweep
     python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
 """
 
@@ -54,14 +56,18 @@ def parse():
     p.add_argument("--counters", action="store_true",
                    help="for runs under hardware-counter collection: no device QR or "
                         "eigendecomposition (host QR for the input bases, no M2 report)")
-    p.add_argument("--study", default=None, choices=["staleness", "copy", "reduce"])
+    p.add_argument("--study", default=None,
+                   choices=["staleness", "interval", "rank", "copy", "reduce"])
+    p.add_argument("--rank-list", default="8,16,32", help="factor ranks (rank study)")
+    p.add_argument("--intervals", default="10,25,50,100", help="refresh intervals (interval study)")
     p.add_argument("--ranks", type=int, default=8, help="ranks of the reduce study")
     p.add_argument("--blocks", type=int, default=1)
     p.add_argument("--hidden", type=int, default=4096)
     p.add_argument("--mlp", type=int, default=11008)
     p.add_argument("--tokens", type=int, default=16384)
     p.add_argument("--angle", type=float, default=0.02)
-    p.add_argument("--study-steps", type=int, default=50)
+    p.add_argument("--study-steps", type=int, default=None,
+                   help="horizon of the staleness (default 50) and interval (default max K) studies")
     return p.parse_args()
 
 
@@ -139,6 +145,12 @@ def main():
         sys.exit(2)
     if args.study == "staleness":
         print(json.dumps(staleness_study(args)), flush=True)
+        return
+    if args.study == "interval":
+        print(json.dumps(interval_study(args)), flush=True)
+        return
+    if args.study == "rank":
+        print(json.dumps(rank_study(args)), flush=True)
         return
     if args.study == "copy":
         print(json.dumps(copy_calibration()), flush=True)
@@ -476,6 +488,77 @@ def copy_calibration(mib=1024, reps=5, device="cuda:0"):
 # staleness study
 # ---------------------------------------------------------------------------
 
+def _rotating_block(args, dev):
+    """Workload of the staleness and interval studies: its inputs, a Haar basis
+    per input and the rotation each input's eigenbasis follows."""
+    import torch
+
+    import synth
+
+    w = synth.llama_stack(args.blocks, args.hidden, args.mlp, args.tokens, exponent=1.5)
+    base, rots = {}, {}
+    for k, spec in enumerate(w.inputs):
+        g = torch.Generator(device=dev).manual_seed(3000 + k)
+        base[spec.name] = synth.haar(spec.d_in, g, dev)
+        rots[spec.name] = synth.rotation_pair(spec.d_in, 4000 + k, dev)
+    return w, base, rots
+
+
+def _inputs_at(w, base, rots, t, angle, dev):
+    """Rotated bases and fresh bf16 activations of every input at step t."""
+    import synth
+
+    Qt, X = {}, {}
+    for k, spec in enumerate(w.inputs):
+        Qt[spec.name] = synth.rotate_input(base[spec.name], rots[spec.name], t * angle) \
+            if t else base[spec.name]
+        X[spec.name] = synth.draw_input(spec, seed=7000 + 100 * t + k, device=dev,
+                                        Q=Qt[spec.name], as_bf16=True)
+    return Qt, X
+
+
+def _step_errors(w, X, Qt, t, methods, block, dev):
+    """M1 and M2 of the round trip of every layer's gradient at step t for each
+    method (name -> factor, None = Euclidean), summed over the layers.  M2 is
+    taken in the metric of the population covariance C_t, whose damped inverse
+    square root is known in closed form for the generator."""
+    import synth
+    import fac_whitening_gift_amd as fg
+
+    sc = fg.SCALE_BLOCK128 if block else fg.SCALE_TENSOR
+    acc = {m: [0.0, 0.0, 0.0] for m in methods}
+    den1 = 0.0
+    for i, l in enumerate(w.layers):
+        inp = X[l.input]
+        G = synth.draw_gradient(l.d_out, Qt[l.input], inp["ev"], seed=9000 + 100 * t + i,
+                                device=dev)
+        lam = 1e-3 * float(inp["ev"].double().sum()) / l.d_in
+        Sdiag = (inp["ev"].double() + lam).rsqrt().float()
+        GS = (G @ Qt[l.input]) * Sdiag
+        den2 = float(GS.double().pow(2).sum())
+        for m, fac in methods.items():
+            L = fg.Layer(G, factor=None if fac is None else fac[l.input], block128=block)
+            if fac is None:
+                fg.gift_euclid_fp8_roundtrip([L], scaling=sc)
+            else:
+                fg.gift_whiten_quantize([L], scaling=sc)
+                fg.gift_dequant_unwhiten([L], scaling=sc)
+            e = fg.gift_roundtrip_error([L]).cpu().numpy()[0]
+            ES = ((L.G_hat - G) @ Qt[l.input]) * Sdiag
+            acc[m][0] += float(e[0])
+            acc[m][1] += float(ES.double().pow(2).sum())
+            acc[m][2] += den2
+        den1 += float(e[1])
+    return {m: (math.sqrt(e1 / den1), math.sqrt(e2 / d2)) for m, (e1, e2, d2) in acc.items()}
+
+
+def _refresh(w, X, factors):
+    import fac_whitening_gift_amd as fg
+
+    fg.gift_refresh_factors([dict(X=X[s.name]["X"], factor=factors[s.name], seed=s_i)
+                             for s_i, s in enumerate(w.inputs)])
+
+
 def staleness_study(args, device="cuda:0"):
     """Error of the round trip as a function of steps since the last factor
     refresh (the falsifier the GIFT review proposes: if at step 49 the stale
@@ -490,62 +573,27 @@ def staleness_study(args, device="cuda:0"):
     closed form for the generator, so no eigensolve is needed)."""
     import torch
 
-    import synth
     import fac_whitening_gift_amd as fg
 
     dev = torch.device(device)
-    w = synth.llama_stack(args.blocks, args.hidden, args.mlp, args.tokens, exponent=1.5)
-    base, rots = {}, {}
-    for k, spec in enumerate(w.inputs):
-        g = torch.Generator(device=dev).manual_seed(3000 + k)
-        base[spec.name] = synth.haar(spec.d_in, g, dev)
-        rots[spec.name] = synth.rotation_pair(spec.d_in, 4000 + k, dev)
+    w, base, rots = _rotating_block(args, dev)
     stale = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
     fresh = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
+    steps = args.study_steps if args.study_steps is not None else 50
     rows = []
-    for t in range(args.study_steps):
-        Qt, X = {}, {}
-        for k, spec in enumerate(w.inputs):
-            Qt[spec.name] = synth.rotate_input(base[spec.name], rots[spec.name], t * args.angle) \
-                if t else base[spec.name]
-            X[spec.name] = synth.draw_input(spec, seed=7000 + 100 * t + k, device=dev,
-                                            Q=Qt[spec.name], as_bf16=True)
+    for t in range(steps):
+        Qt, X = _inputs_at(w, base, rots, t, args.angle, dev)
         if t == 0:
-            fg.gift_refresh_factors([dict(X=X[s.name]["X"], factor=stale[s.name], seed=s_i)
-                                     for s_i, s in enumerate(w.inputs)])
-        fg.gift_refresh_factors([dict(X=X[s.name]["X"], factor=fresh[s.name], seed=s_i)
-                                 for s_i, s in enumerate(w.inputs)])
+            _refresh(w, X, stale)
+        _refresh(w, X, fresh)
         res = {"step": t}
         for block in (False, True):
-            sc = fg.SCALE_BLOCK128 if block else fg.SCALE_TENSOR
-            acc = {m: [0.0, 0.0, 0.0] for m in ("euclid", "stale", "fresh")}
-            den1 = 0.0
-            for i, l in enumerate(w.layers):
-                inp = X[l.input]
-                G = synth.draw_gradient(l.d_out, Qt[l.input], inp["ev"], seed=9000 + 100 * t + i,
-                                        device=dev)
-                lam = 1e-3 * float(inp["ev"].double().sum()) / l.d_in
-                Sdiag = (inp["ev"].double() + lam).rsqrt().float()
-                GS = (G @ Qt[l.input]) * Sdiag
-                den2 = float(GS.double().pow(2).sum())
-                for m, fac in (("euclid", None), ("stale", stale[l.input]),
-                               ("fresh", fresh[l.input])):
-                    L = fg.Layer(G, factor=fac, block128=block)
-                    if fac is None:
-                        fg.gift_euclid_fp8_roundtrip([L], scaling=sc)
-                    else:
-                        fg.gift_whiten_quantize([L], scaling=sc)
-                        fg.gift_dequant_unwhiten([L], scaling=sc)
-                    e = fg.gift_roundtrip_error([L]).cpu().numpy()[0]
-                    ES = ((L.G_hat - G) @ Qt[l.input]) * Sdiag
-                    acc[m][0] += float(e[0])
-                    acc[m][1] += float(ES.double().pow(2).sum())
-                    acc[m][2] += den2
-                den1 += float(e[1])
+            err = _step_errors(w, X, Qt, t, {"euclid": None, "stale": stale, "fresh": fresh},
+                               block, dev)
             tag = "b128" if block else "tensor"
-            for m, (e1, e2, d2) in acc.items():
-                res["m1_%s_%s" % (m, tag)] = math.sqrt(e1 / den1)
-                res["m2_%s_%s" % (m, tag)] = math.sqrt(e2 / d2)
+            for m, (m1, m2) in err.items():
+                res["m1_%s_%s" % (m, tag)] = m1
+                res["m2_%s_%s" % (m, tag)] = m2
         rows.append(res)
         if not args.quiet:
             print("[staleness] %s" % json.dumps({k: (round(v, 5) if isinstance(v, float) else v)
@@ -558,6 +606,130 @@ def staleness_study(args, device="cuda:0"):
             "falsified_at_last_step_m1": bool(last["m1_stale_tensor"] >= last["m1_euclid_tensor"]),
             "rows": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                      for r in rows]}
+
+
+def interval_study(args, device="cuda:0"):
+    """Ablation over the refresh interval K (the GIFT referee report asks for
+    K in {10, 25, 50, 100}, measuring the round-trip error and the cost-quality
+    trade-off).  On the rotating workload of the staleness study, one factor
+    set per K is refreshed at every step t with t % K == 0 and used at every
+    step in between; per-tensor E4M3.  Reported per K: M1 and M2 averaged over
+    the horizon, M2 at the stalest step, and the grouped refresh's time
+    amortized over K steps; the Euclidean round trip alongside."""
+    import torch
+
+    import fac_whitening_gift_amd as fg
+
+    dev = torch.device(device)
+    w, base, rots = _rotating_block(args, dev)
+    intervals = [int(k) for k in args.intervals.split(",")]
+    facs = {k: {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs} for k in intervals}
+    steps = args.study_steps if args.study_steps is not None else max(intervals)
+    sums = {m: [0.0, 0.0, 0.0] for m in ["euclid"] + intervals}   # m1, m2, worst m2
+    refresh_ms = []
+    for t in range(steps):
+        Qt, X = _inputs_at(w, base, rots, t, args.angle, dev)
+        for k in intervals:
+            if t % k == 0:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                _refresh(w, X, facs[k])
+                e1.record()
+                torch.cuda.synchronize()
+                refresh_ms.append(e0.elapsed_time(e1))
+        methods = {"euclid": None}
+        methods.update({k: facs[k] for k in intervals})
+        err = _step_errors(w, X, Qt, t, methods, False, dev)
+        for m, (m1, m2) in err.items():
+            sums[m][0] += m1
+            sums[m][1] += m2
+            sums[m][2] = max(sums[m][2], m2)
+        if not args.quiet:
+            print("[interval] step %d %s" % (t, json.dumps({str(m): round(v[1], 5)
+                                                             for m, v in err.items()})),
+                  file=sys.stderr, flush=True)
+    # the first refresh of a run carries one-time set-up; the median of the rest
+    rms = sorted(refresh_ms[1:] or refresh_ms)[len(refresh_ms[1:] or refresh_ms) // 2]
+    rows = []
+    for k in intervals:
+        rows.append({"K": k, "m1_mean": round(sums[k][0] / steps, 6),
+                     "m2_mean": round(sums[k][1] / steps, 6), "m2_worst": round(sums[k][2], 6),
+                     "m2_reduction_vs_euclid": round(1 - sums[k][1] / sums["euclid"][1], 4),
+                     "refreshes": -(-steps // k),
+                     "refresh_ms_per_step": round(rms / k, 5)})
+    return {"study": "interval", "workload": w.name, "angle_rad_per_step": args.angle,
+            "steps": steps, "refresh_ms": round(rms, 4),
+            "euclid": {"m1_mean": round(sums["euclid"][0] / steps, 6),
+                       "m2_mean": round(sums["euclid"][1] / steps, 6)},
+            "rows": rows}
+
+
+# ---------------------------------------------------------------------------
+# rank study
+# ---------------------------------------------------------------------------
+
+def rank_study(args, device="cuda:0"):
+    """Round-trip error as a function of the factor's rank (the review chose
+    rank 32 from a round-trip error table over ranks).  On the hidden-1024
+    block (4 inputs, 7 gradients): for each rank r, the grouped refresh keeps
+    the top r Ritz pairs of the same subspace iteration (sketch width 64) and
+    damps with the mean of the d_in - r discarded eigenvalues; then the
+    grouped per-tensor E4M3 round trip of all 7 gradients.  M1 from the
+    device error sums, M2 in the metric of the exact damped sample
+    covariance (fp64 eigendecomposition on the device, measurement harness);
+    the Euclidean round trip of the same gradients alongside."""
+    import numpy as np
+    import torch
+
+    import synth
+    import fac_whitening_gift_amd as fg
+
+    dev = torch.device(device)
+    w = synth.llama_block(hidden=1024, mlp=2816, tokens=8192, exponent=1.5)
+    inputs = {s.name: synth.draw_input(s, seed=1000 + k, device=dev, as_bf16=True)
+              for k, s in enumerate(w.inputs)}
+    grads = [synth.draw_gradient(l.d_out, inputs[l.input]["Q"], inputs[l.input]["ev"],
+                                 seed=5000 + i, device=dev) for i, l in enumerate(w.layers)]
+    S = {}
+    for name, inp in inputs.items():
+        X = inp["X"].double()
+        A = X.T @ X / X.shape[0]
+        lam = 1e-3 * torch.trace(A) / A.shape[0]
+        ev_, V = torch.linalg.eigh(A)
+        S[name] = (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
+    den2 = sum(float(torch.linalg.norm(G.double() @ S[l.input]) ** 2)
+               for G, l in zip(grads, w.layers))
+
+    def errors(layers):
+        err = fg.gift_roundtrip_error(layers).cpu().numpy()
+        m1 = float(np.sqrt(err[:, 0].sum() / err[:, 1].sum()))
+        num = sum(float(torch.linalg.norm((L.G_hat.double() - L.G.double()) @ S[l.input]) ** 2)
+                  for L, l in zip(layers, w.layers))
+        return m1, float(np.sqrt(num / den2))
+
+    eu = [fg.Layer(G) for G in grads]
+    fg.gift_euclid_fp8_roundtrip(eu)
+    m1_e, m2_e = errors(eu)
+    rows = []
+    for r in [int(x) for x in args.rank_list.split(",")]:
+        facs = {s.name: fg.Factor(s.d_in, device=dev, rank=r) for s in w.inputs}
+        items = [dict(X=inputs[s.name]["X"], factor=facs[s.name], seed=k)
+                 for k, s in enumerate(w.inputs)]
+        fg.gift_refresh_factors(items)
+        gl = [fg.Layer(G, factor=facs[l.input]) for G, l in zip(grads, w.layers)]
+        fg.gift_whiten_quantize(gl)
+        fg.gift_dequant_unwhiten(gl)
+        m1, m2 = errors(gl)
+        lam = [float(facs[s.name].coef[fg.COEF_LAMBDA_ISO]) for s in w.inputs]
+        rows.append({"rank": r, "m1": round(m1, 5), "m2": round(m2, 5),
+                     "m1_ratio_vs_euclid": round(m1 / m1_e, 4),
+                     "m2_reduction_vs_euclid": round(1 - m2 / m2_e, 4),
+                     "lambda_iso": [float("%.4g" % x) for x in lam]})
+        if not args.quiet:
+            print("[rank] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    return {"study": "rank", "workload": w.name, "scaling": "per-tensor E4M3",
+            "damping": "floor+tail", "euclid": {"m1": round(m1_e, 5), "m2": round(m2_e, 5)},
+            "rows": rows}
 
 
 # ---------------------------------------------------------------------------

@@ -152,16 +152,20 @@ def _dev(t, dtype, shape, name):
 # --------------------------------------------------------------------------
 
 class Factor:
-    """Device buffers of one rank-32 factor: U (d_in x 32), theta (32), coef,
-    and (by default, when d_in % 32 == 0) the operand packs of U.
+    """Device buffers of one factor: U (d_in x 32), theta (32), coef, and (by
+    default, when d_in % 32 == 0) the operand packs of U.  rank (1..32) is
+    the effective rank the refresh keeps; the storage stays 32 columns wide,
+    zero from rank on.
 
     A factor built from given U / coef values has stale packs until
     gift_prepare_factor(factor) runs; gift_refresh_factor(s) rewrite them.
     packs=False leaves the pointer NULL (every grouped call re-packs U).
     """
 
-    def __init__(self, d_in, device="cuda", U=None, theta=None, coef=None, packs=True):
+    def __init__(self, d_in, device="cuda", U=None, theta=None, coef=None, packs=True,
+                 rank=RANK):
         self.d_in = int(d_in)
+        self.rank = int(rank)
         device = U.device if U is not None else device
         self.U = U if U is not None else torch.zeros(d_in, RANK, device=device)
         self.theta = theta if theta is not None else torch.zeros(RANK, device=device)
@@ -173,7 +177,7 @@ class Factor:
         if packs and self.d_in % 32 == 0:
             nb = int(load().gift_factor_pack_bytes(self.d_in))
             self.packs = torch.empty(nb, dtype=torch.uint8, device=self.U.device)
-        self._struct = _Factor(self.d_in, RANK, self.U.data_ptr(), self.theta.data_ptr(),
+        self._struct = _Factor(self.d_in, self.rank, self.U.data_ptr(), self.theta.data_ptr(),
                                self.coef.data_ptr(),
                                self.packs.data_ptr() if self.packs is not None else None)
 

@@ -205,8 +205,8 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
       return fail(GIFT_ERR_INVALID_ARG, "layer %d: device pointers must be 16-byte aligned", i);
     if (whitened(L, op)) {
       const gift_factor& f = *L.factor;
-      if (f.rank != kRank)
-        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor rank %d != %d", i, f.rank, kRank);
+      if (f.rank < 1 || f.rank > kRank)
+        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor rank %d not in [1, %d]", i, f.rank, kRank);
       if (f.d_in != L.d_in)
         return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor d_in %d != layer d_in %lld", i,
                     f.d_in, (long long)L.d_in);
@@ -473,7 +473,7 @@ gift_status gift_prepare_factor(const gift_factor* f, void* stream) {
   if (!f || !f->U || !f->packs) return fail(GIFT_ERR_INVALID_ARG, "factor, U or packs is NULL");
   if (!aligned16(f->U) || !aligned16(f->packs))
     return fail(GIFT_ERR_INVALID_ARG, "U / packs must be 16-byte aligned");
-  if (f->rank != kRank) return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be 32");
+  if (f->rank < 1 || f->rank > kRank) return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be in [1, 32]");
   if (f->d_in < 64 || f->d_in % 32 || f->d_in > kMaxDim)
     return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "d_in must be >= 64 and a multiple of 32");
   PackGroup pg{};

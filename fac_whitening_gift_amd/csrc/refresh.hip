@@ -116,6 +116,7 @@ struct RIn {
   int64_t chunk;
   uint64_t seed;
   int d, nb, npairs, nsplit;
+  int rank;      // effective rank: columns of U from it on are zero
 };
 
 struct RGroup {
@@ -964,20 +965,22 @@ __global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
     order[rank] = i;
   }
   __syncthreads();
-  // T[:, k] = V[:, order[k]] for the top rank
+  // T[:, k] = V[:, order[k]] for the top rank r (zero columns after it)
+  const int rk = Rin.rank;
   for (int e = threadIdx.x; e < W * kRank; e += kST) {
     const int r = e / kRank, k = e % kRank;
-    Rin.T[r * kW + k] = V[r][order[k]];
+    Rin.T[r * kW + k] = k < rk ? V[r][order[k]] : 0.0;
   }
+  // damping from the top r Ritz values: lambda_floor, plus the mean of the
+  // d - r discarded eigenvalues in the floor+tail reading
+  const double t = *Rin.tr;
+  double sum = 0.0;
+  for (int k = 0; k < rk; ++k) sum += fmax(ev[order[k]], 0.0);
+  const double lam_floor = (double)g.eps * t / d;
+  const double tail = d > rk ? fmax(0.0, (t - sum) / (d - rk)) : 0.0;
+  const double lam = fmax(g.mode == GIFT_DAMP_FLOOR_PLUS_TAIL ? lam_floor + tail : lam_floor, 1e-30);
+  const double s0 = sqrt(lam);
   if (threadIdx.x == 0) {
-    const double t = *Rin.tr;
-    double sum = 0.0;
-    for (int k = 0; k < kRank; ++k) sum += fmax(ev[order[k]], 0.0);
-    const double lam_floor = (double)g.eps * t / d;
-    const double tail = d > kRank ? fmax(0.0, (t - sum) / (d - kRank)) : 0.0;
-    double lam = g.mode == GIFT_DAMP_FLOOR_PLUS_TAIL ? lam_floor + tail : lam_floor;
-    lam = fmax(lam, 1e-30);
-    const double s0 = sqrt(lam);
     float* coef = Rin.coef;
     coef[GIFT_COEF_ALPHA] = (float)(1.0 / s0);
     coef[GIFT_COEF_BETA] = (float)s0;
@@ -990,13 +993,7 @@ __global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
   }
   if (threadIdx.x < kRank) {
     const int k = threadIdx.x;
-    const double t = *Rin.tr;
-    double sum = 0.0;
-    for (int j = 0; j < kRank; ++j) sum += fmax(ev[order[j]], 0.0);
-    const double lam_floor = (double)g.eps * t / d;
-    const double tail = d > kRank ? fmax(0.0, (t - sum) / (d - kRank)) : 0.0;
-    const double lam = fmax(g.mode == GIFT_DAMP_FLOOR_PLUS_TAIL ? lam_floor + tail : lam_floor, 1e-30);
-    const double s0 = sqrt(lam), th = fmax(ev[order[k]], 0.0), s = sqrt(th + lam);
+    const double th = k < rk ? fmax(ev[order[k]], 0.0) : 0.0, s = sqrt(th + lam);
     // (th+lam)^-1/2 - lam^-1/2 and (th+lam)^1/2 - lam^1/2 without cancellation
     Rin.coef[GIFT_COEF_DW + k] = (float)(-th / (s * s0 * (s + s0)));
     Rin.coef[GIFT_COEF_DU + k] = (float)(th / (s + s0));
@@ -1084,7 +1081,8 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       return bad(GIFT_ERR_INVALID_ARG, at + "device pointers must be 16-byte aligned");
     if (r.x_dtype != GIFT_DTYPE_F32 && r.x_dtype != GIFT_DTYPE_BF16)
       return bad(GIFT_ERR_INVALID_ARG, at + "unknown x_dtype");
-    if (f->rank != kRank) return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "rank must be 32");
+    if (f->rank < 1 || f->rank > kRank)
+      return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "rank must be in [1, 32]");
     if (f->d_in < 64 || f->d_in % 16 || f->d_in > 16384)
       return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "d_in must be in [64, 16384], % 16 == 0");
     if (f->packs && f->d_in % 32)
@@ -1133,6 +1131,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       x.chunk = p.chunk;
       x.seed = r.seed;
       x.d = d;
+      x.rank = r.factor->rank;
       x.nb = p.nb;
       x.npairs = p.npairs;
       x.nsplit = p.nsplit;

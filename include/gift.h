@@ -111,17 +111,23 @@ enum {
 };
 
 /*
- * Rank-32 input-side factor A_r = U diag(theta) U^T + lambda_iso I of one
- * distinct layer input.  Its inverse square root is
+ * Rank-r input-side factor A_r = U diag(theta) U^T + lambda_iso I of one
+ * distinct layer input (r = 32 in the review's configuration; its
+ * round-trip error table compares ranks, which is why r may be lower).  Its
+ * inverse square root is
  *     A_r^-1/2 = alpha I + U diag(D_w) U^T
  * and its square root A_r^1/2 = beta I + U diag(D_u) U^T (U orthonormal).
+ * The storage always holds GIFT_RANK columns: for r < GIFT_RANK the columns
+ * of U and the entries of theta, D_w and D_u from r on are zero, so every
+ * kernel works on 32 columns and the zero ones add exact zeros.
  * Written by gift_refresh_factor; a caller may also fill it itself.
  */
 typedef struct gift_factor {
     int32_t d_in;     /* rows of U; 64 <= d_in, % 16 == 0 (% 32 to whiten)    */
-    int32_t rank;     /* must be GIFT_RANK                                    */
-    float *U;         /* device, d_in x rank, row-major                       */
-    float *theta;     /* device, rank: Ritz values, descending, >= 0          */
+    int32_t rank;     /* effective rank r, 1 <= r <= GIFT_RANK; the refresh
+                         keeps the top r Ritz pairs and damps with d_in - r   */
+    float *U;         /* device, d_in x GIFT_RANK, row-major                  */
+    float *theta;     /* device, GIFT_RANK: Ritz values, descending, >= 0     */
     float *coef;      /* device, GIFT_COEF_COUNT floats (layout above)        */
     void *packs;      /* optional device buffer of gift_factor_pack_bytes(d_in)
                          bytes: U split into the bf16 operand layouts of the

@@ -72,8 +72,9 @@ def test_block_scaling_needs_multiple_of_128():
 def test_factor_validation():
     f = _lib._Factor(128, 32, 0x20000, 0x30000, 0x40000, None)
     assert _call_whiten([_layer(d_in=256, factor=ctypes.pointer(f))]) == 1   # d_in mismatch
-    f_bad_rank = _lib._Factor(128, 16, 0x20000, 0x30000, 0x40000, None)
-    assert _call_whiten([_layer(d_in=128, factor=ctypes.pointer(f_bad_rank))]) == 2
+    for bad in (0, 33, -1):   # the effective rank is 1..32
+        f_bad_rank = _lib._Factor(128, bad, 0x20000, 0x30000, 0x40000, None)
+        assert _call_whiten([_layer(d_in=128, factor=ctypes.pointer(f_bad_rank))]) == 2
     f_small = _lib._Factor(32, 32, 0x20000, 0x30000, 0x40000, None)
     assert _call_whiten([_layer(d_in=32, factor=ctypes.pointer(f_small))]) == 2
     f_odd = _lib._Factor(80, 32, 0x20000, 0x30000, 0x40000, None)   # d_in % 32 != 0
@@ -130,7 +131,9 @@ def test_refresh_validation():
     r[0].n_tokens = 1024
     f.d_in = 100
     assert call() == 2
-    f.d_in, f.rank = 128, 31
+    f.d_in, f.rank = 128, 33   # the effective rank is 1..32
+    assert call() == 2
+    f.rank = 0
     assert call() == 2
     assert lib.gift_refresh_group_workspace_bytes(r, 1, 64) == 0 or True
     assert lib.gift_factor_pack_bytes(1024) == 1024 * 384

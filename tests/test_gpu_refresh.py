@@ -24,8 +24,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_refresh(X_dev, d, sketch=None, mode=fg.DAMP_FLOOR_PLUS_TAIL, width=64, steps=4,
-                 seed=0, eps=1e-3):
-    f = fg.Factor(d)
+                 seed=0, eps=1e-3, rank=32):
+    f = fg.Factor(d, rank=rank)
     A = torch.empty(d, d, dtype=torch.float32, device=DEV)
     fg.gift_refresh_factor(X_dev, f, damp_eps=eps, damping_mode=mode, sketch_width=width,
                            power_steps=steps, seed=seed, sketch=sketch, A_out=A)
@@ -229,3 +229,48 @@ def test_selection_from_device_factors():
     rhos_o = [None if f is None else rho_o[facs.index(f)] for f in layer_factors]
     for k in (1, 2, 4, 10):
         assert select_layers(layer_factors, k) == og.select_top_k(rhos_o, k)
+
+
+@pytest.mark.parametrize("rank", [8, 16, 1])
+def test_factor_lower_rank(rank):
+    """Effective rank r < 32: the top r Ritz pairs of the same subspace,
+    damping with the d_in - r discarded eigenvalues, zero columns from r on;
+    the round trip through the kernels with that factor matches the oracle's
+    rank-r whitening, codes and reconstruction."""
+    say("factor rank %d d_in 512" % rank)
+    spec = synth.InputSpec("x", 512, 4096, 1.5, bf16=False)
+    inp = synth.draw_input(spec, seed=41)
+    omega = synth.gaussian_sketch(512, 64, seed=42)
+    f_dev, _ = _run_refresh(inp["X"].to(DEV), 512, sketch=omega.to(DEV), rank=rank)
+    f_orc = og.refresh_factor(inp["X"].numpy(), omega.numpy().astype(np.float64), rank=rank)
+    U = host(f_dev.U).astype(np.float64)
+    th = host(f_dev.theta).astype(np.float64)
+    c = host(f_dev.coef).astype(np.float64)
+    dw = c[fg.COEF_DW:fg.COEF_DW + 32]
+    du = c[fg.COEF_DU:fg.COEF_DU + 32]
+    assert np.all(U[:, rank:] == 0) and np.all(th[rank:] == 0)
+    assert np.all(dw[rank:] == 0) and np.all(du[rank:] == 0)
+    assert np.allclose(th[:rank], f_orc.theta, rtol=1e-4, atol=1e-7 * f_orc.theta[0])
+    for k, ref in ((fg.COEF_LAMBDA_ISO, f_orc.lambda_iso), (fg.COEF_ALPHA, f_orc.alpha),
+                   (fg.COEF_SIGMA2_TAIL, f_orc.sigma2_tail)):
+        assert abs(c[k] - ref) <= 1e-5 * abs(ref), k
+    assert np.linalg.norm(U[:, :rank].T @ U[:, :rank] - np.eye(rank)) < 1e-5
+    P = np.random.default_rng(3).standard_normal((64, 512))
+    assert rel_fro(og.whiten_with(P, U, c[fg.COEF_ALPHA], dw), og.whiten(P, f_orc)) <= 1e-4
+    assert rel_fro(og.unwhiten_with(P, U, c[fg.COEF_BETA], du), og.unwhiten(P, f_orc)) <= 1e-4
+    # round trip with the rank-r factor (P-a, P-b, P-c against its own values)
+    G = (np.random.default_rng(5).standard_normal((96, 512)) *
+         np.exp(np.random.default_rng(6).standard_normal((96, 1)))).astype(np.float32)
+    Gd = torch.from_numpy(G).to(DEV)
+    W = torch.empty_like(Gd)
+    L = fg.Layer(Gd, factor=f_dev, W_out=W)
+    fg.gift_whiten_quantize([L])
+    fg.gift_dequant_unwhiten([L])
+    U32, alpha, beta, dw32, du32 = (host(f_dev.U), float(c[fg.COEF_ALPHA]), float(c[fg.COEF_BETA]),
+                                    dw.astype(np.float32), du.astype(np.float32))
+    Wg = host(W)
+    assert rel_fro(Wg, og.whiten_with(G, U32, alpha, dw32)) <= 1e-5
+    codes, inv_o, _ = og.quantize(Wg, False)
+    assert np.array_equal(host(L.q), codes)
+    ref = og.unwhiten_with(og.dequantize(host(L.q), inv_o, False), U32, beta, du32)
+    assert rel_fro(host(L.G_hat), ref) <= 1e-5

@@ -30,3 +30,19 @@ def test_staleness_small():
     # the stale factor degrades with the rotation
     assert r5["m2_stale_tensor"] > 1.5 * r0["m2_stale_tensor"]
     assert np.all(np.diff([r["m2_stale_tensor"] for r in rows]) > -1e-3)
+
+
+def test_interval_small():
+    say("interval study hidden 256 mlp 512, K in 1,2,4 over 8 steps of 0.15 rad")
+    args = argparse.Namespace(blocks=1, hidden=256, mlp=512, tokens=4096, angle=0.15,
+                              study_steps=8, intervals="1,2,4", quiet=True)
+    out = bench.interval_study(args)
+    rows = {r["K"]: r for r in out["rows"]}
+    assert [rows[k]["refreshes"] for k in (1, 2, 4)] == [8, 4, 2]
+    # refreshing every step keeps GIFT's advantage in the K-FAC metric
+    assert rows[1]["m2_mean"] < 0.7 * out["euclid"]["m2_mean"]
+    # a longer interval means staler factors on a rotating eigenbasis
+    assert rows[1]["m2_mean"] <= rows[2]["m2_mean"] + 1e-4
+    assert rows[2]["m2_mean"] <= rows[4]["m2_mean"] + 1e-4
+    assert rows[4]["m2_worst"] >= rows[1]["m2_worst"]
+    assert out["refresh_ms"] > 0 and rows[4]["refresh_ms_per_step"] < rows[1]["refresh_ms_per_step"]
