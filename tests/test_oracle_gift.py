@@ -81,6 +81,28 @@ def test_subspace_iteration_matches_eigh_on_power_law(layer):
     assert abs(f.trace - np.sum(w)) < 1e-10 * np.sum(w)
 
 
+@pytest.mark.parametrize("r", [8, 16])
+def test_lower_rank_factor_matches_eigh(layer, r):
+    """rank r < 32 (the rank sweep): the top r Ritz pairs of the same subspace
+    are the top r eigenpairs of A, the tail variance is the mean of the d - r
+    discarded eigenvalues, and the rank-r part is (near) the best rank-r
+    approximation (Eckart-Young)."""
+    A = layer["A"]
+    f = og.refresh_factor(layer["X"], layer["omega"], rank=r, A=A)
+    w, V = np.linalg.eigh(A)
+    w, V = w[::-1], V[:, ::-1]
+    assert f.U.shape == (512, r) and f.theta.shape == (r,)
+    assert np.allclose(f.theta, w[:r], rtol=1e-6, atol=0)
+    assert np.linalg.svd(V[:, :r].T @ f.U, compute_uv=False).min() > 0.9999
+    assert abs(f.sigma2_tail - np.mean(w[r:])) < 1e-6 * np.mean(w[r:])
+    assert abs(f.lambda_iso - (1e-3 * np.sum(w) / 512 + np.mean(w[r:]))) < 1e-6 * f.lambda_iso
+    best = np.sqrt(np.sum(w[r:] ** 2))
+    assert np.linalg.norm(A - (f.U * f.theta) @ f.U.T) <= best * (1 + 1e-4)
+    # the rank-32 factor's top r pairs are the rank-r factor's
+    f32 = layer["f"]
+    assert np.allclose(f32.theta[:r], f.theta, rtol=1e-12, atol=0)
+
+
 def test_damping_readings():
     theta = np.array([4.0, 2.0])
     lam, lf, tail = og.damping(10.0, theta, 6, 1e-3, og.DAMPING_FLOOR_PLUS_TAIL)
