@@ -41,6 +41,13 @@ implementation's reading, each marked where it is taken:
    the same round trip with the whitened tensor stored as OCP MXFP4
    (oracle/mxfp4.py: E2M1 elements, one power-of-two scale per 32
    elements of a row).
+10. Block-diagonal factor "block-A-b" (the review's round-trip error table
+   names block-A-32 and block-A-64 without defining them; reading): A is
+   replaced by its d_in/b diagonal b x b blocks A_i, each damped by
+   lambda_floor and used in full: W[:, block i] = G[:, block i] S_i with
+   S_i = (A_i + lambda_floor I)^{-1/2}, and G^[:, block i] =
+   W^[:, block i] (A_i + lambda_floor I)^{1/2}.  A block keeps its whole
+   spectrum, so there is no discarded tail to add to the damping.
 
 Precision: inputs are fp32 (activations bf16 values held in fp32); every
 linear-algebra step runs in fp64.  The steps that decide an integer (the
@@ -337,6 +344,77 @@ def gift_roundtrip_mx(G, f):
     W32 = whiten(G, f).astype(np.float32)
     codes, scales, flags = mxfp4.quantize(W32)
     return codes, scales, W32, unwhiten(mxfp4.dequantize(codes, scales), f), flags
+
+
+# --------------------------------------------------------------------------
+# block-diagonal factor (step 10)
+# --------------------------------------------------------------------------
+
+@dataclass
+class BlockFactor:
+    """S and S^-1 of every diagonal block, stacked: rows b*i .. b*i+b-1 of
+    S (d_in x b) hold S_i = (A_i + lambda I)^{-1/2}, likewise S_inv; theta
+    holds each block's eigenvalues, descending within the block."""
+    S: np.ndarray
+    S_inv: np.ndarray
+    theta: np.ndarray
+    lambda_iso: float
+    trace: float
+
+    @property
+    def b(self):
+        return self.S.shape[1]
+
+
+def block_factor(A, b, eps=DAMP_EPS):
+    """Step 10: per diagonal block, eigh, damp by lambda_floor, and form the
+    inverse square root and the square root (eigenvalues clamped at 0)."""
+    A = np.asarray(A, dtype=np.float64)
+    d = A.shape[0]
+    if d % b:
+        raise ValueError("d_in % b != 0")
+    t, lam = trace_floor(A, eps)
+    lam = max(lam, LAMBDA_MIN)
+    S = np.zeros((d, b))
+    S_inv = np.zeros((d, b))
+    theta = np.zeros(d)
+    for i in range(d // b):
+        sl = slice(i * b, (i + 1) * b)
+        w, V = np.linalg.eigh(A[sl, sl])
+        w = np.maximum(w, 0.0)
+        S[sl] = (V * (w + lam) ** -0.5) @ V.T
+        S_inv[sl] = (V * (w + lam) ** 0.5) @ V.T
+        theta[sl] = w[::-1]
+    return BlockFactor(S=S, S_inv=S_inv, theta=theta, lambda_iso=lam, trace=t)
+
+
+def block_apply(G, M):
+    """G [:, block i] M_i for every block, M stacked as in BlockFactor."""
+    G = np.asarray(G, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    b = M.shape[1]
+    out = np.empty_like(G)
+    for i in range(G.shape[1] // b):
+        sl = slice(i * b, (i + 1) * b)
+        out[:, sl] = G[:, sl] @ M[sl]
+    return out
+
+
+def block_whiten(G, bf):
+    return block_apply(G, bf.S)
+
+
+def block_unwhiten(W, bf):
+    return block_apply(W, bf.S_inv)
+
+
+def block_roundtrip(G, bf, block128=False):
+    """block-A: whiten -> fl32 -> quantize -> dequantize -> un-whiten.
+    Returns (codes, inv, W32, G^ fp64, flags)."""
+    W32 = block_whiten(G, bf).astype(np.float32)
+    codes, inv, flags = quantize(W32, block128)
+    What = dequantize(codes, inv, block128)
+    return codes, inv, W32, block_unwhiten(What, bf), flags
 
 
 def reduce_payloads(payloads):
