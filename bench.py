@@ -23,7 +23,7 @@ the timed region.  One JSON line on stdout.
     python bench.py --workload stack600m     # 24 blocks at 1536/4096, 16384 tokens
     python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
     python bench.py --study interval [--intervals 10,25,50,100]   # refresh-interval ablation
-    python bench.py --study rank [--rank-list 8,16,32]             # factor-rank sweep
+    python bench.py --study rank [--rank-list 8,16,32,b32,b64]     # rank / block-A sweep
     python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
 """
 
@@ -58,7 +58,8 @@ def parse():
                         "eigendecomposition (host QR for the input bases, no M2 report)")
     p.add_argument("--study", default=None,
                    choices=["staleness", "interval", "rank", "copy", "reduce"])
-    p.add_argument("--rank-list", default="8,16,32", help="factor ranks (rank study)")
+    p.add_argument("--rank-list", default="8,16,32,b32,b64",
+                   help="factor ranks, and bN for block-diagonal N x N blocks (rank study)")
     p.add_argument("--intervals", default="10,25,50,100", help="refresh intervals (interval study)")
     p.add_argument("--ranks", type=int, default=8, help="ranks of the reduce study")
     p.add_argument("--blocks", type=int, default=1)
@@ -669,11 +670,13 @@ def interval_study(args, device="cuda:0"):
 # ---------------------------------------------------------------------------
 
 def rank_study(args, device="cuda:0"):
-    """Round-trip error as a function of the factor's rank (the review chose
-    rank 32 from a round-trip error table over ranks).  On the hidden-1024
-    block (4 inputs, 7 gradients): for each rank r, the grouped refresh keeps
-    the top r Ritz pairs of the same subspace iteration (sketch width 64) and
-    damps with the mean of the d_in - r discarded eigenvalues; then the
+    """Round-trip error as a function of the factor's structure (the review
+    chose rank 32 from a round-trip error table over ranks, with block-A-32
+    and block-A-64 beside them).  On the hidden-1024 block (4 inputs, 7
+    gradients): for each rank r, the grouped refresh keeps the top r Ritz
+    pairs of the same subspace iteration (sketch width 64) and damps with the
+    mean of the d_in - r discarded eigenvalues; an entry "bN" is the
+    block-diagonal factor with N x N blocks, damped by lambda_floor; then the
     grouped per-tensor E4M3 round trip of all 7 gradients.  M1 from the
     device error sums, M2 in the metric of the exact damped sample
     covariance (fp64 eigendecomposition on the device, measurement harness);
@@ -707,12 +710,33 @@ def rank_study(args, device="cuda:0"):
                   for L, l in zip(layers, w.layers))
         return m1, float(np.sqrt(num / den2))
 
+    elems = sum(G.numel() for G in grads)
+
+    def roundtrip_gbps(layers, n=20):
+        """fp32 gradient GB/s of the grouped whiten + quantize and dequantize +
+        un-whiten calls, back to back on the stream (prepared calls)."""
+        cw = fg.GroupCall(fg.OP_WHITEN_QUANTIZE, layers)
+        cd = fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, layers)
+        for _ in range(3):
+            cw()
+            cd()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            cw()
+            cd()
+        e1.record()
+        torch.cuda.synchronize()
+        return 4 * elems / (e0.elapsed_time(e1) / n * 1e-3) / 1e9
+
     eu = [fg.Layer(G) for G in grads]
     fg.gift_euclid_fp8_roundtrip(eu)
     m1_e, m2_e = errors(eu)
     rows = []
-    for r in [int(x) for x in args.rank_list.split(",")]:
-        facs = {s.name: fg.Factor(s.d_in, device=dev, rank=r) for s in w.inputs}
+    for entry in args.rank_list.split(","):
+        blk = int(entry[1:]) if entry.startswith("b") else 0
+        r = 0 if blk else int(entry)
+        facs = {s.name: fg.Factor(s.d_in, device=dev, rank=r or 32, block=blk) for s in w.inputs}
         items = [dict(X=inputs[s.name]["X"], factor=facs[s.name], seed=k)
                  for k, s in enumerate(w.inputs)]
         fg.gift_refresh_factors(items)
@@ -721,9 +745,12 @@ def rank_study(args, device="cuda:0"):
         fg.gift_dequant_unwhiten(gl)
         m1, m2 = errors(gl)
         lam = [float(facs[s.name].coef[fg.COEF_LAMBDA_ISO]) for s in w.inputs]
-        rows.append({"rank": r, "m1": round(m1, 5), "m2": round(m2, 5),
+        gbps = roundtrip_gbps(gl)
+        rows.append({"factor": "block-A-%d" % blk if blk else "rank %d" % r,
+                     "m1": round(m1, 5), "m2": round(m2, 5),
                      "m1_ratio_vs_euclid": round(m1 / m1_e, 4),
                      "m2_reduction_vs_euclid": round(1 - m2 / m2_e, 4),
+                     "roundtrip_GBps": round(gbps, 1),
                      "lambda_iso": [float("%.4g" % x) for x in lam]})
         if not args.quiet:
             print("[rank] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)

@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     OP_UNWHITEN_F32, gift_dequant_accumulate, gift_unwhiten_f32,
     gift_refresh_factor, gift_refresh_workspace_bytes, gift_whiten_quantize,
     gift_dequant_unwhiten, gift_euclid_fp8_roundtrip, gift_roundtrip_error,
-    gift_group_workspace_bytes, gift_draw_sketch, gift_factor_pack_bytes,
+    gift_group_workspace_bytes, gift_draw_sketch, gift_factor_pack_bytes, gift_block_factor_pack_bytes,
     gift_prepare_factor, gift_refresh_factors, gift_refresh_group_workspace_bytes,
     RANK, MAX_SKETCH, BLOCK, DTYPE_F32, DTYPE_BF16, DAMP_FLOOR, DAMP_FLOOR_PLUS_TAIL,
     SCALE_TENSOR, SCALE_BLOCK128, SCALE_MXFP4, MX_BLOCK, FLAG_NONFINITE, FLAG_ZERO_AMAX, EXPORTS,

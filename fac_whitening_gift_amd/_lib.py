@@ -38,7 +38,7 @@ EXPORTS = (
     "gift_group_workspace_bytes", "gift_status_string", "gift_last_error",
     "gift_abi_version", "gift_draw_sketch", "gift_factor_pack_bytes", "gift_prepare_factor",
     "gift_refresh_factors", "gift_refresh_group_workspace_bytes", "gift_build_hash",
-    "gift_dequant_accumulate", "gift_unwhiten_f32",
+    "gift_dequant_accumulate", "gift_unwhiten_f32", "gift_block_factor_pack_bytes",
 )
 
 
@@ -51,7 +51,7 @@ class GiftError(RuntimeError):
 class _Factor(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("U", ctypes.c_void_p), ("theta", ctypes.c_void_p), ("coef", ctypes.c_void_p),
-                ("packs", ctypes.c_void_p)]
+                ("packs", ctypes.c_void_p), ("block", ctypes.c_int32)]
 
 
 class _RefreshInput(ctypes.Structure):
@@ -98,6 +98,7 @@ def load():
         "gift_unwhiten_f32": (I, [LP, I, P, SZ, P]),
         "gift_draw_sketch": (I, [P, I64, I, U64, P]),
         "gift_factor_pack_bytes": (SZ, [I64]),
+        "gift_block_factor_pack_bytes": (SZ, [I64, I]),
         "gift_prepare_factor": (I, [ctypes.POINTER(_Factor), P]),
         "gift_refresh_factors": (I, [ctypes.POINTER(_RefreshInput), I, F, I, I, I, P, SZ, P]),
         "gift_refresh_group_workspace_bytes": (SZ, [ctypes.POINTER(_RefreshInput), I, I]),
@@ -155,7 +156,9 @@ class Factor:
     """Device buffers of one factor: U (d_in x 32), theta (32), coef, and (by
     default, when d_in % 32 == 0) the operand packs of U.  rank (1..32) is
     the effective rank the refresh keeps; the storage stays 32 columns wide,
-    zero from rank on.
+    zero from rank on.  block=32 or 64 makes a block-diagonal factor
+    (block-A-b): U is d_in x 2*block ([S_i | S_i^-1] per block row), theta
+    d_in floats, packs always present.
 
     A factor built from given U / coef values has stale packs until
     gift_prepare_factor(factor) runs; gift_refresh_factor(s) rewrite them.
@@ -163,23 +166,42 @@ class Factor:
     """
 
     def __init__(self, d_in, device="cuda", U=None, theta=None, coef=None, packs=True,
-                 rank=RANK):
+                 rank=RANK, block=0):
         self.d_in = int(d_in)
-        self.rank = int(rank)
+        self.block = int(block)
+        self.rank = 0 if self.block else int(rank)
+        ucols = 2 * self.block if self.block else RANK
+        nth = self.d_in if self.block else RANK
         device = U.device if U is not None else device
-        self.U = U if U is not None else torch.zeros(d_in, RANK, device=device)
-        self.theta = theta if theta is not None else torch.zeros(RANK, device=device)
+        self.U = U if U is not None else torch.zeros(d_in, ucols, device=device)
+        self.theta = theta if theta is not None else torch.zeros(nth, device=device)
         self.coef = coef if coef is not None else torch.zeros(COEF_COUNT, device=device)
-        _dev(self.U, torch.float32, (d_in, RANK), "U")
-        _dev(self.theta, torch.float32, (RANK,), "theta")
+        _dev(self.U, torch.float32, (d_in, ucols), "U")
+        _dev(self.theta, torch.float32, (nth,), "theta")
         _dev(self.coef, torch.float32, (COEF_COUNT,), "coef")
         self.packs = None
-        if packs and self.d_in % 32 == 0:
+        if self.block:
+            nb = int(load().gift_block_factor_pack_bytes(self.d_in, self.block))
+            if nb == 0:
+                raise ValueError("block factor needs block 32 or 64 dividing d_in")
+            self.packs = torch.empty(nb, dtype=torch.uint8, device=self.U.device)
+        elif packs and self.d_in % 32 == 0:
             nb = int(load().gift_factor_pack_bytes(self.d_in))
             self.packs = torch.empty(nb, dtype=torch.uint8, device=self.U.device)
         self._struct = _Factor(self.d_in, self.rank, self.U.data_ptr(), self.theta.data_ptr(),
                                self.coef.data_ptr(),
-                               self.packs.data_ptr() if self.packs is not None else None)
+                               self.packs.data_ptr() if self.packs is not None else None,
+                               self.block)
+
+    @property
+    def S(self):
+        """Block factor: the stacked S_i (d_in x block)."""
+        return self.U[:, :self.block]
+
+    @property
+    def S_inv(self):
+        """Block factor: the stacked S_i^-1 (d_in x block)."""
+        return self.U[:, self.block:]
 
     @property
     def alpha(self):
@@ -392,6 +414,10 @@ def gift_factor_pack_bytes(d_in):
     return int(load().gift_factor_pack_bytes(d_in))
 
 
+def gift_block_factor_pack_bytes(d_in, block):
+    return int(load().gift_block_factor_pack_bytes(d_in, block))
+
+
 def gift_prepare_factor(factor, stream=None):
     """Rewrite factor.packs from factor.U."""
     _check(load().gift_prepare_factor(ctypes.byref(factor._struct), _stream(stream)))
@@ -462,7 +488,7 @@ def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_T
     _check(lib.gift_refresh_factor(_ptr(X), xdt, n_tokens, ctypes.byref(factor._struct),
                                    float(damp_eps), damping_mode, sketch_width, power_steps,
                                    ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(sketch),
-                                   _ptr(A_out), _ptr(ws), ws.numel() * ws.element_size() * ws.element_size(), _stream(stream)))
+                                   _ptr(A_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def gift_draw_sketch(d_in, width=MAX_SKETCH, seed=0, out=None, device="cuda", stream=None):

@@ -18,6 +18,11 @@ hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
 hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStream_t s);
 hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s);
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
+hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s);
+hipError_t launch_blk_whiten(const GroupDev& g, int b, int scaling, bool write_w, hipStream_t s);
+hipError_t launch_blk_dequant(const GroupDev& g, int b, int scaling, hipStream_t s);
+int blk_col_groups(int64_t d_in, int b);
+size_t blk_pack_bytes(int64_t d_in, int b);
 int64_t row_blocks(int64_t d_out);
 int col_groups(int64_t d_in);
 int frag_floats();
@@ -73,6 +78,9 @@ bool whitened(const gift_layer& L, Op op) {
   return L.factor != nullptr && (op == Op::Whiten || op == Op::Dequant || op == Op::UnwhitenF32);
 }
 
+// block size of a layer's factor: 0 for the rank-r factor (or no factor)
+int fblock(const gift_layer& L) { return L.factor ? L.factor->block : 0; }
+
 // Per-layer workspace needs of one grouped op.
 struct LayerWs {
   size_t cbuf = 0, cfin = 0, part = 0, part2 = 0, amax = 0;
@@ -82,7 +90,10 @@ struct LayerWs {
 };
 
 // workgroups of a whitened layer's tile kernels: row blocks x column groups
-int row_tiles(const gift_layer& L) { return (int)(row_blocks(L.d_out) * col_groups(L.d_in)); }
+int row_tiles(const gift_layer& L) {
+  const int b = fblock(L);
+  return (int)(row_blocks(L.d_out) * (b ? blk_col_groups(L.d_in, b) : col_groups(L.d_in)));
+}
 
 LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
   LayerWs w;
@@ -91,7 +102,12 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
   const size_t cop = (size_t)row_blocks(L.d_out) * cop_bytes();
   switch (op) {
     case Op::Whiten:
-      if (L.factor) {
+      if (L.factor && L.factor->block) {
+        if (!block) {  // one amax per tile, the layer amax
+          w.part = (size_t)row_tiles(L) * sizeof(uint32_t);
+          w.amax = sizeof(uint32_t);
+        }
+      } else if (L.factor) {
         w.cbuf = (size_t)col_groups(L.d_in) * frag;  // partial c per column group
         w.cfin = cop;                                  // c' of every row (operand form)
         if (!block) {  // one amax per tile, the layer amax
@@ -111,7 +127,7 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
       break;
     case Op::Dequant:
     case Op::UnwhitenF32:
-      if (L.factor) {
+      if (L.factor && !L.factor->block) {
         w.cbuf = (size_t)col_groups(L.d_in) * frag;
         w.cfin = cop;
       }
@@ -142,7 +158,7 @@ struct Packs {
 Packs plan_packs(const gift_layer* layers, int n, Op op) {
   Packs p;
   for (int i = 0; i < n; ++i) {
-    if (!whitened(layers[i], op) || layers[i].factor->packs) continue;
+    if (!whitened(layers[i], op) || layers[i].factor->packs || layers[i].factor->block) continue;
     const float* u = layers[i].factor->U;
     bool seen = false;
     for (const float* v : p.U) seen |= v == u;
@@ -203,7 +219,24 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
     if (!aligned16(L.G) || !aligned16(L.q) || !aligned16(L.inv_scale) || !aligned16(L.G_hat) ||
         !aligned16(L.W_out))
       return fail(GIFT_ERR_INVALID_ARG, "layer %d: device pointers must be 16-byte aligned", i);
-    if (whitened(L, op)) {
+    if (L.factor && L.factor->block) {
+      const gift_factor& f = *L.factor;
+      if (op == Op::UnwhitenF32)
+        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: block factors are not taken here", i);
+      if (whitened(L, op)) {
+        if (f.block != 32 && f.block != 64)
+          return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor block %d not 32 or 64", i, f.block);
+        if (scaling == GIFT_SCALE_MXFP4)
+          return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: block factors take no MXFP4", i);
+        if (f.d_in != L.d_in)
+          return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor d_in %d != layer d_in %lld", i,
+                      f.d_in, (long long)L.d_in);
+        if (L.d_in % f.block)
+          return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: d_in %% block != 0", i);
+        if (!f.packs || !aligned16(f.packs))
+          return fail(GIFT_ERR_INVALID_ARG, "layer %d: block factor packs NULL or misaligned", i);
+      }
+    } else if (whitened(L, op)) {
       const gift_factor& f = *L.factor;
       if (f.rank < 1 || f.rank > kRank)
         return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor rank %d not in [1, %d]", i, f.rank, kRank);
@@ -275,7 +308,7 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     d.d_out = L.d_out;
     d.d_in = L.d_in;
     d.n_rb = row_blocks(L.d_out);
-    d.ngrp = whitened(L, op) ? col_groups(L.d_in) : 1;
+    d.ngrp = !whitened(L, op) ? 1 : fblock(L) ? blk_col_groups(L.d_in, fblock(L)) : col_groups(L.d_in);
     d.n_tiles = tiles(L);
     d.tile_begin = g.total_tiles;
     g.total_tiles += d.n_tiles;
@@ -348,22 +381,31 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
   hipStream_t st = (hipStream_t)stream;
   s = run_packs(plan_packs(layers, n_layers, Op::Whiten), ws, st);
   if (s != GIFT_OK) return s;
-  for (int wgrp = 0; wgrp < 2; ++wgrp) {
-    const bool white = wgrp == 0;
+  // groups: rank-r factors, Euclidean layers, block factors of 32, of 64
+  for (int wgrp = 0; wgrp < 4; ++wgrp) {
+    auto pick = [&](const gift_layer& L) {
+      return wgrp == 0 ? L.factor != nullptr && !L.factor->block
+           : wgrp == 1 ? L.factor == nullptr
+                       : fblock(L) == (wgrp == 2 ? 32 : 64);
+    };
     bool any_w = false;
     for (int i = 0; i < n_layers; ++i)
-      if ((layers[i].factor != nullptr) == white && layers[i].W_out) any_w = true;
-    auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
+      if (pick(layers[i]) && layers[i].W_out) any_w = true;
     auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L); };
-    if (white)
+    if (wgrp == 0)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
                         return launch_whiten_quantize(g, scaling, any_w, st);
                       });
-    else
+    else if (wgrp == 1)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_flat, [&](const GroupDev& g, int) {
                         return launch_flat_quantize(g, scaling, false, any_w, st);
+                      });
+    else
+      s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
+                      tiles_rows, [&](const GroupDev& g, int) {
+                        return launch_blk_whiten(g, wgrp == 2 ? 32 : 64, scaling, any_w, st);
                       });
     if (s != GIFT_OK) return s;
   }
@@ -380,14 +422,18 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
   hipStream_t st = (hipStream_t)stream;
   s = run_packs(plan_packs(layers, n_layers, Op::Dequant), ws, st);
   if (s != GIFT_OK) return s;
-  for (int wgrp = 0; wgrp < 2; ++wgrp) {
-    const bool white = wgrp == 0;
-    auto pick = [&](const gift_layer& L) { return (L.factor != nullptr) == white; };
-    auto tiles = [&](const gift_layer& L) {
-      return white ? row_tiles(L) : tiles_flat(L);
+  for (int wgrp = 0; wgrp < 4; ++wgrp) {
+    auto pick = [&](const gift_layer& L) {
+      return wgrp == 0 ? L.factor != nullptr && !L.factor->block
+           : wgrp == 1 ? L.factor == nullptr
+                       : fblock(L) == (wgrp == 2 ? 32 : 64);
     };
+    auto tiles = [&](const gift_layer& L) { return wgrp == 1 ? tiles_flat(L) : row_tiles(L); };
     s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles,
-                    [&](const GroupDev& g, int) { return launch_dequant(g, scaling, white, st); });
+                    [&](const GroupDev& g, int) {
+                      if (wgrp >= 2) return launch_blk_dequant(g, wgrp == 2 ? 32 : 64, scaling, st);
+                      return launch_dequant(g, scaling, wgrp == 0, st);
+                    });
     if (s != GIFT_OK) return s;
   }
   return GIFT_OK;
@@ -469,10 +515,28 @@ gift_status gift_refresh_factor(const void* X, int x_dtype, int64_t n_tokens,
 
 size_t gift_factor_pack_bytes(int64_t d_in) { return d_in > 0 ? pack_bytes(d_in) : 0; }
 
+size_t gift_block_factor_pack_bytes(int64_t d_in, int block) {
+  if ((block != 32 && block != 64) || d_in < block || d_in % block) return 0;
+  return blk_pack_bytes(d_in, block);
+}
+
 gift_status gift_prepare_factor(const gift_factor* f, void* stream) {
   if (!f || !f->U || !f->packs) return fail(GIFT_ERR_INVALID_ARG, "factor, U or packs is NULL");
   if (!aligned16(f->U) || !aligned16(f->packs))
     return fail(GIFT_ERR_INVALID_ARG, "U / packs must be 16-byte aligned");
+  if (f->block) {
+    if ((f->block != 32 && f->block != 64) || f->d_in < f->block || f->d_in % f->block ||
+        f->d_in > kMaxDim)
+      return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "block must be 32 or 64 and divide d_in");
+    PackGroup pg{};
+    pg.n = 1;
+    pg.f[0].U = f->U;
+    pg.f[0].P = static_cast<uint4*>(f->packs);
+    pg.f[0].d_in = f->d_in;
+    hipError_t e = launch_blk_pack(pg, f->block, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+    return GIFT_OK;
+  }
   if (f->rank < 1 || f->rank > kRank) return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be in [1, 32]");
   if (f->d_in < 64 || f->d_in % 32 || f->d_in > kMaxDim)
     return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "d_in must be >= 64 and a multiple of 32");

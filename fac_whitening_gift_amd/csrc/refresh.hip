@@ -31,6 +31,7 @@
 namespace gift {
 
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
+hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s);
 size_t pack_bytes(int64_t d_in);
 
 namespace {
@@ -865,41 +866,17 @@ __global__ __launch_bounds__(kT) void k_apply(RGroup g, int which) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// 5. Rayleigh-Ritz: cyclic Jacobi eigensolver of B = Q^T A Q (Golub & Van
-// Loan, sym.schur2 rotations, round-robin ordering: W/2 disjoint rotations
-// per round), sort, coefficients.  In a round every 2 x 2 block of B is
-// rotated on both sides by one thread, and the pair of columns of V by
-// others, so a round takes two barriers.  grid: (inputs)
-// ---------------------------------------------------------------------------
+// Cyclic Jacobi on the symmetric W x W matrix B in LDS (Golub & Van Loan,
+// sym.schur2 rotations, round-robin ordering: W/2 disjoint rotations per
+// round); V accumulates the rotations.  On return B is diagonal to the
+// sweep tolerance.  In a round every 2 x 2 block of B is rotated on both
+// sides by one thread, and the pair of columns of V by others, so a round
+// takes two barriers.  All kST threads call it.
 template <int W>
-__global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
+__device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, double* rs, int* rp,
+                       int* rq, double* red) {
   constexpr int kP = W / 2;   // rotations per round
   constexpr int kM = W - 1;   // rounds per sweep
-  const RIn& Rin = g.r[blockIdx.x];
-  const int d = Rin.d;
-  __shared__ double B[W][W + 1];
-  __shared__ double V[W][W + 1];
-  __shared__ double rc[kP], rs[kP];
-  __shared__ int rp[kP], rq[kP];
-  __shared__ double ev[W];
-  __shared__ int order[W];
-  __shared__ double red[kST / 64];
-  gram_reduce<W>(Rin.gram, B);
-  for (int e = threadIdx.x; e < W * W; e += kST) {
-    const int a = e / W, b = e % W;
-    V[a][b] = a == b ? 1.0 : 0.0;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < W * W; e += kST) {
-    const int a = e / W, b = e % W;
-    if (a < b) {
-      const double m = 0.5 * (B[a][b] + B[b][a]);
-      B[a][b] = m;
-      B[b][a] = m;
-    }
-  }
-  __syncthreads();
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
     double off = 0.0, tot = 0.0;
     for (int e = threadIdx.x; e < W * W; e += kST) {
@@ -954,6 +931,40 @@ __global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
       __syncthreads();
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// 5. Rayleigh-Ritz: the Jacobi eigensolver on B = Q^T A Q, sort,
+// coefficients.  grid: (inputs)
+// ---------------------------------------------------------------------------
+template <int W>
+__global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
+  constexpr int kP = W / 2;   // rotations per round
+  const RIn& Rin = g.r[blockIdx.x];
+  const int d = Rin.d;
+  __shared__ double B[W][W + 1];
+  __shared__ double V[W][W + 1];
+  __shared__ double rc[kP], rs[kP];
+  __shared__ int rp[kP], rq[kP];
+  __shared__ double ev[W];
+  __shared__ int order[W];
+  __shared__ double red[kST / 64];
+  gram_reduce<W>(Rin.gram, B);
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
+    V[a][b] = a == b ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
+    if (a < b) {
+      const double m = 0.5 * (B[a][b] + B[b][a]);
+      B[a][b] = m;
+      B[b][a] = m;
+    }
+  }
+  __syncthreads();
+  jacobi<W>(B, V, rc, rs, rp, rq, red);
   // sort eigenvalues descending (rank by count; ties by index)
   if (threadIdx.x < W) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
   __syncthreads();
@@ -998,6 +1009,80 @@ __global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
     Rin.coef[GIFT_COEF_DW + k] = (float)(-th / (s * s0 * (s + s0)));
     Rin.coef[GIFT_COEF_DU + k] = (float)(th / (s + s0));
     Rin.theta[k] = (float)th;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 6. Block-diagonal factor (block-A-W, W = 32 or 64): for diagonal block i
+// of A, the Jacobi eigensolver, then S_i = V (theta + lambda)^-1/2 V^T and
+// S_i^-1 = V (theta + lambda)^1/2 V^T with lambda = lambda_floor (a block
+// keeps its whole spectrum) and theta clamped at 0.  U is d x 2W: row
+// W i + a holds row a of S_i, then row a of S_i^-1; theta holds each
+// block's eigenvalues, descending.  grid: (max d / W, inputs)
+// ---------------------------------------------------------------------------
+template <int W>
+__global__ __launch_bounds__(kST) void k_blk_eig(RGroup g) {
+  constexpr int kP = W / 2;
+  const RIn& Rin = g.r[blockIdx.y];
+  const int d = Rin.d, i0 = blockIdx.x * W;
+  if (i0 >= d) return;
+  __shared__ double B[W][W + 1];
+  __shared__ double V[W][W + 1];
+  __shared__ double rc[kP], rs[kP];
+  __shared__ int rp[kP], rq[kP];
+  __shared__ double ev[W], fw[W], fu[W];
+  __shared__ int order[W];
+  __shared__ double red[kST / 64];
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
+    B[a][b] = (double)Rin.A[(int64_t)(i0 + a) * d + i0 + b];
+    V[a][b] = a == b ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
+    if (a < b) {
+      const double m = 0.5 * (B[a][b] + B[b][a]);
+      B[a][b] = m;
+      B[b][a] = m;
+    }
+  }
+  __syncthreads();
+  jacobi<W>(B, V, rc, rs, rp, rq, red);
+  if (threadIdx.x < W) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
+  __syncthreads();
+  const double t = *Rin.tr;
+  const double lam_floor = (double)g.eps * t / d;
+  const double lam = fmax(lam_floor, 1e-30);
+  if (threadIdx.x < W) {
+    const int k = threadIdx.x;
+    const double x = ev[k];
+    int rank = 0;
+    for (int j = 0; j < W; ++j) rank += (ev[j] > x) || (ev[j] == x && j < k);
+    order[rank] = k;
+    const double th = fmax(x, 0.0);
+    fw[k] = 1.0 / sqrt(th + lam);
+    fu[k] = sqrt(th + lam);
+  }
+  __syncthreads();
+  if (threadIdx.x < W) Rin.theta[i0 + threadIdx.x] = (float)fmax(ev[order[threadIdx.x]], 0.0);
+  for (int e = threadIdx.x; e < W * W; e += kST) {
+    const int a = e / W, b = e % W;
+    double sw = 0.0, su = 0.0;
+    for (int k = 0; k < W; ++k) {
+      const double vv = V[a][k] * V[b][k];
+      sw += vv * fw[k];
+      su += vv * fu[k];
+    }
+    Rin.U[(int64_t)(i0 + a) * 2 * W + b] = (float)sw;
+    Rin.U[(int64_t)(i0 + a) * 2 * W + W + b] = (float)su;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    float* coef = Rin.coef;
+    for (int k = 0; k < GIFT_COEF_COUNT; ++k) coef[k] = 0.f;
+    coef[GIFT_COEF_LAMBDA_ISO] = (float)lam;
+    coef[GIFT_COEF_LAMBDA_FLOOR] = (float)lam_floor;
+    coef[GIFT_COEF_TRACE] = (float)t;
   }
 }
 
@@ -1081,7 +1166,13 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       return bad(GIFT_ERR_INVALID_ARG, at + "device pointers must be 16-byte aligned");
     if (r.x_dtype != GIFT_DTYPE_F32 && r.x_dtype != GIFT_DTYPE_BF16)
       return bad(GIFT_ERR_INVALID_ARG, at + "unknown x_dtype");
-    if (f->rank < 1 || f->rank > kRank)
+    if (f->block != in[0].factor->block)
+      return bad(GIFT_ERR_INVALID_ARG, at + "the inputs of one call must share the factor kind");
+    if (f->block != 0 && f->block != 32 && f->block != 64)
+      return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "block must be 0, 32 or 64");
+    if (f->block && (f->d_in % f->block || !f->packs))
+      return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "a block factor needs d_in % block == 0 and packs");
+    if (!f->block && (f->rank < 1 || f->rank > kRank))
       return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "rank must be in [1, 32]");
     if (f->d_in < 64 || f->d_in % 16 || f->d_in > 16384)
       return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "d_in must be in [64, 16384], % 16 == 0");
@@ -1155,6 +1246,22 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     }
     k_syrk_reduce<<<dim3(maxpairs, nb), kT, 0, st>>>(g);
     k_trace<<<nb, kT, 0, st>>>(g);
+    const int kind = in[b0].factor->block;
+    if (kind) {  // block-diagonal factors: per-block eigensolve and packs
+      if (kind == 32) k_blk_eig<32><<<dim3((unsigned)(maxd / 32), nb), kST, 0, st>>>(g);
+      else k_blk_eig<64><<<dim3((unsigned)(maxd / 64), nb), kST, 0, st>>>(g);
+      PackGroup pg{};
+      for (int i = 0; i < nb; ++i) {
+        pg.f[i].U = in[b0 + i].factor->U;
+        pg.f[i].P = static_cast<uint4*>(in[b0 + i].factor->packs);
+        pg.f[i].d_in = in[b0 + i].factor->d_in;
+      }
+      pg.n = nb;
+      hipError_t e = launch_blk_pack(pg, kind, st);
+      if (e == hipSuccess) e = hipGetLastError();
+      if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+      continue;
+    }
     k_sketch<<<dim3((unsigned)(((int64_t)maxd * width / 4 + kT) / kT), nb), kT, 0, st>>>(g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));

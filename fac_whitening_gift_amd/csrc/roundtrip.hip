@@ -720,6 +720,257 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
 }
 
 // ---------------------------------------------------------------------------
+// block-diagonal factor (block-A-b, b = 32 or 64): W[:, block i] =
+// G[:, block i] S_i and G^[:, block i] = W^[:, block i] S_i^-1 on MFMA with
+// the bf16x3 split.  A wave owns one block (b/32 chunks) of the tile's 64
+// rows, so the tile kernels' geometry holds with b/32 chunks per wave.  The
+// G values a lane loads (load_gc: K-permuted) are the B operand as they
+// are; the operand packs hold, for M = S (m = 0) or S^-1 (m = 1), output
+// chunk oc and K chunk kc of block i, element e of lane l (r16 = l % 16,
+// g = l / 16) = M_i[32 kc + perm(e)][32 oc + 16 h + r16] at uint4 index
+// (((((m nblk + i) kb + oc) kb + kc) 2 + h) 3 + split) 64 + l, kb = b / 32.
+// U of a block factor is d_in x 2b: row b i + a = [row a of S_i, row a of S_i^-1].
+// ---------------------------------------------------------------------------
+size_t blk_pack_bytes(int64_t d_in, int b) {
+  const int64_t kb = b / kChunk;
+  return (size_t)(2 * (d_in / b) * kb * kb * 2 * 3 * 64) * sizeof(uint4);
+}
+
+__global__ __launch_bounds__(kThreads) void k_pack_blk(PackGroup pg, int b) {
+  const PackDev& F = pg.f[blockIdx.y];
+  const int kb = b / kChunk;
+  const int64_t nblk = F.d_in / b;
+  const int64_t lanes = 2 * nblk * kb * kb * 2 * 64;
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= lanes) return;
+  const int lane = (int)(e & 63);
+  const int64_t q = e >> 6;  // (((m nblk + i) kb + oc) kb + kc) 2 + h
+  int64_t r = q;
+  const int h = (int)(r & 1);
+  r >>= 1;
+  const int kc = (int)(r % kb);
+  r /= kb;
+  const int oc = (int)(r % kb);
+  r /= kb;
+  const int64_t i = r % nblk;
+  const int m = (int)(r / nblk);
+  const int r16 = lane & 15, g = lane >> 4;
+  float v[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t row = b * i + kChunk * kc + perm8(t, g);
+    v[t] = F.U[row * 2 * b + m * b + kChunk * oc + 16 * h + r16];
+  }
+  bf16x8 sp[3];
+  split3(v, sp);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) F.P[(size_t)(q * 3 + t) * 64 + lane] = __builtin_bit_cast(uint4, sp[t]);
+}
+
+template <int kb>
+__device__ __forceinline__ void load_blk_packs(const uint4* P, int64_t nblk, int m, int64_t blk,
+                                               int oc, int lane, uint4 (&a)[kb][2][3]) {
+#pragma unroll
+  for (int kc = 0; kc < kb; ++kc)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        a[kc][h][t] = P[(size_t)((((((m * nblk + blk) * kb + oc) * kb + kc) * 2 + h) * 3 + t) * 64) + lane];
+}
+
+// one output chunk of one 16-row tile: sum over the block's K chunks of
+// (M packs) x (G chunk split three ways)
+template <int kb>
+__device__ __forceinline__ void blk_product(const uint4 (&pa)[kb][2][3], const float4 (*gv)[2],
+                                            f32x4 (&out)[2]) {
+  out[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  out[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < kb; ++kc) {
+    bf16x8 a[2][3];
+    as_ops(pa[kc], a);
+    const float v[8] = {gv[kc][0].x, gv[kc][0].y, gv[kc][0].z, gv[kc][0].w,
+                        gv[kc][1].x, gv[kc][1].y, gv[kc][1].z, gv[kc][1].w};
+    bf16x8 sp[3];
+    split3(v, sp);
+    const bf16x8(*pa2[2])[3] = {&a[0], &a[1]};
+    const bf16x8(*pb2[2])[3] = {&sp, &sp};
+    mfma3x3_n<2>(pa2, pb2, out);
+  }
+}
+
+// kMode 0: per-tensor amax pass (tile partial to L.part); 1: per-tensor
+// quantize pass; 2: 1x128 block scaling (codes and segment scales)
+template <int kB, int kMode, bool kWriteW>
+__global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
+  constexpr int kb = kB / kChunk;
+  constexpr int kWPS = 4 / kb;  // waves per 128-column segment
+  const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
+  const int tile = blockIdx.x - L.tile_begin;
+  const Tile x = tile_ctx<kb>(L, tile);
+  __shared__ uint32_t mx[kMode == 2 ? kTW * kTR * 64 : kTW];
+  const int64_t nblk = L.d_in / kB, blk = x.c0 / kb;
+  float4 w[kb][kTR][2];
+  if (x.nmine) {  // wave-uniform: a wave has a whole block or nothing
+    float4 gv[kTR][kb][2];
+    uint4 pa[kb][2][3];
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt)
+#pragma unroll
+      for (int kc = 0; kc < kb; ++kc) load_gc(L, x.row[rt], x.g, x.c0 + kc, gv[rt][kc]);
+    load_blk_packs<kb>(L.P, nblk, 0, blk, 0, x.lane, pa);
+#pragma unroll
+    for (int oc = 0; oc < kb; ++oc) {
+      if (oc) load_blk_packs<kb>(L.P, nblk, 0, blk, oc, x.lane, pa);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        f32x4 out[2];
+        blk_product<kb>(pa, gv[rt], out);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) w[oc][rt][t] = make_float4(out[t][0], out[t][1], out[t][2], out[t][3]);
+      }
+    }
+  }
+  if constexpr (kMode == 0) {
+    uint32_t m = 0u;
+    if (x.nmine)
+#pragma unroll
+      for (int oc = 0; oc < kb; ++oc)
+#pragma unroll
+        for (int rt = 0; rt < kTR; ++rt)
+          if (x.ok[rt]) m = amax4(amax4(m, w[oc][rt][0]), w[oc][rt][1]);
+    m = block_max_u32<kTileThreads>(m, mx);
+    if (threadIdx.x == 0) L.part[tile] = m;
+  } else if constexpr (kMode == 1) {
+    uint32_t m = 0u;
+    if (L.n_tiles > kPartialLimit) {
+      m = *L.amax;
+    } else {
+      for (int i = threadIdx.x; i < L.n_tiles; i += kTileThreads) m = max(m, L.part[i]);
+      m = block_max_u32<kTileThreads>(m, mx);
+    }
+    const Scale sc = scale_from_amax_bits(m);
+    if (tile == 0 && threadIdx.x == 0) {
+      L.inv[0] = sc.inv;
+      if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
+    }
+    if (x.nmine == 0) return;  // wave-uniform; no barrier below
+    const bool nonfinite = (sc.flags & GIFT_FLAG_NONFINITE) != 0;
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) {
+      if (!x.ok[rt]) continue;
+#pragma unroll
+      for (int oc = 0; oc < kb; ++oc)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int64_t o = (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) + 16 * t + 4 * x.g;
+          *reinterpret_cast<uint32_t*>(L.q + o) = e4m3_encode4_scaled(w[oc][rt][t], sc.scale, nonfinite);
+          if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = w[oc][rt][t];
+        }
+    }
+  } else {
+    // per-segment amax: lane max over its chunks, then over the lanes of the
+    // same row (xor 16, 32), then over the segment's waves through LDS
+    uint32_t (*sm)[kTR][64] = reinterpret_cast<uint32_t (*)[kTR][64]>(mx);
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) {
+      uint32_t m = 0u;
+      if (x.nmine)
+#pragma unroll
+        for (int oc = 0; oc < kb; ++oc) m = amax4(amax4(m, w[oc][rt][0]), w[oc][rt][1]);
+      m = max(m, (uint32_t)__shfl_xor(m, 16, 64));
+      m = max(m, (uint32_t)__shfl_xor(m, 32, 64));
+      sm[x.wave][rt][x.lane] = m;
+    }
+    __syncthreads();
+    if (x.nmine == 0) return;  // wave-uniform; no barrier below
+    const int w0 = x.wave - x.wave % kWPS;
+    const int seg = x.c0 / 4;
+    const int64_t nseg = L.d_in / kBlock;
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int v = 0; v < kWPS; ++v) m = max(m, sm[w0 + v][rt][x.lane]);
+      const Scale sc = scale_from_amax_bits(m);
+      if (!x.ok[rt]) continue;
+      if (x.g == 0 && x.wave == w0) {
+        L.inv[x.row[rt] * nseg + seg] = sc.inv;
+        if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
+      }
+#pragma unroll
+      for (int oc = 0; oc < kb; ++oc)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int64_t o = (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) + 16 * t + 4 * x.g;
+          *reinterpret_cast<uint32_t*>(L.q + o) =
+              e4m3_encode4_scaled(w[oc][rt][t], sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
+          if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = w[oc][rt][t];
+        }
+    }
+  }
+}
+
+// G^[:, block] = inv * (decode(q)[:, block] S^-1): codes are exact in bf16,
+// so the product takes the three splits of S^-1 only; the scale (per tensor,
+// or the 128-column segment's, which holds the whole block) comes after.
+template <int kB, bool kB128>
+__global__ __launch_bounds__(kTileThreads) void k_blk_dequant(GroupDev gd) {
+  constexpr int kb = kB / kChunk;
+  const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
+  const int tile = blockIdx.x - L.tile_begin;
+  const Tile x = tile_ctx<kb>(L, tile);
+  if (x.nmine == 0) return;  // wave-uniform; the kernel has no barrier
+  const int64_t nblk = L.d_in / kB, blk = x.c0 / kb;
+  uint32_t qv[kTR][kb][2];
+  uint4 pa[kb][2][3];
+  float inv[kTR];
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt) {
+#pragma unroll
+    for (int kc = 0; kc < kb; ++kc) load_qc(L, x.row[rt], x.g, x.c0 + kc, qv[rt][kc]);
+    inv[rt] = kB128 ? L.inv[(int64_t)x.row[rt] * (L.d_in / kBlock) + x.c0 / 4] : L.inv[0];
+  }
+  load_blk_packs<kb>(L.P, nblk, 1, blk, 0, x.lane, pa);
+  float4 gh[kb][kTR][2];
+#pragma unroll
+  for (int oc = 0; oc < kb; ++oc) {
+    if (oc) load_blk_packs<kb>(L.P, nblk, 1, blk, oc, x.lane, pa);
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) {
+      f32x4 out[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kc = 0; kc < kb; ++kc) {
+        bf16x8 a[2][3];
+        as_ops(pa[kc], a);
+        float v[8];
+        decode8(qv[rt][kc][0], qv[rt][kc][1], v);
+        bf16x8 bq;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bq[t] = (__bf16)v[t];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) out[h] = mfma3x1(a[h], bq, out[h]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        gh[oc][rt][t] = make_float4(inv[rt] * out[t][0], inv[rt] * out[t][1], inv[rt] * out[t][2],
+                                    inv[rt] * out[t][3]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt) {
+    if (!x.ok[rt]) continue;
+#pragma unroll
+    for (int oc = 0; oc < kb; ++oc)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<float4*>(L.Ghat + (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) +
+                                   16 * t + 4 * x.g) = gh[oc][rt][t];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dequantize + un-whiten, pass 2: G^ = beta W^ + c'^ U^T with
 // W^ = decode(q) * inv and c'^ the row block's (W^ U) * D_u.
 // ---------------------------------------------------------------------------
@@ -1103,6 +1354,48 @@ hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_
     else if (scaling == GIFT_SCALE_MXFP4) k_flat_dequant<GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
     else k_flat_dequant<GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s) {
+  int64_t maxl = 0;
+  for (int i = 0; i < pg.n; ++i) {
+    const int64_t kb = b / kChunk, l = 2 * (pg.f[i].d_in / b) * kb * kb * 2 * 64;
+    maxl = l > maxl ? l : maxl;
+  }
+  k_pack_blk<<<dim3((unsigned)((maxl + kThreads - 1) / kThreads), pg.n), dim3(kThreads), 0, s>>>(pg, b);
+  return hipGetLastError();
+}
+
+int blk_col_groups(int64_t d_in, int b) {
+  const int64_t per = (int64_t)kTW * (b / kChunk);  // chunks per workgroup
+  return (int)((d_in / kChunk + per - 1) / per);
+}
+
+// block-diagonal factors of block size b (32 or 64); scaling: per tensor or 1x128
+hipError_t launch_blk_whiten(const GroupDev& g, int b, int scaling, bool write_w, hipStream_t s) {
+  const dim3 grid(g.total_tiles), blk(kTileThreads);
+#define GIFT_BW(B, M, W) k_blk_whiten<B, M, W><<<grid, blk, 0, s>>>(g)
+  if (scaling == GIFT_SCALE_BLOCK128) {
+    if (b == 32) { if (write_w) GIFT_BW(32, 2, true); else GIFT_BW(32, 2, false); }
+    else { if (write_w) GIFT_BW(64, 2, true); else GIFT_BW(64, 2, false); }
+    return hipGetLastError();
+  }
+  if (b == 32) GIFT_BW(32, 0, false); else GIFT_BW(64, 0, false);
+  bool tall = false;
+  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_tiles > kPartialLimit;
+  if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
+  if (b == 32) { if (write_w) GIFT_BW(32, 1, true); else GIFT_BW(32, 1, false); }
+  else { if (write_w) GIFT_BW(64, 1, true); else GIFT_BW(64, 1, false); }
+#undef GIFT_BW
+  return hipGetLastError();
+}
+
+hipError_t launch_blk_dequant(const GroupDev& g, int b, int scaling, hipStream_t s) {
+  const dim3 grid(g.total_tiles), blk(kTileThreads);
+  const bool b128 = scaling == GIFT_SCALE_BLOCK128;
+  if (b == 32) { if (b128) k_blk_dequant<32, true><<<grid, blk, 0, s>>>(g); else k_blk_dequant<32, false><<<grid, blk, 0, s>>>(g); }
+  else { if (b128) k_blk_dequant<64, true><<<grid, blk, 0, s>>>(g); else k_blk_dequant<64, false><<<grid, blk, 0, s>>>(g); }
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GIFT_ABI_VERSION 2
+#define GIFT_ABI_VERSION 3
 
 /* Rank of the factor (GIFT review, free-parameter ledger: rank 32). */
 #define GIFT_RANK 32
@@ -121,6 +121,22 @@ enum {
  * of U and the entries of theta, D_w and D_u from r on are zero, so every
  * kernel works on 32 columns and the zero ones add exact zeros.
  * Written by gift_refresh_factor; a caller may also fill it itself.
+ *
+ * block = 32 or 64 makes it a block-diagonal factor instead ("block-A-b",
+ * named in the review's round-trip error table; reading: A is replaced by
+ * its d_in/b diagonal b x b blocks A_i, each damped by lambda_floor and
+ * used in full): W[:, block i] = G[:, block i] S_i with
+ * S_i = (A_i + lambda_floor I)^-1/2, and G^[:, block i] = W^[:, block i]
+ * (A_i + lambda_floor I)^1/2.  Then
+ *   U     is d_in x 2b: row b i + a holds row a of S_i, then row a of S_i^-1;
+ *   theta is d_in floats: each block's eigenvalues, descending, >= 0;
+ *   coef  holds LAMBDA_ISO (= lambda_floor), LAMBDA_FLOOR and TRACE, the
+ *         rest 0;
+ *   packs is required: gift_block_factor_pack_bytes(d_in, b) bytes, S and
+ *         S^-1 in the kernels' operand layout;
+ *   rank  is not used.
+ * d_in % b == 0.  Block factors take per-tensor and 1x128 scaling (not
+ * MXFP4) and are not taken by gift_unwhiten_f32.
  */
 typedef struct gift_factor {
     int32_t d_in;     /* rows of U; 64 <= d_in, % 16 == 0 (% 32 to whiten)    */
@@ -135,10 +151,16 @@ typedef struct gift_factor {
                          and gift_prepare_factor; it must be rewritten after
                          U changes.  NULL: every grouped call re-packs U into
                          its workspace.                                     */
+    int32_t block;    /* 0: the rank-r factor; 32 or 64: block-diagonal
+                         factor of that block size (see above)                 */
 } gift_factor;
 
 /* Size of gift_factor.packs for a factor with d_in rows (d_in % 32 == 0). */
 size_t gift_factor_pack_bytes(int64_t d_in);
+
+/* Size of gift_factor.packs for a block-diagonal factor (block 32 or 64,
+ * d_in % block == 0); 0 for other arguments. */
+size_t gift_block_factor_pack_bytes(int64_t d_in, int block);
 
 /* Rewrite f->packs from f->U (for callers that fill U themselves). */
 gift_status gift_prepare_factor(const gift_factor *f, void *stream);

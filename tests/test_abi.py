@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fg.EXPORTS)
-    assert lib.gift_abi_version() == 2
+    assert lib.gift_abi_version() == 3
 
 
 def test_status_strings():
@@ -139,3 +139,23 @@ def test_refresh_validation():
     assert lib.gift_factor_pack_bytes(1024) == 1024 * 384
     assert lib.gift_prepare_factor(None, None) == 1
     assert lib.gift_draw_sketch(None, 10, 64, 0, None) == 1
+
+
+def test_block_factor_validation():
+    """block-A factors: sizes of the packs, and the argument errors that come
+    back before any launch."""
+    lib = _lib.load()
+    assert lib.gift_block_factor_pack_bytes(1024, 32) == 1024 * 384
+    assert lib.gift_block_factor_pack_bytes(1024, 64) == 1024 * 768
+    assert lib.gift_block_factor_pack_bytes(100, 32) == 0
+    assert lib.gift_block_factor_pack_bytes(1024, 48) == 0
+    ok = dict(U=0x20000, theta=0x30000, coef=0x40000, packs=0x50000)
+
+    def fac(d_in, block, packs=0x50000):
+        f = _lib._Factor(d_in, 0, ok["U"], ok["theta"], ok["coef"], packs, block)
+        return ctypes.pointer(f)
+    assert _call_whiten([_layer(d_in=128, factor=fac(128, 48))]) == 2          # block size
+    assert _call_whiten([_layer(d_in=96, factor=fac(96, 64))]) == 2            # d_in % block
+    assert _call_whiten([_layer(d_in=128, factor=fac(128, 32, None))]) == 1    # packs required
+    assert _call_whiten([_layer(d_in=128, factor=fac(128, 32))], scaling=2) == 2   # no MXFP4
+    assert _call_whiten([_layer(d_in=256, factor=fac(128, 32))]) == 1          # d_in mismatch
