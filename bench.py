@@ -24,6 +24,7 @@ the timed region.  One JSON line on stdout.
     python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
     python bench.py --study interval [--intervals 10,25,50,100]   # refresh-interval ablation
     python bench.py --study rank [--rank-list 8,16,32,b32,b64]     # rank / block-A sweep
+    python bench.py --study reference     # full-rank, Cholesky-form and two-sided references
     python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
 """
 
@@ -57,7 +58,9 @@ def parse():
                    help="for runs under hardware-counter collection: no device QR or "
                         "eigendecomposition (host QR for the input bases, no M2 report)")
     p.add_argument("--study", default=None,
-                   choices=["staleness", "interval", "rank", "copy", "reduce"])
+                   choices=["staleness", "interval", "rank", "reference", "copy", "reduce"])
+    p.add_argument("--ref-shape", default="1024,2816,8192",
+                   help="hidden,mlp,tokens of the block of the reference study")
     p.add_argument("--rank-list", default="8,16,32,b32,b64",
                    help="factor ranks, and bN for block-diagonal N x N blocks (rank study)")
     p.add_argument("--intervals", default="10,25,50,100", help="refresh intervals (interval study)")
@@ -152,6 +155,9 @@ def main():
         return
     if args.study == "rank":
         print(json.dumps(rank_study(args)), flush=True)
+        return
+    if args.study == "reference":
+        print(json.dumps(reference_study(args)), flush=True)
         return
     if args.study == "copy":
         print(json.dumps(copy_calibration()), flush=True)
@@ -757,6 +763,95 @@ def rank_study(args, device="cuda:0"):
     return {"study": "rank", "workload": w.name, "scaling": "per-tensor E4M3",
             "damping": "floor+tail", "euclid": {"m1": round(m1_e, 5), "m2": round(m2_e, 5)},
             "rows": rows}
+
+
+# ---------------------------------------------------------------------------
+# full-rank and two-sided references
+# ---------------------------------------------------------------------------
+
+def reference_study(args, device="cuda:0"):
+    """Where the rank-32 input-side factor stands against the transforms it
+    simplifies (the review: the input-side factor alone matches the full
+    two-sided K-FAC transform almost exactly; its Eq. 14 Cholesky form).
+    On a Llama-style block (default hidden 1024, MLP 2816, 8192 tokens), per
+    gradient: Euclidean FP8; GIFT with the rank-32 factor (the library's
+    path end to end); full-rank input-side W = G (A + lam I)^-1/2; its
+    Cholesky form W = G L^-T (L L^T = A + lam I); two-sided
+    W = (B + mu I)^-1/2 G (A + lam I)^-1/2 with the output-side factor read as
+    B = G G^T / d_in.  The reference transforms and their inverses are fp64
+    torch on the device (measurement harness, from the exact sample A); the
+    whitened tensors are quantized by the library's per-tensor E4M3 kernels.
+    M1 and M2 (input-side K-FAC metric) summed over the block's gradients."""
+    import numpy as np
+    import torch
+
+    import synth
+    import fac_whitening_gift_amd as fg
+
+    dev = torch.device(device)
+    h, m, n = (int(x) for x in args.ref_shape.split(","))
+    w = synth.llama_block(hidden=h, mlp=m, tokens=n, exponent=1.5)
+    inputs = {s.name: synth.draw_input(s, seed=1000 + k, device=dev, as_bf16=True)
+              for k, s in enumerate(w.inputs)}
+    facs = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
+    fg.gift_refresh_factors([dict(X=inputs[s.name]["X"], factor=facs[s.name], seed=k)
+                             for k, s in enumerate(w.inputs)])
+
+    def sym_pair(M):
+        lam = 1e-3 * torch.trace(M) / M.shape[0]
+        ev_, V = torch.linalg.eigh(M + lam * torch.eye(M.shape[0], dtype=M.dtype, device=dev))
+        ev_ = ev_.clamp_min(0)
+        return (V * ev_.rsqrt()) @ V.T, (V * ev_.sqrt()) @ V.T
+
+    methods = ["euclid", "gift_rank32", "input_full", "input_cholesky", "two_sided"]
+    num1 = {k: 0.0 for k in methods}
+    num2 = {k: 0.0 for k in methods}
+    den1 = den2 = 0.0
+    cache = {}
+    for i, l in enumerate(w.layers):
+        inp = inputs[l.input]
+        if l.input not in cache:
+            X = inp["X"].double()
+            A = X.T @ X / X.shape[0]
+            S, Si = sym_pair(A)
+            lam = 1e-3 * torch.trace(A) / A.shape[0]
+            L = torch.linalg.cholesky(A + lam * torch.eye(A.shape[0], dtype=A.dtype, device=dev))
+            Linv = torch.linalg.solve_triangular(L, torch.eye(A.shape[0], dtype=A.dtype, device=dev),
+                                                 upper=False)
+            cache[l.input] = (S, Si, Linv.T.contiguous(), L.T.contiguous())
+        S, Si, Lt_inv, Lt = cache[l.input]
+        G = synth.draw_gradient(l.d_out, inp["Q"], inp["ev"], seed=5000 + i, device=dev)
+        G64 = G.double()
+        SB, SBi = sym_pair(G64 @ G64.T / G64.shape[1])
+        outs = {}
+        eu = fg.Layer(G)
+        fg.gift_euclid_fp8_roundtrip([eu])
+        outs["euclid"] = eu.G_hat.double()
+        gl = fg.Layer(G, factor=facs[l.input])
+        fg.gift_whiten_quantize([gl])
+        fg.gift_dequant_unwhiten([gl])
+        outs["gift_rank32"] = gl.G_hat.double()
+        for name, (lt, rt, lti, rti) in (("input_full", (None, S, None, Si)),
+                                          ("input_cholesky", (None, Lt_inv, None, Lt)),
+                                          ("two_sided", (SB, S, SBi, Si))):
+            W = G64 if lt is None else lt @ G64
+            W32 = (W @ rt).float().contiguous()
+            q = fg.Layer(W32)
+            fg.gift_euclid_fp8_roundtrip([q])
+            Wh = q.G_hat.double()
+            outs[name] = (Wh if lti is None else lti @ Wh) @ rti
+        for k in methods:
+            E = outs[k] - G64
+            num1[k] += float(E.pow(2).sum())
+            num2[k] += float((E @ S).pow(2).sum())
+        den1 += float(G64.pow(2).sum())
+        den2 += float((G64 @ S).pow(2).sum())
+    rows = {k: {"m1": round(float(np.sqrt(num1[k] / den1)), 5),
+                "m2": round(float(np.sqrt(num2[k] / den2)), 5),
+                "m2_reduction_vs_euclid": round(1 - float(np.sqrt(num2[k] / num2["euclid"])), 4)}
+            for k in methods}
+    return {"study": "reference", "workload": w.name, "scaling": "per-tensor E4M3",
+            "output_factor": "G G^T / d_in", "rows": rows}
 
 
 # ---------------------------------------------------------------------------

@@ -48,6 +48,15 @@ implementation's reading, each marked where it is taken:
    S_i = (A_i + lambda_floor I)^{-1/2}, and G^[:, block i] =
    W^[:, block i] (A_i + lambda_floor I)^{1/2}.  A block keeps its whole
    spectrum, so there is no discarded tail to add to the damping.
+11. Full-rank and two-sided references (the review's claim that the
+   input-side factor captures nearly all of the full two-sided K-FAC
+   transform's benefit, "The pith", and its Eq. 14 Cholesky form L_A^-T):
+   input-side symmetric W = G (A + lambda I)^{-1/2}; input-side Cholesky
+   W = G L^-T with L L^T = A + lambda I, undone by W^ L^T; two-sided
+   W = (B + mu I)^{-1/2} G (A + lambda I)^{-1/2} with the output-side factor
+   read as the gradient's row second moment B = G G^T / d_in and
+   mu = eps tr(B) / d_out (reading: the pages give no output-side
+   generator).  Each is quantized like W of step 6.
 
 Precision: inputs are fp32 (activations bf16 values held in fp32); every
 linear-algebra step runs in fp64.  The steps that decide an integer (the
@@ -415,6 +424,63 @@ def block_roundtrip(G, bf, block128=False):
     codes, inv, flags = quantize(W32, block128)
     What = dequantize(codes, inv, block128)
     return codes, inv, W32, block_unwhiten(What, bf), flags
+
+
+# --------------------------------------------------------------------------
+# full-rank and two-sided references (step 11)
+# --------------------------------------------------------------------------
+
+def _damped(M, eps):
+    M = np.asarray(M, dtype=np.float64)
+    lam = max(eps * np.trace(M) / M.shape[0], LAMBDA_MIN)
+    return M + lam * np.eye(M.shape[0])
+
+
+def sym_pair(M, eps=DAMP_EPS):
+    """((M + lam I)^{-1/2}, (M + lam I)^{1/2}), lam = eps tr(M) / n, by eigh."""
+    w, V = np.linalg.eigh(_damped(M, eps))
+    w = np.maximum(w, 0.0)
+    return (V * w ** -0.5) @ V.T, (V * w ** 0.5) @ V.T
+
+
+def cholesky_pair(A, eps=DAMP_EPS):
+    """(L^-T, L^T) with L L^T = A + lam I (L lower triangular)."""
+    L = np.linalg.cholesky(_damped(A, eps))
+    Linv = np.linalg.solve(L, np.eye(L.shape[0]))
+    return Linv.T, L.T
+
+
+def output_factor(G):
+    """Output-side factor read as the gradient's row second moment G G^T / d_in."""
+    G = np.asarray(G, dtype=np.float64)
+    return G @ G.T / G.shape[1]
+
+
+def reference_transforms(G, A, eps=DAMP_EPS):
+    """{name: (left, right, left_inv, right_inv)} of the references; None
+    stands for the identity."""
+    S, Si = sym_pair(A, eps)
+    Lt_inv, Lt = cholesky_pair(A, eps)
+    SB, SBi = sym_pair(output_factor(G), eps)
+    return {"input_full": (None, S, None, Si),
+            "input_cholesky": (None, Lt_inv, None, Lt),
+            "two_sided": (SB, S, SBi, Si)}
+
+
+def _lr(M, left, right):
+    M = np.asarray(M, dtype=np.float64)
+    if left is not None:
+        M = left @ M
+    return M @ right if right is not None else M
+
+
+def reference_roundtrip(G, transform, block128=False):
+    """W = left G right -> fl32 -> quantize -> dequantize -> left_inv W^ right_inv.
+    Returns (codes, inv, W32, G^ fp64)."""
+    left, right, left_inv, right_inv = transform
+    W32 = _lr(G, left, right).astype(np.float32)
+    codes, inv, _ = quantize(W32, block128)
+    return codes, inv, W32, _lr(dequantize(codes, inv, block128), left_inv, right_inv)
 
 
 def reduce_payloads(payloads):

@@ -46,3 +46,15 @@ def test_interval_small():
     assert rows[2]["m2_mean"] <= rows[4]["m2_mean"] + 1e-4
     assert rows[4]["m2_worst"] >= rows[1]["m2_worst"]
     assert out["refresh_ms"] > 0 and rows[4]["refresh_ms_per_step"] < rows[1]["refresh_ms_per_step"]
+
+
+def test_reference_study_small():
+    """Full-rank input-side whitening beats the rank-32 factor, which beats
+    Euclidean FP8, in the input-side K-FAC metric; the Cholesky form and the
+    two-sided transform also beat Euclid."""
+    say("reference study hidden 256 mlp 512 tokens 4096")
+    args = argparse.Namespace(ref_shape="256,512,4096", quiet=True)
+    rows = bench.reference_study(args)["rows"]
+    assert rows["input_full"]["m2"] < rows["gift_rank32"]["m2"] < rows["euclid"]["m2"]
+    assert rows["input_cholesky"]["m2"] < rows["euclid"]["m2"]
+    assert rows["two_sided"]["m2"] < rows["euclid"]["m2"]
