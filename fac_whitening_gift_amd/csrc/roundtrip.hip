@@ -214,6 +214,42 @@ __device__ __forceinline__ Tile tile_ctx(const LayerDev& L, int tile) {
   return x;
 }
 
+// E4M3 codes of a whole tile are staged in LDS and stored as 16-byte pieces
+// of whole row segments (up to 256 or 512 bytes per row): a wave's own stores
+// would write 32 bytes per row and instruction, a quarter of a cache line.
+// One 32-bit word holds four codes; the row stride (8 words per chunk plus 4)
+// puts the 64 lanes of a write on distinct banks.
+template <int kCPW>
+struct CodeTile {
+  static constexpr int kStride = kTW * kCPW * 8 + 4;
+  uint32_t w[kTileRows][kStride];
+};
+
+// the four codes of chunk j, 16-row tile rt, half t of this lane
+template <int kCPW>
+__device__ __forceinline__ void put_codes(CodeTile<kCPW>& ct, const Tile& x, int j, int rt, int t,
+                                          uint32_t c) {
+  ct.w[16 * rt + x.r16][8 * (x.wave * kCPW + j) + 4 * t + x.g] = c;
+}
+
+// after a workgroup barrier: every row of the tile inside the layer, every
+// chunk inside d_in
+template <int kCPW>
+__device__ __forceinline__ void store_code_tile(const LayerDev& L, const Tile& x,
+                                                const CodeTile<kCPW>& ct) {
+  constexpr int kQ = kTW * kCPW * 2;  // 16-byte pieces per row
+  const int nch = (int)(L.d_in / kChunk), cfirst = x.cg * kTW * kCPW;
+  const int nvalid = nch - cfirst < kTW * kCPW ? nch - cfirst : kTW * kCPW;
+#pragma unroll
+  for (int h = 0; h < kTileRows * kQ / kTileThreads; ++h) {
+    const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
+    const int64_t row = x.rb * kTileRows + r;
+    if (row < L.d_out && (qd >> 1) < nvalid)
+      *reinterpret_cast<uint4*>(L.q + row * L.d_in + kChunk * cfirst + 16 * qd) =
+          *reinterpret_cast<const uint4*>(&ct.w[r][4 * qd]);
+  }
+}
+
 __device__ __forceinline__ void load_a(const uint4* P, int c, int lane, uint4 (&a)[2][3]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -498,6 +534,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
   const Tile x = tile_ctx<kCPW>(L, tile);
   __shared__ uint4 cs[kCOp];
   __shared__ uint32_t mx[kBlock128 ? kTW * kTR * 64 : kTW];
+  __shared__ uint32_t ctw[kBlock128 ? sizeof(CodeTile<kCPW>) / 4 : 1];
+  CodeTile<kCPW>* ct = reinterpret_cast<CodeTile<kCPW>*>(ctw);
   const uint4* P2 = p2_of(L);
   const float alpha = L.coef[kFmt == kFmtUnwhiten ? GIFT_COEF_BETA : GIFT_COEF_ALPHA];
   // this wave's operands and gradient in flight while c' is staged
@@ -610,34 +648,38 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
       sm[x.wave][rt][x.lane] = m;
     }
     __syncthreads();
-    if (x.nmine == 0) return;  // wave-uniform; no barrier below
     const int w0 = x.wave - x.wave % kWPS;
     const int seg = x.c0 / 4;
     const int64_t nseg = L.d_in / kBlock;
+    if (x.nmine) {  // wave-uniform
 #pragma unroll
-    for (int rt = 0; rt < kTR; ++rt) {
-      uint32_t m = 0u;
+      for (int rt = 0; rt < kTR; ++rt) {
+        uint32_t m = 0u;
 #pragma unroll
-      for (int v = 0; v < kWPS; ++v) m = max(m, sm[w0 + v][rt][x.lane]);
-      const Scale sc = scale_from_amax_bits(m);
-      if (!x.ok[rt]) continue;
-      if (x.g == 0 && x.wave == w0) {
-        L.inv[x.row[rt] * nseg + seg] = sc.inv;
-        if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
-      }
-      with_count<kCPW>(x.nmine, [&](auto N) {
-        static_for<decltype(N)::value>([&](auto J) {
-          constexpr int j = decltype(J)::value;
+        for (int v = 0; v < kWPS; ++v) m = max(m, sm[w0 + v][rt][x.lane]);
+        const Scale sc = scale_from_amax_bits(m);
+        if (x.ok[rt] && x.g == 0 && x.wave == w0) {
+          L.inv[x.row[rt] * nseg + seg] = sc.inv;
+          if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
+        }
+        with_count<kCPW>(x.nmine, [&](auto N) {
+          static_for<decltype(N)::value>([&](auto J) {
+            constexpr int j = decltype(J)::value;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int64_t o = x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g;
-            const float4 v = w[j][rt][t];
-            *reinterpret_cast<uint32_t*>(L.q + o) = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
-            if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = v;
-          }
+            for (int t = 0; t < 2; ++t) {
+              const float4 v = w[j][rt][t];
+              put_codes(*ct, x, j, rt, t,
+                        e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE));
+              if (kWriteW && L.Wout && x.ok[rt])
+                *reinterpret_cast<float4*>(L.Wout + x.row[rt] * L.d_in + kChunk * (x.c0 + j) +
+                                           16 * t + 4 * x.g) = v;
+            }
+          });
         });
-      });
+      }
     }
+    __syncthreads();
+    store_code_tile(L, x, *ct);
   }
 }
 
@@ -677,13 +719,10 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
     if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
   }
   stage_c(L, x, cs);
-  if (x.nmine == 0) return;  // wave-uniform; no barrier below
+  __shared__ CodeTile<kCPW> ct;
   const bool nonfinite = (sc.flags & GIFT_FLAG_NONFINITE) != 0;
-  uint32_t codes[kCPW][kTR][2];
-  float4 wv[kWriteW ? kCPW : 1][kTR][2];
   with_count<kCPW>(x.nmine, [&](auto N) {
-    constexpr int n = decltype(N)::value;
-    static_for<n>([&](auto J) {
+    static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
       bf16x8 a[2][3];
       as_ops(pa[j], a);
@@ -698,25 +737,16 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
           const float4 gg = gv[j][rt][t];
           const float4 v = make_float4(fmaf(alpha, gg.x, corr[t][0]), fmaf(alpha, gg.y, corr[t][1]),
                                        fmaf(alpha, gg.z, corr[t][2]), fmaf(alpha, gg.w, corr[t][3]));
-          codes[j][rt][t] = e4m3_encode4_scaled(v, sc.scale, nonfinite);
-          if constexpr (kWriteW) wv[j][rt][t] = v;
-        }
-      }
-    });
-    static_for<n>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-#pragma unroll
-      for (int rt = 0; rt < kTR; ++rt) {
-        if (!x.ok[rt]) continue;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int64_t o = x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g;
-          *reinterpret_cast<uint32_t*>(L.q + o) = codes[j][rt][t];
-          if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = wv[j][rt][t];
+          put_codes(ct, x, j, rt, t, e4m3_encode4_scaled(v, sc.scale, nonfinite));
+          if (kWriteW && L.Wout && x.ok[rt])
+            *reinterpret_cast<float4*>(L.Wout + x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t +
+                                       4 * x.g) = v;
         }
       }
     });
   });
+  __syncthreads();
+  store_code_tile(L, x, ct);
 }
 
 // ---------------------------------------------------------------------------
@@ -810,6 +840,8 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kb>(L, tile);
   __shared__ uint32_t mx[kMode == 2 ? kTW * kTR * 64 : kTW];
+  __shared__ uint32_t ctw[kMode != 0 ? sizeof(CodeTile<kb>) / 4 : 1];
+  CodeTile<kb>& ct = *reinterpret_cast<CodeTile<kb>*>(ctw);
   const int64_t nblk = L.d_in / kB, blk = x.c0 / kb;
   float4 w[kb][kTR][2];
   if (x.nmine) {  // wave-uniform: a wave has a whole block or nothing
@@ -855,20 +887,21 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
       L.inv[0] = sc.inv;
       if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
     }
-    if (x.nmine == 0) return;  // wave-uniform; no barrier below
     const bool nonfinite = (sc.flags & GIFT_FLAG_NONFINITE) != 0;
+    if (x.nmine)  // wave-uniform
 #pragma unroll
-    for (int rt = 0; rt < kTR; ++rt) {
-      if (!x.ok[rt]) continue;
+      for (int rt = 0; rt < kTR; ++rt)
 #pragma unroll
-      for (int oc = 0; oc < kb; ++oc)
+        for (int oc = 0; oc < kb; ++oc)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int64_t o = (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) + 16 * t + 4 * x.g;
-          *reinterpret_cast<uint32_t*>(L.q + o) = e4m3_encode4_scaled(w[oc][rt][t], sc.scale, nonfinite);
-          if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = w[oc][rt][t];
-        }
-    }
+          for (int t = 0; t < 2; ++t) {
+            put_codes(ct, x, oc, rt, t, e4m3_encode4_scaled(w[oc][rt][t], sc.scale, nonfinite));
+            if (kWriteW && L.Wout && x.ok[rt])
+              *reinterpret_cast<float4*>(L.Wout + (int64_t)x.row[rt] * L.d_in +
+                                         kChunk * (x.c0 + oc) + 16 * t + 4 * x.g) = w[oc][rt][t];
+          }
+    __syncthreads();
+    store_code_tile(L, x, ct);
   } else {
     // per-segment amax: lane max over its chunks, then over the lanes of the
     // same row (xor 16, 32), then over the segment's waves through LDS
@@ -884,31 +917,33 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
       sm[x.wave][rt][x.lane] = m;
     }
     __syncthreads();
-    if (x.nmine == 0) return;  // wave-uniform; no barrier below
     const int w0 = x.wave - x.wave % kWPS;
     const int seg = x.c0 / 4;
     const int64_t nseg = L.d_in / kBlock;
+    if (x.nmine)  // wave-uniform
 #pragma unroll
-    for (int rt = 0; rt < kTR; ++rt) {
-      uint32_t m = 0u;
+      for (int rt = 0; rt < kTR; ++rt) {
+        uint32_t m = 0u;
 #pragma unroll
-      for (int v = 0; v < kWPS; ++v) m = max(m, sm[w0 + v][rt][x.lane]);
-      const Scale sc = scale_from_amax_bits(m);
-      if (!x.ok[rt]) continue;
-      if (x.g == 0 && x.wave == w0) {
-        L.inv[x.row[rt] * nseg + seg] = sc.inv;
-        if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
-      }
-#pragma unroll
-      for (int oc = 0; oc < kb; ++oc)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int64_t o = (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) + 16 * t + 4 * x.g;
-          *reinterpret_cast<uint32_t*>(L.q + o) =
-              e4m3_encode4_scaled(w[oc][rt][t], sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
-          if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + o) = w[oc][rt][t];
+        for (int v = 0; v < kWPS; ++v) m = max(m, sm[w0 + v][rt][x.lane]);
+        const Scale sc = scale_from_amax_bits(m);
+        if (x.ok[rt] && x.g == 0 && x.wave == w0) {
+          L.inv[x.row[rt] * nseg + seg] = sc.inv;
+          if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
         }
-    }
+#pragma unroll
+        for (int oc = 0; oc < kb; ++oc)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            put_codes(ct, x, oc, rt, t,
+                      e4m3_encode4_scaled(w[oc][rt][t], sc.scale, sc.flags & GIFT_FLAG_NONFINITE));
+            if (kWriteW && L.Wout && x.ok[rt])
+              *reinterpret_cast<float4*>(L.Wout + (int64_t)x.row[rt] * L.d_in +
+                                         kChunk * (x.c0 + oc) + 16 * t + 4 * x.g) = w[oc][rt][t];
+          }
+      }
+    __syncthreads();
+    store_code_tile(L, x, ct);
   }
 }
 
