@@ -250,6 +250,48 @@ __device__ __forceinline__ void store_code_tile(const LayerDev& L, const Tile& x
   }
 }
 
+// The reverse for the dequantize side: the tile's codes are loaded as 16-byte
+// pieces of whole row segments (zero outside the layer), put in LDS in the
+// same layout, and each lane then takes its words.
+template <int kCPW>
+struct CodePieces {
+  static constexpr int kQ = kTW * kCPW * 2;                 // 16-byte pieces per row
+  static constexpr int kN = kTileRows * kQ / kTileThreads;  // per thread
+  uint4 v[kN];
+};
+
+template <int kCPW>
+__device__ __forceinline__ void load_code_pieces(const LayerDev& L, const Tile& x,
+                                                 CodePieces<kCPW>& pc) {
+  constexpr int kQ = CodePieces<kCPW>::kQ;
+  const int nch = (int)(L.d_in / kChunk), cfirst = x.cg * kTW * kCPW;
+  const int nvalid = nch - cfirst < kTW * kCPW ? nch - cfirst : kTW * kCPW;
+#pragma unroll
+  for (int h = 0; h < CodePieces<kCPW>::kN; ++h) {
+    const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
+    const int64_t row = x.rb * kTileRows + r;
+    const bool in = row < L.d_out && (qd >> 1) < nvalid;
+    pc.v[h] = in ? *reinterpret_cast<const uint4*>(L.q + row * L.d_in + kChunk * cfirst + 16 * qd)
+                 : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int kCPW>
+__device__ __forceinline__ void put_code_pieces(CodeTile<kCPW>& ct, const CodePieces<kCPW>& pc) {
+  constexpr int kQ = CodePieces<kCPW>::kQ;
+#pragma unroll
+  for (int h = 0; h < CodePieces<kCPW>::kN; ++h) {
+    const int e = threadIdx.x + h * kTileThreads;
+    *reinterpret_cast<uint4*>(&ct.w[e / kQ][4 * (e % kQ)]) = pc.v[h];
+  }
+}
+
+template <int kCPW>
+__device__ __forceinline__ uint32_t get_codes(const CodeTile<kCPW>& ct, const Tile& x, int j,
+                                              int rt, int t) {
+  return ct.w[16 * rt + x.r16][8 * (x.wave * kCPW + j) + 4 * t + x.g];
+}
+
 __device__ __forceinline__ void load_a(const uint4* P, int c, int lane, uint4 (&a)[2][3]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -419,6 +461,15 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
 #pragma unroll
   for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t nseg = L.d_in / kBlock;
+  constexpr bool kStaged = kCodes && !kMX;  // codes come through LDS
+  __shared__ uint32_t ctw[kStaged ? sizeof(CodeTile<kCPW>) / 4 : 1];
+  CodeTile<kCPW>& ct = *reinterpret_cast<CodeTile<kCPW>*>(ctw);
+  if constexpr (kStaged) {
+    CodePieces<kCPW> pcs;
+    load_code_pieces(L, x, pcs);
+    put_code_pieces(ct, pcs);
+    __syncthreads();
+  }
   with_count<kCPW>(x.nmine, [&](auto N) {
     constexpr int n = decltype(N)::value;
     uint4 pa[n][2][3];
@@ -432,7 +483,9 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
         if constexpr (kMX) load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
-        else if constexpr (kCodes) load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
+        else if constexpr (kCodes)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) qv[j][rt][t] = get_codes(ct, x, j, rt, t);
         else load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
         if constexpr (kB128) sc[j][rt] = L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)];
       }
@@ -1024,23 +1077,36 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
   uint32_t qv[kCPW][kTR][2];
   float sc[kCPW][kTR];
   uint32_t mc[kMX ? kCPW : 1][kTR];
+  __shared__ uint32_t ctw[kMX ? 1 : sizeof(CodeTile<kCPW>) / 4];
+  CodeTile<kCPW>& ct = *reinterpret_cast<CodeTile<kCPW>*>(ctw);
+  CodePieces<kCPW> pcs;
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
       load_a(P2, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        if constexpr (kMX) {
-          load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
-        } else {
-          load_qc(L, x.row[rt], x.g, x.c0 + j, qv[j][rt]);
-          sc[j][rt] = kB128 ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
-        }
+        if constexpr (kMX) load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
+        else sc[j][rt] = kB128 ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
       }
     });
   });
-  stage_c(L, x, cs);
+  if constexpr (!kMX) {
+    load_code_pieces(L, x, pcs);
+    put_code_pieces(ct, pcs);
+  }
+  stage_c(L, x, cs);  // its barrier also publishes the codes
   if (x.nmine == 0) return;  // wave-uniform; no barrier below
+  if constexpr (!kMX)
+    with_count<kCPW>(x.nmine, [&](auto N) {
+      static_for<decltype(N)::value>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+#pragma unroll
+        for (int rt = 0; rt < kTR; ++rt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) qv[j][rt][t] = get_codes(ct, x, j, rt, t);
+      });
+    });
   float4 out[kCPW][kTR][2];
   with_count<kCPW>(x.nmine, [&](auto N) {
     constexpr int n = decltype(N)::value;
