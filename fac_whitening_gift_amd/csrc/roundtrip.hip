@@ -1003,24 +1003,35 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
 // G^[:, block] = inv * (decode(q)[:, block] S^-1): codes are exact in bf16,
 // so the product takes the three splits of S^-1 only; the scale (per tensor,
 // or the 128-column segment's, which holds the whole block) comes after.
+// The codes come through LDS as in k_tile_unwhiten.
 template <int kB, bool kB128>
 __global__ __launch_bounds__(kTileThreads) void k_blk_dequant(GroupDev gd) {
   constexpr int kb = kB / kChunk;
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kb>(L, tile);
-  if (x.nmine == 0) return;  // wave-uniform; the kernel has no barrier
   const int64_t nblk = L.d_in / kB, blk = x.c0 / kb;
   uint32_t qv[kTR][kb][2];
   uint4 pa[kb][2][3];
   float inv[kTR];
+  __shared__ CodeTile<kb> ct;
+  if (x.nmine) {  // wave-uniform
+    load_blk_packs<kb>(L.P, nblk, 1, blk, 0, x.lane, pa);
 #pragma unroll
-  for (int rt = 0; rt < kTR; ++rt) {
-#pragma unroll
-    for (int kc = 0; kc < kb; ++kc) load_qc(L, x.row[rt], x.g, x.c0 + kc, qv[rt][kc]);
-    inv[rt] = kB128 ? L.inv[(int64_t)x.row[rt] * (L.d_in / kBlock) + x.c0 / 4] : L.inv[0];
+    for (int rt = 0; rt < kTR; ++rt)
+      inv[rt] = kB128 ? L.inv[(int64_t)x.row[rt] * (L.d_in / kBlock) + x.c0 / 4] : L.inv[0];
   }
-  load_blk_packs<kb>(L.P, nblk, 1, blk, 0, x.lane, pa);
+  CodePieces<kb> pcs;
+  load_code_pieces(L, x, pcs);
+  put_code_pieces(ct, pcs);
+  __syncthreads();
+  if (x.nmine == 0) return;  // wave-uniform; no barrier below
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt)
+#pragma unroll
+    for (int kc = 0; kc < kb; ++kc)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) qv[rt][kc][t] = get_codes(ct, x, kc, rt, t);
   float4 gh[kb][kTR][2];
 #pragma unroll
   for (int oc = 0; oc < kb; ++oc) {
