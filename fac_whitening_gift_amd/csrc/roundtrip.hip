@@ -292,6 +292,75 @@ __device__ __forceinline__ uint32_t get_codes(const CodeTile<kCPW>& ct, const Ti
   return ct.w[16 * rt + x.r16][8 * (x.wave * kCPW + j) + 4 * t + x.g];
 }
 
+// The same for MXFP4: per row and chunk 16 bytes of E2M1 codes (16 bits per
+// lane and half) and one E8M0 scale byte.
+template <int kCPW>
+struct MxTile {
+  static constexpr int kChunks = kTW * kCPW;
+  static constexpr int kStride = kChunks * 8 + 8;  // 16-bit units per row of codes
+  uint16_t c[kTileRows][kStride];
+  uint8_t s[kTileRows][kChunks + 8];
+};
+
+template <int kCPW>
+__device__ __forceinline__ int mx_valid(const LayerDev& L, const Tile& x) {
+  const int nch = (int)(L.d_in / kChunk), cfirst = x.cg * kTW * kCPW;
+  return nch - cfirst < kTW * kCPW ? nch - cfirst : kTW * kCPW;
+}
+
+template <int kCPW>
+__device__ __forceinline__ void store_mx_tile(const LayerDev& L, const Tile& x,
+                                              const MxTile<kCPW>& mt) {
+  constexpr int kQ = MxTile<kCPW>::kChunks;  // 16-byte pieces (one chunk each) per row
+  const int cfirst = x.cg * kTW * kCPW, nvalid = mx_valid<kCPW>(L, x);
+  const int64_t nblk = L.d_in / kMxBlock;
+  for (int e = threadIdx.x; e < kTileRows * kQ; e += kTileThreads) {
+    const int r = e / kQ, qd = e % kQ;
+    const int64_t row = x.rb * kTileRows + r;
+    if (row < L.d_out && qd < nvalid) {
+      *reinterpret_cast<uint4*>(L.q + row * (L.d_in / 2) + 16 * (cfirst + qd)) =
+          *reinterpret_cast<const uint4*>(&mt.c[r][8 * qd]);
+      reinterpret_cast<uint8_t*>(L.inv)[row * nblk + cfirst + qd] = mt.s[r][qd];
+    }
+  }
+}
+
+template <int kCPW>
+__device__ __forceinline__ void load_mx_tile(const LayerDev& L, const Tile& x, MxTile<kCPW>& mt) {
+  constexpr int kQ = MxTile<kCPW>::kChunks;
+  constexpr int kN = (kTileRows * kQ + kTileThreads - 1) / kTileThreads;
+  const int cfirst = x.cg * kTW * kCPW, nvalid = mx_valid<kCPW>(L, x);
+  const int64_t nblk = L.d_in / kMxBlock;
+  uint4 v[kN];
+  uint32_t sc[kN];
+#pragma unroll
+  for (int h = 0; h < kN; ++h) {
+    const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
+    const int64_t row = x.rb * kTileRows + r;
+    const bool in = e < kTileRows * kQ && row < L.d_out && qd < nvalid;
+    v[h] = in ? *reinterpret_cast<const uint4*>(L.q + row * (L.d_in / 2) + 16 * (cfirst + qd))
+              : make_uint4(0u, 0u, 0u, 0u);
+    sc[h] = in ? reinterpret_cast<const uint8_t*>(L.inv)[row * nblk + cfirst + qd] : 127u;
+  }
+#pragma unroll
+  for (int h = 0; h < kN; ++h) {
+    const int e = threadIdx.x + h * kTileThreads;
+    if (e < kTileRows * kQ) {
+      *reinterpret_cast<uint4*>(&mt.c[e / kQ][8 * (e % kQ)]) = v[h];
+      mt.s[e / kQ][e % kQ] = (uint8_t)sc[h];
+    }
+  }
+}
+
+template <int kCPW>
+__device__ __forceinline__ void get_mx(const MxTile<kCPW>& mt, const Tile& x, int j, int rt,
+                                       uint32_t (&v)[2], uint32_t& code) {
+  const int r = 16 * rt + x.r16, k = x.wave * kCPW + j;
+  v[0] = mt.c[r][8 * k + x.g];
+  v[1] = mt.c[r][8 * k + 4 + x.g];
+  code = mt.s[r][k];
+}
+
 __device__ __forceinline__ void load_a(const uint4* P, int c, int lane, uint4 (&a)[2][3]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -327,16 +396,6 @@ __device__ __forceinline__ void load_qc(const LayerDev& L, int64_t row, int g, i
   const uint8_t* p = L.q + row * L.d_in + kChunk * c + 4 * g;
   v[0] = *reinterpret_cast<const uint32_t*>(p);
   v[1] = *reinterpret_cast<const uint32_t*>(p + 16);
-}
-
-// MXFP4 codes of one chunk for this lane and 16-row tile: the same 2 x 4
-// columns as load_gc, 16 bits each, and the chunk's (= the block's) scale
-__device__ __forceinline__ void load_mx(const LayerDev& L, int64_t row, int g, int c,
-                                        uint32_t (&v)[2], uint32_t& code) {
-  const uint8_t* p = L.q + row * (L.d_in / 2) + 16 * c + 2 * g;
-  v[0] = *reinterpret_cast<const uint16_t*>(p);
-  v[1] = *reinterpret_cast<const uint16_t*>(p + 8);
-  code = reinterpret_cast<const uint8_t*>(L.inv)[row * (L.d_in / kMxBlock) + c];
 }
 
 // first product on MXFP4 values (code value * 2^e is exact in bf16)
@@ -461,13 +520,18 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
 #pragma unroll
   for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t nseg = L.d_in / kBlock;
-  constexpr bool kStaged = kCodes && !kMX;  // codes come through LDS
-  __shared__ uint32_t ctw[kStaged ? sizeof(CodeTile<kCPW>) / 4 : 1];
+  constexpr bool kStaged = kCodes && !kMX;  // E4M3 codes come through LDS
+  __shared__ __align__(16) uint32_t ctw[kStaged ? sizeof(CodeTile<kCPW>) / 4
+                          : kMX ? (sizeof(MxTile<kCPW>) + 3) / 4 : 1];
   CodeTile<kCPW>& ct = *reinterpret_cast<CodeTile<kCPW>*>(ctw);
+  MxTile<kCPW>& mt = *reinterpret_cast<MxTile<kCPW>*>(ctw);
   if constexpr (kStaged) {
     CodePieces<kCPW> pcs;
     load_code_pieces(L, x, pcs);
     put_code_pieces(ct, pcs);
+    __syncthreads();
+  } else if constexpr (kMX) {
+    load_mx_tile(L, x, mt);
     __syncthreads();
   }
   with_count<kCPW>(x.nmine, [&](auto N) {
@@ -482,7 +546,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
       load_a(L.P, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        if constexpr (kMX) load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
+        if constexpr (kMX) get_mx(mt, x, j, rt, qv[j][rt], mc[j][rt]);
         else if constexpr (kCodes)
 #pragma unroll
           for (int t = 0; t < 2; ++t) qv[j][rt][t] = get_codes(ct, x, j, rt, t);
@@ -587,7 +651,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
   const Tile x = tile_ctx<kCPW>(L, tile);
   __shared__ uint4 cs[kCOp];
   __shared__ uint32_t mx[kBlock128 ? kTW * kTR * 64 : kTW];
-  __shared__ uint32_t ctw[kBlock128 ? sizeof(CodeTile<kCPW>) / 4 : 1];
+  __shared__ __align__(16) uint32_t ctw[kBlock128 ? sizeof(CodeTile<kCPW>) / 4
+                          : kFmt == GIFT_SCALE_MXFP4 ? (sizeof(MxTile<kCPW>) + 3) / 4 : 1];
   CodeTile<kCPW>* ct = reinterpret_cast<CodeTile<kCPW>*>(ctw);
   const uint4* P2 = p2_of(L);
   const float alpha = L.coef[kFmt == kFmtUnwhiten ? GIFT_COEF_BETA : GIFT_COEF_ALPHA];
@@ -651,8 +716,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
       });
     });
   } else if constexpr (kFmt == GIFT_SCALE_MXFP4) {
-    if (x.nmine == 0) return;  // wave-uniform; no barrier below
-    const int64_t nblk = L.d_in / kMxBlock;
+    MxTile<kCPW>& mt = *reinterpret_cast<MxTile<kCPW>*>(ctw);
     with_count<kCPW>(x.nmine, [&](auto N) {
       static_for<decltype(N)::value>([&](auto J) {
         constexpr int j = decltype(J)::value;
@@ -665,16 +729,12 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
           const uint32_t code = mx_scale_code(m, fl);
           const float s = mx_scale_operand(code);
           const bool nonfinite = code == kMxScaleNaN;
-          const uint32_t q0 = mx_encode4(w[j][rt][0], s, nonfinite);
-          const uint32_t q1 = mx_encode4(w[j][rt][1], s, nonfinite);
+          const int r = 16 * rt + x.r16, k = x.wave * kCPW + j;
+          mt.c[r][8 * k + x.g] = (uint16_t)mx_encode4(w[j][rt][0], s, nonfinite);
+          mt.c[r][8 * k + 4 + x.g] = (uint16_t)mx_encode4(w[j][rt][1], s, nonfinite);
+          if (x.g == 0) mt.s[r][k] = (uint8_t)code;
           if (!x.ok[rt]) continue;
-          uint8_t* p = L.q + (int64_t)x.row[rt] * (L.d_in / 2) + 16 * (x.c0 + j) + 2 * x.g;
-          *reinterpret_cast<uint16_t*>(p) = (uint16_t)q0;
-          *reinterpret_cast<uint16_t*>(p + 8) = (uint16_t)q1;
-          if (x.g == 0) {
-            reinterpret_cast<uint8_t*>(L.inv)[x.row[rt] * nblk + x.c0 + j] = (uint8_t)code;
-            if (gd.flags && fl) atomicOr(gd.flags, fl);
-          }
+          if (x.g == 0 && gd.flags && fl) atomicOr(gd.flags, fl);
           if (kWriteW && L.Wout) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -684,6 +744,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
         }
       });
     });
+    __syncthreads();
+    store_mx_tile(L, x, mt);
   } else {
     // per-segment amax: lane max over its chunks of the segment, then over
     // the lanes of the same row (xor 16, 32), then over the segment's waves
@@ -772,7 +834,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
     if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
   }
   stage_c(L, x, cs);
-  __shared__ CodeTile<kCPW> ct;
+  __shared__ __align__(16) CodeTile<kCPW> ct;
   const bool nonfinite = (sc.flags & GIFT_FLAG_NONFINITE) != 0;
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
@@ -893,7 +955,7 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kb>(L, tile);
   __shared__ uint32_t mx[kMode == 2 ? kTW * kTR * 64 : kTW];
-  __shared__ uint32_t ctw[kMode != 0 ? sizeof(CodeTile<kb>) / 4 : 1];
+  __shared__ __align__(16) uint32_t ctw[kMode != 0 ? sizeof(CodeTile<kb>) / 4 : 1];
   CodeTile<kb>& ct = *reinterpret_cast<CodeTile<kb>*>(ctw);
   const int64_t nblk = L.d_in / kB, blk = x.c0 / kb;
   float4 w[kb][kTR][2];
@@ -1014,7 +1076,7 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_dequant(GroupDev gd) {
   uint32_t qv[kTR][kb][2];
   uint4 pa[kb][2][3];
   float inv[kTR];
-  __shared__ CodeTile<kb> ct;
+  __shared__ __align__(16) CodeTile<kb> ct;
   if (x.nmine) {  // wave-uniform
     load_blk_packs<kb>(L.P, nblk, 1, blk, 0, x.lane, pa);
 #pragma unroll
@@ -1088,8 +1150,9 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
   uint32_t qv[kCPW][kTR][2];
   float sc[kCPW][kTR];
   uint32_t mc[kMX ? kCPW : 1][kTR];
-  __shared__ uint32_t ctw[kMX ? 1 : sizeof(CodeTile<kCPW>) / 4];
+  __shared__ __align__(16) uint32_t ctw[kMX ? (sizeof(MxTile<kCPW>) + 3) / 4 : sizeof(CodeTile<kCPW>) / 4];
   CodeTile<kCPW>& ct = *reinterpret_cast<CodeTile<kCPW>*>(ctw);
+  MxTile<kCPW>& mt = *reinterpret_cast<MxTile<kCPW>*>(ctw);
   CodePieces<kCPW> pcs;
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
@@ -1097,27 +1160,32 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
       load_a(P2, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        if constexpr (kMX) load_mx(L, x.row[rt], x.g, x.c0 + j, qv[j][rt], mc[j][rt]);
-        else sc[j][rt] = kB128 ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
+        if constexpr (!kMX) sc[j][rt] = kB128 ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
       }
     });
   });
-  if constexpr (!kMX) {
+  if constexpr (kMX) {
+    load_mx_tile(L, x, mt);
+  } else {
     load_code_pieces(L, x, pcs);
     put_code_pieces(ct, pcs);
   }
   stage_c(L, x, cs);  // its barrier also publishes the codes
   if (x.nmine == 0) return;  // wave-uniform; no barrier below
-  if constexpr (!kMX)
-    with_count<kCPW>(x.nmine, [&](auto N) {
-      static_for<decltype(N)::value>([&](auto J) {
-        constexpr int j = decltype(J)::value;
+  with_count<kCPW>(x.nmine, [&](auto N) {
+    static_for<decltype(N)::value>([&](auto J) {
+      constexpr int j = decltype(J)::value;
 #pragma unroll
-        for (int rt = 0; rt < kTR; ++rt)
+      for (int rt = 0; rt < kTR; ++rt) {
+        if constexpr (kMX) {
+          get_mx(mt, x, j, rt, qv[j][rt], mc[j][rt]);
+        } else {
 #pragma unroll
           for (int t = 0; t < 2; ++t) qv[j][rt][t] = get_codes(ct, x, j, rt, t);
-      });
+        }
+      }
     });
+  });
   float4 out[kCPW][kTR][2];
   with_count<kCPW>(x.nmine, [&](auto N) {
     constexpr int n = decltype(N)::value;
