@@ -17,7 +17,7 @@
 //   4. subspace iteration: Y = A Q on fp32 MFMA as partial products over
 //      disjoint K ranges (k_gemm_aq), Q = orth(Y) by CholeskyQR (Fukaya et
 //      al.) with an fp64 Gram matrix (k_gram, which also sums the partials,
-//      k_chol, k_apply); the final basis gets a second CholeskyQR pass.
+//      k_chol, k_solve); the final basis gets a second CholeskyQR pass.
 //   5. Rayleigh-Ritz: B = Q^T A Q (k_gemm_aq + k_gram), cyclic Jacobi on B in
 //      one workgroup per input (Golub & Van Loan, sym.schur2 rotations,
 //      round-robin ordering: 32 disjoint rotations at once), sort,
@@ -700,10 +700,10 @@ __device__ double block_sum(double v, double* red) {
 }
 
 // ---------------------------------------------------------------------------
-// 4c. Cholesky of the Gram matrix, G = R^T R (R upper triangular, fp64), and
-// T = R^-1.  Pivots below kDropTol * max diagonal mark a column as
-// dependent: its row of R and column of T are zero, so that column of the
-// orthonormalised Q is 0.  grid: (inputs), kCT threads.
+// 4c. Cholesky of the Gram matrix, G = R^T R (R upper triangular, fp64).
+// Pivots below kDropTol * max diagonal mark a column as dependent: its row of
+// R is zero and so is that column of the orthonormalised Q (k_solve).  The
+// output is R with 1/R[k][k] on the diagonal.  grid: (inputs), kCT threads.
 //
 // Every thread owns a fixed set of entries (i, j), i <= j, of the upper
 // triangle (at most 3) and keeps them in registers; a step needs one
@@ -713,10 +713,6 @@ __device__ double block_sum(double v, double* red) {
 //     rank-1 update G[i][j] -= G[k][i] G[k][j] / p (right-looking Cholesky
 //     in its unnormalised form); an entry of row k+1 is stored to LDS once
 //     updated, ready for the next step.
-//   * Inverse, step k from the last row up: every entry (i, c), i <= k < c,
-//     adds R[i][k+1] T[k+1][c] to its sum, and row k of T becomes
-//     T[k][c] = (delta_kc - sum) / R[k][k] (column-oriented back
-//     substitution for all columns at once).
 // The thread owning a diagonal entry computes the pivot's reciprocal square
 // root y (the hardware estimate refined by two Newton steps) and 1/p = y^2
 // once the entry is final, and leaves them in LDS for the next step.
@@ -738,7 +734,6 @@ __global__ __launch_bounds__(kCT) void k_chol(RGroup g) {
   const RIn& Rin = g.r[blockIdx.x];
   __shared__ double Gs[W][W + 1];  // row k of the partly reduced G, when final
   __shared__ double R[W][W + 1];
-  __shared__ double Ts[W][W + 1];
   __shared__ double pinv[W], rinv[W];  // 1/p and 1/sqrt(p) of each pivot (0: dropped)
   __shared__ double red[kCT / 64];
   // this thread's entries, row-major over the packed upper triangle: row i
@@ -784,9 +779,6 @@ __global__ __launch_bounds__(kCT) void k_chol(RGroup g) {
   }
   for (int o = 32; o > 0; o >>= 1) dm = fmax(dm, __shfl_xor(dm, o, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dm;
-  // lower triangle of the output T is zero
-  for (int e = threadIdx.x; e < W * W; e += kCT)
-    if (e / W > e % W) Rin.T[(e / W) * kW + e % W] = 0.0;
   __syncthreads();
   double dmax = 0.0;
 #pragma unroll
@@ -824,22 +816,11 @@ __global__ __launch_bounds__(kCT) void k_chol(RGroup g) {
     }
     __syncthreads();
   }
-  // T = R^-1
-#pragma unroll
-  for (int r = 0; r < kE; ++r) v[r] = 0.0;
-  for (int k = W - 1; k >= 0; --k) {
-    const double y = rinv[k];
-#pragma unroll
-    for (int r = 0; r < kE; ++r) {
-      const int i = ei[r], c = ej[r];
-      if (k + 1 < W && i <= k && c > k) v[r] += R[i][k + 1] * Ts[k + 1][c];
-      if (i == k) Ts[k][c] = ((k == c ? 1.0 : 0.0) - v[r]) * y;
-    }
-    __syncthreads();
-  }
+  // R to the output, its diagonal replaced by 1/R[k][k] (0 for a dropped
+  // pivot, whose row of R is 0): what the substitution in k_solve takes
 #pragma unroll
   for (int r = 0; r < kE; ++r)
-    if (ei[r] < W) Rin.T[ei[r] * kW + ej[r]] = Ts[ei[r]][ej[r]];
+    if (ei[r] < W) Rin.T[ei[r] * kW + ej[r]] = ei[r] == ej[r] ? rinv[ei[r]] : R[ei[r]][ej[r]];
 }
 
 // 4d. Out = In T (fp64 accumulate), Out[i][c] for c < ncols.
@@ -931,6 +912,52 @@ __device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, doubl
       __syncthreads();
     }
   }
+}
+
+// 4e. Q = In R^-1 by forward substitution along each row (one row per
+// thread): q_j = (in_j - sum_{k<j} q_k R[k][j]) / R[j][j], fp64, with R and
+// the reciprocal diagonal from k_chol in LDS (broadcast reads).  Replaces an
+// explicit inverse: the rows are independent, so no step needs a barrier.
+// grid: (max d / kT, inputs).  which: 0 = Q1 = Y R^-1, 1 = Q = Q1 R^-1,
+// 2 = Q = Y R^-1
+// ---------------------------------------------------------------------------
+template <int W>
+__global__ __launch_bounds__(kT) void k_solve(RGroup g, int which) {
+  const RIn& R = g.r[blockIdx.y];
+  const int d = R.d;
+  __shared__ double sR[W][W];
+  for (int e = threadIdx.x; e < W * W; e += kT) {
+    const int a = e / W, b = e % W;
+    sR[a][b] = a <= b ? R.T[a * kW + b] : 0.0;
+  }
+  __syncthreads();
+  const int i = blockIdx.x * kT + threadIdx.x;
+  if (i >= d) return;
+  const float* __restrict__ in = (which == 1 ? R.Q1 : R.Y) + (int64_t)i * W;
+  float* __restrict__ out = (which == 0 ? R.Q1 : R.Q) + (int64_t)i * W;
+  double q[W];
+#pragma unroll
+  for (int j = 0; j < W; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(in + j);
+    q[j] = v.x;
+    q[j + 1] = v.y;
+    q[j + 2] = v.z;
+    q[j + 3] = v.w;
+  }
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    double s0 = q[j], s1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < j; ++k) {
+      if (k & 1) s1 -= q[k] * sR[k][j];
+      else s0 -= q[k] * sR[k][j];
+    }
+    q[j] = (s0 + s1) * sR[j][j];
+  }
+#pragma unroll
+  for (int j = 0; j < W; j += 4)
+    *reinterpret_cast<float4*>(out + j) =
+        make_float4((float)q[j], (float)q[j + 1], (float)q[j + 2], (float)q[j + 3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1090,6 +1117,13 @@ void chol(const RGroup& g, int nb, hipStream_t st) {
   if (g.w == 32) k_chol<32><<<nb, kCT, 0, st>>>(g);
   else if (g.w == 48) k_chol<48><<<nb, kCT, 0, st>>>(g);
   else k_chol<64><<<nb, kCT, 0, st>>>(g);
+}
+
+void solve(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
+  const dim3 grid((unsigned)((maxd + kT - 1) / kT), nb);
+  if (g.w == 32) k_solve<32><<<grid, kT, 0, st>>>(g, which);
+  else if (g.w == 48) k_solve<48><<<grid, kT, 0, st>>>(g, which);
+  else k_solve<64><<<grid, kT, 0, st>>>(g, which);
 }
 
 void ritz(const RGroup& g, int nb, hipStream_t st) {
@@ -1271,16 +1305,16 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     for (int s = 0; s < power_steps; ++s) {
       k_gram<<<grams, kT, 0, st>>>(g, 0);
       chol(g, nb, st);
-      k_apply<<<rows, kT, 0, st>>>(g, 2);  // Q = Y T
+      solve(g, 2, maxd, nb, st);  // Q = Y R^-1
       k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 1);
     }
     // final basis: CholeskyQR2 of Y
     k_gram<<<grams, kT, 0, st>>>(g, 0);
     chol(g, nb, st);
-    k_apply<<<rows, kT, 0, st>>>(g, 0);  // Q1 = Y T
+    solve(g, 0, maxd, nb, st);  // Q1 = Y R^-1
     k_gram<<<grams, kT, 0, st>>>(g, 1);
     chol(g, nb, st);
-    k_apply<<<rows, kT, 0, st>>>(g, 1);  // Q = Q1 T
+    solve(g, 1, maxd, nb, st);  // Q = Q1 R^-1
     // 3. Rayleigh-Ritz on B = Q^T A Q
     k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 1);  // Y = A Q
     k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
