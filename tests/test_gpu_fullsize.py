@@ -1,0 +1,118 @@
+"""Parity at the larger layer shapes the benchmark and studies run.
+
+* 600M-stack shapes (hidden 1536, MLP 4096, 16384 bf16 tokens per input):
+  the grouped refresh of an attention-side and an MLP-side input, and the
+  grouped round trip of q (1536 x 1536), gate (4096 x 1536) and down
+  (1536 x 4096) gradients, checked over whole tensors against the oracle
+  on the device's factor values: W within 1e-5, codes bit-exact, G^ within
+  1e-5 (per-tensor and 1x128).
+* 4096 / 11008 shapes (the staleness and interval studies' block), too
+  large for whole-tensor fp64 checks: sampled rows, with the codes of the
+  sampled rows encoded at the device's tensor scale.
+* The refresh at full size, where the oracle's eigensolve is too slow: the
+  properties that hold at any size -- U orthonormal, theta equal to the
+  Rayleigh quotients u^T A u, and within 1e-4 of the top eigenvalues of the
+  exact A (fp64 on the device, measurement harness) on the separated part
+  of the spectrum.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import fac_whitening_gift_amd as fg
+from oracle import e4m3
+from oracle import gift as og
+from gpu_util import DEV, factor_host, host, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _refresh_inputs(specs, seed):
+    inputs, facs = [], []
+    for k, spec in enumerate(specs):
+        inputs.append(synth.draw_input(spec, seed=seed + k, device=DEV, as_bf16=True))
+        facs.append(fg.Factor(spec.d_in, device=DEV))
+    fg.gift_refresh_factors([dict(X=inp["X"], factor=f, seed=k)
+                             for k, (inp, f) in enumerate(zip(inputs, facs))])
+    torch.cuda.synchronize()
+    return inputs, facs
+
+
+def _check_refresh_properties(inp, f):
+    X = inp["X"].double()
+    A = X.T @ X / X.shape[0]
+    U = f.U.double()
+    th = f.theta.double()
+    assert float(torch.linalg.norm(U.T @ U - torch.eye(32, dtype=U.dtype, device=U.device))) < 1e-5
+    rq = torch.einsum("ik,ij,jk->k", U, A, U)
+    assert float((rq - th).abs().max() / th[0]) < 1e-5
+    ev = torch.linalg.eigvalsh(A).flip(0)[:32]
+    rel = ((th - ev).abs() / ev).cpu().numpy()
+    assert rel[:24].max() < 1e-4 and rel.max() < 1e-3
+    return A
+
+
+def test_stack600m_shapes_whole_tensors():
+    say("600M-stack shapes: refresh d 1536 / 4096 (16384 tokens), round trip q, gate, down")
+    w = synth.llama_block(hidden=1536, mlp=4096, tokens=16384, exponent=1.5)
+    specs = [s for s in w.inputs if s.d_in in (1536, 4096)]
+    specs = [next(s for s in specs if s.d_in == 1536), next(s for s in specs if s.d_in == 4096)]
+    inputs, facs = _refresh_inputs(specs, seed=610)
+    for inp, f in zip(inputs, facs):
+        _check_refresh_properties(inp, f)
+    shapes = [(1536, 0), (4096, 0), (1536, 1)]   # (d_out, which input)
+    Gs = [synth.draw_gradient(d_out, inputs[k]["Q"], inputs[k]["ev"], seed=620 + i, device=DEV)
+          for i, (d_out, k) in enumerate(shapes)]
+    for block in (False, True):
+        sc = fg.SCALE_BLOCK128 if block else fg.SCALE_TENSOR
+        Ws = [torch.empty_like(G) for G in Gs]
+        layers = [fg.Layer(G, factor=facs[k], W_out=W, block128=block)
+                  for G, (_, k), W in zip(Gs, shapes, Ws)]
+        fg.gift_whiten_quantize(layers, scaling=sc)
+        fg.gift_dequant_unwhiten(layers, scaling=sc)
+        for L, W, (d_out, k) in zip(layers, Ws, shapes):
+            say("  %d x %d block=%s" % (d_out, L.G.shape[1], block))
+            U, alpha, beta, dw, du = factor_host(facs[k])
+            G = host(L.G)
+            Wg = host(W)
+            assert rel_fro(Wg, og.whiten_with(G, U, alpha, dw)) <= 1e-5
+            codes, inv_o, _ = og.quantize(Wg, block)
+            assert np.array_equal(host(L.q), codes)
+            inv = host(L.inv_scale).reshape(np.shape(inv_o))
+            assert np.array_equal(inv, inv_o)
+            ref = og.unwhiten_with(og.dequantize(codes, inv_o, block), U, beta, du)
+            assert rel_fro(host(L.G_hat), ref) <= 1e-5
+
+
+def test_block4096_shapes_sampled_rows():
+    say("4096 / 11008 shapes: refresh d 4096 and 11008 (16384 tokens), sampled rows")
+    w = synth.llama_block(hidden=4096, mlp=11008, tokens=16384, exponent=1.5)
+    specs = [next(s for s in w.inputs if s.d_in == 4096), next(s for s in w.inputs if s.d_in == 11008)]
+    inputs, facs = _refresh_inputs(specs, seed=710)
+    _check_refresh_properties(inputs[0], facs[0])
+    shapes = [(11008, 0), (4096, 1)]   # gate (11008 x 4096), down (4096 x 11008)
+    rng = np.random.default_rng(7)
+    for i, (d_out, k) in enumerate(shapes):
+        G = synth.draw_gradient(d_out, inputs[k]["Q"], inputs[k]["ev"], seed=720 + i, device=DEV)
+        W = torch.empty_like(G)
+        L = fg.Layer(G, factor=facs[k], W_out=W)
+        fg.gift_whiten_quantize([L])
+        fg.gift_dequant_unwhiten([L])
+        say("  %d x %d sampled" % (d_out, G.shape[1]))
+        rows = np.sort(rng.choice(d_out, 192, replace=False))
+        rows = np.unique(np.concatenate([rows, [0, d_out - 1]]))
+        U, alpha, beta, dw, du = factor_host(facs[k])
+        Gr = host(G[rows])
+        Wr = host(W[rows])
+        assert rel_fro(Wr, og.whiten_with(Gr, U, alpha, dw)) <= 1e-5
+        # the tensor scale from the device's whole W, codes of the sampled rows
+        amax = og.amax(host(W))
+        scale, inv, _ = og.scale_from_amax(amax)
+        assert host(L.inv_scale)[0] == inv
+        codes = e4m3.encode((Wr * scale).astype(np.float32))
+        qr = host(L.q[rows])
+        assert np.array_equal(qr, codes)
+        ref = og.unwhiten_with(og.dequantize_tensor(qr, inv), U, beta, du)
+        assert rel_fro(host(L.G_hat[rows]), ref) <= 1e-5
