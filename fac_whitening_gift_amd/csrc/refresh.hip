@@ -914,50 +914,70 @@ __device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, doubl
   }
 }
 
-// 4e. Q = In R^-1 by forward substitution along each row (one row per
-// thread): q_j = (in_j - sum_{k<j} q_k R[k][j]) / R[j][j], fp64, with R and
-// the reciprocal diagonal from k_chol in LDS (broadcast reads).  Replaces an
-// explicit inverse: the rows are independent, so no step needs a barrier.
-// grid: (max d / kT, inputs).  which: 0 = Q1 = Y R^-1, 1 = Q = Q1 R^-1,
+// 4e. Q = In R^-1 by forward substitution along each row, fp64, with R and
+// the reciprocal diagonal from k_chol in LDS:
+//   q_j = (in_j - sum_{k<j} q_k R[k][j]) / R[j][j].
+// A row belongs to a quad of lanes; lane p keeps the running sums of the
+// columns j = p mod 4 in registers.  At step j the lane holding column j
+// finishes q_j, a DPP quad permutation hands it to the other three, and every
+// lane subtracts q_j R[j][.] from its later columns (column-oriented
+// substitution).  Rows are independent, so no step needs a barrier.
+// grid: (max d * 4 / kT, inputs).  which: 0 = Q1 = Y R^-1, 1 = Q = Q1 R^-1,
 // 2 = Q = Y R^-1
 // ---------------------------------------------------------------------------
+// value of lane `src` (0..3) of this lane's quad
+template <int src>
+__device__ __forceinline__ double quad_bcast(double v) {
+  constexpr int ctrl = src | (src << 2) | (src << 4) | (src << 6);  // quad_perm
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)b, ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), ctrl, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 template <int W>
 __global__ __launch_bounds__(kT) void k_solve(RGroup g, int which) {
+  constexpr int kM = W / 4;  // columns per lane
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d;
-  __shared__ double sR[W][W];
+  __shared__ double sR[W][W + 1];
   for (int e = threadIdx.x; e < W * W; e += kT) {
     const int a = e / W, b = e % W;
     sR[a][b] = a <= b ? R.T[a * kW + b] : 0.0;
   }
   __syncthreads();
-  const int i = blockIdx.x * kT + threadIdx.x;
-  if (i >= d) return;
-  const float* __restrict__ in = (which == 1 ? R.Q1 : R.Y) + (int64_t)i * W;
-  float* __restrict__ out = (which == 0 ? R.Q1 : R.Q) + (int64_t)i * W;
-  double q[W];
+  const int t = blockIdx.x * kT + threadIdx.x;
+  const int i = t >> 2, p = t & 3;
+  // rows past d (whole quads: kT is a multiple of 4) load row d - 1 and store nothing
+  const int ii = i < d ? i : d - 1;
+  const float* __restrict__ in = (which == 1 ? R.Q1 : R.Y) + (int64_t)ii * W;
+  float* __restrict__ out = (which == 0 ? R.Q1 : R.Q) + (int64_t)ii * W;
+  double acc[kM];
 #pragma unroll
-  for (int j = 0; j < W; j += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(in + j);
-    q[j] = v.x;
-    q[j + 1] = v.y;
-    q[j + 2] = v.z;
-    q[j + 3] = v.w;
-  }
+  for (int m = 0; m < kM; ++m) acc[m] = in[4 * m + p];
 #pragma unroll
   for (int j = 0; j < W; ++j) {
-    double s0 = q[j], s1 = 0.0;
-#pragma unroll
-    for (int k = 0; k < j; ++k) {
-      if (k & 1) s1 -= q[k] * sR[k][j];
-      else s0 -= q[k] * sR[k][j];
+    const int mj = j >> 2;
+    // the owner (p == j % 4) finishes q_j; every lane of the quad gets it
+    const double mine = acc[mj] * sR[j][j];
+    double qj;
+    switch (j & 3) {
+      case 0: qj = quad_bcast<0>(mine); break;
+      case 1: qj = quad_bcast<1>(mine); break;
+      case 2: qj = quad_bcast<2>(mine); break;
+      default: qj = quad_bcast<3>(mine); break;
     }
-    q[j] = (s0 + s1) * sR[j][j];
-  }
+    if (p == (j & 3)) acc[mj] = qj;
 #pragma unroll
-  for (int j = 0; j < W; j += 4)
-    *reinterpret_cast<float4*>(out + j) =
-        make_float4((float)q[j], (float)q[j + 1], (float)q[j + 2], (float)q[j + 3]);
+    for (int m = mj; m < kM; ++m) {
+      const int col = 4 * m + p;
+      const double nv = acc[m] - qj * sR[j][col];
+      acc[m] = col > j ? nv : acc[m];
+    }
+  }
+  if (i < d)
+#pragma unroll
+    for (int m = 0; m < kM; ++m) out[4 * m + p] = (float)acc[m];
 }
 
 // ---------------------------------------------------------------------------
@@ -1120,7 +1140,7 @@ void chol(const RGroup& g, int nb, hipStream_t st) {
 }
 
 void solve(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
-  const dim3 grid((unsigned)((maxd + kT - 1) / kT), nb);
+  const dim3 grid((unsigned)((4 * maxd + kT - 1) / kT), nb);
   if (g.w == 32) k_solve<32><<<grid, kT, 0, st>>>(g, which);
   else if (g.w == 48) k_solve<48><<<grid, kT, 0, st>>>(g, which);
   else k_solve<64><<<grid, kT, 0, st>>>(g, which);
