@@ -719,6 +719,14 @@ __device__ double block_sum(double v, double* red) {
 // ---------------------------------------------------------------------------
 constexpr int kCT = 1024;
 
+// 1/x for finite x != 0: the hardware estimate and two Newton steps
+__device__ __forceinline__ double rcp_f64(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+  y = y * (2.0 - x * y);
+  y = y * (2.0 - x * y);
+  return y;
+}
+
 __device__ __forceinline__ double rsqrt_f64(double p) {
   const double h = 0.5 * p;
   double y = __builtin_amdgcn_rsq(p);
@@ -853,6 +861,20 @@ __global__ __launch_bounds__(kT) void k_apply(RGroup g, int which) {
 // sweep tolerance.  In a round every 2 x 2 block of B is rotated on both
 // sides by one thread, and the pair of columns of V by others, so a round
 // takes two barriers.  All kST threads call it.
+// the round-robin schedule: pair i of round r (W/2 disjoint pairs per round,
+// every pair once in W - 1 rounds), smaller index first
+template <int W>
+__device__ __forceinline__ void pair_of(int round, int i, int& p, int& q) {
+  constexpr int kM = W - 1;
+  p = i == 0 ? kM : (round + i) % kM;
+  q = i == 0 ? round : (round - i + kM) % kM;
+  if (p > q) {
+    const int t = p;
+    p = q;
+    q = t;
+  }
+}
+
 template <int W>
 __device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, double* rs, int* rp,
                        int* rq, double* red) {
@@ -872,16 +894,23 @@ __device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, doubl
     for (int round = 0; round < kM; ++round) {
       if (threadIdx.x < kP) {
         const int i = threadIdx.x;
-        int p = i == 0 ? kM : (round + i) % kM;
-        int q = i == 0 ? round : (round - i + kM) % kM;
-        if (p > q) { const int t = p; p = q; q = t; }
+        int p, q;
+        pair_of<W>(round, i, p, q);
         const double apq = B[p][q], app = B[p][p], aqq = B[q][q];
         double c = 1.0, s = 0.0;
         if (apq != 0.0) {
+          // t = sign(tau) / (|tau| + sqrt(1 + tau^2)), c = 1 / sqrt(1 + t^2), with
+          // reciprocals and reciprocal square roots as estimates + Newton steps
           const double tau = (aqq - app) / (2.0 * apq);
-          const double t = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau))
-                                      : -1.0 / (-tau + sqrt(1.0 + tau * tau));
-          c = 1.0 / sqrt(1.0 + t * t);
+          double t;
+          if (fabs(tau) < 1e100) {
+            const double u = fma(tau, tau, 1.0);
+            t = rcp_f64(fabs(tau) + u * rsqrt_f64(u));
+            if (tau < 0.0) t = -t;
+          } else {
+            t = 0.5 / tau;
+          }
+          c = rsqrt_f64(fma(t, t, 1.0));
           s = t * c;
         }
         rp[i] = p; rq[i] = q; rc[i] = c; rs[i] = s;
@@ -1116,6 +1145,7 @@ __global__ __launch_bounds__(kST) void k_blk_eig(RGroup g) {
   for (int e = threadIdx.x; e < W * W; e += kST) {
     const int a = e / W, b = e % W;
     double sw = 0.0, su = 0.0;
+#pragma unroll 4
     for (int k = 0; k < W; ++k) {
       const double vv = V[a][k] * V[b][k];
       sw += vv * fw[k];
