@@ -153,6 +153,67 @@ __device__ __forceinline__ float4 mx_decode4(uint32_t c16, uint32_t code) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32-accurate products on the bf16 matrix cores: every fp32 operand is split
+// into three bf16 parts, x = x1 + x2 + x3 exactly, and the six partial
+// products of weight >= 2^-16 are accumulated in fp32.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// x = s[0] + s[1] + s[2] exactly (RNE at each level; the remainders are exact)
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8 (&s)[3]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 a = (__bf16)x[i];
+    const float r = x[i] - (float)a;
+    const __bf16 b = (__bf16)r;
+    const float r2 = r - (float)b;
+    s[0][i] = a;
+    s[1][i] = b;
+    s[2][i] = (__bf16)r2;
+  }
+}
+
+// acc += (a0 + a1 + a2)(b0 + b1 + b2), products of weight >= 2^-16
+__device__ __forceinline__ f32x4 mfma3x3(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 acc) {
+  acc = mfma(a[2], b[0], acc);
+  acc = mfma(a[1], b[1], acc);
+  acc = mfma(a[0], b[2], acc);
+  acc = mfma(a[1], b[0], acc);
+  acc = mfma(a[0], b[1], acc);
+  return mfma(a[0], b[0], acc);
+}
+
+// The six products of mfma3x3, issued round-robin over N independent
+// accumulators (acc[i] += a[ia[i]] * b[ib[i]]) so the matrix pipe never waits
+// on one accumulator's previous product.
+template <int N>
+__device__ __forceinline__ void mfma3x3_n(const bf16x8 (*const (&a)[N])[3],
+                                          const bf16x8 (*const (&b)[N])[3], f32x4 (&acc)[N]) {
+  constexpr int ia[6] = {2, 1, 0, 1, 0, 0};
+  constexpr int ib[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+  for (int p = 0; p < 6; ++p)
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = mfma((*a[i])[ia[p]], (*b[i])[ib[p]], acc[i]);
+}
+
+// acc += (a0 + a1 + a2) b  (b exact in bf16)
+__device__ __forceinline__ f32x4 mfma3x1(const bf16x8 (&a)[3], const bf16x8& b, f32x4 acc) {
+  acc = mfma(a[2], b, acc);
+  acc = mfma(a[1], b, acc);
+  return mfma(a[0], b, acc);
+}
+
+// ---------------------------------------------------------------------------
 // reductions (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -14,10 +14,11 @@
 //   2. k_syrk_reduce: fixed-order sum of the partials, / N; the tile and its
 //      mirror image are written row-contiguous through LDS.  k_trace: tr(A).
 //   3. k_sketch: Omega from Philox4x32-10 + Box-Muller (unless given).
-//   4. subspace iteration: Y = A Q on fp32 MFMA as partial products over
-//      disjoint K ranges (k_gemm_aq), Q = orth(Y) by CholeskyQR (Fukaya et
-//      al.) with an fp64 Gram matrix (k_gram, which also sums the partials,
-//      k_chol, k_solve); the final basis gets a second CholeskyQR pass.
+//   4. subspace iteration: Y = A Q on bf16 MFMA with three-way split operands
+//      (k_pack_q, k_gemm_aq), as partial products over disjoint K ranges;
+//      Q = orth(Y) by CholeskyQR (Fukaya et al.) with an fp64 Gram matrix
+//      (k_gram, which also sums the partials, k_chol, k_solve); the final
+//      basis gets a second CholeskyQR pass.
 //   5. Rayleigh-Ritz: B = Q^T A Q (k_gemm_aq + k_gram), cyclic Jacobi on B in
 //      one workgroup per input (Golub & Van Loan, sym.schur2 rotations,
 //      round-robin ordering: 32 disjoint rotations at once), sort,
@@ -49,8 +50,6 @@ constexpr int kMaxSweeps = 20;
 // norm ~3e-8 of the total, below the fp32 rounding of U and theta
 constexpr double kJacobiTol = 1e-15;
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -75,7 +74,7 @@ SyrkPlan syrk_plan(int64_t d, int64_t n, int n_inputs) {
 }
 
 struct WsLayout {
-  size_t A, part, om, y, yp, q, q1, gram, T, tr, total;
+  size_t A, part, om, y, yp, qp, q, q1, gram, T, tr, total;
 };
 
 WsLayout ws_layout(int64_t d, int64_t n, int w, int n_inputs) {
@@ -87,6 +86,7 @@ WsLayout ws_layout(int64_t d, int64_t n, int w, int n_inputs) {
   L.om = o; o += al((size_t)d * w * 4);
   L.y = o; o += al((size_t)d * w * 4);
   L.yp = o; o += al((size_t)kYSplit * d * w * 4);
+  L.qp = o; o += al((size_t)((d + 31) / 32) * (kW / 16) * 3 * 64 * 16);
   L.q = o; o += al((size_t)d * w * 4);
   L.q1 = o; o += al((size_t)d * w * 4);
   L.gram = o; o += al((size_t)kGramParts * kW * kW * 8);
@@ -105,6 +105,7 @@ struct RIn {
   float* om_ws;
   float* Y;
   float* Yp;     // kYSplit partial products A Q, each d x w
+  uint4* QP;     // the right operand of the next A Q, split in MFMA packs
   float* Q;
   float* Q1;
   double* gram;
@@ -503,21 +504,46 @@ __global__ __launch_bounds__(kT) void k_sketch(RGroup g) {
 }
 
 // ---------------------------------------------------------------------------
-// 4a. Y = A Q  (A d x d fp32 symmetric, Q d x w) on v_mfma_f32_16x16x4_f32,
-// as kYSplit partial products over disjoint K ranges (k_gram sums them in
-// split order).  Workgroup: 16 rows of one partial; its 4 waves split the
-// K range further and are summed in wave order through LDS.  Lane group g's
-// k-slot in MFMA s of a 16-wide K chunk is k0 + 4g + s.
-// grid: (max d / 16, kYSplit, inputs).  which: 0 = Y = A Om, 1 = Y = A Q
+// 4a. Y = A Q  (A d x d fp32 symmetric, Q d x w) on v_mfma_f32_16x16x32_bf16
+// with both operands split three ways (fp32-level products), as kYSplit
+// partial products over disjoint K ranges (k_gram sums them in split order).
+// k_pack_q puts Q in the B-operand layout first: for K chunk c (32 rows of
+// Q), column tile t and split s, element i of lane l (r16 = l % 16,
+// g = l / 16) = Q[32c + 8g + i][16t + r16], at ((c T + t) 3 + s) 64 + l
+// (T = w / 16).  In k_gemm_aq lane l holds A[row0 + r16][32c + 8g .. +7],
+// split as it is loaded.  Workgroup: 16 rows of one partial; its 4 waves
+// split the K range further and are summed in wave order through LDS.
+// Rows of Q past d (d % 32 == 16) are zero, and so are A's columns there.
 // ---------------------------------------------------------------------------
+// grid: (max chunks * T * 64 / kT, inputs).  which: 0 = Omega, 1 = Q
+__global__ __launch_bounds__(kT) void k_pack_q(RGroup g, int which) {
+  const RIn& R = g.r[blockIdx.y];
+  const int d = R.d, w = g.w, nt = w / 16, nch = (d + 31) / 32;
+  const int e = blockIdx.x * kT + threadIdx.x;
+  if (e >= nch * nt * 64) return;
+  const float* __restrict__ Q = which == 0 ? R.om : R.Q;
+  const int lane = e & 63, ct = e >> 6, c = ct / nt, t = ct % nt;
+  const int r16 = lane & 15, gq = lane >> 4;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = 32 * c + 8 * gq + i;
+    v[i] = k < d ? Q[(int64_t)k * w + 16 * t + r16] : 0.f;
+  }
+  bf16x8 sp[3];
+  split3(v, sp);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) R.QP[(size_t)(ct * 3 + s) * 64 + lane] = __builtin_bit_cast(uint4, sp[s]);
+}
+
 constexpr int kGemmWaves = 4;
 
-__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which) {
+// grid: (max d / 16, kYSplit, inputs)
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g) {
   const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
   if ((int)blockIdx.x * 16 >= d) return;
   const float* __restrict__ A = R.A;
-  const float* __restrict__ Q = which == 0 ? R.om : R.Q;
   __shared__ float red[kGemmWaves][16][kW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, gq = lane >> 4;
@@ -526,31 +552,36 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which
   f32x4 acc[kW / 16];
 #pragma unroll
   for (int t = 0; t < kW / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int kchunks = d / 16, slice = blockIdx.y * kGemmWaves + wave;
+  const int kchunks = (d + 31) / 32, slice = blockIdx.y * kGemmWaves + wave;
   constexpr int kSlices = kYSplit * kGemmWaves;
   const int kc_begin = slice * kchunks / kSlices, kc_end = (slice + 1) * kchunks / kSlices;
   const float* arow = A + (int64_t)(row0 + r16) * d;
-  // one K chunk of 16: this lane's 4 values of A's row and its 4 x 4 of Q
+  // one K chunk of 32: this lane's 8 values of A's row and its packs of Q
   struct Chunk {
-    float4 a;
-    float q[4][kW / 16];
+    float4 a[2];
+    uint4 q[kW / 16][3];
   };
   auto load = [&](int kc, Chunk& c) {
-    const int k0 = 16 * kc + 4 * gq;
-    c.a = *reinterpret_cast<const float4*>(arow + k0);
+    const int k0 = 32 * kc + 8 * gq;
+    const bool in = k0 < d;  // d % 16 == 0: a lane's 8 columns are all in or all out
+    c.a[0] = in ? *reinterpret_cast<const float4*>(arow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    c.a[1] = in ? *reinterpret_cast<const float4*>(arow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int t = 0; t < kW / 16; ++t)
 #pragma unroll
-      for (int t = 0; t < kW / 16; ++t)
-        c.q[s][t] = t < ntile ? Q[(int64_t)(k0 + s) * w + 16 * t + r16] : 0.f;
+      for (int s = 0; s < 3; ++s)
+        c.q[t][s] = t < ntile ? R.QP[(size_t)((kc * ntile + t) * 3 + s) * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
   };
   auto comp = [&](const Chunk& c) {
-    const float av[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
+    const float v[8] = {c.a[0].x, c.a[0].y, c.a[0].z, c.a[0].w, c.a[1].x, c.a[1].y, c.a[1].z, c.a[1].w};
+    bf16x8 sa[3];
+    split3(v, sa);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < kW / 16; ++t)
-        if (t < ntile) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], c.q[s][t], acc[t], 0, 0, 0);
+    for (int t = 0; t < kW / 16; ++t)
+      if (t < ntile) {
+        const bf16x8 sb[3] = {as_bf16x8(c.q[t][0]), as_bf16x8(c.q[t][1]), as_bf16x8(c.q[t][2])};
+        acc[t] = mfma3x3(sa, sb, acc[t]);
+      }
   };
   // two-stage pipeline; the prefetch is unconditional (the last chunk is
   // loaded twice) so the compiler waits for exactly the chunk in use
@@ -567,6 +598,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g, int which
       if (++kc == kc_end) break;
     }
   }
+  // D layout: lane holds rows 4 gq .. 4 gq + 3 of column r16 of each 16x16 tile
 #pragma unroll
   for (int t = 0; t < kW / 16; ++t)
     if (t < ntile)
@@ -1169,6 +1201,11 @@ void chol(const RGroup& g, int nb, hipStream_t st) {
   else k_chol<64><<<nb, kCT, 0, st>>>(g);
 }
 
+void pack_q(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
+  const int n = (maxd + 31) / 32 * (g.w / 16) * 64;
+  k_pack_q<<<dim3((unsigned)((n + kT - 1) / kT), nb), kT, 0, st>>>(g, which);
+}
+
 void solve(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
   const dim3 grid((unsigned)((4 * maxd + kT - 1) / kT), nb);
   if (g.w == 32) k_solve<32><<<grid, kT, 0, st>>>(g, which);
@@ -1294,6 +1331,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       x.om = r.sketch ? r.sketch : x.om_ws;
       x.Y = reinterpret_cast<float*>(base + L.y);
       x.Yp = reinterpret_cast<float*>(base + L.yp);
+      x.QP = reinterpret_cast<uint4*>(base + L.qp);
       x.Q = reinterpret_cast<float*>(base + L.q);
       x.Q1 = reinterpret_cast<float*>(base + L.q1);
       x.gram = reinterpret_cast<double*>(base + L.gram);
@@ -1351,12 +1389,14 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
     // 2. subspace iteration: Y = A Omega, then power_steps x (Q = orth(Y); Y = A Q)
     const dim3 rows(maxd / 16, nb), grams(kGramParts * 4, nb), gemm(maxd / 16, kYSplit, nb);
-    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 0);
+    pack_q(g, 0, maxd, nb, st);
+    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
     for (int s = 0; s < power_steps; ++s) {
       k_gram<<<grams, kT, 0, st>>>(g, 0);
       chol(g, nb, st);
       solve(g, 2, maxd, nb, st);  // Q = Y R^-1
-      k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 1);
+      pack_q(g, 1, maxd, nb, st);
+      k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
     }
     // final basis: CholeskyQR2 of Y
     k_gram<<<grams, kT, 0, st>>>(g, 0);
@@ -1366,7 +1406,8 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     chol(g, nb, st);
     solve(g, 1, maxd, nb, st);  // Q = Q1 R^-1
     // 3. Rayleigh-Ritz on B = Q^T A Q
-    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g, 1);  // Y = A Q
+    pack_q(g, 1, maxd, nb, st);
+    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);  // Y = A Q
     k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
     ritz(g, nb, st);
     k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V
