@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include <string>
+#include <type_traits>
 
 #include "device.hpp"
 
@@ -68,6 +69,9 @@ SyrkPlan syrk_plan(int64_t d, int64_t n, int n_inputs) {
   const int64_t maxs = steps / 8 > 0 ? steps / 8 : 1;      // at least 8 K-steps each
   int64_t s = want < maxs ? want : maxs;
   if (s < 1) s = 1;
+  // a workgroup's tokens are one raw buffer of at most 2^31 bytes
+  const int64_t cap = ((int64_t(1) << 31) / (2 * d)) / kKStepB;
+  if ((steps + s - 1) / s > cap) s = (steps + cap - 1) / cap;
   p.chunk = ((steps + s - 1) / s) * kKStepB;
   p.nsplit = (int)((n + p.chunk - 1) / p.chunk);
   return p;
@@ -210,14 +214,28 @@ struct SyrkRegs {
   uint32_t v[16];
 };
 
-__device__ __forceinline__ void syrk_fetch(SyrkRegs& r, const uint16_t* X, int64_t n0,
-                                           int64_t n_end, int c0, int d) {
-  const int cp = threadIdx.x & 63, tg = threadIdx.x >> 6;
-  const int col = c0 + 2 * cp;
+// The tokens of one step are a raw buffer that starts at the step's first
+// token and ends at the workgroup's last (size 0 past it): a lane's load of
+// token row 16 tg + s of the step sits at byte s 2d + voff, voff =
+// (16 tg d + col) 2, and rows past the range read as zero in the buffer unit,
+// so the loads need no branch and can not leave X.  Columns at or beyond d
+// are zeroed by colok.
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t syrk_rsrc(const uint16_t* X, int64_t n0,
+                                                            int64_t n_end, int d) {
+  const int64_t rows = n_end > n0 ? n_end - n0 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X + (n_end > n0 ? n0 : n_end) * d),
+                                           (short)0, (int)((uint32_t)rows * 2u * (uint32_t)d),
+                                           (int)kRawBufferWord3);
+}
+
+__device__ __forceinline__ void syrk_fetch(SyrkRegs& r, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                           uint32_t rowbytes, bool colok) {
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    const int64_t n = n0 + 16 * tg + s;
-    r.v[s] = (n < n_end && col < d) ? *reinterpret_cast<const uint32_t*>(X + n * d + col) : 0u;
+    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + (uint32_t)s * rowbytes, 0, 0);
+    r.v[s] = colok ? v : 0u;
   }
 }
 
@@ -241,7 +259,7 @@ __device__ __forceinline__ void syrk_stash(const SyrkRegs& r, uint16_t (*lds)[kK
 }
 
 // grid: (max npairs, max nsplit, inputs of this dtype); idx maps z -> input
-__global__ __launch_bounds__(kT) void k_syrk_bf16(RGroup g, int4 idx) {
+__global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g, int4 idx) {
   const int zi = blockIdx.z == 0 ? idx.x : blockIdx.z == 1 ? idx.y : blockIdx.z == 2 ? idx.z : idx.w;
   const RIn& R = g.r[zi];
   if ((int)blockIdx.x >= R.npairs || (int)blockIdx.y >= R.nsplit) return;
@@ -250,7 +268,6 @@ __global__ __launch_bounds__(kT) void k_syrk_bf16(RGroup g, int4 idx) {
   decode_pair(blockIdx.x, R.nb, bi, bj);
   const int d = R.d;
   const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
-  const bool diag = bi == bj;
   const int64_t n_begin = (int64_t)blockIdx.y * R.chunk;
   const int64_t n_end = min(R.N, n_begin + R.chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -263,20 +280,34 @@ __global__ __launch_bounds__(kT) void k_syrk_bf16(RGroup g, int4 idx) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int steps = (int)((n_end - n_begin + kKStepB - 1) / kKStepB);
-  SyrkRegs ra, rb;
+  // Two register sets: while step st is multiplied out of LDS, the tokens of
+  // step st + 1 (issued one step earlier) are stashed into the other LDS
+  // buffer and those of step st + 2 are in flight, so a load has two steps
+  // of MFMA work to arrive.  Set k holds the steps st with st % 2 == k.
+  SyrkRegs ra[2], rb[2];
+  const int cpl = 2 * (threadIdx.x & 63), tgl = threadIdx.x >> 6;
+  const uint32_t rowbytes = 2u * (uint32_t)d;
+  const uint32_t va = (uint32_t)(16 * tgl) * rowbytes + 2u * (uint32_t)(ci0 + cpl);
+  const uint32_t vb = (uint32_t)(16 * tgl) * rowbytes + 2u * (uint32_t)(cj0 + cpl);
+  const bool oka = ci0 + cpl < d, okb = cj0 + cpl < d;
   if (steps > 0) {
-    syrk_fetch(ra, X, n_begin, n_end, ci0, d);
-    if (!diag) syrk_fetch(rb, X, n_begin, n_end, cj0, d);
-    syrk_stash(ra, sb[0].a);
-    if (!diag) syrk_stash(rb, sb[0].b);
+    const __amdgpu_buffer_rsrc_t r0 = syrk_rsrc(X, n_begin, n_end, d);
+    const __amdgpu_buffer_rsrc_t r1 = syrk_rsrc(X, n_begin + kKStepB, n_end, d);
+    syrk_fetch(ra[0], r0, va, rowbytes, oka);
+    syrk_fetch(rb[0], r0, vb, rowbytes, okb);
+    syrk_fetch(ra[1], r1, va, rowbytes, oka);
+    syrk_fetch(rb[1], r1, vb, rowbytes, okb);
+    syrk_stash(ra[0], sb[0].a);
+    syrk_stash(rb[0], sb[0].b);
   }
   __syncthreads();
-  for (int st = 0; st < steps; ++st) {
-    const int64_t nn = n_begin + (int64_t)(st + 1) * kKStepB;  // beyond n_end: zeros
-    syrk_fetch(ra, X, nn, n_end, ci0, d);
-    if (!diag) syrk_fetch(rb, X, nn, n_end, cj0, d);
-    const SyrkBuf& cur = sb[st & 1];
-    const uint16_t (*tb)[kKStepB + 8] = diag ? cur.a : cur.b;
+  auto step = [&](int st, auto K) {
+    constexpr int k = decltype(K)::value;  // st % 2
+    const __amdgpu_buffer_rsrc_t rn = syrk_rsrc(X, n_begin + (int64_t)(st + 2) * kKStepB, n_end, d);
+    syrk_fetch(ra[k], rn, va, rowbytes, oka);
+    syrk_fetch(rb[k], rn, vb, rowbytes, okb);
+    const SyrkBuf& cur = sb[k];
+    const uint16_t (*tb)[kKStepB + 8] = cur.b;
 #pragma unroll
     for (int ks = 0; ks < kKStepB / 32; ++ks) {
       bf16x8 fa[4], fb[4];
@@ -291,10 +322,14 @@ __global__ __launch_bounds__(kT) void k_syrk_bf16(RGroup g, int4 idx) {
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
     }
-    SyrkBuf& nxt = sb[(st + 1) & 1];
-    syrk_stash(ra, nxt.a);
-    if (!diag) syrk_stash(rb, nxt.b);
+    SyrkBuf& nxt = sb[k ^ 1];
+    syrk_stash(ra[k ^ 1], nxt.a);
+    syrk_stash(rb[k ^ 1], nxt.b);
     __syncthreads();
+  };
+  for (int st = 0; st < steps; st += 2) {
+    step(st, std::integral_constant<int, 0>{});
+    if (st + 1 < steps) step(st + 1, std::integral_constant<int, 1>{});
   }
   // D layout: lane holds rows 4gq..4gq+3 of column r16 of each 16x16 tile
   float* out = R.part + ((size_t)blockIdx.y * R.npairs + blockIdx.x) * kSyrkTile * kSyrkTile;
