@@ -59,13 +59,19 @@ struct SyrkPlan {
   int64_t chunk;
 };
 
-SyrkPlan syrk_plan(int64_t d, int64_t n, int n_inputs) {
+// Token split of the covariance tiles: a launch covers the inputs of one
+// group (batch_pairs upper-triangle tiles in all), and each tile's tokens are
+// split so the launch holds about kSyrkTarget workgroups (two per CU, twice
+// over), with at least 8 steps per workgroup.
+constexpr int64_t kSyrkTarget = 1024;
+
+SyrkPlan syrk_plan(int64_t d, int64_t n, int64_t batch_pairs) {
   SyrkPlan p;
   p.nb = (int)((d + kSyrkTile - 1) / kSyrkTile);
   p.npairs = p.nb * (p.nb + 1) / 2;
   const int64_t steps = (n + kKStepB - 1) / kKStepB;
-  const int64_t tiles = (int64_t)p.npairs * (n_inputs > 0 ? n_inputs : 1);
-  const int64_t want = (512 + tiles - 1) / tiles;          // about 2 workgroups per CU
+  const int64_t tiles = batch_pairs > p.npairs ? batch_pairs : p.npairs;
+  const int64_t want = (kSyrkTarget + tiles - 1) / tiles;
   const int64_t maxs = steps / 8 > 0 ? steps / 8 : 1;      // at least 8 K-steps each
   int64_t s = want < maxs ? want : maxs;
   if (s < 1) s = 1;
@@ -81,8 +87,8 @@ struct WsLayout {
   size_t A, part, om, y, yp, qp, q, q1, gram, T, tr, total;
 };
 
-WsLayout ws_layout(int64_t d, int64_t n, int w, int n_inputs) {
-  const SyrkPlan p = syrk_plan(d, n, n_inputs);
+WsLayout ws_layout(int64_t d, int64_t n, int w, int64_t batch_pairs) {
+  const SyrkPlan p = syrk_plan(d, n, batch_pairs);
   WsLayout L;
   size_t o = 0;
   L.A = o; o += al((size_t)d * d * 4);
@@ -130,6 +136,11 @@ struct RGroup {
   int w;
   float eps;
   int mode;
+  // bf16 covariance work list: input sy_in[k] owns workgroups
+  // sy_begin[k] .. sy_begin[k + 1] - 1 (npairs x nsplit of them)
+  int sy_n;
+  int sy_in[kMaxGroup];
+  int sy_begin[kMaxGroup];
   RIn r[kMaxGroup];
 };
 
@@ -258,17 +269,22 @@ __device__ __forceinline__ void syrk_stash(const SyrkRegs& r, uint16_t (*lds)[kK
   }
 }
 
-// grid: (max npairs, max nsplit, inputs of this dtype); idx maps z -> input
-__global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g, int4 idx) {
-  const int zi = blockIdx.z == 0 ? idx.x : blockIdx.z == 1 ? idx.y : blockIdx.z == 2 ? idx.z : idx.w;
-  const RIn& R = g.r[zi];
-  if ((int)blockIdx.x >= R.npairs || (int)blockIdx.y >= R.nsplit) return;
+// grid: one workgroup per (tile, token range) of every bf16 input of the
+// group, tiles of one token range consecutive
+__global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
+  int k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < g.sy_n && (int)blockIdx.x >= g.sy_begin[i]) k = i;
+  const RIn& R = g.r[g.sy_in[k]];
+  const int local = (int)blockIdx.x - g.sy_begin[k];
+  const int pair = local % R.npairs, split = local / R.npairs;
   __shared__ SyrkBuf sb[2];
   int bi, bj;
-  decode_pair(blockIdx.x, R.nb, bi, bj);
+  decode_pair(pair, R.nb, bi, bj);
   const int d = R.d;
   const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
-  const int64_t n_begin = (int64_t)blockIdx.y * R.chunk;
+  const int64_t n_begin = (int64_t)split * R.chunk;
   const int64_t n_end = min(R.N, n_begin + R.chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wi = wave >> 1, wj = wave & 1;
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g, int4 idx) {
     if (st + 1 < steps) step(st + 1, std::integral_constant<int, 1>{});
   }
   // D layout: lane holds rows 4gq..4gq+3 of column r16 of each 16x16 tile
-  float* out = R.part + ((size_t)blockIdx.y * R.npairs + blockIdx.x) * kSyrkTile * kSyrkTile;
+  float* out = R.part + ((size_t)split * R.npairs + pair) * kSyrkTile * kSyrkTile;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1259,18 +1275,31 @@ void ritz(const RGroup& g, int nb, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // host orchestration
 // ---------------------------------------------------------------------------
+// upper-triangle covariance tiles of the group (kMaxGroup inputs in call
+// order) that input i belongs to
+int64_t batch_pairs(const gift_refresh_input* in, int n, int i) {
+  const int b0 = i / kMaxGroup * kMaxGroup, b1 = n < b0 + kMaxGroup ? n : b0 + kMaxGroup;
+  int64_t t = 0;
+  for (int j = b0; j < b1; ++j) {
+    const int64_t nb = (in[j].factor->d_in + kSyrkTile - 1) / kSyrkTile;
+    t += nb * (nb + 1) / 2;
+  }
+  return t;
+}
+
 size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int width) {
   size_t t = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < n; ++i)
     if (!in[i].factor || in[i].factor->d_in < 1 || in[i].n_tokens < 1) return 0;
-    t += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, n).total;
-  }
+  for (int i = 0; i < n; ++i)
+    t += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_pairs(in, n, i)).total;
   return t;
 }
 
 size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int, int width) {
   if (d_in < 1 || n_tokens < 1 || width < 1) return 0;
-  return ws_layout(d_in, n_tokens, width, 1).total;
+  const int64_t nb = (d_in + kSyrkTile - 1) / kSyrkTile;
+  return ws_layout(d_in, n_tokens, width, nb * (nb + 1) / 2).total;
 }
 
 gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t st,
@@ -1351,13 +1380,15 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     g.eps = damp_eps;
     g.mode = damping_mode;
     char* base = static_cast<char*>(ws);
-    for (int i = 0; i < b0; ++i) base += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, n).total;
+    for (int i = 0; i < b0; ++i)
+      base += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_pairs(in, n, i)).total;
     int maxd = 0, maxpairs = 0, maxsplit = 0;
     for (int i = 0; i < nb; ++i) {
       const gift_refresh_input& r = in[b0 + i];
       const int d = r.factor->d_in;
-      const WsLayout L = ws_layout(d, r.n_tokens, width, n);
-      const SyrkPlan p = syrk_plan(d, r.n_tokens, n);
+      const int64_t bp = batch_pairs(in, n, b0 + i);
+      const WsLayout L = ws_layout(d, r.n_tokens, width, bp);
+      const SyrkPlan p = syrk_plan(d, r.n_tokens, bp);
       RIn& x = g.r[i];
       x.X = r.X;
       x.A = r.A_out ? r.A_out : reinterpret_cast<float*>(base + L.A);
@@ -1388,17 +1419,25 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       maxpairs = p.npairs > maxpairs ? p.npairs : maxpairs;
       maxsplit = p.nsplit > maxsplit ? p.nsplit : maxsplit;
     }
-    // 1. covariance, per activation dtype (<= 4 inputs per SYRK launch)
-    for (int dt = 0; dt < 2; ++dt) {
+    // 1. covariance: bf16 inputs in one launch over a work list, fp32 inputs
+    // (<= 4 per launch) on a (pair, split, input) grid
+    {
+      int wg = 0;
+      g.sy_n = 0;
+      for (int i = 0; i < nb; ++i)
+        if (in[b0 + i].x_dtype == GIFT_DTYPE_BF16) {
+          g.sy_in[g.sy_n] = i;
+          g.sy_begin[g.sy_n++] = wg;
+          wg += g.r[i].npairs * g.r[i].nsplit;
+        }
+      if (wg) k_syrk_bf16<<<dim3(wg), kT, 0, st>>>(g);
       int sel[kMaxGroup], ns = 0;
       for (int i = 0; i < nb; ++i)
-        if (in[b0 + i].x_dtype == (dt ? GIFT_DTYPE_BF16 : GIFT_DTYPE_F32)) sel[ns++] = i;
+        if (in[b0 + i].x_dtype == GIFT_DTYPE_F32) sel[ns++] = i;
       for (int k = 0; k < ns; k += 4) {
         const int m = ns - k < 4 ? ns - k : 4;
         int4 idx = make_int4(sel[k], m > 1 ? sel[k + 1] : 0, m > 2 ? sel[k + 2] : 0, m > 3 ? sel[k + 3] : 0);
-        const dim3 grid(maxpairs, maxsplit, m);
-        if (dt) k_syrk_bf16<<<grid, kT, 0, st>>>(g, idx);
-        else k_syrk<false><<<grid, kT, 0, st>>>(g, idx);
+        k_syrk<false><<<dim3(maxpairs, maxsplit, m), kT, 0, st>>>(g, idx);
       }
     }
     k_syrk_reduce<<<dim3(maxpairs, nb), kT, 0, st>>>(g);
