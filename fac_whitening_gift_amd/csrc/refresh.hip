@@ -296,11 +296,12 @@ __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int steps = (int)((n_end - n_begin + kKStepB - 1) / kKStepB);
-  // Two register sets: while step st is multiplied out of LDS, the tokens of
-  // step st + 1 (issued one step earlier) are stashed into the other LDS
-  // buffer and those of step st + 2 are in flight, so a load has two steps
-  // of MFMA work to arrive.  Set k holds the steps st with st % 2 == k.
-  SyrkRegs ra[2], rb[2];
+  // Three register sets: while step st is multiplied out of LDS, the tokens
+  // of step st + 1 (issued two steps earlier) are stashed into the other LDS
+  // buffer and those of steps st + 2 and st + 3 are in flight, so a load has
+  // three steps of MFMA work to arrive.  Set k holds the steps st with
+  // st % 3 == k; LDS buffer b the steps with st % 2 == b.
+  SyrkRegs ra[3], rb[3];
   const int cpl = 2 * (threadIdx.x & 63), tgl = threadIdx.x >> 6;
   const uint32_t rowbytes = 2u * (uint32_t)d;
   const uint32_t va = (uint32_t)(16 * tgl) * rowbytes + 2u * (uint32_t)(ci0 + cpl);
@@ -309,43 +310,55 @@ __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
   if (steps > 0) {
     const __amdgpu_buffer_rsrc_t r0 = syrk_rsrc(X, n_begin, n_end, d);
     const __amdgpu_buffer_rsrc_t r1 = syrk_rsrc(X, n_begin + kKStepB, n_end, d);
+    const __amdgpu_buffer_rsrc_t r2 = syrk_rsrc(X, n_begin + 2 * kKStepB, n_end, d);
     syrk_fetch(ra[0], r0, va, rowbytes, oka);
     syrk_fetch(rb[0], r0, vb, rowbytes, okb);
     syrk_fetch(ra[1], r1, va, rowbytes, oka);
     syrk_fetch(rb[1], r1, vb, rowbytes, okb);
+    syrk_fetch(ra[2], r2, va, rowbytes, oka);
+    syrk_fetch(rb[2], r2, vb, rowbytes, okb);
     syrk_stash(ra[0], sb[0].a);
     syrk_stash(rb[0], sb[0].b);
   }
   __syncthreads();
-  auto step = [&](int st, auto K) {
-    constexpr int k = decltype(K)::value;  // st % 2
-    const __amdgpu_buffer_rsrc_t rn = syrk_rsrc(X, n_begin + (int64_t)(st + 2) * kKStepB, n_end, d);
-    syrk_fetch(ra[k], rn, va, rowbytes, oka);
-    syrk_fetch(rb[k], rn, vb, rowbytes, okb);
-    const SyrkBuf& cur = sb[k];
-    const uint16_t (*tb)[kKStepB + 8] = cur.b;
+  // step st: registers k = st % 3, LDS buffer b = st % 2
+  auto step = [&](int st, auto K, auto B) {
+    constexpr int k = decltype(K)::value, b = decltype(B)::value;
+    constexpr int k1 = (k + 1) % 3;
+    const SyrkBuf& cur = sb[b];
 #pragma unroll
     for (int ks = 0; ks < kKStepB / 32; ++ks) {
       bf16x8 fa[4], fb[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         fa[t] = *reinterpret_cast<const bf16x8*>(&cur.a[64 * wi + 16 * t + r16][32 * ks + 8 * gq]);
-        fb[t] = *reinterpret_cast<const bf16x8*>(&tb[64 * wj + 16 * t + r16][32 * ks + 8 * gq]);
+        fb[t] = *reinterpret_cast<const bf16x8*>(&cur.b[64 * wj + 16 * t + r16][32 * ks + 8 * gq]);
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        for (int c = 0; c < 4; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[c], acc[a][c], 0, 0, 0);
     }
-    SyrkBuf& nxt = sb[k ^ 1];
-    syrk_stash(ra[k ^ 1], nxt.a);
-    syrk_stash(rb[k ^ 1], nxt.b);
+    SyrkBuf& nxt = sb[b ^ 1];
+    syrk_stash(ra[k1], nxt.a);
+    syrk_stash(rb[k1], nxt.b);
+    // set k is free again: the tokens of step st + 3
+    const __amdgpu_buffer_rsrc_t rn = syrk_rsrc(X, n_begin + (int64_t)(st + 3) * kKStepB, n_end, d);
+    syrk_fetch(ra[k], rn, va, rowbytes, oka);
+    syrk_fetch(rb[k], rn, vb, rowbytes, okb);
     __syncthreads();
   };
-  for (int st = 0; st < steps; st += 2) {
-    step(st, std::integral_constant<int, 0>{});
-    if (st + 1 < steps) step(st + 1, std::integral_constant<int, 1>{});
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int st = 0; st < steps; st += 6) {
+    step(st, I0{}, I0{});
+    if (st + 1 < steps) step(st + 1, I1{}, I1{});
+    if (st + 2 < steps) step(st + 2, I2{}, I0{});
+    if (st + 3 < steps) step(st + 3, I0{}, I1{});
+    if (st + 4 < steps) step(st + 4, I1{}, I0{});
+    if (st + 5 < steps) step(st + 5, I2{}, I1{});
   }
   // D layout: lane holds rows 4gq..4gq+3 of column r16 of each 16x16 tile
   float* out = R.part + ((size_t)split * R.npairs + pair) * kSyrkTile * kSyrkTile;
