@@ -274,3 +274,26 @@ def test_factor_lower_rank(rank):
     assert np.array_equal(host(L.q), codes)
     ref = og.unwhiten_with(og.dequantize(host(L.q), inv_o, False), U32, beta, du32)
     assert rel_fro(host(L.G_hat), ref) <= 1e-5
+
+
+def test_grouped_covariance_two_batches():
+    """Nineteen bf16 inputs of mixed widths (64 .. 1040, partial column tiles)
+    and token counts (ragged, fewer than one 64-token step, many steps) in one
+    call: the covariance work list spans two groups of inputs with their own
+    token splits.  Every A against the oracle, exactly symmetric."""
+    dims = [64, 192, 1040, 272, 128, 512, 80, 336, 64, 1024, 208, 96, 144, 400, 64, 256, 176, 960, 112]
+    toks = [100, 3000, 777, 1500, 63, 2048, 5, 640, 5000, 999, 130, 64, 2500, 300, 4097, 17, 1234, 700, 65]
+    items, ref = [], []
+    for k, (d, n) in enumerate(zip(dims, toks)):
+        spec = synth.InputSpec("x%d" % k, d, n, 1.5, bf16=True)
+        inp = synth.draw_input(spec, seed=3000 + k, as_bf16=True)
+        A = torch.empty(d, d, dtype=torch.float32, device=DEV)
+        items.append(dict(X=inp["X"].to(DEV), factor=fg.Factor(d), A_out=A, seed=k))
+        ref.append(og.covariance(inp["X"].float().numpy()))
+    say("grouped covariance: %d inputs" % len(items))
+    fg.gift_refresh_factors(items, power_steps=1)
+    torch.cuda.synchronize()
+    for k, (it, A_orc) in enumerate(zip(items, ref)):
+        Ad = host(it["A_out"])
+        assert np.array_equal(Ad, Ad.T), k
+        assert rel_fro(Ad, A_orc) <= 1e-5, (k, dims[k], toks[k])
