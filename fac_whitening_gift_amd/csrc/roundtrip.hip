@@ -23,11 +23,15 @@
 // same way.  U's two operand forms are split and packed when the factor is
 // refreshed (or once per call, k_pack_u).
 //
-// Work is split into strips of 16 rows over the full row length (one
-// workgroup each), so a row's c never leaves its workgroup.  Per-tensor
-// scaling takes two launches (pass 1: c' and the strip's amax; pass 2: the
-// layer amax, W again and the codes); 1x128 block scaling and the
-// dequantize side are one launch each.
+// Work is split into tiles of 64 rows by 256 columns (one workgroup each).
+// A row's c = g U needs every column, so it is formed in two launches: each
+// tile writes its partial c, then one workgroup per 64-row block sums the
+// column groups' partials in a fixed order (k_tile_cpart, k_tile_reduce).
+// Per-tensor scaling then takes two more passes over G (k_tile_whiten: the
+// tiles' amax; k_tile_quant: the layer amax, W again and the codes); 1x128
+// block scaling and MXFP4 take one (k_tile_whiten with codes and scales).
+// The dequantize side is k_tile_cpart on the codes, k_tile_reduce and
+// k_tile_unwhiten.
 #include <type_traits>
 
 #include "device.hpp"
