@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgift.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "roundtrip.hip", "refresh.hip"]
+SOURCES = ["api.cpp", "roundtrip.hip", "roundtrip_rt2.hip", "refresh.hip"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops (the host
 # pass does not know the feature and warns; that is expected).

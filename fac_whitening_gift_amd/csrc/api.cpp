@@ -10,25 +10,66 @@
 #include "device.hpp"
 
 namespace gift {
-hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s);
-hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool write_w,
-                                hipStream_t s);
-hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s);
-hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);
-hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStream_t s);
-hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s);
-hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
-hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s);
-hipError_t launch_blk_whiten(const GroupDev& g, int b, int scaling, bool write_w, hipStream_t s);
-hipError_t launch_blk_dequant(const GroupDev& g, int b, int scaling, hipStream_t s);
-int blk_col_groups(int64_t d_in, int b);
-size_t blk_pack_bytes(int64_t d_in, int b);
-int64_t row_blocks(int64_t d_out);
-int col_groups(int64_t d_in);
-int frag_floats();
-int cop_bytes();
-int flat_tiles(int64_t n);
-size_t pack_bytes(int64_t d_in);
+// roundtrip.hip, built with 64-row tiles (rt4) and 32-row tiles (rt2)
+#define GIFT_TILE_DECLS                                                                          \
+  hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s); \
+  hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool write_w,         \
+                                  hipStream_t s);                                                \
+  hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s);           \
+  hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);                       \
+  hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStream_t s);        \
+  hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s);                              \
+  hipError_t launch_pack(const PackGroup& pg, hipStream_t s);                                    \
+  hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s);                         \
+  hipError_t launch_blk_whiten(const GroupDev& g, int b, int scaling, bool write_w,              \
+                               hipStream_t s);                                                   \
+  hipError_t launch_blk_dequant(const GroupDev& g, int b, int scaling, hipStream_t s);            \
+  int blk_col_groups(int64_t d_in, int b);                                                       \
+  size_t blk_pack_bytes(int64_t d_in, int b);                                                    \
+  int64_t row_blocks(int64_t d_out);                                                             \
+  int col_groups(int64_t d_in);                                                                  \
+  int frag_floats();                                                                             \
+  int cop_bytes();                                                                               \
+  int flat_tiles(int64_t n);                                                                     \
+  size_t pack_bytes(int64_t d_in);
+namespace rt4 {
+GIFT_TILE_DECLS
+}
+namespace rt2 {
+GIFT_TILE_DECLS
+}
+#undef GIFT_TILE_DECLS
+// what does not depend on the tile height comes from rt4
+using rt4::blk_col_groups;
+using rt4::blk_pack_bytes;
+using rt4::col_groups;
+using rt4::flat_tiles;
+using rt4::launch_accumulate;
+using rt4::launch_blk_pack;
+using rt4::launch_error;
+using rt4::launch_flat_quantize;
+using rt4::launch_pack;
+using rt4::pack_bytes;
+
+// The tile-height dependent part: rows per tile and the launchers.
+struct TileOps {
+  int64_t (*row_blocks)(int64_t d_out);
+  int (*frag_floats)();
+  int (*cop_bytes)();
+  hipError_t (*whiten_quantize)(const GroupDev& g, int scaling, bool write_w, hipStream_t s);
+  hipError_t (*dequant)(const GroupDev& g, int scaling, bool white, hipStream_t s);
+  hipError_t (*unwhiten_f32)(const GroupDev& g, hipStream_t s);
+  hipError_t (*blk_whiten)(const GroupDev& g, int b, int scaling, bool write_w, hipStream_t s);
+  hipError_t (*blk_dequant)(const GroupDev& g, int b, int scaling, hipStream_t s);
+};
+const TileOps kTiles64 = {rt4::row_blocks,           rt4::frag_floats,      rt4::cop_bytes,
+                          rt4::launch_whiten_quantize, rt4::launch_dequant,
+                          rt4::launch_unwhiten_f32,    rt4::launch_blk_whiten,
+                          rt4::launch_blk_dequant};
+const TileOps kTiles32 = {rt2::row_blocks,           rt2::frag_floats,      rt2::cop_bytes,
+                          rt2::launch_whiten_quantize, rt2::launch_dequant,
+                          rt2::launch_unwhiten_f32,    rt2::launch_blk_whiten,
+                          rt2::launch_blk_dequant};
 
 // refresh.hip
 size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype, int width);
@@ -90,28 +131,39 @@ struct LayerWs {
 };
 
 // workgroups of a whitened layer's tile kernels: row blocks x column groups
-int row_tiles(const gift_layer& L) {
+int row_tiles(const gift_layer& L, const TileOps& t) {
   const int b = fblock(L);
-  return (int)(row_blocks(L.d_out) * (b ? blk_col_groups(L.d_in, b) : col_groups(L.d_in)));
+  return (int)(t.row_blocks(L.d_out) * (b ? blk_col_groups(L.d_in, b) : col_groups(L.d_in)));
+}
+
+int row_tiles_max(const gift_layer& L) {
+  const int a = row_tiles(L, kTiles64), b = row_tiles(L, kTiles32);
+  return a > b ? a : b;
 }
 
 LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
   LayerWs w;
   const int64_t n = L.d_out * L.d_in;
-  const size_t frag = (size_t)row_blocks(L.d_out) * frag_floats() * sizeof(float);
-  const size_t cop = (size_t)row_blocks(L.d_out) * cop_bytes();
+  // either tile height (the larger of the two layouts)
+  size_t frag = 0, cop = 0;
+  for (const TileOps* t : {&kTiles64, &kTiles32}) {
+    const size_t f = (size_t)t->row_blocks(L.d_out) * t->frag_floats() * sizeof(float);
+    const size_t c = (size_t)t->row_blocks(L.d_out) * t->cop_bytes();
+    frag = f > frag ? f : frag;
+    cop = c > cop ? c : cop;
+  }
   switch (op) {
     case Op::Whiten:
       if (L.factor && L.factor->block) {
         if (!block) {  // one amax per tile, the layer amax
-          w.part = (size_t)row_tiles(L) * sizeof(uint32_t);
+          w.part = (size_t)row_tiles_max(L) * sizeof(uint32_t);
           w.amax = sizeof(uint32_t);
         }
       } else if (L.factor) {
         w.cbuf = (size_t)col_groups(L.d_in) * frag;  // partial c per column group
         w.cfin = cop;                                  // c' of every row (operand form)
         if (!block) {  // one amax per tile, the layer amax
-          w.part = (size_t)row_tiles(L) * sizeof(uint32_t);
+          w.part = (size_t)row_tiles_max(L) * sizeof(uint32_t);
           w.amax = sizeof(uint32_t);
         }
       } else if (!block) {
@@ -253,11 +305,24 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
   return GIFT_OK;
 }
 
+// Groups below this many whitened gradient elements (about 2048 tiles of 64
+// rows) run the 32-row tile kernels: with twice the workgroups, the last
+// round of workgroups on the machine is shorter.
+constexpr int64_t kSmallGroupElems = int64_t(1) << 25;
+
+const TileOps& tile_ops(const gift_layer* layers, int n, Op op) {
+  int64_t e = 0;
+  for (int i = 0; i < n; ++i)
+    if (whitened(layers[i], op)) e += layers[i].d_out * layers[i].d_in;
+  return e < kSmallGroupElems ? kTiles32 : kTiles64;
+}
+
 // Walk the layers selected by `pick` in chunks of kMaxGroup, filling the
 // descriptors (workspace slices in layer order) and calling `launch`.
 template <class Pick, class Tiles, class Launch>
 gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void* ws,
-                        uint32_t* flags, double* out, Pick pick, Tiles tiles, Launch launch) {
+                        uint32_t* flags, double* out, Pick pick, Tiles tiles, Launch launch,
+                        const TileOps& geo = kTiles64) {
   // workspace: operand packs first, then per-layer slices in layer order
   // (independent of the chunking)
   const Packs packs = plan_packs(layers, n, op);
@@ -307,7 +372,7 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     d.amax = lw.amax ? (uint32_t*)base : nullptr;
     d.d_out = L.d_out;
     d.d_in = L.d_in;
-    d.n_rb = row_blocks(L.d_out);
+    d.n_rb = geo.row_blocks(L.d_out);
     d.ngrp = !whitened(L, op) ? 1 : fblock(L) ? blk_col_groups(L.d_in, fblock(L)) : col_groups(L.d_in);
     d.n_tiles = tiles(L);
     d.tile_begin = g.total_tiles;
@@ -381,6 +446,7 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
   hipStream_t st = (hipStream_t)stream;
   s = run_packs(plan_packs(layers, n_layers, Op::Whiten), ws, st);
   if (s != GIFT_OK) return s;
+  const TileOps& geo = tile_ops(layers, n_layers, Op::Whiten);
   // groups: rank-r factors, Euclidean layers, block factors of 32, of 64
   for (int wgrp = 0; wgrp < 4; ++wgrp) {
     auto pick = [&](const gift_layer& L) {
@@ -391,12 +457,12 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
     bool any_w = false;
     for (int i = 0; i < n_layers; ++i)
       if (pick(layers[i]) && layers[i].W_out) any_w = true;
-    auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L); };
+    auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L, geo); };
     if (wgrp == 0)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
-                        return launch_whiten_quantize(g, scaling, any_w, st);
-                      });
+                        return geo.whiten_quantize(g, scaling, any_w, st);
+                      }, geo);
     else if (wgrp == 1)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_flat, [&](const GroupDev& g, int) {
@@ -405,8 +471,8 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
     else
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
-                        return launch_blk_whiten(g, wgrp == 2 ? 32 : 64, scaling, any_w, st);
-                      });
+                        return geo.blk_whiten(g, wgrp == 2 ? 32 : 64, scaling, any_w, st);
+                      }, geo);
     if (s != GIFT_OK) return s;
   }
   return GIFT_OK;
@@ -422,18 +488,19 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
   hipStream_t st = (hipStream_t)stream;
   s = run_packs(plan_packs(layers, n_layers, Op::Dequant), ws, st);
   if (s != GIFT_OK) return s;
+  const TileOps& geo = tile_ops(layers, n_layers, Op::Dequant);
   for (int wgrp = 0; wgrp < 4; ++wgrp) {
     auto pick = [&](const gift_layer& L) {
       return wgrp == 0 ? L.factor != nullptr && !L.factor->block
            : wgrp == 1 ? L.factor == nullptr
                        : fblock(L) == (wgrp == 2 ? 32 : 64);
     };
-    auto tiles = [&](const gift_layer& L) { return wgrp == 1 ? tiles_flat(L) : row_tiles(L); };
+    auto tiles = [&](const gift_layer& L) { return wgrp == 1 ? tiles_flat(L) : row_tiles(L, geo); };
     s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles,
                     [&](const GroupDev& g, int) {
-                      if (wgrp >= 2) return launch_blk_dequant(g, wgrp == 2 ? 32 : 64, scaling, st);
-                      return launch_dequant(g, scaling, wgrp == 0, st);
-                    });
+                      if (wgrp >= 2) return geo.blk_dequant(g, wgrp == 2 ? 32 : 64, scaling, st);
+                      return geo.dequant(g, scaling, wgrp == 0, st);
+                    }, geo);
     if (s != GIFT_OK) return s;
   }
   return GIFT_OK;
@@ -493,9 +560,10 @@ gift_status gift_unwhiten_f32(const gift_layer* layers, int n_layers, void* ws, 
   s = run_packs(plan_packs(layers, n_layers, Op::UnwhitenF32), ws, st);
   if (s != GIFT_OK) return s;
   auto pick = [](const gift_layer& L) { return L.factor != nullptr; };
-  auto tiles = [](const gift_layer& L) { return row_tiles(L); };
+  const TileOps& geo = tile_ops(layers, n_layers, Op::UnwhitenF32);
+  auto tiles = [&](const gift_layer& L) { return row_tiles(L, geo); };
   return run_grouped(layers, n_layers, Op::UnwhitenF32, true, ws, nullptr, nullptr, pick, tiles,
-                     [&](const GroupDev& g, int) { return launch_unwhiten_f32(g, st); });
+                     [&](const GroupDev& g, int) { return geo.unwhiten_f32(g, st); }, geo);
 }
 
 size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype,

@@ -32,9 +32,14 @@
 
 namespace gift {
 
+namespace rt4 {  // roundtrip.hip (the operand packs do not depend on the tile height)
 hipError_t launch_pack(const PackGroup& pg, hipStream_t s);
 hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s);
 size_t pack_bytes(int64_t d_in);
+}  // namespace rt4
+using rt4::launch_blk_pack;
+using rt4::launch_pack;
+using rt4::pack_bytes;
 
 namespace {
 

@@ -42,7 +42,17 @@
 // 2 reads the rounded product back.  Every fma below is written out.
 #pragma clang fp contract(off)
 
+// Tile height of the tile kernels, in 16-row MFMA tiles: this file is built
+// twice, with 64-row tiles (namespace rt4) and, from roundtrip_rt2.hip, with
+// 32-row tiles (namespace rt2) for groups too small to fill the machine with
+// 64-row tiles.
+#ifndef GIFT_TILE_RT
+#define GIFT_TILE_RT 4
+#define GIFT_TILE_NS rt4
+#endif
+
 namespace gift {
+namespace GIFT_TILE_NS {
 
 constexpr int kThreads = 256;       // flat kernels
 constexpr int kFlatTile = 4096;     // elements per workgroup (flat kernels)
@@ -103,10 +113,15 @@ __global__ __launch_bounds__(kThreads) void k_pack_u(PackGroup pg) {
 // ---------------------------------------------------------------------------
 constexpr int kTW = 8;                    // waves per tile workgroup
 constexpr int kTileThreads = 64 * kTW;
-constexpr int kTR = 4;                    // 16-row MFMA tiles per workgroup
+constexpr int kTR = GIFT_TILE_RT;         // 16-row MFMA tiles per workgroup
 constexpr int kTileRows = 16 * kTR;
 constexpr int kFrag = kTR * 8 * 64;       // floats of one row block's coefficients
 constexpr int kReduceThreads = kTR * 64;  // one thread per lane of each 16-row tile
+// the waves' partial c are summed through LDS in kHalves passes of kPerHalf
+// 16-row tiles (kRedRows floats per lane and wave)
+constexpr int kHalves = kTR >= 2 ? 2 : 1;
+constexpr int kPerHalf = kTR / kHalves;
+constexpr int kRedRows = kPerHalf * 8;
 // Above this many tiles in a layer the per-tile amax partials are first
 // reduced by one workgroup (k_amax_final) instead of by every quantize
 // workgroup.
@@ -186,13 +201,14 @@ template <int kCPW>
 __device__ __forceinline__ void store_code_tile(const LayerDev& L, const Tile& x,
                                                 const CodeTile<kCPW>& ct) {
   constexpr int kQ = kTW * kCPW * 2;  // 16-byte pieces per row
+  constexpr int kN = kTileRows * kQ;  // pieces per tile
   const int nch = (int)(L.d_in / kChunk), cfirst = x.cg * kTW * kCPW;
   const int nvalid = nch - cfirst < kTW * kCPW ? nch - cfirst : kTW * kCPW;
 #pragma unroll
-  for (int h = 0; h < kTileRows * kQ / kTileThreads; ++h) {
+  for (int h = 0; h < (kN + kTileThreads - 1) / kTileThreads; ++h) {
     const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
     const int64_t row = x.rb * kTileRows + r;
-    if (row < L.d_out && (qd >> 1) < nvalid)
+    if (e < kN && row < L.d_out && (qd >> 1) < nvalid)
       *reinterpret_cast<uint4*>(L.q + row * L.d_in + kChunk * cfirst + 16 * qd) =
           *reinterpret_cast<const uint4*>(&ct.w[r][4 * qd]);
   }
@@ -204,7 +220,8 @@ __device__ __forceinline__ void store_code_tile(const LayerDev& L, const Tile& x
 template <int kCPW>
 struct CodePieces {
   static constexpr int kQ = kTW * kCPW * 2;                 // 16-byte pieces per row
-  static constexpr int kN = kTileRows * kQ / kTileThreads;  // per thread
+  static constexpr int kPieces = kTileRows * kQ;             // per tile
+  static constexpr int kN = (kPieces + kTileThreads - 1) / kTileThreads;  // per thread
   uint4 v[kN];
 };
 
@@ -218,7 +235,7 @@ __device__ __forceinline__ void load_code_pieces(const LayerDev& L, const Tile& 
   for (int h = 0; h < CodePieces<kCPW>::kN; ++h) {
     const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
     const int64_t row = x.rb * kTileRows + r;
-    const bool in = row < L.d_out && (qd >> 1) < nvalid;
+    const bool in = e < CodePieces<kCPW>::kPieces && row < L.d_out && (qd >> 1) < nvalid;
     pc.v[h] = in ? *reinterpret_cast<const uint4*>(L.q + row * L.d_in + kChunk * cfirst + 16 * qd)
                  : make_uint4(0u, 0u, 0u, 0u);
   }
@@ -230,7 +247,8 @@ __device__ __forceinline__ void put_code_pieces(CodeTile<kCPW>& ct, const CodePi
 #pragma unroll
   for (int h = 0; h < CodePieces<kCPW>::kN; ++h) {
     const int e = threadIdx.x + h * kTileThreads;
-    *reinterpret_cast<uint4*>(&ct.w[e / kQ][4 * (e % kQ)]) = pc.v[h];
+    if (e < CodePieces<kCPW>::kPieces)
+      *reinterpret_cast<uint4*>(&ct.w[e / kQ][4 * (e % kQ)]) = pc.v[h];
   }
 }
 
@@ -408,30 +426,33 @@ __device__ __forceinline__ void correction(const bf16x8 (&a)[2][3], const bf16x8
 }
 
 // Sum the waves' partial c (acc of every wave) in wave order through LDS and
-// store the tile's partial for its column group in fragment order, in two
-// halves of kTR / 2 row tiles (32 KB of LDS).  Contains workgroup barriers.
+// store the tile's partial for its column group in fragment order, in
+// kHalves passes of kPerHalf row tiles.  Contains workgroup barriers.
 __device__ __forceinline__ void store_partial(const LayerDev& L, const Tile& x,
                                               const f32x4 (&acc)[kTR][2],
-                                              float (*red)[kTR * 4][64]) {
+                                              float (*red)[kRedRows][64]) {
+  constexpr int kN = kFrag / kHalves;  // floats per pass
   float* out = L.cbuf + ((int64_t)x.cg * L.n_rb + x.rb) * kFrag;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < kHalves; ++half) {
     if (half) __syncthreads();  // the first half has been read
 #pragma unroll
-    for (int r = 0; r < kTR / 2; ++r)
+    for (int r = 0; r < kPerHalf; ++r)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          red[x.wave][r * 8 + 4 * h + i][x.lane] = acc[half * (kTR / 2) + r][h][i];
+          red[x.wave][r * 8 + 4 * h + i][x.lane] = acc[half * kPerHalf + r][h][i];
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kFrag / 2 / kTileThreads; ++e) {
+    for (int e = 0; e < (kN + kTileThreads - 1) / kTileThreads; ++e) {
       const int p = e * kTileThreads + threadIdx.x;
-      float s = 0.f;
+      if (p < kN) {
+        float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < kTW; ++w) s += red[w][p >> 6][p & 63];
-      out[half * (kFrag / 2) + p] = s;
+        for (int w = 0; w < kTW; ++w) s += red[w][p >> 6][p & 63];
+        out[half * kN + p] = s;
+      }
     }
   }
 }
@@ -463,7 +484,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kCPW>(L, tile);
-  __shared__ float red[kTW][kTR * 4][64];
+  __shared__ float red[kTW][kRedRows][64];
   f32x4 acc[kTR][2];
 #pragma unroll
   for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1558,4 +1579,5 @@ hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s) {
   return hipGetLastError();
 }
 
+}  // namespace GIFT_TILE_NS
 }  // namespace gift

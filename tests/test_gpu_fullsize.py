@@ -9,6 +9,11 @@
 * 4096 / 11008 shapes (the staleness and interval studies' block), too
   large for whole-tensor fp64 checks: sampled rows, with the codes of the
   sampled rows encoded at the device's tensor scale.
+* A 16384 x 2048 layer (2^25 elements: a group of this size runs the 64-row
+  tile kernels, smaller groups the 32-row ones) through 1x128 E4M3 and MXFP4
+  scaling, on sampled rows: the scales are row-local, so codes and scales of
+  the sampled rows are bit-exact against the oracle's encoding of the
+  device's W.
 * The refresh at full size, where the oracle's eigensolve is too slow: the
   properties that hold at any size -- U orthonormal, theta equal to the
   Rayleigh quotients u^T A u, and within 1e-4 of the top eigenvalues of the
@@ -24,6 +29,7 @@ import synth
 import fac_whitening_gift_amd as fg
 from oracle import e4m3
 from oracle import gift as og
+from oracle import mxfp4 as mx
 from gpu_util import DEV, factor_host, host, rel_fro, say
 
 pytestmark = pytest.mark.gpu
@@ -116,3 +122,41 @@ def test_block4096_shapes_sampled_rows():
         assert np.array_equal(qr, codes)
         ref = og.unwhiten_with(og.dequantize_tensor(qr, inv), U, beta, du)
         assert rel_fro(host(L.G_hat[rows]), ref) <= 1e-5
+
+
+def test_large_group_block_scalings_sampled_rows():
+    say("16384 x 2048 layer: 1x128 and MXFP4 scaling, sampled rows")
+    spec = synth.InputSpec("x", 2048, 4096, 1.5, bf16=True)
+    inputs, facs = _refresh_inputs([spec], seed=760)
+    inp, f = inputs[0], facs[0]
+    d_out = 16384
+    G = synth.draw_gradient(d_out, inp["Q"], inp["ev"], seed=770, device=DEV)
+    U, alpha, beta, dw, du = factor_host(f)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([np.sort(rng.choice(d_out, 128, replace=False)), [0, d_out - 1]]))
+    W_orc = og.whiten_with(host(G[rows]), U, alpha, dw)
+    # 1 x 128 E4M3
+    W = torch.empty_like(G)
+    L = fg.Layer(G, factor=f, W_out=W, block128=True)
+    fg.gift_whiten_quantize([L], scaling=fg.SCALE_BLOCK128)
+    fg.gift_dequant_unwhiten([L], scaling=fg.SCALE_BLOCK128)
+    Wr = host(W[rows])
+    assert rel_fro(Wr, W_orc) <= 1e-5
+    codes, inv, _ = og.quantize_block128(Wr)
+    assert np.array_equal(host(L.q[rows]), codes)
+    assert np.array_equal(host(L.inv_scale[rows]), inv)
+    ref = og.unwhiten_with(og.dequantize_block128(codes, inv), U, beta, du)
+    assert rel_fro(host(L.G_hat[rows]), ref) <= 1e-5
+    del L, W
+    # MXFP4
+    W2 = torch.empty_like(G)
+    L2 = fg.Layer(G, factor=f, W_out=W2, mxfp4=True)
+    fg.gift_whiten_quantize([L2], scaling=fg.SCALE_MXFP4)
+    fg.gift_dequant_unwhiten([L2], scaling=fg.SCALE_MXFP4)
+    W2r = host(W2[rows])
+    assert rel_fro(W2r, W_orc) <= 1e-5
+    mc, ms, _ = mx.quantize(W2r)
+    assert np.array_equal(host(L2.q[rows]), mc)
+    assert np.array_equal(host(L2.inv_scale[rows]), ms)
+    ref2 = og.unwhiten_with(mx.dequantize(mc, ms), U, beta, du)
+    assert rel_fro(host(L2.G_hat[rows]), ref2) <= 1e-5
