@@ -23,10 +23,11 @@
 // same way.  U's two operand forms are split and packed when the factor is
 // refreshed (or once per call, k_pack_u).
 //
-// Work is split into tiles of 64 rows by 256 columns (one workgroup each).
-// A row's c = g U needs every column, so it is formed in two launches: each
-// tile writes its partial c, then one workgroup per 64-row block sums the
-// column groups' partials in a fixed order (k_tile_cpart, k_tile_reduce).
+// Work is split into tiles of 64 (or 32) rows by 256 columns (one workgroup
+// each).  A row's c = g U needs every column, so it is formed in two
+// launches: each tile writes its partial c, then one workgroup per row block
+// sums the column groups' partials in a fixed order (k_tile_cpart,
+// k_tile_reduce).
 // Per-tensor scaling then takes two more passes over G (k_tile_whiten: the
 // tiles' amax; k_tile_quant: the layer amax, W again and the codes); 1x128
 // block scaling and MXFP4 take one (k_tile_whiten with codes and scales).
@@ -94,10 +95,10 @@ __global__ __launch_bounds__(kThreads) void k_pack_u(PackGroup pg) {
 }
 
 // ---------------------------------------------------------------------------
-// tile geometry.  A workgroup owns a tile of kTR x 16 = 64 gradient rows by
-// one column group of kTW * kCPW 32-column chunks; each wave takes kCPW
-// chunks of the group for all 64 rows, so every operand-pack load feeds four
-// 16-row MFMA tiles.  A row's c = g U is split over the column groups: each
+// tile geometry.  A workgroup owns a tile of kTR x 16 gradient rows (64 or
+// 32) by one column group of kTW * kCPW 32-column chunks; each wave takes
+// kCPW chunks of the group for all the tile's rows, so every operand-pack
+// load feeds kTR 16-row MFMA tiles.  A row's c = g U is split over the column groups: each
 // tile stores its partial (summed over its waves through LDS), and the next
 // pass sums the partials of a row block in column-group order.
 //
