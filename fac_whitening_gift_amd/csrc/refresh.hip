@@ -804,21 +804,23 @@ __device__ double block_sum(double v, double* red) {
 // 4c. Cholesky of the Gram matrix, G = R^T R (R upper triangular, fp64).
 // Pivots below kDropTol * max diagonal mark a column as dependent: its row of
 // R is zero and so is that column of the orthonormalised Q (k_solve).  The
-// output is R with 1/R[k][k] on the diagonal.  grid: (inputs), kCT threads.
+// output is R with 1/R[k][k] on the diagonal.  grid: (inputs), kCholT threads.
 //
-// Every thread owns a fixed set of entries (i, j), i <= j, of the upper
-// triangle (at most 3) and keeps them in registers; a step needs one
-// workgroup barrier.
-//   * Factorization, step k: with p = G[k][k] (row k is final and in LDS),
-//     row k of R is G[k][.] / sqrt(p) and every entry below it takes the
-//     rank-1 update G[i][j] -= G[k][i] G[k][j] / p (right-looking Cholesky
-//     in its unnormalised form); an entry of row k+1 is stored to LDS once
-//     updated, ready for the next step.
-// The thread owning a diagonal entry computes the pivot's reciprocal square
-// root y (the hardware estimate refined by two Newton steps) and 1/p = y^2
-// once the entry is final, and leaves them in LDS for the next step.
+// Right-looking Cholesky in its unnormalised form (at step k, with the pivot
+// p = G[k][k], row k of R is G[k][.] / sqrt(p) and every entry (i, j) below
+// it takes G[i][j] -= G[k][i] G[k][j] / p), blocked by panels of 16 columns
+// so that a panel costs three workgroup barriers instead of sixteen:
+//   1. one wave factors the panel's 16 x 16 diagonal block (lane j holds
+//      column j of the block in registers; the pivot's reciprocal square root
+//      is the hardware estimate refined by two Newton steps);
+//   2. one thread per later column applies the panel's 16 steps to the
+//      panel rows of that column;
+//   3. the panel's 16 rank-1 updates of the trailing triangle, in step order.
+// Every entry takes the same updates in the same order as in the unblocked
+// form; G is kept in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kCT = 1024;
+constexpr int kCholT = 512;  // k_chol: the serial phases need one wave; 8 waves keep 256 VGPRs each
 
 // 1/x for finite x != 0: the hardware estimate and two Newton steps
 __device__ __forceinline__ double rcp_f64(double x) {
@@ -836,100 +838,138 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
-template <int W>
-__global__ __launch_bounds__(kCT) void k_chol(RGroup g) {
-  constexpr int kN = W * (W + 1) / 2;          // upper-triangle entries
-  constexpr int kE = (kN + kCT - 1) / kCT;     // entries per thread
-  const RIn& Rin = g.r[blockIdx.x];
-  __shared__ double Gs[W][W + 1];  // row k of the partly reduced G, when final
-  __shared__ double R[W][W + 1];
-  __shared__ double pinv[W], rinv[W];  // 1/p and 1/sqrt(p) of each pivot (0: dropped)
-  __shared__ double red[kCT / 64];
-  // this thread's entries, row-major over the packed upper triangle: row i
-  // starts at i (2W + 1 - i) / 2
-  int ei[kE], ej[kE];
-  double v[kE];
-#pragma unroll
-  for (int r = 0; r < kE; ++r) {
-    int e = threadIdx.x + r * kCT;
-    const bool none = e >= kN;
-    if (none) e = kN - 1;
-    const float b = 2.f * W + 1.f;
-    int row = (int)((b - sqrtf(b * b - 8.f * (float)e)) * 0.5f);
-    row = row < 0 ? 0 : (row > W - 1 ? W - 1 : row);
-    if (row * (2 * W + 1 - row) / 2 > e) --row;
-    if ((row + 1) * (2 * W - row) / 2 <= e) ++row;
-    ei[r] = none ? W : row;  // row W: never active
-    ej[r] = row + e - row * (2 * W + 1 - row) / 2;
+// f(integral_constant<int, i>) for i = 0 .. N - 1, in order
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
   }
-  // Gram entries: fixed-order sum of the partials, all loads in flight
+}
+
+// the value of lane l (a compile-time constant) of a wave, as a scalar
+template <int l>
+__device__ __forceinline__ double lane_value(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+template <int W>
+__global__ __launch_bounds__(kCholT) void k_chol(RGroup g) {
+  constexpr int kP = 16;  // panel width
+  static_assert(W % kP == 0, "the sketch width is a multiple of 16");
+  const RIn& Rin = g.r[blockIdx.x];
+  __shared__ double A[W][W + 1];       // upper triangle of G, reduced in place
+  __shared__ double pinv[W], rinv[W];  // 1/p and 1/sqrt(p) of each pivot (0: dropped)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Gram entries: fixed-order sum of the partials, every load of a thread in
+  // flight at once (entries of the packed upper triangle, row i starting at
+  // i (2W + 1 - i) / 2, dealt round-robin to the threads)
   {
+    constexpr int kN = W * (W + 1) / 2, kE = (kN + kCholT - 1) / kCholT;
+    int ei[kE], ej[kE];
+#pragma unroll
+    for (int r = 0; r < kE; ++r) {
+      int e = threadIdx.x + r * kCholT;
+      const bool none = e >= kN;
+      if (none) e = kN - 1;
+      const float b = 2.f * W + 1.f;
+      int row = (int)((b - sqrtf(b * b - 8.f * (float)e)) * 0.5f);
+      row = row < 0 ? 0 : (row > W - 1 ? W - 1 : row);
+      if (row * (2 * W + 1 - row) / 2 > e) --row;
+      if ((row + 1) * (2 * W - row) / 2 <= e) ++row;
+      ei[r] = none ? W : row;  // row W: no entry
+      ej[r] = row + e - row * (2 * W + 1 - row) / 2;
+    }
     double part[kE][kGramParts];
 #pragma unroll
     for (int r = 0; r < kE; ++r) {
-      const int a = ei[r] < W ? ei[r] : W - 1, b = ej[r];
+      const int a = ei[r] < W ? ei[r] : W - 1;
 #pragma unroll
-      for (int c = 0; c < kGramParts; ++c) part[r][c] = Rin.gram[(size_t)c * kW * kW + a * kW + b];
+      for (int c = 0; c < kGramParts; ++c) part[r][c] = Rin.gram[(size_t)c * kW * kW + a * kW + ej[r]];
     }
 #pragma unroll
     for (int r = 0; r < kE; ++r) {
-      double s = 0.0;
+      double sum = 0.0;
 #pragma unroll
-      for (int c = 0; c < kGramParts; ++c) s += part[r][c];
-      v[r] = s;
+      for (int c = 0; c < kGramParts; ++c) sum += part[r][c];
+      if (ei[r] < W) A[ei[r]][ej[r]] = sum;
     }
   }
-  // largest diagonal entry; row 0 to LDS
-  double dm = 0.0;
-#pragma unroll
-  for (int r = 0; r < kE; ++r) {
-    if (ei[r] < W && ei[r] == ej[r]) dm = fmax(dm, v[r]);
-    if (ei[r] == 0) Gs[0][ej[r]] = v[r];
-  }
-  for (int o = 32; o > 0; o >>= 1) dm = fmax(dm, __shfl_xor(dm, o, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dm;
   __syncthreads();
+  // largest diagonal entry (wave 0, which takes the pivots)
   double dmax = 0.0;
+  if (wave == 0) {
+    dmax = lane < W ? A[lane][lane] : 0.0;
+    for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
+  }
+  for (int k0 = 0; k0 < W; k0 += kP) {
+    // 1. the diagonal block: lane j < 16 holds a[i] = A[k0 + i][k0 + j], i <= j
+    if (wave == 0) {
+      const int j = lane < kP ? lane : kP - 1;
+      double a[kP];
 #pragma unroll
-  for (int w = 0; w < kCT / 64; ++w) dmax = fmax(dmax, red[w]);
-  // the owner of a diagonal entry sets up its pivot once the entry is final
-  auto pivot = [&](int k, double p) {
-    const bool ok = dmax > 0.0 && p > kDropTol * dmax;
-    const double y = ok ? rsqrt_f64(p) : 0.0;
-    pinv[k] = y * y;
-    rinv[k] = y;
-  };
-  if (ei[0] == 0 && ej[0] == 0) pivot(0, v[0]);
-  __syncthreads();
-  // Loads are unconditional (indices clamped into the arrays) so that one
-  // wait covers them all; values read for inactive entries are discarded by
-  // the selects.
-  for (int k = 0; k < W; ++k) {
-    const double inv = pinv[k], y = rinv[k];
-    double a[kE], b[kE];
+      for (int i = 0; i < kP; ++i) a[i] = i <= j ? A[k0 + i][k0 + j] : 0.0;
+      static_for<kP>([&](auto M) {
+        constexpr int m = decltype(M)::value;
+        const double p = lane_value<m>(a[m]);  // the pivot, held by lane m
+        const bool ok = dmax > 0.0 && p > kDropTol * dmax;
+        const double y = ok ? rsqrt_f64(p) : 0.0, inv = y * y;
+        if (lane == m) {
+          pinv[k0 + m] = inv;
+          rinv[k0 + m] = y;
+        }
+        static_for<kP - 1 - m>([&](auto I) {
+          constexpr int i = m + 1 + decltype(I)::value;
+          const double gmi = lane_value<i>(a[m]);  // G[k0 + m][k0 + i], held by lane i
+          const double nv = a[i] - (gmi * inv) * a[m];
+          a[i] = i <= j ? nv : a[i];
+        });
+      });
+      if (lane < kP)
 #pragma unroll
-    for (int r = 0; r < kE; ++r) {
-      a[r] = Gs[k][ei[r] < W ? ei[r] : W - 1];
-      b[r] = Gs[k][ej[r]];
+        for (int i = 0; i < kP; ++i)
+          if (i <= j) A[k0 + i][k0 + j] = a[i];
     }
+    __syncthreads();
+    // 2. the panel rows of every later column
+    const int c = k0 + kP + (int)threadIdx.x;
+    if (c < W) {
+      double v[kP];
 #pragma unroll
-    for (int r = 0; r < kE; ++r) {
-      const int i = ei[r], jj = ej[r];
-      if (i == k) R[k][jj] = y != 0.0 ? v[r] * y : 0.0;
-      const double nv = v[r] - (a[r] * inv) * b[r];
-      v[r] = i > k && i < W ? nv : v[r];
-      if (i == k + 1) {
-        Gs[k + 1][jj] = v[r];
-        if (jj == k + 1) pivot(k + 1, v[r]);
+      for (int i = 0; i < kP; ++i) v[i] = A[k0 + i][c];
+#pragma unroll
+      for (int m = 0; m < kP; ++m) {
+        const double inv = pinv[k0 + m];
+#pragma unroll
+        for (int i = m + 1; i < kP; ++i) v[i] = v[i] - (A[k0 + m][k0 + i] * inv) * v[m];
       }
+#pragma unroll
+      for (int i = 0; i < kP; ++i) A[k0 + i][c] = v[i];
+    }
+    __syncthreads();
+    // 3. the trailing triangle
+    const int t0 = k0 + kP, nt = W - t0;
+    for (int e = threadIdx.x; e < nt * nt; e += kCholT) {
+      const int i = t0 + e / nt, jj = t0 + e % nt;
+      if (i > jj) continue;
+      double v = A[i][jj];
+#pragma unroll
+      for (int m = 0; m < kP; ++m) v = v - (A[k0 + m][i] * pinv[k0 + m]) * A[k0 + m][jj];
+      A[i][jj] = v;
     }
     __syncthreads();
   }
   // R to the output, its diagonal replaced by 1/R[k][k] (0 for a dropped
   // pivot, whose row of R is 0): what the substitution in k_solve takes
-#pragma unroll
-  for (int r = 0; r < kE; ++r)
-    if (ei[r] < W) Rin.T[ei[r] * kW + ej[r]] = ei[r] == ej[r] ? rinv[ei[r]] : R[ei[r]][ej[r]];
+  for (int e = threadIdx.x; e < W * W; e += kCholT) {
+    const int i = e / W, j = e % W;
+    if (i > j) continue;
+    const double y = rinv[i];
+    Rin.T[i * kW + j] = i == j ? y : (y != 0.0 ? A[i][j] * y : 0.0);
+  }
 }
 
 // 4d. Out = In T (fp64 accumulate), Out[i][c] for c < ncols.
@@ -1265,9 +1305,9 @@ __global__ __launch_bounds__(kST) void k_blk_eig(RGroup g) {
 }
 
 void chol(const RGroup& g, int nb, hipStream_t st) {
-  if (g.w == 32) k_chol<32><<<nb, kCT, 0, st>>>(g);
-  else if (g.w == 48) k_chol<48><<<nb, kCT, 0, st>>>(g);
-  else k_chol<64><<<nb, kCT, 0, st>>>(g);
+  if (g.w == 32) k_chol<32><<<nb, kCholT, 0, st>>>(g);
+  else if (g.w == 48) k_chol<48><<<nb, kCholT, 0, st>>>(g);
+  else k_chol<64><<<nb, kCholT, 0, st>>>(g);
 }
 
 void pack_q(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
