@@ -297,3 +297,25 @@ def test_grouped_covariance_two_batches():
         Ad = host(it["A_out"])
         assert np.array_equal(Ad, Ad.T), k
         assert rel_fro(Ad, A_orc) <= 1e-5, (k, dims[k], toks[k])
+
+
+def test_grouped_covariance_large_group():
+    """Three bf16 inputs with 1134 upper-triangle 128 x 128 tiles in one
+    call (a group that fills the machine without a token split): widths 4112
+    (33 blocks of 128, 16 valid columns in the last), 4096 and 1040; ragged
+    token counts.  Every A against the oracle, exactly symmetric."""
+    dims, toks = [4112, 4096, 1040], [1000, 777, 300]
+    items, ref = [], []
+    for k, (d, n) in enumerate(zip(dims, toks)):
+        spec = synth.InputSpec("w%d" % k, d, n, 1.5, bf16=True)
+        inp = synth.draw_input(spec, seed=3100 + k, as_bf16=True)
+        A = torch.empty(d, d, dtype=torch.float32, device=DEV)
+        items.append(dict(X=inp["X"].to(DEV), factor=fg.Factor(d), A_out=A, seed=k))
+        ref.append(og.covariance(inp["X"].float().numpy()))
+    say("grouped covariance, large group: widths %s" % dims)
+    fg.gift_refresh_factors(items, power_steps=1)
+    torch.cuda.synchronize()
+    for k, (it, A_orc) in enumerate(zip(items, ref)):
+        Ad = host(it["A_out"])
+        assert np.array_equal(Ad, Ad.T), k
+        assert rel_fro(Ad, A_orc) <= 1e-5, (k, dims[k])
