@@ -5,9 +5,10 @@
 // The pages only name the refresh (GIFT review: the input-side factor
 // A = E[a a^T] is refreshed every 50 steps, "Load-bearing premise"; referee
 // report major comment 2 on Algorithm 1) and the rank (32, free-parameter
-// ledger).  Steps, in launch order; every launch covers all inputs of the
-// group (blockIdx.z, or .y, selects the input), so the small serial
-// kernels of different inputs run side by side:
+// ledger).  Steps, in launch order; the covariance launches cover a group of
+// up to kMaxGroup inputs each, every later launch all inputs of the call
+// (blockIdx.z, or .y, selects the input), so the small serial kernels of
+// different inputs run side by side:
 //   1. k_syrk: upper-triangle 128x128 tiles of X^T X on MFMA (bf16 inputs on
 //      v_mfma_f32_16x16x32_bf16, fp32 inputs on v_mfma_f32_16x16x4_f32),
 //      split over token ranges; fp32 partial tiles in the workspace.
@@ -27,6 +28,7 @@
 
 #include <string>
 #include <type_traits>
+#include <vector>
 
 #include "device.hpp"
 
@@ -148,6 +150,33 @@ struct RGroup {
   int sy_begin[kMaxGroup];
   RIn r[kMaxGroup];
 };
+
+// The kernels after the covariance (k_syrk_reduce onwards) run once over a
+// whole chain of inputs, so their latency-bound steps are paid once per call
+// rather than once per kMaxGroup inputs.  A chain of at most kMaxGroup inputs
+// takes its descriptors inline (RGroup); a longer one reads them from an
+// array in the workspace (RChain), written by k_put_desc from each group's
+// kernel arguments before the group's covariance.  Both expose r[i], w, eps
+// and mode, so the chain kernels are templates over the two.
+struct RChain {
+  int n;
+  int w;
+  float eps;
+  int mode;
+  const RIn* r;
+};
+// inputs of one chain launch: grid dimensions stay far below their limits
+constexpr int kChainMax = 1024;
+static_assert(kChainMax % kMaxGroup == 0, "chains hold whole covariance groups");
+static_assert(sizeof(RIn) % 4 == 0, "descriptors are copied as 32-bit words");
+
+// dst[0 .. g.n) = the group's descriptors.  grid: (1), kT threads
+__global__ __launch_bounds__(256) void k_put_desc(RGroup g, RIn* dst) {
+  constexpr int kWords = (int)(sizeof(RIn) / 4);
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(g.r);
+  uint32_t* out = reinterpret_cast<uint32_t*>(dst);
+  for (int e = threadIdx.x; e < g.n * kWords; e += 256) out[e] = src[e];
+}
 
 // ---------------------------------------------------------------------------
 // 1. SYRK partial tiles
@@ -465,7 +494,8 @@ __global__ __launch_bounds__(kT) void k_syrk(RGroup g, int4 idx) {
 // 2. A = (sum_s part[s]) / N over the upper-triangle tiles; each 32-row slab
 // of a tile is summed into LDS and written twice, as rows of the tile and as
 // rows of its mirror image.  grid: (max npairs, inputs)
-__global__ __launch_bounds__(kT) void k_syrk_reduce(RGroup g) {
+template <class G>
+__global__ __launch_bounds__(kT) void k_syrk_reduce(G g) {
   const RIn& R = g.r[blockIdx.y];
   if ((int)blockIdx.x >= R.npairs) return;
   __shared__ float sl[32][kSyrkTile + 1];
@@ -511,7 +541,8 @@ __global__ __launch_bounds__(kT) void k_syrk_reduce(RGroup g) {
 }
 
 // tr(A), fp64, fixed order.  grid: (inputs)
-__global__ __launch_bounds__(kT) void k_trace(RGroup g) {
+template <class G>
+__global__ __launch_bounds__(kT) void k_trace(G g) {
   const RIn& R = g.r[blockIdx.x];
   __shared__ double sh[kT / 64];
   double s = 0.0;
@@ -566,7 +597,8 @@ __global__ __launch_bounds__(kT) void k_sketch_one(float* om, int64_t total, uin
 }
 
 // grid: (blocks for the largest input, inputs); inputs with a given sketch skip
-__global__ __launch_bounds__(kT) void k_sketch(RGroup g) {
+template <class G>
+__global__ __launch_bounds__(kT) void k_sketch(G g) {
   const RIn& R = g.r[blockIdx.y];
   if (R.om != R.om_ws) return;
   sketch_block(R.om_ws, (int64_t)R.d * g.w, R.seed, (int64_t)blockIdx.x * kT + threadIdx.x);
@@ -585,7 +617,8 @@ __global__ __launch_bounds__(kT) void k_sketch(RGroup g) {
 // Rows of Q past d (d % 32 == 16) are zero, and so are A's columns there.
 // ---------------------------------------------------------------------------
 // grid: (max chunks * T * 64 / kT, inputs).  which: 0 = Omega, 1 = Q
-__global__ __launch_bounds__(kT) void k_pack_q(RGroup g, int which) {
+template <class G>
+__global__ __launch_bounds__(kT) void k_pack_q(G g, int which) {
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d, w = g.w, nt = w / 16, nch = (d + 31) / 32;
   const int e = blockIdx.x * kT + threadIdx.x;
@@ -608,7 +641,8 @@ __global__ __launch_bounds__(kT) void k_pack_q(RGroup g, int which) {
 constexpr int kGemmWaves = 4;
 
 // grid: (max d / 16, kYSplit, inputs)
-__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g) {
+template <class G>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
   if ((int)blockIdx.x * 16 >= d) return;
@@ -695,7 +729,8 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(RGroup g) {
 // write the sum to Y for k_apply.
 // grid: (kGramParts * 4, inputs).  which: 0 = Y^T Y, 1 = Q1^T Q1, 2 = Q^T Y
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_gram(RGroup g, int which) {
+template <class G>
+__global__ __launch_bounds__(kT) void k_gram(G g, int which) {
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d, w = g.w;
   const int part = blockIdx.x >> 2, blk = blockIdx.x & 3;
@@ -856,8 +891,8 @@ __device__ __forceinline__ double lane_value(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-template <int W>
-__global__ __launch_bounds__(kCholT) void k_chol(RGroup g) {
+template <int W, class G>
+__global__ __launch_bounds__(kCholT) void k_chol(G g) {
   constexpr int kP = 16;  // panel width
   static_assert(W % kP == 0, "the sketch width is a multiple of 16");
   const RIn& Rin = g.r[blockIdx.x];
@@ -975,7 +1010,8 @@ __global__ __launch_bounds__(kCholT) void k_chol(RGroup g) {
 // 4d. Out = In T (fp64 accumulate), Out[i][c] for c < ncols.
 // grid: (max d / 16, inputs).  which: 0 = Q1 = Y T, 1 = Q = Q1 T, 2 = Q = Y T,
 // 3 = U = Q T[:, :32]
-__global__ __launch_bounds__(kT) void k_apply(RGroup g, int which) {
+template <class G>
+__global__ __launch_bounds__(kT) void k_apply(G g, int which) {
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d, w = g.w;
   if ((int)blockIdx.x * 16 >= d) return;
@@ -1105,8 +1141,8 @@ __device__ __forceinline__ double quad_bcast(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-template <int W>
-__global__ __launch_bounds__(kT) void k_solve(RGroup g, int which) {
+template <int W, class G>
+__global__ __launch_bounds__(kT) void k_solve(G g, int which) {
   constexpr int kM = W / 4;  // columns per lane
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d;
@@ -1154,8 +1190,8 @@ __global__ __launch_bounds__(kT) void k_solve(RGroup g, int which) {
 // 5. Rayleigh-Ritz: the Jacobi eigensolver on B = Q^T A Q, sort,
 // coefficients.  grid: (inputs)
 // ---------------------------------------------------------------------------
-template <int W>
-__global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
+template <int W, class G>
+__global__ __launch_bounds__(kST) void k_ritz(G g) {
   constexpr int kP = W / 2;   // rotations per round
   const RIn& Rin = g.r[blockIdx.x];
   const int d = Rin.d;
@@ -1237,8 +1273,8 @@ __global__ __launch_bounds__(kST) void k_ritz(RGroup g) {
 // W i + a holds row a of S_i, then row a of S_i^-1; theta holds each
 // block's eigenvalues, descending.  grid: (max d / W, inputs)
 // ---------------------------------------------------------------------------
-template <int W>
-__global__ __launch_bounds__(kST) void k_blk_eig(RGroup g) {
+template <int W, class G>
+__global__ __launch_bounds__(kST) void k_blk_eig(G g) {
   constexpr int kP = W / 2;
   const RIn& Rin = g.r[blockIdx.y];
   const int d = Rin.d, i0 = blockIdx.x * W;
@@ -1304,25 +1340,29 @@ __global__ __launch_bounds__(kST) void k_blk_eig(RGroup g) {
   }
 }
 
-void chol(const RGroup& g, int nb, hipStream_t st) {
+template <class G>
+void chol(const G& g, int nb, hipStream_t st) {
   if (g.w == 32) k_chol<32><<<nb, kCholT, 0, st>>>(g);
   else if (g.w == 48) k_chol<48><<<nb, kCholT, 0, st>>>(g);
   else k_chol<64><<<nb, kCholT, 0, st>>>(g);
 }
 
-void pack_q(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
+template <class G>
+void pack_q(const G& g, int which, int maxd, int nb, hipStream_t st) {
   const int n = (maxd + 31) / 32 * (g.w / 16) * 64;
   k_pack_q<<<dim3((unsigned)((n + kT - 1) / kT), nb), kT, 0, st>>>(g, which);
 }
 
-void solve(const RGroup& g, int which, int maxd, int nb, hipStream_t st) {
+template <class G>
+void solve(const G& g, int which, int maxd, int nb, hipStream_t st) {
   const dim3 grid((unsigned)((4 * maxd + kT - 1) / kT), nb);
   if (g.w == 32) k_solve<32><<<grid, kT, 0, st>>>(g, which);
   else if (g.w == 48) k_solve<48><<<grid, kT, 0, st>>>(g, which);
   else k_solve<64><<<grid, kT, 0, st>>>(g, which);
 }
 
-void ritz(const RGroup& g, int nb, hipStream_t st) {
+template <class G>
+void ritz(const G& g, int nb, hipStream_t st) {
   if (g.w == 32) k_ritz<32><<<nb, kST, 0, st>>>(g);
   else if (g.w == 48) k_ritz<48><<<nb, kST, 0, st>>>(g);
   else k_ritz<64><<<nb, kST, 0, st>>>(g);
@@ -1345,8 +1385,12 @@ int64_t batch_pairs(const gift_refresh_input* in, int n, int i) {
   return t;
 }
 
+// the chain's descriptor array at the start of the workspace (only for
+// chains longer than one inline group)
+size_t desc_array_bytes(int n) { return n > kMaxGroup ? al((size_t)n * sizeof(RIn)) : 0; }
+
 size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int width) {
-  size_t t = 0;
+  size_t t = desc_array_bytes(n);
   for (int i = 0; i < n; ++i)
     if (!in[i].factor || in[i].factor->d_in < 1 || in[i].n_tokens < 1) return 0;
   for (int i = 0; i < n; ++i)
@@ -1377,6 +1421,94 @@ gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStre
   if (e != hipSuccess) {
     *err = std::string("gift_draw_sketch: ") + hipGetErrorString(e);
     return GIFT_ERR_HIP;
+  }
+  return GIFT_OK;
+}
+
+// Steps 2 - 5 of the refresh over one chain of nc inputs (descriptors g,
+// host copies hd, the inputs' arguments in): A from the covariance partials,
+// tr(A), then the block-diagonal eigensolve or the sketch, the subspace
+// iteration and the Rayleigh-Ritz step, and the operand packs of the new
+// factors.
+template <class G>
+gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, int nc,
+                      int power_steps, hipStream_t st, std::string* err) {
+  auto bad = [&](gift_status s, const std::string& msg) {
+    *err = "gift_refresh_factors: " + msg;
+    return s;
+  };
+  int maxd = 0, maxpairs = 0;
+  for (int i = 0; i < nc; ++i) {
+    maxd = hd[i].d > maxd ? hd[i].d : maxd;
+    maxpairs = hd[i].npairs > maxpairs ? hd[i].npairs : maxpairs;
+  }
+  const int width = g.w;
+  k_syrk_reduce<<<dim3(maxpairs, nc), kT, 0, st>>>(g);
+  k_trace<<<nc, kT, 0, st>>>(g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+  const int kind = in[0].factor->block;
+  if (kind) {  // block-diagonal factors: per-block eigensolve and packs
+    if (kind == 32) k_blk_eig<32><<<dim3((unsigned)(maxd / 32), nc), kST, 0, st>>>(g);
+    else k_blk_eig<64><<<dim3((unsigned)(maxd / 64), nc), kST, 0, st>>>(g);
+    for (int p0 = 0; p0 < nc; p0 += kMaxGroup) {
+      PackGroup pg{};
+      for (int i = p0; i < nc && i < p0 + kMaxGroup; ++i) {
+        pg.f[pg.n].U = in[i].factor->U;
+        pg.f[pg.n].P = static_cast<uint4*>(in[i].factor->packs);
+        pg.f[pg.n].d_in = in[i].factor->d_in;
+        ++pg.n;
+      }
+      e = launch_blk_pack(pg, kind, st);
+      if (e == hipSuccess) e = hipGetLastError();
+      if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+    }
+    return GIFT_OK;
+  }
+  k_sketch<<<dim3((unsigned)(((int64_t)maxd * width / 4 + kT) / kT), nc), kT, 0, st>>>(g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+  // subspace iteration: Y = A Omega, then power_steps x (Q = orth(Y); Y = A Q)
+  const dim3 rows(maxd / 16, nc), grams(kGramParts * 4, nc), gemm(maxd / 16, kYSplit, nc);
+  pack_q(g, 0, maxd, nc, st);
+  k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
+  for (int s = 0; s < power_steps; ++s) {
+    k_gram<<<grams, kT, 0, st>>>(g, 0);
+    chol(g, nc, st);
+    solve(g, 2, maxd, nc, st);  // Q = Y R^-1
+    pack_q(g, 1, maxd, nc, st);
+    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
+  }
+  // final basis: CholeskyQR2 of Y
+  k_gram<<<grams, kT, 0, st>>>(g, 0);
+  chol(g, nc, st);
+  solve(g, 0, maxd, nc, st);  // Q1 = Y R^-1
+  k_gram<<<grams, kT, 0, st>>>(g, 1);
+  chol(g, nc, st);
+  solve(g, 1, maxd, nc, st);  // Q = Q1 R^-1
+  // Rayleigh-Ritz on B = Q^T A Q
+  pack_q(g, 1, maxd, nc, st);
+  k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);  // Y = A Q
+  k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
+  ritz(g, nc, st);
+  k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V
+  e = hipGetLastError();
+  if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+  // operand packs of the new U, for factors that carry them
+  PackGroup pg{};
+  for (int i = 0; i < nc; ++i) {
+    const gift_factor* f = in[i].factor;
+    if (f->packs) {
+      pg.f[pg.n].U = f->U;
+      pg.f[pg.n].P = static_cast<uint4*>(f->packs);
+      pg.f[pg.n].d_in = f->d_in;
+      ++pg.n;
+    }
+    if (pg.n == kMaxGroup || (i + 1 == nc && pg.n)) {
+      e = launch_pack(pg, st);
+      if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+      pg = PackGroup{};
+    }
   }
   return GIFT_OK;
 }
@@ -1430,24 +1562,18 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
                "workspace too small (" + std::to_string(ws_bytes) + " < " + std::to_string(need) + ")");
   if (!ws || ((uintptr_t)ws & 255u)) return bad(GIFT_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
 
-  for (int b0 = 0; b0 < n; b0 += kMaxGroup) {
-    const int nb = n - b0 < kMaxGroup ? n - b0 : kMaxGroup;
-    RGroup g{};
-    g.n = nb;
-    g.w = width;
-    g.eps = damp_eps;
-    g.mode = damping_mode;
-    char* base = static_cast<char*>(ws);
-    for (int i = 0; i < b0; ++i)
-      base += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_pairs(in, n, i)).total;
-    int maxd = 0, maxpairs = 0, maxsplit = 0;
-    for (int i = 0; i < nb; ++i) {
-      const gift_refresh_input& r = in[b0 + i];
+  // descriptors of every input, in call order
+  std::vector<RIn> desc((size_t)n);
+  {
+    char* base = static_cast<char*>(ws) + desc_array_bytes(n);
+    for (int i = 0; i < n; ++i) {
+      const gift_refresh_input& r = in[i];
       const int d = r.factor->d_in;
-      const int64_t bp = batch_pairs(in, n, b0 + i);
+      const int64_t bp = batch_pairs(in, n, i);
       const WsLayout L = ws_layout(d, r.n_tokens, width, bp);
       const SyrkPlan p = syrk_plan(d, r.n_tokens, bp);
-      RIn& x = g.r[i];
+      RIn& x = desc[i];
+      x = RIn{};
       x.X = r.X;
       x.A = r.A_out ? r.A_out : reinterpret_cast<float*>(base + L.A);
       x.part = reinterpret_cast<float*>(base + L.part);
@@ -1473,92 +1599,60 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       x.npairs = p.npairs;
       x.nsplit = p.nsplit;
       base += L.total;
-      maxd = d > maxd ? d : maxd;
-      maxpairs = p.npairs > maxpairs ? p.npairs : maxpairs;
-      maxsplit = p.nsplit > maxsplit ? p.nsplit : maxsplit;
     }
-    // 1. covariance: bf16 inputs in one launch over a work list, fp32 inputs
-    // (<= 4 per launch) on a (pair, split, input) grid
-    {
-      int wg = 0;
-      g.sy_n = 0;
-      for (int i = 0; i < nb; ++i)
-        if (in[b0 + i].x_dtype == GIFT_DTYPE_BF16) {
-          g.sy_in[g.sy_n] = i;
-          g.sy_begin[g.sy_n++] = wg;
-          wg += g.r[i].npairs * g.r[i].nsplit;
-        }
-      if (wg) k_syrk_bf16<<<dim3(wg), kT, 0, st>>>(g);
-      int sel[kMaxGroup], ns = 0;
-      for (int i = 0; i < nb; ++i)
-        if (in[b0 + i].x_dtype == GIFT_DTYPE_F32) sel[ns++] = i;
-      for (int k = 0; k < ns; k += 4) {
-        const int m = ns - k < 4 ? ns - k : 4;
-        int4 idx = make_int4(sel[k], m > 1 ? sel[k + 1] : 0, m > 2 ? sel[k + 2] : 0, m > 3 ? sel[k + 3] : 0);
-        k_syrk<false><<<dim3(maxpairs, maxsplit, m), kT, 0, st>>>(g, idx);
-      }
-    }
-    k_syrk_reduce<<<dim3(maxpairs, nb), kT, 0, st>>>(g);
-    k_trace<<<nb, kT, 0, st>>>(g);
-    const int kind = in[b0].factor->block;
-    if (kind) {  // block-diagonal factors: per-block eigensolve and packs
-      if (kind == 32) k_blk_eig<32><<<dim3((unsigned)(maxd / 32), nb), kST, 0, st>>>(g);
-      else k_blk_eig<64><<<dim3((unsigned)(maxd / 64), nb), kST, 0, st>>>(g);
-      PackGroup pg{};
-      for (int i = 0; i < nb; ++i) {
-        pg.f[i].U = in[b0 + i].factor->U;
-        pg.f[i].P = static_cast<uint4*>(in[b0 + i].factor->packs);
-        pg.f[i].d_in = in[b0 + i].factor->d_in;
-      }
-      pg.n = nb;
-      hipError_t e = launch_blk_pack(pg, kind, st);
-      if (e == hipSuccess) e = hipGetLastError();
-      if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
-      continue;
-    }
-    k_sketch<<<dim3((unsigned)(((int64_t)maxd * width / 4 + kT) / kT), nb), kT, 0, st>>>(g);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
-    // 2. subspace iteration: Y = A Omega, then power_steps x (Q = orth(Y); Y = A Q)
-    const dim3 rows(maxd / 16, nb), grams(kGramParts * 4, nb), gemm(maxd / 16, kYSplit, nb);
-    pack_q(g, 0, maxd, nb, st);
-    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
-    for (int s = 0; s < power_steps; ++s) {
-      k_gram<<<grams, kT, 0, st>>>(g, 0);
-      chol(g, nb, st);
-      solve(g, 2, maxd, nb, st);  // Q = Y R^-1
-      pack_q(g, 1, maxd, nb, st);
-      k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
-    }
-    // final basis: CholeskyQR2 of Y
-    k_gram<<<grams, kT, 0, st>>>(g, 0);
-    chol(g, nb, st);
-    solve(g, 0, maxd, nb, st);  // Q1 = Y R^-1
-    k_gram<<<grams, kT, 0, st>>>(g, 1);
-    chol(g, nb, st);
-    solve(g, 1, maxd, nb, st);  // Q = Q1 R^-1
-    // 3. Rayleigh-Ritz on B = Q^T A Q
-    pack_q(g, 1, maxd, nb, st);
-    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);  // Y = A Q
-    k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
-    ritz(g, nb, st);
-    k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V
-    e = hipGetLastError();
-    if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
-    // 4. operand packs of the new U, for factors that carry them
-    PackGroup pg{};
+  }
+  RIn* dev_desc = n > kMaxGroup ? static_cast<RIn*>(ws) : nullptr;
+  auto group_of = [&](int b0, int nb) {
+    RGroup g{};
+    g.n = nb;
+    g.w = width;
+    g.eps = damp_eps;
+    g.mode = damping_mode;
+    for (int i = 0; i < nb; ++i) g.r[i] = desc[b0 + i];
+    return g;
+  };
+
+  // 1. covariance, one group of kMaxGroup inputs per launch: bf16 inputs over
+  // a work list, fp32 inputs (<= 4 per launch) on a (pair, split, input) grid
+  for (int b0 = 0; b0 < n; b0 += kMaxGroup) {
+    const int nb = n - b0 < kMaxGroup ? n - b0 : kMaxGroup;
+    RGroup g = group_of(b0, nb);
+    if (dev_desc) k_put_desc<<<1, 256, 0, st>>>(g, dev_desc + b0);
+    int wg = 0, maxpairs = 0, maxsplit = 0;
+    g.sy_n = 0;
     for (int i = 0; i < nb; ++i) {
-      const gift_factor* f = in[b0 + i].factor;
-      if (!f->packs) continue;
-      pg.f[pg.n].U = f->U;
-      pg.f[pg.n].P = static_cast<uint4*>(f->packs);
-      pg.f[pg.n].d_in = f->d_in;
-      ++pg.n;
+      maxpairs = g.r[i].npairs > maxpairs ? g.r[i].npairs : maxpairs;
+      maxsplit = g.r[i].nsplit > maxsplit ? g.r[i].nsplit : maxsplit;
+      if (in[b0 + i].x_dtype == GIFT_DTYPE_BF16) {
+        g.sy_in[g.sy_n] = i;
+        g.sy_begin[g.sy_n++] = wg;
+        wg += g.r[i].npairs * g.r[i].nsplit;
+      }
     }
-    if (pg.n) {
-      e = launch_pack(pg, st);
-      if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+    if (wg) k_syrk_bf16<<<dim3(wg), kT, 0, st>>>(g);
+    int sel[kMaxGroup], ns = 0;
+    for (int i = 0; i < nb; ++i)
+      if (in[b0 + i].x_dtype == GIFT_DTYPE_F32) sel[ns++] = i;
+    for (int k = 0; k < ns; k += 4) {
+      const int m = ns - k < 4 ? ns - k : 4;
+      int4 idx = make_int4(sel[k], m > 1 ? sel[k + 1] : 0, m > 2 ? sel[k + 2] : 0, m > 3 ? sel[k + 3] : 0);
+      k_syrk<false><<<dim3(maxpairs, maxsplit, m), kT, 0, st>>>(g, idx);
     }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+
+  // 2. - 5. the rest, one chain over up to kChainMax inputs
+  for (int c0 = 0; c0 < n; c0 += kChainMax) {
+    const int nc = n - c0 < kChainMax ? n - c0 : kChainMax;
+    gift_status s;
+    if (dev_desc) {
+      RChain g{nc, width, damp_eps, damping_mode, dev_desc + c0};
+      s = run_chain(g, desc.data() + c0, in + c0, nc, power_steps, st, err);
+    } else {
+      s = run_chain(group_of(c0, nc), desc.data() + c0, in + c0, nc, power_steps, st, err);
+    }
+    if (s != GIFT_OK) return s;
   }
   return GIFT_OK;
 }

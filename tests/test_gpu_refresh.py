@@ -319,3 +319,45 @@ def test_grouped_covariance_large_group():
         Ad = host(it["A_out"])
         assert np.array_equal(Ad, Ad.T), k
         assert rel_fro(Ad, A_orc) <= 1e-5, (k, dims[k])
+
+
+def test_chained_refresh_many_inputs():
+    """Thirty-seven inputs in one call (three covariance groups, the last
+    ragged; bf16 and fp32; widths 128 .. 384; ragged token counts): the chain
+    after the covariance runs once over all of them with its descriptors in
+    the workspace.  Every factor against the oracle, the operand packs equal
+    gift_prepare_factor's, and the first sixteen (one whole covariance group,
+    so the same covariance plan) bit-identical to a call of those sixteen
+    alone, whose chain takes its descriptors as kernel arguments."""
+    dims = [128, 192, 256, 320, 384, 160]
+    toks = [700, 1500, 2048, 900, 1333]
+    n = 37
+    items, ref = [], []
+    for k in range(n):
+        d, t = dims[k % len(dims)], toks[k % len(toks)]
+        bf16 = k % 5 != 3
+        spec = synth.InputSpec("c%d" % k, d, t, 1.2 + 0.1 * (k % 6), bf16=bf16)
+        inp = synth.draw_input(spec, seed=4000 + k, as_bf16=bf16)
+        om = synth.gaussian_sketch(d, 64, seed=4100 + k)
+        X = inp["X"].to(DEV)
+        items.append(dict(X=X, factor=fg.Factor(d), sketch=om.to(DEV)))
+        ref.append((inp["X"].float().numpy(), om.numpy().astype(np.float64)))
+    say("chained refresh: %d inputs" % n)
+    fg.gift_refresh_factors(items)
+    torch.cuda.synchronize()
+    for k, (it, (Xh, om)) in enumerate(zip(items, ref)):
+        f_orc = og.refresh_factor(Xh, om)
+        P = np.random.default_rng(40 + k).standard_normal((16, Xh.shape[1]))
+        _check_factor(it["factor"], f_orc, P)
+        packs = it["factor"].packs.clone()
+        fg.gift_prepare_factor(it["factor"])
+        assert torch.equal(packs, it["factor"].packs), k
+    say("chained refresh: first 16 inputs alone")
+    alone = [dict(X=it["X"], factor=fg.Factor(it["factor"].d_in), sketch=it["sketch"])
+             for it in items[:16]]
+    fg.gift_refresh_factors(alone)
+    torch.cuda.synchronize()
+    for k, (a, it) in enumerate(zip(alone, items[:16])):
+        fa, fb = a["factor"], it["factor"]
+        assert torch.equal(fa.U, fb.U) and torch.equal(fa.theta, fb.theta), k
+        assert torch.equal(fa.coef, fb.coef) and torch.equal(fa.packs, fb.packs), k
