@@ -612,8 +612,7 @@ __global__ __launch_bounds__(kT) void k_sketch(G g) {
 // Q), column tile t and split s, element i of lane l (r16 = l % 16,
 // g = l / 16) = Q[32c + 8g + i][16t + r16], at ((c T + t) 3 + s) 64 + l
 // (T = w / 16).  In k_gemm_aq lane l holds A[row0 + r16][32c + 8g .. +7],
-// split as it is loaded.  Workgroup: 16 rows of one partial; its 4 waves
-// split the K range further and are summed in wave order through LDS.
+// split as it is loaded.
 // Rows of Q past d (d % 32 == 16) are zero, and so are A's columns there.
 // ---------------------------------------------------------------------------
 // grid: (max chunks * T * 64 / kT, inputs).  which: 0 = Omega, 1 = Q
@@ -639,25 +638,36 @@ __global__ __launch_bounds__(kT) void k_pack_q(G g, int which) {
 }
 
 constexpr int kGemmWaves = 4;
+// workgroups of 64-row shape from which a call takes that shape (eight per CU)
+constexpr int64_t kGemmRowTileMin = 2048;
 
-// grid: (max d / 16, kYSplit, inputs)
-template <class G>
+// Two workgroup shapes (four waves each):
+//   kRowTiles = false: 16 rows of one partial; the waves split the partial's
+//     K range into four and their sums are added in wave order through LDS.
+//     grid: (max d / 16, kYSplit, inputs).
+//   kRowTiles = true: 64 rows of one partial, each wave 16 of them over the
+//     partial's whole K range; the four waves read the same Q packs at about
+//     the same time, so most of those reads hit in cache, and each wave's
+//     pipeline runs four times as long.  grid: (max d / 64, kYSplit, inputs).
+// The second needs a quarter of the workgroups, so it is taken only when a
+// call has enough rows to fill the machine with it.
+template <bool kRowTiles, class G>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
-  if ((int)blockIdx.x * 16 >= d) return;
-  const float* __restrict__ A = R.A;
-  __shared__ float red[kGemmWaves][16][kW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = kRowTiles ? (blockIdx.x * kGemmWaves + wave) * 16 : blockIdx.x * 16;
+  if (row0 >= d) return;  // uniform over the wave (kRowTiles: no barrier follows) or workgroup
+  const float* __restrict__ A = R.A;
   const int r16 = lane & 15, gq = lane >> 4;
-  const int row0 = blockIdx.x * 16;
   const int ntile = w / 16;
   f32x4 acc[kW / 16];
 #pragma unroll
   for (int t = 0; t < kW / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int kchunks = (d + 31) / 32, slice = blockIdx.y * kGemmWaves + wave;
-  constexpr int kSlices = kYSplit * kGemmWaves;
-  const int kc_begin = slice * kchunks / kSlices, kc_end = (slice + 1) * kchunks / kSlices;
+  const int kchunks = (d + 31) / 32;
+  const int slices = kRowTiles ? kYSplit : kYSplit * kGemmWaves;
+  const int slice = kRowTiles ? blockIdx.y : blockIdx.y * kGemmWaves + wave;
+  const int kc_begin = slice * kchunks / slices, kc_end = (slice + 1) * kchunks / slices;
   const float* arow = A + (int64_t)(row0 + r16) * d;
   // one K chunk of 32: this lane's 8 values of A's row and its packs of Q
   struct Chunk {
@@ -702,19 +712,41 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
     }
   }
   // D layout: lane holds rows 4 gq .. 4 gq + 3 of column r16 of each 16x16 tile
-#pragma unroll
-  for (int t = 0; t < kW / 16; ++t)
-    if (t < ntile)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][4 * gq + i][16 * t + r16] = acc[t][i];
-  __syncthreads();
   float* __restrict__ Yp = R.Yp + (size_t)blockIdx.y * d * w;
-  for (int e = threadIdx.x; e < 16 * w; e += 64 * kGemmWaves) {
-    const int r = e / w, c = e % w;
-    float s = red[0][r][c];
+  if constexpr (kRowTiles) {
 #pragma unroll
-    for (int v = 1; v < kGemmWaves; ++v) s += red[v][r][c];
-    Yp[(int64_t)(row0 + r) * w + c] = s;
+    for (int t = 0; t < kW / 16; ++t)
+      if (t < ntile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Yp[(int64_t)(row0 + 4 * gq + i) * w + 16 * t + r16] = acc[t][i];
+  } else {
+    __shared__ float red[kGemmWaves][16][kW];
+#pragma unroll
+    for (int t = 0; t < kW / 16; ++t)
+      if (t < ntile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][4 * gq + i][16 * t + r16] = acc[t][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * w; e += 64 * kGemmWaves) {
+      const int r = e / w, c = e % w;
+      float s = red[0][r][c];
+#pragma unroll
+      for (int v = 1; v < kGemmWaves; ++v) s += red[v][r][c];
+      Yp[(int64_t)(row0 + r) * w + c] = s;
+    }
+  }
+}
+
+// Y = A Q for every input of a chain, in the workgroup shape its size suits
+template <class G>
+void gemm_aq(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
+  int64_t tiles = 0;
+  for (int i = 0; i < nc; ++i) tiles += (hd[i].d + 16 * kGemmWaves - 1) / (16 * kGemmWaves);
+  if (tiles * kYSplit >= kGemmRowTileMin) {
+    const dim3 grid((maxd + 16 * kGemmWaves - 1) / (16 * kGemmWaves), kYSplit, nc);
+    k_gemm_aq<true><<<grid, 64 * kGemmWaves, 0, st>>>(g);
+  } else {
+    k_gemm_aq<false><<<dim3(maxd / 16, kYSplit, nc), 64 * kGemmWaves, 0, st>>>(g);
   }
 }
 
@@ -1469,15 +1501,15 @@ gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, i
   e = hipGetLastError();
   if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
   // subspace iteration: Y = A Omega, then power_steps x (Q = orth(Y); Y = A Q)
-  const dim3 rows(maxd / 16, nc), grams(kGramParts * 4, nc), gemm(maxd / 16, kYSplit, nc);
+  const dim3 rows(maxd / 16, nc), grams(kGramParts * 4, nc);
   pack_q(g, 0, maxd, nc, st);
-  k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
+  gemm_aq(g, hd, nc, maxd, st);
   for (int s = 0; s < power_steps; ++s) {
     k_gram<<<grams, kT, 0, st>>>(g, 0);
     chol(g, nc, st);
     solve(g, 2, maxd, nc, st);  // Q = Y R^-1
     pack_q(g, 1, maxd, nc, st);
-    k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);
+    gemm_aq(g, hd, nc, maxd, st);
   }
   // final basis: CholeskyQR2 of Y
   k_gram<<<grams, kT, 0, st>>>(g, 0);
@@ -1488,7 +1520,7 @@ gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, i
   solve(g, 1, maxd, nc, st);  // Q = Q1 R^-1
   // Rayleigh-Ritz on B = Q^T A Q
   pack_q(g, 1, maxd, nc, st);
-  k_gemm_aq<<<gemm, 64 * kGemmWaves, 0, st>>>(g);  // Y = A Q
+  gemm_aq(g, hd, nc, maxd, st);  // Y = A Q
   k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
   ritz(g, nc, st);
   k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V

@@ -361,3 +361,34 @@ def test_chained_refresh_many_inputs():
         fa, fb = a["factor"], it["factor"]
         assert torch.equal(fa.U, fb.U) and torch.equal(fa.theta, fb.theta), k
         assert torch.equal(fa.coef, fb.coef) and torch.equal(fa.packs, fb.packs), k
+
+
+def test_chained_refresh_wide_inputs():
+    """Twenty-four bf16 inputs of width 1536 in one call: enough rows that
+    Y = A Q runs in its 64-row workgroup shape.  Inputs 0, 11 and 23 against
+    the oracle (same sketch); every factor's U orthonormal and theta equal to
+    its Rayleigh quotients u^T A u."""
+    n, d, t = 24, 1536, 2048
+    items, ref = [], []
+    for k in range(n):
+        spec = synth.InputSpec("w%d" % k, d, t, 1.3 + 0.02 * k, bf16=True)
+        inp = synth.draw_input(spec, seed=4200 + k, as_bf16=True)
+        om = synth.gaussian_sketch(d, 64, seed=4300 + k)
+        items.append(dict(X=inp["X"].to(DEV), factor=fg.Factor(d), sketch=om.to(DEV)))
+        ref.append((inp["X"], om))
+    say("chained refresh: %d inputs of width %d" % (n, d))
+    fg.gift_refresh_factors(items)
+    torch.cuda.synchronize()
+    for k, it in enumerate(items):
+        X = it["X"].double()
+        A = X.T @ X / X.shape[0]
+        U = it["factor"].U.double()
+        th = it["factor"].theta.double()
+        assert float(torch.linalg.norm(U.T @ U - torch.eye(32, dtype=U.dtype, device=U.device))) < 1e-5, k
+        rq = ((A @ U) * U).sum(0)
+        assert float((rq - th).abs().max() / th[0]) < 1e-5, k
+    for k in (0, 11, 23):
+        Xh, om = ref[k]
+        f_orc = og.refresh_factor(Xh.float().numpy(), om.numpy().astype(np.float64))
+        P = np.random.default_rng(60 + k).standard_normal((16, d))
+        _check_factor(items[k]["factor"], f_orc, P)
