@@ -141,6 +141,23 @@ def test_refresh_validation():
     assert lib.gift_draw_sketch(None, 10, 64, 0, None) == 1
 
 
+def test_refresh_workspace_holds_chain_descriptors():
+    """A call of more than 16 inputs needs, on top of its inputs' own
+    workspaces (the covariance groups of 16 in call order), room for the
+    per-input descriptors of its chain: 256-byte aligned, 176 bytes each."""
+    lib = fg.load()
+    facs = [_lib._Factor(d, 32, 0x20000, 0x30000, 0x40000, None) for d in (128, 256, 384)]
+    r = (_lib._RefreshInput * 17)()
+    for k in range(17):
+        r[k].X, r[k].x_dtype, r[k].n_tokens = 0x60000, fg.DTYPE_BF16, 1000 + 37 * k
+        r[k].factor = ctypes.pointer(facs[k % 3])
+    need16 = lib.gift_refresh_group_workspace_bytes(r, 16, 64)
+    need17 = lib.gift_refresh_group_workspace_bytes(r, 17, 64)
+    alone = lib.gift_refresh_workspace_bytes(facs[16 % 3].d_in, r[16].n_tokens, fg.DTYPE_BF16, 64)
+    assert need16 > 0 and alone > 0
+    assert need17 == need16 + alone + (17 * 176 + 255) // 256 * 256
+
+
 def test_block_factor_validation():
     """block-A factors: sizes of the packs, and the argument errors that come
     back before any launch."""
