@@ -139,3 +139,36 @@ def test_prepare_factor_packs_match_refresh():
     g = fg.Factor(256, U=f.U.clone(), theta=f.theta.clone(), coef=f.coef.clone(), block=64)
     fg.gift_prepare_factor(g)
     assert torch.equal(g.packs, f.packs)
+
+
+def test_grouped_block_refresh_chain():
+    """Eighteen block-32 factors (widths 128, 192, 256; bf16 and fp32
+    inputs) in one refresh call, so the eigensolve runs over the whole call
+    with its descriptors in the workspace and the packs go out in two
+    groups: each factor against the oracle's block factor of the device's A,
+    its packs equal to gift_prepare_factor's."""
+    dims = [128, 192, 256]
+    items = []
+    for k in range(18):
+        d = dims[k % 3]
+        bf16 = k % 4 != 1
+        spec = synth.InputSpec("b%d" % k, d, 1500 + 100 * k, 1.5, bf16=bf16)
+        inp = synth.draw_input(spec, seed=500 + k, as_bf16=bf16)
+        A = torch.empty(d, d, dtype=torch.float32, device=DEV)
+        items.append(dict(X=inp["X"].to(DEV), factor=fg.Factor(d, block=32), A_out=A))
+    say("grouped block-32 refresh: %d inputs" % len(items))
+    fg.gift_refresh_factors(items)
+    torch.cuda.synchronize()
+    for k, it in enumerate(items):
+        f = it["factor"]
+        d = f.d_in
+        bo = og.block_factor(host(it["A_out"]).astype(np.float64), 32)
+        S, Si, th = host(f.S), host(f.S_inv), host(f.theta)
+        for i in range(d // 32):
+            sl = slice(i * 32, (i + 1) * 32)
+            assert rel_fro(S[sl], bo.S[sl]) <= TOL, (k, i)
+            assert rel_fro(Si[sl], bo.S_inv[sl]) <= TOL, (k, i)
+            assert np.allclose(th[sl], bo.theta[sl], rtol=1e-5, atol=1e-6 * bo.theta[sl][0]), (k, i)
+        g = fg.Factor(d, U=f.U.clone(), theta=f.theta.clone(), coef=f.coef.clone(), block=32)
+        fg.gift_prepare_factor(g)
+        assert torch.equal(g.packs, f.packs), k
