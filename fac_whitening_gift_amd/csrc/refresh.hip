@@ -169,6 +169,7 @@ struct RChain {
 constexpr int kChainMax = 1024;
 static_assert(kChainMax % kMaxGroup == 0, "chains hold whole covariance groups");
 static_assert(sizeof(RIn) % 4 == 0, "descriptors are copied as 32-bit words");
+static_assert(sizeof(RIn) == 176, "the workspace size query counts 176 bytes per descriptor");
 
 // dst[0 .. g.n) = the group's descriptors.  grid: (1), kT threads
 __global__ __launch_bounds__(256) void k_put_desc(RGroup g, RIn* dst) {

@@ -218,12 +218,16 @@ size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens,
 
 /*
  * gift_refresh_factors -- gift_refresh_factor for n inputs in one grouped
- * pass: every launch covers all inputs, so the small serial steps of the
- * eigensolve of different inputs run concurrently.  Per input: X (device,
+ * pass: the covariance runs in launches of up to 16 inputs (in call order),
+ * every later launch covers all inputs (up to 1024 at a time), so the small
+ * serial steps of the eigensolve of different inputs run concurrently and
+ * their latency is paid once per call.  Per input: X (device,
  * n_tokens x factor->d_in, x_dtype), factor (host struct, device buffers
  * written), sketch / A_out optional as above, seed of its Philox sketch.
- * The scalar arguments apply to every input.  The workspace is laid out per
- * input in order; query it with gift_refresh_group_workspace_bytes.
+ * The scalar arguments apply to every input; all factors of one call are of
+ * one kind (rank-r or the same block size).  The workspace holds, for
+ * n > 16, the inputs' launch descriptors, then each input's own area in
+ * order; query it with gift_refresh_group_workspace_bytes.
  */
 typedef struct gift_refresh_input {
     const void *X;
