@@ -392,3 +392,30 @@ def test_chained_refresh_wide_inputs():
         f_orc = og.refresh_factor(Xh.float().numpy(), om.numpy().astype(np.float64))
         P = np.random.default_rng(60 + k).standard_normal((16, d))
         _check_factor(items[k]["factor"], f_orc, P)
+
+
+def test_refresh_more_inputs_than_one_chain():
+    """1025 small inputs in one call: two chains (1024 inputs, then 1), each
+    reading its descriptors from the workspace.  Results depend only on an
+    input's own covariance group, so the lone last input equals a refresh of
+    that input alone and the first sixteen equal a call of those sixteen,
+    bit for bit."""
+    n, d = 1025, 128
+    items = []
+    for k in range(n):
+        g = torch.Generator().manual_seed(5000 + k)
+        X = (torch.randn(96 + k % 7, d, generator=g) * (1.0 + (k % 5))).to(torch.bfloat16)
+        items.append(dict(X=X.to(DEV), factor=fg.Factor(d), seed=k))
+    say("refresh of %d inputs (two chains)" % n)
+    fg.gift_refresh_factors(items, power_steps=2)
+    torch.cuda.synchronize()
+    alone = [dict(X=items[-1]["X"], factor=fg.Factor(d), seed=n - 1)]
+    fg.gift_refresh_factors(alone, power_steps=2)
+    first = [dict(X=it["X"], factor=fg.Factor(d), seed=k) for k, it in enumerate(items[:16])]
+    fg.gift_refresh_factors(first, power_steps=2)
+    torch.cuda.synchronize()
+    for a, b in [(alone[0], items[-1])] + list(zip(first, items[:16])):
+        fa, fb = a["factor"], b["factor"]
+        assert bool(torch.isfinite(fb.U).all()) and bool(torch.isfinite(fb.coef).all())
+        assert torch.equal(fa.U, fb.U) and torch.equal(fa.theta, fb.theta)
+        assert torch.equal(fa.coef, fb.coef) and torch.equal(fa.packs, fb.packs)
