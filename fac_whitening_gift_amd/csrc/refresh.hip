@@ -396,16 +396,46 @@ __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
     if (st + 5 < steps) step(st + 5, I2{}, I1{});
   }
   // D layout: lane holds rows 4gq..4gq+3 of column r16 of each 16x16 tile
-  float* out = R.part + ((size_t)split * R.npairs + pair) * kSyrkTile * kSyrkTile;
+  if (R.part) {
+    float* out = R.part + ((size_t)split * R.npairs + pair) * kSyrkTile * kSyrkTile;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 64 * wi + 16 * a + 4 * gq + i, c = 64 * wj + 16 * b + r16;
+          out[r * kSyrkTile + c] = acc[a][b][i];
+        }
+    return;
+  }
+  // One token range (no partials): A = acc / N written here, as k_syrk_reduce
+  // would -- the tile's upper part and its mirror image, by the same division.
+  // The mirror of a lane's four rows is four consecutive columns of row j.
+  const bool diag = bi == bj;
+  const float fn = (float)R.N;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b) {
+      const int r0 = 64 * wi + 16 * a + 4 * gq, c = 64 * wj + 16 * b + r16;
+      const int i0 = ci0 + r0, j = cj0 + c;
+      if (i0 >= d || j >= d) continue;  // d % 16 == 0: rows i0 .. i0 + 3 are all in or all out
+      float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wi + 16 * a + 4 * gq + i, c = 64 * wj + 16 * b + r16;
-        out[r * kSyrkTile + c] = acc[a][b][i];
+      for (int i = 0; i < 4; ++i) v[i] = acc[a][b][i] / fn;
+      if (!diag) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R.A[(int64_t)(i0 + i) * d + j] = v[i];
+        *reinterpret_cast<float4*>(R.A + (int64_t)j * d + i0) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (r0 + i <= c) R.A[(int64_t)(i0 + i) * d + j] = v[i];
+          if (r0 + i < c) R.A[(int64_t)j * d + i0 + i] = v[i];
+        }
       }
+    }
 }
 
 // grid: (max npairs, max nsplit, inputs of this dtype); idx maps z -> input
@@ -498,7 +528,7 @@ __global__ __launch_bounds__(kT) void k_syrk(RGroup g, int4 idx) {
 template <class G>
 __global__ __launch_bounds__(kT) void k_syrk_reduce(G g) {
   const RIn& R = g.r[blockIdx.y];
-  if ((int)blockIdx.x >= R.npairs) return;
+  if ((int)blockIdx.x >= R.npairs || !R.part) return;  // no partials: A written by k_syrk_bf16
   __shared__ float sl[32][kSyrkTile + 1];
   int bi, bj;
   decode_pair(blockIdx.x, R.nb, bi, bj);
@@ -1609,7 +1639,10 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       x = RIn{};
       x.X = r.X;
       x.A = r.A_out ? r.A_out : reinterpret_cast<float*>(base + L.A);
-      x.part = reinterpret_cast<float*>(base + L.part);
+      // a bf16 input with one token range has its A written by the covariance
+      // kernel itself (no partial tiles)
+      x.part = r.x_dtype == GIFT_DTYPE_BF16 && p.nsplit == 1 ? nullptr
+                                                           : reinterpret_cast<float*>(base + L.part);
       x.om_ws = reinterpret_cast<float*>(base + L.om);
       x.om = r.sketch ? r.sketch : x.om_ws;
       x.Y = reinterpret_cast<float*>(base + L.y);
