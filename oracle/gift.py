@@ -32,7 +32,10 @@ implementation's reading, each marked where it is taken:
    D_u = (Theta + lambda_iso)^{1/2} - lambda_iso^{1/2}.
 6. Per-tensor E4M3 quantization of the whitened fp32 tensor W:
    amax = max |W|; scale = fl32(448 / amax); inv = fl32(amax / 448);
-   code = E4M3(fl32(W * scale)); amax == 0 gives scale = inv = 1.
+   code = E4M3(fl32(W * scale)); amax == 0 gives scale = inv = 1.  A
+   finite amax so small that 448 / amax overflows fp32 (below 448 /
+   FLT_MAX, about 1.3e-36) gets the largest finite fp32 as its scale, so
+   zeros stay zeros and no finite input turns into a NaN code (reading).
 7. Dequantize W^ = fl32(decode(code) * inv); un-whiten G^ = W^ A_r^{1/2}.
 8. A data-parallel reduction of R payloads (the ranks' quantized whitened
    gradients summed in the collective) is read as fp32 additions of the
@@ -258,8 +261,10 @@ def scale_from_amax(a):
     if a == 0:
         return np.float32(1.0), np.float32(1.0), flags | FLAG_ZERO_AMAX
     with np.errstate(all="ignore"):
-        scale = np.float32(e4m3.MAX_FINITE) / a
+        scale = np.float32(np.float32(e4m3.MAX_FINITE) / a)
         inv = a / np.float32(e4m3.MAX_FINITE)
+    if np.isfinite(a) and np.isinf(scale):
+        scale = np.finfo(np.float32).max   # 448 / amax overflows: largest finite scale
     return np.float32(scale), np.float32(inv), flags
 
 
@@ -304,6 +309,7 @@ def quantize_block128(w32):
 
 
 def dequantize_block128(codes, inv):
+    """W^ = fl32(decode(code) * inv of the code's 128-element row segment)."""
     codes = np.asarray(codes, dtype=np.uint8)
     inv_full = np.repeat(np.asarray(inv, dtype=np.float32), BLOCK, axis=1)
     with np.errstate(all="ignore"):

@@ -317,3 +317,104 @@ def test_unwhitened_sum_of_whitened_gradients_is_the_sum_of_gradients():
     Gs = [rng.standard_normal((7, 96)) for _ in range(4)]
     S = sum(og.whiten(G, f) for G in Gs)
     assert np.allclose(og.unwhiten(S, f), sum(Gs), rtol=1e-10, atol=1e-10)
+
+
+# --------------------------------------------------------------------------- pins added for
+# the block-scaled dequantization, the K-FAC metric and the tiny-amax scale
+
+def test_dequantize_block128_uses_each_segments_own_scale():
+    """Hand-built codes: row i, segment b holds code 0x38 (1.0) except one
+    0x3C (1.5) at column 5 of the segment; the inverse scales are distinct
+    powers of two per (row, segment), so a segment-to-scale mix-up (tiling
+    the scales along the row instead of repeating them, or transposing them)
+    changes the result."""
+    d_out, nseg = 3, 4
+    codes = np.full((d_out, nseg * 128), 0x38, dtype=np.uint8)
+    inv = np.empty((d_out, nseg), dtype=np.float32)
+    for i in range(d_out):
+        for b in range(nseg):
+            codes[i, 128 * b + 5] = 0x3C
+            inv[i, b] = np.float32(2.0 ** (4 * i + b - 6))
+    W = og.dequantize_block128(codes, inv)
+    assert W.dtype == np.float32 and W.shape == codes.shape
+    for i in range(d_out):
+        for b in range(nseg):
+            s = 2.0 ** (4 * i + b - 6)
+            seg = W[i, 128 * b:128 * (b + 1)]
+            assert seg[5] == 1.5 * s
+            assert np.all(np.delete(seg, 5) == s)
+    # round trip of per-segment quantization: every segment's largest element
+    # comes back as +-448 times its own segment's inverse scale, within one
+    # ulp of the element (segments differ in scale by up to 1e5)
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((2, 256)) * np.array([[1.0], [1e3]])).astype(np.float32)
+    w[:, 128:] *= np.float32(1e-2)
+    c, s, _ = og.quantize_block128(w)
+    back = og.dequantize_block128(c, s)
+    for i in range(2):
+        for b in range(2):
+            seg = w[i, 128 * b:128 * (b + 1)]
+            k = np.argmax(np.abs(seg))
+            assert back[i, 128 * b + k] == np.float32(np.sign(seg[k]) * 448) * s[i, b]
+            assert abs(back[i, 128 * b + k] - seg[k]) <= np.spacing(np.abs(seg[k]))
+
+
+def test_metric_sqrt_inv_closed_form():
+    """(A + lam I)^{-1/2} of matrices with known eigenpairs: diag(4, 1/4) gives
+    diag(1/2, 2) (an exponent of the wrong sign gives diag(2, 1/2)); a rotated
+    copy gives the rotated result; damping adds lam before the root."""
+    S = og.metric_sqrt_inv(np.diag([4.0, 0.25]), 0.0)
+    assert np.allclose(S, np.diag([0.5, 2.0]), rtol=0, atol=1e-14)
+    c, s = np.cos(0.3), np.sin(0.3)
+    R = np.array([[c, -s, 0.0], [s, c, 0.0], [0.0, 0.0, 1.0]])
+    A = R @ np.diag([4.0, 0.25, 9.0]) @ R.T
+    S = og.metric_sqrt_inv(A, 0.0)
+    assert np.allclose(S, R @ np.diag([0.5, 2.0, 1.0 / 3.0]) @ R.T, rtol=0, atol=1e-13)
+    assert np.allclose(S @ A @ S, np.eye(3), rtol=0, atol=1e-13)
+    S = og.metric_sqrt_inv(np.diag([3.0, 15.0]), 1.0)
+    assert np.allclose(S, np.diag([0.5, 0.25]), rtol=0, atol=1e-14)
+
+
+def test_rel_error_kfac_closed_form():
+    """M2 of an error along one eigenvector of A and a gradient along another:
+    A = diag(4, 1/4), G rows along e1 (metric weight 1/2), error along e2
+    (metric weight 2): M2 = (0.1 * 2) / (1 * 1/2) = 0.4 while M1 = 0.1; the
+    error moved to e1 gives M2 = M1.  G has three rows so a product taken on
+    the wrong side (S E instead of E S) does not even have a valid shape."""
+    S = og.metric_sqrt_inv(np.diag([4.0, 0.25]), 0.0)
+    G = np.array([[1.0, 0.0], [0.0, 0.0], [0.0, 0.0]])
+    Gh = G + np.array([[0.0, 0.1], [0.0, 0.0], [0.0, 0.0]])
+    assert abs(og.rel_frobenius(G, Gh) - 0.1) < 1e-15
+    assert abs(og.rel_error_kfac(G, Gh, S) - 0.4) < 1e-14
+    Gh1 = G + np.array([[0.1, 0.0], [0.0, 0.0], [0.0, 0.0]])
+    assert abs(og.rel_error_kfac(G, Gh1, S) - 0.1) < 1e-14
+    # a gradient along e2 with error along e1: weights swap, M2 = 0.1 * (1/2) / 2
+    G2 = np.array([[0.0, 1.0], [0.0, 0.0], [0.0, 0.0]])
+    Gh2 = G2 + np.array([[0.1, 0.0], [0.0, 0.0], [0.0, 0.0]])
+    assert abs(og.rel_error_kfac(G2, Gh2, S) - 0.025) < 1e-14
+
+
+def test_tiny_amax_gets_the_largest_finite_scale():
+    """An amax below 448 / FLT_MAX (about 1.3e-36): 448 / amax overflows, the
+    scale is FLT_MAX, zeros stay code 0 (no NaN from 0 * inf), the largest
+    element gets E4M3(fl32(amax * FLT_MAX)) and no flag is raised.  Just above
+    the threshold the division is finite and used as is."""
+    fmax = np.finfo(np.float32).max
+    w = np.zeros((2, 128), dtype=np.float32)
+    w[0, 3] = np.float32(1e-38)
+    w[1, 7] = np.float32(-5e-39)
+    scale, inv, flags = og.scale_from_amax(og.amax(w))
+    assert scale == fmax and flags == 0
+    assert inv == np.float32(1e-38) / np.float32(448)
+    codes, inv2, flags2 = og.quantize_tensor(w)
+    assert flags2 == 0 and inv2 == inv
+    assert np.count_nonzero(codes) == 2 and not np.any((codes & 0x7F) == 0x7F)
+    assert codes[0, 3] == e4m3.encode(np.array([np.float32(1e-38) * fmax], np.float32))[0]
+    assert codes[0, 3] == 0x46          # 3.403 is above the 3.375 midpoint: 3.5 (0x46)
+    assert codes[1, 7] == e4m3.encode(np.array([np.float32(-5e-39) * fmax], np.float32))[0]
+    a = np.float32(1e-35)               # above the threshold: the plain quotient
+    s_ok, _, _ = og.scale_from_amax(a)
+    assert s_ok == np.float32(448) / a and np.isfinite(s_ok)
+    # per-segment scaling takes the same rule
+    c128, inv128, _ = og.quantize_block128(w)
+    assert np.array_equal(c128, codes) and inv128[0, 0] == inv
