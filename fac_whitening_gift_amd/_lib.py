@@ -83,7 +83,7 @@ def load():
     LP = ctypes.POINTER(_Layer)
     sig = {
         "gift_refresh_factor": (I, [P, I, I64, ctypes.POINTER(_Factor), F, I, I, I, U64, P, P, P,
-                                    SZ, P]),
+                                    P, SZ, P]),
         "gift_refresh_workspace_bytes": (SZ, [I64, I64, I, I]),
         "gift_whiten_quantize": (I, [LP, I, I, P, P, SZ, P]),
         "gift_dequant_unwhiten": (I, [LP, I, I, P, SZ, P]),
@@ -100,7 +100,7 @@ def load():
         "gift_factor_pack_bytes": (SZ, [I64]),
         "gift_block_factor_pack_bytes": (SZ, [I64, I]),
         "gift_prepare_factor": (I, [ctypes.POINTER(_Factor), P]),
-        "gift_refresh_factors": (I, [ctypes.POINTER(_RefreshInput), I, F, I, I, I, P, SZ, P]),
+        "gift_refresh_factors": (I, [ctypes.POINTER(_RefreshInput), I, F, I, I, I, P, P, SZ, P]),
         "gift_refresh_group_workspace_bytes": (SZ, [ctypes.POINTER(_RefreshInput), I, I]),
     }
     for name, (res, args) in sig.items():
@@ -453,8 +453,10 @@ def gift_refresh_group_workspace_bytes(items, sketch_width=MAX_SKETCH):
 
 
 def gift_refresh_factors(items, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,
-                         sketch_width=MAX_SKETCH, power_steps=4, ws=None, stream=None):
-    """items: list of dicts {X, factor, [sketch], [A_out], [seed]}."""
+                         sketch_width=MAX_SKETCH, power_steps=4, flags=None, ws=None,
+                         stream=None):
+    """items: list of dicts {X, factor, [sketch], [A_out], [seed]}; flags: optional
+    device int32 word that collects GIFT_FLAG_NONFINITE."""
     lib = load()
     for it in items:
         _dev(it.get("sketch"), torch.float32, (it["factor"].d_in, sketch_width), "sketch")
@@ -463,13 +465,13 @@ def gift_refresh_factors(items, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL
     need = lib.gift_refresh_group_workspace_bytes(arr, len(items), sketch_width)
     ws = _workspace(need, items[0]["X"].device, ws)
     _check(lib.gift_refresh_factors(arr, len(items), float(damp_eps), damping_mode, sketch_width,
-                                    power_steps, _ptr(ws), ws.numel() * ws.element_size(),
-                                    _stream(stream)))
+                                    power_steps, _ptr(flags), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,
                         sketch_width=MAX_SKETCH, power_steps=4, seed=0, sketch=None,
-                        A_out=None, ws=None, stream=None):
+                        A_out=None, flags=None, ws=None, stream=None):
     lib = load()
     if X.dtype == torch.bfloat16:
         xdt = DTYPE_BF16
@@ -488,7 +490,8 @@ def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_T
     _check(lib.gift_refresh_factor(_ptr(X), xdt, n_tokens, ctypes.byref(factor._struct),
                                    float(damp_eps), damping_mode, sketch_width, power_steps,
                                    ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(sketch),
-                                   _ptr(A_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                                   _ptr(A_out), _ptr(flags), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
 
 
 def gift_draw_sketch(d_in, width=MAX_SKETCH, seed=0, out=None, device="cuda", stream=None):

@@ -75,14 +75,14 @@ const TileOps kTiles32 = {rt2::row_blocks,           rt2::frag_floats,      rt2:
 size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype, int width);
 gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const gift_factor* f,
                            float damp_eps, int damping_mode, int width, int power_steps,
-                           uint64_t seed, const float* sketch, float* A_out, void* ws,
-                           size_t ws_bytes, hipStream_t s, std::string* err);
+                           uint64_t seed, const float* sketch, float* A_out, uint32_t* flags,
+                           void* ws, size_t ws_bytes, hipStream_t s, std::string* err);
 gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t s,
                         std::string* err);
 size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int width);
 gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps, int damping_mode,
-                            int width, int power_steps, void* ws, size_t ws_bytes, hipStream_t st,
-                            std::string* err);
+                            int width, int power_steps, uint32_t* flags, void* ws, size_t ws_bytes,
+                            hipStream_t st, std::string* err);
 }  // namespace gift
 
 using namespace gift;
@@ -574,11 +574,11 @@ size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype,
 gift_status gift_refresh_factor(const void* X, int x_dtype, int64_t n_tokens,
                                 const gift_factor* f, float damp_eps, int damping_mode,
                                 int sketch_width, int power_steps, uint64_t seed,
-                                const float* sketch, float* A_out, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                const float* sketch, float* A_out, uint32_t* dev_flags, void* ws,
+                                size_t ws_bytes, void* stream) {
   return refresh_factor(X, x_dtype, n_tokens, f, damp_eps, damping_mode, sketch_width,
-                        power_steps, seed, sketch, A_out, ws, ws_bytes, (hipStream_t)stream,
-                        &t_err);
+                        power_steps, seed, sketch, A_out, dev_flags, ws, ws_bytes,
+                        (hipStream_t)stream, &t_err);
 }
 
 size_t gift_factor_pack_bytes(int64_t d_in) { return d_in > 0 ? pack_bytes(d_in) : 0; }
@@ -619,10 +619,10 @@ gift_status gift_prepare_factor(const gift_factor* f, void* stream) {
 }
 
 gift_status gift_refresh_factors(const gift_refresh_input* inputs, int n, float damp_eps,
-                                 int damping_mode, int sketch_width, int power_steps, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  return refresh_factors(inputs, n, damp_eps, damping_mode, sketch_width, power_steps, ws,
-                         ws_bytes, (hipStream_t)stream, &t_err);
+                                 int damping_mode, int sketch_width, int power_steps,
+                                 uint32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
+  return refresh_factors(inputs, n, damp_eps, damping_mode, sketch_width, power_steps, dev_flags,
+                         ws, ws_bytes, (hipStream_t)stream, &t_err);
 }
 
 size_t gift_refresh_group_workspace_bytes(const gift_refresh_input* inputs, int n,

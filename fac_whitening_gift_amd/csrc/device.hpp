@@ -73,7 +73,10 @@ __device__ __forceinline__ uint32_t abs_bits(float x) {
   return __float_as_uint(x) & 0x7fffffffu;
 }
 
-// scale / inv / flags from an amax given as |x| bits (IEEE division).
+// scale / inv / flags from an amax given as |x| bits (IEEE division).  A
+// finite amax below 448 / FLT_MAX makes the quotient overflow; such a tensor
+// gets the largest finite scale, so its zeros stay zeros (0 * inf would be
+// NaN) and no finite value becomes a NaN code.
 struct Scale {
   float scale, inv;
   uint32_t flags;
@@ -89,6 +92,8 @@ __device__ __forceinline__ Scale scale_from_amax_bits(uint32_t bits) {
   } else {
     s.scale = kE4M3Max / a;
     s.inv = a / kE4M3Max;
+    // only a finite amax can give +inf here (NaN and inf amax give NaN and 0)
+    if (s.scale > __FLT_MAX__) s.scale = __FLT_MAX__;
   }
   return s;
 }

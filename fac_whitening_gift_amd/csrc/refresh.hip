@@ -94,12 +94,19 @@ struct WsLayout {
   size_t A, part, om, y, yp, qp, q, q1, gram, T, tr, total;
 };
 
-WsLayout ws_layout(int64_t d, int64_t n, int w, int64_t batch_pairs) {
+// A bf16 input whose tiles take one token range each has A written by the
+// covariance kernel itself and needs no partial tiles.
+bool needs_partials(int x_dtype, const SyrkPlan& p) {
+  return !(x_dtype == GIFT_DTYPE_BF16 && p.nsplit == 1);
+}
+
+WsLayout ws_layout(int64_t d, int64_t n, int w, int64_t batch_pairs, int x_dtype) {
   const SyrkPlan p = syrk_plan(d, n, batch_pairs);
   WsLayout L;
   size_t o = 0;
   L.A = o; o += al((size_t)d * d * 4);
-  L.part = o; o += al((size_t)p.nsplit * p.npairs * kSyrkTile * kSyrkTile * 4);
+  L.part = o;
+  if (needs_partials(x_dtype, p)) o += al((size_t)p.nsplit * p.npairs * kSyrkTile * kSyrkTile * 4);
   L.om = o; o += al((size_t)d * w * 4);
   L.y = o; o += al((size_t)d * w * 4);
   L.yp = o; o += al((size_t)kYSplit * d * w * 4);
@@ -143,6 +150,7 @@ struct RGroup {
   int w;
   float eps;
   int mode;
+  uint32_t* flags;  // GIFT_FLAG_NONFINITE when a trace is not finite; may be NULL
   // bf16 covariance work list: input sy_in[k] owns workgroups
   // sy_begin[k] .. sy_begin[k + 1] - 1 (npairs x nsplit of them)
   int sy_n;
@@ -163,6 +171,7 @@ struct RChain {
   int w;
   float eps;
   int mode;
+  uint32_t* flags;
   const RIn* r;
 };
 // inputs of one chain launch: grid dimensions stay far below their limits
@@ -571,7 +580,9 @@ __global__ __launch_bounds__(kT) void k_syrk_reduce(G g) {
   }
 }
 
-// tr(A), fp64, fixed order.  grid: (inputs)
+// tr(A), fp64, fixed order.  A NaN or infinity in X (or a square that
+// overflows fp32) reaches the diagonal of A, so a non-finite trace flags the
+// input.  grid: (inputs)
 template <class G>
 __global__ __launch_bounds__(kT) void k_trace(G g) {
   const RIn& R = g.r[blockIdx.x];
@@ -585,6 +596,7 @@ __global__ __launch_bounds__(kT) void k_trace(G g) {
     double t = 0.0;
     for (int w = 0; w < kT / 64; ++w) t += sh[w];
     *R.tr = t;
+    if (g.flags && !isfinite(t)) atomicOr(g.flags, GIFT_FLAG_NONFINITE);
   }
 }
 
@@ -1101,6 +1113,11 @@ __global__ __launch_bounds__(kT) void k_apply(G g, int which) {
 // sweep tolerance.  In a round every 2 x 2 block of B is rotated on both
 // sides by one thread, and the pair of columns of V by others, so a round
 // takes two barriers.  All kST threads call it.
+// Sort key of an eigenvalue: NaN (a non-finite input) orders below every
+// number, so ranking by count gives every index a distinct rank and the
+// permutation built from it stays inside the matrix.
+__device__ __forceinline__ double sort_key(double x) { return x != x ? -__builtin_inf() : x; }
+
 // the round-robin schedule: pair i of round r (W/2 disjoint pairs per round,
 // every pair once in W - 1 rounds), smaller index first
 template <int W>
@@ -1286,9 +1303,12 @@ __global__ __launch_bounds__(kST) void k_ritz(G g) {
   __syncthreads();
   if (threadIdx.x < W) {
     const int i = threadIdx.x;
-    const double x = ev[i];
+    const double x = sort_key(ev[i]);
     int rank = 0;
-    for (int j = 0; j < W; ++j) rank += (ev[j] > x) || (ev[j] == x && j < i);
+    for (int j = 0; j < W; ++j) {
+      const double y = sort_key(ev[j]);
+      rank += (y > x) || (y == x && j < i);
+    }
     order[rank] = i;
   }
   __syncthreads();
@@ -1372,9 +1392,12 @@ __global__ __launch_bounds__(kST) void k_blk_eig(G g) {
   const double lam = fmax(lam_floor, 1e-30);
   if (threadIdx.x < W) {
     const int k = threadIdx.x;
-    const double x = ev[k];
+    const double x = sort_key(ev[k]);
     int rank = 0;
-    for (int j = 0; j < W; ++j) rank += (ev[j] > x) || (ev[j] == x && j < k);
+    for (int j = 0; j < W; ++j) {
+      const double y = sort_key(ev[j]);
+      rank += (y > x) || (y == x && j < k);
+    }
     order[rank] = k;
     const double th = fmax(x, 0.0);
     fw[k] = 1.0 / sqrt(th + lam);
@@ -1457,14 +1480,15 @@ size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int wi
   for (int i = 0; i < n; ++i)
     if (!in[i].factor || in[i].factor->d_in < 1 || in[i].n_tokens < 1) return 0;
   for (int i = 0; i < n; ++i)
-    t += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_pairs(in, n, i)).total;
+    t += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_pairs(in, n, i),
+                   in[i].x_dtype).total;
   return t;
 }
 
-size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int, int width) {
+size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype, int width) {
   if (d_in < 1 || n_tokens < 1 || width < 1) return 0;
   const int64_t nb = (d_in + kSyrkTile - 1) / kSyrkTile;
-  return ws_layout(d_in, n_tokens, width, nb * (nb + 1) / 2).total;
+  return ws_layout(d_in, n_tokens, width, nb * (nb + 1) / 2, x_dtype).total;
 }
 
 gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t st,
@@ -1577,8 +1601,8 @@ gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, i
 }
 
 gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps, int damping_mode,
-                            int width, int power_steps, void* ws, size_t ws_bytes, hipStream_t st,
-                            std::string* err) {
+                            int width, int power_steps, uint32_t* flags, void* ws, size_t ws_bytes,
+                            hipStream_t st, std::string* err) {
   auto bad = [&](gift_status s, const std::string& msg) {
     *err = "gift_refresh_factors: " + msg;
     return s;
@@ -1624,6 +1648,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     return bad(GIFT_ERR_WORKSPACE_TOO_SMALL,
                "workspace too small (" + std::to_string(ws_bytes) + " < " + std::to_string(need) + ")");
   if (!ws || ((uintptr_t)ws & 255u)) return bad(GIFT_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+  if ((uintptr_t)flags & 3u) return bad(GIFT_ERR_INVALID_ARG, "dev_flags not 4-byte aligned");
 
   // descriptors of every input, in call order
   std::vector<RIn> desc((size_t)n);
@@ -1633,7 +1658,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       const gift_refresh_input& r = in[i];
       const int d = r.factor->d_in;
       const int64_t bp = batch_pairs(in, n, i);
-      const WsLayout L = ws_layout(d, r.n_tokens, width, bp);
+      const WsLayout L = ws_layout(d, r.n_tokens, width, bp, r.x_dtype);
       const SyrkPlan p = syrk_plan(d, r.n_tokens, bp);
       RIn& x = desc[i];
       x = RIn{};
@@ -1641,8 +1666,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       x.A = r.A_out ? r.A_out : reinterpret_cast<float*>(base + L.A);
       // a bf16 input with one token range has its A written by the covariance
       // kernel itself (no partial tiles)
-      x.part = r.x_dtype == GIFT_DTYPE_BF16 && p.nsplit == 1 ? nullptr
-                                                           : reinterpret_cast<float*>(base + L.part);
+      x.part = needs_partials(r.x_dtype, p) ? reinterpret_cast<float*>(base + L.part) : nullptr;
       x.om_ws = reinterpret_cast<float*>(base + L.om);
       x.om = r.sketch ? r.sketch : x.om_ws;
       x.Y = reinterpret_cast<float*>(base + L.y);
@@ -1674,6 +1698,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     g.w = width;
     g.eps = damp_eps;
     g.mode = damping_mode;
+    g.flags = flags;
     for (int i = 0; i < nb; ++i) g.r[i] = desc[b0 + i];
     return g;
   };
@@ -1713,7 +1738,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     const int nc = n - c0 < kChainMax ? n - c0 : kChainMax;
     gift_status s;
     if (dev_desc) {
-      RChain g{nc, width, damp_eps, damping_mode, dev_desc + c0};
+      RChain g{nc, width, damp_eps, damping_mode, flags, dev_desc + c0};
       s = run_chain(g, desc.data() + c0, in + c0, nc, power_steps, st, err);
     } else {
       s = run_chain(group_of(c0, nc), desc.data() + c0, in + c0, nc, power_steps, st, err);
@@ -1725,8 +1750,8 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
 
 gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const gift_factor* f,
                            float damp_eps, int damping_mode, int width, int power_steps,
-                           uint64_t seed, const float* sketch, float* A_out, void* ws,
-                           size_t ws_bytes, hipStream_t st, std::string* err) {
+                           uint64_t seed, const float* sketch, float* A_out, uint32_t* flags,
+                           void* ws, size_t ws_bytes, hipStream_t st, std::string* err) {
   gift_refresh_input r;
   r.X = X;
   r.x_dtype = x_dtype;
@@ -1739,7 +1764,8 @@ gift_status refresh_factor(const void* X, int x_dtype, int64_t n_tokens, const g
     *err = "gift_refresh_factor: factor is NULL";
     return GIFT_ERR_INVALID_ARG;
   }
-  return refresh_factors(&r, 1, damp_eps, damping_mode, width, power_steps, ws, ws_bytes, st, err);
+  return refresh_factors(&r, 1, damp_eps, damping_mode, width, power_steps, flags, ws, ws_bytes, st,
+                         err);
 }
 
 }  // namespace gift

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GIFT_ABI_VERSION 3
+#define GIFT_ABI_VERSION 4
 
 /* Rank of the factor (GIFT review, free-parameter ledger: rank 32). */
 #define GIFT_RANK 32
@@ -94,7 +94,9 @@ enum { GIFT_DAMP_FLOOR = 0, GIFT_DAMP_FLOOR_PLUS_TAIL = 1 };
 enum { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1, GIFT_SCALE_MXFP4 = 2 };
 
 /* Bits OR-ed into *dev_flags. */
-#define GIFT_FLAG_NONFINITE 1u  /* an amax was NaN or +inf                   */
+#define GIFT_FLAG_NONFINITE 1u  /* an amax was NaN or +inf; or (refresh) the
+                                   trace of A was, i.e. X held a NaN or an
+                                   infinity, or a square overflowed fp32     */
 #define GIFT_FLAG_ZERO_AMAX 2u  /* a tensor / block was all zero: scale = 1 */
 
 /* Layout of gift_factor.coef (fp32, GIFT_COEF_COUNT entries). */
@@ -205,12 +207,17 @@ typedef struct gift_layer {
  * X: device, n_tokens x f->d_in, x_dtype.  f: host struct with device
  * buffers, written.  A_out: optional device d_in x d_in fp32, receives A.
  * sketch_width: rank <= width <= 64, multiple of 16.  power_steps >= 0.
+ * dev_flags: optional device word (4-byte aligned); GIFT_FLAG_NONFINITE is
+ * OR-ed into it when tr(A) is not finite (a NaN or infinity in X reaches
+ * the diagonal of A).  The factor written in that case is not meaningful;
+ * the caller checks the flag before using it.
  */
 gift_status gift_refresh_factor(const void *X, int x_dtype, int64_t n_tokens,
                                 const gift_factor *f, float damp_eps,
                                 int damping_mode, int sketch_width,
                                 int power_steps, uint64_t seed,
                                 const float *sketch, float *A_out,
+                                uint32_t *dev_flags,
                                 void *ws, size_t ws_bytes, void *stream);
 
 size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens,
@@ -225,9 +232,12 @@ size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens,
  * n_tokens x factor->d_in, x_dtype), factor (host struct, device buffers
  * written), sketch / A_out optional as above, seed of its Philox sketch.
  * The scalar arguments apply to every input; all factors of one call are of
- * one kind (rank-r or the same block size).  The workspace holds, for
- * n > 16, the inputs' launch descriptors, then each input's own area in
- * order; query it with gift_refresh_group_workspace_bytes.
+ * one kind (rank-r or the same block size); dev_flags (optional) collects
+ * GIFT_FLAG_NONFINITE over all inputs as in gift_refresh_factor.  The
+ * workspace holds, for n > 16, the inputs' launch descriptors, then each
+ * input's own area in order (A, the covariance partial tiles unless the
+ * input is bf16 with one token range per tile, the subspace-iteration
+ * buffers); query it with gift_refresh_group_workspace_bytes.
  */
 typedef struct gift_refresh_input {
     const void *X;
@@ -242,6 +252,7 @@ typedef struct gift_refresh_input {
 gift_status gift_refresh_factors(const gift_refresh_input *inputs, int n,
                                  float damp_eps, int damping_mode,
                                  int sketch_width, int power_steps,
+                                 uint32_t *dev_flags,
                                  void *ws, size_t ws_bytes, void *stream);
 
 size_t gift_refresh_group_workspace_bytes(const gift_refresh_input *inputs,

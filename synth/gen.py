@@ -157,19 +157,24 @@ def to_bf16_values(x):
     return x.to(torch.bfloat16).to(torch.float32)
 
 
-def draw_input(spec, seed, device="cpu", tokens=None, Q=None, as_bf16=False, host_qr=False):
+def draw_input(spec, seed, device="cpu", tokens=None, Q=None, as_bf16=False, host_qr=False,
+               axis_aligned=False):
     """-> dict(Q, ev, X): eigenbasis, spectrum and N x d activations.
 
     X is fp32 (holding bf16 values when spec.bf16) unless as_bf16, which
-    returns a bf16 tensor for bf16 inputs.
+    returns a bf16 tensor for bf16 inputs.  axis_aligned: the eigenbasis is
+    the identity (Q is None), X = Z diag(ev^1/2) -- no QR, for runs under
+    hardware-counter collection, where only the bytes moved matter.
     """
     n = spec.tokens if tokens is None else tokens
     g = _gen(seed, device)
-    if Q is None:
+    if Q is None and not axis_aligned:
         Q = haar(spec.d_in, g, device, host_qr=host_qr)
     ev = power_law(spec.d_in, spec.exponent, device)
     z = torch.randn(n, spec.d_in, generator=g, device=device, dtype=torch.float32)
-    X = (z * ev.sqrt()) @ Q.T
+    X = z * ev.sqrt()
+    if Q is not None:
+        X = X @ Q.T
     if spec.bf16:
         X = X.to(torch.bfloat16)
         if not as_bf16:
@@ -178,12 +183,16 @@ def draw_input(spec, seed, device="cpu", tokens=None, Q=None, as_bf16=False, hos
 
 
 def draw_gradient(d_out, Q, ev, seed, device="cpu"):
-    """G = diag(s) Z diag(ev^1/2) Q^T, s lognormal(0, 1) per row; fp32."""
+    """G = diag(s) Z diag(ev^1/2) Q^T, s lognormal(0, 1) per row; fp32 (Q None:
+    the axis-aligned basis, no product)."""
     g = _gen(seed, device)
-    d = Q.shape[0]
+    d = ev.shape[0]
     s = torch.exp(torch.randn(d_out, generator=g, device=device, dtype=torch.float32))
     z = torch.randn(d_out, d, generator=g, device=device, dtype=torch.float32)
-    return ((z * ev.sqrt()) @ Q.T) * s.unsqueeze(1)
+    G = z * ev.sqrt()
+    if Q is not None:
+        G = G @ Q.T
+    return G * s.unsqueeze(1)
 
 
 def draw_isotropic_gradient(d_out, d_in, seed, device="cpu"):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fg.EXPORTS)
-    assert lib.gift_abi_version() == 3
+    assert lib.gift_abi_version() == 4
 
 
 def test_status_strings():
@@ -113,8 +113,8 @@ def test_refresh_validation():
     ok = dict(damp=1e-3, mode=fg.DAMP_FLOOR_PLUS_TAIL, w=64, steps=4)
 
     def call(n=1, damp=1e-3, mode=fg.DAMP_FLOOR_PLUS_TAIL, w=64, steps=4, ws=0x100000,
-             nbytes=1 << 40):
-        return lib.gift_refresh_factors(r, n, damp, mode, w, steps, ws, nbytes, None)
+             nbytes=1 << 40, flags=None):
+        return lib.gift_refresh_factors(r, n, damp, mode, w, steps, flags, ws, nbytes, None)
 
     assert call(n=0) == 0                      # empty group: nothing to do
     assert call(mode=7) == 1
@@ -123,6 +123,7 @@ def test_refresh_validation():
     assert call(steps=-1) == 1
     assert call(nbytes=16) == 3
     assert call(ws=0x100010) == 1
+    assert call(flags=0x70002) == 1            # dev_flags not 4-byte aligned
     r[0].x_dtype = 9
     assert call() == 1
     r[0].x_dtype = fg.DTYPE_BF16
@@ -176,3 +177,33 @@ def test_block_factor_validation():
     assert _call_whiten([_layer(d_in=128, factor=fac(128, 32, None))]) == 1    # packs required
     assert _call_whiten([_layer(d_in=128, factor=fac(128, 32))], scaling=2) == 2   # no MXFP4
     assert _call_whiten([_layer(d_in=256, factor=fac(128, 32))]) == 1          # d_in mismatch
+
+
+def test_refresh_workspace_has_no_partials_for_single_range_bf16():
+    """Sixteen bf16 inputs of width 4096 and 16384 tokens form a covariance
+    group of 8448 tiles, so every tile takes all tokens in one range and the
+    covariance kernel writes A itself: the workspace of each input is A and
+    the subspace-iteration buffers only.  The same inputs in fp32 reserve one
+    partial tile per (tile, range) on top."""
+    lib = fg.load()
+    d, n, w = 4096, 16384, 64
+    f = _lib._Factor(d, 32, 0x20000, 0x30000, 0x40000, None)
+    r = (_lib._RefreshInput * 16)()
+    for k in range(16):
+        r[k].X, r[k].x_dtype, r[k].n_tokens = 0x60000, fg.DTYPE_BF16, n
+        r[k].factor = ctypes.pointer(f)
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    per = (al(d * d * 4) + 4 * al(d * w * 4) + al(4 * d * w * 4) + al(d // 32 * 4 * 3 * 64 * 16)
+           + al(16 * 64 * 64 * 8) + al(64 * 64 * 8) + al(64))
+    bf16 = lib.gift_refresh_group_workspace_bytes(r, 16, w)
+    assert bf16 == 16 * per
+    for k in range(16):
+        r[k].x_dtype = fg.DTYPE_F32
+    npairs = (d // 128) * (d // 128 + 1) // 2
+    f32 = lib.gift_refresh_group_workspace_bytes(r, 16, w)
+    assert f32 - bf16 >= 16 * npairs * 128 * 128 * 4
+    # one such input alone splits its tokens over two ranges: partials needed
+    alone = lib.gift_refresh_workspace_bytes(d, n, fg.DTYPE_BF16, w)
+    assert alone > per

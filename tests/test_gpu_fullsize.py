@@ -14,11 +14,11 @@
   scaling, on sampled rows: the scales are row-local, so codes and scales of
   the sampled rows are bit-exact against the oracle's encoding of the
   device's W.
-* The refresh at full size, where the oracle's eigensolve is too slow: the
-  properties that hold at any size -- U orthonormal, theta equal to the
-  Rayleigh quotients u^T A u, and within 1e-4 of the top eigenvalues of the
-  exact A (fp64 on the device, measurement harness) on the separated part
-  of the spectrum.
+* The refresh at full size (d_in 1536, 4096 and 11008), where the oracle's
+  eigensolve is too slow: the properties that hold at any size -- U
+  orthonormal, theta equal to the Rayleigh quotients u^T A u, and within
+  1e-4 of the top eigenvalues of the exact A (fp64 on the device,
+  measurement harness) on the separated part of the spectrum.
 """
 
 import numpy as np
@@ -98,6 +98,8 @@ def test_block4096_shapes_sampled_rows():
     specs = [next(s for s in w.inputs if s.d_in == 4096), next(s for s in w.inputs if s.d_in == 11008)]
     inputs, facs = _refresh_inputs(specs, seed=710)
     _check_refresh_properties(inputs[0], facs[0])
+    say("  refresh properties at d_in 11008")
+    _check_refresh_properties(inputs[1], facs[1])
     shapes = [(11008, 0), (4096, 1)]   # gate (11008 x 4096), down (4096 x 11008)
     rng = np.random.default_rng(7)
     for i, (d_out, k) in enumerate(shapes):
