@@ -1,31 +1,34 @@
 """Benchmark of the GIFT FP8 gradient round trip on one MI355X.
 
-Default workload (the metric's configuration): one Llama-style block at
-hidden 1024 -- q, k, v, o (1024 x 1024), gate and up (2816 x 1024), down
-(1024 x 2816) fp32 weight gradients, 8192 bf16 activation tokens per
-distinct input (attention in, o in, MLP in, down in) with a power-law
-spectrum of exponent 1.5; rank-32 factors; all 7 matrices whitened;
-per-tensor E4M3.
+Default workload: a synthetic stack of 32 Llama-style blocks at hidden 4096,
+MLP 11008 -- per block q, k, v, o (4096 x 4096), gate and up (11008 x 4096),
+down (4096 x 11008) fp32 weight gradients, 224 layers and 6.48 G elements
+(25.9 GB) resident in HBM -- with 16384 bf16 activation tokens per distinct
+input (4 per block, 128 in all: attention in, o in, MLP in at width 4096,
+down in at width 11008), power-law spectrum of exponent 1.5, rank-32 factors,
+every layer whitened, per-tensor E4M3.
 
-One step = the per-step path of GIFT over the workload: the grouped
-whiten + quantize of the whitened gradients, the grouped dequantize +
-un-whiten, the Euclidean round trip of the layers not selected (none in the
-default workload) -- prepared once and captured in a HIP graph, one replay
-per step -- and the grouped factor refresh of every input, run eagerly
-inside the timed loop every 50 steps (the paper's refresh interval), so it
-is amortized exactly as in training.  Each step takes the next gradient set
-from a ring of resident sets whose footprint is several times the 256 MB
-Infinity Cache, so the gradients come from HBM.  Inputs are resident before
-the timed region.  One JSON line on stdout.
+One step = the per-step path of GIFT over the whole stack: the grouped
+whiten + quantize of every gradient and the grouped dequantize + un-whiten
+(prepared once and captured in one HIP graph, one replay per step), plus the
+step's share of the factor refresh (the paper refreshes every factor every 50
+steps): step s refreshes the inputs i with floor(50 i / n_inputs) ==
+s mod 50, so any 50 consecutive steps refresh every input exactly once and
+each timed step carries 1/50 of the refresh work whatever --steps is.  The
+gradients (25.9 GB) are a hundred times the 256 MB Infinity Cache, so every
+step reads them from HBM.  Inputs are resident before the timed region.  One
+JSON line on stdout.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10]
-    python bench.py --workload stack300m     # 24 blocks + embed/head, top-8 by rho
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
     python bench.py --workload stack600m     # 24 blocks at 1536/4096, 16384 tokens
+    python bench.py --workload stack300m     # 24 blocks at 1024/2816 + embed/head, top-8 by rho
+    python bench.py --workload block1024     # one block at hidden 1024
     python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
     python bench.py --study interval [--intervals 10,25,50,100]   # refresh-interval ablation
     python bench.py --study rank [--rank-list 8,16,32,b32,b64]     # rank / block-A sweep
     python bench.py --study reference     # full-rank, Cholesky-form and two-sided references
     python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
+    python bench.py --study matrixfree    # refresh power steps with A Q = X^T (X Q) / N
 """
 
 import argparse
@@ -46,19 +49,22 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="block1024",
-                   choices=["block1024", "stack300m", "stack600m"])
-    p.add_argument("--ring", type=int, default=4, help="resident gradient sets")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="stack4096",
+                   choices=["stack4096", "stack600m", "stack300m", "block1024"])
+    p.add_argument("--ring", type=int, default=None,
+                   help="resident gradient sets (default: 4 for block1024, else 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-quality", action="store_true")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--counters", action="store_true",
-                   help="for runs under hardware-counter collection: no device QR or "
-                        "eigendecomposition (host QR for the input bases, no M2 report)")
+                   help="for runs under hardware-counter collection: axis-aligned spectra "
+                        "(no device QR or eigendecomposition), no quality report")
     p.add_argument("--study", default=None,
-                   choices=["staleness", "interval", "rank", "reference", "copy", "reduce"])
+                   choices=["staleness", "interval", "rank", "reference", "copy", "reduce",
+                            "matrixfree"])
     p.add_argument("--ref-shape", default="1024,2816,8192",
                    help="hidden,mlp,tokens of the block of the reference study")
     p.add_argument("--rank-list", default="8,16,32,b32,b64",
@@ -93,20 +99,23 @@ def kernel_source_hash():
 
 
 def load_traffic(kernel, src_hash, elems):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (its "traffic:" lines), if it was taken on the current kernel sources and
-    the same number of elements; else None."""
-    path = os.path.join(HERE, "profiles", "hbm_traffic_roundtrip_llama_block_h1024.md")
-    if not os.path.exists(path):
+    """HBM bytes per launch from the committed rocprofv3 counter summaries
+    (their "traffic:" lines), if taken on the current kernel sources and the
+    same number of elements; else None."""
+    pdir = os.path.join(HERE, "profiles")
+    if not os.path.isdir(pdir):
         return None
-    with open(path) as fh:
-        for line in fh:
-            if not line.startswith("traffic:"):
-                continue
-            kv = dict(f.split("=", 1) for f in line.split()[1:])
-            if (kv.get("kernel") == kernel and kv.get("source_hash") == src_hash
-                    and int(kv.get("elements", -1)) == elems):
-                return int(kv["hbm_bytes_per_launch"])
+    for name in sorted(os.listdir(pdir)):
+        if not name.startswith("hbm_traffic"):
+            continue
+        with open(os.path.join(pdir, name)) as fh:
+            for line in fh:
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(f.split("=", 1) for f in line.split()[1:])
+                if (kv.get("kernel") == kernel and kv.get("source_hash") == src_hash
+                        and int(kv.get("elements", -1)) == elems):
+                    return int(kv["hbm_bytes_per_launch"])
     return None
 
 
@@ -115,30 +124,79 @@ def load_traffic(kernel, src_hash, elems):
 # ---------------------------------------------------------------------------
 
 def build_workload(args):
+    """-> (workload, top-k selection or None for all, ring sets)."""
     import synth
+    ring = args.ring
     if args.workload == "block1024":
         w = synth.llama_block(hidden=1024, mlp=2816, tokens=8192, exponent=1.5)
-        return w, None, args.ring
+        return w, None, ring or 4
     if args.workload == "stack300m":
         w = synth.llama_stack(24, 1024, 2816, 8192, exponent_range=(1.0, 2.0), vocab=32000)
-        return w, 8, 1
-    w = synth.llama_stack(24, 1536, 4096, 16384, exponent=1.5)
-    return w, None, 1
+        return w, 8, ring or 1
+    if args.workload == "stack600m":
+        return synth.llama_stack(24, 1536, 4096, 16384, exponent=1.5), None, ring or 1
+    return synth.llama_stack(32, 4096, 11008, 16384, exponent=1.5), None, ring or 1
 
 
 def describe(args, w, select_k, ring):
+    refresh = ("the refresh staggered over the %d-step interval (step s refreshes the inputs i with "
+               "floor(%d i / %d) == s mod %d)" % (REFRESH_EVERY, REFRESH_EVERY, len(w.inputs),
+                                                  REFRESH_EVERY))
     if args.workload == "block1024":
         return ("%s: q,k,v,o 1024x1024, gate/up 2816x1024, down 1024x2816 fp32 gradients; 8192 "
-                "bf16 tokens per input, spectrum i^-1.5; rank 32; per-tensor E4M3; refresh every "
-                "%d steps; ring of %d gradient sets" % (w.name, REFRESH_EVERY, ring))
+                "bf16 tokens per input, spectrum i^-1.5; rank 32; per-tensor E4M3; %s; ring of %d "
+                "gradient sets" % (w.name, refresh, ring))
     if args.workload == "stack300m":
         return ("%s: 24 Llama blocks (hidden 1024, MLP 2816) + 32000x1024 embedding and head "
                 "(Euclidean); 8192 bf16 tokens per input, per-input spectrum exponent ~U[1,2]; "
                 "GIFT on the top-%d layers by theta_1/tr(A), the rest Euclidean; per-tensor E4M3; "
-                "refresh of all 96 inputs every %d steps" % (w.name, select_k, REFRESH_EVERY))
-    return ("%s: 24 Llama blocks (hidden 1536, MLP 4096); 16384 bf16 tokens per input, spectrum "
-            "i^-1.5; all 168 layers whitened; per-tensor E4M3; refresh of all 96 inputs every "
-            "%d steps" % (w.name, REFRESH_EVERY))
+                "%s" % (w.name, select_k, refresh))
+    if args.workload == "stack600m":
+        return ("%s: 24 Llama blocks (hidden 1536, MLP 4096); 16384 bf16 tokens per input, "
+                "spectrum i^-1.5; all 168 layers whitened; per-tensor E4M3; %s"
+                % (w.name, refresh))
+    return ("%s: 32 Llama blocks (hidden 4096, MLP 11008), 224 fp32 gradients (25.9 GB resident); "
+            "16384 bf16 tokens per input (128 inputs), spectrum i^-1.5; rank 32; all layers "
+            "whitened; per-tensor E4M3; %s" % (w.name, refresh))
+
+
+def draw_all(args, w, dev, ring_n):
+    """Activations of every input (bf16) and ring_n gradient sets, drawn input
+    by input so only one eigenbasis is held at a time."""
+    import synth
+    inputs, grads = {}, [dict() for _ in range(ring_n)]
+    by_input = {}
+    for i, l in enumerate(w.layers):
+        by_input.setdefault(l.input, []).append(i)
+    for k, spec in enumerate(w.inputs):
+        inp = synth.draw_input(spec, seed=1000 + k, device=dev, as_bf16=True,
+                               axis_aligned=args.counters)
+        for r in range(ring_n):
+            for i in by_input.get(spec.name, []):
+                grads[r][i] = synth.draw_gradient(w.layers[i].d_out, inp["Q"], inp["ev"],
+                                                  seed=5000 + 1000 * r + i, device=dev)
+        inputs[spec.name] = {"X": inp["X"], "ev": inp["ev"]}
+        del inp
+    for r in range(ring_n):
+        for i in by_input.get(None, []):
+            l = w.layers[i]
+            grads[r][i] = synth.draw_isotropic_gradient(l.d_out, l.d_in, seed=5000 + 1000 * r + i,
+                                                        device=dev)
+    return inputs, [[g[i] for i in range(len(w.layers))] for g in grads]
+
+
+def refresh_shares(n):
+    """Inputs refreshed at each step of a REFRESH_EVERY-step window."""
+    shares = [[] for _ in range(REFRESH_EVERY)]
+    for i in range(n):
+        shares[i * REFRESH_EVERY // n].append(i)
+    return shares
+
+
+def refresh_macs(specs):
+    """Algorithmic multiply-adds of the covariances: N d (d + 1) / 2 per input
+    (one triangle of the symmetric X^T X)."""
+    return sum(s.tokens * s.d_in * (s.d_in + 1) / 2 for s in specs)
 
 
 def main():
@@ -147,29 +205,18 @@ def main():
         print("bench.py measures one GPU: the GIFT path here has no inter-GPU part "
               "(the collective is out of scope); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    if args.study == "staleness":
-        print(json.dumps(staleness_study(args)), flush=True)
-        return
-    if args.study == "interval":
-        print(json.dumps(interval_study(args)), flush=True)
-        return
-    if args.study == "rank":
-        print(json.dumps(rank_study(args)), flush=True)
-        return
-    if args.study == "reference":
-        print(json.dumps(reference_study(args)), flush=True)
-        return
+    studies = {"staleness": staleness_study, "interval": interval_study, "rank": rank_study,
+               "reference": reference_study, "reduce": reduce_study,
+               "matrixfree": matrixfree_study}
     if args.study == "copy":
         print(json.dumps(copy_calibration()), flush=True)
         return
-    if args.study == "reduce":
-        print(json.dumps(reduce_study(args)), flush=True)
+    if args.study is not None:
+        print(json.dumps(studies[args.study](args)), flush=True)
         return
 
-    import numpy as np
     import torch
 
-    import synth
     import fac_whitening_gift_amd as fg
     from fac_whitening_gift_amd.select import select_layers
 
@@ -179,49 +226,37 @@ def main():
     w, select_k, ring_n = build_workload(args)
     elems = w.gradient_elements
     grad_bytes = 4 * elems
-    log(args, "workload %s: %d layers, %.1f M gradient elements" %
-        (w.name, len(w.layers), elems / 1e6))
+    log(args, "workload %s: %d layers, %d inputs, %.1f M gradient elements (%.2f GB fp32)" %
+        (w.name, len(w.layers), len(w.inputs), elems / 1e6, grad_bytes / 1e9))
 
     # ---- resident inputs ---------------------------------------------------
-    inputs, factors = {}, {}
-    for k, spec in enumerate(w.inputs):
-        inputs[spec.name] = synth.draw_input(spec, seed=1000 + k, device=dev, as_bf16=True,
-                                             host_qr=args.counters)
-        factors[spec.name] = fg.Factor(spec.d_in, device=dev)
-    items = [dict(X=inputs[s.name]["X"], factor=factors[s.name], seed=0) for s in w.inputs]
-    ws_ref = torch.empty(max(fg.gift_refresh_group_workspace_bytes(items), 256),
-                         dtype=torch.uint8, device=dev)
-
-    def refresh_all(seed):
-        for k, it in enumerate(items):
-            it["seed"] = seed + k
-        fg.gift_refresh_factors(items, ws=ws_ref)
-
-    refresh_all(1)
+    t0 = time.perf_counter()
+    inputs, ring_grads = draw_all(args, w, dev, ring_n)
     torch.cuda.synchronize()
-    layer_factor = [factors[l.input] if l.input is not None else None for l in w.layers]
-    if select_k is None:
-        selected = [i for i, f in enumerate(layer_factor) if f is not None]
-    else:
-        selected = select_layers(layer_factor, select_k)
-    sel = set(selected)
-    log(args, "whitened layers: %s" % [w.layers[i].name for i in selected])
+    log(args, "inputs drawn in %.1f s" % (time.perf_counter() - t0))
+    factors = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
+    items = [dict(X=inputs[s.name]["X"], factor=factors[s.name], seed=k)
+             for k, s in enumerate(w.inputs)]
+    ws_all = torch.empty(max(fg.gift_refresh_group_workspace_bytes(items), 256),
+                         dtype=torch.uint8, device=dev)
+    rflags = torch.zeros(1, dtype=torch.int32, device=dev)
+    fg.gift_refresh_factors(items, flags=rflags, ws=ws_all)
+    torch.cuda.synchronize()
+    if int(rflags.item()):
+        raise RuntimeError("refresh flagged non-finite activations")
+    shares = [[items[i] for i in sh] for sh in refresh_shares(len(items))]
+    ws_share = torch.empty(max(max(fg.gift_refresh_group_workspace_bytes(sh) for sh in shares if sh),
+                               256), dtype=torch.uint8, device=dev)
 
+    layer_factor = [factors[l.input] if l.input is not None else None for l in w.layers]
+    selected = ([i for i, f in enumerate(layer_factor) if f is not None] if select_k is None
+                else select_layers(layer_factor, select_k))
+    sel = set(selected)
+    log(args, "whitened layers: %d of %d" % (len(selected), len(w.layers)))
     ring = []
-    for r in range(ring_n):
-        gl, el = [], []
-        for i, l in enumerate(w.layers):
-            if l.input is not None:
-                inp = inputs[l.input]
-                G = synth.draw_gradient(l.d_out, inp["Q"], inp["ev"], seed=5000 + 1000 * r + i,
-                                        device=dev)
-            else:
-                G = synth.draw_isotropic_gradient(l.d_out, l.d_in, seed=5000 + 1000 * r + i,
-                                                  device=dev)
-            if i in sel:
-                gl.append(fg.Layer(G, factor=layer_factor[i]))
-            else:
-                el.append(fg.Layer(G))
+    for grads in ring_grads:
+        gl = [fg.Layer(G, factor=layer_factor[i]) for i, G in enumerate(grads) if i in sel]
+        el = [fg.Layer(G) for i, G in enumerate(grads) if i not in sel]
         ring.append((gl, el))
     gl0, el0 = ring[0]
 
@@ -246,10 +281,10 @@ def main():
                 c()
         return graph, calls         # the calls own the workspaces the graph writes
 
-    # Per ring slot the per-step path -- grouped whiten + quantize, grouped
-    # dequantize + un-whiten, Euclidean round trip of the other layers -- as
-    # prepared calls captured in one HIP graph (one launch per step), and each
-    # entry point also in a graph of its own for the per-call timings below.
+    # Per ring slot the per-step round trip -- grouped whiten + quantize,
+    # grouped dequantize + un-whiten, Euclidean round trip of the other layers
+    # -- as prepared calls captured in one HIP graph, and each entry point in a
+    # graph of its own for the per-call timings below.
     def entry_calls(gl, el):
         calls = []
         if gl:
@@ -270,21 +305,24 @@ def main():
     torch.cuda.synchronize()
 
     def step(s):
-        if s % REFRESH_EVERY == 0:
-            refresh_all(7 * s + 1)
+        share = shares[s % REFRESH_EVERY]
+        if share:
+            fg.gift_refresh_factors(share, ws=ws_share)
         slot_graphs[s % len(ring)][0].replay()
 
     for s in range(args.warmup):
-        step(s + 1)
+        step(s)
     torch.cuda.synchronize()
     log(args, "timing %d steps" % args.steps)
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(args.warmup, args.warmup + args.steps):
         step(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     value = grad_bytes * args.steps / elapsed / 1e9
     ms_per_step = elapsed / args.steps * 1e3
+    refreshed = sum(len(shares[s % REFRESH_EVERY])
+                    for s in range(args.warmup, args.warmup + args.steps))
 
     # ---- the pieces on their own (graph replays between events) --------------
     def timed(fn, n=10):
@@ -298,15 +336,13 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e-3
 
-    def timed_graph(calls, n=20):
+    def timed_graph(calls, n=10):
         if not calls:
             return 0.0
         held = [capture(c) for c in calls]
         torch.cuda.synchronize()
         return timed(lambda: [g.replay() for g, _ in held], n) / len(held)
 
-    refresh_s = timed(lambda: refresh_all(11), 3)
-    syrk_flops = sum(2.0 * s.tokens * s.d_in * s.d_in for s in w.inputs)
     # Each entry point on its own: its graph for every ring slot replayed in
     # turn, back to back between two events on the launch stream (torch's
     # current stream, where the graphs replay), right after the timed steps.
@@ -319,22 +355,30 @@ def main():
     t_whiten = entry_time("whiten_quantize")
     t_dq = entry_time("dequant_unwhiten")
     t_eu = entry_time("euclid_rest")
+    refresh_s = timed(lambda: fg.gift_refresh_factors(items, ws=ws_all), 3)
+    share_s = sorted(timed(lambda: fg.gift_refresh_factors(sh, ws=ws_share), 3)
+                     for sh in shares[:5] if sh)
     gift_elems = sum(L.d_out * L.d_in for L in gl0)
-    all_eu = [fg.Layer(L.G) for L in gl0 + el0]
+    # the other payloads, reusing the codes and reconstruction buffers
+    all_eu = [fg.Layer(L.G, q=L.q, G_hat=L.G_hat) for L in gl0 + el0]
     t_eu_all = timed_graph([[fg.GroupCall(fg.OP_EUCLID_ROUNDTRIP, all_eu)]])
-    blk = [fg.Layer(L.G, factor=L.factor, block128=True) for L in gl0]
+    blk = [fg.Layer(L.G, factor=L.factor, q=L.q, G_hat=L.G_hat, block128=True) for L in gl0]
     t_b = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, blk, fg.SCALE_BLOCK128),
                         fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, blk, fg.SCALE_BLOCK128)]]) \
         if blk else 0.0
-    mxl = [fg.Layer(L.G, factor=L.factor, mxfp4=True) for L in gl0]
+    mxl = [fg.Layer(L.G, factor=L.factor, q=L.q.view(-1)[:L.q.numel() // 2].view(L.d_out, -1),
+                    G_hat=L.G_hat, mxfp4=True) for L in gl0]
     t_mx = timed_graph([[fg.GroupCall(fg.OP_WHITEN_QUANTIZE, mxl, fg.SCALE_MXFP4),
                          fg.GroupCall(fg.OP_DEQUANT_UNWHITEN, mxl, fg.SCALE_MXFP4)]]) \
         if mxl else 0.0
     del all_eu, blk, mxl
+    torch.cuda.synchronize()
 
     # ---- quality: relative error vs Euclidean FP8 on the whitened layers -----
-    quality = quality_report(gl0, w, selected, inputs, ws_w, ws_d) \
-        if gl0 and not args.counters else None
+    quality = None
+    if gl0 and not args.counters and not args.no_quality:
+        log(args, "quality")
+        quality = quality_report(w, selected, gl0, inputs, items, ws_all, ws_w, ws_d, dev)
 
     # ---- roofline of the dominant launch -------------------------------------
     src = kernel_source_hash()
@@ -347,10 +391,22 @@ def main():
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(kname, src, gift_elems), "kernel": kname,
-            "launch_ms": round(t_k * 1e3, 4), "source_hash": src}
+            "launch_ms": round(t_k * 1e3, 4), "alg_bytes_per_launch": int(alg_bytes),
+            "source_hash": src}
+    macs = refresh_macs(w.inputs)
+    refresh = {"bound": "mfma", "ms": round(refresh_s * 1e3, 3), "inputs": len(w.inputs),
+               "alg_tflop": round(2 * macs / 1e12, 3),
+               "achieved_tflops": round(2 * macs / refresh_s / 1e12, 1),
+               "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+               "frac": round(2 * macs / refresh_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               "work": "covariance triangles N d (d + 1) / 2 multiply-adds per input over the "
+                       "whole grouped refresh (covariance, subspace iteration, Rayleigh-Ritz)",
+               "share_ms_min_max": [round(share_s[0] * 1e3, 3), round(share_s[-1] * 1e3, 3)]
+               if share_s else None,
+               "per_step_ms": round(refresh_s * 1e3 / REFRESH_EVERY, 3)}
 
     cpu = None
-    if not args.no_cpu_baseline and args.workload == "block1024":
+    if not args.no_cpu_baseline:
         cpu = cpu_baseline(gl0, args)
 
     rt = t_whiten + t_dq
@@ -360,15 +416,18 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": describe(args, w, select_k, ring_n), "layers": len(w.layers),
-                   "whitened_layers": len(gl0), "gradient_elements": elems},
+                   "whitened_layers": len(gl0), "inputs": len(w.inputs),
+                   "gradient_elements": elems,
+                   "refresh_charge": "%d input refreshes in the %d timed steps (%.3f of all "
+                                     "inputs per step)" % (refreshed, args.steps,
+                                                          refreshed / args.steps / len(w.inputs))},
         "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
         "roundtrip_only_gbps": round(4 * gift_elems / rt / 1e9, 2) if rt > 0 else None,
+        "roundtrip_hbm_frac": round(10 * gift_elems / rt / 1e9 / HBM_PEAK_GBS, 4) if rt > 0 else None,
         "whiten_quantize_ms": round(t_whiten * 1e3, 4), "dequant_unwhiten_ms": round(t_dq * 1e3, 4),
         "euclid_rest_ms": round(t_eu * 1e3, 4),
         "layers_per_s": round(len(w.layers) * args.steps / elapsed, 1),
-        "refresh_ms": round(refresh_s * 1e3, 3), "refresh_inputs": len(w.inputs),
-        "refresh_syrk_mfma_frac_lower_bound": round(syrk_flops / refresh_s / 1e12 /
-                                                     MFMA_BF16_PEAK_TFLOPS, 4),
+        "refresh": refresh,
         "euclid_all_layers_gbps": round(grad_bytes / t_eu_all / 1e9, 2),
         "block128_roundtrip_gbps": round(4 * gift_elems / t_b / 1e9, 2) if t_b > 0 else None,
         "mxfp4_roundtrip_gbps": round(4 * gift_elems / t_mx / 1e9, 2) if t_mx > 0 else None,
@@ -379,90 +438,137 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def quality_report(gl, w, selected, inputs, ws_w, ws_d):
-    """M1 (plain relative Frobenius) from the device error sums and M2 (error
-    in the K-FAC metric of the exact sample covariance, fp64 torch on the
-    device as measurement harness) for GIFT and for Euclidean quantization of
-    the same gradients: per-tensor E4M3 and MXFP4."""
+# ---------------------------------------------------------------------------
+# quality
+# ---------------------------------------------------------------------------
+
+def kfac_metric(X, eps=1e-3):
+    """S = (A + lambda_floor I)^-1/2 of A = X^T X / N from the exact fp64
+    eigendecomposition (measurement harness, on the device)."""
+    import torch
+    X = X.double()
+    A = X.T @ X / X.shape[0]
+    lam = eps * torch.trace(A) / A.shape[0]
+    ev_, V = torch.linalg.eigh(A)
+    return (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
+
+
+def m2_parts(G, G_hat, S):
+    """(||(G^ - G) S||_F^2, ||G S||_F^2) in fp64: the terms of the K-FAC metric
+    error M2 of one layer."""
+    G = G.double()
+    return (float(((G_hat.double() - G) @ S).pow(2).sum()), float((G @ S).pow(2).sum()))
+
+
+def quality_report(w, selected, gl, inputs, items, ws_all, ws_w, ws_d, dev):
+    """Relative reconstruction error of GIFT and of Euclidean quantization of
+    the same gradients, for both damping readings (floor+tail, the default
+    factors; floor, factors refreshed again with GIFT_DAMP_FLOOR) and for the
+    per-tensor E4M3 and MXFP4 payloads.  M1 (plain relative Frobenius) over
+    every whitened layer from the device error sums; M2 (error in the K-FAC
+    metric of the exact damped sample covariance, fp64 torch on the device as
+    measurement harness) over the layers of the first block (the first 7
+    whitened layers), whose inputs' exact eigendecompositions it needs."""
     import numpy as np
     import torch
 
     import fac_whitening_gift_amd as fg
-    fg.gift_whiten_quantize(gl, ws=ws_w)
-    fg.gift_dequant_unwhiten(gl, ws=ws_d)
-    eu = [fg.Layer(L.G) for L in gl]
-    fg.gift_euclid_fp8_roundtrip(eu)
-    gm = [fg.Layer(L.G, factor=L.factor, mxfp4=True) for L in gl]
-    fg.gift_whiten_quantize(gm, scaling=fg.SCALE_MXFP4)
-    fg.gift_dequant_unwhiten(gm, scaling=fg.SCALE_MXFP4)
-    em = [fg.Layer(L.G, mxfp4=True) for L in gl]
-    fg.gift_euclid_fp8_roundtrip(em, scaling=fg.SCALE_MXFP4)
-    sets = {"gift": gl, "euclid": eu, "gift_mxfp4": gm, "euclid_mxfp4": em}
-    m1 = {}
-    for k, layers in sets.items():
+
+    m2_layers = list(range(min(7, len(gl))))
+    S = {}
+    for j in m2_layers:
+        name = w.layers[selected[j]].input
+        if name not in S:
+            S[name] = kfac_metric(inputs[name]["X"])
+    den2 = sum(m2_parts(gl[j].G, gl[j].G, S[w.layers[selected[j]].input])[1] for j in m2_layers)
+
+    def measure(layers, run, scaling=fg.SCALE_TENSOR):
+        run(layers, scaling)
         err = fg.gift_roundtrip_error(layers).cpu().numpy()
-        m1[k] = float(np.sqrt(err[:, 0].sum() / err[:, 1].sum()))
-    num = {k: 0.0 for k in sets}
-    den = 0.0
-    S_cache = {}
-    for j, i in enumerate(selected):
-        name = w.layers[i].input
-        if name not in S_cache:
-            X = inputs[name]["X"].double()
-            A = X.T @ X / X.shape[0]
-            lam = 1e-3 * torch.trace(A) / A.shape[0]
-            ev_, V = torch.linalg.eigh(A)
-            S_cache[name] = (V * (ev_.clamp_min(0) + lam).rsqrt()) @ V.T
-        S = S_cache[name]
-        G = gl[j].G.double()
-        for k, layers in sets.items():
-            num[k] += float(torch.linalg.norm((layers[j].G_hat.double() - G) @ S) ** 2)
-        den += float(torch.linalg.norm(G @ S) ** 2)
-    m2 = {k: float(np.sqrt(v / den)) for k, v in num.items()}
-    return {"m1_gift": round(m1["gift"], 5), "m1_euclid": round(m1["euclid"], 5),
-            "m1_ratio": round(m1["gift"] / m1["euclid"], 4), "m2_gift": round(m2["gift"], 5),
-            "m2_euclid": round(m2["euclid"], 5), "m2_ratio": round(m2["gift"] / m2["euclid"], 4),
-            "m2_reduction": round(1 - m2["gift"] / m2["euclid"], 4),
-            "mxfp4": {"m1_gift": round(m1["gift_mxfp4"], 5),
-                      "m1_euclid": round(m1["euclid_mxfp4"], 5),
-                      "m2_gift": round(m2["gift_mxfp4"], 5),
-                      "m2_euclid": round(m2["euclid_mxfp4"], 5),
-                      "m2_reduction": round(1 - m2["gift_mxfp4"] / m2["euclid_mxfp4"], 4)},
-            "damping": "floor+tail"}
+        m1 = float(np.sqrt(err[:, 0].sum() / err[:, 1].sum()))
+        num = sum(m2_parts(layers[j].G, layers[j].G_hat, S[w.layers[selected[j]].input])[0]
+                  for j in m2_layers)
+        return m1, float(np.sqrt(num / den2))
+
+    def gift(layers, sc):
+        fg.gift_whiten_quantize(layers, scaling=sc, ws=ws_w if sc == fg.SCALE_TENSOR else None)
+        fg.gift_dequant_unwhiten(layers, scaling=sc, ws=ws_d if sc == fg.SCALE_TENSOR else None)
+
+    def euclid(layers, sc):
+        fg.gift_euclid_fp8_roundtrip(layers, scaling=sc)
+
+    res = {}
+    eu = [fg.Layer(L.G, q=L.q, G_hat=L.G_hat) for L in gl]
+    res["euclid"] = measure(eu, euclid)
+    res["gift_floor+tail"] = measure(gl, gift)
+    mx_q = lambda L: L.q.view(-1)[:L.q.numel() // 2].view(L.d_out, -1)  # noqa: E731
+    gm = [fg.Layer(L.G, factor=L.factor, q=mx_q(L), G_hat=L.G_hat, mxfp4=True) for L in gl]
+    res["gift_mxfp4"] = measure(gm, gift, fg.SCALE_MXFP4)
+    em = [fg.Layer(L.G, q=mx_q(L), G_hat=L.G_hat, mxfp4=True) for L in gl]
+    res["euclid_mxfp4"] = measure(em, euclid, fg.SCALE_MXFP4)
+    del gm, em
+    # the literal damping reading: every input refreshed again with the floor only
+    floor = {}
+    for it in items:
+        f = it["factor"]
+        floor[f.U.data_ptr()] = fg.Factor(f.d_in, device=dev)
+    fitems = [dict(X=it["X"], factor=floor[it["factor"].U.data_ptr()], seed=it["seed"])
+              for it in items]
+    fg.gift_refresh_factors(fitems, damping_mode=fg.DAMP_FLOOR, ws=ws_all)
+    gf = [fg.Layer(L.G, factor=floor[L.factor.U.data_ptr()], q=L.q, G_hat=L.G_hat) for L in gl]
+    res["gift_floor"] = measure(gf, gift)
+    del gf, floor, fitems
+    torch.cuda.synchronize()
+
+    def row(g, e):
+        return {"m1_gift": round(res[g][0], 5), "m1_euclid": round(res[e][0], 5),
+                "m1_ratio": round(res[g][0] / res[e][0], 4),
+                "m2_gift": round(res[g][1], 5), "m2_euclid": round(res[e][1], 5),
+                "m2_ratio": round(res[g][1] / res[e][1], 4),
+                "m2_reduction": round(1 - res[g][1] / res[e][1], 4)}
+
+    return {"e4m3_floor+tail": row("gift_floor+tail", "euclid"),
+            "e4m3_floor": row("gift_floor", "euclid"),
+            "mxfp4_floor+tail": row("gift_mxfp4", "euclid_mxfp4"),
+            "m1_layers": len(gl), "m2_layers": [w.layers[selected[j]].name for j in m2_layers],
+            "m2_metric": "(A + 1e-3 tr(A)/d_in I)^-1/2 of the sample A, exact fp64 eigh"}
 
 
 def cpu_baseline(layers, args):
     """The oracle (fp64 numpy, as it stands) on the host: the same round trip
-    (whiten, E4M3, dequantize, un-whiten) on the block's gradients, repeated
-    until about cpu_seconds of work; GB/s of fp32 gradient."""
+    (whiten, E4M3, dequantize, un-whiten) on the workload's first gradients,
+    layer after layer, until about cpu_seconds of work; GB/s of fp32 gradient."""
     from threadpoolctl import threadpool_info
 
     from oracle import gift as og
 
     log(args, "cpu baseline (oracle)")
-    host = []
-    for L in layers:
-        c = L.factor.coef.cpu().numpy().astype("float64")
-        f = og.factor_from_parts(L.factor.U.cpu().numpy(), L.factor.theta.cpu().numpy(),
-                                 c[2], c[3], c[4], c[5])
-        host.append((L.G.cpu().numpy(), f))
     done_bytes, t0 = 0, time.perf_counter()
-    passes = 0
-    while True:
-        for G, f in host:
-            og.gift_roundtrip(G, f)
-            done_bytes += G.nbytes
-        passes += 1
+    n_layers = 0
+    shapes = []
+    facs = {}
+    for L in layers:
+        key = L.factor.U.data_ptr()
+        if key not in facs:
+            c = L.factor.coef.cpu().numpy().astype("float64")
+            facs[key] = og.factor_from_parts(L.factor.U.cpu().numpy(), L.factor.theta.cpu().numpy(),
+                                             c[2], c[3], c[4], c[5])
+        G = L.G.cpu().numpy()
+        og.gift_roundtrip(G, facs[key])
+        done_bytes += G.nbytes
+        n_layers += 1
+        shapes.append("%dx%d" % G.shape)
+        del G
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     el = time.perf_counter() - t0
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": "%d pass(es) over the block's 7 gradients (%.1f MB fp32), %.1f s, "
-                      "BLAS threads %d, host CPUs %d" % (passes, sum(G.nbytes for G, _ in host)
-                                                         / 1e6, el, threads,
-                                                         len(os.sched_getaffinity(0)))}
+            "sample": "the first %d gradients of the workload (%s; %.2f GB fp32) through the "
+                      "oracle's fp64 round trip, %.1f s (including the host copies), BLAS threads "
+                      "%d, host CPUs %d" % (n_layers, ", ".join(shapes), done_bytes / 1e9, el,
+                                            threads, len(os.sched_getaffinity(0)))}
 
 
 # ---------------------------------------------------------------------------
@@ -769,6 +875,57 @@ def rank_study(args, device="cuda:0"):
 # full-rank and two-sided references
 # ---------------------------------------------------------------------------
 
+def reference_factors(A, dev):
+    """The harness's fp64 transforms of one input: (S, S^-1) = ((A + lam I)^-1/2,
+    (A + lam I)^1/2) by eigh, and the Cholesky pair (L^-T, L^T) of A + lam I,
+    lam = 1e-3 tr(A) / d_in."""
+    import torch
+
+    def sym_pair(M):
+        lam = 1e-3 * torch.trace(M) / M.shape[0]
+        ev_, V = torch.linalg.eigh(M + lam * torch.eye(M.shape[0], dtype=M.dtype, device=dev))
+        ev_ = ev_.clamp_min(0)
+        return (V * ev_.rsqrt()) @ V.T, (V * ev_.sqrt()) @ V.T
+
+    S, Si = sym_pair(A)
+    lam = 1e-3 * torch.trace(A) / A.shape[0]
+    eye = torch.eye(A.shape[0], dtype=A.dtype, device=dev)
+    L = torch.linalg.cholesky(A + lam * eye)
+    Linv = torch.linalg.solve_triangular(L, eye, upper=False)
+    return {"S": S, "Si": Si, "Lt_inv": Linv.T.contiguous(), "Lt": L.T.contiguous(),
+            "sym_pair": sym_pair}
+
+
+def reference_outputs(G, rf, factor):
+    """Round trips of one gradient G (fp32, device) under every method of the
+    reference study.  Returns {method: (W32, codes, inv, G^ fp64)}; W32 is
+    None for the library's own paths (Euclid, GIFT rank 32).  The reference
+    transforms are fp64 torch (harness); each whitened tensor is rounded to
+    fp32 and quantized by the library's per-tensor E4M3 kernels."""
+    import fac_whitening_gift_amd as fg
+
+    G64 = G.double()
+    SB, SBi = rf["sym_pair"](G64 @ G64.T / G64.shape[1])
+    outs = {}
+    eu = fg.Layer(G)
+    fg.gift_euclid_fp8_roundtrip([eu])
+    outs["euclid"] = (None, eu.q, eu.inv_scale, eu.G_hat.double())
+    gl = fg.Layer(G, factor=factor)
+    fg.gift_whiten_quantize([gl])
+    fg.gift_dequant_unwhiten([gl])
+    outs["gift_rank32"] = (None, gl.q, gl.inv_scale, gl.G_hat.double())
+    for name, (lt, rt, lti, rti) in (("input_full", (None, rf["S"], None, rf["Si"])),
+                                      ("input_cholesky", (None, rf["Lt_inv"], None, rf["Lt"])),
+                                      ("two_sided", (SB, rf["S"], SBi, rf["Si"]))):
+        W = G64 if lt is None else lt @ G64
+        W32 = (W @ rt).float().contiguous()
+        q = fg.Layer(W32)
+        fg.gift_euclid_fp8_roundtrip([q])
+        Wh = q.G_hat.double()
+        outs[name] = (W32, q.q, q.inv_scale, (Wh if lti is None else lti @ Wh) @ rti)
+    return outs
+
+
 def reference_study(args, device="cuda:0"):
     """Where the rank-32 input-side factor stands against the transforms it
     simplifies (the review: the input-side factor alone matches the full
@@ -796,13 +953,6 @@ def reference_study(args, device="cuda:0"):
     facs = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
     fg.gift_refresh_factors([dict(X=inputs[s.name]["X"], factor=facs[s.name], seed=k)
                              for k, s in enumerate(w.inputs)])
-
-    def sym_pair(M):
-        lam = 1e-3 * torch.trace(M) / M.shape[0]
-        ev_, V = torch.linalg.eigh(M + lam * torch.eye(M.shape[0], dtype=M.dtype, device=dev))
-        ev_ = ev_.clamp_min(0)
-        return (V * ev_.rsqrt()) @ V.T, (V * ev_.sqrt()) @ V.T
-
     methods = ["euclid", "gift_rank32", "input_full", "input_cholesky", "two_sided"]
     num1 = {k: 0.0 for k in methods}
     num2 = {k: 0.0 for k in methods}
@@ -812,40 +962,17 @@ def reference_study(args, device="cuda:0"):
         inp = inputs[l.input]
         if l.input not in cache:
             X = inp["X"].double()
-            A = X.T @ X / X.shape[0]
-            S, Si = sym_pair(A)
-            lam = 1e-3 * torch.trace(A) / A.shape[0]
-            L = torch.linalg.cholesky(A + lam * torch.eye(A.shape[0], dtype=A.dtype, device=dev))
-            Linv = torch.linalg.solve_triangular(L, torch.eye(A.shape[0], dtype=A.dtype, device=dev),
-                                                 upper=False)
-            cache[l.input] = (S, Si, Linv.T.contiguous(), L.T.contiguous())
-        S, Si, Lt_inv, Lt = cache[l.input]
+            cache[l.input] = reference_factors(X.T @ X / X.shape[0], dev)
+        rf = cache[l.input]
         G = synth.draw_gradient(l.d_out, inp["Q"], inp["ev"], seed=5000 + i, device=dev)
+        outs = reference_outputs(G, rf, facs[l.input])
         G64 = G.double()
-        SB, SBi = sym_pair(G64 @ G64.T / G64.shape[1])
-        outs = {}
-        eu = fg.Layer(G)
-        fg.gift_euclid_fp8_roundtrip([eu])
-        outs["euclid"] = eu.G_hat.double()
-        gl = fg.Layer(G, factor=facs[l.input])
-        fg.gift_whiten_quantize([gl])
-        fg.gift_dequant_unwhiten([gl])
-        outs["gift_rank32"] = gl.G_hat.double()
-        for name, (lt, rt, lti, rti) in (("input_full", (None, S, None, Si)),
-                                          ("input_cholesky", (None, Lt_inv, None, Lt)),
-                                          ("two_sided", (SB, S, SBi, Si))):
-            W = G64 if lt is None else lt @ G64
-            W32 = (W @ rt).float().contiguous()
-            q = fg.Layer(W32)
-            fg.gift_euclid_fp8_roundtrip([q])
-            Wh = q.G_hat.double()
-            outs[name] = (Wh if lti is None else lti @ Wh) @ rti
         for k in methods:
-            E = outs[k] - G64
-            num1[k] += float(E.pow(2).sum())
-            num2[k] += float((E @ S).pow(2).sum())
+            e2, g2 = m2_parts(G64, outs[k][3], rf["S"])
+            num1[k] += float((outs[k][3] - G64).pow(2).sum())
+            num2[k] += e2
         den1 += float(G64.pow(2).sum())
-        den2 += float((G64 @ S).pow(2).sum())
+        den2 += g2
     rows = {k: {"m1": round(float(np.sqrt(num1[k] / den1)), 5),
                 "m2": round(float(np.sqrt(num2[k] / den2)), 5),
                 "m2_reduction_vs_euclid": round(1 - float(np.sqrt(num2[k] / num2["euclid"])), 4)}
@@ -937,6 +1064,72 @@ def reduce_study(args, device="cuda:0"):
         res["m2_reduction"] = round(1 - res["gift"]["m2"] / res["euclid"]["m2"], 4)
         out[fmt] = res
     return out
+
+
+# ---------------------------------------------------------------------------
+# matrix-free refresh study
+# ---------------------------------------------------------------------------
+
+def matrixfree_study(args, device="cuda:0"):
+    """Would the matrix-free form of the refresh's products, A Q = X^T (X Q) / N,
+    pay on these shapes?  It skips the covariance but reads X twice per
+    product.  On the 600M stack's 96 inputs (72 of width 1536, 24 of width
+    4096, 16384 bf16 tokens each): the library's grouped refresh (covariance
+    on bf16 MFMA, then six products with A on split-bf16 MFMA, CholeskyQR and
+    Rayleigh-Ritz) against the six products alone in matrix-free form as
+    plain fp32 library GEMMs (torch on the device; the products need fp32
+    accuracy, and X is exact in fp32).  If the products alone take longer
+    than the whole library refresh, the matrix-free form cannot win.  The
+    matrix-free product is checked against A Q on one input (fp64)."""
+    import torch
+
+    import synth
+    import fac_whitening_gift_amd as fg
+
+    dev = torch.device(device)
+    w = synth.llama_stack(24, 1536, 4096, 16384, exponent=1.5)
+    inputs = [synth.draw_input(s, seed=1000 + k, device=dev, as_bf16=True, axis_aligned=True)
+              for k, s in enumerate(w.inputs)]
+    facs = [fg.Factor(s.d_in, device=dev) for s in w.inputs]
+    items = [dict(X=inp["X"], factor=f, seed=k) for k, (inp, f) in enumerate(zip(inputs, facs))]
+    ws = torch.empty(fg.gift_refresh_group_workspace_bytes(items), dtype=torch.uint8, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    t_lib = timed(lambda: fg.gift_refresh_factors(items, ws=ws))
+    Xf = [inp["X"].float() for inp in inputs]
+    Qs = [torch.linalg.qr(torch.randn(s.d_in, 64, device=dev))[0] for s in w.inputs]
+
+    def products():
+        for X, Q in zip(Xf, Qs):
+            for _ in range(6):
+                (X.T @ (X @ Q)) / X.shape[0]
+
+    t_mf = timed(products)
+    X64 = Xf[-1].double()
+    A = X64.T @ X64 / X64.shape[0]
+    Q = Qs[-1]
+    ref = A @ Q.double()
+    got = (Xf[-1].T @ (Xf[-1] @ Q)) / Xf[-1].shape[0]
+    rel = float(torch.linalg.norm(got.double() - ref) / torch.linalg.norm(ref))
+    flops = sum(6 * 2 * 2 * s.tokens * s.d_in * 64 for s in w.inputs)
+    return {"study": "matrixfree", "workload": w.name, "inputs": len(w.inputs),
+            "library_refresh_ms": round(t_lib, 3),
+            "matrix_free_six_products_ms": round(t_mf, 3),
+            "matrix_free_tflop": round(flops / 1e12, 3),
+            "matrix_free_tflops": round(flops / t_mf / 1e9, 1),
+            "matrix_free_rel_err_vs_fp64": rel,
+            "ratio_products_over_library_refresh": round(t_mf / t_lib, 3)}
 
 
 if __name__ == "__main__":
