@@ -39,6 +39,7 @@ EXPORTS = (
     "gift_abi_version", "gift_draw_sketch", "gift_factor_pack_bytes", "gift_prepare_factor",
     "gift_refresh_factors", "gift_refresh_group_workspace_bytes", "gift_build_hash",
     "gift_dequant_accumulate", "gift_unwhiten_f32", "gift_block_factor_pack_bytes",
+    "gift_whiten_quantize_static", "gift_static_scratch_bytes",
 )
 
 
@@ -86,6 +87,8 @@ def load():
                                     P, SZ, P]),
         "gift_refresh_workspace_bytes": (SZ, [I64, I64, I, I]),
         "gift_whiten_quantize": (I, [LP, I, I, P, P, SZ, P]),
+        "gift_whiten_quantize_static": (I, [LP, I, I, P, P]),
+        "gift_static_scratch_bytes": (SZ, []),
         "gift_dequant_unwhiten": (I, [LP, I, I, P, SZ, P]),
         "gift_euclid_fp8_roundtrip": (I, [LP, I, I, P, P, SZ, P]),
         "gift_roundtrip_error": (I, [LP, I, P, P, SZ, P]),
@@ -312,6 +315,18 @@ def gift_whiten_quantize(layers, scaling=SCALE_TENSOR, flags=None, ws=None, stre
     ws = _workspace(need, _device_of(layers), ws)
     _check(lib.gift_whiten_quantize(arr, len(layers), scaling, _ptr(flags), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gift_whiten_quantize_static(layers, scaling=SCALE_TENSOR, flags=None, stream=None):
+    """gift_whiten_quantize with the library's static device scratch (no
+    workspace, nothing allocated); calls on one GPU must not overlap."""
+    arr = _layers_array(layers)
+    _check(load().gift_whiten_quantize_static(arr, len(layers), scaling, _ptr(flags),
+                                              _stream(stream)))
+
+
+def gift_static_scratch_bytes():
+    return int(load().gift_static_scratch_bytes())
 
 
 def gift_dequant_unwhiten(layers, scaling=SCALE_TENSOR, ws=None, stream=None):

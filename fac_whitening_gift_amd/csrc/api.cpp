@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -399,6 +400,39 @@ gift_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return GIFT_OK;
 }
 
+// Scratch of gift_whiten_quantize_static: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never uses the array's
+// name as an address: each device's copy is found once with
+// hipGetSymbolAddress (with that device current) and kept in
+// g_scratch_ptr.  The whiten kernels need nothing in it zeroed: every word
+// they read there was written earlier in the same call.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+gift_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "device %d: the static scratch serves devices 0..%d",
+                dev, kScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p % kAlign))
+      return fail(GIFT_ERR_HIP, "static scratch of device %d is not 256-byte aligned", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GIFT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -476,6 +510,24 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
     if (s != GIFT_OK) return s;
   }
   return GIFT_OK;
+}
+
+size_t gift_static_scratch_bytes(void) { return kScratchBytes; }
+
+gift_status gift_whiten_quantize_static(const gift_layer* layers, int n_layers, int scaling,
+                                        uint32_t* dev_flags, void* stream) {
+  gift_status s = check_layers(layers, n_layers, Op::Whiten, scaling);
+  if (s != GIFT_OK) return s;
+  const size_t need = group_ws(layers, n_layers, Op::Whiten, scaling != GIFT_SCALE_TENSOR);
+  if (need > kScratchBytes)
+    return fail(GIFT_ERR_WORKSPACE_TOO_SMALL,
+                "gift_whiten_quantize_static: the call needs %zu bytes of scratch, more than the "
+                "%zu of the static array; split the group or call gift_whiten_quantize",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != GIFT_OK) return s;
+  return gift_whiten_quantize(layers, n_layers, scaling, dev_flags, ws, kScratchBytes, stream);
 }
 
 gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int scaling, void* ws,

@@ -285,6 +285,28 @@ gift_status gift_whiten_quantize(const gift_layer *layers, int n_layers,
                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * gift_whiten_quantize_static -- gift_whiten_quantize for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture
+ * that may not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and flags as gift_whiten_quantize;
+ * its scratch (the partial row coefficients, the split c' operands, the tile
+ * and layer amax words, the operand packs of factors without packs) lives
+ * in a static device array of gift_static_scratch_bytes() bytes (16 MiB)
+ * compiled into the library, one per GPU, held until the process ends.  A
+ * call whose gift_group_workspace_bytes(GIFT_OP_WHITEN_QUANTIZE, ...) exceeds
+ * that size returns GIFT_ERR_WORKSPACE_TOO_SMALL before enqueueing anything
+ * (split the group).  The call allocates nothing; its first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress).  Every
+ * call on one GPU uses the same array: calls that overlap in time on one GPU
+ * (different streams, or threads) race and must be serialised by the
+ * caller.  Nothing in the array needs to start zeroed.
+ */
+gift_status gift_whiten_quantize_static(const gift_layer *layers, int n_layers,
+                                        int scaling, uint32_t *dev_flags,
+                                        void *stream);
+size_t gift_static_scratch_bytes(void);
+
+/*
  * gift_dequant_unwhiten -- the receive side ("maps the result back", "The
  * pith"): W^ = decode(q) * inv; G_hat = W^ A_r^1/2 (factor != NULL) or
  * G_hat = W^ (factor == NULL).  Reads q, inv_scale (and the factor); writes

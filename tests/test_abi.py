@@ -207,3 +207,19 @@ def test_refresh_workspace_has_no_partials_for_single_range_bf16():
     # one such input alone splits its tokens over two ranges: partials needed
     alone = lib.gift_refresh_workspace_bytes(d, n, fg.DTYPE_BF16, w)
     assert alone > per
+
+
+def test_static_scratch_entry_rejects_groups_beyond_its_array():
+    """gift_whiten_quantize_static serves groups whose whiten workspace fits
+    its 16 MiB static array; a larger group is refused before anything is
+    enqueued (no GPU needed), with the sizes in the message."""
+    lib = fg.load()
+    assert lib.gift_static_scratch_bytes() == 16 << 20
+    f = _lib._Factor(4096, 32, 0x20000, 0x30000, 0x40000, 0x50000)
+    layers = [_layer(d_out=11008, d_in=4096, factor=ctypes.pointer(f))]
+    arr = (_lib._Layer * 1)(*layers)
+    need = lib.gift_group_workspace_bytes(_lib.OP_WHITEN_QUANTIZE, arr, 1, fg.SCALE_TENSOR)
+    assert need > 16 << 20
+    assert lib.gift_whiten_quantize_static(arr, 1, fg.SCALE_TENSOR, None, None) == 3
+    assert b"16777216" in lib.gift_last_error()
+    assert lib.gift_whiten_quantize_static(arr, 1, 9, None, None) == 1
