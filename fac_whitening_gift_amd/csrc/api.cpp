@@ -35,6 +35,7 @@ namespace gift {
   size_t pack_bytes(int64_t d_in);
 namespace rt4 {
 GIFT_TILE_DECLS
+hipError_t launch_slab_whiten_quantize(const GroupDev& g, bool write_w, hipStream_t s);
 }
 namespace rt2 {
 GIFT_TILE_DECLS
@@ -311,6 +312,18 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
 // round of workgroups on the machine is shorter.
 constexpr int64_t kSmallGroupElems = int64_t(1) << 25;
 
+// Rank-r whitened layers of at least this many elements, with per-tensor
+// scaling, whiten as slabs (one workgroup per 64-row block: no partial
+// buffer, no reduction launch), then quantize on the 64-row tile kernels.
+// The choice depends on the layer alone, so a layer's results do not depend
+// on the group it is called with.
+constexpr int64_t kSlabMinElems = int64_t(1) << 22;
+
+bool slab_layer(const gift_layer& L, int scaling) {
+  return L.factor && !L.factor->block && scaling == GIFT_SCALE_TENSOR &&
+         L.d_out * L.d_in >= kSlabMinElems;
+}
+
 const TileOps& tile_ops(const gift_layer* layers, int n, Op op) {
   int64_t e = 0;
   for (int i = 0; i < n; ++i)
@@ -323,7 +336,7 @@ const TileOps& tile_ops(const gift_layer* layers, int n, Op op) {
 template <class Pick, class Tiles, class Launch>
 gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void* ws,
                         uint32_t* flags, double* out, Pick pick, Tiles tiles, Launch launch,
-                        const TileOps& geo = kTiles64) {
+                        const TileOps& geo = kTiles64, bool slab = false) {
   // workspace: operand packs first, then per-layer slices in layer order
   // (independent of the chunking)
   const Packs packs = plan_packs(layers, n, op);
@@ -376,6 +389,7 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     d.n_rb = geo.row_blocks(L.d_out);
     d.ngrp = !whitened(L, op) ? 1 : fblock(L) ? blk_col_groups(L.d_in, fblock(L)) : col_groups(L.d_in);
     d.n_tiles = tiles(L);
+    d.n_part = slab ? (int)d.n_rb : d.n_tiles;  // one amax partial per row block or per tile
     d.tile_begin = g.total_tiles;
     g.total_tiles += d.n_tiles;
     d.rb_begin = g.total_rb;
@@ -481,11 +495,13 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
   s = run_packs(plan_packs(layers, n_layers, Op::Whiten), ws, st);
   if (s != GIFT_OK) return s;
   const TileOps& geo = tile_ops(layers, n_layers, Op::Whiten);
-  // groups: rank-r factors, Euclidean layers, block factors of 32, of 64
-  for (int wgrp = 0; wgrp < 4; ++wgrp) {
+  // groups: rank-r factors on tiles, Euclidean layers, block factors of 32,
+  // of 64, rank-r factors as slabs
+  for (int wgrp = 0; wgrp < 5; ++wgrp) {
     auto pick = [&](const gift_layer& L) {
-      return wgrp == 0 ? L.factor != nullptr && !L.factor->block
+      return wgrp == 0 ? L.factor != nullptr && !L.factor->block && !slab_layer(L, scaling)
            : wgrp == 1 ? L.factor == nullptr
+           : wgrp == 4 ? slab_layer(L, scaling)
                        : fblock(L) == (wgrp == 2 ? 32 : 64);
     };
     bool any_w = false;
@@ -502,6 +518,12 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
                       tiles_flat, [&](const GroupDev& g, int) {
                         return launch_flat_quantize(g, scaling, false, any_w, st);
                       });
+    else if (wgrp == 4)
+      s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
+                      [&](const gift_layer& L) { return row_tiles(L, kTiles64); },
+                      [&](const GroupDev& g, int) {
+                        return rt4::launch_slab_whiten_quantize(g, any_w, st);
+                      }, kTiles64, true);
     else
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {

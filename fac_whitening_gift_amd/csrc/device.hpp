@@ -281,6 +281,7 @@ struct LayerDev {
   int64_t n_rb;         // row blocks of the tile kernels
   int ngrp;             // column groups of the tile kernels
   int tile_begin, n_tiles;
+  int n_part;           // amax partials of the layer (tiles, or row blocks of a slab layer)
   int rb_begin;         // first row block of the layer in the group
 };
 

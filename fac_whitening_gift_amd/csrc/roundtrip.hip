@@ -792,10 +792,10 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
     });
   });
   uint32_t m = 0u;
-  if (L.n_tiles > kPartialLimit) {
+  if (L.n_part > kPartialLimit) {
     m = *L.amax;
   } else {
-    for (int i = threadIdx.x; i < L.n_tiles; i += kTileThreads) m = max(m, L.part[i]);
+    for (int i = threadIdx.x; i < L.n_part; i += kTileThreads) m = max(m, L.part[i]);
     m = block_max_u32<kTileThreads>(m, mx);
   }
   const Scale sc = scale_from_amax_bits(m);
@@ -961,10 +961,10 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_whiten(GroupDev gd) {
     if (threadIdx.x == 0) L.part[tile] = m;
   } else if constexpr (kMode == 1) {
     uint32_t m = 0u;
-    if (L.n_tiles > kPartialLimit) {
+    if (L.n_part > kPartialLimit) {
       m = *L.amax;
     } else {
-      for (int i = threadIdx.x; i < L.n_tiles; i += kTileThreads) m = max(m, L.part[i]);
+      for (int i = threadIdx.x; i < L.n_part; i += kTileThreads) m = max(m, L.part[i]);
       m = block_max_u32<kTileThreads>(m, mx);
     }
     const Scale sc = scale_from_amax_bits(m);
@@ -1226,7 +1226,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_final(GroupDev g) {
   const LayerDev& L = g.L[blockIdx.x];
   __shared__ uint32_t mx[kThreads / 64];
   uint32_t m = 0u;
-  for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) m = max(m, L.part[i]);
+  for (int i = threadIdx.x; i < L.n_part; i += kThreads) m = max(m, L.part[i]);
   m = block_max_u32<kThreads>(m, mx);
   if (threadIdx.x == 0) *L.amax = m;
 }
@@ -1411,6 +1411,185 @@ __global__ __launch_bounds__(kThreads) void k_err_final(GroupDev g, int out_base
   }
 }
 
+#if GIFT_TILE_RT == 4
+// ---------------------------------------------------------------------------
+// slab kernels.  A workgroup of kSW waves owns one row block -- kTileRows
+// rows of one layer and every column -- so a row's c = g U is complete
+// inside it: no partial buffer and no reduction launch.  Wave w takes the
+// 32-column chunks w, w + kSW, w + 2 kSW, ... (the waves of one step cover
+// adjacent columns).  Phase 1 forms the wave's partial c over its chunks on
+// MFMA with the next chunk's operands in flight while the current one is
+// multiplied; the waves' partials are summed in wave order through LDS, c'
+// is formed and split into the second product's operand form; phase 2 walks
+// the chunks again, last first (the most recently read data is the likeliest
+// to be still in a cache), for the second product.  The gradient is read
+// twice, both times by the same workgroup.  Chunk loads are issued
+// unconditionally (past the wave's last chunk it loads its current chunk
+// again, a cache hit), so every wait is for the chunk in use.  Only the
+// whiten side runs this way: a dequantize slab (codes read twice, G^
+// written once, no partials) measured slower than the three tile kernels.
+// ---------------------------------------------------------------------------
+constexpr int kSW = 8;                    // waves per slab workgroup
+constexpr int kSlabThreads = 64 * kSW;
+
+struct Slab {
+  int row[kTR];   // this lane's gradient row in each 16-row tile (clamped)
+  bool ok[kTR];   // row < d_out
+  int nch;        // 32-column chunks of the layer
+  int nmine;      // chunks of this wave: wave, wave + kSW, ...
+  int lane, wave, r16, g;
+};
+
+__device__ __forceinline__ Slab slab_ctx(const LayerDev& L, int64_t rb) {
+  Slab x;
+  x.lane = threadIdx.x & 63;
+  x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  x.r16 = x.lane & 15;
+  x.g = x.lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt) {
+    const int64_t r = rb * kTileRows + 16 * rt + x.r16;
+    x.ok[rt] = r < L.d_out;
+    x.row[rt] = (int)(x.ok[rt] ? r : L.d_out - 1);
+  }
+  x.nch = (int)(L.d_in / kChunk);
+  x.nmine = x.wave < x.nch ? (x.nch - x.wave + kSW - 1) / kSW : 0;
+  return x;
+}
+
+// the operands of the wave's k-th chunk (k clamped to its last chunk)
+template <bool kCodes>
+struct SlabOps {
+  uint4 pa[2][3];
+  float4 gv[kCodes ? 1 : kTR][2];
+  uint32_t qv[kCodes ? kTR : 1][2];
+};
+
+template <bool kCodes>
+__device__ __forceinline__ void slab_load(const LayerDev& L, const Slab& x, const uint4* P, int k,
+                                          SlabOps<kCodes>& o) {
+  const int c = x.wave + kSW * (k < x.nmine ? k : x.nmine - 1);
+  load_a(P, c, x.lane, o.pa);
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt) {
+    if constexpr (kCodes) load_qc(L, x.row[rt], x.g, c, o.qv[rt]);
+    else load_gc(L, x.row[rt], x.g, c, o.gv[rt]);
+  }
+}
+
+// Phase 1 and the reduction: c' of the slab's rows (times D_w; on codes,
+// times D_u and the tensor's inverse scale) in operand form in cs, and, when
+// cfin is not NULL, also in global memory for a later pass.  Contains
+// workgroup barriers.
+template <bool kCodes>
+__device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, int64_t rb,
+                                            float (*red)[kTR * 8][64], uint4* cs) {
+  f32x4 acc[kTR][2];
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (x.nmine > 0) {  // wave-uniform
+    SlabOps<kCodes> o[2];
+    slab_load<kCodes>(L, x, L.P, 0, o[0]);
+    auto mult = [&](const SlabOps<kCodes>& op) {
+      bf16x8 a[2][3];
+      as_ops(op.pa, a);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        if constexpr (kCodes) cpart_q(a, op.qv[rt], acc[rt]);
+        else cpart_g(a, op.gv[rt], acc[rt]);
+      }
+    };
+    for (int k = 0; k < x.nmine; k += 2) {
+      slab_load<kCodes>(L, x, L.P, k + 1, o[1]);
+      mult(o[0]);
+      if (k + 1 >= x.nmine) break;
+      slab_load<kCodes>(L, x, L.P, k + 2, o[0]);
+      mult(o[1]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < kTR; ++rt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[x.wave][rt * 8 + 4 * h + i][x.lane] = acc[rt][h][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kTR * 64; e += kSlabThreads) {
+    const int rt = e >> 6, lane = e & 63;
+    const float* dk = L.coef + (kCodes ? GIFT_COEF_DU : GIFT_COEF_DW);
+    const float extra = kCodes ? L.inv[0] : 1.f;
+    float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kSW; ++w)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s8[k] += red[w][rt * 8 + k][lane];
+    float cp[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cp[k] = s8[k] * (dk[rank_of(k, lane >> 4)] * extra);
+    bf16x8 cb[3];
+    split3(cp, cb);
+    uint4* out = L.cfin ? reinterpret_cast<uint4*>(L.cfin) + rb * kCOp : nullptr;
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) {
+      const uint4 v = __builtin_bit_cast(uint4, cb[sp]);
+      cs[(rt * 3 + sp) * 64 + lane] = v;
+      if (out) out[(rt * 3 + sp) * 64 + lane] = v;
+    }
+  }
+  __syncthreads();
+}
+
+// whiten, first pass of per-tensor scaling: c' (to the workspace, for the
+// quantize pass) and the slab's amax of |W| (to the layer's partials).
+// grid: one workgroup per row block of the group.
+__global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
+  const LayerDev L = gd.L[find_layer_rb(gd, blockIdx.x)];
+  const int64_t rb = blockIdx.x - L.rb_begin;
+  const Slab x = slab_ctx(L, rb);
+  __shared__ float red[kSW][kTR * 8][64];
+  __shared__ uint4 cs[kCOp];
+  __shared__ uint32_t mx[kSW];
+  slab_cprime<false>(L, x, rb, red, cs);
+  const uint4* P2 = p2_of(L);
+  const float alpha = L.coef[GIFT_COEF_ALPHA];
+  uint32_t m = 0u;
+  if (x.nmine > 0) {  // wave-uniform
+    SlabOps<false> o[2];
+    const int last = x.nmine - 1;
+    slab_load<false>(L, x, P2, last, o[0]);
+    auto amax_of = [&](const SlabOps<false>& op) {
+      bf16x8 a[2][3];
+      as_ops(op.pa, a);
+#pragma unroll
+      for (int rt = 0; rt < kTR; ++rt) {
+        bf16x8 cb[3];
+        c_operand(cs, rt, x.lane, cb);
+        f32x4 corr[2];
+        correction(a, cb, corr);
+        if (!x.ok[rt]) continue;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float4 gg = op.gv[rt][t];
+          const float4 w = make_float4(fmaf(alpha, gg.x, corr[t][0]), fmaf(alpha, gg.y, corr[t][1]),
+                                       fmaf(alpha, gg.z, corr[t][2]), fmaf(alpha, gg.w, corr[t][3]));
+          m = amax4(m, w);
+        }
+      }
+    };
+    for (int k = last; k >= 0; k -= 2) {
+      slab_load<false>(L, x, P2, k > 0 ? k - 1 : 0, o[1]);
+      amax_of(o[0]);
+      if (k == 0) break;
+      slab_load<false>(L, x, P2, k > 1 ? k - 2 : 0, o[0]);
+      amax_of(o[1]);
+    }
+  }
+  m = block_max_u32<kSlabThreads>(m, mx);
+  if (threadIdx.x == 0) L.part[rb] = m;
+}
+
+#endif  // GIFT_TILE_RT == 4
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -1451,7 +1630,7 @@ hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, 
   GIFT_TW(GIFT_SCALE_TENSOR, false);
 #undef GIFT_TW
   bool tall = false;
-  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_tiles > kPartialLimit;
+  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_part > kPartialLimit;
   if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
   if (write_w) k_tile_quant<kCPW, true><<<grid, blk, 0, s>>>(g);
   else k_tile_quant<kCPW, false><<<grid, blk, 0, s>>>(g);
@@ -1480,6 +1659,24 @@ hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool w
 #undef GIFT_FQ
   return hipGetLastError();
 }
+
+#if GIFT_TILE_RT == 4
+// per-tensor whiten + quantize of layers whose row blocks run as slabs:
+// k_slab_whiten (c' and one amax partial per row block), the layer amax
+// (k_amax_final for layers of more than kPartialLimit row blocks), and the
+// 64-row tile quantize pass on the slabs' c'
+hipError_t launch_slab_whiten_quantize(const GroupDev& g, bool write_w, hipStream_t s) {
+  k_slab_whiten<<<dim3(g.total_rb), dim3(kSlabThreads), 0, s>>>(g);
+  bool tall = false;
+  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_part > kPartialLimit;
+  if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
+  const dim3 grid(g.total_tiles), blk(kTileThreads);
+  if (write_w) k_tile_quant<kCPW, true><<<grid, blk, 0, s>>>(g);
+  else k_tile_quant<kCPW, false><<<grid, blk, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+#endif
 
 hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s) {
   if (white) {
@@ -1533,7 +1730,7 @@ hipError_t launch_blk_whiten(const GroupDev& g, int b, int scaling, bool write_w
   }
   if (b == 32) GIFT_BW(32, 0, false); else GIFT_BW(64, 0, false);
   bool tall = false;
-  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_tiles > kPartialLimit;
+  for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_part > kPartialLimit;
   if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
   if (b == 32) { if (write_w) GIFT_BW(32, 1, true); else GIFT_BW(32, 1, false); }
   else { if (write_w) GIFT_BW(64, 1, true); else GIFT_BW(64, 1, false); }
