@@ -25,7 +25,7 @@ JSON line on stdout.
     python bench.py --workload block1024     # one block at hidden 1024
     python bench.py --study staleness [--blocks 1 --hidden 4096 --mlp 11008]
     python bench.py --study interval [--intervals 10,25,50,100]   # refresh-interval ablation
-    python bench.py --study rank [--rank-list 8,16,32,b32,b64]     # rank / block-A sweep
+    python bench.py --study rank [--rank-list 8,16,32,64,b32,b64]  # rank / block-A sweep
     python bench.py --study reference     # full-rank, Cholesky-form and two-sided references
     python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
     python bench.py --study matrixfree    # refresh power steps with A Q = X^T (X Q) / N
@@ -67,7 +67,7 @@ def parse():
                             "matrixfree"])
     p.add_argument("--ref-shape", default="1024,2816,8192",
                    help="hidden,mlp,tokens of the block of the reference study")
-    p.add_argument("--rank-list", default="8,16,32,b32,b64",
+    p.add_argument("--rank-list", default="8,16,32,64,b32,b64",
                    help="factor ranks, and bN for block-diagonal N x N blocks (rank study)")
     p.add_argument("--intervals", default="10,25,50,100", help="refresh intervals (interval study)")
     p.add_argument("--ranks", type=int, default=8, help="ranks of the reduce study")
@@ -786,7 +786,8 @@ def rank_study(args, device="cuda:0"):
     chose rank 32 from a round-trip error table over ranks, with block-A-32
     and block-A-64 beside them).  On the hidden-1024 block (4 inputs, 7
     gradients): for each rank r, the grouped refresh keeps the top r Ritz
-    pairs of the same subspace iteration (sketch width 64) and damps with the
+    pairs of a subspace iteration of sketch width r + 32 rounded to the
+    factor's storage (64 up to rank 32, 96 for rank 64) and damps with the
     mean of the d_in - r discarded eigenvalues; an entry "bN" is the
     block-diagonal factor with N x N blocks, damped by lambda_floor; then the
     grouped per-tensor E4M3 round trip of all 7 gradients.  M1 from the

@@ -13,8 +13,8 @@ from ._lib import (  # noqa: F401
     gift_dequant_unwhiten, gift_euclid_fp8_roundtrip, gift_roundtrip_error,
     gift_group_workspace_bytes, gift_draw_sketch, gift_factor_pack_bytes, gift_block_factor_pack_bytes,
     gift_prepare_factor, gift_refresh_factors, gift_refresh_group_workspace_bytes,
-    gift_whiten_quantize_static, gift_static_scratch_bytes,
-    RANK, MAX_SKETCH, BLOCK, DTYPE_F32, DTYPE_BF16, DAMP_FLOOR, DAMP_FLOOR_PLUS_TAIL,
+    gift_whiten_quantize_static, gift_static_scratch_bytes, factor_cols, MAX_RANK,
+    RANK, MAX_SKETCH, SKETCH_WIDTH, sketch_width_for, BLOCK, DTYPE_F32, DTYPE_BF16, DAMP_FLOOR, DAMP_FLOOR_PLUS_TAIL,
     SCALE_TENSOR, SCALE_BLOCK128, SCALE_MXFP4, MX_BLOCK, FLAG_NONFINITE, FLAG_ZERO_AMAX, EXPORTS,
     COEF_ALPHA, COEF_BETA, COEF_LAMBDA_ISO, COEF_LAMBDA_FLOOR, COEF_TRACE, COEF_SIGMA2_TAIL,
     COEF_DW, COEF_DU, COEF_COUNT,

@@ -15,7 +15,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgift.so")
 
 RANK = 32
-MAX_SKETCH = 64
+MAX_RANK = 64
+MAX_SKETCH = 96
+SKETCH_WIDTH = 64      # the refresh's subspace width for rank <= 32 (rank + 32)
+
+
+def sketch_width_for(rank):
+    """Subspace width of the refresh for a factor of this rank: rank + 32
+    oversampling rounded to the 32-column storage, i.e. 64 up to rank 32 and
+    96 above."""
+    return SKETCH_WIDTH if rank <= RANK else MAX_SKETCH
 BLOCK = 128
 
 GIFT_OK = 0
@@ -32,6 +41,11 @@ COEF_DW = 8
 COEF_DU = 8 + RANK
 COEF_COUNT = 8 + 2 * RANK
 
+
+def factor_cols(rank):
+    """Storage columns of a rank-r factor: 32 up to rank 32, else 64."""
+    return RANK if rank <= RANK else 2 * RANK
+
 EXPORTS = (
     "gift_refresh_factor", "gift_refresh_workspace_bytes", "gift_whiten_quantize",
     "gift_dequant_unwhiten", "gift_euclid_fp8_roundtrip", "gift_roundtrip_error",
@@ -39,7 +53,7 @@ EXPORTS = (
     "gift_abi_version", "gift_draw_sketch", "gift_factor_pack_bytes", "gift_prepare_factor",
     "gift_refresh_factors", "gift_refresh_group_workspace_bytes", "gift_build_hash",
     "gift_dequant_accumulate", "gift_unwhiten_f32", "gift_block_factor_pack_bytes",
-    "gift_whiten_quantize_static", "gift_static_scratch_bytes",
+    "gift_whiten_quantize_static", "gift_static_scratch_bytes", "gift_factor_pack_bytes_rank",
 )
 
 
@@ -101,6 +115,7 @@ def load():
         "gift_unwhiten_f32": (I, [LP, I, P, SZ, P]),
         "gift_draw_sketch": (I, [P, I64, I, U64, P]),
         "gift_factor_pack_bytes": (SZ, [I64]),
+        "gift_factor_pack_bytes_rank": (SZ, [I64, I]),
         "gift_block_factor_pack_bytes": (SZ, [I64, I]),
         "gift_prepare_factor": (I, [ctypes.POINTER(_Factor), P]),
         "gift_refresh_factors": (I, [ctypes.POINTER(_RefreshInput), I, F, I, I, I, P, P, SZ, P]),
@@ -156,12 +171,12 @@ def _dev(t, dtype, shape, name):
 # --------------------------------------------------------------------------
 
 class Factor:
-    """Device buffers of one factor: U (d_in x 32), theta (32), coef, and (by
-    default, when d_in % 32 == 0) the operand packs of U.  rank (1..32) is
-    the effective rank the refresh keeps; the storage stays 32 columns wide,
-    zero from rank on.  block=32 or 64 makes a block-diagonal factor
-    (block-A-b): U is d_in x 2*block ([S_i | S_i^-1] per block row), theta
-    d_in floats, packs always present.
+    """Device buffers of one factor: U (d_in x C), theta (C), coef (8 + 2 C),
+    and (by default, when d_in % 32 == 0) the operand packs of U.  rank
+    (1..64) is the effective rank the refresh keeps; the storage is C = 32
+    columns up to rank 32 and C = 64 above, zero from rank on.  block=32 or
+    64 makes a block-diagonal factor (block-A-b): U is d_in x 2*block
+    ([S_i | S_i^-1] per block row), theta d_in floats, packs always present.
 
     A factor built from given U / coef values has stale packs until
     gift_prepare_factor(factor) runs; gift_refresh_factor(s) rewrite them.
@@ -173,15 +188,17 @@ class Factor:
         self.d_in = int(d_in)
         self.block = int(block)
         self.rank = 0 if self.block else int(rank)
-        ucols = 2 * self.block if self.block else RANK
-        nth = self.d_in if self.block else RANK
+        self.cols = 0 if self.block else factor_cols(self.rank)
+        ucols = 2 * self.block if self.block else self.cols
+        nth = self.d_in if self.block else self.cols
+        ncoef = COEF_COUNT if self.block else 8 + 2 * self.cols
         device = U.device if U is not None else device
         self.U = U if U is not None else torch.zeros(d_in, ucols, device=device)
         self.theta = theta if theta is not None else torch.zeros(nth, device=device)
-        self.coef = coef if coef is not None else torch.zeros(COEF_COUNT, device=device)
+        self.coef = coef if coef is not None else torch.zeros(ncoef, device=device)
         _dev(self.U, torch.float32, (d_in, ucols), "U")
         _dev(self.theta, torch.float32, (nth,), "theta")
-        _dev(self.coef, torch.float32, (COEF_COUNT,), "coef")
+        _dev(self.coef, torch.float32, (ncoef,), "coef")
         self.packs = None
         if self.block:
             nb = int(load().gift_block_factor_pack_bytes(self.d_in, self.block))
@@ -189,7 +206,7 @@ class Factor:
                 raise ValueError("block factor needs block 32 or 64 dividing d_in")
             self.packs = torch.empty(nb, dtype=torch.uint8, device=self.U.device)
         elif packs and self.d_in % 32 == 0:
-            nb = int(load().gift_factor_pack_bytes(self.d_in))
+            nb = int(load().gift_factor_pack_bytes_rank(self.d_in, self.rank))
             self.packs = torch.empty(nb, dtype=torch.uint8, device=self.U.device)
         self._struct = _Factor(self.d_in, self.rank, self.U.data_ptr(), self.theta.data_ptr(),
                                self.coef.data_ptr(),
@@ -212,11 +229,11 @@ class Factor:
 
     @property
     def d_w(self):
-        return self.coef[COEF_DW:COEF_DW + RANK]
+        return self.coef[COEF_DW:COEF_DW + self.cols]
 
     @property
     def d_u(self):
-        return self.coef[COEF_DU:COEF_DU + RANK]
+        return self.coef[COEF_DW + self.cols:COEF_DW + 2 * self.cols]
 
 
 class Layer:
@@ -304,7 +321,7 @@ def gift_group_workspace_bytes(op, layers, scaling=SCALE_TENSOR):
     return int(load().gift_group_workspace_bytes(op, arr, len(layers), scaling))
 
 
-def gift_refresh_workspace_bytes(d_in, n_tokens, x_dtype=DTYPE_BF16, sketch_width=MAX_SKETCH):
+def gift_refresh_workspace_bytes(d_in, n_tokens, x_dtype=DTYPE_BF16, sketch_width=SKETCH_WIDTH):
     return int(load().gift_refresh_workspace_bytes(d_in, n_tokens, x_dtype, sketch_width))
 
 
@@ -462,17 +479,26 @@ def _refresh_array(items):
     return arr
 
 
-def gift_refresh_group_workspace_bytes(items, sketch_width=MAX_SKETCH):
+def _width(items, sketch_width):
+    if sketch_width is not None:
+        return sketch_width
+    return sketch_width_for(max(it["factor"].rank for it in items))
+
+
+def gift_refresh_group_workspace_bytes(items, sketch_width=None):
+    sketch_width = _width(items, sketch_width)
     arr = _refresh_array(items)
     return int(load().gift_refresh_group_workspace_bytes(arr, len(items), sketch_width))
 
 
 def gift_refresh_factors(items, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,
-                         sketch_width=MAX_SKETCH, power_steps=4, flags=None, ws=None,
+                         sketch_width=None, power_steps=4, flags=None, ws=None,
                          stream=None):
     """items: list of dicts {X, factor, [sketch], [A_out], [seed]}; flags: optional
-    device int32 word that collects GIFT_FLAG_NONFINITE."""
+    device int32 word that collects GIFT_FLAG_NONFINITE; sketch_width None:
+    sketch_width_for the largest rank of the call."""
     lib = load()
+    sketch_width = _width(items, sketch_width)
     for it in items:
         _dev(it.get("sketch"), torch.float32, (it["factor"].d_in, sketch_width), "sketch")
         _dev(it.get("A_out"), torch.float32, (it["factor"].d_in, it["factor"].d_in), "A_out")
@@ -485,7 +511,7 @@ def gift_refresh_factors(items, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL
 
 
 def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_TAIL,
-                        sketch_width=MAX_SKETCH, power_steps=4, seed=0, sketch=None,
+                        sketch_width=None, power_steps=4, seed=0, sketch=None,
                         A_out=None, flags=None, ws=None, stream=None):
     lib = load()
     if X.dtype == torch.bfloat16:
@@ -495,6 +521,8 @@ def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_T
     else:
         raise ValueError("X must be bf16 or fp32")
     n_tokens, d_in = X.shape
+    if sketch_width is None:
+        sketch_width = sketch_width_for(factor.rank) if not factor.block else SKETCH_WIDTH
     if d_in != factor.d_in:
         raise ValueError("X width %d != factor d_in %d" % (d_in, factor.d_in))
     _dev(X, X.dtype, None, "X")
@@ -509,7 +537,7 @@ def gift_refresh_factor(X, factor, damp_eps=1e-3, damping_mode=DAMP_FLOOR_PLUS_T
                                    _stream(stream)))
 
 
-def gift_draw_sketch(d_in, width=MAX_SKETCH, seed=0, out=None, device="cuda", stream=None):
+def gift_draw_sketch(d_in, width=SKETCH_WIDTH, seed=0, out=None, device="cuda", stream=None):
     """-> device fp32 (d_in, width) Gaussian sketch (Philox4x32-10 + Box-Muller)."""
     if out is None:
         out = torch.empty(d_in, width, dtype=torch.float32, device=device)

@@ -13,13 +13,14 @@
 namespace gift {
 // roundtrip.hip, built with 64-row tiles (rt4) and 32-row tiles (rt2)
 #define GIFT_TILE_DECLS                                                                          \
-  hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s); \
+  hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s,  \
+                                    int rb);                                                     \
   hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool write_w,         \
                                   hipStream_t s);                                                \
-  hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s);           \
+  hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s, int rb);   \
   hipError_t launch_error(const GroupDev& g, int out_base, hipStream_t s);                       \
   hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStream_t s);        \
-  hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s);                              \
+  hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s, int rb);                      \
   hipError_t launch_pack(const PackGroup& pg, hipStream_t s);                                    \
   hipError_t launch_blk_pack(const PackGroup& pg, int b, hipStream_t s);                         \
   hipError_t launch_blk_whiten(const GroupDev& g, int b, int scaling, bool write_w,              \
@@ -58,9 +59,10 @@ struct TileOps {
   int64_t (*row_blocks)(int64_t d_out);
   int (*frag_floats)();
   int (*cop_bytes)();
-  hipError_t (*whiten_quantize)(const GroupDev& g, int scaling, bool write_w, hipStream_t s);
-  hipError_t (*dequant)(const GroupDev& g, int scaling, bool white, hipStream_t s);
-  hipError_t (*unwhiten_f32)(const GroupDev& g, hipStream_t s);
+  hipError_t (*whiten_quantize)(const GroupDev& g, int scaling, bool write_w, hipStream_t s,
+                                int rb);
+  hipError_t (*dequant)(const GroupDev& g, int scaling, bool white, hipStream_t s, int rb);
+  hipError_t (*unwhiten_f32)(const GroupDev& g, hipStream_t s, int rb);
   hipError_t (*blk_whiten)(const GroupDev& g, int b, int scaling, bool write_w, hipStream_t s);
   hipError_t (*blk_dequant)(const GroupDev& g, int b, int scaling, hipStream_t s);
 };
@@ -124,6 +126,11 @@ bool whitened(const gift_layer& L, Op op) {
 // block size of a layer's factor: 0 for the rank-r factor (or no factor)
 int fblock(const gift_layer& L) { return L.factor ? L.factor->block : 0; }
 
+// rank blocks (32 columns each) of a layer's rank-r factor: 1 or 2
+int frb(const gift_layer& L) {
+  return L.factor && !L.factor->block ? factor_cols(L.factor->rank) / kRank : 1;
+}
+
 // Per-layer workspace needs of one grouped op.
 struct LayerWs {
   size_t cbuf = 0, cfin = 0, part = 0, part2 = 0, amax = 0;
@@ -162,8 +169,8 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
           w.amax = sizeof(uint32_t);
         }
       } else if (L.factor) {
-        w.cbuf = (size_t)col_groups(L.d_in) * frag;  // partial c per column group
-        w.cfin = cop;                                  // c' of every row (operand form)
+        w.cbuf = (size_t)col_groups(L.d_in) * frag * frb(L);  // partial c per column group
+        w.cfin = cop * frb(L);                                 // c' of every row (operand form)
         if (!block) {  // one amax per tile, the layer amax
           w.part = (size_t)row_tiles_max(L) * sizeof(uint32_t);
           w.amax = sizeof(uint32_t);
@@ -182,8 +189,8 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
     case Op::Dequant:
     case Op::UnwhitenF32:
       if (L.factor && !L.factor->block) {
-        w.cbuf = (size_t)col_groups(L.d_in) * frag;
-        w.cfin = cop;
+        w.cbuf = (size_t)col_groups(L.d_in) * frag * frb(L);
+        w.cfin = cop * frb(L);
       }
       break;
     case Op::Error:
@@ -200,6 +207,7 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
 struct Packs {
   std::vector<const float*> U;
   std::vector<int> d_in;
+  std::vector<int> cols;   // storage columns of U (32 or 64)
   std::vector<size_t> off;
   size_t bytes = 0;
   size_t find(const float* u) const {
@@ -217,10 +225,12 @@ Packs plan_packs(const gift_layer* layers, int n, Op op) {
     bool seen = false;
     for (const float* v : p.U) seen |= v == u;
     if (seen) continue;
+    const int cols = factor_cols(layers[i].factor->rank);
     p.U.push_back(u);
     p.d_in.push_back((int)layers[i].d_in);
+    p.cols.push_back(cols);
     p.off.push_back(p.bytes);
-    p.bytes += align_up(pack_bytes(layers[i].d_in));
+    p.bytes += align_up(pack_bytes(layers[i].d_in) * (cols / kRank));
   }
   return p;
 }
@@ -231,20 +241,38 @@ size_t group_ws(const gift_layer* layers, int n, Op op, bool block) {
   return t;
 }
 
-gift_status run_packs(const Packs& p, void* ws, hipStream_t st) {
+// One pack launch entry per rank block: U's block b starts at column 32 b,
+// its packs at b * pack_bytes(d_in).
+gift_status launch_factor_packs(const std::vector<PackDev>& blocks, hipStream_t st) {
   PackGroup pg{};
-  for (size_t i = 0; i < p.U.size(); ++i) {
-    PackDev& d = pg.f[pg.n++];
-    d.U = p.U[i];
-    d.P = reinterpret_cast<uint4*>((char*)ws + p.off[i]);
-    d.d_in = p.d_in[i];
-    if (pg.n == kMaxGroup || i + 1 == p.U.size()) {
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    pg.f[pg.n++] = blocks[i];
+    if (pg.n == kMaxGroup || i + 1 == blocks.size()) {
       hipError_t e = launch_pack(pg, st);
       if (e != hipSuccess) return hip_fail(e, "pack launch");
       pg.n = 0;
     }
   }
   return GIFT_OK;
+}
+
+void add_pack_blocks(std::vector<PackDev>& out, const float* U, uint4* P, int d_in, int cols) {
+  for (int b = 0; b < cols / kRank; ++b) {
+    PackDev d{};
+    d.U = U + kRank * b;
+    d.P = P + b * pack_bytes(d_in) / sizeof(uint4);
+    d.d_in = d_in;
+    d.ucols = cols;
+    out.push_back(d);
+  }
+}
+
+gift_status run_packs(const Packs& p, void* ws, hipStream_t st) {
+  std::vector<PackDev> blocks;
+  for (size_t i = 0; i < p.U.size(); ++i)
+    add_pack_blocks(blocks, p.U[i], reinterpret_cast<uint4*>((char*)ws + p.off[i]), p.d_in[i],
+                    p.cols[i]);
+  return launch_factor_packs(blocks, st);
 }
 
 gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
@@ -292,8 +320,9 @@ gift_status check_layers(const gift_layer* layers, int n, Op op, int scaling) {
       }
     } else if (whitened(L, op)) {
       const gift_factor& f = *L.factor;
-      if (f.rank < 1 || f.rank > kRank)
-        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor rank %d not in [1, %d]", i, f.rank, kRank);
+      if (f.rank < 1 || f.rank > kMaxRank)
+        return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "layer %d: factor rank %d not in [1, %d]", i, f.rank,
+                    kMaxRank);
       if (f.d_in != L.d_in)
         return fail(GIFT_ERR_INVALID_ARG, "layer %d: factor d_in %d != layer d_in %lld", i,
                     f.d_in, (long long)L.d_in);
@@ -320,7 +349,7 @@ constexpr int64_t kSmallGroupElems = int64_t(1) << 25;
 constexpr int64_t kSlabMinElems = int64_t(1) << 22;
 
 bool slab_layer(const gift_layer& L, int scaling) {
-  return L.factor && !L.factor->block && scaling == GIFT_SCALE_TENSOR &&
+  return L.factor && !L.factor->block && L.factor->rank <= kRank && scaling == GIFT_SCALE_TENSOR &&
          L.d_out * L.d_in >= kSlabMinElems;
 }
 
@@ -495,23 +524,26 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
   s = run_packs(plan_packs(layers, n_layers, Op::Whiten), ws, st);
   if (s != GIFT_OK) return s;
   const TileOps& geo = tile_ops(layers, n_layers, Op::Whiten);
-  // groups: rank-r factors on tiles, Euclidean layers, block factors of 32,
-  // of 64, rank-r factors as slabs
-  for (int wgrp = 0; wgrp < 5; ++wgrp) {
+  // groups: rank-r factors of one rank block on tiles, Euclidean layers,
+  // block factors of 32, of 64, rank-r factors as slabs, rank-r factors of
+  // two rank blocks on tiles
+  for (int wgrp = 0; wgrp < 6; ++wgrp) {
     auto pick = [&](const gift_layer& L) {
-      return wgrp == 0 ? L.factor != nullptr && !L.factor->block && !slab_layer(L, scaling)
+      const bool rankr = L.factor != nullptr && !L.factor->block;
+      return wgrp == 0 ? rankr && frb(L) == 1 && !slab_layer(L, scaling)
            : wgrp == 1 ? L.factor == nullptr
            : wgrp == 4 ? slab_layer(L, scaling)
+           : wgrp == 5 ? rankr && frb(L) == 2
                        : fblock(L) == (wgrp == 2 ? 32 : 64);
     };
     bool any_w = false;
     for (int i = 0; i < n_layers; ++i)
       if (pick(layers[i]) && layers[i].W_out) any_w = true;
     auto tiles_rows = [&](const gift_layer& L) { return row_tiles(L, geo); };
-    if (wgrp == 0)
+    if (wgrp == 0 || wgrp == 5)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {
-                        return geo.whiten_quantize(g, scaling, any_w, st);
+                        return geo.whiten_quantize(g, scaling, any_w, st, wgrp == 5 ? 2 : 1);
                       }, geo);
     else if (wgrp == 1)
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
@@ -563,17 +595,22 @@ gift_status gift_dequant_unwhiten(const gift_layer* layers, int n_layers, int sc
   s = run_packs(plan_packs(layers, n_layers, Op::Dequant), ws, st);
   if (s != GIFT_OK) return s;
   const TileOps& geo = tile_ops(layers, n_layers, Op::Dequant);
-  for (int wgrp = 0; wgrp < 4; ++wgrp) {
+  // groups: rank-r factors of one rank block, Euclidean layers, block
+  // factors of 32, of 64, rank-r factors of two rank blocks
+  for (int wgrp = 0; wgrp < 5; ++wgrp) {
     auto pick = [&](const gift_layer& L) {
-      return wgrp == 0 ? L.factor != nullptr && !L.factor->block
+      const bool rankr = L.factor != nullptr && !L.factor->block;
+      return wgrp == 0 ? rankr && frb(L) == 1
            : wgrp == 1 ? L.factor == nullptr
+           : wgrp == 4 ? rankr && frb(L) == 2
                        : fblock(L) == (wgrp == 2 ? 32 : 64);
     };
     auto tiles = [&](const gift_layer& L) { return wgrp == 1 ? tiles_flat(L) : row_tiles(L, geo); };
     s = run_grouped(layers, n_layers, Op::Dequant, block, ws, nullptr, nullptr, pick, tiles,
                     [&](const GroupDev& g, int) {
-                      if (wgrp >= 2) return geo.blk_dequant(g, wgrp == 2 ? 32 : 64, scaling, st);
-                      return geo.dequant(g, scaling, wgrp == 0, st);
+                      if (wgrp == 2 || wgrp == 3)
+                        return geo.blk_dequant(g, wgrp == 2 ? 32 : 64, scaling, st);
+                      return geo.dequant(g, scaling, wgrp != 1, st, wgrp == 4 ? 2 : 1);
                     }, geo);
     if (s != GIFT_OK) return s;
   }
@@ -633,11 +670,15 @@ gift_status gift_unwhiten_f32(const gift_layer* layers, int n_layers, void* ws, 
   hipStream_t st = (hipStream_t)stream;
   s = run_packs(plan_packs(layers, n_layers, Op::UnwhitenF32), ws, st);
   if (s != GIFT_OK) return s;
-  auto pick = [](const gift_layer& L) { return L.factor != nullptr; };
   const TileOps& geo = tile_ops(layers, n_layers, Op::UnwhitenF32);
   auto tiles = [&](const gift_layer& L) { return row_tiles(L, geo); };
-  return run_grouped(layers, n_layers, Op::UnwhitenF32, true, ws, nullptr, nullptr, pick, tiles,
-                     [&](const GroupDev& g, int) { return geo.unwhiten_f32(g, st); }, geo);
+  for (int rb = 1; rb <= 2; ++rb) {
+    auto pick = [&](const gift_layer& L) { return L.factor != nullptr && frb(L) == rb; };
+    s = run_grouped(layers, n_layers, Op::UnwhitenF32, true, ws, nullptr, nullptr, pick, tiles,
+                    [&](const GroupDev& g, int) { return geo.unwhiten_f32(g, st, rb); }, geo);
+    if (s != GIFT_OK) return s;
+  }
+  return GIFT_OK;
 }
 
 size_t gift_refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype,
@@ -656,6 +697,11 @@ gift_status gift_refresh_factor(const void* X, int x_dtype, int64_t n_tokens,
 }
 
 size_t gift_factor_pack_bytes(int64_t d_in) { return d_in > 0 ? pack_bytes(d_in) : 0; }
+
+size_t gift_factor_pack_bytes_rank(int64_t d_in, int rank) {
+  if (d_in <= 0 || rank < 1 || rank > kMaxRank) return 0;
+  return pack_bytes(d_in) * (factor_cols(rank) / kRank);
+}
 
 size_t gift_block_factor_pack_bytes(int64_t d_in, int block) {
   if ((block != 32 && block != 64) || d_in < block || d_in % block) return 0;
@@ -679,17 +725,13 @@ gift_status gift_prepare_factor(const gift_factor* f, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "pack launch");
     return GIFT_OK;
   }
-  if (f->rank < 1 || f->rank > kRank) return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be in [1, 32]");
+  if (f->rank < 1 || f->rank > kMaxRank)
+    return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "rank must be in [1, 64]");
   if (f->d_in < 64 || f->d_in % 32 || f->d_in > kMaxDim)
     return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "d_in must be >= 64 and a multiple of 32");
-  PackGroup pg{};
-  pg.n = 1;
-  pg.f[0].U = f->U;
-  pg.f[0].P = static_cast<uint4*>(f->packs);
-  pg.f[0].d_in = f->d_in;
-  hipError_t e = launch_pack(pg, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "pack launch");
-  return GIFT_OK;
+  std::vector<PackDev> blocks;
+  add_pack_blocks(blocks, f->U, static_cast<uint4*>(f->packs), f->d_in, factor_cols(f->rank));
+  return launch_factor_packs(blocks, (hipStream_t)stream);
 }
 
 gift_status gift_refresh_factors(const gift_refresh_input* inputs, int n, float damp_eps,

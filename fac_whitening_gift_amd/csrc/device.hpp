@@ -9,7 +9,11 @@
 
 namespace gift {
 
-constexpr int kRank = GIFT_RANK;
+constexpr int kRank = GIFT_RANK;          // columns of one rank block
+constexpr int kMaxRank = GIFT_MAX_RANK;   // largest factor rank (two rank blocks)
+
+// storage columns of a rank-r factor: one rank block up to rank 32, else two
+__host__ __device__ __forceinline__ int factor_cols(int rank) { return rank > kRank ? 2 * kRank : kRank; }
 constexpr int kBlock = GIFT_BLOCK;
 constexpr int kMaxGroup = 16;          // layers per grouped launch
 constexpr float kE4M3Max = 448.0f;     // largest finite OCP E4M3 magnitude
@@ -295,10 +299,13 @@ struct GroupDev {
 };
 
 // One factor to pack: U (d_in x 32 fp32) -> P (bf16x3 operand packs).
+// One rank block (32 columns) of a factor to pack: U points at the block's
+// first column of a d_in x ucols matrix (ucols 32 or 64).
 struct PackDev {
   const float* U;
   uint4* P;
   int d_in;
+  int ucols;
 };
 struct PackGroup {
   int n;

@@ -694,7 +694,7 @@ constexpr int64_t kGemmRowTileMin = 2048;
 //     pipeline runs four times as long.  grid: (max d / 64, kYSplit, inputs).
 // The second needs a quarter of the workgroups, so it is taken only when a
 // call has enough rows to fill the machine with it.
-template <bool kRowTiles, class G>
+template <bool kRowTiles, int kWT, class G>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
@@ -704,9 +704,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   const float* __restrict__ A = R.A;
   const int r16 = lane & 15, gq = lane >> 4;
   const int ntile = w / 16;
-  f32x4 acc[kW / 16];
+  f32x4 acc[kWT];
 #pragma unroll
-  for (int t = 0; t < kW / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < kWT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int kchunks = (d + 31) / 32;
   const int slices = kRowTiles ? kYSplit : kYSplit * kGemmWaves;
   const int slice = kRowTiles ? blockIdx.y : blockIdx.y * kGemmWaves + wave;
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   // one K chunk of 32: this lane's 8 values of A's row and its packs of Q
   struct Chunk {
     float4 a[2];
-    uint4 q[kW / 16][3];
+    uint4 q[kWT][3];
   };
   auto load = [&](int kc, Chunk& c) {
     const int k0 = 32 * kc + 8 * gq;
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
     c.a[0] = in ? *reinterpret_cast<const float4*>(arow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
     c.a[1] = in ? *reinterpret_cast<const float4*>(arow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int t = 0; t < kW / 16; ++t)
+    for (int t = 0; t < kWT; ++t)
 #pragma unroll
       for (int s = 0; s < 3; ++s)
         c.q[t][s] = t < ntile ? R.QP[(size_t)((kc * ntile + t) * 3 + s) * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
     bf16x8 sa[3];
     split3(v, sa);
 #pragma unroll
-    for (int t = 0; t < kW / 16; ++t)
+    for (int t = 0; t < kWT; ++t)
       if (t < ntile) {
         const bf16x8 sb[3] = {as_bf16x8(c.q[t][0]), as_bf16x8(c.q[t][1]), as_bf16x8(c.q[t][2])};
         acc[t] = mfma3x3(sa, sb, acc[t]);
@@ -758,14 +758,14 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   float* __restrict__ Yp = R.Yp + (size_t)blockIdx.y * d * w;
   if constexpr (kRowTiles) {
 #pragma unroll
-    for (int t = 0; t < kW / 16; ++t)
+    for (int t = 0; t < kWT; ++t)
       if (t < ntile)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Yp[(int64_t)(row0 + 4 * gq + i) * w + 16 * t + r16] = acc[t][i];
   } else {
-    __shared__ float red[kGemmWaves][16][kW];
+    __shared__ float red[kGemmWaves][16][16 * kWT];
 #pragma unroll
-    for (int t = 0; t < kW / 16; ++t)
+    for (int t = 0; t < kWT; ++t)
       if (t < ntile)
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[wave][4 * gq + i][16 * t + r16] = acc[t][i];
@@ -781,16 +781,23 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
 }
 
 // Y = A Q for every input of a chain, in the workgroup shape its size suits
-template <class G>
-void gemm_aq(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
+// (kWT: 16-column tiles of Q the accumulators hold, 4 up to width 64, else 6)
+template <int kWT, class G>
+void gemm_aq_w(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
   int64_t tiles = 0;
   for (int i = 0; i < nc; ++i) tiles += (hd[i].d + 16 * kGemmWaves - 1) / (16 * kGemmWaves);
   if (tiles * kYSplit >= kGemmRowTileMin) {
     const dim3 grid((maxd + 16 * kGemmWaves - 1) / (16 * kGemmWaves), kYSplit, nc);
-    k_gemm_aq<true><<<grid, 64 * kGemmWaves, 0, st>>>(g);
+    k_gemm_aq<true, kWT><<<grid, 64 * kGemmWaves, 0, st>>>(g);
   } else {
-    k_gemm_aq<false><<<dim3(maxd / 16, kYSplit, nc), 64 * kGemmWaves, 0, st>>>(g);
+    k_gemm_aq<false, kWT><<<dim3(maxd / 16, kYSplit, nc), 64 * kGemmWaves, 0, st>>>(g);
   }
+}
+
+template <class G>
+void gemm_aq(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
+  if (g.w <= 64) gemm_aq_w<4>(g, hd, nc, maxd, st);
+  else gemm_aq_w<kW / 16>(g, hd, nc, maxd, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -802,14 +809,16 @@ void gemm_aq(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
 // Y comes as the kYSplit partial products of k_gemm_aq, summed here in split
 // order as rows are staged; the two diagonal blocks (Y's two column halves)
 // write the sum to Y for k_apply.
-// grid: (kGramParts * 4, inputs).  which: 0 = Y^T Y, 1 = Q1^T Q1, 2 = Q^T Y
+// grid: (kGramParts * nb * nb, inputs), nb = ceil(w / 32) blocks of 32 per
+// side.  which: 0 = Y^T Y, 1 = Q1^T Q1, 2 = Q^T Y
 // ---------------------------------------------------------------------------
 template <class G>
 __global__ __launch_bounds__(kT) void k_gram(G g, int which) {
   const RIn& R = g.r[blockIdx.y];
   const int d = R.d, w = g.w;
-  const int part = blockIdx.x >> 2, blk = blockIdx.x & 3;
-  const int a0 = (blk >> 1) * 32, b0 = (blk & 1) * 32;
+  const int nb = (w + 31) / 32;
+  const int part = blockIdx.x / (nb * nb), blk = blockIdx.x % (nb * nb);
+  const int a0 = (blk / nb) * 32, b0 = (blk % nb) * 32;
   if (a0 >= w || b0 >= w) return;
   const bool py = which == 0, sy = which != 1;  // operand from the Y partials
   const float* __restrict__ P = py ? R.Yp : which == 1 ? R.Q1 : R.Q;
@@ -880,8 +889,8 @@ __global__ __launch_bounds__(kT) void k_gram(G g, int which) {
 }
 
 // The small dense kernels below run one 1024-thread workgroup per input on a
-// W x W fp64 matrix in LDS (W = sketch width 32, 48 or 64, a compile-time
-// constant so no index needs a runtime division).
+// W x W fp64 matrix in LDS (W = sketch width 32, 48, 64, 80 or 96, a
+// compile-time constant so no index needs a runtime division).
 constexpr int kST = 1024;
 
 // fixed-order reduction of the Gram partials into LDS (W x W, fp64)
@@ -977,12 +986,14 @@ __global__ __launch_bounds__(kCholT) void k_chol(G g) {
   // Gram entries: fixed-order sum of the partials, every load of a thread in
   // flight at once (entries of the packed upper triangle, row i starting at
   // i (2W + 1 - i) / 2, dealt round-robin to the threads)
-  {
-    constexpr int kN = W * (W + 1) / 2, kE = (kN + kCholT - 1) / kCholT;
+  // (in batches of kB entries per thread above width 64, to bound registers)
+  constexpr int kN = W * (W + 1) / 2, kEall = (kN + kCholT - 1) / kCholT;
+  constexpr int kE = W <= 64 ? kEall : 2;
+  for (int r0 = 0; r0 < kEall; r0 += kE) {
     int ei[kE], ej[kE];
 #pragma unroll
     for (int r = 0; r < kE; ++r) {
-      int e = threadIdx.x + r * kCholT;
+      int e = threadIdx.x + (r0 + r) * kCholT;
       const bool none = e >= kN;
       if (none) e = kN - 1;
       const float b = 2.f * W + 1.f;
@@ -1012,7 +1023,7 @@ __global__ __launch_bounds__(kCholT) void k_chol(G g) {
   // largest diagonal entry (wave 0, which takes the pivots)
   double dmax = 0.0;
   if (wave == 0) {
-    dmax = lane < W ? A[lane][lane] : 0.0;
+    for (int i = lane; i < W; i += 64) dmax = fmax(dmax, A[i][i]);
     for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
   }
   for (int k0 = 0; k0 < W; k0 += kP) {
@@ -1084,17 +1095,17 @@ __global__ __launch_bounds__(kCholT) void k_chol(G g) {
 
 // 4d. Out = In T (fp64 accumulate), Out[i][c] for c < ncols.
 // grid: (max d / 16, inputs).  which: 0 = Q1 = Y T, 1 = Q = Q1 T, 2 = Q = Y T,
-// 3 = U = Q T[:, :32]
-template <class G>
+// 3 = U = Q T[:, :cols] (the factor's 32 or 64 storage columns)
+template <int W, class G>
 __global__ __launch_bounds__(kT) void k_apply(G g, int which) {
   const RIn& R = g.r[blockIdx.y];
-  const int d = R.d, w = g.w;
+  const int d = R.d, w = W;
   if ((int)blockIdx.x * 16 >= d) return;
   const float* __restrict__ In = which == 0 || which == 2 ? R.Y : which == 1 ? R.Q1 : R.Q;
   float* __restrict__ Out = which == 0 ? R.Q1 : which == 3 ? R.U : R.Q;
-  const int ncols = which == 3 ? kRank : w;
-  __shared__ double sT[kW][kW];
-  __shared__ float sIn[16][kW];
+  const int ncols = which == 3 ? factor_cols(R.rank) : w;
+  __shared__ double sT[W][W];
+  __shared__ float sIn[16][W];
   for (int e = threadIdx.x; e < w * ncols; e += kT) sT[e / ncols][e % ncols] = R.T[(e / ncols) * kW + e % ncols];
   const int i0 = blockIdx.x * 16;
   for (int e = threadIdx.x; e < 16 * w; e += kT) sIn[e / w][e % w] = In[(int64_t)(i0 + e / w) * w + e % w];
@@ -1241,24 +1252,46 @@ __global__ __launch_bounds__(kT) void k_solve(G g, int which) {
   double acc[kM];
 #pragma unroll
   for (int m = 0; m < kM; ++m) acc[m] = in[4 * m + p];
-#pragma unroll
-  for (int j = 0; j < W; ++j) {
-    const int mj = j >> 2;
-    // the owner (p == j % 4) finishes q_j; every lane of the quad gets it
-    const double mine = acc[mj] * sR[j][j];
-    double qj;
+  // the owner (p == j % 4) finishes q_j; every lane of the quad gets it
+  auto bcast = [&](int j, double mine) {
     switch (j & 3) {
-      case 0: qj = quad_bcast<0>(mine); break;
-      case 1: qj = quad_bcast<1>(mine); break;
-      case 2: qj = quad_bcast<2>(mine); break;
-      default: qj = quad_bcast<3>(mine); break;
+      case 0: return quad_bcast<0>(mine);
+      case 1: return quad_bcast<1>(mine);
+      case 2: return quad_bcast<2>(mine);
+      default: return quad_bcast<3>(mine);
     }
-    if (p == (j & 3)) acc[mj] = qj;
+  };
+  if constexpr (W <= 64) {
 #pragma unroll
-    for (int m = mj; m < kM; ++m) {
-      const int col = 4 * m + p;
-      const double nv = acc[m] - qj * sR[j][col];
-      acc[m] = col > j ? nv : acc[m];
+    for (int j = 0; j < W; ++j) {
+      const int mj = j >> 2;
+      const double qj = bcast(j, acc[mj] * sR[j][j]);
+      if (p == (j & 3)) acc[mj] = qj;
+#pragma unroll
+      for (int m = mj; m < kM; ++m) {
+        const int col = 4 * m + p;
+        const double nv = acc[m] - qj * sR[j][col];
+        acc[m] = col > j ? nv : acc[m];
+      }
+    }
+  } else {
+    // wider bases: the step loop stays rolled (a fully unrolled one does not
+    // fit the register file); every register index is still a constant and
+    // the same updates run in the same order
+    for (int j = 0; j < W; ++j) {
+      const int mj = j >> 2;
+      double am = 0.0;
+#pragma unroll
+      for (int m = 0; m < kM; ++m) am = m == mj ? acc[m] : am;
+      const double qj = bcast(j, am * sR[j][j]);
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        if (m < mj) continue;
+        if (m == mj && p == (j & 3)) acc[m] = qj;
+        const int col = 4 * m + p;
+        const double nv = acc[m] - qj * sR[j][col];
+        acc[m] = col > j ? nv : acc[m];
+      }
     }
   }
   if (i < d)
@@ -1312,10 +1345,11 @@ __global__ __launch_bounds__(kST) void k_ritz(G g) {
     order[rank] = i;
   }
   __syncthreads();
-  // T[:, k] = V[:, order[k]] for the top rank r (zero columns after it)
-  const int rk = Rin.rank;
-  for (int e = threadIdx.x; e < W * kRank; e += kST) {
-    const int r = e / kRank, k = e % kRank;
+  // T[:, k] = V[:, order[k]] for the top rank r (zero columns after it, up
+  // to the factor's 32 or 64 storage columns)
+  const int rk = Rin.rank, cols = factor_cols(rk);
+  for (int e = threadIdx.x; e < W * cols; e += kST) {
+    const int r = e / cols, k = e % cols;
     Rin.T[r * kW + k] = k < rk ? V[r][order[k]] : 0.0;
   }
   // damping from the top r Ritz values: lambda_floor, plus the mean of the
@@ -1338,12 +1372,13 @@ __global__ __launch_bounds__(kST) void k_ritz(G g) {
     coef[6] = 0.f;
     coef[7] = 0.f;
   }
-  if (threadIdx.x < kRank) {
+  if (threadIdx.x < cols) {
     const int k = threadIdx.x;
     const double th = k < rk ? fmax(ev[order[k]], 0.0) : 0.0, s = sqrt(th + lam);
-    // (th+lam)^-1/2 - lam^-1/2 and (th+lam)^1/2 - lam^1/2 without cancellation
+    // (th+lam)^-1/2 - lam^-1/2 and (th+lam)^1/2 - lam^1/2 without cancellation;
+    // D_w at 8, D_u at 8 + cols
     Rin.coef[GIFT_COEF_DW + k] = (float)(-th / (s * s0 * (s + s0)));
-    Rin.coef[GIFT_COEF_DU + k] = (float)(th / (s + s0));
+    Rin.coef[GIFT_COEF_DW + cols + k] = (float)(th / (s + s0));
     Rin.theta[k] = (float)th;
   }
 }
@@ -1430,7 +1465,9 @@ template <class G>
 void chol(const G& g, int nb, hipStream_t st) {
   if (g.w == 32) k_chol<32><<<nb, kCholT, 0, st>>>(g);
   else if (g.w == 48) k_chol<48><<<nb, kCholT, 0, st>>>(g);
-  else k_chol<64><<<nb, kCholT, 0, st>>>(g);
+  else if (g.w == 64) k_chol<64><<<nb, kCholT, 0, st>>>(g);
+  else if (g.w == 80) k_chol<80><<<nb, kCholT, 0, st>>>(g);
+  else k_chol<96><<<nb, kCholT, 0, st>>>(g);
 }
 
 template <class G>
@@ -1444,14 +1481,27 @@ void solve(const G& g, int which, int maxd, int nb, hipStream_t st) {
   const dim3 grid((unsigned)((4 * maxd + kT - 1) / kT), nb);
   if (g.w == 32) k_solve<32><<<grid, kT, 0, st>>>(g, which);
   else if (g.w == 48) k_solve<48><<<grid, kT, 0, st>>>(g, which);
-  else k_solve<64><<<grid, kT, 0, st>>>(g, which);
+  else if (g.w == 64) k_solve<64><<<grid, kT, 0, st>>>(g, which);
+  else if (g.w == 80) k_solve<80><<<grid, kT, 0, st>>>(g, which);
+  else k_solve<96><<<grid, kT, 0, st>>>(g, which);
 }
 
 template <class G>
 void ritz(const G& g, int nb, hipStream_t st) {
   if (g.w == 32) k_ritz<32><<<nb, kST, 0, st>>>(g);
   else if (g.w == 48) k_ritz<48><<<nb, kST, 0, st>>>(g);
-  else k_ritz<64><<<nb, kST, 0, st>>>(g);
+  else if (g.w == 64) k_ritz<64><<<nb, kST, 0, st>>>(g);
+  else if (g.w == 80) k_ritz<80><<<nb, kST, 0, st>>>(g);
+  else k_ritz<96><<<nb, kST, 0, st>>>(g);
+}
+
+template <class G>
+void apply(const G& g, int which, const dim3& grid, hipStream_t st) {
+  if (g.w == 32) k_apply<32><<<grid, kT, 0, st>>>(g, which);
+  else if (g.w == 48) k_apply<48><<<grid, kT, 0, st>>>(g, which);
+  else if (g.w == 64) k_apply<64><<<grid, kT, 0, st>>>(g, which);
+  else if (g.w == 80) k_apply<80><<<grid, kT, 0, st>>>(g, which);
+  else k_apply<96><<<grid, kT, 0, st>>>(g, which);
 }
 
 }  // namespace
@@ -1556,7 +1606,8 @@ gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, i
   e = hipGetLastError();
   if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
   // subspace iteration: Y = A Omega, then power_steps x (Q = orth(Y); Y = A Q)
-  const dim3 rows(maxd / 16, nc), grams(kGramParts * 4, nc);
+  const int gb = (width + 31) / 32;
+  const dim3 rows(maxd / 16, nc), grams(kGramParts * gb * gb, nc);
   pack_q(g, 0, maxd, nc, st);
   gemm_aq(g, hd, nc, maxd, st);
   for (int s = 0; s < power_steps; ++s) {
@@ -1578,25 +1629,32 @@ gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, i
   gemm_aq(g, hd, nc, maxd, st);  // Y = A Q
   k_gram<<<grams, kT, 0, st>>>(g, 2);                  // Q^T Y
   ritz(g, nc, st);
-  k_apply<<<rows, kT, 0, st>>>(g, 3);                  // U = Q V
+  apply(g, 3, rows, st);                               // U = Q V
   e = hipGetLastError();
   if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
-  // operand packs of the new U, for factors that carry them
+  // operand packs of the new U, for factors that carry them (one entry per
+  // rank block of 32 columns)
   PackGroup pg{};
+  auto flush = [&]() -> hipError_t {
+    if (!pg.n) return hipSuccess;
+    const hipError_t le = launch_pack(pg, st);
+    pg = PackGroup{};
+    return le;
+  };
   for (int i = 0; i < nc; ++i) {
     const gift_factor* f = in[i].factor;
-    if (f->packs) {
-      pg.f[pg.n].U = f->U;
-      pg.f[pg.n].P = static_cast<uint4*>(f->packs);
-      pg.f[pg.n].d_in = f->d_in;
-      ++pg.n;
-    }
-    if (pg.n == kMaxGroup || (i + 1 == nc && pg.n)) {
-      e = launch_pack(pg, st);
-      if (e != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
-      pg = PackGroup{};
+    if (!f->packs) continue;
+    const int cols = factor_cols(f->rank);
+    for (int b = 0; b < cols / kRank; ++b) {
+      if (pg.n == kMaxGroup && (e = flush()) != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
+      PackDev& pd = pg.f[pg.n++];
+      pd.U = f->U + kRank * b;
+      pd.P = static_cast<uint4*>(f->packs) + b * pack_bytes(f->d_in) / sizeof(uint4);
+      pd.d_in = f->d_in;
+      pd.ucols = cols;
     }
   }
+  if ((e = flush()) != hipSuccess) return bad(GIFT_ERR_HIP, hipGetErrorString(e));
   return GIFT_OK;
 }
 
@@ -1615,7 +1673,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     return bad(GIFT_ERR_INVALID_ARG, "unknown damping_mode");
   if (!(damp_eps >= 0.f) || !isfinite(damp_eps)) return bad(GIFT_ERR_INVALID_ARG, "bad damp_eps");
   if (width < kRank || width > kW || width % 16)
-    return bad(GIFT_ERR_UNSUPPORTED_SHAPE, "sketch_width must be 32, 48 or 64");
+    return bad(GIFT_ERR_UNSUPPORTED_SHAPE, "sketch_width must be 32, 48, 64, 80 or 96");
   if (power_steps < 0 || power_steps > 64) return bad(GIFT_ERR_INVALID_ARG, "power_steps out of range");
   for (int i = 0; i < n; ++i) {
     const gift_refresh_input& r = in[i];
@@ -1634,8 +1692,8 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "block must be 0, 32 or 64");
     if (f->block && (f->d_in % f->block || !f->packs))
       return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "a block factor needs d_in % block == 0 and packs");
-    if (!f->block && (f->rank < 1 || f->rank > kRank))
-      return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "rank must be in [1, 32]");
+    if (!f->block && (f->rank < 1 || f->rank > kMaxRank || f->rank > width))
+      return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "rank must be in [1, 64] and at most sketch_width");
     if (f->d_in < 64 || f->d_in % 16 || f->d_in > 16384)
       return bad(GIFT_ERR_UNSUPPORTED_SHAPE, at + "d_in must be in [64, 16384], % 16 == 0");
     if (f->packs && f->d_in % 32)

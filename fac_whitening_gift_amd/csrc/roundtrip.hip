@@ -66,6 +66,11 @@ constexpr int kChunk = 32;          // columns per MFMA K chunk
 //          g = l/16) = U[32c + perm(i)][16h + r16]
 //   second (U operand of w = c' U^T): element i = U[32c + 16h + r16][perm(i)]
 // with perm(i) = 16*(i/4) + 4g + i%4.
+// A factor of rank above 32 stores U with 64 columns as two rank blocks of
+// 32; its packs are the two blocks' packs one after the other (block b at
+// uint4 offset b * nch * 2 * 2 * 3 * 64), and the kernels below take the
+// number of rank blocks kRB as a template argument: one set of partial and
+// final row coefficients per block, the second product summed over blocks.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int perm8(int i, int g) { return 16 * (i >> 2) + 4 * g + (i & 3); }
 
@@ -83,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void k_pack_u(PackGroup pg) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int p = perm8(i, g);
-    v[i] = which == 0 ? F.U[(int64_t)(kChunk * c + p) * kRank + 16 * h + r16]
-                      : F.U[(int64_t)(kChunk * c + 16 * h + r16) * kRank + p];
+    v[i] = which == 0 ? F.U[(int64_t)(kChunk * c + p) * F.ucols + 16 * h + r16]
+                      : F.U[(int64_t)(kChunk * c + 16 * h + r16) * F.ucols + p];
   }
   bf16x8 s[3];
   split3(v, s);
@@ -342,8 +347,12 @@ __device__ __forceinline__ void as_ops(const uint4 (&u)[2][3], bf16x8 (&a)[2][3]
     for (int s = 0; s < 3; ++s) a[h][s] = as_bf16x8(u[h][s]);
 }
 
-__device__ __forceinline__ const uint4* p2_of(const LayerDev& L) {
-  return L.P + (size_t)(L.d_in / kChunk) * 2 * 3 * 64;
+// first-form packs of rank block b, and (p2_of) its second-form packs
+__device__ __forceinline__ const uint4* p1_of(const LayerDev& L, int b = 0) {
+  return L.P + (size_t)b * (L.d_in / kChunk) * 2 * 2 * 3 * 64;
+}
+__device__ __forceinline__ const uint4* p2_of(const LayerDev& L, int b = 0) {
+  return p1_of(L, b) + (size_t)(L.d_in / kChunk) * 2 * 3 * 64;
 }
 
 // rank index of element k (0..7) of a lane's c vector
@@ -429,11 +438,12 @@ __device__ __forceinline__ void correction(const bf16x8 (&a)[2][3], const bf16x8
 // Sum the waves' partial c (acc of every wave) in wave order through LDS and
 // store the tile's partial for its column group in fragment order, in
 // kHalves passes of kPerHalf row tiles.  Contains workgroup barriers.
+template <int kRB>
 __device__ __forceinline__ void store_partial(const LayerDev& L, const Tile& x,
                                               const f32x4 (&acc)[kTR][2],
-                                              float (*red)[kRedRows][64]) {
+                                              float (*red)[kRedRows][64], int b) {
   constexpr int kN = kFrag / kHalves;  // floats per pass
-  float* out = L.cbuf + ((int64_t)x.cg * L.n_rb + x.rb) * kFrag;
+  float* out = L.cbuf + (((int64_t)x.cg * L.n_rb + x.rb) * kRB + b) * kFrag;
 #pragma unroll
   for (int half = 0; half < kHalves; ++half) {
     if (half) __syncthreads();  // the first half has been read
@@ -461,10 +471,12 @@ __device__ __forceinline__ void store_partial(const LayerDev& L, const Tile& x,
 // The row block's c' operand of the second product, already split three
 // ways: [rt][split][lane] 16-byte groups of 8 bf16 (kCOp uint4 per row
 // block), into LDS.  Contains a workgroup barrier.
+// Rank block b of a row block at (rb * kRB + b) * kCOp.
 constexpr int kCOp = kTR * 3 * 64;
+template <int kRB = 1>
 __device__ __forceinline__ void stage_c(const LayerDev& L, const Tile& x, uint4* lds) {
-  const uint4* src = reinterpret_cast<const uint4*>(L.cfin) + x.rb * kCOp;
-  for (int e = threadIdx.x; e < kCOp; e += kTileThreads) lds[e] = src[e];
+  const uint4* src = reinterpret_cast<const uint4*>(L.cfin) + x.rb * kCOp * kRB;
+  for (int e = threadIdx.x; e < kCOp * kRB; e += kTileThreads) lds[e] = src[e];
   __syncthreads();
 }
 
@@ -474,11 +486,42 @@ __device__ __forceinline__ void c_operand(const uint4* lds, int rt, int lane, bf
   for (int s = 0; s < 3; ++s) cb[s] = as_bf16x8(lds[(rt * 3 + s) * 64 + lane]);
 }
 
+// second product over the kRB rank blocks, one chunk and 16-row tile:
+// corr[t] = sum over blocks b in order of (c'_b U_b^T) for the lane's 2 x 4
+// columns (c' of block b in lds at b * kCOp)
+template <int kRB>
+__device__ __forceinline__ void correction_rb(const bf16x8 (&a)[kRB][2][3], const uint4* lds,
+                                              int rt, int lane, f32x4 (&corr)[2]) {
+  corr[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  corr[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    bf16x8 cb[3];
+    c_operand(lds + b * kCOp, rt, lane, cb);
+    const bf16x8(*pa2[2])[3] = {&a[b][0], &a[b][1]};
+    const bf16x8(*pb2[2])[3] = {&cb, &cb};
+    mfma3x3_n<2>(pa2, pb2, corr);
+  }
+}
+
+template <int kRB>
+__device__ __forceinline__ void load_a_rb(const LayerDev& L, bool second, int c, int lane,
+                                          uint4 (&a)[kRB][2][3]) {
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) load_a(second ? p2_of(L, b) : p1_of(L, b), c, lane, a[b]);
+}
+
+template <int kRB>
+__device__ __forceinline__ void as_ops_rb(const uint4 (&u)[kRB][2][3], bf16x8 (&a)[kRB][2][3]) {
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) as_ops(u[b], a[b]);
+}
+
 // ---------------------------------------------------------------------------
 // first product of a tile: partial c over the column group (whiten: of G;
 // dequantize: of the codes, each chunk scaled by its inverse scale).
 // ---------------------------------------------------------------------------
-template <int kCPW, bool kCodes, int kFmt>
+template <int kCPW, bool kCodes, int kFmt, int kRB>
 __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
   constexpr bool kB128 = kFmt == GIFT_SCALE_BLOCK128, kMX = kFmt == GIFT_SCALE_MXFP4;
   // a local copy: the descriptor's fields stay in scalar registers
@@ -486,9 +529,11 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kCPW>(L, tile);
   __shared__ float red[kTW][kRedRows][64];
-  f32x4 acc[kTR][2];
+  f32x4 acc[kRB][kTR][2];
 #pragma unroll
-  for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < kRB; ++b)
+#pragma unroll
+    for (int rt = 0; rt < kTR; ++rt) acc[b][rt][0] = acc[b][rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t nseg = L.d_in / kBlock;
   constexpr bool kStaged = kCodes && !kMX;  // E4M3 codes come through LDS
   __shared__ __align__(16) uint32_t ctw[kStaged ? sizeof(CodeTile<kCPW>) / 4
@@ -506,14 +551,14 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
   }
   with_count<kCPW>(x.nmine, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    uint4 pa[n][2][3];
+    uint4 pa[n][kRB][2][3];
     float4 gv[kCodes ? 1 : n][kTR][2];
     uint32_t qv[kCodes ? n : 1][kTR][2];
     float sc[kB128 ? n : 1][kTR];
     uint32_t mc[kMX ? n : 1][kTR];
     static_for<n>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      load_a(L.P, x.c0 + j, x.lane, pa[j]);
+      load_a_rb<kRB>(L, false, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
         if constexpr (kMX) get_mx(mt, x, j, rt, qv[j][rt], mc[j][rt]);
@@ -526,28 +571,35 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
     });
     static_for<n>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      bf16x8 a[2][3];
-      as_ops(pa[j], a);
 #pragma unroll
-      for (int rt = 0; rt < kTR; ++rt) {
-        if constexpr (kMX) {
-          cpart_mx(a, qv[j][rt], mc[j][rt], acc[rt]);
-        } else if constexpr (kCodes) {
-          if constexpr (kB128) {
-            f32x4 t[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            cpart_q(a, qv[j][rt], t);
+      for (int b = 0; b < kRB; ++b) {
+        bf16x8 a[2][3];
+        as_ops(pa[j][b], a);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) acc[rt][h] += t[h] * sc[j][rt];
+        for (int rt = 0; rt < kTR; ++rt) {
+          if constexpr (kMX) {
+            cpart_mx(a, qv[j][rt], mc[j][rt], acc[b][rt]);
+          } else if constexpr (kCodes) {
+            if constexpr (kB128) {
+              f32x4 t[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+              cpart_q(a, qv[j][rt], t);
+#pragma unroll
+              for (int h = 0; h < 2; ++h) acc[b][rt][h] += t[h] * sc[j][rt];
+            } else {
+              cpart_q(a, qv[j][rt], acc[b][rt]);
+            }
           } else {
-            cpart_q(a, qv[j][rt], acc[rt]);
+            cpart_g(a, gv[j][rt], acc[b][rt]);
           }
-        } else {
-          cpart_g(a, gv[j][rt], acc[rt]);
         }
       }
     });
   });
-  store_partial(L, x, acc, red);
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    if (b) __syncthreads();  // the previous block's partial has been read from LDS
+    store_partial<kRB>(L, x, acc[b], red, b);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -555,10 +607,11 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
 // times the lane's rank coefficient (whiten: D_w; dequantize: D_u, and the
 // tensor's inverse scale for per-tensor scaling).  One workgroup per row block.
 // ---------------------------------------------------------------------------
-template <bool kDequant, bool kBlockScale>
-__device__ __forceinline__ void reduce_row_block(const LayerDev& L, int64_t rb, int tid) {
+template <bool kDequant, bool kBlockScale, int kRB>
+__device__ __forceinline__ void reduce_row_block(const LayerDev& L, int64_t rb, int tid, int b) {
   const int rt = tid >> 6, lane = tid & 63;  // one lane of one 16-row tile
-  const float* dk = L.coef + (kDequant ? GIFT_COEF_DU : GIFT_COEF_DW);
+  // D_w at 8, D_u after the factor's 32 kRB D_w entries; block b's ranks 32 b ..
+  const float* dk = L.coef + 8 + (kDequant ? kRank * kRB : 0) + kRank * b;
   const float extra = (kDequant && !kBlockScale) ? L.inv[0] : 1.f;
   float d8[8];
 #pragma unroll
@@ -566,8 +619,8 @@ __device__ __forceinline__ void reduce_row_block(const LayerDev& L, int64_t rb, 
   // partials in group order; eight groups' loads in flight at a time
   constexpr int kB = 8;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const float* base = L.cbuf + rb * kFrag + rt * 8 * 64 + lane;
-  const int64_t stride = L.n_rb * kFrag;
+  const float* base = L.cbuf + (rb * kRB + b) * kFrag + rt * 8 * 64 + lane;
+  const int64_t stride = L.n_rb * kRB * kFrag;
   for (int c0 = 0; c0 < L.ngrp; c0 += kB) {
     float v[kB][8];
 #pragma unroll
@@ -587,15 +640,17 @@ __device__ __forceinline__ void reduce_row_block(const LayerDev& L, int64_t rb, 
   for (int k = 0; k < 8; ++k) cp[k] = s[k] * d8[k];
   bf16x8 cb[3];
   split3(cp, cb);
-  uint4* out = reinterpret_cast<uint4*>(L.cfin) + rb * kCOp;
+  uint4* out = reinterpret_cast<uint4*>(L.cfin) + (rb * kRB + b) * kCOp;
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp) out[(rt * 3 + sp) * 64 + lane] = __builtin_bit_cast(uint4, cb[sp]);
 }
 
-template <bool kDequant, bool kBlockScale>
+template <bool kDequant, bool kBlockScale, int kRB>
 __global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
   const LayerDev L = gd.L[find_layer_rb(gd, blockIdx.x)];
-  reduce_row_block<kDequant, kBlockScale>(L, blockIdx.x - L.rb_begin, threadIdx.x);
+#pragma unroll
+  for (int b = 0; b < kRB; ++b)
+    reduce_row_block<kDequant, kBlockScale, kRB>(L, blockIdx.x - L.rb_begin, threadIdx.x, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -611,7 +666,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_tile_reduce(GroupDev gd) {
 // G^ = beta S + c'(D_u) U^T, written to G_hat
 constexpr int kFmtUnwhiten = 3;
 
-template <int kCPW, int kFmt, bool kWriteW>
+template <int kCPW, int kFmt, bool kWriteW, int kRB>
 __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
   constexpr bool kBlock128 = kFmt == GIFT_SCALE_BLOCK128;
   constexpr int kWPS = 4 / kCPW;  // waves per segment (block scaling)
@@ -619,37 +674,34 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kCPW>(L, tile);
-  __shared__ uint4 cs[kCOp];
+  __shared__ uint4 cs[kCOp * kRB];
   __shared__ uint32_t mx[kBlock128 ? kTW * kTR * 64 : kTW];
   __shared__ __align__(16) uint32_t ctw[kBlock128 ? sizeof(CodeTile<kCPW>) / 4
                           : kFmt == GIFT_SCALE_MXFP4 ? (sizeof(MxTile<kCPW>) + 3) / 4 : 1];
   CodeTile<kCPW>* ct = reinterpret_cast<CodeTile<kCPW>*>(ctw);
-  const uint4* P2 = p2_of(L);
   const float alpha = L.coef[kFmt == kFmtUnwhiten ? GIFT_COEF_BETA : GIFT_COEF_ALPHA];
   // this wave's operands and gradient in flight while c' is staged
-  uint4 pa[kCPW][2][3];
+  uint4 pa[kCPW][kRB][2][3];
   float4 gv[kCPW][kTR][2];
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      load_a(P2, x.c0 + j, x.lane, pa[j]);
+      load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
     });
   });
-  stage_c(L, x, cs);
+  stage_c<kRB>(L, x, cs);
   float4 w[kCPW][kTR][2];
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      bf16x8 a[2][3];
-      as_ops(pa[j], a);
+      bf16x8 a[kRB][2][3];
+      as_ops_rb<kRB>(pa[j], a);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        bf16x8 cb[3];
-        c_operand(cs, rt, x.lane, cb);
         f32x4 corr[2];
-        correction(a, cb, corr);
+        correction_rb<kRB>(a, cs, rt, x.lane, corr);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const float4 gg = gv[j][rt][t];
@@ -772,21 +824,20 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
 // per-tensor whiten pass 3: layer amax from the tile partials (or from
 // k_amax_final for very tall layers), W again from the row block's c', codes.
 // ---------------------------------------------------------------------------
-template <int kCPW, bool kWriteW>
+template <int kCPW, bool kWriteW, int kRB>
 __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kCPW>(L, tile);
-  __shared__ uint4 cs[kCOp];
+  __shared__ uint4 cs[kCOp * kRB];
   __shared__ uint32_t mx[kTW];
-  const uint4* P2 = p2_of(L);
   const float alpha = L.coef[GIFT_COEF_ALPHA];
-  uint4 pa[kCPW][2][3];
+  uint4 pa[kCPW][kRB][2][3];
   float4 gv[kCPW][kTR][2];
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      load_a(P2, x.c0 + j, x.lane, pa[j]);
+      load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
     });
@@ -803,20 +854,18 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
     L.inv[0] = sc.inv;
     if (gd.flags && sc.flags) atomicOr(gd.flags, sc.flags);
   }
-  stage_c(L, x, cs);
+  stage_c<kRB>(L, x, cs);
   __shared__ __align__(16) CodeTile<kCPW> ct;
   const bool nonfinite = (sc.flags & GIFT_FLAG_NONFINITE) != 0;
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      bf16x8 a[2][3];
-      as_ops(pa[j], a);
+      bf16x8 a[kRB][2][3];
+      as_ops_rb<kRB>(pa[j], a);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        bf16x8 cb[3];
-        c_operand(cs, rt, x.lane, cb);
         f32x4 corr[2];
-        correction(a, cb, corr);
+        correction_rb<kRB>(a, cs, rt, x.lane, corr);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const float4 gg = gv[j][rt][t];
@@ -1105,18 +1154,17 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_dequant(GroupDev gd) {
 // dequantize + un-whiten, pass 2: G^ = beta W^ + c'^ U^T with
 // W^ = decode(q) * inv and c'^ the row block's (W^ U) * D_u.
 // ---------------------------------------------------------------------------
-template <int kCPW, int kFmt>
+template <int kCPW, int kFmt, int kRB>
 __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
   constexpr bool kB128 = kFmt == GIFT_SCALE_BLOCK128, kMX = kFmt == GIFT_SCALE_MXFP4;
   const LayerDev L = gd.L[find_layer(gd, blockIdx.x)];
   const int tile = blockIdx.x - L.tile_begin;
   const Tile x = tile_ctx<kCPW>(L, tile);
-  __shared__ uint4 cs[kCOp];
-  const uint4* P2 = p2_of(L);
+  __shared__ uint4 cs[kCOp * kRB];
   const int64_t nseg = L.d_in / kBlock;
   const float inv0 = kFmt == GIFT_SCALE_TENSOR ? L.inv[0] : 1.f;
   const float beta = L.coef[GIFT_COEF_BETA];
-  uint4 pa[kCPW][2][3];
+  uint4 pa[kCPW][kRB][2][3];
   uint32_t qv[kCPW][kTR][2];
   float sc[kCPW][kTR];
   uint32_t mc[kMX ? kCPW : 1][kTR];
@@ -1127,7 +1175,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      load_a(P2, x.c0 + j, x.lane, pa[j]);
+      load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
         if constexpr (!kMX) sc[j][rt] = kB128 ? L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)] : inv0;
@@ -1140,7 +1188,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
     load_code_pieces(L, x, pcs);
     put_code_pieces(ct, pcs);
   }
-  stage_c(L, x, cs);  // its barrier also publishes the codes
+  stage_c<kRB>(L, x, cs);  // its barrier also publishes the codes
   if (x.nmine == 0) return;  // wave-uniform; no barrier below
   with_count<kCPW>(x.nmine, [&](auto N) {
     static_for<decltype(N)::value>([&](auto J) {
@@ -1161,14 +1209,12 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
     constexpr int n = decltype(N)::value;
     static_for<n>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      bf16x8 a[2][3];
-      as_ops(pa[j], a);
+      bf16x8 a[kRB][2][3];
+      as_ops_rb<kRB>(pa[j], a);
 #pragma unroll
       for (int rt = 0; rt < kTR; ++rt) {
-        bf16x8 cb[3];
-        c_operand(cs, rt, x.lane, cb);
         f32x4 corr[2];
-        correction(a, cb, corr);
+        correction_rb<kRB>(a, cs, rt, x.lane, corr);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const uint32_t qq = qv[j][rt][t];
@@ -1614,11 +1660,12 @@ hipError_t launch_pack(const PackGroup& pg, hipStream_t s) {
 }
 
 // scaling: GIFT_SCALE_TENSOR, GIFT_SCALE_BLOCK128 or GIFT_SCALE_MXFP4
-hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s) {
+template <int kRB>
+hipError_t whiten_quantize_rb(const GroupDev& g, int scaling, bool write_w, hipStream_t s) {
   const dim3 grid(g.total_tiles), blk(kTileThreads);
-  k_tile_cpart<kCPW, false, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
-  k_tile_reduce<false, false><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
-#define GIFT_TW(F, W) k_tile_whiten<kCPW, F, W><<<grid, blk, 0, s>>>(g)
+  k_tile_cpart<kCPW, false, GIFT_SCALE_TENSOR, kRB><<<grid, blk, 0, s>>>(g);
+  k_tile_reduce<false, false, kRB><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
+#define GIFT_TW(F, W) k_tile_whiten<kCPW, F, W, kRB><<<grid, blk, 0, s>>>(g)
   if (scaling == GIFT_SCALE_BLOCK128) {
     if (write_w) GIFT_TW(GIFT_SCALE_BLOCK128, true); else GIFT_TW(GIFT_SCALE_BLOCK128, false);
     return hipGetLastError();
@@ -1632,9 +1679,16 @@ hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, 
   bool tall = false;
   for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_part > kPartialLimit;
   if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
-  if (write_w) k_tile_quant<kCPW, true><<<grid, blk, 0, s>>>(g);
-  else k_tile_quant<kCPW, false><<<grid, blk, 0, s>>>(g);
+  if (write_w) k_tile_quant<kCPW, true, kRB><<<grid, blk, 0, s>>>(g);
+  else k_tile_quant<kCPW, false, kRB><<<grid, blk, 0, s>>>(g);
   return hipGetLastError();
+}
+
+// rb: rank blocks of the group's factors (1: rank <= 32, 2: rank <= 64)
+hipError_t launch_whiten_quantize(const GroupDev& g, int scaling, bool write_w, hipStream_t s,
+                                  int rb) {
+  return rb == 2 ? whiten_quantize_rb<2>(g, scaling, write_w, s)
+                 : whiten_quantize_rb<1>(g, scaling, write_w, s);
 }
 
 hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool write_w,
@@ -1671,30 +1725,36 @@ hipError_t launch_slab_whiten_quantize(const GroupDev& g, bool write_w, hipStrea
   for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_part > kPartialLimit;
   if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);
   const dim3 grid(g.total_tiles), blk(kTileThreads);
-  if (write_w) k_tile_quant<kCPW, true><<<grid, blk, 0, s>>>(g);
-  else k_tile_quant<kCPW, false><<<grid, blk, 0, s>>>(g);
+  if (write_w) k_tile_quant<kCPW, true, 1><<<grid, blk, 0, s>>>(g);
+  else k_tile_quant<kCPW, false, 1><<<grid, blk, 0, s>>>(g);
   return hipGetLastError();
 }
 
 #endif
 
-hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s) {
+template <int kRB>
+void dequant_white_rb(const GroupDev& g, int scaling, hipStream_t s) {
+  const dim3 grid(g.total_tiles), blk(kTileThreads);
+  const dim3 rgrid(g.total_rb), rblk(kReduceThreads);
+  if (scaling == GIFT_SCALE_BLOCK128) {
+    k_tile_cpart<kCPW, true, GIFT_SCALE_BLOCK128, kRB><<<grid, blk, 0, s>>>(g);
+    k_tile_reduce<true, true, kRB><<<rgrid, rblk, 0, s>>>(g);
+    k_tile_unwhiten<kCPW, GIFT_SCALE_BLOCK128, kRB><<<grid, blk, 0, s>>>(g);
+  } else if (scaling == GIFT_SCALE_MXFP4) {
+    k_tile_cpart<kCPW, true, GIFT_SCALE_MXFP4, kRB><<<grid, blk, 0, s>>>(g);
+    k_tile_reduce<true, true, kRB><<<rgrid, rblk, 0, s>>>(g);
+    k_tile_unwhiten<kCPW, GIFT_SCALE_MXFP4, kRB><<<grid, blk, 0, s>>>(g);
+  } else {
+    k_tile_cpart<kCPW, true, GIFT_SCALE_TENSOR, kRB><<<grid, blk, 0, s>>>(g);
+    k_tile_reduce<true, false, kRB><<<rgrid, rblk, 0, s>>>(g);
+    k_tile_unwhiten<kCPW, GIFT_SCALE_TENSOR, kRB><<<grid, blk, 0, s>>>(g);
+  }
+}
+
+hipError_t launch_dequant(const GroupDev& g, int scaling, bool white, hipStream_t s, int rb) {
   if (white) {
-    const dim3 grid(g.total_tiles), blk(kTileThreads);
-    const dim3 rgrid(g.total_rb), rblk(kReduceThreads);
-    if (scaling == GIFT_SCALE_BLOCK128) {
-      k_tile_cpart<kCPW, true, GIFT_SCALE_BLOCK128><<<grid, blk, 0, s>>>(g);
-      k_tile_reduce<true, true><<<rgrid, rblk, 0, s>>>(g);
-      k_tile_unwhiten<kCPW, GIFT_SCALE_BLOCK128><<<grid, blk, 0, s>>>(g);
-    } else if (scaling == GIFT_SCALE_MXFP4) {
-      k_tile_cpart<kCPW, true, GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
-      k_tile_reduce<true, true><<<rgrid, rblk, 0, s>>>(g);
-      k_tile_unwhiten<kCPW, GIFT_SCALE_MXFP4><<<grid, blk, 0, s>>>(g);
-    } else {
-      k_tile_cpart<kCPW, true, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
-      k_tile_reduce<true, false><<<rgrid, rblk, 0, s>>>(g);
-      k_tile_unwhiten<kCPW, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
-    }
+    if (rb == 2) dequant_white_rb<2>(g, scaling, s);
+    else dequant_white_rb<1>(g, scaling, s);
   } else {
     const dim3 grid(g.total_tiles), blk(kThreads);
     if (scaling == GIFT_SCALE_BLOCK128) k_flat_dequant<GIFT_SCALE_BLOCK128><<<grid, blk, 0, s>>>(g);
@@ -1763,11 +1823,17 @@ hipError_t launch_accumulate(const GroupDev& g, int scaling, bool first, hipStre
 }
 
 // G_hat = G_hat A_r^1/2 in place (the descriptors' G points at G_hat)
-hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s) {
+template <int kRB>
+void unwhiten_f32_rb(const GroupDev& g, hipStream_t s) {
   const dim3 grid(g.total_tiles), blk(kTileThreads);
-  k_tile_cpart<kCPW, false, GIFT_SCALE_TENSOR><<<grid, blk, 0, s>>>(g);
-  k_tile_reduce<true, true><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
-  k_tile_whiten<kCPW, kFmtUnwhiten, false><<<grid, blk, 0, s>>>(g);
+  k_tile_cpart<kCPW, false, GIFT_SCALE_TENSOR, kRB><<<grid, blk, 0, s>>>(g);
+  k_tile_reduce<true, true, kRB><<<dim3(g.total_rb), dim3(kReduceThreads), 0, s>>>(g);
+  k_tile_whiten<kCPW, kFmtUnwhiten, false, kRB><<<grid, blk, 0, s>>>(g);
+}
+
+hipError_t launch_unwhiten_f32(const GroupDev& g, hipStream_t s, int rb) {
+  if (rb == 2) unwhiten_f32_rb<2>(g, s);
+  else unwhiten_f32_rb<1>(g, s);
   return hipGetLastError();
 }
 

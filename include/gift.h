@@ -48,10 +48,13 @@ extern "C" {
 
 #define GIFT_ABI_VERSION 4
 
-/* Rank of the factor (GIFT review, free-parameter ledger: rank 32). */
+/* Rank of the factor (GIFT review, free-parameter ledger: rank 32), and the
+ * columns of one rank block: a factor of rank up to 32 stores 32 columns,
+ * one of rank 33..64 (the rank sweep's largest) two blocks, 64 columns. */
 #define GIFT_RANK 32
+#define GIFT_MAX_RANK 64
 /* Largest subspace width of the refresh eigensolve (rank + oversampling). */
-#define GIFT_MAX_SKETCH 64
+#define GIFT_MAX_SKETCH 96
 /* Row-segment length of 1x128 block scaling. */
 #define GIFT_BLOCK 128
 
@@ -99,7 +102,9 @@ enum { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1, GIFT_SCALE_MXFP4 = 2 };
                                    infinity, or a square overflowed fp32     */
 #define GIFT_FLAG_ZERO_AMAX 2u  /* a tensor / block was all zero: scale = 1 */
 
-/* Layout of gift_factor.coef (fp32, GIFT_COEF_COUNT entries). */
+/* Layout of gift_factor.coef (fp32, GIFT_COEF_COUNT entries) for a factor of
+ * 32 storage columns; a factor of 64 columns (rank above 32) has D_w at 8
+ * and D_u at 8 + 64, GIFT_COEF_COUNT_64 entries in all. */
 enum {
     GIFT_COEF_ALPHA = 0,        /* lambda_iso^-1/2                            */
     GIFT_COEF_BETA = 1,         /* lambda_iso^+1/2                            */
@@ -109,7 +114,9 @@ enum {
     GIFT_COEF_SIGMA2_TAIL = 5,  /* mean discarded eigenvalue                  */
     GIFT_COEF_DW = 8,           /* D_w[32] = (theta+lambda)^-1/2 - lambda^-1/2 */
     GIFT_COEF_DU = 8 + GIFT_RANK, /* D_u[32] = (theta+lambda)^1/2 - lambda^1/2 */
-    GIFT_COEF_COUNT = 8 + 2 * GIFT_RANK
+    GIFT_COEF_COUNT = 8 + 2 * GIFT_RANK,
+    GIFT_COEF_DU_64 = 8 + GIFT_MAX_RANK,
+    GIFT_COEF_COUNT_64 = 8 + 2 * GIFT_MAX_RANK
 };
 
 /*
@@ -119,9 +126,11 @@ enum {
  * inverse square root is
  *     A_r^-1/2 = alpha I + U diag(D_w) U^T
  * and its square root A_r^1/2 = beta I + U diag(D_u) U^T (U orthonormal).
- * The storage always holds GIFT_RANK columns: for r < GIFT_RANK the columns
- * of U and the entries of theta, D_w and D_u from r on are zero, so every
- * kernel works on 32 columns and the zero ones add exact zeros.
+ * The storage holds C = 32 columns for r <= 32 and C = 64 for 32 < r <= 64:
+ * U is d_in x C, theta C floats, coef 8 + 2 C floats (D_w at 8, D_u at
+ * 8 + C); the columns of U and the entries of theta, D_w and D_u from r on
+ * are zero, so every kernel works on whole 32-column rank blocks and the
+ * zero ones add exact zeros.
  * Written by gift_refresh_factor; a caller may also fill it itself.
  *
  * block = 32 or 64 makes it a block-diagonal factor instead ("block-A-b",
@@ -142,23 +151,28 @@ enum {
  */
 typedef struct gift_factor {
     int32_t d_in;     /* rows of U; 64 <= d_in, % 16 == 0 (% 32 to whiten)    */
-    int32_t rank;     /* effective rank r, 1 <= r <= GIFT_RANK; the refresh
-                         keeps the top r Ritz pairs and damps with d_in - r   */
-    float *U;         /* device, d_in x GIFT_RANK, row-major                  */
-    float *theta;     /* device, GIFT_RANK: Ritz values, descending, >= 0     */
-    float *coef;      /* device, GIFT_COEF_COUNT floats (layout above)        */
-    void *packs;      /* optional device buffer of gift_factor_pack_bytes(d_in)
-                         bytes: U split into the bf16 operand layouts of the
-                         whitening kernels.  Written by gift_refresh_factor(s)
-                         and gift_prepare_factor; it must be rewritten after
-                         U changes.  NULL: every grouped call re-packs U into
+    int32_t rank;     /* effective rank r, 1 <= r <= GIFT_MAX_RANK; the
+                         refresh keeps the top r Ritz pairs and damps with
+                         d_in - r                                             */
+    float *U;         /* device, d_in x C, row-major (C above)                */
+    float *theta;     /* device, C: Ritz values, descending, >= 0             */
+    float *coef;      /* device, 8 + 2 C floats (layout above)                */
+    void *packs;      /* optional device buffer of
+                         gift_factor_pack_bytes_rank(d_in, rank) bytes: U
+                         split into the bf16 operand layouts of the whitening
+                         kernels.  Written by gift_refresh_factor(s) and
+                         gift_prepare_factor; it must be rewritten after U
+                         changes.  NULL: every grouped call re-packs U into
                          its workspace.                                     */
     int32_t block;    /* 0: the rank-r factor; 32 or 64: block-diagonal
                          factor of that block size (see above)                 */
 } gift_factor;
 
-/* Size of gift_factor.packs for a factor with d_in rows (d_in % 32 == 0). */
+/* Size of gift_factor.packs for a factor with d_in rows (d_in % 32 == 0) of
+ * rank up to 32; gift_factor_pack_bytes_rank gives it for any rank (twice
+ * that above rank 32), 0 for a rank outside [1, 64]. */
 size_t gift_factor_pack_bytes(int64_t d_in);
+size_t gift_factor_pack_bytes_rank(int64_t d_in, int rank);
 
 /* Size of gift_factor.packs for a block-diagonal factor (block 32 or 64,
  * d_in % block == 0); 0 for other arguments. */
@@ -206,7 +220,9 @@ typedef struct gift_layer {
  *
  * X: device, n_tokens x f->d_in, x_dtype.  f: host struct with device
  * buffers, written.  A_out: optional device d_in x d_in fp32, receives A.
- * sketch_width: rank <= width <= 64, multiple of 16.  power_steps >= 0.
+ * sketch_width: 32 <= width <= 96, multiple of 16, at least the rank (the
+ * rank sweep's reading: width = rank + 32, i.e. 64 for rank <= 32 and 96
+ * for rank 64).  power_steps >= 0.
  * dev_flags: optional device word (4-byte aligned); GIFT_FLAG_NONFINITE is
  * OR-ed into it when tr(A) is not finite (a NaN or infinity in X reaches
  * the diagonal of A).  The factor written in that case is not meaningful;

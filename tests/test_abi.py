@@ -72,7 +72,7 @@ def test_block_scaling_needs_multiple_of_128():
 def test_factor_validation():
     f = _lib._Factor(128, 32, 0x20000, 0x30000, 0x40000, None)
     assert _call_whiten([_layer(d_in=256, factor=ctypes.pointer(f))]) == 1   # d_in mismatch
-    for bad in (0, 33, -1):   # the effective rank is 1..32
+    for bad in (0, 65, -1):   # the effective rank is 1..64
         f_bad_rank = _lib._Factor(128, bad, 0x20000, 0x30000, 0x40000, None)
         assert _call_whiten([_layer(d_in=128, factor=ctypes.pointer(f_bad_rank))]) == 2
     f_small = _lib._Factor(32, 32, 0x20000, 0x30000, 0x40000, None)
@@ -132,12 +132,19 @@ def test_refresh_validation():
     r[0].n_tokens = 1024
     f.d_in = 100
     assert call() == 2
-    f.d_in, f.rank = 128, 33   # the effective rank is 1..32
+    f.d_in, f.rank = 128, 65   # the effective rank is 1..64
     assert call() == 2
+    f.rank = 48                # and at most the sketch width
+    assert call(w=32) == 2
+    assert call(w=112) == 2    # widths up to 96
     f.rank = 0
     assert call() == 2
     assert lib.gift_refresh_group_workspace_bytes(r, 1, 64) == 0 or True
     assert lib.gift_factor_pack_bytes(1024) == 1024 * 384
+    assert lib.gift_factor_pack_bytes_rank(1024, 32) == 1024 * 384
+    assert lib.gift_factor_pack_bytes_rank(1024, 33) == 2 * 1024 * 384
+    assert lib.gift_factor_pack_bytes_rank(1024, 64) == 2 * 1024 * 384
+    assert lib.gift_factor_pack_bytes_rank(1024, 65) == 0
     assert lib.gift_prepare_factor(None, None) == 1
     assert lib.gift_draw_sketch(None, 10, 64, 0, None) == 1
 
@@ -195,8 +202,10 @@ def test_refresh_workspace_has_no_partials_for_single_range_bf16():
 
     def al(x):
         return (x + 255) // 256 * 256
-    per = (al(d * d * 4) + 4 * al(d * w * 4) + al(4 * d * w * 4) + al(d // 32 * 4 * 3 * 64 * 16)
-           + al(16 * 64 * 64 * 8) + al(64 * 64 * 8) + al(64))
+    wmax = 96   # the operand packs of Q, the Gram partials and the triangle are laid out
+    # for the largest width, so one layout serves every width
+    per = (al(d * d * 4) + 4 * al(d * w * 4) + al(4 * d * w * 4) + al(d // 32 * wmax // 16 * 3 * 64 * 16)
+           + al(16 * wmax * wmax * 8) + al(wmax * wmax * 8) + al(64))
     bf16 = lib.gift_refresh_group_workspace_bytes(r, 16, w)
     assert bf16 == 16 * per
     for k in range(16):
