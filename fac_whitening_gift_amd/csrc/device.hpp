@@ -16,6 +16,7 @@ constexpr int kMaxRank = GIFT_MAX_RANK;   // largest factor rank (two rank block
 __host__ __device__ __forceinline__ int factor_cols(int rank) { return rank > kRank ? 2 * kRank : kRank; }
 constexpr int kBlock = GIFT_BLOCK;
 constexpr int kMaxGroup = 16;          // layers per grouped launch
+constexpr int kXcd = 8;                // XCDs of the MI355X; workgroups go to them in turn
 constexpr float kE4M3Max = 448.0f;     // largest finite OCP E4M3 magnitude
 
 // ---------------------------------------------------------------------------

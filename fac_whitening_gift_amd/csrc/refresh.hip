@@ -214,6 +214,49 @@ __device__ __forceinline__ void decode_pair(int pair, int nb, int& bi, int& bj) 
   bj = i + rem;
 }
 
+// Covariance tile of the l-th workgroup (l in [0, npairs)) of one input's
+// token range.  Workgroups go to the kXcd XCDs in turn, so XCD x runs
+// l = x, x + kXcd, ...; it is given the x-th contiguous run of the tiles in
+// band order -- bands of kBand tile rows, each walked column by column -- so
+// the tiles that run together on one XCD read few distinct column panels of
+// X and share them through its L2.
+constexpr int kBand = 8;
+__device__ __forceinline__ void band_tile(int l, int npairs, int nb, int& bi, int& bj) {
+  const int x = l % kXcd, r = l / kXcd;
+  const int len = (npairs + kXcd - 1) / kXcd, rem = npairs % kXcd;
+  int t = x * len + r;  // XCD x: tiles [x len - max(0, x - rem), ...) of the band order
+  if (rem && x > rem) t -= x - rem;
+  for (int r0 = 0; r0 < nb;) {
+    const int rc = nb - r0 < kBand ? nb - r0 : kBand;
+    const int tri = rc * (rc + 1) / 2;  // columns r0 .. r0 + rc - 1: c - r0 + 1 tiles each
+    const int band = tri + (nb - r0 - rc) * rc;
+    if (t < band) {
+      if (t < tri) {
+        int c = 0;
+        while (t > c) {
+          t -= c + 1;
+          ++c;
+        }
+        bi = r0 + t;
+        bj = r0 + c;
+      } else {
+        t -= tri;
+        bi = r0 + t % rc;
+        bj = r0 + rc + t / rc;
+      }
+      return;
+    }
+    t -= band;
+    r0 += rc;
+  }
+  bi = bj = 0;  // not reached for l < npairs
+}
+
+// row-major index of upper-triangle tile (bi, bj), the layout of the partials
+__device__ __forceinline__ int pair_index(int bi, int bj, int nb) {
+  return bi * nb - bi * (bi - 1) / 2 + (bj - bi);
+}
+
 // bf16: thread t loads columns c0+2(t%64), +1 for tokens n0+8(t/64)..+7 and
 // stores each column's 8 tokens as one 16-byte LDS row segment.
 __device__ __forceinline__ void syrk_load_tile(uint16_t (*lds)[kKStep + 8], const uint16_t* X,
@@ -322,10 +365,11 @@ __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
     if (i < g.sy_n && (int)blockIdx.x >= g.sy_begin[i]) k = i;
   const RIn& R = g.r[g.sy_in[k]];
   const int local = (int)blockIdx.x - g.sy_begin[k];
-  const int pair = local % R.npairs, split = local / R.npairs;
+  const int split = local / R.npairs;
   __shared__ SyrkBuf sb[2];
   int bi, bj;
-  decode_pair(pair, R.nb, bi, bj);
+  band_tile(local - split * R.npairs, R.npairs, R.nb, bi, bj);
+  const int pair = pair_index(bi, bj, R.nb);
   const int d = R.d;
   const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
   const int64_t n_begin = (int64_t)split * R.chunk;
@@ -681,47 +725,66 @@ __global__ __launch_bounds__(kT) void k_pack_q(G g, int which) {
 }
 
 constexpr int kGemmWaves = 4;
-// workgroups of 64-row shape from which a call takes that shape (eight per CU)
+// 16-row tiles of A per wave in the 64-row shape: each load of Q's packs
+// feeds this many tiles
+constexpr int kGemmTR = 2;
+constexpr int kGemmRows = 16 * kGemmWaves * kGemmTR;  // rows per workgroup of that shape
+// workgroups of that shape from which a call takes it (eight per CU)
 constexpr int64_t kGemmRowTileMin = 2048;
 
 // Two workgroup shapes (four waves each):
 //   kRowTiles = false: 16 rows of one partial; the waves split the partial's
 //     K range into four and their sums are added in wave order through LDS.
 //     grid: (max d / 16, kYSplit, inputs).
-//   kRowTiles = true: 64 rows of one partial, each wave 16 of them over the
-//     partial's whole K range; the four waves read the same Q packs at about
-//     the same time, so most of those reads hit in cache, and each wave's
-//     pipeline runs four times as long.  grid: (max d / 64, kYSplit, inputs).
-// The second needs a quarter of the workgroups, so it is taken only when a
-// call has enough rows to fill the machine with it.
+//   kRowTiles = true: kGemmRows rows of one partial, each wave kGemmTR
+//     16-row tiles of them over the partial's whole K range; a wave's load of
+//     Q's packs for a K chunk feeds all its tiles, and the four waves read the
+//     same packs at about the same time, so most of those reads hit in cache.
+//     grid: (max d / kGemmRows, kYSplit, inputs).
+// The second needs far fewer workgroups, so it is taken only when a call
+// has enough rows to fill the machine with it.
 template <bool kRowTiles, int kWT, class G>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
+  constexpr int kTRw = kRowTiles ? kGemmTR : 1;  // 16-row tiles of this wave
   const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = kRowTiles ? (blockIdx.x * kGemmWaves + wave) * 16 : blockIdx.x * 16;
+  const int row0 = kRowTiles ? (blockIdx.x * kGemmWaves + wave) * 16 * kTRw : blockIdx.x * 16;
   if (row0 >= d) return;  // uniform over the wave (kRowTiles: no barrier follows) or workgroup
   const float* __restrict__ A = R.A;
   const int r16 = lane & 15, gq = lane >> 4;
   const int ntile = w / 16;
-  f32x4 acc[kWT];
+  f32x4 acc[kTRw][kWT];
 #pragma unroll
-  for (int t = 0; t < kWT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kTRw; ++j)
+#pragma unroll
+    for (int t = 0; t < kWT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int kchunks = (d + 31) / 32;
   const int slices = kRowTiles ? kYSplit : kYSplit * kGemmWaves;
   const int slice = kRowTiles ? blockIdx.y : blockIdx.y * kGemmWaves + wave;
   const int kc_begin = slice * kchunks / slices, kc_end = (slice + 1) * kchunks / slices;
-  const float* arow = A + (int64_t)(row0 + r16) * d;
-  // one K chunk of 32: this lane's 8 values of A's row and its packs of Q
+  // d % 16 == 0: a 16-row tile is all inside A or all past it (wave-uniform)
+  bool rin[kTRw];
+  const float* arow[kTRw];
+#pragma unroll
+  for (int j = 0; j < kTRw; ++j) {
+    rin[j] = row0 + 16 * j < d;
+    arow[j] = A + (int64_t)(rin[j] ? row0 + 16 * j + r16 : row0 + r16) * d;
+  }
+  // one K chunk of 32: this lane's 8 values of each tile's row of A and its
+  // packs of Q
   struct Chunk {
-    float4 a[2];
+    float4 a[kTRw][2];
     uint4 q[kWT][3];
   };
   auto load = [&](int kc, Chunk& c) {
     const int k0 = 32 * kc + 8 * gq;
     const bool in = k0 < d;  // d % 16 == 0: a lane's 8 columns are all in or all out
-    c.a[0] = in ? *reinterpret_cast<const float4*>(arow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-    c.a[1] = in ? *reinterpret_cast<const float4*>(arow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kTRw; ++j) {
+      c.a[j][0] = in ? *reinterpret_cast<const float4*>(arow[j] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      c.a[j][1] = in ? *reinterpret_cast<const float4*>(arow[j] + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int t = 0; t < kWT; ++t)
 #pragma unroll
@@ -729,15 +792,19 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
         c.q[t][s] = t < ntile ? R.QP[(size_t)((kc * ntile + t) * 3 + s) * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
   };
   auto comp = [&](const Chunk& c) {
-    const float v[8] = {c.a[0].x, c.a[0].y, c.a[0].z, c.a[0].w, c.a[1].x, c.a[1].y, c.a[1].z, c.a[1].w};
-    bf16x8 sa[3];
-    split3(v, sa);
 #pragma unroll
-    for (int t = 0; t < kWT; ++t)
-      if (t < ntile) {
-        const bf16x8 sb[3] = {as_bf16x8(c.q[t][0]), as_bf16x8(c.q[t][1]), as_bf16x8(c.q[t][2])};
-        acc[t] = mfma3x3(sa, sb, acc[t]);
-      }
+    for (int j = 0; j < kTRw; ++j) {
+      const float v[8] = {c.a[j][0].x, c.a[j][0].y, c.a[j][0].z, c.a[j][0].w,
+                          c.a[j][1].x, c.a[j][1].y, c.a[j][1].z, c.a[j][1].w};
+      bf16x8 sa[3];
+      split3(v, sa);
+#pragma unroll
+      for (int t = 0; t < kWT; ++t)
+        if (t < ntile) {
+          const bf16x8 sb[3] = {as_bf16x8(c.q[t][0]), as_bf16x8(c.q[t][1]), as_bf16x8(c.q[t][2])};
+          acc[j][t] = mfma3x3(sa, sb, acc[j][t]);
+        }
+    }
   };
   // two-stage pipeline; the prefetch is unconditional (the last chunk is
   // loaded twice) so the compiler waits for exactly the chunk in use
@@ -758,17 +825,21 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   float* __restrict__ Yp = R.Yp + (size_t)blockIdx.y * d * w;
   if constexpr (kRowTiles) {
 #pragma unroll
-    for (int t = 0; t < kWT; ++t)
-      if (t < ntile)
+    for (int j = 0; j < kTRw; ++j)
+      if (rin[j])
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Yp[(int64_t)(row0 + 4 * gq + i) * w + 16 * t + r16] = acc[t][i];
+        for (int t = 0; t < kWT; ++t)
+          if (t < ntile)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              Yp[(int64_t)(row0 + 16 * j + 4 * gq + i) * w + 16 * t + r16] = acc[j][t][i];
   } else {
     __shared__ float red[kGemmWaves][16][16 * kWT];
 #pragma unroll
     for (int t = 0; t < kWT; ++t)
       if (t < ntile)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][4 * gq + i][16 * t + r16] = acc[t][i];
+        for (int i = 0; i < 4; ++i) red[wave][4 * gq + i][16 * t + r16] = acc[0][t][i];
     __syncthreads();
     for (int e = threadIdx.x; e < 16 * w; e += 64 * kGemmWaves) {
       const int r = e / w, c = e % w;
@@ -785,9 +856,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
 template <int kWT, class G>
 void gemm_aq_w(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
   int64_t tiles = 0;
-  for (int i = 0; i < nc; ++i) tiles += (hd[i].d + 16 * kGemmWaves - 1) / (16 * kGemmWaves);
+  for (int i = 0; i < nc; ++i) tiles += (hd[i].d + kGemmRows - 1) / kGemmRows;
   if (tiles * kYSplit >= kGemmRowTileMin) {
-    const dim3 grid((maxd + 16 * kGemmWaves - 1) / (16 * kGemmWaves), kYSplit, nc);
+    const dim3 grid((maxd + kGemmRows - 1) / kGemmRows, kYSplit, nc);
     k_gemm_aq<true, kWT><<<grid, 64 * kGemmWaves, 0, st>>>(g);
   } else {
     k_gemm_aq<false, kWT><<<dim3(maxd / 16, kYSplit, nc), 64 * kGemmWaves, 0, st>>>(g);

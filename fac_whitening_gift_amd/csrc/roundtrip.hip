@@ -168,8 +168,17 @@ __device__ __forceinline__ Tile tile_ctx(const LayerDev& L, int tile) {
   x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   x.r16 = x.lane & 15;
   x.g = x.lane >> 4;
-  x.rb = tile / L.ngrp;
-  x.cg = tile % L.ngrp;
+  // Workgroups are handed to the kXcd XCDs in turn.  The tiles of one row
+  // block are numbered kXcd apart (within groups of kXcd row blocks), so they
+  // all run on one XCD, close together in time, and read the row block's
+  // shared data (c' in operand form) through one L2.  The last, shorter
+  // group of a layer spaces its tiles by its own row-block count.
+  const int span = kXcd * L.ngrp;
+  const int sg = tile / span, w = tile - sg * span;
+  const int rb_left = (int)L.n_rb - sg * kXcd;
+  const int nr = rb_left < kXcd ? rb_left : kXcd;
+  x.rb = (int64_t)sg * kXcd + w % nr;
+  x.cg = w / nr;
 #pragma unroll
   for (int rt = 0; rt < kTR; ++rt) {
     const int64_t r = x.rb * kTileRows + 16 * rt + x.r16;
