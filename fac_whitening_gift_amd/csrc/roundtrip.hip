@@ -1741,21 +1741,44 @@ hipError_t launch_slab_whiten_quantize(const GroupDev& g, bool write_w, hipStrea
 
 #endif
 
+// chunks per wave of the dequantize side's first product: column groups of
+// 256 kDeqCPW columns, so half the partial coefficients are written and
+// summed (the un-whiten pass keeps kCPW: with two chunks per wave it spills)
+constexpr int kDeqCPW = 2;
+
+// g with the column groups of kDeqCPW chunks per wave (the tiles of the
+// first product and the partials the reduction sums)
+GroupDev deq_groups(const GroupDev& g) {
+  GroupDev w = g;
+  int tiles = 0;
+  for (int i = 0; i < g.n; ++i) {
+    LayerDev& L = w.L[i];
+    const int nch = (int)(L.d_in / kChunk), per = kTW * kDeqCPW;
+    L.ngrp = (nch + per - 1) / per;
+    L.n_tiles = (int)L.n_rb * L.ngrp;
+    L.tile_begin = tiles;
+    tiles += L.n_tiles;
+  }
+  w.total_tiles = tiles;
+  return w;
+}
+
 template <int kRB>
 void dequant_white_rb(const GroupDev& g, int scaling, hipStream_t s) {
-  const dim3 grid(g.total_tiles), blk(kTileThreads);
+  const GroupDev gw = kDeqCPW == kCPW ? g : deq_groups(g);
+  const dim3 grid(g.total_tiles), wgrid(gw.total_tiles), blk(kTileThreads);
   const dim3 rgrid(g.total_rb), rblk(kReduceThreads);
   if (scaling == GIFT_SCALE_BLOCK128) {
-    k_tile_cpart<kCPW, true, GIFT_SCALE_BLOCK128, kRB><<<grid, blk, 0, s>>>(g);
-    k_tile_reduce<true, true, kRB><<<rgrid, rblk, 0, s>>>(g);
+    k_tile_cpart<kDeqCPW, true, GIFT_SCALE_BLOCK128, kRB><<<wgrid, blk, 0, s>>>(gw);
+    k_tile_reduce<true, true, kRB><<<rgrid, rblk, 0, s>>>(gw);
     k_tile_unwhiten<kCPW, GIFT_SCALE_BLOCK128, kRB><<<grid, blk, 0, s>>>(g);
   } else if (scaling == GIFT_SCALE_MXFP4) {
-    k_tile_cpart<kCPW, true, GIFT_SCALE_MXFP4, kRB><<<grid, blk, 0, s>>>(g);
-    k_tile_reduce<true, true, kRB><<<rgrid, rblk, 0, s>>>(g);
+    k_tile_cpart<kDeqCPW, true, GIFT_SCALE_MXFP4, kRB><<<wgrid, blk, 0, s>>>(gw);
+    k_tile_reduce<true, true, kRB><<<rgrid, rblk, 0, s>>>(gw);
     k_tile_unwhiten<kCPW, GIFT_SCALE_MXFP4, kRB><<<grid, blk, 0, s>>>(g);
   } else {
-    k_tile_cpart<kCPW, true, GIFT_SCALE_TENSOR, kRB><<<grid, blk, 0, s>>>(g);
-    k_tile_reduce<true, false, kRB><<<rgrid, rblk, 0, s>>>(g);
+    k_tile_cpart<kDeqCPW, true, GIFT_SCALE_TENSOR, kRB><<<wgrid, blk, 0, s>>>(gw);
+    k_tile_reduce<true, false, kRB><<<rgrid, rblk, 0, s>>>(gw);
     k_tile_unwhiten<kCPW, GIFT_SCALE_TENSOR, kRB><<<grid, blk, 0, s>>>(g);
   }
 }
