@@ -36,7 +36,9 @@ namespace gift {
   size_t pack_bytes(int64_t d_in);
 namespace rt4 {
 GIFT_TILE_DECLS
-hipError_t launch_slab_whiten_quantize(const GroupDev& g, bool write_w, hipStream_t s);
+hipError_t launch_slab_whiten(const GroupDev& all, hipStream_t s);
+hipError_t launch_slab_quantize(const GroupDev& g, bool write_w, hipStream_t s);
+hipError_t launch_put_layers(const LayerDev* host, int n, LayerDev* dst, hipStream_t s);
 }
 namespace rt2 {
 GIFT_TILE_DECLS
@@ -235,10 +237,21 @@ Packs plan_packs(const gift_layer* layers, int n, Op op) {
   return p;
 }
 
+bool slab_layer(const gift_layer& L, int scaling);
+
+// Descriptors of the slab layers of a whiten call in device memory, after
+// the per-layer slices, when there are more than fit inline in a launch.
+size_t slab_desc_bytes(const gift_layer* layers, int n, Op op, bool block) {
+  if (op != Op::Whiten || block) return 0;
+  int k = 0;
+  for (int i = 0; i < n; ++i) k += slab_layer(layers[i], GIFT_SCALE_TENSOR);
+  return k > kMaxGroup ? align_up((size_t)k * sizeof(LayerDev)) : 0;
+}
+
 size_t group_ws(const gift_layer* layers, int n, Op op, bool block) {
   size_t t = plan_packs(layers, n, op).bytes;
   for (int i = 0; i < n; ++i) t += layer_ws(layers[i], op, block).total();
-  return t;
+  return t + slab_desc_bytes(layers, n, op, block);
 }
 
 // One pack launch entry per rank block: U's block b starts at column 32 b,
@@ -361,38 +374,29 @@ const TileOps& tile_ops(const gift_layer* layers, int n, Op op) {
 }
 
 // Walk the layers selected by `pick` in chunks of kMaxGroup, filling the
-// descriptors (workspace slices in layer order) and calling `launch`.
+// descriptors (workspace slices in layer order) and calling `launch` per
+// chunk.  slab: the layers whiten as slabs; k_slab_whiten first runs once
+// over all of them (descriptors past kMaxGroup in device memory, after the
+// per-layer slices), then `launch` quantizes chunk by chunk.
 template <class Pick, class Tiles, class Launch>
 gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void* ws,
                         uint32_t* flags, double* out, Pick pick, Tiles tiles, Launch launch,
-                        const TileOps& geo = kTiles64, bool slab = false) {
+                        const TileOps& geo = kTiles64, bool slab = false,
+                        hipStream_t st = nullptr) {
   // workspace: operand packs first, then per-layer slices in layer order
   // (independent of the chunking)
   const Packs packs = plan_packs(layers, n, op);
   std::vector<size_t> off(n + 1, packs.bytes);
   for (int i = 0; i < n; ++i) off[i + 1] = off[i] + layer_ws(layers[i], op, block).total();
-  GroupDev g{};
-  g.flags = flags;
-  g.out = out;
-  int first = -1;
-  auto flush = [&]() -> gift_status {
-    if (g.n == 0) return GIFT_OK;
-    hipError_t e = launch(g, first);
-    if (e != hipSuccess) return hip_fail(e, "kernel launch");
-    g.n = 0;
-    g.total_tiles = 0;
-    g.total_rb = 0;
-    first = -1;
-    return GIFT_OK;
-  };
+  std::vector<LayerDev> all;
+  std::vector<int> index;  // call position of each picked layer
+  int64_t tiles_all = 0, rb_all = 0;
   for (int i = 0; i < n; ++i) {
     const gift_layer& L = layers[i];
     if (!pick(L)) continue;
-    if (first < 0) first = i;
     LayerWs lw = layer_ws(L, op, block);
     char* base = (char*)ws + off[i];
-    LayerDev& d = g.L[g.n];
-    d = LayerDev{};
+    LayerDev d{};
     d.G = op == Op::UnwhitenF32 ? L.G_hat : L.G;
     d.q = L.q;
     d.inv = L.inv_scale;
@@ -419,17 +423,52 @@ gift_status run_grouped(const gift_layer* layers, int n, Op op, bool block, void
     d.ngrp = !whitened(L, op) ? 1 : fblock(L) ? blk_col_groups(L.d_in, fblock(L)) : col_groups(L.d_in);
     d.n_tiles = tiles(L);
     d.n_part = slab ? (int)d.n_rb : d.n_tiles;  // one amax partial per row block or per tile
-    d.tile_begin = g.total_tiles;
-    g.total_tiles += d.n_tiles;
-    d.rb_begin = g.total_rb;
-    if (whitened(L, op)) g.total_rb += (int)d.n_rb;
-    ++g.n;
-    if (g.n == kMaxGroup) {
-      gift_status s = flush();
-      if (s != GIFT_OK) return s;
-    }
+    d.tile_begin = (int)tiles_all;
+    tiles_all += d.n_tiles;
+    d.rb_begin = (int)rb_all;
+    if (whitened(L, op)) rb_all += d.n_rb;
+    all.push_back(d);
+    index.push_back(i);
   }
-  return flush();
+  if (all.empty()) return GIFT_OK;
+  GroupDev g{};
+  g.flags = flags;
+  g.out = out;
+  if (slab) {  // the slab pass over all layers at once
+    if (rb_all > INT32_MAX) return fail(GIFT_ERR_UNSUPPORTED_SHAPE, "too many row blocks in one call");
+    GroupDev ga = g;
+    ga.n = (int)all.size();
+    ga.total_rb = (int)rb_all;
+    if (ga.n <= kMaxGroup) {
+      for (int k = 0; k < ga.n; ++k) ga.L[k] = all[k];
+    } else {
+      LayerDev* dst = reinterpret_cast<LayerDev*>((char*)ws + off[n]);
+      hipError_t e = rt4::launch_put_layers(all.data(), ga.n, dst, st);
+      if (e != hipSuccess) return hip_fail(e, "kernel launch");
+      ga.Lx = dst;
+    }
+    hipError_t e = rt4::launch_slab_whiten(ga, st);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  }
+  // chunks of kMaxGroup layers with inline descriptors, tiles and row blocks
+  // counted from each chunk's start
+  for (size_t c0 = 0; c0 < all.size(); c0 += kMaxGroup) {
+    const size_t c1 = all.size() - c0 < (size_t)kMaxGroup ? all.size() : c0 + kMaxGroup;
+    g.n = 0;
+    g.total_tiles = 0;
+    g.total_rb = 0;
+    for (size_t k = c0; k < c1; ++k) {
+      LayerDev& d = g.L[g.n++];
+      d = all[k];
+      d.tile_begin = g.total_tiles;
+      g.total_tiles += d.n_tiles;
+      d.rb_begin = g.total_rb;
+      if (whitened(layers[index[k]], op)) g.total_rb += (int)d.n_rb;
+    }
+    hipError_t e = launch(g, index[c0]);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  }
+  return GIFT_OK;
 }
 
 int tiles_flat(const gift_layer& L) { return flat_tiles(L.d_out * L.d_in); }
@@ -554,8 +593,8 @@ gift_status gift_whiten_quantize(const gift_layer* layers, int n_layers, int sca
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       [&](const gift_layer& L) { return row_tiles(L, kTiles64); },
                       [&](const GroupDev& g, int) {
-                        return rt4::launch_slab_whiten_quantize(g, any_w, st);
-                      }, kTiles64, true);
+                        return rt4::launch_slab_quantize(g, any_w, st);
+                      }, kTiles64, true, st);
     else
       s = run_grouped(layers, n_layers, Op::Whiten, block, ws, dev_flags, nullptr, pick,
                       tiles_rows, [&](const GroupDev& g, int) {

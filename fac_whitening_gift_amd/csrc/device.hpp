@@ -15,7 +15,10 @@ constexpr int kMaxRank = GIFT_MAX_RANK;   // largest factor rank (two rank block
 // storage columns of a rank-r factor: one rank block up to rank 32, else two
 __host__ __device__ __forceinline__ int factor_cols(int rank) { return rank > kRank ? 2 * kRank : kRank; }
 constexpr int kBlock = GIFT_BLOCK;
-constexpr int kMaxGroup = 16;          // layers per grouped launch
+constexpr int kMaxGroup = 16;          // layers per grouped launch (descriptors inline)
+// Above this many amax partials in a layer they are first reduced by one
+// workgroup (k_amax_final) instead of by every quantize workgroup.
+constexpr int kPartialLimit = 2048;
 constexpr int kXcd = 8;                // XCDs of the MI355X; workgroups go to them in turn
 constexpr float kE4M3Max = 448.0f;     // largest finite OCP E4M3 magnitude
 
@@ -296,6 +299,10 @@ struct GroupDev {
   int total_rb;         // row blocks over the group (tile kernels)
   uint32_t* flags;      // may be NULL
   double* out;          // roundtrip_error output, may be NULL
+  // NULL: the n <= kMaxGroup layers are L[0 .. n).  Else the descriptors of
+  // all n layers in device memory; only k_slab_whiten is launched so (it
+  // looks its layer up with find_layer_rb and layer_at).
+  const LayerDev* Lx;
   LayerDev L[kMaxGroup];
 };
 
@@ -324,11 +331,24 @@ __device__ __forceinline__ int find_layer(const GroupDev& g, int tile) {
 }
 
 __device__ __forceinline__ int find_layer_rb(const GroupDev& g, int rb) {
+  if (g.Lx) {  // the last layer whose first row block is <= rb
+    int lo = 0, hi = g.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (rb >= g.Lx[mid].rb_begin) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  }
   int l = 0;
 #pragma unroll
   for (int i = 1; i < kMaxGroup; ++i)
     if (i < g.n && rb >= g.L[i].rb_begin) l = i;
   return l;
+}
+
+__device__ __forceinline__ LayerDev layer_at(const GroupDev& g, int i) {
+  return g.Lx ? g.Lx[i] : g.L[i];
 }
 
 }  // namespace gift

@@ -6,7 +6,7 @@
 // A = E[a a^T] is refreshed every 50 steps, "Load-bearing premise"; referee
 // report major comment 2 on Algorithm 1) and the rank (32, free-parameter
 // ledger).  Steps, in launch order; the covariance launches cover a group of
-// up to kMaxGroup inputs each, every later launch all inputs of the call
+// up to kRefGroup inputs each, every later launch all inputs of the call
 // (blockIdx.z, or .y, selects the input), so the small serial kernels of
 // different inputs run side by side:
 //   1. k_syrk: upper-triangle 128x128 tiles of X^T X on MFMA (bf16 inputs on
@@ -45,6 +45,7 @@ using rt4::pack_bytes;
 
 namespace {
 
+constexpr int kRefGroup = 16;     // inputs per covariance launch (descriptors inline)
 constexpr int kT = 256;              // threads per workgroup
 constexpr int kSyrkTile = 128;
 constexpr int kKStep = 32;           // tokens per SYRK step (fp32 activations)
@@ -154,14 +155,14 @@ struct RGroup {
   // bf16 covariance work list: input sy_in[k] owns workgroups
   // sy_begin[k] .. sy_begin[k + 1] - 1 (npairs x nsplit of them)
   int sy_n;
-  int sy_in[kMaxGroup];
-  int sy_begin[kMaxGroup];
-  RIn r[kMaxGroup];
+  int sy_in[kRefGroup];
+  int sy_begin[kRefGroup];
+  RIn r[kRefGroup];
 };
 
 // The kernels after the covariance (k_syrk_reduce onwards) run once over a
 // whole chain of inputs, so their latency-bound steps are paid once per call
-// rather than once per kMaxGroup inputs.  A chain of at most kMaxGroup inputs
+// rather than once per kRefGroup inputs.  A chain of at most kRefGroup inputs
 // takes its descriptors inline (RGroup); a longer one reads them from an
 // array in the workspace (RChain), written by k_put_desc from each group's
 // kernel arguments before the group's covariance.  Both expose r[i], w, eps
@@ -176,7 +177,7 @@ struct RChain {
 };
 // inputs of one chain launch: grid dimensions stay far below their limits
 constexpr int kChainMax = 1024;
-static_assert(kChainMax % kMaxGroup == 0, "chains hold whole covariance groups");
+static_assert(kChainMax % kRefGroup == 0, "chains hold whole covariance groups");
 static_assert(sizeof(RIn) % 4 == 0, "descriptors are copied as 32-bit words");
 static_assert(sizeof(RIn) == 176, "the workspace size query counts 176 bytes per descriptor");
 
@@ -361,7 +362,7 @@ __device__ __forceinline__ void syrk_stash(const SyrkRegs& r, uint16_t (*lds)[kK
 __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
   int k = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i)
+  for (int i = 1; i < kRefGroup; ++i)
     if (i < g.sy_n && (int)blockIdx.x >= g.sy_begin[i]) k = i;
   const RIn& R = g.r[g.sy_in[k]];
   const int local = (int)blockIdx.x - g.sy_begin[k];
@@ -1580,10 +1581,10 @@ void apply(const G& g, int which, const dim3& grid, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // host orchestration
 // ---------------------------------------------------------------------------
-// upper-triangle covariance tiles of the group (kMaxGroup inputs in call
+// upper-triangle covariance tiles of the group (kRefGroup inputs in call
 // order) that input i belongs to
 int64_t batch_pairs(const gift_refresh_input* in, int n, int i) {
-  const int b0 = i / kMaxGroup * kMaxGroup, b1 = n < b0 + kMaxGroup ? n : b0 + kMaxGroup;
+  const int b0 = i / kRefGroup * kRefGroup, b1 = n < b0 + kRefGroup ? n : b0 + kRefGroup;
   int64_t t = 0;
   for (int j = b0; j < b1; ++j) {
     const int64_t nb = (in[j].factor->d_in + kSyrkTile - 1) / kSyrkTile;
@@ -1594,7 +1595,7 @@ int64_t batch_pairs(const gift_refresh_input* in, int n, int i) {
 
 // the chain's descriptor array at the start of the workspace (only for
 // chains longer than one inline group)
-size_t desc_array_bytes(int n) { return n > kMaxGroup ? al((size_t)n * sizeof(RIn)) : 0; }
+size_t desc_array_bytes(int n) { return n > kRefGroup ? al((size_t)n * sizeof(RIn)) : 0; }
 
 size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int width) {
   size_t t = desc_array_bytes(n);
@@ -1659,9 +1660,9 @@ gift_status run_chain(const G& g, const RIn* hd, const gift_refresh_input* in, i
   if (kind) {  // block-diagonal factors: per-block eigensolve and packs
     if (kind == 32) k_blk_eig<32><<<dim3((unsigned)(maxd / 32), nc), kST, 0, st>>>(g);
     else k_blk_eig<64><<<dim3((unsigned)(maxd / 64), nc), kST, 0, st>>>(g);
-    for (int p0 = 0; p0 < nc; p0 += kMaxGroup) {
+    for (int p0 = 0; p0 < nc; p0 += kRefGroup) {
       PackGroup pg{};
-      for (int i = p0; i < nc && i < p0 + kMaxGroup; ++i) {
+      for (int i = p0; i < nc && i < p0 + kRefGroup; ++i) {
         pg.f[pg.n].U = in[i].factor->U;
         pg.f[pg.n].P = static_cast<uint4*>(in[i].factor->packs);
         pg.f[pg.n].d_in = in[i].factor->d_in;
@@ -1820,7 +1821,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       base += L.total;
     }
   }
-  RIn* dev_desc = n > kMaxGroup ? static_cast<RIn*>(ws) : nullptr;
+  RIn* dev_desc = n > kRefGroup ? static_cast<RIn*>(ws) : nullptr;
   auto group_of = [&](int b0, int nb) {
     RGroup g{};
     g.n = nb;
@@ -1832,10 +1833,10 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     return g;
   };
 
-  // 1. covariance, one group of kMaxGroup inputs per launch: bf16 inputs over
+  // 1. covariance, one group of kRefGroup inputs per launch: bf16 inputs over
   // a work list, fp32 inputs (<= 4 per launch) on a (pair, split, input) grid
-  for (int b0 = 0; b0 < n; b0 += kMaxGroup) {
-    const int nb = n - b0 < kMaxGroup ? n - b0 : kMaxGroup;
+  for (int b0 = 0; b0 < n; b0 += kRefGroup) {
+    const int nb = n - b0 < kRefGroup ? n - b0 : kRefGroup;
     RGroup g = group_of(b0, nb);
     if (dev_desc) k_put_desc<<<1, 256, 0, st>>>(g, dev_desc + b0);
     int wg = 0, maxpairs = 0, maxsplit = 0;
@@ -1850,7 +1851,7 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       }
     }
     if (wg) k_syrk_bf16<<<dim3(wg), kT, 0, st>>>(g);
-    int sel[kMaxGroup], ns = 0;
+    int sel[kRefGroup], ns = 0;
     for (int i = 0; i < nb; ++i)
       if (in[b0 + i].x_dtype == GIFT_DTYPE_F32) sel[ns++] = i;
     for (int k = 0; k < ns; k += 4) {

@@ -128,10 +128,6 @@ constexpr int kReduceThreads = kTR * 64;  // one thread per lane of each 16-row 
 constexpr int kHalves = kTR >= 2 ? 2 : 1;
 constexpr int kPerHalf = kTR / kHalves;
 constexpr int kRedRows = kPerHalf * 8;
-// Above this many tiles in a layer the per-tile amax partials are first
-// reduced by one workgroup (k_amax_final) instead of by every quantize
-// workgroup.
-constexpr int kPartialLimit = 2048;
 
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -1598,7 +1594,7 @@ __device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, in
 // quantize pass) and the slab's amax of |W| (to the layer's partials).
 // grid: one workgroup per row block of the group.
 __global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
-  const LayerDev L = gd.L[find_layer_rb(gd, blockIdx.x)];
+  const LayerDev L = layer_at(gd, find_layer_rb(gd, blockIdx.x));
   const int64_t rb = blockIdx.x - L.rb_begin;
   const Slab x = slab_ctx(L, rb);
   __shared__ float red[kSW][kTR * 8][64];
@@ -1645,9 +1641,30 @@ __global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
 
 #endif  // GIFT_TILE_RT == 4
 
+// descriptors of a large group into device memory, kPutLayers per launch
+// (the kernel argument holds them)
+constexpr int kPutLayers = 24;
+struct LayerBatch {
+  int n;
+  LayerDev L[kPutLayers];
+};
+__global__ __launch_bounds__(64) void k_put_layers(LayerBatch b, LayerDev* dst) {
+  if ((int)threadIdx.x < b.n) dst[threadIdx.x] = b.L[threadIdx.x];
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_put_layers(const LayerDev* host, int n, LayerDev* dst, hipStream_t s) {
+  for (int i0 = 0; i0 < n; i0 += kPutLayers) {
+    LayerBatch b{};
+    b.n = n - i0 < kPutLayers ? n - i0 : kPutLayers;
+    for (int i = 0; i < b.n; ++i) b.L[i] = host[i0 + i];
+    k_put_layers<<<dim3(1), dim3(64), 0, s>>>(b, dst + i0);
+  }
+  return hipGetLastError();
+}
+
 constexpr int kCPW = 1;  // chunks per wave of the tile kernels
 
 int64_t row_blocks(int64_t d_out) { return (d_out + kTileRows - 1) / kTileRows; }
@@ -1725,11 +1742,19 @@ hipError_t launch_flat_quantize(const GroupDev& g, int scaling, bool deq, bool w
 
 #if GIFT_TILE_RT == 4
 // per-tensor whiten + quantize of layers whose row blocks run as slabs:
-// k_slab_whiten (c' and one amax partial per row block), the layer amax
-// (k_amax_final for layers of more than kPartialLimit row blocks), and the
-// 64-row tile quantize pass on the slabs' c'
-hipError_t launch_slab_whiten_quantize(const GroupDev& g, bool write_w, hipStream_t s) {
-  k_slab_whiten<<<dim3(g.total_rb), dim3(kSlabThreads), 0, s>>>(g);
+// k_slab_whiten (c' and one amax partial per row block) runs once over all
+// of them -- its workgroups are long, so a launch per 16 layers would leave
+// the machine part idle at each launch's end -- then, per group of inline
+// descriptors, the layer amax (k_amax_final for layers of more than
+// kPartialLimit row blocks) and the 64-row tile quantize pass on the slabs'
+// c'.  The quantize workgroups are short: looking their layer up in device
+// memory would cost them more than the launch ends cost.
+hipError_t launch_slab_whiten(const GroupDev& all, hipStream_t s) {
+  k_slab_whiten<<<dim3(all.total_rb), dim3(kSlabThreads), 0, s>>>(all);
+  return hipGetLastError();
+}
+
+hipError_t launch_slab_quantize(const GroupDev& g, bool write_w, hipStream_t s) {
   bool tall = false;
   for (int i = 0; i < g.n; ++i) tall |= g.L[i].n_part > kPartialLimit;
   if (tall) k_amax_final<<<dim3(g.n), dim3(kThreads), 0, s>>>(g);

@@ -10,7 +10,8 @@ pass reduces itself.  Protocol as for the tile kernels: W within 1e-5 of
 the oracle, codes and scale bit-exact against the oracle's encoding of the
 device's W, G^ within 1e-5 of the oracle's un-whitening of the device's
 codes, error sums within 1e-12.  A grouped call gives every layer the
-results of its own call (the slab / tile choice depends on the layer alone).
+results of its own call (the slab / tile choice depends on the layer alone),
+also when the slab pass runs over more layers than one launch holds inline.
 """
 
 import numpy as np
@@ -90,3 +91,39 @@ def test_slab_nonfinite_and_zero():
             assert fl == og.FLAG_ZERO_AMAX and not np.any(host(L.q)) and not np.any(host(L.G_hat))
         else:
             assert fl & og.FLAG_NONFINITE and np.all(np.isnan(host(L.G_hat)))
+
+
+def test_slab_group_beyond_inline_descriptors():
+    """More slab layers than a launch holds inline (the slab pass then reads
+    its layer descriptors from the workspace), mixed with tile-path and
+    Euclidean layers: every layer's codes, scale and reconstruction are
+    bit-identical to those of its own call, and the flags to the OR of the
+    single calls' flags."""
+    say("slab group of 20 + 3 other layers vs alone")
+    fa, Ua = _cheap_factor(1024, seed=21)
+    fb, Ub = _cheap_factor(512, seed=22)
+    da, db = upload_factor(fa), upload_factor(fb)
+    rng = np.random.default_rng(23)
+    specs = []
+    for k in range(20):
+        d_in, U, f = (512, Ub, db) if k % 2 else (1024, Ua, da)
+        specs.append((_anisotropic(SLAB_MIN // d_in + 37 * k, d_in, U, seed=100 + k), f))
+        if k in (4, 10, 16):  # a tile-path layer, a Euclidean layer, a tile-path layer
+            small = _anisotropic(300 + k, 512, Ub, seed=200 + k)
+            specs.append((small, None if k == 10 else db))
+    assert sum(1 for G, f in specs if f is not None and G.size >= SLAB_MIN) == 20
+    group = [fg.Layer(to_dev(G), factor=f) for G, f in specs]
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fg.gift_whiten_quantize(group, flags=flags)
+    fg.gift_dequant_unwhiten(group)
+    want_flags = 0
+    for i, (G, f) in enumerate(specs):
+        one = fg.Layer(to_dev(G), factor=f)
+        fl1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        fg.gift_whiten_quantize([one], flags=fl1)
+        fg.gift_dequant_unwhiten([one])
+        want_flags |= int(host(fl1)[0])
+        assert np.array_equal(host(group[i].q), host(one.q)), i
+        assert host(group[i].inv_scale)[0] == host(one.inv_scale)[0], i
+        assert np.array_equal(host(group[i].G_hat).view(np.uint32), host(one.G_hat).view(np.uint32)), i
+    assert int(host(flags)[0]) == want_flags
