@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-quality", action="store_true")
+    p.add_argument("--serial-refresh", action="store_true",
+                   help="run each step's refresh share before its round trip on the same stream "
+                        "(default: on a second stream into the next interval's factor set)")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--counters", action="store_true",
                    help="for runs under hardware-counter collection: axis-aligned spectra "
@@ -247,6 +250,16 @@ def main():
     shares = [[items[i] for i in sh] for sh in refresh_shares(len(items))]
     ws_share = torch.empty(max(max(fg.gift_refresh_group_workspace_bytes(sh) for sh in shares if sh),
                                256), dtype=torch.uint8, device=dev)
+    # Overlapped refresh: a second factor set, so the shares of one 50-step
+    # interval build the factors of the next while the round trip reads the
+    # current ones.
+    overlap = not args.serial_refresh
+    if overlap:
+        factors_b = {s.name: fg.Factor(s.d_in, device=dev) for s in w.inputs}
+        items_b = [dict(X=it["X"], factor=factors_b[s.name], seed=it["seed"])
+                   for it, s in zip(items, w.inputs)]
+        fg.gift_refresh_factors(items_b, ws=ws_all)
+        shares_b = [[items_b[i] for i in sh] for sh in refresh_shares(len(items_b))]
 
     layer_factor = [factors[l.input] if l.input is not None else None for l in w.layers]
     selected = ([i for i, f in enumerate(layer_factor) if f is not None] if select_k is None
@@ -259,6 +272,9 @@ def main():
         el = [fg.Layer(G) for i, G in enumerate(grads) if i not in sel]
         ring.append((gl, el))
     gl0, el0 = ring[0]
+    if overlap:  # the same gradients and payload buffers, whitened with the second set
+        ring_b = [([fg.Layer(L.G, factor=factors_b[w.layers[i].input], q=L.q, G_hat=L.G_hat)
+                    for L, i in zip(gl, sorted(sel))], el) for gl, el in ring]
 
     def ws_for(op, layers, scaling=fg.SCALE_TENSOR):
         nb = fg.gift_group_workspace_bytes(op, layers, scaling) if layers else 0
@@ -302,13 +318,32 @@ def main():
         slot_graphs.append(capture([c for _, c in calls]))
         for name, c in calls:
             entry_graphs.setdefault(name, []).append(capture([c]))
+    slot_graphs_b = [capture([c for _, c in entry_calls(gl, el)]) for gl, el in ring_b] \
+        if overlap else None
     torch.cuda.synchronize()
+    main_stream = torch.cuda.current_stream()
+    side_stream = torch.cuda.Stream() if overlap else None
 
     def step(s):
-        share = shares[s % REFRESH_EVERY]
+        k, ph = divmod(s, REFRESH_EVERY)
+        if not overlap:
+            if shares[ph]:
+                fg.gift_refresh_factors(shares[ph], ws=ws_share)
+            slot_graphs[s % len(ring)][0].replay()
+            return
+        # interval k whitens with set k % 2 and refreshes the other one on the
+        # side stream; at an interval's first step the round trip waits for
+        # the shares that built its set, and the shares wait for the round
+        # trips that read the set they overwrite
+        cur = k % 2
+        if ph == 0 and s > 0:
+            main_stream.wait_stream(side_stream)
+            side_stream.wait_stream(main_stream)
+        share = (shares_b if cur == 0 else shares)[ph]
         if share:
-            fg.gift_refresh_factors(share, ws=ws_share)
-        slot_graphs[s % len(ring)][0].replay()
+            with torch.cuda.stream(side_stream):
+                fg.gift_refresh_factors(share, ws=ws_share)
+        (slot_graphs_b if cur == 1 else slot_graphs)[s % len(ring)][0].replay()
 
     for s in range(args.warmup):
         step(s)
@@ -419,8 +454,11 @@ def main():
                    "whitened_layers": len(gl0), "inputs": len(w.inputs),
                    "gradient_elements": elems,
                    "refresh_charge": "%d input refreshes in the %d timed steps (%.3f of all "
-                                     "inputs per step)" % (refreshed, args.steps,
-                                                          refreshed / args.steps / len(w.inputs))},
+                                     "inputs per step), %s" % (
+                                         refreshed, args.steps, refreshed / args.steps / len(w.inputs),
+                                         "on a second stream, overlapping the round trip, into the "
+                                         "factor set of the next 50-step interval" if overlap else
+                                         "before each step's round trip on the same stream")},
         "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
         "roundtrip_only_gbps": round(4 * gift_elems / rt / 1e9, 2) if rt > 0 else None,
         "roundtrip_hbm_frac": round(10 * gift_elems / rt / 1e9 / HBM_PEAK_GBS, 4) if rt > 0 else None,
