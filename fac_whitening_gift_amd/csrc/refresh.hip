@@ -63,23 +63,35 @@ constexpr double kJacobiTol = 1e-15;
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 struct SyrkPlan {
-  int nb, npairs, nsplit;
+  int nb, npairs, nsplit;  // 128 x 128 tiles (partials, k_syrk_reduce, fp32 kernel)
   int64_t chunk;
 };
 
-// Token split of the covariance tiles: a launch covers the inputs of one
-// group (batch_pairs upper-triangle tiles in all), and each tile's tokens are
-// split so the launch holds about kSyrkTarget workgroups (two per CU, twice
-// over), with at least 8 steps per workgroup.
-constexpr int64_t kSyrkTarget = 1024;
+// upper-triangle tiles of a d-wide covariance: 128 x 128 (fp32 inputs, and
+// the partial tiles of every input) or 256 x 256 (the bf16 kernel)
+int64_t tile_pairs(int64_t d, int tile) {
+  const int64_t nb = (d + tile - 1) / tile;
+  return nb * (nb + 1) / 2;
+}
+constexpr int kCovTileHost = 256;
 
-SyrkPlan syrk_plan(int64_t d, int64_t n, int64_t batch_pairs) {
+// Token split of the covariance tiles: a launch covers the inputs of one
+// group (batch_tiles upper-triangle tiles of the input's kernel in all), and
+// each tile's tokens are split so the launch holds about kSyrkTarget
+// workgroups (fp32: 128-tiles, two per CU, twice over; bf16: 256-tiles, one
+// per CU, twice over), with at least 8 steps of 64 tokens per workgroup.
+constexpr int64_t kSyrkTarget = 1024;
+constexpr int64_t kCovTarget = 512;
+
+SyrkPlan syrk_plan(int64_t d, int64_t n, int64_t batch_tiles, int x_dtype) {
   SyrkPlan p;
   p.nb = (int)((d + kSyrkTile - 1) / kSyrkTile);
   p.npairs = p.nb * (p.nb + 1) / 2;
+  const bool bf16 = x_dtype == GIFT_DTYPE_BF16;
+  const int64_t own = bf16 ? tile_pairs(d, kCovTileHost) : p.npairs;
   const int64_t steps = (n + kKStepB - 1) / kKStepB;
-  const int64_t tiles = batch_pairs > p.npairs ? batch_pairs : p.npairs;
-  const int64_t want = (kSyrkTarget + tiles - 1) / tiles;
+  const int64_t tiles = batch_tiles > own ? batch_tiles : own;
+  const int64_t want = ((bf16 ? kCovTarget : kSyrkTarget) + tiles - 1) / tiles;
   const int64_t maxs = steps / 8 > 0 ? steps / 8 : 1;      // at least 8 K-steps each
   int64_t s = want < maxs ? want : maxs;
   if (s < 1) s = 1;
@@ -101,8 +113,8 @@ bool needs_partials(int x_dtype, const SyrkPlan& p) {
   return !(x_dtype == GIFT_DTYPE_BF16 && p.nsplit == 1);
 }
 
-WsLayout ws_layout(int64_t d, int64_t n, int w, int64_t batch_pairs, int x_dtype) {
-  const SyrkPlan p = syrk_plan(d, n, batch_pairs);
+WsLayout ws_layout(int64_t d, int64_t n, int w, int64_t batch_tiles, int x_dtype) {
+  const SyrkPlan p = syrk_plan(d, n, batch_tiles, x_dtype);
   WsLayout L;
   size_t o = 0;
   L.A = o; o += al((size_t)d * d * 4);
@@ -300,166 +312,193 @@ __device__ __forceinline__ void syrk_load_tile(float (*lds)[kKStep + 4], const f
         make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-// bf16 SYRK with a double-buffered LDS tile: the next 64-token step is
-// loaded into registers while the MFMAs of the current one run, then stored
-// to the other buffer; one barrier per step.
-struct SyrkBuf {
-  uint16_t a[kSyrkTile][kKStepB + 8];  // row = 72 bf16 = 144 B (one column of X)
-  uint16_t b[kSyrkTile][kKStepB + 8];
-};
-
-// thread t: columns c0 + 2(t % 64), +1 for tokens n0 + 16(t / 64) .. +15
-struct SyrkRegs {
-  uint32_t v[16];
-};
-
-// The tokens of one step are a raw buffer that starts at the step's first
-// token and ends at the workgroup's last (size 0 past it): a lane's load of
-// token row 16 tg + s of the step sits at byte s 2d + voff, voff =
-// (16 tg d + col) 2, and rows past the range read as zero in the buffer unit,
-// so the loads need no branch and can not leave X.  Columns at or beyond d
-// are zeroed by colok.
+// bf16 covariance on 256 x 256 tiles.  The tokens of a step (64 rows of X,
+// token-major, as stored) are copied into LDS by the buffer unit itself (LDS
+// DMA: buffer_load_dwordx4 ... lds, 16 bytes per lane at m0 + 16 lane), and
+// gfx950's transposed LDS read (ds_read_b64_tr_b16) turns four token rows of
+// sixteen features into each lane's MFMA operand, so X needs no transposing
+// pass through registers.  LDS: two stages of [A | B] operand tiles, 64
+// tokens x 256 features each (128 KB); one workgroup per CU, 8 waves, wave
+// (wr, wc) accumulates rows 128 wr .. +127 and columns 64 wc .. +63 of the
+// tile on v_mfma_f32_16x16x32_bf16.
+//
+// LDS layout of an operand tile: token row t at t * 512 bytes; its 32
+// 16-byte chunks (8 features each) stored at chunk c ^ cov_swz(t).  A
+// transposed read serves each 16-lane group with four token rows of one
+// 16-feature block; with this swizzle the sixteen rows of one read fall in
+// eight distinct 32-byte bank windows, two rows each.
+constexpr int kCovTile = 256;
+static_assert(kCovTile == kCovTileHost, "one tile size on both sides");
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data format
+constexpr int kCovK = 64;                  // tokens per step
+constexpr int kCovRow = 512;               // LDS bytes per token row of one operand
+constexpr int kCovOp = kCovK * kCovRow;    // one operand tile of one stage (32 KB)
+constexpr int kCovThreads = 512;
+constexpr int kCovDma = 4;                 // LDS DMA loads per thread per operand and step
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t syrk_rsrc(const uint16_t* X, int64_t n0,
-                                                            int64_t n_end, int d) {
-  const int64_t rows = n_end > n0 ? n_end - n0 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X + (n_end > n0 ? n0 : n_end) * d),
-                                           (short)0, (int)((uint32_t)rows * 2u * (uint32_t)d),
-                                           (int)kRawBufferWord3);
+__device__ __forceinline__ int cov_swz(int t) {
+  return 2 * ((t & 3) + 4 * (((t >> 3) + ((t >> 2) & 1)) & 1));
 }
 
-__device__ __forceinline__ void syrk_fetch(SyrkRegs& r, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                           uint32_t rowbytes, bool colok) {
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + (uint32_t)s * rowbytes, 0, 0);
-    r.v[s] = colok ? v : 0u;
-  }
+// 16 bytes per lane from the raw buffer (voff + soff) into LDS at m0 + 16
+// lane.  Written in asm so the compiler does not make every LDS read wait
+// for all LDS DMA in flight (it cannot tell the two stages apart): the kernel
+// waits with explicit vmcnt counts before its barriers.  The instruction
+// writes no VGPR; m0 is set in the same statement.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void cov_dma(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff,
+                                        uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+template <int kOff>
+__device__ __forceinline__ v4i16 cov_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(uintptr_t)(addr + kOff));
 }
 
-__device__ __forceinline__ void syrk_stash(const SyrkRegs& r, uint16_t (*lds)[kKStepB + 8]) {
-  const int cp = threadIdx.x & 63, tg = threadIdx.x >> 6;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t* v = r.v + 8 * h;
-    uint4 lo, hi;
-    lo.x = (v[0] & 0xffffu) | (v[1] << 16);
-    lo.y = (v[2] & 0xffffu) | (v[3] << 16);
-    lo.z = (v[4] & 0xffffu) | (v[5] << 16);
-    lo.w = (v[6] & 0xffffu) | (v[7] << 16);
-    hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
-    hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
-    hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
-    hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
-    *reinterpret_cast<uint4*>(&lds[2 * cp][16 * tg + 8 * h]) = lo;
-    *reinterpret_cast<uint4*>(&lds[2 * cp + 1][16 * tg + 8 * h]) = hi;
-  }
-}
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; the fields not waited on at their maximum)
+constexpr int kWaitVm8 = 0x0F78;      // vmcnt(8)
+constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;    // lgkmcnt(0)
+static_assert(2 * kCovDma == 8, "vmcnt(8): the DMA loads of one step");
 
-// grid: one workgroup per (tile, token range) of every bf16 input of the
-// group, tiles of one token range consecutive
-__global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
+// grid: one workgroup per (256-tile, token range) of every bf16 input of
+// the group, the tiles of one token range consecutive
+__global__ __launch_bounds__(kCovThreads, 1) void k_syrk_bf16(RGroup g) {
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kCovOp];  // A0 A1 B0 B1
   int k = 0;
 #pragma unroll
   for (int i = 1; i < kRefGroup; ++i)
     if (i < g.sy_n && (int)blockIdx.x >= g.sy_begin[i]) k = i;
   const RIn& R = g.r[g.sy_in[k]];
   const int local = (int)blockIdx.x - g.sy_begin[k];
-  const int split = local / R.npairs;
-  __shared__ SyrkBuf sb[2];
-  int bi, bj;
-  band_tile(local - split * R.npairs, R.npairs, R.nb, bi, bj);
-  const int pair = pair_index(bi, bj, R.nb);
   const int d = R.d;
-  const int ci0 = bi * kSyrkTile, cj0 = bj * kSyrkTile;
+  const int nb2 = (d + kCovTile - 1) / kCovTile, npairs2 = nb2 * (nb2 + 1) / 2;
+  const int split = local / npairs2;
+  int bi, bj;
+  band_tile(local - split * npairs2, npairs2, nb2, bi, bj);
+  const int fi = bi * kCovTile, fj = bj * kCovTile;
   const int64_t n_begin = (int64_t)split * R.chunk;
   const int64_t n_end = min(R.N, n_begin + R.chunk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wi = wave >> 1, wj = wave & 1;
-  const int r16 = lane & 15, gq = lane >> 4;
-  const uint16_t* X = static_cast<const uint16_t*>(R.X);
-  f32x4 acc[4][4];
+  const int steps = (int)((n_end - n_begin + kCovK - 1) / kCovK);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = w >> 2, wc = w & 3;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  // The token range as a raw buffer: reads past its end return zero, so a
+  // ragged last step needs no branch and no load leaves X.  Features at or
+  // beyond d (the last tile column of a width that is not a multiple of
+  // 256) read whatever follows in the buffer; they only reach rows and
+  // columns of the tile that are never written.
+  // (wave-uniform values, made scalar explicitly: the DMA takes the
+  // resource in SGPRs)
+  const uint64_t xa = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(R.X) + n_begin * d);
+  const uint64_t xs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(xa >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)xa);
+  const int nrec = __builtin_amdgcn_readfirstlane((int)((uint32_t)(n_end - n_begin) * 2u * (uint32_t)d));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(xs), (short)0, nrec, (int)kRawBufferWord3);
+  // DMA: wave w, load i: token rows 8 w + 2 i + (lane >> 5) of the step,
+  // LDS chunk lane & 31 holding feature chunk (lane & 31) ^ cov_swz(row)
+  uint32_t voa[kCovDma], vob[kCovDma];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int steps = (int)((n_end - n_begin + kKStepB - 1) / kKStepB);
-  // Three register sets: while step st is multiplied out of LDS, the tokens
-  // of step st + 1 (issued two steps earlier) are stashed into the other LDS
-  // buffer and those of steps st + 2 and st + 3 are in flight, so a load has
-  // three steps of MFMA work to arrive.  Set k holds the steps st with
-  // st % 3 == k; LDS buffer b the steps with st % 2 == b.
-  SyrkRegs ra[3], rb[3];
-  const int cpl = 2 * (threadIdx.x & 63), tgl = threadIdx.x >> 6;
-  const uint32_t rowbytes = 2u * (uint32_t)d;
-  const uint32_t va = (uint32_t)(16 * tgl) * rowbytes + 2u * (uint32_t)(ci0 + cpl);
-  const uint32_t vb = (uint32_t)(16 * tgl) * rowbytes + 2u * (uint32_t)(cj0 + cpl);
-  const bool oka = ci0 + cpl < d, okb = cj0 + cpl < d;
-  if (steps > 0) {
-    const __amdgpu_buffer_rsrc_t r0 = syrk_rsrc(X, n_begin, n_end, d);
-    const __amdgpu_buffer_rsrc_t r1 = syrk_rsrc(X, n_begin + kKStepB, n_end, d);
-    const __amdgpu_buffer_rsrc_t r2 = syrk_rsrc(X, n_begin + 2 * kKStepB, n_end, d);
-    syrk_fetch(ra[0], r0, va, rowbytes, oka);
-    syrk_fetch(rb[0], r0, vb, rowbytes, okb);
-    syrk_fetch(ra[1], r1, va, rowbytes, oka);
-    syrk_fetch(rb[1], r1, vb, rowbytes, okb);
-    syrk_fetch(ra[2], r2, va, rowbytes, oka);
-    syrk_fetch(rb[2], r2, vb, rowbytes, okb);
-    syrk_stash(ra[0], sb[0].a);
-    syrk_stash(rb[0], sb[0].b);
+  for (int i = 0; i < kCovDma; ++i) {
+    const int t = 8 * w + 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ cov_swz(t);
+    voa[i] = ((uint32_t)t * (uint32_t)d + (uint32_t)(fi + 8 * c)) * 2u;
+    vob[i] = ((uint32_t)t * (uint32_t)d + (uint32_t)(fj + 8 * c)) * 2u;
   }
-  __syncthreads();
-  // step st: registers k = st % 3, LDS buffer b = st % 2
-  auto step = [&](int st, auto K, auto B) {
-    constexpr int k = decltype(K)::value, b = decltype(B)::value;
-    constexpr int k1 = (k + 1) % 3;
-    const SyrkBuf& cur = sb[b];
+  const uint32_t stepb = (uint32_t)kCovK * (uint32_t)d * 2u;
+  auto issue = [&](int buf, int st) {
+    const uint32_t soff = (uint32_t)st * stepb;
 #pragma unroll
-    for (int ks = 0; ks < kKStepB / 32; ++ks) {
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        fa[t] = *reinterpret_cast<const bf16x8*>(&cur.a[64 * wi + 16 * t + r16][32 * ks + 8 * gq]);
-        fb[t] = *reinterpret_cast<const bf16x8*>(&cur.b[64 * wj + 16 * t + r16][32 * ks + 8 * gq]);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[c], acc[a][c], 0, 0, 0);
+    for (int i = 0; i < kCovDma; ++i) {
+      const uint32_t row = (uint32_t)(8 * w + 2 * i) * kCovRow;
+      cov_dma(rs, lds0 + (uint32_t)buf * kCovOp + row, voa[i], soff);
+      cov_dma(rs, lds0 + (uint32_t)(2 + buf) * kCovOp + row, vob[i], soff);
     }
-    SyrkBuf& nxt = sb[b ^ 1];
-    syrk_stash(ra[k1], nxt.a);
-    syrk_stash(rb[k1], nxt.b);
-    // set k is free again: the tokens of step st + 3
-    const __amdgpu_buffer_rsrc_t rn = syrk_rsrc(X, n_begin + (int64_t)(st + 3) * kKStepB, n_end, d);
-    syrk_fetch(ra[k], rn, va, rowbytes, oka);
-    syrk_fetch(rb[k], rn, vb, rowbytes, okb);
-    __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  for (int st = 0; st < steps; st += 6) {
-    step(st, I0{}, I0{});
-    if (st + 1 < steps) step(st + 1, I1{}, I1{});
-    if (st + 2 < steps) step(st + 2, I2{}, I0{});
-    if (st + 3 < steps) step(st + 3, I0{}, I1{});
-    if (st + 4 < steps) step(st + 4, I1{}, I0{});
-    if (st + 5 < steps) step(st + 5, I2{}, I1{});
+  // transposed-read addresses: lane (gq, s) of a read takes token row
+  // 8 gq + 4 r + (s >> 2) (+ 32 per half step) and features 4 (s & 3) .. +3
+  // of a 16-feature block
+  const int gq = lane >> 4, s = lane & 15, q = s >> 2;
+  uint32_t pa[2][8], pb[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = 8 * gq + 4 * r + q;
+    const int v = q + 4 * ((gq + r) & 1);  // cov_swz(t) / 2
+    const uint32_t base = lds0 + (uint32_t)t * kCovRow + 16u * ((s & 3) >> 1) + 8u * (s & 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pa[r][i] = base + 32u * (uint32_t)((8 * wr + i) ^ v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb[r][j] = base + 2u * kCovOp + 32u * (uint32_t)((4 * wc + j) ^ v);
   }
-  // D layout: lane holds rows 4gq..4gq+3 of column r16 of each 16x16 tile
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 32 tokens of stage b: B operands (4 column blocks), A operands (8 row
+  // blocks), 32 MFMAs
+  auto half = [&](auto OFF) {
+    constexpr int o = decltype(OFF)::value;
+    bf16x8 fa[8], fb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[j] = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(cov_tr<o>(pb[0][j]), cov_tr<o>(pb[1][j]), 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      fa[i] = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(cov_tr<o>(pa[0][i]), cov_tr<o>(pa[1][i]), 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // step st in stage b: wait for its DMA (the next step's may still be in
+  // flight), barrier, two halves, barrier (every wave is done with stage b),
+  // then the DMA of step st + 2 into stage b
+  auto step = [&](auto B, int st) {
+    constexpr int b = decltype(B)::value;
+    if (st + 1 < steps) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    half(std::integral_constant<int, b * kCovOp>{});
+    half(std::integral_constant<int, b * kCovOp + 32 * kCovRow>{});
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + 2 < steps) issue(b, st + 2);
+  };
+  if (steps > 0) issue(0, 0);
+  if (steps > 1) issue(1, 1);
+  for (int st = 0; st < steps; st += 2) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < steps) step(std::integral_constant<int, 1>{}, st + 1);
+  }
+  // D layout: lane holds rows 4 gq .. 4 gq + 3 of column s of each 16x16 tile
   if (R.part) {
-    float* out = R.part + ((size_t)split * R.npairs + pair) * kSyrkTile * kSyrkTile;
+    // partials in the layout of the 128 x 128 tiles (k_syrk_reduce): this
+    // wave's 128 x 64 block lies in 128-tile (2 bi + wr, 2 bj + wc / 2)
+    const int ti = 2 * bi + wr, tj = 2 * bj + (wc >> 1);
+    if (ti > tj || tj >= R.nb) return;
+    float* out = R.part + ((size_t)split * R.npairs + pair_index(ti, tj, R.nb)) * kSyrkTile * kSyrkTile;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 64 * wi + 16 * a + 4 * gq + i, c = 64 * wj + 16 * b + r16;
-          out[r * kSyrkTile + c] = acc[a][b][i];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * gq + e, c = 64 * (wc & 1) + 16 * j + s;
+          out[r * kSyrkTile + c] = acc[i][j][e];
         }
     return;
   }
@@ -469,24 +508,23 @@ __global__ __launch_bounds__(kT, 2) void k_syrk_bf16(RGroup g) {
   const bool diag = bi == bj;
   const float fn = (float)R.N;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r0 = 64 * wi + 16 * a + 4 * gq, c = 64 * wj + 16 * b + r16;
-      const int i0 = ci0 + r0, j = cj0 + c;
-      if (i0 >= d || j >= d) continue;  // d % 16 == 0: rows i0 .. i0 + 3 are all in or all out
+    for (int j = 0; j < 4; ++j) {
+      const int i0 = fi + 128 * wr + 16 * i + 4 * gq, jj = fj + 64 * wc + 16 * j + s;
+      if (i0 >= d || jj >= d) continue;  // d % 16 == 0: rows i0 .. i0 + 3 are all in or all out
       float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[a][b][i] / fn;
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] / fn;
       if (!diag) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.A[(int64_t)(i0 + i) * d + j] = v[i];
-        *reinterpret_cast<float4*>(R.A + (int64_t)j * d + i0) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int e = 0; e < 4; ++e) R.A[(int64_t)(i0 + e) * d + jj] = v[e];
+        *reinterpret_cast<float4*>(R.A + (int64_t)jj * d + i0) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (r0 + i <= c) R.A[(int64_t)(i0 + i) * d + j] = v[i];
-          if (r0 + i < c) R.A[(int64_t)j * d + i0 + i] = v[i];
+        for (int e = 0; e < 4; ++e) {
+          if (i0 + e <= jj) R.A[(int64_t)(i0 + e) * d + jj] = v[e];
+          if (i0 + e < jj) R.A[(int64_t)jj * d + i0 + e] = v[e];
         }
       }
     }
@@ -1581,14 +1619,16 @@ void apply(const G& g, int which, const dim3& grid, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // host orchestration
 // ---------------------------------------------------------------------------
-// upper-triangle covariance tiles of the group (kRefGroup inputs in call
-// order) that input i belongs to
-int64_t batch_pairs(const gift_refresh_input* in, int n, int i) {
+// covariance tiles of the launch that input i belongs to (its group of
+// kRefGroup inputs in call order): for a bf16 input the 256-tiles of the
+// group's bf16 inputs, for an fp32 input the 128-tiles of all its inputs
+int64_t batch_tiles(const gift_refresh_input* in, int n, int i) {
   const int b0 = i / kRefGroup * kRefGroup, b1 = n < b0 + kRefGroup ? n : b0 + kRefGroup;
+  const bool bf16 = in[i].x_dtype == GIFT_DTYPE_BF16;
   int64_t t = 0;
   for (int j = b0; j < b1; ++j) {
-    const int64_t nb = (in[j].factor->d_in + kSyrkTile - 1) / kSyrkTile;
-    t += nb * (nb + 1) / 2;
+    if (bf16 && in[j].x_dtype != GIFT_DTYPE_BF16) continue;
+    t += tile_pairs(in[j].factor->d_in, bf16 ? kCovTileHost : kSyrkTile);
   }
   return t;
 }
@@ -1602,15 +1642,15 @@ size_t refresh_group_workspace_bytes(const gift_refresh_input* in, int n, int wi
   for (int i = 0; i < n; ++i)
     if (!in[i].factor || in[i].factor->d_in < 1 || in[i].n_tokens < 1) return 0;
   for (int i = 0; i < n; ++i)
-    t += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_pairs(in, n, i),
+    t += ws_layout(in[i].factor->d_in, in[i].n_tokens, width, batch_tiles(in, n, i),
                    in[i].x_dtype).total;
   return t;
 }
 
 size_t refresh_workspace_bytes(int64_t d_in, int64_t n_tokens, int x_dtype, int width) {
   if (d_in < 1 || n_tokens < 1 || width < 1) return 0;
-  const int64_t nb = (d_in + kSyrkTile - 1) / kSyrkTile;
-  return ws_layout(d_in, n_tokens, width, nb * (nb + 1) / 2, x_dtype).total;
+  const int64_t own = tile_pairs(d_in, x_dtype == GIFT_DTYPE_BF16 ? kCovTileHost : kSyrkTile);
+  return ws_layout(d_in, n_tokens, width, own, x_dtype).total;
 }
 
 gift_status draw_sketch(float* out, int64_t d, int width, uint64_t seed, hipStream_t st,
@@ -1787,9 +1827,9 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
     for (int i = 0; i < n; ++i) {
       const gift_refresh_input& r = in[i];
       const int d = r.factor->d_in;
-      const int64_t bp = batch_pairs(in, n, i);
+      const int64_t bp = batch_tiles(in, n, i);
       const WsLayout L = ws_layout(d, r.n_tokens, width, bp, r.x_dtype);
-      const SyrkPlan p = syrk_plan(d, r.n_tokens, bp);
+      const SyrkPlan p = syrk_plan(d, r.n_tokens, bp, r.x_dtype);
       RIn& x = desc[i];
       x = RIn{};
       x.X = r.X;
@@ -1847,10 +1887,10 @@ gift_status refresh_factors(const gift_refresh_input* in, int n, float damp_eps,
       if (in[b0 + i].x_dtype == GIFT_DTYPE_BF16) {
         g.sy_in[g.sy_n] = i;
         g.sy_begin[g.sy_n++] = wg;
-        wg += g.r[i].npairs * g.r[i].nsplit;
+        wg += (int)tile_pairs(g.r[i].d, kCovTileHost) * g.r[i].nsplit;
       }
     }
-    if (wg) k_syrk_bf16<<<dim3(wg), kT, 0, st>>>(g);
+    if (wg) k_syrk_bf16<<<dim3(wg), kCovThreads, 0, st>>>(g);
     int sel[kRefGroup], ns = 0;
     for (int i = 0; i < nb; ++i)
       if (in[b0 + i].x_dtype == GIFT_DTYPE_F32) sel[ns++] = i;

@@ -220,8 +220,8 @@ __device__ __forceinline__ void store_code_tile(const LayerDev& L, const Tile& x
     const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
     const int64_t row = x.rb * kTileRows + r;
     if (e < kN && row < L.d_out && (qd >> 1) < nvalid)
-      *reinterpret_cast<uint4*>(L.q + row * L.d_in + kChunk * cfirst + 16 * qd) =
-          *reinterpret_cast<const uint4*>(&ct.w[r][4 * qd]);
+      st_q16(L.q + row * L.d_in + kChunk * cfirst + 16 * qd,
+             *reinterpret_cast<const uint4*>(&ct.w[r][4 * qd]));
   }
 }
 
@@ -247,7 +247,7 @@ __device__ __forceinline__ void load_code_pieces(const LayerDev& L, const Tile& 
     const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
     const int64_t row = x.rb * kTileRows + r;
     const bool in = e < CodePieces<kCPW>::kPieces && row < L.d_out && (qd >> 1) < nvalid;
-    pc.v[h] = in ? *reinterpret_cast<const uint4*>(L.q + row * L.d_in + kChunk * cfirst + 16 * qd)
+    pc.v[h] = in ? ld_q16(L.q + row * L.d_in + kChunk * cfirst + 16 * qd)
                  : make_uint4(0u, 0u, 0u, 0u);
   }
 }
@@ -295,8 +295,8 @@ __device__ __forceinline__ void store_mx_tile(const LayerDev& L, const Tile& x,
     const int r = e / kQ, qd = e % kQ;
     const int64_t row = x.rb * kTileRows + r;
     if (row < L.d_out && qd < nvalid) {
-      *reinterpret_cast<uint4*>(L.q + row * (L.d_in / 2) + 16 * (cfirst + qd)) =
-          *reinterpret_cast<const uint4*>(&mt.c[r][8 * qd]);
+      st_q16(L.q + row * (L.d_in / 2) + 16 * (cfirst + qd),
+             *reinterpret_cast<const uint4*>(&mt.c[r][8 * qd]));
       reinterpret_cast<uint8_t*>(L.inv)[row * nblk + cfirst + qd] = mt.s[r][qd];
     }
   }
@@ -315,7 +315,7 @@ __device__ __forceinline__ void load_mx_tile(const LayerDev& L, const Tile& x, M
     const int e = threadIdx.x + h * kTileThreads, r = e / kQ, qd = e % kQ;
     const int64_t row = x.rb * kTileRows + r;
     const bool in = e < kTileRows * kQ && row < L.d_out && qd < nvalid;
-    v[h] = in ? *reinterpret_cast<const uint4*>(L.q + row * (L.d_in / 2) + 16 * (cfirst + qd))
+    v[h] = in ? ld_q16(L.q + row * (L.d_in / 2) + 16 * (cfirst + qd))
               : make_uint4(0u, 0u, 0u, 0u);
     sc[h] = in ? reinterpret_cast<const uint8_t*>(L.inv)[row * nblk + cfirst + qd] : 127u;
   }
@@ -365,18 +365,19 @@ __device__ __forceinline__ int rank_of(int k, int g) { return 16 * (k >> 2) + 4 
 
 // gradient values of one chunk for this lane and 16-row tile: columns
 // 32c + 4g .. +3 (t = 0) and 32c + 16 + 4g .. +3 (t = 1) of its row
+template <bool kNT = GIFT_NT_G>
 __device__ __forceinline__ void load_gc(const LayerDev& L, int64_t row, int g, int c,
                                         float4 (&v)[2]) {
   const float* p = L.G + row * L.d_in + kChunk * c + 4 * g;
-  v[0] = *reinterpret_cast<const float4*>(p);
-  v[1] = *reinterpret_cast<const float4*>(p + 16);
+  v[0] = ld_g<kNT>(p);
+  v[1] = ld_g<kNT>(p + 16);
 }
 
 __device__ __forceinline__ void load_qc(const LayerDev& L, int64_t row, int g, int c,
                                         uint32_t (&v)[2]) {
   const uint8_t* p = L.q + row * L.d_in + kChunk * c + 4 * g;
-  v[0] = *reinterpret_cast<const uint32_t*>(p);
-  v[1] = *reinterpret_cast<const uint32_t*>(p + 16);
+  v[0] = ld_q4(p);
+  v[1] = ld_q4(p + 16);
 }
 
 // first product on MXFP4 values (code value * 2^e is exact in bf16)
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
         else if constexpr (kCodes)
 #pragma unroll
           for (int t = 0; t < 2; ++t) qv[j][rt][t] = get_codes(ct, x, j, rt, t);
-        else load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+        else load_gc<GIFT_NT_S1>(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
         if constexpr (kB128) sc[j][rt] = L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)];
       }
     });
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
       constexpr int j = decltype(J)::value;
       load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
-      for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+      for (int rt = 0; rt < kTR; ++rt) load_gc<GIFT_NT_S2>(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
     });
   });
   stage_c<kRB>(L, x, cs);
@@ -737,8 +738,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
           if (!x.ok[rt]) continue;
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            *reinterpret_cast<float4*>(L.Ghat + x.row[rt] * L.d_in + kChunk * (x.c0 + j) +
-                                       16 * t + 4 * x.g) = w[j][rt][t];
+            st_f4(L.Ghat + x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g,
+                  w[j][rt][t]);
         }
       });
     });
@@ -844,7 +845,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
       constexpr int j = decltype(J)::value;
       load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
-      for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+      for (int rt = 0; rt < kTR; ++rt) load_gc<GIFT_NT_S3>(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
     });
   });
   uint32_t m = 0u;
@@ -1150,8 +1151,8 @@ __global__ __launch_bounds__(kTileThreads) void k_blk_dequant(GroupDev gd) {
     for (int oc = 0; oc < kb; ++oc)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        *reinterpret_cast<float4*>(L.Ghat + (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) +
-                                   16 * t + 4 * x.g) = gh[oc][rt][t];
+        st_f4(L.Ghat + (int64_t)x.row[rt] * L.d_in + kChunk * (x.c0 + oc) + 16 * t + 4 * x.g,
+              gh[oc][rt][t]);
   }
 }
 
@@ -1243,8 +1244,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_unwhiten(GroupDev gd) {
         if (!x.ok[rt]) continue;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          *reinterpret_cast<float4*>(L.Ghat + x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t +
-                                     4 * x.g) = out[j][rt][t];
+          st_f4(L.Ghat + x.row[rt] * L.d_in + kChunk * (x.c0 + j) + 16 * t + 4 * x.g,
+                out[j][rt][t]);
       }
     });
   });
@@ -1264,7 +1265,7 @@ __global__ __launch_bounds__(kThreads) void k_flat_amax(GroupDev g) {
   for (int i = 0; i < kFlatTile / (4 * kThreads); ++i) {
     const int64_t e = base + 4 * ((int64_t)i * kThreads + threadIdx.x);
     if (e < n) {
-      const float4 v = *reinterpret_cast<const float4*>(L.G + e);
+      const float4 v = ld_g(L.G + e);
       m = max(max(m, abs_bits(v.x)), max(abs_bits(v.y), max(abs_bits(v.z), abs_bits(v.w))));
     }
   }
@@ -1304,7 +1305,7 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
     const int64_t e = base + 4 * ((int64_t)i * kThreads + threadIdx.x);
     const bool act = e < n;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (act) v = *reinterpret_cast<const float4*>(L.G + e);
+    if (act) v = ld_g(L.G + e);
     uint32_t m = max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w)));
     if constexpr (kB128) {
       // 32 consecutive lanes hold one 128-element segment (d_in % 128 == 0)
@@ -1329,12 +1330,12 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
         if (g.flags && fl) atomicOr(g.flags, fl);
       }
       if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + e) = v;
-      if (kDeq) *reinterpret_cast<float4*>(L.Ghat + e) = mx_decode4(q, code);
+      if (kDeq) st_f4(L.Ghat + e, mx_decode4(q, code));
       continue;
     }
     if (!act) continue;
     const uint32_t c = e4m3_encode4_scaled(v, sc.scale, sc.flags & GIFT_FLAG_NONFINITE);
-    *reinterpret_cast<uint32_t*>(L.q + e) = c;
+    st_q4(L.q + e, c);
     if (kWriteW && L.Wout) *reinterpret_cast<float4*>(L.Wout + e) = v;
     if (kDeq) {
       float4 o;
@@ -1342,7 +1343,7 @@ __global__ __launch_bounds__(kThreads) void k_flat_quant(GroupDev g) {
       o.y = e4m3_decode(c, 1) * sc.inv;
       o.z = e4m3_decode(c, 2) * sc.inv;
       o.w = e4m3_decode(c, 3) * sc.inv;
-      *reinterpret_cast<float4*>(L.Ghat + e) = o;
+      st_f4(L.Ghat + e, o);
     }
   }
 }
@@ -1362,17 +1363,17 @@ __global__ __launch_bounds__(kThreads) void k_flat_dequant(GroupDev g) {
     if constexpr (kFmt == GIFT_SCALE_MXFP4) {
       const uint32_t q = *reinterpret_cast<const uint16_t*>(L.q + e / 2);
       const uint32_t code = reinterpret_cast<const uint8_t*>(L.inv)[e / kMxBlock];
-      *reinterpret_cast<float4*>(L.Ghat + e) = mx_decode4(q, code);
+      st_f4(L.Ghat + e, mx_decode4(q, code));
       continue;
     }
     const float s = kFmt == GIFT_SCALE_BLOCK128 ? L.inv[e / kBlock] : inv0;
-    const uint32_t c = *reinterpret_cast<const uint32_t*>(L.q + e);
+    const uint32_t c = ld_q4(L.q + e);
     float4 o;
     o.x = e4m3_decode(c, 0) * s;
     o.y = e4m3_decode(c, 1) * s;
     o.z = e4m3_decode(c, 2) * s;
     o.w = e4m3_decode(c, 3) * s;
-    *reinterpret_cast<float4*>(L.Ghat + e) = o;
+    st_f4(L.Ghat + e, o);
   }
 }
 
@@ -1395,7 +1396,7 @@ __global__ __launch_bounds__(kThreads) void k_flat_accumulate(GroupDev g) {
       o = mx_decode4(q, reinterpret_cast<const uint8_t*>(L.inv)[e / kMxBlock]);
     } else {
       const float s = kFmt == GIFT_SCALE_BLOCK128 ? L.inv[e / kBlock] : inv0;
-      const uint32_t c = *reinterpret_cast<const uint32_t*>(L.q + e);
+      const uint32_t c = ld_q4(L.q + e);
       o = make_float4(e4m3_decode(c, 0) * s, e4m3_decode(c, 1) * s, e4m3_decode(c, 2) * s,
                       e4m3_decode(c, 3) * s);
     }
@@ -1419,8 +1420,8 @@ __global__ __launch_bounds__(kThreads) void k_err_partial(GroupDev g) {
   for (int i = 0; i < kFlatTile / (4 * kThreads); ++i) {
     const int64_t e = base + 4 * ((int64_t)i * kThreads + threadIdx.x);
     if (e < n) {
-      const float4 a = *reinterpret_cast<const float4*>(L.G + e);
-      const float4 b = *reinterpret_cast<const float4*>(L.Ghat + e);
+      const float4 a = ld_g(L.G + e);
+      const float4 b = ld_g(L.Ghat + e);
       const double d0 = (double)b.x - (double)a.x, d1 = (double)b.y - (double)a.y;
       const double d2 = (double)b.z - (double)a.z, d3 = (double)b.w - (double)a.w;
       se += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
@@ -1516,7 +1517,7 @@ struct SlabOps {
   uint32_t qv[kCodes ? kTR : 1][2];
 };
 
-template <bool kCodes>
+template <bool kCodes, bool kNT = false>
 __device__ __forceinline__ void slab_load(const LayerDev& L, const Slab& x, const uint4* P, int k,
                                           SlabOps<kCodes>& o) {
   const int c = x.wave + kSW * (k < x.nmine ? k : x.nmine - 1);
@@ -1524,7 +1525,7 @@ __device__ __forceinline__ void slab_load(const LayerDev& L, const Slab& x, cons
 #pragma unroll
   for (int rt = 0; rt < kTR; ++rt) {
     if constexpr (kCodes) load_qc(L, x.row[rt], x.g, c, o.qv[rt]);
-    else load_gc(L, x.row[rt], x.g, c, o.gv[rt]);
+    else load_gc<kNT>(L, x.row[rt], x.g, c, o.gv[rt]);
   }
 }
 
@@ -1540,7 +1541,7 @@ __device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, in
   for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (x.nmine > 0) {  // wave-uniform
     SlabOps<kCodes> o[2];
-    slab_load<kCodes>(L, x, L.P, 0, o[0]);
+    slab_load<kCodes, GIFT_NT_S1>(L, x, L.P, 0, o[0]);
     auto mult = [&](const SlabOps<kCodes>& op) {
       bf16x8 a[2][3];
       as_ops(op.pa, a);
@@ -1551,10 +1552,10 @@ __device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, in
       }
     };
     for (int k = 0; k < x.nmine; k += 2) {
-      slab_load<kCodes>(L, x, L.P, k + 1, o[1]);
+      slab_load<kCodes, GIFT_NT_S1>(L, x, L.P, k + 1, o[1]);
       mult(o[0]);
       if (k + 1 >= x.nmine) break;
-      slab_load<kCodes>(L, x, L.P, k + 2, o[0]);
+      slab_load<kCodes, GIFT_NT_S1>(L, x, L.P, k + 2, o[0]);
       mult(o[1]);
     }
   }
@@ -1607,7 +1608,7 @@ __global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
   if (x.nmine > 0) {  // wave-uniform
     SlabOps<false> o[2];
     const int last = x.nmine - 1;
-    slab_load<false>(L, x, P2, last, o[0]);
+    slab_load<false, GIFT_NT_S2>(L, x, P2, last, o[0]);
     auto amax_of = [&](const SlabOps<false>& op) {
       bf16x8 a[2][3];
       as_ops(op.pa, a);
@@ -1628,10 +1629,10 @@ __global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
       }
     };
     for (int k = last; k >= 0; k -= 2) {
-      slab_load<false>(L, x, P2, k > 0 ? k - 1 : 0, o[1]);
+      slab_load<false, GIFT_NT_S2>(L, x, P2, k > 0 ? k - 1 : 0, o[1]);
       amax_of(o[0]);
       if (k == 0) break;
-      slab_load<false>(L, x, P2, k > 1 ? k - 2 : 0, o[0]);
+      slab_load<false, GIFT_NT_S2>(L, x, P2, k > 1 ? k - 2 : 0, o[0]);
       amax_of(o[1]);
     }
   }
