@@ -82,71 +82,32 @@ __device__ __forceinline__ uint32_t abs_bits(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming accesses of the bulk tensors (G, the codes, G^): loads and stores
-// with the nontemporal (`nt`) bit, so each pass streams them through the
-// caches at low priority and the small operands (packs, row coefficients)
-// keep their lines.  A float4 read stream reaches about 7.0 TB/s on the
-// MI355X this way against about 5.4 TB/s with plain loads.
+// Accesses of the bulk tensors.  G is read with plain loads: the per-tensor
+// whiten reads it three times, and the second read of a slab row block finds
+// part of it still in the caches (with nontemporal G loads the whiten of
+// eight hidden-4096 blocks took 5.5 ms instead of 4.8).  The codes and G^ are touched once per pass and go through
+// nontemporal (`nt`) loads and stores, so they do not evict the operands that
+// are reused (packs, row coefficients).
 // ---------------------------------------------------------------------------
-#ifndef GIFT_NT_G
-#define GIFT_NT_G 0
-#endif
-#ifndef GIFT_NT_S1
-#define GIFT_NT_S1 0
-#endif
-#ifndef GIFT_NT_S2
-#define GIFT_NT_S2 0
-#endif
-#ifndef GIFT_NT_S3
-#define GIFT_NT_S3 0
-#endif
-#ifndef GIFT_NT_Q
-#define GIFT_NT_Q 1
-#endif
-#ifndef GIFT_NT_ST
-#define GIFT_NT_ST 1
-#endif
-typedef __attribute__((ext_vector_type(4))) float nt_f4;
 typedef __attribute__((ext_vector_type(4))) unsigned nt_u4;
+typedef __attribute__((ext_vector_type(4))) float nt_f4;
 
-template <bool kNT = GIFT_NT_G>
-__device__ __forceinline__ float4 ld_g(const float* p) {
-  if constexpr (kNT) {
-    const nt_f4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p));
-    return make_float4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const float4*>(p);
-  }
-}
+__device__ __forceinline__ float4 ld_g(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ uint4 ld_q16(const uint8_t* p) {
-  if constexpr (GIFT_NT_Q) {
-    const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const uint4*>(p);
-  }
+  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint32_t ld_q4(const uint8_t* p) {
-  if constexpr (GIFT_NT_Q) return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
-  else return *reinterpret_cast<const uint32_t*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
 }
 __device__ __forceinline__ void st_f4(float* p, const float4& v) {
-  if constexpr (GIFT_NT_ST) {
-    __builtin_nontemporal_store(nt_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f4*>(p));
-  } else {
-    *reinterpret_cast<float4*>(p) = v;
-  }
+  __builtin_nontemporal_store(nt_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f4*>(p));
 }
 __device__ __forceinline__ void st_q16(uint8_t* p, const uint4& v) {
-  if constexpr (GIFT_NT_ST) {
-    __builtin_nontemporal_store(nt_u4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u4*>(p));
-  } else {
-    *reinterpret_cast<uint4*>(p) = v;
-  }
+  __builtin_nontemporal_store(nt_u4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u4*>(p));
 }
 __device__ __forceinline__ void st_q4(uint8_t* p, uint32_t v) {
-  if constexpr (GIFT_NT_ST) __builtin_nontemporal_store(v, reinterpret_cast<unsigned*>(p));
-  else *reinterpret_cast<uint32_t*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<unsigned*>(p));
 }
 
 // scale / inv / flags from an amax given as |x| bits (IEEE division).  A

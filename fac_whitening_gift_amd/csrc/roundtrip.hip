@@ -365,12 +365,11 @@ __device__ __forceinline__ int rank_of(int k, int g) { return 16 * (k >> 2) + 4 
 
 // gradient values of one chunk for this lane and 16-row tile: columns
 // 32c + 4g .. +3 (t = 0) and 32c + 16 + 4g .. +3 (t = 1) of its row
-template <bool kNT = GIFT_NT_G>
 __device__ __forceinline__ void load_gc(const LayerDev& L, int64_t row, int g, int c,
                                         float4 (&v)[2]) {
   const float* p = L.G + row * L.d_in + kChunk * c + 4 * g;
-  v[0] = ld_g<kNT>(p);
-  v[1] = ld_g<kNT>(p + 16);
+  v[0] = ld_g(p);
+  v[1] = ld_g(p + 16);
 }
 
 __device__ __forceinline__ void load_qc(const LayerDev& L, int64_t row, int g, int c,
@@ -571,7 +570,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_cpart(GroupDev gd) {
         else if constexpr (kCodes)
 #pragma unroll
           for (int t = 0; t < 2; ++t) qv[j][rt][t] = get_codes(ct, x, j, rt, t);
-        else load_gc<GIFT_NT_S1>(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+        else load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
         if constexpr (kB128) sc[j][rt] = L.inv[x.row[rt] * nseg + ((x.c0 + j) >> 2)];
       }
     });
@@ -694,7 +693,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_whiten(GroupDev gd) {
       constexpr int j = decltype(J)::value;
       load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
-      for (int rt = 0; rt < kTR; ++rt) load_gc<GIFT_NT_S2>(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+      for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
     });
   });
   stage_c<kRB>(L, x, cs);
@@ -845,7 +844,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_quant(GroupDev gd) {
       constexpr int j = decltype(J)::value;
       load_a_rb<kRB>(L, true, x.c0 + j, x.lane, pa[j]);
 #pragma unroll
-      for (int rt = 0; rt < kTR; ++rt) load_gc<GIFT_NT_S3>(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
+      for (int rt = 0; rt < kTR; ++rt) load_gc(L, x.row[rt], x.g, x.c0 + j, gv[j][rt]);
     });
   });
   uint32_t m = 0u;
@@ -1517,7 +1516,7 @@ struct SlabOps {
   uint32_t qv[kCodes ? kTR : 1][2];
 };
 
-template <bool kCodes, bool kNT = false>
+template <bool kCodes>
 __device__ __forceinline__ void slab_load(const LayerDev& L, const Slab& x, const uint4* P, int k,
                                           SlabOps<kCodes>& o) {
   const int c = x.wave + kSW * (k < x.nmine ? k : x.nmine - 1);
@@ -1525,7 +1524,7 @@ __device__ __forceinline__ void slab_load(const LayerDev& L, const Slab& x, cons
 #pragma unroll
   for (int rt = 0; rt < kTR; ++rt) {
     if constexpr (kCodes) load_qc(L, x.row[rt], x.g, c, o.qv[rt]);
-    else load_gc<kNT>(L, x.row[rt], x.g, c, o.gv[rt]);
+    else load_gc(L, x.row[rt], x.g, c, o.gv[rt]);
   }
 }
 
@@ -1541,7 +1540,7 @@ __device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, in
   for (int rt = 0; rt < kTR; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (x.nmine > 0) {  // wave-uniform
     SlabOps<kCodes> o[2];
-    slab_load<kCodes, GIFT_NT_S1>(L, x, L.P, 0, o[0]);
+    slab_load<kCodes>(L, x, L.P, 0, o[0]);
     auto mult = [&](const SlabOps<kCodes>& op) {
       bf16x8 a[2][3];
       as_ops(op.pa, a);
@@ -1552,10 +1551,10 @@ __device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, in
       }
     };
     for (int k = 0; k < x.nmine; k += 2) {
-      slab_load<kCodes, GIFT_NT_S1>(L, x, L.P, k + 1, o[1]);
+      slab_load<kCodes>(L, x, L.P, k + 1, o[1]);
       mult(o[0]);
       if (k + 1 >= x.nmine) break;
-      slab_load<kCodes, GIFT_NT_S1>(L, x, L.P, k + 2, o[0]);
+      slab_load<kCodes>(L, x, L.P, k + 2, o[0]);
       mult(o[1]);
     }
   }
@@ -1608,7 +1607,7 @@ __global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
   if (x.nmine > 0) {  // wave-uniform
     SlabOps<false> o[2];
     const int last = x.nmine - 1;
-    slab_load<false, GIFT_NT_S2>(L, x, P2, last, o[0]);
+    slab_load<false>(L, x, P2, last, o[0]);
     auto amax_of = [&](const SlabOps<false>& op) {
       bf16x8 a[2][3];
       as_ops(op.pa, a);
@@ -1629,10 +1628,10 @@ __global__ __launch_bounds__(kSlabThreads) void k_slab_whiten(GroupDev gd) {
       }
     };
     for (int k = last; k >= 0; k -= 2) {
-      slab_load<false, GIFT_NT_S2>(L, x, P2, k > 0 ? k - 1 : 0, o[1]);
+      slab_load<false>(L, x, P2, k > 0 ? k - 1 : 0, o[1]);
       amax_of(o[0]);
       if (k == 0) break;
-      slab_load<false, GIFT_NT_S2>(L, x, P2, k > 1 ? k - 2 : 0, o[0]);
+      slab_load<false>(L, x, P2, k > 1 ? k - 2 : 0, o[0]);
       amax_of(o[1]);
     }
   }
