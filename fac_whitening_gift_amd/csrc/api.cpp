@@ -172,7 +172,7 @@ LayerWs layer_ws(const gift_layer& L, Op op, bool block) {
         }
       } else if (L.factor) {
         w.cbuf = (size_t)col_groups(L.d_in) * frag * frb(L);  // partial c per column group
-        w.cfin = cop * frb(L);                                 // c' of every row (operand form)
+        w.cfin = cop * frb(L);                                 // c' of every row (fp32)
         if (!block) {  // one amax per tile, the layer amax
           w.part = (size_t)row_tiles_max(L) * sizeof(uint32_t);
           w.amax = sizeof(uint32_t);

@@ -310,7 +310,7 @@ struct LayerDev {
   const float* coef;    // GIFT_COEF_COUNT
   const uint4* P;       // the factor's split MFMA operand packs
   float* cbuf;          // workspace: column-group partials of the row coefficients
-  float* cfin;          // workspace: c' of every row, split into the bf16 operand form
+  float* cfin;          // workspace: c' of every row (fp32, in the lanes' fragment order)
   uint32_t* part;       // workspace: one partial amax per tile
   uint32_t* amax;       // workspace: the layer's amax as |x| bits
   double* part2;        // workspace: two fp64 partial sums per tile

@@ -764,32 +764,27 @@ __global__ __launch_bounds__(kT) void k_pack_q(G g, int which) {
 }
 
 constexpr int kGemmWaves = 4;
-// 16-row tiles of A per wave in the 64-row shape: each load of Q's packs
-// feeds this many tiles
+// 16-row tiles of A per wave in the wide shape: each read of Q's packs feeds
+// this many tiles
 constexpr int kGemmTR = 2;
-constexpr int kGemmRows = 16 * kGemmWaves * kGemmTR;  // rows per workgroup of that shape
-// workgroups of that shape from which a call takes it (eight per CU)
-constexpr int64_t kGemmRowTileMin = 2048;
 
-// Two workgroup shapes (four waves each):
-//   kRowTiles = false: 16 rows of one partial; the waves split the partial's
-//     K range into four and their sums are added in wave order through LDS.
-//     grid: (max d / 16, kYSplit, inputs).
-//   kRowTiles = true: kGemmRows rows of one partial, each wave kGemmTR
-//     16-row tiles of them over the partial's whole K range; a wave's load of
-//     Q's packs for a K chunk feeds all its tiles, and the four waves read the
-//     same packs at about the same time, so most of those reads hit in cache.
-//     grid: (max d / kGemmRows, kYSplit, inputs).
-// The second needs far fewer workgroups, so it is taken only when a call
-// has enough rows to fill the machine with it.
-template <bool kRowTiles, int kWT, class G>
+// Two workgroup shapes, chosen per input by its width alone (so an input's
+// factor does not depend on the other inputs of the call):
+//   k_gemm_aq (d < kGemmWideD): 16 rows of one partial, four waves; the waves
+//     split the partial's K range into four and their sums are added in wave
+//     order through LDS.  grid: (max d / 16, kYSplit, inputs).
+//   k_gemm_aq_l (d >= kGemmWideD): below.
+constexpr int kGemmWideD = 1024;
+
+template <int kWT, class G>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
-  constexpr int kTRw = kRowTiles ? kGemmTR : 1;  // 16-row tiles of this wave
+  constexpr int kTRw = 1;  // 16-row tiles of this wave
   const RIn& R = g.r[blockIdx.z];
   const int d = R.d, w = g.w;
+  if (d >= kGemmWideD) return;  // the wide kernel's input (uniform over the workgroup)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = kRowTiles ? (blockIdx.x * kGemmWaves + wave) * 16 * kTRw : blockIdx.x * 16;
-  if (row0 >= d) return;  // uniform over the wave (kRowTiles: no barrier follows) or workgroup
+  const int row0 = blockIdx.x * 16;
+  if (row0 >= d) return;  // uniform over the workgroup
   const float* __restrict__ A = R.A;
   const int r16 = lane & 15, gq = lane >> 4;
   const int ntile = w / 16;
@@ -799,8 +794,8 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
 #pragma unroll
     for (int t = 0; t < kWT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int kchunks = (d + 31) / 32;
-  const int slices = kRowTiles ? kYSplit : kYSplit * kGemmWaves;
-  const int slice = kRowTiles ? blockIdx.y : blockIdx.y * kGemmWaves + wave;
+  const int slices = kYSplit * kGemmWaves;
+  const int slice = blockIdx.y * kGemmWaves + wave;
   const int kc_begin = slice * kchunks / slices, kc_end = (slice + 1) * kchunks / slices;
   // d % 16 == 0: a 16-row tile is all inside A or all past it (wave-uniform)
   bool rin[kTRw];
@@ -862,17 +857,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   }
   // D layout: lane holds rows 4 gq .. 4 gq + 3 of column r16 of each 16x16 tile
   float* __restrict__ Yp = R.Yp + (size_t)blockIdx.y * d * w;
-  if constexpr (kRowTiles) {
-#pragma unroll
-    for (int j = 0; j < kTRw; ++j)
-      if (rin[j])
-#pragma unroll
-        for (int t = 0; t < kWT; ++t)
-          if (t < ntile)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              Yp[(int64_t)(row0 + 16 * j + 4 * gq + i) * w + 16 * t + r16] = acc[j][t][i];
-  } else {
+  {
     __shared__ float red[kGemmWaves][16][16 * kWT];
 #pragma unroll
     for (int t = 0; t < kWT; ++t)
@@ -890,18 +875,179 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_aq(G g) {
   }
 }
 
-// Y = A Q for every input of a chain, in the workgroup shape its size suits
-// (kWT: 16-column tiles of Q the accumulators hold, 4 up to width 64, else 6)
+// Large calls: 128 rows of one partial per workgroup of 4 waves, each wave
+// 32 rows (two 16-row tiles) over the partial's whole K range.  Q's packs for
+// two K chunks at a time are loaded once per workgroup into LDS (double
+// buffered, one barrier per stage) and read from there by all four waves;
+// A streams from HBM into registers one stage ahead.  Two such workgroups
+// share a CU (48 KB of LDS each at width 64).  On a group of 16 hidden-4096
+// inputs, 8-wave workgroups of 256 rows took 0.90 ms per product, 4-wave
+// ones 0.73 ms, 2-wave ones 0.82 ms; a third register stage of A did not
+// help.
+// grid: (max d / kGemmRowsL, kYSplit, inputs)
+constexpr int kGemmWavesL = 4;
+constexpr int kGemmRowsL = 16 * kGemmWavesL * kGemmTR;  // 128
+
+// kFull: the width is 16 kWT (every accumulator tile in use); the six
+// split products then go round-robin over all 2 kWT accumulators of the wave.
+template <int kWT, bool kFull, class G>
+__global__ __launch_bounds__(64 * kGemmWavesL) void k_gemm_aq_l(G g) {
+  constexpr int kThreads = 64 * kGemmWavesL;
+  constexpr int kStageU4 = 2 * kWT * 3 * 64;                      // uint4 of packs per stage (max)
+  constexpr int kPer = (kStageU4 + kThreads - 1) / kThreads;
+  constexpr int kN = kGemmTR * kWT;                               // accumulator tiles per wave
+  __shared__ uint4 qs[2][kStageU4];
+  const RIn& R = g.r[blockIdx.z];
+  const int d = R.d, w = g.w, ntile = kFull ? kWT : w / 16;
+  if (d < kGemmWideD || (int)blockIdx.x * kGemmRowsL >= d) return;  // uniform over the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, gq = lane >> 4;
+  const int row0 = (int)blockIdx.x * kGemmRowsL + wave * 16 * kGemmTR;
+  const float* __restrict__ A = R.A;
+  const int kchunks = (d + 31) / 32;
+  const int kc_begin = (int)blockIdx.y * kchunks / kYSplit;
+  const int kc_end = ((int)blockIdx.y + 1) * kchunks / kYSplit;
+  const int nst = (kc_end - kc_begin + 1) / 2;  // stages of two K chunks
+  const int cu4 = ntile * 3 * 64;               // uint4 of packs per K chunk
+  const int64_t tot4 = (int64_t)kchunks * cu4;
+  // d % 16 == 0: a 16-row tile is all inside A or all past it (wave-uniform)
+  bool rin[kGemmTR];
+  const float* arow[kGemmTR];
+#pragma unroll
+  for (int j = 0; j < kGemmTR; ++j) {
+    rin[j] = row0 + 16 * j < d;
+    arow[j] = A + (int64_t)(rin[j] ? row0 + 16 * j + r16 : d - 16 + r16) * d;
+  }
+  f32x4 acc[kN];  // tile j, column tile t at j kWT + t
+#pragma unroll
+  for (int i = 0; i < kN; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // loads of stage st (clamped to the last stage, so every stage issues the
+  // same loads unconditionally): the packs of chunks kc_begin + 2 st, +1 and
+  // this lane's 8 values of A per tile and chunk (zero past d and past the
+  // partial's K range)
+  struct Stage {
+    uint4 q[kPer];
+    float4 a[2][kGemmTR][2];
+  };
+  auto load = [&](int st, Stage& S) {
+    st = st < nst ? st : nst - 1;
+    const int64_t base = (int64_t)(kc_begin + 2 * st) * cu4;
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+      const int e = (int)threadIdx.x + kThreads * h;
+      const int64_t idx = base + e < tot4 ? base + e : tot4 - 1;
+      const uint4 v = R.QP[idx];
+      S.q[h] = (e < 2 * cu4 && base + e < tot4) ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kc = kc_begin + 2 * st + c;
+      const int k0 = 32 * kc + 8 * gq;
+      const bool in = kc < kc_end && k0 < d;  // d % 16 == 0: a lane's 8 columns are all in or all out
+      const int kk = in ? k0 : 0;
+#pragma unroll
+      for (int j = 0; j < kGemmTR; ++j) {
+        const float4 lo = *reinterpret_cast<const float4*>(arow[j] + kk);
+        const float4 hi = *reinterpret_cast<const float4*>(arow[j] + kk + 4);
+        S.a[c][j][0] = in ? lo : make_float4(0.f, 0.f, 0.f, 0.f);
+        S.a[c][j][1] = in ? hi : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  auto put = [&](const Stage& S, int buf) {
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+      const int e = (int)threadIdx.x + kThreads * h;
+      if (e < kStageU4) qs[buf][e] = S.q[h];
+    }
+  };
+  auto comp = [&](const Stage& S, int buf, int st) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (kc_begin + 2 * st + c >= kc_end) break;  // uniform
+      bf16x8 sa[kGemmTR][3];
+#pragma unroll
+      for (int j = 0; j < kGemmTR; ++j) {
+        const float v[8] = {S.a[c][j][0].x, S.a[c][j][0].y, S.a[c][j][0].z, S.a[c][j][0].w,
+                            S.a[c][j][1].x, S.a[c][j][1].y, S.a[c][j][1].z, S.a[c][j][1].w};
+        split3(v, sa[j]);
+      }
+      if constexpr (kFull) {
+        bf16x8 sb[kWT][3];
+#pragma unroll
+        for (int t = 0; t < kWT; ++t)
+#pragma unroll
+          for (int sp = 0; sp < 3; ++sp)
+            sb[t][sp] = as_bf16x8(qs[buf][((c * kWT + t) * 3 + sp) * 64 + lane]);
+        const bf16x8(*pa[kN])[3];
+        const bf16x8(*pb[kN])[3];
+#pragma unroll
+        for (int j = 0; j < kGemmTR; ++j)
+#pragma unroll
+          for (int t = 0; t < kWT; ++t) {
+            pa[j * kWT + t] = &sa[j];
+            pb[j * kWT + t] = &sb[t];
+          }
+        mfma3x3_n<kN>(pa, pb, acc);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kGemmTR; ++j)
+#pragma unroll
+          for (int t = 0; t < kWT; ++t)
+            if (t < ntile) {
+              const uint4* qp = &qs[buf][((c * ntile + t) * 3) * 64 + lane];
+              const bf16x8 sb[3] = {as_bf16x8(qp[0]), as_bf16x8(qp[64]), as_bf16x8(qp[128])};
+              acc[j * kWT + t] = mfma3x3(sa[j], sb, acc[j * kWT + t]);
+            }
+      }
+    }
+  };
+  if (nst > 0) {
+    Stage s0, s1;
+    load(0, s0);
+    put(s0, 0);
+    __syncthreads();
+    load(1, s1);
+    for (int st = 0;;) {
+      // s0 holds stage st (its packs in qs[0]); s1's loads of st + 1 are in flight
+      comp(s0, 0, st);
+      put(s1, 1);
+      __syncthreads();
+      if (++st == nst) break;
+      load(st + 1, s0);
+      comp(s1, 1, st);
+      put(s0, 0);
+      __syncthreads();
+      if (++st == nst) break;
+      load(st + 1, s1);
+    }
+  }
+  float* __restrict__ Yp = R.Yp + (size_t)blockIdx.y * d * w;
+#pragma unroll
+  for (int j = 0; j < kGemmTR; ++j)
+    if (rin[j])
+#pragma unroll
+      for (int t = 0; t < kWT; ++t)
+        if (t < ntile)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Yp[(int64_t)(row0 + 16 * j + 4 * gq + i) * w + 16 * t + r16] = acc[j * kWT + t][i];
+}
+
+// Y = A Q for every input of a chain, each in the workgroup shape of its
+// width (kWT: 16-column tiles of Q the accumulators hold, 4 up to width 64,
+// else 6)
 template <int kWT, class G>
 void gemm_aq_w(const G& g, const RIn* hd, int nc, int maxd, hipStream_t st) {
-  int64_t tiles = 0;
-  for (int i = 0; i < nc; ++i) tiles += (hd[i].d + kGemmRows - 1) / kGemmRows;
-  if (tiles * kYSplit >= kGemmRowTileMin) {
-    const dim3 grid((maxd + kGemmRows - 1) / kGemmRows, kYSplit, nc);
-    k_gemm_aq<true, kWT><<<grid, 64 * kGemmWaves, 0, st>>>(g);
-  } else {
-    k_gemm_aq<false, kWT><<<dim3(maxd / 16, kYSplit, nc), 64 * kGemmWaves, 0, st>>>(g);
+  int dmax_narrow = 0;
+  for (int i = 0; i < nc; ++i)
+    if (hd[i].d < kGemmWideD && hd[i].d > dmax_narrow) dmax_narrow = hd[i].d;
+  if (maxd >= kGemmWideD) {
+    const dim3 grid((maxd + kGemmRowsL - 1) / kGemmRowsL, kYSplit, nc);
+    if (g.w == 16 * kWT) k_gemm_aq_l<kWT, true><<<grid, 64 * kGemmWavesL, 0, st>>>(g);
+    else k_gemm_aq_l<kWT, false><<<grid, 64 * kGemmWavesL, 0, st>>>(g);
   }
+  if (dmax_narrow > 0) k_gemm_aq<kWT><<<dim3(dmax_narrow / 16, kYSplit, nc), 64 * kGemmWaves, 0, st>>>(g);
 }
 
 template <class G>

@@ -473,15 +473,38 @@ __device__ __forceinline__ void store_partial(const LayerDev& L, const Tile& x,
   }
 }
 
-// The row block's c' operand of the second product, already split three
-// ways: [rt][split][lane] 16-byte groups of 8 bf16 (kCOp uint4 per row
-// block), into LDS.  Contains a workgroup barrier.
-// Rank block b of a row block at (rb * kRB + b) * kCOp.
+// The row block's c' operand of the second product in LDS, split three
+// ways: [rt][split][lane] 16-byte groups of 8 bf16 (kCOp uint4 per row block
+// and rank block).  In the workspace c' is kept in fp32, [rt][half][lane]
+// float4s (kCF per row block and rank block, rank block b of row block rb at
+// (rb * kRB + b) * kCF): two thirds of the bytes of the split form, which
+// every tile of the row block reads.  stage_c splits it as it fills LDS (the
+// same split3 as where c' is formed, so the operand is the same bits).
+// Contains a workgroup barrier.
 constexpr int kCOp = kTR * 3 * 64;
+constexpr int kCF = kTR * 2 * 64;
+
+// c' of one (rank block, 16-row tile, lane) into the workspace
+__device__ __forceinline__ void put_cfin(const LayerDev& L, int64_t rbb, int rt, int lane,
+                                         const float (&cp)[8]) {
+  float4* out = reinterpret_cast<float4*>(L.cfin) + rbb * kCF + (rt * 2) * 64 + lane;
+  out[0] = make_float4(cp[0], cp[1], cp[2], cp[3]);
+  out[64] = make_float4(cp[4], cp[5], cp[6], cp[7]);
+}
+
 template <int kRB = 1>
 __device__ __forceinline__ void stage_c(const LayerDev& L, const Tile& x, uint4* lds) {
-  const uint4* src = reinterpret_cast<const uint4*>(L.cfin) + x.rb * kCOp * kRB;
-  for (int e = threadIdx.x; e < kCOp * kRB; e += kTileThreads) lds[e] = src[e];
+  const float4* src = reinterpret_cast<const float4*>(L.cfin) + x.rb * kCF * kRB;
+  for (int e = threadIdx.x; e < kTR * 64 * kRB; e += kTileThreads) {
+    const int b = e / (kTR * 64), rt = (e / 64) % kTR, lane = e % 64;
+    const float4 lo = src[b * kCF + (rt * 2) * 64 + lane];
+    const float4 hi = src[b * kCF + (rt * 2 + 1) * 64 + lane];
+    const float cp[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    bf16x8 cb[3];
+    split3(cp, cb);
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) lds[b * kCOp + (rt * 3 + sp) * 64 + lane] = __builtin_bit_cast(uint4, cb[sp]);
+  }
   __syncthreads();
 }
 
@@ -643,11 +666,7 @@ __device__ __forceinline__ void reduce_row_block(const LayerDev& L, int64_t rb, 
   float cp[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) cp[k] = s[k] * d8[k];
-  bf16x8 cb[3];
-  split3(cp, cb);
-  uint4* out = reinterpret_cast<uint4*>(L.cfin) + (rb * kRB + b) * kCOp;
-#pragma unroll
-  for (int sp = 0; sp < 3; ++sp) out[(rt * 3 + sp) * 64 + lane] = __builtin_bit_cast(uint4, cb[sp]);
+  put_cfin(L, rb * kRB + b, rt, lane, cp);
 }
 
 template <bool kDequant, bool kBlockScale, int kRB>
@@ -1579,13 +1598,9 @@ __device__ __forceinline__ void slab_cprime(const LayerDev& L, const Slab& x, in
     for (int k = 0; k < 8; ++k) cp[k] = s8[k] * (dk[rank_of(k, lane >> 4)] * extra);
     bf16x8 cb[3];
     split3(cp, cb);
-    uint4* out = L.cfin ? reinterpret_cast<uint4*>(L.cfin) + rb * kCOp : nullptr;
 #pragma unroll
-    for (int sp = 0; sp < 3; ++sp) {
-      const uint4 v = __builtin_bit_cast(uint4, cb[sp]);
-      cs[(rt * 3 + sp) * 64 + lane] = v;
-      if (out) out[(rt * 3 + sp) * 64 + lane] = v;
-    }
+    for (int sp = 0; sp < 3; ++sp) cs[(rt * 3 + sp) * 64 + lane] = __builtin_bit_cast(uint4, cb[sp]);
+    if (L.cfin) put_cfin(L, rb, rt, lane, cp);
   }
   __syncthreads();
 }
@@ -1673,7 +1688,7 @@ int col_groups(int64_t d_in) {
   return (int)((nch + per - 1) / per);
 }
 int frag_floats() { return kFrag; }
-int cop_bytes() { return kCOp * 16; }
+int cop_bytes() { return kCF * 16; }
 int flat_tiles(int64_t n) { return (int)((n + kFlatTile - 1) / kFlatTile); }
 size_t pack_bytes(int64_t d_in) { return (size_t)(d_in / kChunk) * 2 * 2 * 3 * 64 * 16; }
 

@@ -364,8 +364,9 @@ def test_chained_refresh_many_inputs():
 
 
 def test_chained_refresh_wide_inputs():
-    """Twenty-four bf16 inputs of width 1536 in one call: enough rows that
-    Y = A Q runs in its 64-row workgroup shape.  Inputs 0, 11 and 23 against
+    """Twenty-four bf16 inputs of width 1536 in one call: Y = A Q runs in its
+    wide workgroup shape (inputs of width 1024 and more: 128 rows per
+    workgroup, Q's operand packs shared through LDS).  Inputs 0, 11 and 23 against
     the oracle (same sketch); every factor's U orthonormal and theta equal to
     its Rayleigh quotients u^T A u."""
     n, d, t = 24, 1536, 2048
