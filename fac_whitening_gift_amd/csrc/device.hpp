@@ -82,24 +82,21 @@ __device__ __forceinline__ uint32_t abs_bits(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Accesses of the bulk tensors.  G is read with plain loads: the per-tensor
-// whiten reads it three times, and the second read of a slab row block finds
-// part of it still in the caches (with nontemporal G loads the whiten of
-// eight hidden-4096 blocks took 5.5 ms instead of 4.8).  The codes and G^ are touched once per pass and go through
-// nontemporal (`nt`) loads and stores, so they do not evict the operands that
-// are reused (packs, row coefficients).
+// Accesses of the bulk tensors.  G and the codes are read with plain loads:
+// the whiten's second read of a slab row block finds part of G still in the
+// caches (with nontemporal G loads the whiten of eight hidden-4096 blocks
+// took 5.5 ms instead of 4.8), and nontemporal code loads made the
+// dequantize side of a hidden-1024 block about 15% slower.  The codes and G^
+// are written once per pass and go out with the nontemporal (`nt`) bit, so
+// the stores do not evict the operands that are reused (packs, row
+// coefficients).
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) unsigned nt_u4;
 typedef __attribute__((ext_vector_type(4))) float nt_f4;
 
 __device__ __forceinline__ float4 ld_g(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ uint4 ld_q16(const uint8_t* p) {
-  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t ld_q4(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
-}
+__device__ __forceinline__ uint4 ld_q16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ld_q4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ void st_f4(float* p, const float4& v) {
   __builtin_nontemporal_store(nt_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f4*>(p));
 }

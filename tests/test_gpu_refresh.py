@@ -300,10 +300,12 @@ def test_grouped_covariance_two_batches():
 
 
 def test_grouped_covariance_large_group():
-    """Three bf16 inputs with 1134 upper-triangle 128 x 128 tiles in one
-    call (a group that fills the machine without a token split): widths 4112
-    (33 blocks of 128, 16 valid columns in the last), 4096 and 1040; ragged
-    token counts.  Every A against the oracle, exactly symmetric."""
+    """Three bf16 inputs in one call: widths 4112 (17 tiles of 256, the last
+    with 16 valid columns; 33 of the 128-tile partials, the last also with
+    16), 4096 and 1040, ragged token counts.  The group's 304 covariance
+    tiles of 256 split the longer token ranges in two, so the partials are
+    written in the 128-tile layout and reduced.  Every A against the oracle,
+    exactly symmetric."""
     dims, toks = [4112, 4096, 1040], [1000, 777, 300]
     items, ref = [], []
     for k, (d, n) in enumerate(zip(dims, toks)):
@@ -319,6 +321,31 @@ def test_grouped_covariance_large_group():
         Ad = host(it["A_out"])
         assert np.array_equal(Ad, Ad.T), k
         assert rel_fro(Ad, A_orc) <= 1e-5, (k, dims[k])
+
+
+def test_grouped_covariance_direct_write_ragged():
+    """Five bf16 inputs whose 657 covariance tiles of 256 fill the machine
+    without a token split, so the covariance kernel writes A and its mirror
+    image itself: widths 4112 and 2064 (the last tile column 16 wide, the
+    DMA loads of the missing features landing only in rows and columns that
+    are never written), token counts 300 .. 65 (ragged last steps read as
+    zero past the token range).  Every A against the oracle, exactly
+    symmetric."""
+    dims, toks = [4112, 4112, 2064, 4112, 4112], [300, 200, 129, 100, 65]
+    items, ref = [], []
+    for k, (d, n) in enumerate(zip(dims, toks)):
+        spec = synth.InputSpec("r%d" % k, d, n, 1.5, bf16=True)
+        inp = synth.draw_input(spec, seed=3200 + k, as_bf16=True)
+        A = torch.empty(d, d, dtype=torch.float32, device=DEV)
+        items.append(dict(X=inp["X"].to(DEV), factor=fg.Factor(d), A_out=A, seed=k))
+        ref.append(og.covariance(inp["X"].float().numpy()))
+    say("grouped covariance, direct write: widths %s tokens %s" % (dims, toks))
+    fg.gift_refresh_factors(items, power_steps=1)
+    torch.cuda.synchronize()
+    for k, (it, A_orc) in enumerate(zip(items, ref)):
+        Ad = host(it["A_out"])
+        assert np.array_equal(Ad, Ad.T), k
+        assert rel_fro(Ad, A_orc) <= 1e-5, (k, dims[k], toks[k])
 
 
 def test_chained_refresh_many_inputs():
