@@ -1378,30 +1378,52 @@ __global__ __launch_bounds__(kT) void k_apply(G g, int which) {
 // sym.schur2 rotations, round-robin ordering: W/2 disjoint rotations per
 // round); V accumulates the rotations.  On return B is diagonal to the
 // sweep tolerance.  In a round every 2 x 2 block of B is rotated on both
-// sides by one thread, and the pair of columns of V by others, so a round
-// takes two barriers.  All kST threads call it.
+// sides by one thread, and the pair of columns of V in two rows by another,
+// each reading a pair's indices and rotation as one int2 and one double2, so
+// a round takes two barriers.  All kST threads call it.
 // Sort key of an eigenvalue: NaN (a non-finite input) orders below every
 // number, so ranking by count gives every index a distinct rank and the
 // permutation built from it stays inside the matrix.
 __device__ __forceinline__ double sort_key(double x) { return x != x ? -__builtin_inf() : x; }
 
 // the round-robin schedule: pair i of round r (W/2 disjoint pairs per round,
-// every pair once in W - 1 rounds), smaller index first
+// every pair once in W - 1 rounds).  Index W - 1 stays in pair 0; p runs up
+// and q down with i, so the threads of a wave that update pairs i, i + 1, ...
+// touch consecutive columns of B and V (no LDS bank conflicts).
 template <int W>
 __device__ __forceinline__ void pair_of(int round, int i, int& p, int& q) {
   constexpr int kM = W - 1;
   p = i == 0 ? kM : (round + i) % kM;
   q = i == 0 ? round : (round - i + kM) % kM;
-  if (p > q) {
-    const int t = p;
-    p = q;
-    q = t;
+}
+
+// The rotation that annihilates the off-diagonal entry of the symmetric 2 x 2
+// block [[app, apq], [apq, aqq]] (sym.schur2): with
+// tau = (aqq - app) / (2 apq), t = sign(tau) / (|tau| + sqrt(1 + tau^2)),
+// c = 1 / sqrt(1 + t^2) and s = t c, J = [[c, s], [-s, c]] makes J^T B J
+// diagonal.  Reciprocals and reciprocal square roots are hardware estimates
+// refined by Newton steps.
+__device__ __forceinline__ void jacobi_rotation(double app, double aqq, double apq, double& c,
+                                                double& s) {
+  c = 1.0;
+  s = 0.0;
+  if (apq != 0.0) {
+    const double tau = (aqq - app) / (2.0 * apq);
+    double t;
+    if (fabs(tau) < 1e100) {
+      const double u = fma(tau, tau, 1.0);
+      t = rcp_f64(fabs(tau) + u * rsqrt_f64(u));
+      if (tau < 0.0) t = -t;
+    } else {
+      t = 0.5 / tau;
+    }
+    c = rsqrt_f64(fma(t, t, 1.0));
+    s = t * c;
   }
 }
 
 template <int W>
-__device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, double* rs, int* rp,
-                       int* rq, double* red) {
+__device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], int2* pq, double2* cs, double* red) {
   constexpr int kP = W / 2;   // rotations per round
   constexpr int kM = W - 1;   // rounds per sweep
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
@@ -1420,47 +1442,36 @@ __device__ void jacobi(double (*B)[W + 1], double (*V)[W + 1], double* rc, doubl
         const int i = threadIdx.x;
         int p, q;
         pair_of<W>(round, i, p, q);
-        const double apq = B[p][q], app = B[p][p], aqq = B[q][q];
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0) {
-          // t = sign(tau) / (|tau| + sqrt(1 + tau^2)), c = 1 / sqrt(1 + t^2), with
-          // reciprocals and reciprocal square roots as estimates + Newton steps
-          const double tau = (aqq - app) / (2.0 * apq);
-          double t;
-          if (fabs(tau) < 1e100) {
-            const double u = fma(tau, tau, 1.0);
-            t = rcp_f64(fabs(tau) + u * rsqrt_f64(u));
-            if (tau < 0.0) t = -t;
-          } else {
-            t = 0.5 / tau;
-          }
-          c = rsqrt_f64(fma(t, t, 1.0));
-          s = t * c;
-        }
-        rp[i] = p; rq[i] = q; rc[i] = c; rs[i] = s;
+        double c, s;
+        jacobi_rotation(B[p][p], B[q][q], B[p][q], c, s);
+        pq[i] = make_int2(p, q);
+        cs[i] = make_double2(c, s);
       }
       __syncthreads();
       // B <- J^T B J, one 2 x 2 block (rows of pair i, columns of pair j)
       for (int e = threadIdx.x; e < kP * kP; e += kST) {
         const int i = e / kP, j = e % kP;
-        const int pi = rp[i], qi = rq[i], pj = rp[j], qj = rq[j];
-        const double ci = rc[i], si = rs[i], cj = rc[j], sj = rs[j];
-        const double m00 = B[pi][pj], m01 = B[pi][qj], m10 = B[qi][pj], m11 = B[qi][qj];
-        const double r00 = ci * m00 - si * m10, r01 = ci * m01 - si * m11;
-        const double r10 = si * m00 + ci * m10, r11 = si * m01 + ci * m11;
-        B[pi][pj] = cj * r00 - sj * r01;
-        B[pi][qj] = sj * r00 + cj * r01;
-        B[qi][pj] = cj * r10 - sj * r11;
-        B[qi][qj] = sj * r10 + cj * r11;
+        const int2 a = pq[i], b = pq[j];
+        const double2 x = cs[i], y = cs[j];
+        const double m00 = B[a.x][b.x], m01 = B[a.x][b.y], m10 = B[a.y][b.x], m11 = B[a.y][b.y];
+        const double r00 = x.x * m00 - x.y * m10, r01 = x.x * m01 - x.y * m11;
+        const double r10 = x.y * m00 + x.x * m10, r11 = x.y * m01 + x.x * m11;
+        B[a.x][b.x] = y.x * r00 - y.y * r01;
+        B[a.x][b.y] = y.y * r00 + y.x * r01;
+        B[a.y][b.x] = y.x * r10 - y.y * r11;
+        B[a.y][b.y] = y.y * r10 + y.x * r11;
       }
-      // V <- V J
-      for (int e = threadIdx.x; e < W * kP; e += kST) {
-        const int row = e / kP, j = e % kP;
-        const int pj = rp[j], qj = rq[j];
-        const double cj = rc[j], sj = rs[j];
-        const double vp = V[row][pj], vq = V[row][qj];
-        V[row][pj] = cj * vp - sj * vq;
-        V[row][qj] = sj * vp + cj * vq;
+      // V <- V J: rows r and r + W/2 of pair j
+      for (int e = threadIdx.x; e < kP * kP; e += kST) {
+        const int r = e / kP, j = e % kP;
+        const int2 b = pq[j];
+        const double2 y = cs[j];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const double vp = V[r + h * kP][b.x], vq = V[r + h * kP][b.y];
+          V[r + h * kP][b.x] = y.x * vp - y.y * vq;
+          V[r + h * kP][b.y] = y.y * vp + y.x * vq;
+        }
       }
       __syncthreads();
     }
@@ -1566,8 +1577,8 @@ __global__ __launch_bounds__(kST) void k_ritz(G g) {
   const int d = Rin.d;
   __shared__ double B[W][W + 1];
   __shared__ double V[W][W + 1];
-  __shared__ double rc[kP], rs[kP];
-  __shared__ int rp[kP], rq[kP];
+  __shared__ int2 pq[kP];
+  __shared__ double2 cs[kP];
   __shared__ double ev[W];
   __shared__ int order[W];
   __shared__ double red[kST / 64];
@@ -1586,7 +1597,7 @@ __global__ __launch_bounds__(kST) void k_ritz(G g) {
     }
   }
   __syncthreads();
-  jacobi<W>(B, V, rc, rs, rp, rq, red);
+  jacobi<W>(B, V, pq, cs, red);
   // sort eigenvalues descending (rank by count; ties by index)
   if (threadIdx.x < W) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
   __syncthreads();
@@ -1655,8 +1666,8 @@ __global__ __launch_bounds__(kST) void k_blk_eig(G g) {
   if (i0 >= d) return;
   __shared__ double B[W][W + 1];
   __shared__ double V[W][W + 1];
-  __shared__ double rc[kP], rs[kP];
-  __shared__ int rp[kP], rq[kP];
+  __shared__ int2 pq[kP];
+  __shared__ double2 cs[kP];
   __shared__ double ev[W], fw[W], fu[W];
   __shared__ int order[W];
   __shared__ double red[kST / 64];
@@ -1675,7 +1686,7 @@ __global__ __launch_bounds__(kST) void k_blk_eig(G g) {
     }
   }
   __syncthreads();
-  jacobi<W>(B, V, rc, rs, rp, rq, red);
+  jacobi<W>(B, V, pq, cs, red);
   if (threadIdx.x < W) ev[threadIdx.x] = B[threadIdx.x][threadIdx.x];
   __syncthreads();
   const double t = *Rin.tr;
