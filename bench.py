@@ -29,6 +29,7 @@ JSON line on stdout.
     python bench.py --study reference     # full-rank, Cholesky-form and two-sided references
     python bench.py --study reduce [--ranks 8]   # simulated data-parallel reduction
     python bench.py --study matrixfree    # refresh power steps with A Q = X^T (X Q) / N
+    python bench.py --study stream        # HBM rates of the round trip's access patterns
 """
 
 import argparse
@@ -67,7 +68,7 @@ def parse():
                         "(no device QR or eigendecomposition), no quality report")
     p.add_argument("--study", default=None,
                    choices=["staleness", "interval", "rank", "reference", "copy", "reduce",
-                            "matrixfree"])
+                            "matrixfree", "stream"])
     p.add_argument("--ref-shape", default="1024,2816,8192",
                    help="hidden,mlp,tokens of the block of the reference study")
     p.add_argument("--rank-list", default="8,16,32,64,b32,b64",
@@ -210,7 +211,7 @@ def main():
         sys.exit(2)
     studies = {"staleness": staleness_study, "interval": interval_study, "rank": rank_study,
                "reference": reference_study, "reduce": reduce_study,
-               "matrixfree": matrixfree_study}
+               "matrixfree": matrixfree_study, "stream": stream_study}
     if args.study == "copy":
         print(json.dumps(copy_calibration()), flush=True)
         return
@@ -633,6 +634,66 @@ def copy_calibration(mib=1024, reps=5, device="cuda:0"):
     t = e0.elapsed_time(e1) / reps * 1e-3
     return {"study": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": reps + 1,
             "us_per_copy": round(t * 1e6, 2), "GBps": round(8 * n / t / 1e9, 1)}
+
+
+def stream_study(args, mib=1024, reps=20, device="cuda:0"):
+    """HBM rates of the access patterns the round-trip kernels use, from the
+    probe kernels of libgift_probe.so (include/gift_probe.h) on one 1 GiB
+    buffer (a 65536 x 4096 fp32 matrix for the tile and slab patterns):
+    float4 read, write and copy streams with plain and nontemporal accesses,
+    the 64 x 256 tiles read in one load round, and the 64-row slabs walked
+    32 columns at a time.  GB/s counts the bytes each kernel must move."""
+    import ctypes
+
+    import torch
+
+    from fac_whitening_gift_amd import build as fb
+
+    if not os.path.exists(fb.PROBE_LIB):
+        raise RuntimeError("libgift_probe.so is not built: python -m fac_whitening_gift_amd.build")
+    lib = ctypes.CDLL(fb.PROBE_LIB)
+    vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+    for name, types in (("gift_probe_read", [vp, sz, ctypes.c_int, vp]),
+                        ("gift_probe_write", [vp, sz, ctypes.c_int, vp]),
+                        ("gift_probe_copy", [vp, vp, sz, ctypes.c_int, vp]),
+                        ("gift_probe_tile_read", [vp, i64, i64, vp]),
+                        ("gift_probe_slab_read", [vp, i64, i64, vp])):
+        getattr(lib, name).argtypes = types
+        getattr(lib, name).restype = ctypes.c_int
+    dev = torch.device(device)
+    torch.cuda.set_device(dev)
+    nbytes = mib * 2 ** 20
+    a = torch.randn(nbytes // 4, device=dev)
+    b = torch.empty_like(a)
+    rows, cols = nbytes // 4 // 4096, 4096
+    st = torch.cuda.current_stream().cuda_stream
+    pa, pb = a.data_ptr(), b.data_ptr()
+    cases = [
+        ("read", nbytes, lambda: lib.gift_probe_read(pa, nbytes, 0, st)),
+        ("read_nt", nbytes, lambda: lib.gift_probe_read(pa, nbytes, 1, st)),
+        ("write", nbytes, lambda: lib.gift_probe_write(pb, nbytes, 0, st)),
+        ("write_nt", nbytes, lambda: lib.gift_probe_write(pb, nbytes, 1, st)),
+        ("copy", 2 * nbytes, lambda: lib.gift_probe_copy(pa, pb, nbytes, 0, st)),
+        ("copy_nt", 2 * nbytes, lambda: lib.gift_probe_copy(pa, pb, nbytes, 1, st)),
+        ("tile_read_64x256", nbytes, lambda: lib.gift_probe_tile_read(pa, rows, cols, st)),
+        ("slab_read_64_rows", nbytes, lambda: lib.gift_probe_slab_read(pa, rows, cols, st)),
+    ]
+    out = {}
+    for name, moved, fn in cases:
+        for _ in range(3):
+            if fn() != 0:
+                raise RuntimeError("probe %s failed" % name)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        out[name] = {"us": round(t * 1e6, 1), "GBps": round(moved / t / 1e9, 1)}
+    return {"study": "stream", "bytes": nbytes, "reps": reps, "hbm_peak_GBps": 8000.0,
+            "patterns": out}
 
 
 # ---------------------------------------------------------------------------

@@ -17,6 +17,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgift.so")
+# HBM streaming probes (include/gift_probe.h), a separate library used by
+# bench.py --study stream; not part of libgift.so or its source hash
+PROBE_SRC = os.path.join(CSRC, "probe", "stream.hip")
+PROBE_LIB = os.path.join(HERE, "libgift_probe.so")
+PROBE_HEADER = os.path.join(ROOT, "include", "gift_probe.h")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "roundtrip.hip", "roundtrip_rt2.hip", "refresh.hip"]
@@ -37,7 +42,8 @@ def source_hash():
     library and returned by gift_build_hash()."""
     h = hashlib.sha256()
     files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))]
-    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+              if f != os.path.basename(PROBE_HEADER)]
     for path in files:
         if os.path.isfile(path):
             h.update(os.path.basename(path).encode())
@@ -80,7 +86,18 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe():
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc()] + HIPFLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on %s:\n%s" % (PROBE_SRC, r.stdout + r.stderr))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

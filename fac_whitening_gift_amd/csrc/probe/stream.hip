@@ -1,0 +1,173 @@
+// HBM streaming probes (include/gift_probe.h): one kernel per access
+// pattern, launched on the caller's stream for event timing.  A read probe
+// folds what it loads into a value that is stored only if it equals a
+// sentinel no real input produces, so the loads cannot be dropped and
+// nothing is written.
+#include <hip/hip_runtime.h>
+
+#include "gift_probe.h"
+
+namespace {
+
+constexpr int kT = 256;        // threads of the flat probes
+constexpr int kUnroll = 4;     // float4 per thread per step
+constexpr int kGrid = 256 * 8; // workgroups of the flat probes
+constexpr int kPW = 8;         // waves of the tile and slab probes
+constexpr float kSentinel = 1.2345678e37f;  // positive: a max of |values| can reach it
+
+typedef __attribute__((ext_vector_type(4))) float f4;
+
+template <bool kNt>
+__device__ __forceinline__ f4 ld(const f4* p) {
+  if constexpr (kNt) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool kNt>
+__device__ __forceinline__ void st(f4* p, f4 v) {
+  if constexpr (kNt) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+__device__ __forceinline__ float fold(f4 v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
+
+template <bool kNt>
+__global__ __launch_bounds__(kT) void k_read(const f4* __restrict__ p, size_t n, float* sink) {
+  float m = 0.f;
+  const size_t step = (size_t)gridDim.x * kT * kUnroll;
+  for (size_t i = (size_t)blockIdx.x * kT * kUnroll + threadIdx.x; i < n; i += step) {
+    f4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = i + u * kT < n ? ld<kNt>(p + i + u * kT) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) m = fmaxf(m, fold(v[u]));
+  }
+  if (m == kSentinel) sink[0] = m;
+}
+
+template <bool kNt>
+__global__ __launch_bounds__(kT) void k_write(f4* __restrict__ p, size_t n) {
+  const size_t step = (size_t)gridDim.x * kT * kUnroll;
+  for (size_t i = (size_t)blockIdx.x * kT * kUnroll + threadIdx.x; i < n; i += step)
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (i + u * kT < n) st<kNt>(p + i + u * kT, f4{0.f, 0.f, 0.f, 0.f});
+}
+
+template <bool kNt>
+__global__ __launch_bounds__(kT) void k_copy(const f4* __restrict__ s, f4* __restrict__ d, size_t n) {
+  const size_t step = (size_t)gridDim.x * kT * kUnroll;
+  for (size_t i = (size_t)blockIdx.x * kT * kUnroll + threadIdx.x; i < n; i += step) {
+    f4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = i + u * kT < n ? ld<kNt>(s + i + u * kT) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (i + u * kT < n) st<kNt>(d + i + u * kT, v[u]);
+  }
+}
+
+// the float4s lane (r16, g) of a wave loads from a 32-column chunk c of a
+// 64-row block: rows 16 rt + r16, columns 32 c + 4 g and 32 c + 16 + 4 g
+__device__ __forceinline__ void chunk_loads(const float* m, int64_t cols, int64_t row0, int c,
+                                            f4 (&v)[4][2]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const float* p = m + (row0 + 16 * rt + r16) * cols + 32 * c + 4 * g;
+    v[rt][0] = *reinterpret_cast<const f4*>(p);
+    v[rt][1] = *reinterpret_cast<const f4*>(p + 16);
+  }
+}
+__device__ __forceinline__ float fold8(const f4 (&v)[4][2]) {
+  float m = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) m = fmaxf(m, fmaxf(fold(v[rt][0]), fold(v[rt][1])));
+  return m;
+}
+
+// one workgroup per 64 x 256 tile; wave w takes chunk w of the tile
+__global__ __launch_bounds__(64 * kPW) void k_tile_read(const float* __restrict__ m, int64_t cols,
+                                                       float* sink) {
+  const int64_t tiles_per_row = cols / 256;
+  const int64_t rb = blockIdx.x / tiles_per_row, cg = blockIdx.x % tiles_per_row;
+  const int w = threadIdx.x >> 6;
+  f4 v[4][2];
+  chunk_loads(m, cols, rb * 64, (int)(cg * kPW + w), v);
+  const float x = fold8(v);
+  if (x == kSentinel) sink[0] = x;
+}
+
+// one workgroup per 64-row slab; wave w walks chunks w, w + 8, ... with the
+// next chunk's loads issued before the current one is folded
+__global__ __launch_bounds__(64 * kPW) void k_slab_read(const float* __restrict__ m, int64_t cols,
+                                                       float* sink) {
+  const int w = threadIdx.x >> 6;
+  const int nch = (int)(cols / 32);
+  const int64_t row0 = (int64_t)blockIdx.x * 64;
+  float acc = 0.f;
+  f4 a[4][2], b[4][2];
+  chunk_loads(m, cols, row0, w, a);
+  for (int c = w; c < nch; c += 2 * kPW) {
+    const int c1 = c + kPW < nch ? c + kPW : c;
+    chunk_loads(m, cols, row0, c1, b);
+    acc = fmaxf(acc, fold8(a));
+    const int c2 = c + 2 * kPW < nch ? c + 2 * kPW : c1;
+    chunk_loads(m, cols, row0, c2, a);
+    acc = fmaxf(acc, fold8(b));
+  }
+  if (acc == kSentinel) sink[0] = acc;
+}
+
+bool aligned(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
+int launched() { return hipGetLastError() == hipSuccess ? 0 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int gift_probe_read(const void* buf, size_t bytes, int nontemporal, void* stream) {
+  if (!aligned(buf) || bytes == 0 || bytes % 16) return 1;
+  const f4* p = static_cast<const f4*>(buf);
+  float* sink = const_cast<float*>(static_cast<const float*>(buf));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal) k_read<true><<<kGrid, kT, 0, s>>>(p, bytes / 16, sink);
+  else k_read<false><<<kGrid, kT, 0, s>>>(p, bytes / 16, sink);
+  return launched();
+}
+
+int gift_probe_write(void* buf, size_t bytes, int nontemporal, void* stream) {
+  if (!aligned(buf) || bytes == 0 || bytes % 16) return 1;
+  f4* p = static_cast<f4*>(buf);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal) k_write<true><<<kGrid, kT, 0, s>>>(p, bytes / 16);
+  else k_write<false><<<kGrid, kT, 0, s>>>(p, bytes / 16);
+  return launched();
+}
+
+int gift_probe_copy(const void* src, void* dst, size_t bytes, int nontemporal, void* stream) {
+  if (!aligned(src) || !aligned(dst) || bytes == 0 || bytes % 16) return 1;
+  const f4* a = static_cast<const f4*>(src);
+  f4* b = static_cast<f4*>(dst);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal) k_copy<true><<<kGrid, kT, 0, s>>>(a, b, bytes / 16);
+  else k_copy<false><<<kGrid, kT, 0, s>>>(a, b, bytes / 16);
+  return launched();
+}
+
+int gift_probe_tile_read(const float* m, int64_t rows, int64_t cols, void* stream) {
+  if (!aligned(m) || rows <= 0 || cols <= 0 || rows % 64 || cols % 256) return 1;
+  const int64_t tiles = rows / 64 * (cols / 256);
+  if (tiles > 0x7fffffff) return 1;
+  k_tile_read<<<(unsigned)tiles, 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(
+      m, cols, const_cast<float*>(m));
+  return launched();
+}
+
+int gift_probe_slab_read(const float* m, int64_t rows, int64_t cols, void* stream) {
+  if (!aligned(m) || rows <= 0 || cols <= 0 || rows % 64 || cols % 256) return 1;
+  if (rows / 64 > 0x7fffffff) return 1;
+  k_slab_read<<<(unsigned)(rows / 64), 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(
+      m, cols, const_cast<float*>(m));
+  return launched();
+}
+
+}  // extern "C"

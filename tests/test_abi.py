@@ -232,3 +232,27 @@ def test_static_scratch_entry_rejects_groups_beyond_its_array():
     assert lib.gift_whiten_quantize_static(arr, 1, fg.SCALE_TENSOR, None, None) == 3
     assert b"16777216" in lib.gift_last_error()
     assert lib.gift_whiten_quantize_static(arr, 1, 9, None, None) == 1
+
+
+def test_probe_library_exports_every_declared_function():
+    """libgift_probe.so (the streaming probes of bench.py --study stream)
+    exports what include/gift_probe.h declares and rejects bad arguments
+    before any launch."""
+    from fac_whitening_gift_amd import build as fb
+    if not os.path.exists(fb.PROBE_LIB):
+        pytest.skip("libgift_probe.so not built")
+    src = open(os.path.join(ROOT, "include", "gift_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(gift_probe_\w+)\s*\(", src)))
+    assert len(names) == 5
+    lib = ctypes.CDLL(fb.PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+    lib.gift_probe_read.argtypes = [vp, sz, ctypes.c_int, vp]
+    lib.gift_probe_tile_read.argtypes = [vp, i64, i64, vp]
+    assert lib.gift_probe_read(None, 1024, 0, None) == 1
+    assert lib.gift_probe_read(0x10008, 1024, 0, None) == 1
+    assert lib.gift_probe_read(0x10000, 1000, 0, None) == 1
+    assert lib.gift_probe_tile_read(0x10000, 100, 4096, None) == 1
+    assert lib.gift_probe_tile_read(0x10000, 128, 300, None) == 1
