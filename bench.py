@@ -641,8 +641,8 @@ def stream_study(args, mib=1024, reps=20, device="cuda:0"):
     probe kernels of libgift_probe.so (include/gift_probe.h) on one 1 GiB
     buffer (a 65536 x 4096 fp32 matrix for the tile and slab patterns):
     float4 read, write and copy streams with plain and nontemporal accesses,
-    the 64 x 256 tiles read in one load round, and the 64-row slabs walked
-    32 columns at a time.  GB/s counts the bytes each kernel must move."""
+    the 64 x 256 tiles read in one load round and written in the un-whiten
+    pass's store pattern, and the 64-row slabs walked 32 columns at a time.  GB/s counts the bytes each kernel must move."""
     import ctypes
 
     import torch
@@ -657,6 +657,7 @@ def stream_study(args, mib=1024, reps=20, device="cuda:0"):
                         ("gift_probe_write", [vp, sz, ctypes.c_int, vp]),
                         ("gift_probe_copy", [vp, vp, sz, ctypes.c_int, vp]),
                         ("gift_probe_tile_read", [vp, i64, i64, vp]),
+                        ("gift_probe_tile_write", [vp, i64, i64, ctypes.c_int, vp]),
                         ("gift_probe_slab_read", [vp, i64, i64, vp])):
         getattr(lib, name).argtypes = types
         getattr(lib, name).restype = ctypes.c_int
@@ -676,6 +677,8 @@ def stream_study(args, mib=1024, reps=20, device="cuda:0"):
         ("copy", 2 * nbytes, lambda: lib.gift_probe_copy(pa, pb, nbytes, 0, st)),
         ("copy_nt", 2 * nbytes, lambda: lib.gift_probe_copy(pa, pb, nbytes, 1, st)),
         ("tile_read_64x256", nbytes, lambda: lib.gift_probe_tile_read(pa, rows, cols, st)),
+        ("tile_write_64x256", nbytes, lambda: lib.gift_probe_tile_write(pb, rows, cols, 0, st)),
+        ("tile_write_64x256_nt", nbytes, lambda: lib.gift_probe_tile_write(pb, rows, cols, 1, st)),
         ("slab_read_64_rows", nbytes, lambda: lib.gift_probe_slab_read(pa, rows, cols, st)),
     ]
     out = {}

@@ -96,6 +96,22 @@ __global__ __launch_bounds__(64 * kPW) void k_tile_read(const float* __restrict_
   if (x == kSentinel) sink[0] = x;
 }
 
+// one workgroup per 64 x 256 tile, each lane storing its fragments' float4s
+// (the un-whiten pass's stores: 16 rows x 64 bytes per store instruction)
+template <bool kNt>
+__global__ __launch_bounds__(64 * kPW) void k_tile_write(float* __restrict__ m, int64_t cols) {
+  const int64_t tiles_per_row = cols / 256;
+  const int64_t rb = blockIdx.x / tiles_per_row, cg = blockIdx.x % tiles_per_row;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4, w = threadIdx.x >> 6;
+  const int c = (int)(cg * kPW + w);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    float* p = m + (rb * 64 + 16 * rt + r16) * cols + 32 * c + 4 * g;
+    st<kNt>(reinterpret_cast<f4*>(p), f4{0.f, 0.f, 0.f, 0.f});
+    st<kNt>(reinterpret_cast<f4*>(p + 16), f4{0.f, 0.f, 0.f, 0.f});
+  }
+}
+
 // one workgroup per 64-row slab; wave w walks chunks w, w + 8, ... with the
 // next chunk's loads issued before the current one is folded
 __global__ __launch_bounds__(64 * kPW) void k_slab_read(const float* __restrict__ m, int64_t cols,
@@ -159,6 +175,16 @@ int gift_probe_tile_read(const float* m, int64_t rows, int64_t cols, void* strea
   if (tiles > 0x7fffffff) return 1;
   k_tile_read<<<(unsigned)tiles, 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(
       m, cols, const_cast<float*>(m));
+  return launched();
+}
+
+int gift_probe_tile_write(float* m, int64_t rows, int64_t cols, int nontemporal, void* stream) {
+  if (!aligned(m) || rows <= 0 || cols <= 0 || rows % 64 || cols % 256) return 1;
+  const int64_t tiles = rows / 64 * (cols / 256);
+  if (tiles > 0x7fffffff) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal) k_tile_write<true><<<(unsigned)tiles, 64 * kPW, 0, s>>>(m, cols);
+  else k_tile_write<false><<<(unsigned)tiles, 64 * kPW, 0, s>>>(m, cols);
   return launched();
 }
 

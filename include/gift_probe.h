@@ -36,6 +36,10 @@ int gift_probe_copy(const void* src, void* dst, size_t bytes, int nontemporal, v
  * 64 x 256 tiles, one workgroup of 8 waves per tile, each lane loading its
  * 16-row MFMA fragments' float4s in one round */
 int gift_probe_tile_read(const float* m, int64_t rows, int64_t cols, void* stream);
+/* write zeros to the same matrix in 64 x 256 tiles, each lane storing the
+ * float4s of its 16-row MFMA fragments (16 rows x 64 bytes per store
+ * instruction) */
+int gift_probe_tile_write(float* m, int64_t rows, int64_t cols, int nontemporal, void* stream);
 /* read the same matrix in 64-row slabs (rows % 64 == 0, cols % 256 == 0),
  * one workgroup of 8 waves per slab, wave w walking the 32-column chunks
  * w, w + 8, ... with the next chunk's loads in flight */
