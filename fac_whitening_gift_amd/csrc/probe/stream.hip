@@ -1,11 +1,15 @@
 // HBM streaming probes (include/gift_probe.h): one kernel per access
 // pattern, launched on the caller's stream for event timing.  A read probe
-// folds what it loads into a value that is stored only if it equals a
-// sentinel no real input produces, so the loads cannot be dropped and
-// nothing is written.
+// folds what it loads into a value that it stores (into the library's own
+// device word g_sink) only if it equals a sentinel no real input produces,
+// so the loads cannot be dropped and the caller's memory is never written.
 #include <hip/hip_runtime.h>
 
 #include "gift_probe.h"
+
+// written only when a fold hits the sentinel; external linkage, so the
+// stores (and the loads they depend on) stay in the kernels
+__device__ float g_sink;
 
 namespace {
 
@@ -13,7 +17,7 @@ constexpr int kT = 256;        // threads of the flat probes
 constexpr int kUnroll = 4;     // float4 per thread per step
 constexpr int kGrid = 256 * 8; // workgroups of the flat probes
 constexpr int kPW = 8;         // waves of the tile and slab probes
-constexpr float kSentinel = 1.2345678e37f;  // positive: a max of |values| can reach it
+constexpr float kSentinel = 1.2345678e37f;  // positive: a max that starts at 0 may reach it
 
 typedef __attribute__((ext_vector_type(4))) float f4;
 
@@ -30,7 +34,7 @@ __device__ __forceinline__ void st(f4* p, f4 v) {
 __device__ __forceinline__ float fold(f4 v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
 
 template <bool kNt>
-__global__ __launch_bounds__(kT) void k_read(const f4* __restrict__ p, size_t n, float* sink) {
+__global__ __launch_bounds__(kT) void k_read(const f4* __restrict__ p, size_t n) {
   float m = 0.f;
   const size_t step = (size_t)gridDim.x * kT * kUnroll;
   for (size_t i = (size_t)blockIdx.x * kT * kUnroll + threadIdx.x; i < n; i += step) {
@@ -40,7 +44,7 @@ __global__ __launch_bounds__(kT) void k_read(const f4* __restrict__ p, size_t n,
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) m = fmaxf(m, fold(v[u]));
   }
-  if (m == kSentinel) sink[0] = m;
+  if (m == kSentinel) g_sink = m;
 }
 
 template <bool kNt>
@@ -85,15 +89,14 @@ __device__ __forceinline__ float fold8(const f4 (&v)[4][2]) {
 }
 
 // one workgroup per 64 x 256 tile; wave w takes chunk w of the tile
-__global__ __launch_bounds__(64 * kPW) void k_tile_read(const float* __restrict__ m, int64_t cols,
-                                                       float* sink) {
+__global__ __launch_bounds__(64 * kPW) void k_tile_read(const float* __restrict__ m, int64_t cols) {
   const int64_t tiles_per_row = cols / 256;
   const int64_t rb = blockIdx.x / tiles_per_row, cg = blockIdx.x % tiles_per_row;
   const int w = threadIdx.x >> 6;
   f4 v[4][2];
   chunk_loads(m, cols, rb * 64, (int)(cg * kPW + w), v);
   const float x = fold8(v);
-  if (x == kSentinel) sink[0] = x;
+  if (x == kSentinel) g_sink = x;
 }
 
 // one workgroup per 64 x 256 tile, each lane storing its fragments' float4s
@@ -114,8 +117,7 @@ __global__ __launch_bounds__(64 * kPW) void k_tile_write(float* __restrict__ m, 
 
 // one workgroup per 64-row slab; wave w walks chunks w, w + 8, ... with the
 // next chunk's loads issued before the current one is folded
-__global__ __launch_bounds__(64 * kPW) void k_slab_read(const float* __restrict__ m, int64_t cols,
-                                                       float* sink) {
+__global__ __launch_bounds__(64 * kPW) void k_slab_read(const float* __restrict__ m, int64_t cols) {
   const int w = threadIdx.x >> 6;
   const int nch = (int)(cols / 32);
   const int64_t row0 = (int64_t)blockIdx.x * 64;
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(64 * kPW) void k_slab_read(const float* __restrict_
     chunk_loads(m, cols, row0, c2, a);
     acc = fmaxf(acc, fold8(b));
   }
-  if (acc == kSentinel) sink[0] = acc;
+  if (acc == kSentinel) g_sink = acc;
 }
 
 bool aligned(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
@@ -143,10 +145,9 @@ extern "C" {
 int gift_probe_read(const void* buf, size_t bytes, int nontemporal, void* stream) {
   if (!aligned(buf) || bytes == 0 || bytes % 16) return 1;
   const f4* p = static_cast<const f4*>(buf);
-  float* sink = const_cast<float*>(static_cast<const float*>(buf));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (nontemporal) k_read<true><<<kGrid, kT, 0, s>>>(p, bytes / 16, sink);
-  else k_read<false><<<kGrid, kT, 0, s>>>(p, bytes / 16, sink);
+  if (nontemporal) k_read<true><<<kGrid, kT, 0, s>>>(p, bytes / 16);
+  else k_read<false><<<kGrid, kT, 0, s>>>(p, bytes / 16);
   return launched();
 }
 
@@ -173,8 +174,7 @@ int gift_probe_tile_read(const float* m, int64_t rows, int64_t cols, void* strea
   if (!aligned(m) || rows <= 0 || cols <= 0 || rows % 64 || cols % 256) return 1;
   const int64_t tiles = rows / 64 * (cols / 256);
   if (tiles > 0x7fffffff) return 1;
-  k_tile_read<<<(unsigned)tiles, 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(
-      m, cols, const_cast<float*>(m));
+  k_tile_read<<<(unsigned)tiles, 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(m, cols);
   return launched();
 }
 
@@ -191,8 +191,7 @@ int gift_probe_tile_write(float* m, int64_t rows, int64_t cols, int nontemporal,
 int gift_probe_slab_read(const float* m, int64_t rows, int64_t cols, void* stream) {
   if (!aligned(m) || rows <= 0 || cols <= 0 || rows % 64 || cols % 256) return 1;
   if (rows / 64 > 0x7fffffff) return 1;
-  k_slab_read<<<(unsigned)(rows / 64), 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(
-      m, cols, const_cast<float*>(m));
+  k_slab_read<<<(unsigned)(rows / 64), 64 * kPW, 0, static_cast<hipStream_t>(stream)>>>(m, cols);
   return launched();
 }
 
