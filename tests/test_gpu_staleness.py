@@ -58,3 +58,59 @@ def test_reference_study_small():
     assert rows["input_full"]["m2"] < rows["gift_rank32"]["m2"] < rows["euclid"]["m2"]
     assert rows["input_cholesky"]["m2"] < rows["euclid"]["m2"]
     assert rows["two_sided"]["m2"] < rows["euclid"]["m2"]
+
+
+def test_staleness_values_match_oracle():
+    """The study's M2 at step 1 against the oracle on the same seeded inputs:
+    the factors from the oracle's refresh (its own Philox sketch of the seeds
+    the device uses), the oracle's round trips, and the metric
+    (C_t + lambda I)^-1/2 of the population covariance C_t = Q_t diag(ev) Q_t^T
+    by the oracle's eigendecomposition instead of the study's closed form;
+    M2 pooled over the layers as the study pools it.  Euclidean codes are the
+    same on both sides, so its M2 agrees to rounding; the GIFT factors differ
+    by fp32 against fp64, which can move a few codes (measured: 2e-5
+    relative).  The interval study runs the same refresh and error helpers."""
+    import torch
+
+    import synth
+    from oracle import gift as og
+    from oracle import philox
+
+    say("staleness values vs oracle, hidden 256 mlp 512, 2 steps of 0.15 rad")
+    args = argparse.Namespace(blocks=1, hidden=256, mlp=512, tokens=4096, angle=0.15,
+                              study_steps=2, quiet=True)
+    out = bench.staleness_study(args)
+    row = out["rows"][1]
+    dev = torch.device("cuda:0")
+    w, base, rots = bench._rotating_block(args, dev)
+    stale, fresh, S = {}, {}, {}
+    for t in (0, 1):
+        Qt, X = bench._inputs_at(w, base, rots, t, args.angle, dev)
+        for k, spec in enumerate(w.inputs):
+            Xh = X[spec.name]["X"].float().cpu().numpy()
+            f = og.refresh_factor(Xh, philox.gaussian_sketch(spec.d_in, 64, k))
+            if t == 0:
+                stale[spec.name] = f
+            else:
+                fresh[spec.name] = f
+                ev = X[spec.name]["ev"].double().cpu().numpy()
+                Q = Qt[spec.name].double().cpu().numpy()
+                lam = 1e-3 * ev.sum() / spec.d_in
+                S[spec.name] = og.metric_sqrt_inv((Q * ev) @ Q.T, lam)
+    num = {"euclid": 0.0, "stale": 0.0, "fresh": 0.0}
+    den = 0.0
+    for i, l in enumerate(w.layers):
+        G = synth.draw_gradient(l.d_out, Qt[l.input], X[l.input]["ev"], seed=9000 + 100 + i,
+                                device=dev).cpu().numpy().astype(np.float64)
+        M = S[l.input]
+        den += np.linalg.norm(G @ M) ** 2
+        for m, G_hat in (("euclid", og.euclid_roundtrip(G)[2]),
+                         ("stale", og.gift_roundtrip(G, stale[l.input])[3]),
+                         ("fresh", og.gift_roundtrip(G, fresh[l.input])[3])):
+            num[m] += np.linalg.norm((np.asarray(G_hat, dtype=np.float64) - G) @ M) ** 2
+    m2 = {m: np.sqrt(v / den) for m, v in num.items()}
+    say("M2 study %s, oracle %s" % ({m: row["m2_%s_tensor" % m] for m in m2},
+                                    {m: round(float(v), 6) for m, v in m2.items()}))
+    assert abs(row["m2_euclid_tensor"] - m2["euclid"]) <= 1e-4 * m2["euclid"]
+    for m in ("stale", "fresh"):
+        assert abs(row["m2_%s_tensor" % m] - m2[m]) <= 1e-3 * m2[m], (m, row, m2)
